@@ -1,0 +1,382 @@
+"""Plain fp64 CPU oracle of the GPTQ layer quantizer.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s cpu_baseline leg, never by the HIP product path. It shares
+no code with the HIP library; the only thing both sides share is the seeded
+input generator, which holds none of the method's arithmetic.
+
+Sources (web pages, cited by title and section):
+
+* [CHMC] "Warum Geometrie Gewichte nicht komprimiert" (nonndazone.ru), section
+  "Methodik. Was ist CHMC", Schritt 2 (GPTQ residual step: Hessian from the
+  calibration activations, damping lambda*mean(diag H)*I, inverse via Cholesky,
+  act-order, per-column rounding and error propagation with the row of the
+  inverse factor), Schritt 3 (bits-per-weight formula, groups along input
+  channels for GPTQ), Tabelle 1 (GPTQ stores integer indices + group scales).
+* [BABAI] "The Geometry of LLM Quantization: GPTQ as Babai's Nearest Plane
+  Algorithm" (gist.science), section 2.1 (CVP with basis X*diag(s); Satz 1: any
+  factorisation of the Hessian gives an equivalent instance), 2.2 (error
+  propagation = projection on the nearest hyperplane; Satz 4: GPTQ run from
+  the back equals Babai without LLL), 2.3 (Satz 5: no-clipping bound with the
+  LDL diagonal of the permuted Hessian; min-pivot vs act-order).
+* [HIGHRATE] "Quantisierte Matrixmultiplikation mit hoher Rate I"
+  (gist.science), "Methodik und Theoretischer Rahmen" (rounding error modelled
+  as independent uniform noise).
+
+Readings of what the pages leave open (each listed in the design doc):
+
+* H = (2/n) * X^T X. The CHMC page writes X^T X / n; the positive factor does
+  not change codes (the update uses U[j,k]/U[j,j]) and only scales the loss.
+* Damping: H += damp * mean(diag H) * I, mean over the undamped diagonal.
+* The "row of H^-1" in the propagation step is the row of the upper Cholesky
+  factor U of H^-1 (U^T U = H^-1), the page's "inverse via Cholesky".
+* Groups: gs consecutive columns in sweep (permuted) order, along input
+  channels, one fp16 scale and one integer zero point per (row, group).
+* Grid (asymmetric min-max): when the sweep reaches a group's first column the
+  grid is taken from the *current* (error-updated) values of the group's
+  columns: xmin = min(0, min v), xmax = max(0, max v);
+  scale = (xmax - xmin)/maxq rounded to the nearest-even fp16 value,
+  zero = clamp(rint(-xmin/scale), 0, maxq). A group with xmax == xmin, or
+  whose scale rounds to fp16 zero, gets scale 1 and zero 0. A scale that
+  overflows fp16 is an error.
+* Rounding is round-half-to-even (rint); codes are clamped to [0, maxq]
+  unless ``clip=False`` (the no-clipping regime of [BABAI] 2.3).
+* Act-order: stable argsort of -diag(H) (ties keep the lower index first).
+* Per-row loss: sum_j e_j^2 with e_j = (w~_j - q_j)/U[j,j]; this equals
+  (w-q) H (w-q)^T for the damped, permuted H.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+
+__all__ = [
+    "NotSPD", "NonFinite", "hessian_sum", "hessian_entry", "damped_hessian",
+    "act_order_perm", "permute_sym", "hinv_upper", "fp16_round", "group_grid",
+    "gptq_sweep", "gptq_layer", "rtn_quantize", "dequantize_sweep",
+    "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
+    "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups",
+]
+
+F64 = np.float64
+
+
+class NotSPD(ValueError):
+    """The damped Hessian is not symmetric positive definite."""
+
+
+class NonFinite(ValueError):
+    """A non-finite input, or a group scale that overflows fp16."""
+
+
+# --------------------------------------------------------------------------
+# Hessian statistics  ([CHMC] Schritt 2: H = X^T X / n from the calibration
+# activations of the layer; accumulation is a plain sum over tokens)
+# --------------------------------------------------------------------------
+
+def hessian_sum(chunks):
+    """S = sum over token chunks of X_c^T X_c in fp64, and the token count.
+
+    ``chunks`` is one fp32 array [n_tokens x in_features] or an iterable of
+    them. fp32 x fp32 products are exact in fp64; only the summation rounds.
+    """
+    if isinstance(chunks, np.ndarray):
+        chunks = [chunks]
+    S = None
+    n = 0
+    for X in chunks:
+        Xd = np.asarray(X, dtype=np.float32).astype(F64)
+        if not np.all(np.isfinite(Xd)):
+            raise NonFinite("calibration activations contain NaN/Inf")
+        part = Xd.T @ Xd
+        S = part if S is None else S + part
+        n += Xd.shape[0]
+    return S, n
+
+
+def hessian_entry(X, f, g):
+    """One entry S[f, g] = sum_t X[t,f] X[t,g], summed with math.fsum.
+
+    The products are exact in fp64 and fsum returns the correctly rounded
+    sum, so this is the exact value rounded once; used for sampled checks of
+    Hessians too large to form on the CPU.
+    """
+    a = np.asarray(X[:, f], dtype=np.float32).astype(F64)
+    b = np.asarray(X[:, g], dtype=np.float32).astype(F64)
+    return math.fsum((a * b).tolist())
+
+
+def damped_hessian(S, n_tokens, damp):
+    """H = (2/n) S + damp * mean(diag((2/n) S)) * I   ([CHMC] Schritt 2)."""
+    if n_tokens <= 0:
+        raise ValueError("n_tokens must be positive")
+    H = (2.0 / n_tokens) * np.asarray(S, dtype=F64)
+    lam = damp * float(np.mean(np.diag(H)))
+    H = H + lam * np.eye(H.shape[0])
+    return H
+
+
+def act_order_perm(H):
+    """Columns in descending importance = descending diag(H), stable
+    ([CHMC] Schritt 2 "act-order"; [BABAI] 2.3)."""
+    return np.argsort(-np.diag(H), kind="stable").astype(np.int64)
+
+
+def permute_sym(H, perm):
+    return H[np.ix_(perm, perm)]
+
+
+def hinv_upper(Hp):
+    """U upper triangular with U^T U = Hp^-1: inverse of the Hessian, then
+    its Cholesky factor, written as the upper factor ([CHMC] Schritt 2
+    "H^-1 via the Cholesky decomposition")."""
+    try:
+        np.linalg.cholesky(Hp)  # SPD check on H itself
+        Hinv = np.linalg.inv(Hp)
+        L = np.linalg.cholesky(Hinv)
+    except np.linalg.LinAlgError as exc:
+        raise NotSPD(str(exc)) from exc
+    return L.T.copy()
+
+
+# --------------------------------------------------------------------------
+# Grid and rounding  ([CHMC] Schritt 2: q_j = round(col_j/scale_g)*scale_g;
+# asymmetric min-max grid per group, fp16 scale, integer zero point)
+# --------------------------------------------------------------------------
+
+def fp16_round(x):
+    """Nearest-even fp16 value of fp64 ``x`` (returned as fp64)."""
+    return np.asarray(x, dtype=F64).astype(np.float16).astype(F64)
+
+
+def group_grid(V, bits):
+    """Per-row (scale, zero) from the current values V [rows x g] of a group."""
+    maxq = (1 << bits) - 1
+    V = np.asarray(V, dtype=F64)
+    xmin = np.minimum(V.min(axis=1), 0.0)
+    xmax = np.maximum(V.max(axis=1), 0.0)
+    with np.errstate(over="ignore"):
+        scale = fp16_round((xmax - xmin) / maxq)
+    if not np.all(np.isfinite(scale)):
+        raise NonFinite("group scale overflows fp16")
+    degenerate = (xmax == xmin) | (scale == 0.0)
+    scale = np.where(degenerate, 1.0, scale)
+    zero = np.clip(np.rint(-xmin / scale), 0, maxq)
+    zero = np.where(degenerate, 0.0, zero)
+    return scale, zero
+
+
+def _quantize(v, scale, zero, maxq, clip):
+    q = np.rint(v / scale) + zero
+    if clip:
+        q = np.clip(q, 0, maxq)
+    return q, scale * (q - zero)
+
+
+def num_groups(cols, group_size):
+    return -(-cols // group_size)
+
+
+# --------------------------------------------------------------------------
+# The column sweep  ([CHMC] Schritt 2 "strict_sequential": one column at a
+# time with the full row of the factor; [BABAI] 2.2: the propagation is the
+# projection onto the nearest hyperplane)
+# --------------------------------------------------------------------------
+
+def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
+               block=None):
+    """Sweep the columns of Wp (already in sweep order) with the factor U.
+
+    Strict form (``block=None``): after column j is rounded, its scaled error
+    e_j = (w~_j - q_j)/U[j,j] is subtracted from every later column through
+    row j of U. Lazy form (``block=B``): within a block of B columns the
+    update reaches only the block; the remaining columns receive
+    E[:, block] @ U[block, rest] when the block ends — the same sums in
+    another order. ``static_grid=(scales, zeros)`` [rows x groups] fixes the
+    grid instead of taking it at each group start.
+
+    Returns dict with codes (sweep order, int64), scales, zeros
+    [rows x groups], E [rows x cols], row_loss [rows], deq (dequantized).
+    """
+    W = np.array(Wp, dtype=F64, copy=True)
+    if not np.all(np.isfinite(W)):
+        raise NonFinite("weights contain NaN/Inf")
+    rows, cols = W.shape
+    U = np.asarray(U, dtype=F64)
+    assert U.shape == (cols, cols)
+    maxq = (1 << bits) - 1
+    gs = group_size
+    ng = num_groups(cols, gs)
+    if block is not None and not (block % gs == 0 or gs % block == 0):
+        raise ValueError("lazy blocks need group_size | block or block | group_size")
+    codes = np.zeros((rows, cols), dtype=np.int64)
+    deq = np.zeros((rows, cols), dtype=F64)
+    E = np.zeros((rows, cols), dtype=F64)
+    scales = np.zeros((rows, ng), dtype=F64)
+    zeros = np.zeros((rows, ng), dtype=F64)
+    loss = np.zeros(rows, dtype=F64)
+    step = cols if block is None else block
+    for j0 in range(0, cols, step):
+        j1 = min(j0 + step, cols)
+        for j in range(j0, j1):
+            g = j // gs
+            if j % gs == 0:
+                if static_grid is None:
+                    s, z = group_grid(W[:, j:min(j + gs, cols)], bits)
+                else:
+                    s = np.asarray(static_grid[0], dtype=F64)[:, g]
+                    z = np.asarray(static_grid[1], dtype=F64)[:, g]
+                scales[:, g] = s
+                zeros[:, g] = z
+            q, dq = _quantize(W[:, j], scales[:, g], zeros[:, g], maxq, clip)
+            codes[:, j] = q.astype(np.int64)
+            deq[:, j] = dq
+            e = (W[:, j] - dq) / U[j, j]
+            E[:, j] = e
+            loss += e * e
+            W[:, j + 1:j1] -= np.outer(e, U[j, j + 1:j1])
+        if j1 < cols:
+            W[:, j1:] -= E[:, j0:j1] @ U[j0:j1, j1:]
+    return {"codes": codes, "scales": scales, "zeros": zeros, "E": E,
+            "row_loss": loss, "deq": deq}
+
+
+def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
+               act_order=False, clip=True, block=None):
+    """The whole layer: damping, optional act-order, U, sweep, un-permute.
+
+    Outputs follow the library's layout: codes [rows x cols] in the original
+    column order, scales/zeros [rows x groups] with groups in sweep order,
+    g_idx[perm[k]] = k // group_size, perm, U, H (damped, permuted), loss.
+    """
+    W = np.asarray(W_fp16)
+    if W.dtype != np.float16:
+        raise TypeError("W must be fp16")
+    Wd = W.astype(F64)
+    H = damped_hessian(S, n_tokens, damp)
+    if not np.all(np.isfinite(H)):
+        raise NonFinite("Hessian is not finite")
+    cols = H.shape[0]
+    perm = act_order_perm(H) if act_order else np.arange(cols, dtype=np.int64)
+    Hp = permute_sym(H, perm)
+    U = hinv_upper(Hp)
+    res = gptq_sweep(Wd[:, perm], U, bits, group_size, clip=clip, block=block)
+    codes = np.empty_like(res["codes"])
+    codes[:, perm] = res["codes"]
+    g_idx = np.empty(cols, dtype=np.int64)
+    g_idx[perm] = np.arange(cols) // group_size
+    res.update({"codes_sweep": res["codes"], "codes": codes, "g_idx": g_idx,
+                "perm": perm, "U": U, "Hp": Hp})
+    return res
+
+
+def dequantize_sweep(codes_sweep, scales, zeros, group_size):
+    """Q[:, j] = scale[:, g] * (code[:, j] - zero[:, g]) with g = j // gs."""
+    cols = codes_sweep.shape[1]
+    g = np.arange(cols) // group_size
+    return scales[:, g] * (codes_sweep.astype(F64) - zeros[:, g])
+
+
+def loss_quadratic(D, H):
+    """Per-row (w-q) H (w-q)^T for residual rows D."""
+    return np.einsum("ij,jk,ik->i", D, H, D)
+
+
+# --------------------------------------------------------------------------
+# Special cases and independent algorithms used as pins
+# --------------------------------------------------------------------------
+
+def rtn_quantize(W, bits, group_size):
+    """Round-to-nearest on the grid of each group of the untouched weights:
+    what the sweep must reduce to when H is diagonal (no propagation)."""
+    W = np.asarray(W, dtype=F64)
+    rows, cols = W.shape
+    maxq = (1 << bits) - 1
+    ng = num_groups(cols, group_size)
+    codes = np.zeros((rows, cols), dtype=np.int64)
+    scales = np.zeros((rows, ng))
+    zeros = np.zeros((rows, ng))
+    for g in range(ng):
+        sl = slice(g * group_size, min((g + 1) * group_size, cols))
+        s, z = group_grid(W[:, sl], bits)
+        scales[:, g], zeros[:, g] = s, z
+        q = np.clip(np.rint(W[:, sl] / s[:, None]) + z[:, None], 0, maxq)
+        codes[:, sl] = q.astype(np.int64)
+    return codes, scales, zeros
+
+
+def babai_nearest_plane(A, w, s, z, maxq, clip=True):
+    """Babai's nearest-plane algorithm ([BABAI] 2.1-2.2) for one row.
+
+    Lattice basis: columns of A @ diag(s) (A any factor with A^T A = H,
+    Satz 1), shifted by the zero points z; target A @ w. The basis is taken
+    in reverse sweep order and processed from its last vector to its first
+    (textbook Babai on the QR factor), which is GPTQ's front-to-back order
+    (Satz 4). Returns integer codes in sweep order.
+    """
+    A = np.asarray(A, dtype=F64)
+    c = A.shape[1]
+    B = (A * s[None, :])[:, ::-1]
+    y = A @ (w + s * z)
+    Q, R = np.linalg.qr(B)
+    yt = Q.T @ y
+    cr = np.zeros(c)
+    for k in range(c - 1, -1, -1):
+        t = (yt[k] - R[k, k + 1:] @ cr[k + 1:]) / R[k, k]
+        v = np.rint(t)
+        if clip:
+            v = min(max(v, 0.0), float(maxq))
+        cr[k] = v
+    return cr[::-1].astype(np.int64)
+
+
+def brute_force_cvp(H, w, s, z, maxq):
+    """Exact minimiser of (w-q) H (w-q)^T over all codes in [0,maxq]^d
+    (the closest-vector problem of [BABAI] 2.1), by enumeration; d small."""
+    d = len(w)
+    grid = np.array(list(itertools.product(range(maxq + 1), repeat=d)), dtype=F64)
+    Dm = w[None, :] - s[None, :] * (grid - z[None, :])
+    losses = np.einsum("ij,jk,ik->i", Dm, H, Dm)
+    k = int(np.argmin(losses))
+    return grid[k].astype(np.int64), float(losses[k])
+
+
+def ldl_diag(M):
+    """Diagonal D of the LDL^T factorisation M = L D L^T (L unit lower),
+    plain Doolittle recursion without pivoting."""
+    M = np.asarray(M, dtype=F64)
+    n = M.shape[0]
+    L = np.eye(n)
+    D = np.zeros(n)
+    for j in range(n):
+        D[j] = M[j, j] - np.sum(L[j, :j] ** 2 * D[:j])
+        if D[j] <= 0:
+            raise NotSPD("non-positive pivot in LDL")
+        for i in range(j + 1, n):
+            L[i, j] = (M[i, j] - np.sum(L[i, :j] * L[j, :j] * D[:j])) / D[j]
+    return D
+
+
+def noclip_bound(s_cols, U):
+    """Satz 5 ([BABAI] 2.3): without clipping |w~_j - q_j| <= s_j/2, so a
+    row's loss is at most (1/4) sum_j s_j^2 D_j, where D_j = 1/U[j,j]^2 is
+    the LDL pivot of the Hessian taken in reverse sweep order."""
+    d = np.diag(np.asarray(U, dtype=F64))
+    return 0.25 * np.sum(np.asarray(s_cols, dtype=F64) ** 2 / d ** 2, axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Bit accounting  ([CHMC] Schritt 3)
+# --------------------------------------------------------------------------
+
+def bpw_page(o, i, bits, group_size):
+    """The page's GPTQ formula: [b*o*i + 16*o*ceil(i/gs)] / (o*i)."""
+    return (bits * o * i + 16 * o * num_groups(i, group_size)) / (o * i)
+
+
+def bpw_gptq(o, i, bits, group_size):
+    """Bits per weight of this library's output: b-bit codes plus an fp16
+    scale and an fp16 zero point per (row, group)."""
+    return (bits * o * i + 32 * o * num_groups(i, group_size)) / (o * i)

@@ -1,0 +1,328 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the passage (page title + section) it follows. None of them
+retypes the oracle's formula: they use hand-worked values, exact arithmetic,
+special cases that reduce to another routine, an independent algorithm
+(Babai on a QR factor, exhaustive CVP, LDL without inversion) or an
+invariant. A plausible slip in the oracle (dropped damping, wrong sign or
+index in the propagation, transposed factor, inverse-row instead of
+Cholesky-row, off-by-one group boundary, reversed act-order) fails at least
+one of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from post_weight_quantization_hessian_amd import synth
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+
+
+def _rand_problem(rows, cols, n, seed, *, act_order=False, damp=0.01):
+    rng = np.random.default_rng(seed)
+    X = (rng.standard_normal((n, cols)) + 0.7 * rng.standard_normal((n, 1))).astype(np.float32)
+    W = (0.02 * rng.standard_t(4, size=(rows, cols))).astype(np.float16)
+    S, nt = O.hessian_sum(X)
+    return X, W, S, nt
+
+
+# ---------------------------------------------------------------- Hessian
+
+def test_hessian_exact_rational():
+    """S = X^T X: compare with exact rational sums ([CHMC] Schritt 2)."""
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((37, 5)).astype(np.float32)
+    S, n = O.hessian_sum([X[:20], X[20:]])
+    assert n == 37
+    for f in range(5):
+        for g in range(5):
+            exact = sum(Fraction(float(X[t, f])) * Fraction(float(X[t, g])) for t in range(37))
+            assert abs(S[f, g] - float(exact)) <= 4 * np.spacing(abs(float(exact)))
+            assert O.hessian_entry(X, f, g) == float(exact)
+
+
+def test_hessian_chunking_and_symmetry():
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((300, 17)).astype(np.float32)
+    S1, _ = O.hessian_sum(X)
+    S2, _ = O.hessian_sum([X[:7], X[7:150], X[150:]])
+    np.testing.assert_allclose(S1, S2, rtol=1e-13, atol=1e-11)
+    assert np.array_equal(S1, S1.T)
+    assert np.all(np.linalg.eigvalsh(S1) > -1e-9)
+
+
+def test_damping_hand_example():
+    g = GOLD["damping"]
+    H = O.damped_hessian(np.array(g["S"]), g["n_tokens"], g["damp"])
+    assert np.array_equal(H, np.array(g["H"]))
+
+
+def test_act_order_hand_example():
+    g = GOLD["act_order"]
+    H = np.diag(g["diag"])
+    assert O.act_order_perm(H).tolist() == g["perm"]
+
+
+# ---------------------------------------------------------------- factor U
+
+def test_hinv_upper_hand_2x2():
+    g = GOLD["propagation_2x2"]
+    U = O.hinv_upper(np.array(g["H"]))
+    np.testing.assert_allclose(U, np.array(g["U"]), rtol=1e-14, atol=1e-15)
+
+
+def test_hinv_upper_properties_and_ldl():
+    """U upper, positive diagonal, U^T U = H^-1; and 1/U_jj^2 equals the LDL
+    pivots of H taken in reverse order ([BABAI] 2.3, Satz 5's D) computed by a
+    plain LDL recursion without any inverse."""
+    X, W, S, n = _rand_problem(4, 24, 200, 3)
+    H = O.damped_hessian(S, n, 0.01)
+    U = O.hinv_upper(H)
+    assert np.allclose(np.tril(U, -1), 0)
+    assert np.all(np.diag(U) > 0)
+    np.testing.assert_allclose(U.T @ U @ H, np.eye(24), atol=1e-9)
+    D_rev = O.ldl_diag(H[::-1, ::-1])[::-1]
+    np.testing.assert_allclose(1.0 / np.diag(U) ** 2, D_rev, rtol=1e-10)
+
+
+def test_not_spd_detected():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((5, 12)).astype(np.float32)  # rank 5 < 12
+    S, n = O.hessian_sum(X)
+    H = O.damped_hessian(S, n, 0.0)
+    H[3, 3] = -1.0
+    with pytest.raises(O.NotSPD):
+        O.hinv_upper(H)
+
+
+# ---------------------------------------------------------------- grid
+
+@pytest.mark.parametrize("key", ["grid_2bit_mixed_sign", "grid_2bit_positive",
+                                 "grid_2bit_tie", "grid_all_zero"])
+def test_grid_hand_examples(key):
+    """A diagonal H leaves only the grid: hand-worked codes of one group."""
+    g = GOLD[key]
+    v = np.array([g["values"]], dtype=np.float64)
+    U = np.eye(v.shape[1])
+    res = O.gptq_sweep(v, U, g["bits"], v.shape[1])
+    assert res["scales"][0, 0] == g["scale"]
+    assert res["zeros"][0, 0] == g["zero"]
+    assert res["codes"][0].tolist() == g["codes"]
+
+
+def test_groups_partial_tail_and_boundaries():
+    """576 = 4*128 + 64: five groups, the last of 64 columns, each with its own
+    grid; H = I so every group is plain round-to-nearest of its own values."""
+    rng = np.random.default_rng(5)
+    W = (0.02 * rng.standard_t(4, size=(3, 576)))
+    W[:, 512:] *= 7.0  # a different range in the tail group
+    res = O.gptq_sweep(W, np.eye(576), 4, 128)
+    assert res["scales"].shape == (3, 5)
+    for g in range(5):
+        sl = slice(128 * g, min(128 * (g + 1), 576))
+        mx = np.maximum(W[:, sl].max(1), 0)
+        mn = np.minimum(W[:, sl].min(1), 0)
+        # scale within half an fp16 ulp of (max-min)/15
+        np.testing.assert_allclose(res["scales"][:, g], (mx - mn) / 15, rtol=2 ** -11)
+
+
+# ---------------------------------------------------------------- sweep
+
+def test_propagation_hand_2x2():
+    """Hand-worked propagation: the error of column 0 lifts column 1 from 0.4
+    to 0.6, which rounds to 1 (RTN would give 0); loss 0.56."""
+    g = GOLD["propagation_2x2"]
+    H = np.array(g["H"])
+    U = O.hinv_upper(H)
+    grid = (np.array([[g["scale"]]]), np.array([[g["zero"]]]))
+    res = O.gptq_sweep(np.array([g["w"]]), U, g["bits"], 2, static_grid=grid)
+    assert res["codes"][0].tolist() == g["codes"]
+    assert abs(res["row_loss"][0] - g["loss"]) < 1e-12
+    codes, best = O.brute_force_cvp(H, np.array(g["w"]), np.ones(2), np.zeros(2), 3)
+    assert abs(best - g["optimum_loss"]) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_diagonal_hessian_reduces_to_rtn(seed):
+    """With a diagonal H, U is diagonal and nothing propagates: GPTQ is
+    round-to-nearest on each group's own grid, bit for bit."""
+    rng = np.random.default_rng(seed)
+    W = (0.02 * rng.standard_t(4, size=(16, 200))).astype(np.float16)
+    d = rng.uniform(0.5, 2.0, 200)
+    S = np.diag(d) * 100
+    res = O.gptq_layer(W, S, 100, bits=3, group_size=64, damp=0.01)
+    codes, scales, zeros = O.rtn_quantize(W.astype(np.float64), 3, 64)
+    assert np.array_equal(res["codes"], codes)
+    assert np.array_equal(res["scales"], scales)
+    assert np.array_equal(res["zeros"], zeros)
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_loss_identity_from_activations(act_order):
+    """sum_j e_j^2 = (w-q) H (w-q)^T, and that equals
+    (2/n)||X (w-q)^T||^2 + lambda ||w-q||^2 computed from X directly."""
+    X, W, S, n = _rand_problem(9, 70, 150, 6)
+    res = O.gptq_layer(W, S, n, bits=4, group_size=32, damp=0.01, act_order=act_order)
+    perm = res["perm"]
+    D = W.astype(np.float64)[:, perm] - res["deq"]
+    via_H = O.loss_quadratic(D, res["Hp"])
+    lam = 0.01 * np.mean(np.diag((2.0 / n) * S))
+    Xp = X.astype(np.float64)[:, perm]
+    via_X = (2.0 / n) * np.sum((Xp @ D.T) ** 2, axis=0) + lam * np.sum(D ** 2, axis=1)
+    np.testing.assert_allclose(res["row_loss"], via_H, rtol=1e-10)
+    np.testing.assert_allclose(res["row_loss"], via_X, rtol=1e-9)
+
+
+@pytest.mark.parametrize("clip", [True, False])
+def test_babai_equivalence(clip):
+    """[BABAI] Satz 4 with Satz 1: on the grid GPTQ chose, Babai's nearest
+    plane on a QR factor of the stacked activation factor A = [sqrt(2/n) X_p;
+    sqrt(lambda) I] (basis in reverse sweep order) returns the same codes."""
+    X, W, S, n = _rand_problem(6, 40, 120, 7)
+    res = O.gptq_layer(W, S, n, bits=3, group_size=8, damp=0.01, act_order=True,
+                       clip=clip)
+    perm = res["perm"]
+    lam = 0.01 * np.mean(np.diag((2.0 / n) * S))
+    A = np.vstack([np.sqrt(2.0 / n) * X.astype(np.float64)[:, perm],
+                   np.sqrt(lam) * np.eye(40)])
+    g = np.arange(40) // 8
+    Wp = W.astype(np.float64)[:, perm]
+    for r in range(6):
+        c = O.babai_nearest_plane(A, Wp[r], res["scales"][r, g], res["zeros"][r, g], 7, clip=clip)
+        assert np.array_equal(c, res["codes_sweep"][r])
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 6, 8])
+def test_brute_force_cvp_bounds_gptq(d):
+    """GPTQ is a heuristic for the CVP ([BABAI] 2.1-2.2): its loss is never
+    below the exact optimum over all 2-bit codes, and equals it for d = 1."""
+    rng = np.random.default_rng(100 + d)
+    X = (rng.standard_normal((50, d)) + rng.standard_normal((50, 1))).astype(np.float32)
+    S, n = O.hessian_sum(X)
+    H = O.damped_hessian(S, n, 0.01)
+    U = O.hinv_upper(H)
+    ratios = []
+    for r in range(20):
+        w = 0.02 * rng.standard_t(4, size=d)
+        s = np.full(d, 0.01)
+        z = np.full(d, 2.0)
+        res = O.gptq_sweep(w[None], U, 2, d, static_grid=(s[None, :1], z[None, :1]))
+        _, best = O.brute_force_cvp(H, w, s, z, 3)
+        assert res["row_loss"][0] >= best * (1 - 1e-12) - 1e-18
+        if d == 1:
+            assert abs(res["row_loss"][0] - best) <= 1e-12 * max(best, 1e-30)
+        ratios.append(res["row_loss"][0] / max(best, 1e-30))
+    assert np.mean(ratios) < 3.0
+
+
+def test_noclip_bound_satz5():
+    """[BABAI] Satz 5: without clipping each row's loss is at most
+    (1/4) sum_j s_j^2 D_j with D the reverse-order LDL pivots."""
+    X, W, S, n = _rand_problem(12, 48, 200, 8)
+    res = O.gptq_layer(W, S, n, bits=2, group_size=16, damp=0.01, act_order=True, clip=False)
+    g = np.arange(48) // 16
+    D = O.ldl_diag(res["Hp"][::-1, ::-1])[::-1]
+    bound = 0.25 * np.sum(res["scales"][:, g] ** 2 * D[None, :], axis=1)
+    assert np.all(res["row_loss"] <= bound * (1 + 1e-12))
+    np.testing.assert_allclose(bound, O.noclip_bound(res["scales"][:, g], res["U"]), rtol=1e-9)
+
+
+def test_high_rate_uniform_noise_soft_check():
+    """[HIGHRATE]: rounding error behaves like independent uniform noise, so
+    the mean loss is close to sum_j s_j^2 D_j / 12 (statistical, 4-bit)."""
+    X, W, S, n = _rand_problem(400, 64, 400, 9)
+    res = O.gptq_layer(W, S, n, bits=4, group_size=64, damp=0.01, clip=False)
+    pred = O.noclip_bound(res["scales"], res["U"]) / 3.0
+    ratio = np.mean(res["row_loss"]) / np.mean(pred)
+    assert 0.8 < ratio < 1.2, ratio
+
+
+def test_hessian_scale_invariance():
+    """Codes do not depend on a positive factor of H (the update uses
+    U[j,k]/U[j,j]); with a power of two the sweep is bit-identical."""
+    X, W, S, n = _rand_problem(10, 96, 128, 10)
+    a = O.gptq_layer(W, S, n, bits=4, group_size=32, act_order=True)
+    b = O.gptq_layer(W, 4.0 * S, n, bits=4, group_size=32, act_order=True)
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["scales"], b["scales"])
+    np.testing.assert_allclose(b["row_loss"], 4.0 * a["row_loss"], rtol=1e-12)
+
+
+@pytest.mark.parametrize("block,gs", [(128, 128), (32, 64), (64, 16)])
+def test_lazy_blocks_equal_strict(block, gs):
+    """Lazy block updates are the same sums as the strict sweep."""
+    X, W, S, n = _rand_problem(40, 300, 400, 11)
+    a = O.gptq_layer(W, S, n, bits=4, group_size=gs, act_order=True)
+    b = O.gptq_layer(W, S, n, bits=4, group_size=gs, act_order=True, block=block)
+    assert np.mean(a["codes"] == b["codes"]) > 0.999
+    np.testing.assert_allclose(a["row_loss"].sum(), b["row_loss"].sum(), rtol=1e-6)
+
+
+def test_rows_independent_concat_and_permute():
+    """Rows are independent given H: stacking layers or permuting rows
+    permutes the outputs and changes nothing else."""
+    X, W, S, n = _rand_problem(20, 64, 100, 12)
+    full = O.gptq_layer(W, S, n, bits=3, group_size=32, act_order=True)
+    top = O.gptq_layer(W[:7], S, n, bits=3, group_size=32, act_order=True)
+    assert np.array_equal(full["codes"][:7], top["codes"])
+    rp = np.random.default_rng(0).permutation(20)
+    pr = O.gptq_layer(W[rp], S, n, bits=3, group_size=32, act_order=True)
+    assert np.array_equal(pr["codes"], full["codes"][rp])
+
+
+def test_act_order_group_index():
+    X, W, S, n = _rand_problem(4, 50, 80, 13)
+    res = O.gptq_layer(W, S, n, bits=4, group_size=16, act_order=True)
+    perm = res["perm"]
+    assert sorted(perm.tolist()) == list(range(50))
+    assert np.all(np.diff(np.diag(res["Hp"])) <= 0)
+    for k in range(50):
+        assert res["g_idx"][perm[k]] == k // 16
+    assert np.array_equal(res["codes"][:, perm], res["codes_sweep"])
+
+
+def test_nonfinite_inputs_rejected():
+    X, W, S, n = _rand_problem(3, 16, 40, 14)
+    Wb = W.copy()
+    Wb[1, 3] = np.float16(np.nan)
+    with pytest.raises(O.NonFinite):
+        O.gptq_layer(Wb, S, n, bits=4, group_size=16)
+    Xb = X.copy()
+    Xb[0, 0] = np.inf
+    with pytest.raises(O.NonFinite):
+        O.hessian_sum(Xb)
+
+
+def test_bpw_page_formula():
+    g = GOLD["bpw_page_576"]
+    assert abs(O.bpw_page(g["o"], g["i"], g["bits"], g["gs"]) - g["bpw"]) < 1e-12
+    assert abs(O.bpw_gptq(576, 576, 4, 128) - (4 + 32 * 5 / 576)) < 1e-12
+
+
+# ---------------------------------------------------------------- inputs
+
+def test_cone_generator_cosine_target():
+    """The synthetic activations reproduce the measured cone statistic: mean
+    pairwise cosine about 0.75 on a 512-token subsample (CHMC article, Teil 1
+    and Tabelle 2)."""
+    X = synth.activations(0, "x", 2048, 576)
+    c = synth.mean_pairwise_cosine(X)
+    assert 0.72 < c < 0.78, c
+    assert abs(np.mean(X.astype(np.float64) ** 2) - 1.0) < 0.05
+
+
+def test_generator_deterministic_and_chunk_independent():
+    a = synth.activations(3, "t", 20000, 64, chunk=8192)
+    b = synth.activations(3, "t", 20000, 64, chunk=8192, threads=1)
+    assert np.array_equal(a, b)
+    spec = synth.ConeSpec(3, "t", 64)
+    assert np.array_equal(a[8192:16384], spec.chunk(1, 8192))
+    w1 = synth.weights(1, "w", 10, 50)
+    w2 = synth.weights(1, "w", 10, 50)
+    assert w1.dtype == np.float16 and np.array_equal(w1, w2)
+    sd = w1.astype(np.float64).std(axis=1)
+    np.testing.assert_allclose(sd, 0.02, rtol=0.01)
