@@ -1,0 +1,159 @@
+/*
+ * gptq.h — C ABI of the GPTQ layer quantizer for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   - "Warum Geometrie Gewichte nicht komprimiert" (CHMC article, nonndazone.ru),
+ *     Methodik, Schritt 2: the layer Hessian is built from the calibration
+ *     activations X of the layer, damped by lambda*mean(diag H)*I, inverted via
+ *     the Cholesky decomposition; columns are visited in act-order (descending
+ *     diag H); each column is rounded to its group's grid and its error,
+ *     divided by the factor's diagonal entry, is subtracted from the later
+ *     columns through the factor's row. Schritt 3 / Tabelle 1: GPTQ stores
+ *     integer codes plus per-group scales, groups along input channels.
+ *   - "The Geometry of LLM Quantization: GPTQ as Babai's Nearest Plane
+ *     Algorithm" (gist.science), 2.1-2.3: the sweep is Babai's nearest-plane
+ *     algorithm on the lattice of the Hessian; act-order is the pivot order.
+ *
+ * Conventions used by every entry point:
+ *   - All array arguments are DEVICE pointers (HIP global memory) owned by the
+ *     caller; the library allocates no device memory. Scratch space comes from
+ *     a caller workspace whose size the *_workspace_bytes() calls return.
+ *   - Matrices are row-major with an explicit leading dimension (elements).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *     is enqueued on it in order; see each call for where it synchronizes.
+ *   - Arguments are validated on the host first; an invalid call returns
+ *     GPTQ_EINVAL / GPTQ_EWORKSPACE before anything is enqueued.
+ *   - Fp16 values (weights, scales, zero points) travel as uint16_t bit
+ *     patterns (IEEE binary16).
+ *   - No exception crosses the ABI. Calls on different streams with disjoint
+ *     buffers are independent; the optional profiler (gptq_profile_*) is a
+ *     process-wide switch and is not thread-safe.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = 1,      /* null pointer, negative size, bits/group size out of range   */
+  GPTQ_ENOTSPD = 2,     /* damped Hessian not positive definite (pivot <= 0 or NaN)    */
+  GPTQ_EHIP = 3,        /* a HIP runtime call or kernel launch failed                   */
+  GPTQ_EWORKSPACE = 4,  /* workspace pointer null or smaller than required              */
+  GPTQ_ENONFINITE = 5   /* NaN/Inf weight, or a group scale beyond the fp16 range       */
+} gptq_status;
+
+/* flags */
+#define GPTQ_FLAG_ACT_ORDER 1u  /* gptq_prepare_hinv: visit columns by descending diag H */
+
+/* ---------------------------------------------------------------------------
+ * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's
+ * calibration activations). Accumulates the unnormalised sum
+ *     S[i x i] += X^T X,   X = n_tokens x in_features fp32, row stride ldx.
+ * S is fp64 and symmetric: both triangles are updated. The products of two
+ * fp32 values are formed exactly (fp64), only the sums round. Call it once per
+ * token chunk on a zero-initialised S and keep the running token count; the
+ * normalisation (2/n) is applied by gptq_prepare_hinv.
+ * ws may be NULL (ws_bytes 0): the call is then done without token splitting.
+ * With ws of gptq_hessian_workspace_bytes(in_features, n_tokens) bytes the
+ * token range is split across more workgroups and reduced in a fixed order
+ * (results are bitwise reproducible either way for a given ws choice).
+ * n_tokens == 0 or in_features == 0 is a no-op. Asynchronous on `stream`.
+ * ------------------------------------------------------------------------- */
+size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_tokens);
+gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
+                                    const float* X, int64_t n_tokens, int64_t ldx,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps 2-3 — damping, act-order, factor of the inverse.  CHMC article,
+ * Schritt 2 (H = X^T X/n + lambda*mean(diag H)*I, H^-1 via Cholesky,
+ * act-order); The Geometry of LLM Quantization 2.3 (act-order pivoting).
+ *   H  = (2/n_tokens_total) * S + damp * mean(diag((2/n) S)) * I
+ *   perm (out, int32[i]) = stable order of descending diag H when
+ *        flags & GPTQ_FLAG_ACT_ORDER, else the identity;
+ *        perm[k] = original column visited k-th.
+ *   U  (out, fp32 [i x i], row-major, ld = in_features) = the upper triangular
+ *        factor with U^T U = (H[perm][:,perm])^-1, zeros below the diagonal.
+ * Computed in fp64 (one Cholesky of the order-reversed permuted Hessian and
+ * one triangular inverse), stored as fp32. S is read, never written.
+ * Workspace: gptq_prepare_workspace_bytes(in_features) bytes.
+ * Synchronizes `stream` once at the end to read the factorisation status;
+ * returns GPTQ_ENOTSPD if a pivot is <= 0 or not finite (U is then garbage).
+ * ------------------------------------------------------------------------- */
+size_t gptq_prepare_workspace_bytes(int64_t in_features);
+gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_tokens_total,
+                              double damp, uint32_t flags, int32_t* perm, float* U,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps 4-6 — the column sweep.  CHMC article, Schritt 2 (per column:
+ * round to the group grid, err = (col - q)/U[j,j], later columns -= err *
+ * U[j, j+1:]); the lazy form applies the update of a 128-column block to the
+ * columns after it only when they are reached (same sums, other order).
+ *   W     fp16 [rows x cols], leading dimension ldw (>= cols), original order.
+ *   U     fp32 [cols x cols] from gptq_prepare_hinv (sweep order).
+ *   perm  int32[cols] from gptq_prepare_hinv, or NULL for the identity.
+ *   bits  2..8; group_size one of 16, 32, 64, 128 (groups = group_size
+ *         consecutive columns in sweep order; the last may be shorter).
+ * Grid of a group (asymmetric min-max), taken when the sweep reaches the
+ * group's first column from the current, error-updated values v:
+ *   scale = fp16_rne((max(0,max v) - min(0,min v)) / (2^bits - 1)),
+ *   zero  = clamp(rint(-min(0,min v)/scale), 0, 2^bits - 1);
+ *   scale 1 / zero 0 when max == min or the scale rounds to 0.
+ *   code  = clamp(rint(v/scale) + zero, 0, 2^bits - 1)   (round half even).
+ * Outputs:
+ *   codes    uint8 [rows x cols], ld = cols, ORIGINAL column order.
+ *   scales   fp16 [rows x ceil(cols/group_size)], ld = ceil(cols/gs), group g
+ *            covers sweep positions [g*gs, (g+1)*gs).
+ *   zeros    fp16, same layout (integer values).
+ *   g_idx    int32[cols] or NULL: g_idx[perm[k]] = k / group_size.
+ *   row_loss fp64[rows]: sum_j e_j^2, e_j = (v_j - dequant_j)/U[j,j]; equals
+ *            (w-q) H (w-q)^T for the damped, permuted H.
+ * Workspace: gptq_quantize_workspace_bytes(rows, cols, group_size) bytes.
+ * Synchronizes `stream` at the end; returns GPTQ_ENONFINITE if a weight is
+ * NaN/Inf or a scale overflows fp16 (outputs are then unspecified).
+ * rows == 0 or cols == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int group_size);
+gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                const float* U, const int32_t* perm, int bits, int group_size,
+                                uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                int32_t* g_idx, double* row_loss,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Utilities.
+ * gptq_status_string: static, never NULL.
+ * gptq_fp16_round_host: HOST function (host pointers); rounds each double to
+ *   the nearest-even binary16 with the same routine the kernels use for group
+ *   scales (no double rounding through fp32). Returns GPTQ_EINVAL on NULL.
+ * gptq_version: ABI version number (currently 1).
+ * ------------------------------------------------------------------------- */
+const char* gptq_status_string(gptq_status status);
+gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int64_t n);
+int gptq_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Optional kernel timing (process-wide, not thread-safe). While enabled, every
+ * kernel launch of the library is bracketed by HIP events on its stream.
+ * gptq_profile_read synchronizes on the recorded events, adds their durations
+ * per kernel class and clears the record.
+ *   kernel ids: 0 .. gptq_profile_kernel_count()-1; names via
+ *   gptq_profile_kernel_name(id) (static string, NULL for a bad id).
+ *   totals_ms / launches: host arrays of gptq_profile_kernel_count() entries.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_profile_enable(int on);
+int gptq_profile_kernel_count(void);
+const char* gptq_profile_kernel_name(int id);
+gptq_status gptq_profile_read(double* totals_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_H */

@@ -1,0 +1,106 @@
+// Status strings, the fp16 rounding utility and the optional HIP-event
+// kernel profiler of the GPTQ library.
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace gptq {
+
+static const char* const kKernelNames[K_COUNT] = {
+    "hessian_tile", "hessian_reduce", "prepare_diag", "prepare_perm", "prepare_gather",
+    "chol_potrf", "chol_trsm", "chol_syrk", "trtri_row", "trtri_update", "prepare_uout",
+    "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill"};
+
+struct ProfRec {
+  int kid;
+  hipEvent_t a, b;
+};
+
+static bool g_prof_on = false;
+static std::vector<ProfRec> g_prof;
+static std::vector<hipEvent_t> g_open;  // per-launch start events pending an end
+
+void prof_begin(int kid, hipStream_t s) {
+  if (!g_prof_on) return;
+  hipEvent_t a;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventRecord(a, s) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
+  g_open.push_back(a);
+  (void)kid;
+}
+
+void prof_end(int kid, hipStream_t s) {
+  if (!g_prof_on || g_open.empty()) return;
+  hipEvent_t a = g_open.back();
+  g_open.pop_back();
+  hipEvent_t b;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
+  (void)hipEventRecord(b, s);
+  g_prof.push_back({kid, a, b});
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" const char* gptq_status_string(gptq_status status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_EINVAL: return "invalid argument";
+    case GPTQ_ENOTSPD: return "damped Hessian is not positive definite";
+    case GPTQ_EHIP: return "HIP runtime error";
+    case GPTQ_EWORKSPACE: return "workspace missing or too small";
+    case GPTQ_ENONFINITE: return "non-finite weight or fp16 scale overflow";
+  }
+  return "unknown status";
+}
+
+extern "C" gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int64_t n) {
+  if (n < 0 || (n > 0 && (!in || !out))) return GPTQ_EINVAL;
+  for (int64_t i = 0; i < n; ++i) out[i] = f64_to_f16_rne(in[i]);
+  return GPTQ_OK;
+}
+
+extern "C" int gptq_version(void) { return 1; }
+
+extern "C" gptq_status gptq_profile_enable(int on) {
+  g_prof_on = on != 0;
+  return GPTQ_OK;
+}
+
+extern "C" int gptq_profile_kernel_count(void) { return K_COUNT; }
+
+extern "C" const char* gptq_profile_kernel_name(int id) {
+  if (id < 0 || id >= K_COUNT) return nullptr;
+  return kKernelNames[id];
+}
+
+extern "C" gptq_status gptq_profile_read(double* totals_ms, int64_t* launches) {
+  if (!totals_ms || !launches) return GPTQ_EINVAL;
+  for (int k = 0; k < K_COUNT; ++k) {
+    totals_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  gptq_status st = GPTQ_OK;
+  for (auto& r : g_prof) {
+    if (hipEventSynchronize(r.b) != hipSuccess) st = GPTQ_EHIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      totals_ms[r.kid] += ms;
+      launches[r.kid] += 1;
+    } else {
+      st = GPTQ_EHIP;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof.clear();
+  return st;
+}

@@ -1,0 +1,106 @@
+// Shared device/host helpers of the gfx950 GPTQ library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "gptq.h"
+
+namespace gptq {
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16 __attribute__((ext_vector_type(16)));
+
+// Device status word bits (first word of every workspace).
+enum : unsigned { ST_NOTSPD = 1u, ST_NONFINITE = 2u, ST_BADPERM = 4u };
+
+// Kernel classes for the optional HIP-event profiler.
+enum KernelId {
+  K_HESS_TILE = 0, K_HESS_REDUCE, K_PREP_DIAG, K_PREP_PERM, K_PREP_GATHER, K_CHOL_POTRF,
+  K_CHOL_TRSM, K_CHOL_SYRK, K_TRTRI_ROW, K_TRTRI_UPDATE, K_PREP_UOUT, K_Q_INIT, K_Q_PERMUTE,
+  K_Q_GEMM, K_Q_SWEEP, K_Q_FINALIZE, K_FILL, K_COUNT
+};
+
+// Launch bracketing for the profiler (defined in api.hip).
+void prof_begin(int kid, hipStream_t s);
+void prof_end(int kid, hipStream_t s);
+
+struct ProfScope {
+  int kid;
+  hipStream_t s;
+  ProfScope(int k, hipStream_t st) : kid(k), s(st) { prof_begin(kid, s); }
+  ~ProfScope() { prof_end(kid, s); }
+};
+
+#define GPTQ_LAUNCH(kid, stream, ...)                          \
+  do {                                                         \
+    ::gptq::ProfScope _ps((kid), (stream));                    \
+    __VA_ARGS__;                                               \
+    if (hipGetLastError() != hipSuccess) return GPTQ_EHIP;     \
+  } while (0)
+
+// ---------------------------------------------------------------- fp16 bits
+
+// Nearest-even binary16 of a double, computed from the double's bits directly
+// (no intermediate fp32 rounding). Handles subnormals, overflow to Inf, NaN.
+__host__ __device__ inline uint16_t f64_to_f16_rne(double x) {
+  union { double d; uint64_t u; } c;
+  c.d = x;
+  const uint64_t b = c.u;
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const int e = (int)((b >> 52) & 0x7ff);
+  const uint64_t m = b & ((1ull << 52) - 1);
+  if (e == 0x7ff) return sign | 0x7c00u | (m ? 0x200u : 0u);
+  if (e == 0) return sign;  // fp64 subnormal: far below the fp16 range
+  int E = e - 1023;
+  const uint64_t mant = (1ull << 52) | m;  // 53 significant bits
+  int shift = (E >= -14) ? 42 : 42 + (-14 - E);
+  if (shift > 60) return sign;
+  uint64_t q = mant >> shift;
+  const uint64_t rem = mant & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (E >= -14) {
+    if (q == 2048) { q = 1024; ++E; }
+    if (E > 15) return sign | 0x7c00u;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q & 0x3ff);
+  }
+  return sign | (uint16_t)q;  // subnormal; q == 1024 is the smallest normal
+}
+
+__host__ __device__ inline double f16_to_f64(uint16_t h) {
+  const int s = (h >> 15) & 1;
+  const int e = (h >> 10) & 0x1f;
+  const int m = h & 0x3ff;
+  double v;
+  if (e == 0) v = (double)m * (1.0 / 16777216.0);  // m * 2^-24
+  else if (e == 31) v = m ? __builtin_nan("") : __builtin_inf();
+  else v = (double)(1024 + m) * __builtin_ldexp(1.0, e - 25);
+  return s ? -v : v;
+}
+
+// ---------------------------------------------------------------- misc
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+// Workgroup id remapped so that consecutive logical ids land on the same XCD
+// (hardware dispatches workgroup ids round-robin over the 8 XCDs).
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  const int nx = 8;
+  if (nblocks < nx) return bid;
+  const int per = nblocks / nx;
+  const int rem = nblocks - per * nx;
+  const int x = bid % nx;
+  const int k = bid / nx;
+  // XCD x owns logical ids [start(x), start(x) + count(x)) where the first
+  // `rem` XCDs get one extra id.
+  if (k >= per + (x < rem ? 1 : 0)) return bid;  // not reached for exact grids
+  const int start = x * per + (x < rem ? x : rem);
+  return start + k;
+}
+
+}  // namespace gptq

@@ -1,0 +1,124 @@
+// fp64 MFMA tile machinery for gfx950: a 128x128 output tile per 256-thread
+// workgroup (4 waves, each a 64x64 quadrant of 4x4 v_mfma_f64_16x16x4 tiles),
+// K staged through LDS in chunks of 16, double buffered.
+//
+// v_mfma_f64_16x16x4f64 operand layout (lane l of 64):
+//   A[m][k]: m = l % 16, k = l / 16        B[k][n]: n = l % 16, k = l / 16
+//   D[m][n] (4 doubles per lane): n = l % 16, m = l / 16 + 4 * r, r = 0..3
+#pragma once
+#include "common.h"
+
+namespace gptq {
+
+constexpr int GT = 128;          // tile edge
+constexpr int GK = 16;           // K chunk
+constexpr int GLD = GT + 8;      // LDS row pitch (doubles), k-major rows
+constexpr int GCH = GK * GLD;    // doubles per staged operand chunk
+
+typedef double dbl2 __attribute__((ext_vector_type(2)));
+
+// Wave quadrant MFMA over one staged chunk. As/Bs are k-major: As[k*GLD + m].
+__device__ inline void mfma64_chunk(const double* __restrict__ As, const double* __restrict__ Bs,
+                                    d4 (&acc)[4][4], int wm, int wn, int lane) {
+#pragma unroll
+  for (int kk = 0; kk < GK; kk += 4) {
+    const int k = kk + (lane >> 4);
+    double a[4], b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = As[k * GLD + wm * 64 + i * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = Bs[k * GLD + wn * 64 + i * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// Global [k][col] (row stride ld) -> LDS [k][col]. All in bounds, 16B aligned.
+struct LdDirect64 {
+  const double* base;
+  int64_t ld;
+  dbl2 r[4];
+  __device__ void fetch(int c, int t) {
+    const double* p = base + (int64_t)(c * GK + (t >> 4)) * ld + (t & 15) * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const dbl2*>(p + 2 * q);
+  }
+  __device__ void store(double* s, int t) const {
+    double* d = s + (t >> 4) * GLD + (t & 15) * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<dbl2*>(d + 2 * q) = r[q];
+  }
+};
+
+// Global [col][k] (row stride ld) -> LDS [k][col] (transposing). In bounds.
+struct LdTrans64 {
+  const double* base;
+  int64_t ld;
+  dbl2 r[4];
+  __device__ void fetch(int c, int t) {
+    const double* p = base + (int64_t)(t >> 1) * ld + c * GK + (t & 1) * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = *reinterpret_cast<const dbl2*>(p + 2 * q);
+  }
+  __device__ void store(double* s, int t) const {
+    const int col = t >> 1, kh = (t & 1) * 8;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[(kh + 2 * q) * GLD + col] = r[q].x;
+      s[(kh + 2 * q + 1) * GLD + col] = r[q].y;
+    }
+  }
+};
+
+// Double-buffered K loop. If `same` the B operand is the A operand (la only).
+template <class LA, class LB>
+__device__ inline void gemm64_loop(LA& la, LB& lb, bool same, int nchunks, double* sA, double* sB,
+                                   d4 (&acc)[4][4]) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+  la.fetch(0, t);
+  if (!same) lb.fetch(0, t);
+  la.store(sA, t);
+  if (!same) lb.store(sB, t);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+    const int cur = c & 1;
+    const bool more = c + 1 < nchunks;
+    if (more) {
+      la.fetch(c + 1, t);
+      if (!same) lb.fetch(c + 1, t);
+    }
+    const double* a = sA + cur * GCH;
+    const double* b = same ? a : sB + cur * GCH;
+    mfma64_chunk(a, b, acc, wm, wn, lane);
+    if (more) {
+      la.store(sA + (cur ^ 1) * GCH, t);
+      if (!same) lb.store(sB + (cur ^ 1) * GCH, t);
+    }
+    __syncthreads();
+  }
+}
+
+__device__ inline void zero_acc(d4 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
+}
+
+// Visit the tile's accumulators: f(row, col, value) with tile-local row/col.
+template <class F>
+__device__ inline void for_each_acc(const d4 (&acc)[4][4], F f) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f(wm * 64 + i * 16 + (lane >> 4) + 4 * r, wn * 64 + j * 16 + (lane & 15), acc[i][j][r]);
+}
+
+}  // namespace gptq

@@ -1,0 +1,173 @@
+// Step 1: S += X^T X in fp64 (CHMC article, Methodik, Schritt 2: the layer
+// Hessian from the calibration activations).
+//
+// One 128x128 tile of S per workgroup, upper-triangular tiles only (a <= b);
+// an off-diagonal tile is also written to its mirror position. The token axis
+// is the MFMA K axis: fp32 activations are widened to fp64 while staged in
+// LDS, so every product is exact and only the fp64 sums round. When the tile
+// count alone cannot fill the GPU, the token range is split across
+// workgroups that write partial tiles to the workspace; a second kernel adds
+// the partials in a fixed order.
+#include "gemm64.h"
+
+namespace gptq {
+
+// Global X[token][feature] fp32 -> LDS [k][col] fp64, masked at the token and
+// feature ends; vector loads when the rows are 16-byte aligned.
+struct LdX32 {
+  const float* X;
+  int64_t ldx, t_begin, t_end, dim, f0;
+  bool vec;
+  f4 r[2];
+  __device__ void fetch(int c, int t) {
+    const int64_t tok = t_begin + (int64_t)c * GK + (t >> 4);
+    const int64_t f = f0 + (t & 15) * 8;
+    if (tok < t_end && vec && f + 7 < dim) {
+      const float* p = X + tok * ldx + f;
+      r[0] = *reinterpret_cast<const f4*>(p);
+      r[1] = *reinterpret_cast<const f4*>(p + 4);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float v = (tok < t_end && f + q < dim) ? X[tok * ldx + f + q] : 0.0f;
+        r[q >> 2][q & 3] = v;
+      }
+    }
+  }
+  __device__ void store(double* s, int t) const {
+    double* d = s + (t >> 4) * GLD + (t & 15) * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) d[q] = (double)r[q >> 2][q & 3];
+  }
+};
+
+// Upper-triangle tile id -> (a, b), a <= b, row-major over the triangle of an
+// nt x nt tile grid.
+__device__ inline void upper_tile(int id, int nt, int& a, int& b) {
+  // rows have nt, nt-1, ... tiles; walk with a closed-form guess then fix up
+  int row = 0, start = 0;
+  // solve start(row) = row*nt - row*(row-1)/2 <= id
+  double disc = (2.0 * nt + 1.0) * (2.0 * nt + 1.0) - 8.0 * id;
+  row = (int)(((2.0 * nt + 1.0) - sqrt(disc)) * 0.5);
+  if (row < 0) row = 0;
+  if (row > nt - 1) row = nt - 1;
+  while (row > 0 && row * nt - row * (row - 1) / 2 > id) --row;
+  while (row + 1 < nt && (row + 1) * nt - (row + 1) * row / 2 <= id) ++row;
+  start = row * nt - row * (row - 1) / 2;
+  a = row;
+  b = row + (id - start);
+}
+
+__global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict__ X, int64_t ldx,
+                                                        int64_t n_tokens, int64_t dim, int nt,
+                                                        int ntiles, int64_t tok_per_split,
+                                                        double* __restrict__ S, int64_t lds,
+                                                        double* __restrict__ part, bool vec) {
+  __shared__ double sA[2 * GCH];
+  __shared__ double sB[2 * GCH];
+  const int nblocks = gridDim.x;
+  const int lin = xcd_remap(blockIdx.x, nblocks);
+  const int tile = lin % ntiles;
+  const int split = lin / ntiles;
+  int a, b;
+  upper_tile(tile, nt, a, b);
+  const int64_t t0 = (int64_t)split * tok_per_split;
+  int64_t t1 = t0 + tok_per_split;
+  if (t1 > n_tokens) t1 = n_tokens;
+  const int nchunks = t1 > t0 ? (int)cdiv(t1 - t0, GK) : 0;
+
+  d4 acc[4][4];
+  zero_acc(acc);
+  if (nchunks > 0) {
+    LdX32 la{X, ldx, t0, t1, dim, (int64_t)a * GT, vec, {}};
+    LdX32 lb{X, ldx, t0, t1, dim, (int64_t)b * GT, vec, {}};
+    gemm64_loop(la, lb, a == b, nchunks, sA, sB, acc);
+  }
+  if (part) {
+    double* P = part + ((int64_t)split * ntiles + tile) * (GT * GT);
+    for_each_acc(acc, [&](int r, int c, double v) { P[r * GT + c] = v; });
+    return;
+  }
+  const int64_t fa = (int64_t)a * GT, fb = (int64_t)b * GT;
+  for_each_acc(acc, [&](int r, int c, double v) {
+    const int64_t i = fa + r, j = fb + c;
+    if (i < dim && j < dim) {
+      S[i * lds + j] += v;
+      if (a != b) S[j * lds + i] += v;
+    }
+  });
+}
+
+// Sum the token-split partials of every tile in split order and add to S.
+__global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restrict__ part, int nsplit,
+                                                          int nt, int ntiles, int64_t dim,
+                                                          double* __restrict__ S, int64_t lds) {
+  const int tile = blockIdx.y;
+  int a, b;
+  upper_tile(tile, nt, a, b);
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // element within tile
+  if (e >= GT * GT) return;
+  const int r = e / GT, c = e % GT;
+  const int64_t i = (int64_t)a * GT + r, j = (int64_t)b * GT + c;
+  if (i >= dim || j >= dim) return;
+  double s = 0.0;
+  for (int p = 0; p < nsplit; ++p) s += part[((int64_t)p * ntiles + tile) * (GT * GT) + e];
+  S[i * lds + j] += s;
+  if (a != b) S[j * lds + i] += s;
+}
+
+static void hess_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit, int64_t& tps) {
+  nt = (int)cdiv(dim, GT);
+  ntiles = nt * (nt + 1) / 2;
+  int64_t want = cdiv(1024, ntiles);
+  int64_t cap_tok = n / 256;
+  if (want > cap_tok) want = cap_tok;
+  if (want > 64) want = 64;
+  if (want < 1) want = 1;
+  tps = round_up(cdiv(n, want), GK);
+  nsplit = (int)cdiv(n, tps);
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_tokens) {
+  if (in_features <= 0 || n_tokens <= 0) return 0;
+  int nt, ntiles, nsplit;
+  int64_t tps;
+  hess_plan(in_features, n_tokens, nt, ntiles, nsplit, tps);
+  if (nsplit <= 1) return 0;
+  return (size_t)nsplit * ntiles * GT * GT * sizeof(double);
+}
+
+extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, const float* X,
+                                               int64_t n_tokens, int64_t ldx, void* ws,
+                                               size_t ws_bytes, void* stream) {
+  if (in_features < 0 || n_tokens < 0) return GPTQ_EINVAL;
+  if (in_features == 0 || n_tokens == 0) return GPTQ_OK;
+  if (!S || !X || ldx < in_features) return GPTQ_EINVAL;
+  if (in_features > (int64_t)1 << 20) return GPTQ_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  int nt, ntiles, nsplit;
+  int64_t tps;
+  hess_plan(in_features, n_tokens, nt, ntiles, nsplit, tps);
+  const size_t need = gptq_hessian_workspace_bytes(in_features, n_tokens);
+  if (!ws || ws_bytes < need || need == 0) {  // no (usable) workspace: one split
+    nsplit = 1;
+    tps = round_up(n_tokens, GK);
+  }
+  const bool vec = (ldx % 4 == 0) && ((uintptr_t)X % 16 == 0);
+  double* part = nsplit > 1 ? (double*)ws : nullptr;
+  const int nblocks = ntiles * nsplit;
+  GPTQ_LAUNCH(K_HESS_TILE, st,
+              hess_tile_kernel<<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt, ntiles, tps,
+                                                        S, in_features, part, vec));
+  if (part) {
+    dim3 grid(GT * GT / 256, ntiles);
+    GPTQ_LAUNCH(K_HESS_REDUCE, st,
+                hess_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, nt, ntiles, in_features, S,
+                                                         in_features));
+  }
+  return GPTQ_OK;
+}

@@ -1,0 +1,475 @@
+// Steps 4-6: the column sweep (CHMC article, Methodik, Schritt 2: round each
+// column to its group's grid, err_j = (col_j - q_j)/U[j,j], later columns -=
+// err_j * U[j, j+1:]; The Geometry of LLM Quantization 2.2: this is Babai's
+// nearest-plane step).
+//
+// Lazy blocks of 128 columns, with the update of earlier blocks applied just
+// in time: before block [j0, j0+bw) is swept, its current values are
+//     W~[:, blk] = W[:, blk] - E[:, :j0] * U[:j0, blk]
+// (E = the scaled errors of all earlier columns), the same sums as the
+// right-looking update, formed once per block by an fp32-MFMA GEMM whose
+// K-chunks are accumulated in fp64. Inside the block the sweep runs in fp64
+// registers: 4 lanes per row, lane q of a quad owns columns q, q+4, q+8, ...;
+// the register window shifts by one slot every 4 columns so the live column
+// is always slot 0, and the scaled error of the live column is broadcast to
+// the quad with a DPP quad permute. Group min/max reductions also use DPP.
+#include "common.h"
+
+namespace gptq {
+
+constexpr int QB = 128;  // sweep block width
+
+// ---------------------------------------------------------------- helpers
+
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+  union { double d; int i[2]; } a, b;
+  a.d = v;
+  b.i[0] = __builtin_amdgcn_update_dpp(0, a.i[0], CTRL, 0xF, 0xF, false);
+  b.i[1] = __builtin_amdgcn_update_dpp(0, a.i[1], CTRL, 0xF, 0xF, false);
+  return b.d;
+}
+// quad_perm controls: broadcast lane q of the quad; xor 1; xor 2
+template <int Q>
+__device__ inline double quad_bcast(double v) { return dpp_f64<Q * 0x55>(v); }
+__device__ inline double quad_xor1(double v) { return dpp_f64<0xB1>(v); }
+__device__ inline double quad_xor2(double v) { return dpp_f64<0x4E>(v); }
+
+// ---------------------------------------------------------------- small kernels
+
+// row_loss = 0; invperm = -1 (filled by the permute kernel); g_idx[m] = m / gs
+// when there is no permutation (else written by finalize).
+__global__ void q_init_kernel(double* __restrict__ row_loss, int64_t rows,
+                              const int32_t* __restrict__ perm, int32_t* __restrict__ invperm,
+                              int32_t* __restrict__ g_idx, int64_t cols, int gs,
+                              unsigned* __restrict__ status) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
+  if (tid == 0) *status = 0u;
+  for (int64_t r = tid; r < rows; r += nthr) row_loss[r] = 0.0;
+  for (int64_t k = tid; k < cols; k += nthr) {
+    if (perm) invperm[k] = -1;
+    else if (g_idx) g_idx[k] = (int32_t)(k / gs);
+  }
+}
+
+// Wp[r][k] = W[r][perm[k]] (sweep order, ld cols); invperm[perm[k]] = k.
+// An entry of perm outside [0, cols) is reported (ST_BADPERM) and skipped.
+__global__ __launch_bounds__(256) void q_permute_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                        const int32_t* __restrict__ perm,
+                                                        int64_t rows, int64_t cols,
+                                                        uint16_t* __restrict__ Wp,
+                                                        int32_t* __restrict__ invperm,
+                                                        unsigned* __restrict__ status) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const uint16_t* src = W + r * ldw;
+    uint16_t* dst = Wp + r * cols;
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < cols;
+         k += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t pk = perm[k];
+      if (pk < 0 || pk >= cols) {
+        if (r == 0) atomicOr(status, ST_BADPERM);
+        dst[k] = 0;
+        continue;
+      }
+      dst[k] = src[pk];
+      if (r == 0) invperm[pk] = (int32_t)k;
+    }
+  }
+}
+
+// codes[r][m] = codes_s[r][invperm[m]]; g_idx[m] = invperm[m] / gs. An unset
+// invperm entry (perm was not a permutation) is reported and gives code 0.
+__global__ __launch_bounds__(256) void q_finalize_kernel(const uint8_t* __restrict__ codes_s,
+                                                         const int32_t* __restrict__ invperm,
+                                                         int64_t rows, int64_t cols, int gs,
+                                                         uint8_t* __restrict__ codes,
+                                                         int32_t* __restrict__ g_idx,
+                                                         unsigned* __restrict__ status) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    for (int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; m < cols;
+         m += (int64_t)gridDim.x * blockDim.x) {
+      const int32_t k = invperm[m];
+      if (k < 0 || k >= cols) {
+        if (r == 0) atomicOr(status, ST_BADPERM);
+        codes[r * cols + m] = 0;
+        continue;
+      }
+      codes[r * cols + m] = codes_s[r * cols + k];
+      if (r == 0 && g_idx) g_idx[m] = k / gs;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- update GEMM
+//
+// part[p][r][c] = sum_{l in split p} E[r][l] * U[l][j0 + c], l < j0, c < 128.
+// Workgroup tile: 64 rows x 128 columns; wave w owns columns 32w..32w+31 as
+// two 32x32 v_mfma_f32_32x32x2f32 tiles (rows 0-31, 32-63). Each 32-wide K
+// chunk is summed in fp32 by the MFMA, then added into fp64 accumulators.
+//
+// v_mfma_f32_32x32x2f32 layout (lane l): A[m][k]: m = l%32, k = l/32;
+// B[k][n]: n = l%32, k = l/32; D reg x: row 8*(x/4) + 4*(l/32) + x%4, col l%32.
+constexpr int QE_LD = 34;   // Es row pitch (floats)
+constexpr int QU_LD = 160;  // Us row pitch (floats)
+
+__global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E, int64_t lde,
+                                                     const float* __restrict__ U, int64_t ldu,
+                                                     int64_t rows, int64_t j0, int bw,
+                                                     int64_t ksplit, double* __restrict__ part,
+                                                     int64_t part_stride, bool vecU) {
+  __shared__ float Es[2][64 * QE_LD];
+  __shared__ float Us[2][32 * QU_LD];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int p = blockIdx.y;
+  const int64_t k_lo = (int64_t)p * ksplit;
+  int64_t k_hi = k_lo + ksplit;
+  if (k_hi > j0) k_hi = j0;
+  const int nchunks = k_hi > k_lo ? (int)((k_hi - k_lo) / 32) : 0;
+
+  // E loader: row t>>2, 8 floats at (t&3)*8; U loader: row t>>3, 16 floats at (t&7)*16
+  const int er = t >> 2, ec = (t & 3) * 8;
+  const int ur = t >> 3, uc = (t & 7) * 16;
+  f4 eR[2], uR[4];
+  auto fetch = [&](int c) {
+    const int64_t l0 = k_lo + (int64_t)c * 32;
+    if (r0 + er < rows) {
+      const float* pe = E + (r0 + er) * lde + l0 + ec;
+      eR[0] = *reinterpret_cast<const f4*>(pe);
+      eR[1] = *reinterpret_cast<const f4*>(pe + 4);
+    } else {
+      eR[0] = f4{0, 0, 0, 0};
+      eR[1] = f4{0, 0, 0, 0};
+    }
+    const float* pu = U + (l0 + ur) * ldu + j0 + uc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cc = uc + 4 * q;
+      if (vecU && cc + 3 < bw) {
+        uR[q] = *reinterpret_cast<const f4*>(pu + 4 * q);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) uR[q][x] = (cc + x < bw) ? pu[4 * q + x] : 0.0f;
+      }
+    }
+  };
+  auto store = [&](int buf) {
+    float* se = &Es[buf][er * QE_LD + ec];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      se[x] = eR[0][x];
+      se[4 + x] = eR[1][x];
+    }
+    float* su = &Us[buf][ur * QU_LD + uc];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<f4*>(su + 4 * q) = uR[q];
+  };
+
+  f16 acc[2];
+  double acc64[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      acc[i][x] = 0.0f;
+      acc64[i][x] = 0.0;
+    }
+
+  if (nchunks > 0) {
+    fetch(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      const int cur = c & 1;
+      const bool more = c + 1 < nchunks;
+      if (more) fetch(c + 1);
+      const float* es = Es[cur];
+      const float* us = Us[cur];
+#pragma unroll
+      for (int kk = 0; kk < 32; kk += 2) {
+        const int k = kk + (lane >> 5);
+        const float a0 = es[(lane & 31) * QE_LD + k];
+        const float a1 = es[(32 + (lane & 31)) * QE_LD + k];
+        const float b = us[k * QU_LD + w * 32 + (lane & 31)];
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+          acc64[i][x] += (double)acc[i][x];
+          acc[i][x] = 0.0f;
+        }
+      if (more) store(cur ^ 1);
+      __syncthreads();
+    }
+  }
+  double* P = part + (int64_t)p * part_stride;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int64_t row = r0 + 32 * i + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+      const int col = w * 32 + (lane & 31);
+      if (row < rows) P[row * QB + col] = acc64[i][x];
+    }
+}
+
+// ---------------------------------------------------------------- sweep
+//
+// One block of columns [j0, j0+bw). 16 rows per wave (4 lanes per row).
+template <int GS>
+__global__ __launch_bounds__(256) void q_sweep_kernel(
+    const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ part, int P,
+    int64_t part_stride, const float* __restrict__ U, int64_t ldu, int64_t rows, int64_t j0, int bw,
+    int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
+    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
+    double* __restrict__ row_loss, unsigned* __restrict__ status) {
+  __shared__ double Us[QB * QB];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int q4 = lane & 3;
+  const int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 2) + wv * 16 + (lane >> 2);
+  const bool rv = r < rows;
+  const double maxq = (double)((1 << bits) - 1);
+
+  // U slab of this block (upper triangle), zero outside [0, bw).
+  for (int e = t; e < QB * QB; e += blockDim.x) {
+    const int a = e >> 7, c = e & 127;
+    Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] : 0.0;
+  }
+
+  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk].
+  double w[32];
+  bool finite = true;
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    const int c = 4 * s + q4;
+    double v = 0.0;
+    if (rv && c < bw) {
+      v = f16_to_f64(W[r * ldw + j0 + c]);
+      finite = finite && isfinite(v);
+      for (int p = 0; p < P; ++p) v -= part[(int64_t)p * part_stride + r * QB + c];
+    }
+    w[s] = v;
+  }
+  if (!finite) atomicOr(status, ST_NONFINITE);
+  __syncthreads();
+
+  double scale = 1.0, zero = 0.0, loss = 0.0;
+  const int nt4 = (bw + 3) >> 2;
+  for (int tt = 0; tt < nt4; ++tt) {
+    if (((4 * tt) % GS) == 0) {
+      // grid of the group starting here, from the current values
+      double mn = 0.0, mx = 0.0;
+#pragma unroll
+      for (int s = 0; s < GS / 4; ++s) {
+        if (4 * (tt + s) + q4 < bw) {
+          mn = fmin(mn, w[s]);
+          mx = fmax(mx, w[s]);
+        }
+      }
+      mn = fmin(mn, quad_xor1(mn));
+      mx = fmax(mx, quad_xor1(mx));
+      mn = fmin(mn, quad_xor2(mn));
+      mx = fmax(mx, quad_xor2(mx));
+      uint16_t sh = f64_to_f16_rne((mx - mn) / maxq);
+      scale = f16_to_f64(sh);
+      if ((sh & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
+      if (mx == mn || scale == 0.0) {
+        scale = 1.0;
+        sh = 0x3c00;
+        zero = 0.0;
+      } else {
+        zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
+      }
+      if (rv && q4 == 0) {
+        const int64_t g = (j0 + 4 * tt) / GS;
+        scales[r * ldg + g] = sh;
+        zeros[r * ldg + g] = f64_to_f16_rne(zero);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * tt + jj;
+      if (j < bw) {
+        // quantize slot 0 (meaningful on the owner lane q4 == jj)
+        const double v = w[0];
+        double qf = rint(v / scale) + zero;
+        qf = fmin(fmax(qf, 0.0), maxq);
+        const double dq = scale * (qf - zero);
+        const double e = (v - dq) / Us[j * QB + j];
+        double eb;
+        if (jj == 0) eb = quad_bcast<0>(e);
+        else if (jj == 1) eb = quad_bcast<1>(e);
+        else if (jj == 2) eb = quad_bcast<2>(e);
+        else eb = quad_bcast<3>(e);
+        if (q4 == jj && rv) {
+          codes[r * ldc + j0 + j] = (uint8_t)qf;
+          E[r * lde + j0 + j] = (float)e;
+          loss += e * e;
+        }
+        const double* urow = Us + j * QB + 4 * tt + q4;
+        if (q4 > jj) w[0] -= eb * urow[0];
+#pragma unroll
+        for (int s = 1; s < 32; ++s)
+          if (s < 32 - tt) w[s] -= eb * urow[4 * s];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 31; ++s) w[s] = w[s + 1];
+    w[31] = 0.0;
+  }
+  loss += quad_xor1(loss);
+  loss += quad_xor2(loss);
+  if (rv && q4 == 0) row_loss[r] += loss;
+}
+
+// ---------------------------------------------------------------- layout
+
+struct QLayout {
+  int64_t rows, cols, lde, ng;
+  int pmax;
+  size_t off_status, off_invperm, off_wp, off_codes, off_E, off_part, total;
+};
+
+static int q_pmax(int64_t rows) {
+  const int64_t rt = cdiv(rows, 64);
+  int64_t p = cdiv(2048, rt);
+  if (p > 16) p = 16;
+  if (p < 1) p = 1;
+  return (int)p;
+}
+
+static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
+  QLayout L;
+  L.rows = rows;
+  L.cols = cols;
+  L.lde = round_up(cols, QB);
+  L.ng = cdiv(cols, gs);
+  L.pmax = q_pmax(rows);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = (size_t)round_up((int64_t)(o + bytes), 256);
+    return at;
+  };
+  L.off_status = take(4);
+  L.off_invperm = take(4 * (size_t)cols);
+  L.off_wp = take(2 * (size_t)rows * cols);
+  L.off_codes = take((size_t)rows * cols);
+  L.off_E = take(4 * (size_t)rows * L.lde);
+  L.off_part = take(8 * (size_t)L.pmax * rows * QB);
+  L.total = o;
+  return L;
+}
+
+template <int GS>
+static gptq_status launch_sweep(hipStream_t st, int nw, const uint16_t* Wsrc, int64_t ldws,
+                                const double* part, int P, int64_t pstride, const float* U,
+                                int64_t cols, int64_t rows, int64_t j0, int bw, int bits, float* E,
+                                int64_t lde, uint8_t* codes, int64_t ldc, uint16_t* scales,
+                                uint16_t* zeros, int64_t ldg, double* row_loss, unsigned* status) {
+  const unsigned nblk = (unsigned)cdiv(rows, 16 * nw);
+  GPTQ_LAUNCH(K_Q_SWEEP, st,
+              q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, part, P, pstride, U, cols,
+                                                           rows, j0, bw, bits, E, lde, codes, ldc,
+                                                           scales, zeros, ldg, row_loss, status));
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
+
+using namespace gptq;
+
+static bool valid_gs(int gs) { return gs == 16 || gs == 32 || gs == 64 || gs == 128; }
+
+extern "C" size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int group_size) {
+  if (rows <= 0 || cols <= 0 || !valid_gs(group_size)) return 0;
+  return q_layout(rows, cols, group_size).total;
+}
+
+extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                           const float* U, const int32_t* perm, int bits,
+                                           int group_size, uint8_t* codes, uint16_t* scales,
+                                           uint16_t* zeros, int32_t* g_idx, double* row_loss,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0 || cols < 0) return GPTQ_EINVAL;
+  if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
+  if (cols > (int64_t)1 << 20 || rows > (int64_t)1 << 26) return GPTQ_EINVAL;
+  const QLayout L = q_layout(rows, cols, group_size);
+  if (!ws || ws_bytes < L.total) return GPTQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  unsigned* status = (unsigned*)(base + L.off_status);
+  int32_t* invperm = (int32_t*)(base + L.off_invperm);
+  uint16_t* Wp = (uint16_t*)(base + L.off_wp);
+  uint8_t* codes_s = (uint8_t*)(base + L.off_codes);
+  float* E = (float*)(base + L.off_E);
+  double* part = (double*)(base + L.off_part);
+  const int64_t pstride = rows * QB;
+
+  {
+    const int64_t n = rows > cols ? rows : cols;
+    const unsigned nb = (unsigned)std::min<int64_t>(cdiv(n, 256), 4096);
+    GPTQ_LAUNCH(K_Q_INIT, st,
+                q_init_kernel<<<nb, 256, 0, st>>>(row_loss, rows, perm, invperm, g_idx, cols,
+                                                  group_size, status));
+  }
+  const uint16_t* Wsrc = W;
+  int64_t ldws = ldw;
+  uint8_t* csw = codes;  // sweep-order codes
+  if (perm) {
+    dim3 grid((unsigned)std::min<int64_t>(cdiv(cols, 256), 16),
+              (unsigned)std::min<int64_t>(rows, 65535));
+    GPTQ_LAUNCH(K_Q_PERMUTE, st,
+                q_permute_kernel<<<grid, 256, 0, st>>>(W, ldw, perm, rows, cols, Wp, invperm,
+                                                       status));
+    Wsrc = Wp;
+    ldws = cols;
+    csw = codes_s;
+  }
+  const int64_t waves = cdiv(rows, 16);
+  const int nw = waves > 512 ? 4 : (waves > 256 ? 2 : 1);
+  const bool vecU = (cols % 4 == 0) && ((uintptr_t)U % 16 == 0);
+  const int64_t rt = cdiv(rows, 64);
+  for (int64_t j0 = 0; j0 < cols; j0 += QB) {
+    const int bw = (int)std::min<int64_t>(QB, cols - j0);
+    int P = 0;
+    if (j0 > 0) {
+      int64_t p = L.pmax;
+      if (p > j0 / 32) p = j0 / 32;
+      const int64_t ks = round_up(cdiv(j0, p), 32);
+      P = (int)cdiv(j0, ks);
+      dim3 grid((unsigned)rt, (unsigned)P);
+      GPTQ_LAUNCH(K_Q_GEMM, st,
+                  q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, rows, j0, bw, ks, part,
+                                                      pstride, vecU));
+    }
+    gptq_status s;
+    switch (group_size) {
+      case 16: s = launch_sweep<16>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 32: s = launch_sweep<32>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 64: s = launch_sweep<64>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      default: s = launch_sweep<128>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+    }
+    if (s != GPTQ_OK) return s;
+  }
+  if (perm) {
+    dim3 grid((unsigned)std::min<int64_t>(cdiv(cols, 256), 16),
+              (unsigned)std::min<int64_t>(rows, 65535));
+    GPTQ_LAUNCH(K_Q_FINALIZE, st,
+                q_finalize_kernel<<<grid, 256, 0, st>>>(codes_s, invperm, rows, cols, group_size,
+                                                        codes, g_idx, status));
+  }
+  unsigned h_status = 0;
+  if (hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return GPTQ_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return GPTQ_EHIP;
+  if (h_status & ST_BADPERM) return GPTQ_EINVAL;
+  if (h_status & ST_NONFINITE) return GPTQ_ENONFINITE;
+  return GPTQ_OK;
+}

@@ -1,0 +1,224 @@
+"""Thin Python binding of libgptq (argument marshalling only).
+
+Every step of the quantizer runs in the HIP library; this module only checks
+tensor shapes/dtypes/devices, allocates outputs and workspaces with torch on
+the current HIP device, and passes raw pointers plus torch's current stream.
+If the library is missing the import fails: there is no fallback.
+
+Names mirror the C ABI in include/gptq.h:
+    hessian_accumulate(S, X)                    -> S (updated in place)
+    prepare_hinv(S, n_tokens, damp, act_order)  -> (perm, U)
+    quantize_layer(W, U, perm, bits, group_size)-> QuantizedLayer
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptq.so")
+
+GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTSPD, GPTQ_EHIP, GPTQ_EWORKSPACE, GPTQ_ENONFINITE = range(6)
+GPTQ_FLAG_ACT_ORDER = 1
+
+EXPORTS = {
+    "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "gptq_hessian_accumulate": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int64,
+                                          C.c_void_p, C.c_size_t, C.c_void_p]),
+    "gptq_prepare_workspace_bytes": (C.c_size_t, [C.c_int64]),
+    "gptq_prepare_hinv": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_double, C.c_uint32,
+                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "gptq_quantize_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int]),
+    "gptq_quantize_layer": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
+                                      C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                      C.c_void_p]),
+    "gptq_status_string": (C.c_char_p, [C.c_int]),
+    "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
+    "gptq_version": (C.c_int, []),
+    "gptq_profile_enable": (C.c_int, [C.c_int]),
+    "gptq_profile_kernel_count": (C.c_int, []),
+    "gptq_profile_kernel_name": (C.c_char_p, [C.c_int]),
+    "gptq_profile_read": (C.c_int, [C.c_void_p, C.c_void_p]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libgptq.so is not built ({LIB_PATH}); run "
+                          "`python -m post_weight_quantization_hessian_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in EXPORTS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.gptq_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status != GPTQ_OK:
+        raise GPTQError(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    torch = _torch()
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return C.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else C.c_void_p(0)
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda:
+        raise TypeError(f"{name} must be a {dtype} tensor on a HIP device")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- step 1
+
+def hessian_workspace_bytes(in_features: int, n_tokens: int) -> int:
+    return int(lib.gptq_hessian_workspace_bytes(in_features, n_tokens))
+
+
+def hessian_accumulate(S, X, workspace=None):
+    """S += X^T X (fp64 S [i x i], fp32 X [n x i], unit stride along i)."""
+    torch = _torch()
+    _need(S, torch.float64, "S", 2)
+    _need(X, torch.float32, "X", 2)
+    n, i = X.shape
+    if S.shape != (i, i) or not S.is_contiguous():
+        raise ValueError("S must be a contiguous [in_features x in_features] tensor")
+    if X.stride(1) != 1:
+        raise ValueError("X rows must be contiguous")
+    if workspace is None:
+        workspace = _workspace(hessian_workspace_bytes(i, n), X.device)
+    st = lib.gptq_hessian_accumulate(_ptr(S), i, _ptr(X), n, X.stride(0) if n > 0 else i,
+                                     _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "gptq_hessian_accumulate")
+    return S
+
+
+# ---------------------------------------------------------------- steps 2-3
+
+def prepare_workspace_bytes(in_features: int) -> int:
+    return int(lib.gptq_prepare_workspace_bytes(in_features))
+
+
+def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
+                 workspace=None, out=None):
+    """Damped, optionally act-ordered Hessian -> (perm int32 [i], U fp32 [i x i])."""
+    torch = _torch()
+    _need(S, torch.float64, "S", 2)
+    i = S.shape[0]
+    if S.shape != (i, i) or not S.is_contiguous():
+        raise ValueError("S must be a contiguous square tensor")
+    if out is None:
+        perm = torch.empty(i, dtype=torch.int32, device=S.device)
+        U = torch.empty((i, i), dtype=torch.float32, device=S.device)
+    else:
+        perm, U = out
+    if workspace is None:
+        workspace = _workspace(prepare_workspace_bytes(i), S.device)
+    flags = GPTQ_FLAG_ACT_ORDER if act_order else 0
+    st = lib.gptq_prepare_hinv(_ptr(S), i, int(n_tokens), float(damp), flags, _ptr(perm), _ptr(U),
+                               _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "gptq_prepare_hinv")
+    return perm, U
+
+
+# ---------------------------------------------------------------- steps 4-6
+
+@dataclass
+class QuantizedLayer:
+    codes: object      # uint8 [rows x cols], original column order
+    scales: object     # fp16  [rows x groups], groups in sweep order
+    zeros: object      # fp16  [rows x groups]
+    g_idx: object      # int32 [cols]
+    row_loss: object   # fp64  [rows]
+    bits: int
+    group_size: int
+
+
+def quantize_workspace_bytes(rows: int, cols: int, group_size: int) -> int:
+    return int(lib.gptq_quantize_workspace_bytes(rows, cols, group_size))
+
+
+def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, workspace=None):
+    """Sweep the fp16 weights W [rows x cols] with the factor U (and perm)."""
+    torch = _torch()
+    _need(W, torch.float16, "W", 2)
+    _need(U, torch.float32, "U", 2)
+    rows, cols = W.shape
+    if U.shape != (cols, cols) or not U.is_contiguous():
+        raise ValueError("U must be a contiguous [cols x cols] tensor")
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    if perm is not None:
+        _need(perm, torch.int32, "perm", 1)
+        if perm.numel() != cols:
+            raise ValueError("perm must have cols entries")
+    ng = -(-cols // group_size) if group_size > 0 else 0
+    dev = W.device
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, ng), dtype=torch.float16, device=dev)
+    zeros = torch.empty((rows, ng), dtype=torch.float16, device=dev)
+    g_idx = torch.empty(cols, dtype=torch.int32, device=dev)
+    row_loss = torch.empty(rows, dtype=torch.float64, device=dev)
+    if workspace is None:
+        workspace = _workspace(quantize_workspace_bytes(rows, cols, group_size), dev)
+    st = lib.gptq_quantize_layer(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
+                                 _ptr(perm), int(bits), int(group_size), _ptr(codes),
+                                 _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(row_loss),
+                                 _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "gptq_quantize_layer")
+    return QuantizedLayer(codes, scales, zeros, g_idx, row_loss, bits, group_size)
+
+
+# ---------------------------------------------------------------- utilities
+
+def fp16_round_host(values):
+    """Nearest-even fp16 bit patterns of fp64 values (host routine of the library)."""
+    import numpy as np
+    a = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(a.shape, dtype=np.uint16)
+    _check(lib.gptq_fp16_round_host(a.ctypes.data_as(C.c_void_p), out.ctypes.data_as(C.c_void_p),
+                                    a.size), "gptq_fp16_round_host")
+    return out
+
+
+def profile_enable(on: bool = True):
+    _check(lib.gptq_profile_enable(1 if on else 0), "gptq_profile_enable")
+
+
+def profile_read() -> dict:
+    """{kernel name: (total ms, launches)} since the last read."""
+    n = lib.gptq_profile_kernel_count()
+    tot = (C.c_double * n)()
+    cnt = (C.c_int64 * n)()
+    _check(lib.gptq_profile_read(C.cast(tot, C.c_void_p), C.cast(cnt, C.c_void_p)),
+           "gptq_profile_read")
+    return {lib.gptq_profile_kernel_name(k).decode(): (tot[k], cnt[k]) for k in range(n)}

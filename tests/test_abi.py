@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point declared in include/gptq.h, validates arguments before
+touching the device, and its fp16 rounding routine is the nearest-even one."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptq.h")
+
+g = pytest.importorskip("post_weight_quantization_hessian_amd.gptq")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gptq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(g.lib, n), n
+        assert n in g.EXPORTS, n
+
+
+def test_status_strings_and_version():
+    assert g.lib.gptq_version() == 1
+    for s in range(6):
+        assert g.lib.gptq_status_string(s)
+    assert g.lib.gptq_status_string(99) == b"unknown status"
+
+
+def test_fp16_rounding_is_nearest_even():
+    rng = np.random.default_rng(0)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        # exact ties between neighbouring fp16 values (binary64 midpoints)
+        (np.arange(1, 2000, dtype=np.float64) + 0.5) * 2.0 ** -24,
+        (1024 + np.arange(0, 1023) + 0.5) * 2.0 ** -10,
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2 ** -25, 2 ** -24, 6e-8],
+    ])
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(g.fp16_round_host(v), want)
+
+
+def test_workspace_sizes():
+    assert g.quantize_workspace_bytes(0, 10, 128) == 0
+    assert g.quantize_workspace_bytes(10, 10, 100) == 0  # bad group size
+    q = g.quantize_workspace_bytes(896, 4864, 128)
+    assert q >= 896 * 4864 * (2 + 1 + 4)
+    p = g.prepare_workspace_bytes(576)
+    assert p >= 2 * 640 * 640 * 8
+    assert g.hessian_workspace_bytes(576, 2048) > 0
+    assert g.hessian_workspace_bytes(28672, 65536) == 0  # enough tiles, no split
+
+
+FAKE = C.c_void_p(0x10000)  # never dereferenced: validation fails first
+NULL = C.c_void_p(0)
+
+
+def test_invalid_arguments_rejected_on_host():
+    L = g.lib
+    # quantize: bits / group size / null outputs / ld / workspace
+    args = lambda **kw: dict(dict(W=FAKE, rows=4, cols=8, ldw=8, U=FAKE, perm=NULL, bits=4, gs=16,
+                                  codes=FAKE, scales=FAKE, zeros=FAKE, g_idx=NULL, loss=FAKE,
+                                  ws=FAKE, wsb=1 << 40), **kw)
+
+    def q(**kw):
+        a = args(**kw)
+        return L.gptq_quantize_layer(a["W"], a["rows"], a["cols"], a["ldw"], a["U"], a["perm"],
+                                     a["bits"], a["gs"], a["codes"], a["scales"], a["zeros"],
+                                     a["g_idx"], a["loss"], a["ws"], a["wsb"], NULL)
+    assert q(bits=1) == g.GPTQ_EINVAL
+    assert q(bits=9) == g.GPTQ_EINVAL
+    assert q(gs=48) == g.GPTQ_EINVAL
+    assert q(gs=0) == g.GPTQ_EINVAL
+    assert q(codes=NULL) == g.GPTQ_EINVAL
+    assert q(W=NULL) == g.GPTQ_EINVAL
+    assert q(ldw=7) == g.GPTQ_EINVAL
+    assert q(rows=-1) == g.GPTQ_EINVAL
+    assert q(ws=NULL) == g.GPTQ_EWORKSPACE
+    assert q(wsb=16) == g.GPTQ_EWORKSPACE
+    assert q(rows=0) == g.GPTQ_OK and q(cols=0) == g.GPTQ_OK  # empty: no-op
+    # prepare
+    pw = L.gptq_prepare_hinv
+    assert pw(NULL, 8, 10, 0.01, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 0, 0.01, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, -0.1, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, float("nan"), 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, 0.01, 8, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, 0.01, 0, FAKE, FAKE, FAKE, 64, NULL) == g.GPTQ_EWORKSPACE
+    assert pw(FAKE, 0, 10, 0.01, 0, NULL, NULL, NULL, 0, NULL) == g.GPTQ_OK
+    # hessian
+    ha = L.gptq_hessian_accumulate
+    assert ha(NULL, 8, FAKE, 10, 8, NULL, 0, NULL) == g.GPTQ_EINVAL
+    assert ha(FAKE, 8, FAKE, 10, 7, NULL, 0, NULL) == g.GPTQ_EINVAL
+    assert ha(FAKE, 8, NULL, 0, 8, NULL, 0, NULL) == g.GPTQ_OK  # no tokens: no-op
+    assert ha(FAKE, -1, FAKE, 10, 8, NULL, 0, NULL) == g.GPTQ_EINVAL
+
+
+def test_profile_api_without_launches():
+    g.profile_enable(True)
+    r = g.profile_read()
+    g.profile_enable(False)
+    assert "quant_sweep" in r and "hessian_tile" in r
+    assert all(v == (0.0, 0) for v in r.values())
