@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Benchmark of the GPTQ layer quantizer on one MI355X.
+
+A step is one pass of the whole hot path over one workload: for every
+calibration input, the Hessian (S = X^T X over its token chunks), the damped
+and act-ordered factor U of the inverse, and the column sweep of every layer
+that reads the input (rows stacked), at every bit width of the workload.
+Inputs (activations and fp16 weights) are resident in HBM before timing.
+
+Prints ONE JSON line: throughput in quantized weights per second, the
+roofline of the dominant kernel (HIP-event durations measured inside the
+timed steps on the launch stream), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = ("quantized weights/sec per layer + XXᵀ/trailing-GEMM % MFMA peak, 1×MI355X")
+DEFAULT_WORKLOAD = "qwen05b_mlp"
+
+# MI355X published peaks
+PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="rows per layer group for the oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def kernel_work(name, wl, plan):
+    """Algorithmic flops (or bytes) of all launches of one kernel class in a
+    step, with the unit and the roofline it is priced against."""
+    if name == "hessian_tile":
+        f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
+        return f, "flop", "f64_mfma"
+    if name in ("chol_syrk", "chol_trsm", "trtri_update", "trtri_row"):
+        f = 0.0
+        for h in plan:
+            nt = -(-h.dim // 128)
+            for p in range(nt):
+                m = nt - 1 - p
+                if name == "chol_syrk":
+                    f += 2 * 128 ** 3 * m * (m + 1) / 2
+                elif name == "chol_trsm":
+                    f += 2 * 128 ** 3 * m
+                elif name == "trtri_update":
+                    f += 2 * 128 ** 3 * m * (p + 1)
+                else:
+                    f += 2 * 128 ** 3 * p
+        return f, "flop", "f64_mfma"
+    if name == "quant_gemm":
+        f = 0.0
+        for h in plan:
+            for bits in wl.bits:
+                for j0 in range(128, h.dim, 128):
+                    bw = min(128, h.dim - j0)
+                    f += 2.0 * h.rows * j0 * bw
+        return f, "flop", "f32_mfma"
+    if name == "quant_sweep":
+        # bytes per weight: fp16 weight 2 + fp64 update 8 + code 1 + fp32 error 4;
+        # plus 4 bytes (fp16 scale + zero) per group and the fp32 U slab per block
+        b = 0.0
+        for h in plan:
+            for bits in wl.bits:
+                b += h.rows * h.dim * 15 + h.rows * (-(-h.dim // wl.group_size)) * 4
+                b += sum(4 * min(128, h.dim - j0) ** 2 for j0 in range(0, h.dim, 128))
+        return b, "byte", "hbm"
+    return None, None, None
+
+
+class HPlan:
+    def __init__(self, name, dim, n, rows):
+        self.name, self.dim, self.n, self.rows = name, dim, n, rows
+
+
+# ---------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(wl, host_inputs, sample_rows):
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t_total = 0.0
+    sampled = []
+    for hname, (X, W) in host_inputs.items():
+        chunks = [X[s:s + wl.token_chunk] for s in range(0, X.shape[0], wl.token_chunk)]
+        t0 = time.perf_counter()
+        S, n = O.hessian_sum(chunks)
+        t1 = time.perf_counter()
+        H = O.damped_hessian(S, n, wl.damp)
+        perm = O.act_order_perm(H) if wl.act_order else np.arange(H.shape[0])
+        Hp = O.permute_sym(H, perm)
+        U = O.hinv_upper(Hp)
+        t2 = time.perf_counter()
+        rows = W.shape[0]
+        rs = min(rows, sample_rows)
+        Wp = W[:rs].astype(np.float64)[:, perm]
+        ts = 0.0
+        for bits in wl.bits:
+            t3 = time.perf_counter()
+            O.gptq_sweep(Wp, U, bits, wl.group_size)
+            ts += time.perf_counter() - t3
+        t_total += (t1 - t0) + (t2 - t1) + ts * rows / rs
+        sampled.append(f"{hname}: accumulate {X.shape[0]}x{X.shape[1]} + factor "
+                       f"{H.shape[0]} in full, strict sweep on {rs}/{rows} rows "
+                       f"(scaled by rows)")
+    weights = wl.weights_per_step()
+    return {"value": weights / t_total, "unit": "weights/s", "cores": int(threads),
+            "kind": "oracle", "sample": "; ".join(sampled),
+            "seconds_per_step_extrapolated": t_total}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the quantizer's hot path is measured "
+              "on one MI355X (multi-GPU sharding is design-only).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from post_weight_quantization_hessian_amd import synth
+    from post_weight_quantization_hessian_amd.workloads import WORKLOADS
+    import post_weight_quantization_hessian_amd.gptq as G
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- inputs, resident on the device
+    host_inputs = {}
+    dev_inputs = {}
+    plan = []
+    for h in wl.inputs:
+        X = synth.activations(wl.wid, h.name, wl.n_tokens, h.dim, kind=h.kind,
+                              lognormal_sigma=h.lognormal_sigma)
+        Ws = [synth.weights(wl.wid, l.name, l.rows, h.dim, outlier_frac=l.outlier_frac)
+              for l in wl.layers_of(h.name)]
+        W = np.concatenate(Ws, axis=0)
+        host_inputs[h.name] = (X, W)
+        Xd = torch.from_numpy(X).to(dev)
+        Wd = torch.from_numpy(W).to(dev)
+        chunks = [Xd[s:s + wl.token_chunk] for s in range(0, wl.n_tokens, wl.token_chunk)]
+        S = torch.empty((h.dim, h.dim), dtype=torch.float64, device=dev)
+        hws = torch.empty(max(G.hessian_workspace_bytes(h.dim, c.shape[0]) for c in chunks) or 1,
+                          dtype=torch.uint8, device=dev)
+        pws = torch.empty(G.prepare_workspace_bytes(h.dim), dtype=torch.uint8, device=dev)
+        perm = torch.empty(h.dim, dtype=torch.int32, device=dev)
+        U = torch.empty((h.dim, h.dim), dtype=torch.float32, device=dev)
+        qws = torch.empty(G.quantize_workspace_bytes(W.shape[0], h.dim, wl.group_size),
+                          dtype=torch.uint8, device=dev)
+        outs = [G.QuantizedLayer(
+            torch.empty(W.shape, dtype=torch.uint8, device=dev),
+            torch.empty((W.shape[0], -(-h.dim // wl.group_size)), dtype=torch.float16, device=dev),
+            torch.empty((W.shape[0], -(-h.dim // wl.group_size)), dtype=torch.float16, device=dev),
+            torch.empty(h.dim, dtype=torch.int32, device=dev),
+            torch.empty(W.shape[0], dtype=torch.float64, device=dev), b, wl.group_size)
+            for b in wl.bits]
+        dev_inputs[h.name] = dict(chunks=chunks, W=Wd, S=S, hws=hws, pws=pws, perm=perm, U=U,
+                                  qws=qws, outs=outs)
+        plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0]))
+    torch.cuda.synchronize()
+
+    def step():
+        for h in wl.inputs:
+            d = dev_inputs[h.name]
+            for ci, c in enumerate(d["chunks"]):
+                G.hessian_accumulate(d["S"], c, workspace=d["hws"], overwrite=(ci == 0))
+            G.prepare_hinv(d["S"], wl.n_tokens, damp=wl.damp, act_order=wl.act_order,
+                           workspace=d["pws"], out=(d["perm"], d["U"]))
+            for bi, bits in enumerate(wl.bits):
+                G.quantize_layer(d["W"], d["U"], d["perm"] if wl.act_order else None, bits=bits,
+                                 group_size=wl.group_size, workspace=d["qws"], out=d["outs"][bi])
+
+    # ---- warmup: all kernels timed to find the dominant class
+    G.profile_enable(True)
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    prof_warm = G.profile_read()
+    G.profile_enable(False)
+    dominant = max(prof_warm, key=lambda k: prof_warm[k][0])
+
+    # ---- timed steps: only the dominant kernel bracketed by events
+    G.profile_enable([dominant])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = G.profile_read()
+    G.profile_enable(False)
+
+    ms_per_step = 1000.0 * elapsed / args.steps
+    weights = wl.weights_per_step()
+    value = weights * args.steps / elapsed
+
+    dom_ms, dom_launches = prof[dominant]
+    work, unit, peak_key = kernel_work(dominant, wl, plan)
+    roofline = None
+    if work is not None and dom_ms > 0:
+        per_step_s = dom_ms / 1000.0 / args.steps
+        if unit == "flop":
+            achieved = work / per_step_s / 1e12
+            peak = PEAK[peak_key]
+            roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                        "frac": achieved / peak, "traffic": None,
+                        "kernel": dominant, "precision": peak_key,
+                        "launches_per_step": dom_launches / args.steps,
+                        "avg_launch_ms": dom_ms / max(dom_launches, 1),
+                        "frac_vs_bf16_dense": achieved / PEAK["bf16_mfma"],
+                        "frac_vs_f32_mfma": achieved / PEAK["f32_mfma"]}
+        else:
+            achieved = work / per_step_s / 1e9
+            roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"],
+                        "unit": "GB/s", "frac": achieved / PEAK["hbm_gbs"], "traffic": None,
+                        "kernel": dominant, "launches_per_step": dom_launches / args.steps,
+                        "avg_launch_ms": dom_ms / max(dom_launches, 1)}
+
+    breakdown = {k: {"ms_per_step": v[0] / max(args.warmup, 1),
+                     "launches_per_step": v[1] / max(args.warmup, 1)}
+                 for k, v in prof_warm.items() if v[1] > 0}
+    phases = {}
+    for k, v in breakdown.items():
+        w, u, pk = kernel_work(k, wl, plan)
+        if w is not None and v["ms_per_step"] > 0:
+            rate = w / (v["ms_per_step"] / 1000.0)
+            v["achieved"] = rate / (1e12 if u == "flop" else 1e9)
+            v["unit"] = "TFLOP/s" if u == "flop" else "GB/s"
+            v["peak"] = PEAK[pk] if u == "flop" else PEAK["hbm_gbs"]
+            v["frac"] = v["achieved"] / v["peak"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample_rows = args.cpu_sample_rows or 64
+        cpu = cpu_baseline(wl, host_inputs, sample_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.notes,
+                   "layers": [f"{l.name} {l.rows}x{wl.input(l.hessian).dim}" for l in wl.layers],
+                   "n_tokens": wl.n_tokens, "token_chunk": wl.token_chunk,
+                   "bits": list(wl.bits), "group_size": wl.group_size,
+                   "act_order": wl.act_order, "damp": wl.damp,
+                   "weights_per_step": weights,
+                   "arithmetic": "fp64 Hessian/Cholesky/inverse and sweep, fp32 MFMA lazy update"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

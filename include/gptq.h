@@ -49,26 +49,31 @@ typedef enum {
 } gptq_status;
 
 /* flags */
-#define GPTQ_FLAG_ACT_ORDER 1u  /* gptq_prepare_hinv: visit columns by descending diag H */
+#define GPTQ_FLAG_ACT_ORDER 1u          /* gptq_prepare_hinv: visit columns by descending diag H */
+#define GPTQ_FLAG_HESSIAN_OVERWRITE 2u  /* gptq_hessian_accumulate: S = X^T X instead of S += */
 
 /* ---------------------------------------------------------------------------
  * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's
  * calibration activations). Accumulates the unnormalised sum
- *     S[i x i] += X^T X,   X = n_tokens x in_features fp32, row stride ldx.
- * S is fp64 and symmetric: both triangles are updated. The products of two
- * fp32 values are formed exactly (fp64), only the sums round. Call it once per
- * token chunk on a zero-initialised S and keep the running token count; the
- * normalisation (2/n) is applied by gptq_prepare_hinv.
+ *     S[i x i] += X^T X,   X = n_tokens x in_features fp32, row stride ldx,
+ * or S = X^T X with flags & GPTQ_FLAG_HESSIAN_OVERWRITE (S's old contents are
+ * then never read; with n_tokens == 0 S is set to zero). S is fp64 and
+ * symmetric: both triangles are written. The products of two fp32 values are
+ * formed exactly (fp64), only the sums round. Call it once per token chunk
+ * (the first with the overwrite flag, or on a zeroed S) and keep the running
+ * token count; the normalisation (2/n) is applied by gptq_prepare_hinv.
+ * Other flag bits are rejected (GPTQ_EINVAL).
  * ws may be NULL (ws_bytes 0): the call is then done without token splitting.
  * With ws of gptq_hessian_workspace_bytes(in_features, n_tokens) bytes the
  * token range is split across more workgroups and reduced in a fixed order
  * (results are bitwise reproducible either way for a given ws choice).
- * n_tokens == 0 or in_features == 0 is a no-op. Asynchronous on `stream`.
+ * in_features == 0, or n_tokens == 0 without the overwrite flag, is a no-op.
+ * Asynchronous on `stream`.
  * ------------------------------------------------------------------------- */
 size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_tokens);
 gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
                                     const float* X, int64_t n_tokens, int64_t ldx,
-                                    void* ws, size_t ws_bytes, void* stream);
+                                    uint32_t flags, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Steps 2-3 — damping, act-order, factor of the inverse.  CHMC article,
@@ -134,21 +139,26 @@ gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, i
  *   the nearest-even binary16 with the same routine the kernels use for group
  *   scales (no double rounding through fp32). Returns GPTQ_EINVAL on NULL.
  * gptq_version: ABI version number (currently 1).
+ * gptq_last_error_string: text of the last HIP runtime error that made a call
+ *   of this thread return GPTQ_EHIP ("no error" if none); static storage.
  * ------------------------------------------------------------------------- */
 const char* gptq_status_string(gptq_status status);
+const char* gptq_last_error_string(void);
 gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int64_t n);
 int gptq_version(void);
 
 /* ---------------------------------------------------------------------------
- * Optional kernel timing (process-wide, not thread-safe). While enabled, every
- * kernel launch of the library is bracketed by HIP events on its stream.
+ * Optional kernel timing (process-wide, not thread-safe). gptq_profile_enable
+ * takes a bit mask of kernel ids (bit k = kernel id k; 0 turns timing off,
+ * 0xFFFFFFFF times every kernel). Each launch of a selected kernel is then
+ * bracketed by two HIP events recorded on the stream it is launched on.
  * gptq_profile_read synchronizes on the recorded events, adds their durations
  * per kernel class and clears the record.
  *   kernel ids: 0 .. gptq_profile_kernel_count()-1; names via
  *   gptq_profile_kernel_name(id) (static string, NULL for a bad id).
  *   totals_ms / launches: host arrays of gptq_profile_kernel_count() entries.
  * ------------------------------------------------------------------------- */
-gptq_status gptq_profile_enable(int on);
+gptq_status gptq_profile_enable(uint32_t kernel_mask);
 int gptq_profile_kernel_count(void);
 const char* gptq_profile_kernel_name(int id);
 gptq_status gptq_profile_read(double* totals_ms, int64_t* launches);

@@ -17,26 +17,34 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 
-static bool g_prof_on = false;
+static uint32_t g_prof_mask = 0u;
+static thread_local hipError_t g_last_error = hipSuccess;
+
+void note_hip_error(hipError_t e) { g_last_error = e; }
 static std::vector<ProfRec> g_prof;
 static std::vector<hipEvent_t> g_open;  // per-launch start events pending an end
 
+static bool selected(int kid) { return (g_prof_mask >> kid) & 1u; }
+
+// A null start event marks a launch whose start could not be recorded; the
+// matching prof_end then records nothing.
 void prof_begin(int kid, hipStream_t s) {
-  if (!g_prof_on) return;
-  hipEvent_t a;
-  if (hipEventCreate(&a) != hipSuccess) return;
-  if (hipEventRecord(a, s) != hipSuccess) {
+  if (!selected(kid)) return;
+  hipEvent_t a = nullptr;
+  if (hipEventCreate(&a) != hipSuccess) {
+    a = nullptr;
+  } else if (hipEventRecord(a, s) != hipSuccess) {
     (void)hipEventDestroy(a);
-    return;
+    a = nullptr;
   }
   g_open.push_back(a);
-  (void)kid;
 }
 
 void prof_end(int kid, hipStream_t s) {
-  if (!g_prof_on || g_open.empty()) return;
+  if (!selected(kid) || g_open.empty()) return;
   hipEvent_t a = g_open.back();
   g_open.pop_back();
+  if (!a) return;
   hipEvent_t b;
   if (hipEventCreate(&b) != hipSuccess) {
     (void)hipEventDestroy(a);
@@ -70,8 +78,13 @@ extern "C" gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int
 
 extern "C" int gptq_version(void) { return 1; }
 
-extern "C" gptq_status gptq_profile_enable(int on) {
-  g_prof_on = on != 0;
+extern "C" const char* gptq_last_error_string(void) {
+  if (g_last_error == hipSuccess) return "no error";
+  return hipGetErrorString(g_last_error);
+}
+
+extern "C" gptq_status gptq_profile_enable(uint32_t kernel_mask) {
+  g_prof_mask = kernel_mask;
   return GPTQ_OK;
 }
 

@@ -27,6 +27,9 @@ enum KernelId {
 // Launch bracketing for the profiler (defined in api.hip).
 void prof_begin(int kid, hipStream_t s);
 void prof_end(int kid, hipStream_t s);
+// Remember the last HIP error seen by the library (reported by
+// gptq_last_error_string).
+void note_hip_error(hipError_t e);
 
 struct ProfScope {
   int kid;
@@ -35,11 +38,27 @@ struct ProfScope {
   ~ProfScope() { prof_end(kid, s); }
 };
 
+// A launch: clear any stale error left by earlier HIP calls of the process,
+// launch, and report a launch failure as GPTQ_EHIP.
 #define GPTQ_LAUNCH(kid, stream, ...)                          \
   do {                                                         \
+    (void)hipGetLastError();                                   \
     ::gptq::ProfScope _ps((kid), (stream));                    \
     __VA_ARGS__;                                               \
-    if (hipGetLastError() != hipSuccess) return GPTQ_EHIP;     \
+    const hipError_t _e = hipGetLastError();                   \
+    if (_e != hipSuccess) {                                    \
+      ::gptq::note_hip_error(_e);                              \
+      return GPTQ_EHIP;                                        \
+    }                                                          \
+  } while (0)
+
+#define GPTQ_HIP(call)                                         \
+  do {                                                         \
+    const hipError_t _e = (call);                              \
+    if (_e != hipSuccess) {                                    \
+      ::gptq::note_hip_error(_e);                              \
+      return GPTQ_EHIP;                                        \
+    }                                                          \
   } while (0)
 
 // ---------------------------------------------------------------- fp16 bits

@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
                                                         int64_t n_tokens, int64_t dim, int nt,
                                                         int ntiles, int64_t tok_per_split,
                                                         double* __restrict__ S, int64_t lds,
-                                                        double* __restrict__ part, bool vec) {
+                                                        double* __restrict__ part, bool vec,
+                                                        bool overwrite) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
   const int nblocks = gridDim.x;
@@ -92,8 +93,13 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
   for_each_acc(acc, [&](int r, int c, double v) {
     const int64_t i = fa + r, j = fb + c;
     if (i < dim && j < dim) {
-      S[i * lds + j] += v;
-      if (a != b) S[j * lds + i] += v;
+      if (overwrite) {
+        S[i * lds + j] = v;
+        if (a != b) S[j * lds + i] = v;
+      } else {
+        S[i * lds + j] += v;
+        if (a != b) S[j * lds + i] += v;
+      }
     }
   });
 }
@@ -101,7 +107,8 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
 // Sum the token-split partials of every tile in split order and add to S.
 __global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restrict__ part, int nsplit,
                                                           int nt, int ntiles, int64_t dim,
-                                                          double* __restrict__ S, int64_t lds) {
+                                                          double* __restrict__ S, int64_t lds,
+                                                          bool overwrite) {
   const int tile = blockIdx.y;
   int a, b;
   upper_tile(tile, nt, a, b);
@@ -112,8 +119,19 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restri
   if (i >= dim || j >= dim) return;
   double s = 0.0;
   for (int p = 0; p < nsplit; ++p) s += part[((int64_t)p * ntiles + tile) * (GT * GT) + e];
-  S[i * lds + j] += s;
-  if (a != b) S[j * lds + i] += s;
+  if (overwrite) {
+    S[i * lds + j] = s;
+    if (a != b) S[j * lds + i] = s;
+  } else {
+    S[i * lds + j] += s;
+    if (a != b) S[j * lds + i] += s;
+  }
+}
+
+__global__ void hess_zero_kernel(double* __restrict__ S, int64_t count) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * blockDim.x)
+    S[e] = 0.0;
 }
 
 static void hess_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit, int64_t& tps) {
@@ -142,13 +160,23 @@ extern "C" size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_to
 }
 
 extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, const float* X,
-                                               int64_t n_tokens, int64_t ldx, void* ws,
-                                               size_t ws_bytes, void* stream) {
+                                               int64_t n_tokens, int64_t ldx, uint32_t flags,
+                                               void* ws, size_t ws_bytes, void* stream) {
   if (in_features < 0 || n_tokens < 0) return GPTQ_EINVAL;
-  if (in_features == 0 || n_tokens == 0) return GPTQ_OK;
-  if (!S || !X || ldx < in_features) return GPTQ_EINVAL;
+  if (flags & ~GPTQ_FLAG_HESSIAN_OVERWRITE) return GPTQ_EINVAL;
+  const bool overwrite = (flags & GPTQ_FLAG_HESSIAN_OVERWRITE) != 0;
+  if (in_features == 0 || (n_tokens == 0 && !overwrite)) return GPTQ_OK;
+  if (!S) return GPTQ_EINVAL;
   if (in_features > (int64_t)1 << 20) return GPTQ_EINVAL;
   hipStream_t st = (hipStream_t)stream;
+  if (n_tokens == 0) {
+    const int64_t cnt = in_features * in_features;
+    GPTQ_LAUNCH(K_FILL, st,
+                hess_zero_kernel<<<(unsigned)std::min<int64_t>(cdiv(cnt, 256), 65536), 256, 0, st>>>(
+                    S, cnt));
+    return GPTQ_OK;
+  }
+  if (!X || ldx < in_features) return GPTQ_EINVAL;
   int nt, ntiles, nsplit;
   int64_t tps;
   hess_plan(in_features, n_tokens, nt, ntiles, nsplit, tps);
@@ -162,12 +190,13 @@ extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, c
   const int nblocks = ntiles * nsplit;
   GPTQ_LAUNCH(K_HESS_TILE, st,
               hess_tile_kernel<<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt, ntiles, tps,
-                                                        S, in_features, part, vec));
+                                                        S, in_features, part, vec,
+                                                        overwrite));
   if (part) {
     dim3 grid(GT * GT / 256, ntiles);
     GPTQ_LAUNCH(K_HESS_REDUCE, st,
                 hess_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, nt, ntiles, in_features, S,
-                                                         in_features));
+                                                         in_features, overwrite));
   }
   return GPTQ_OK;
 }

@@ -344,9 +344,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     GPTQ_LAUNCH(K_PREP_UOUT, st, prep_uout_kernel<<<grid, 256, 0, st>>>(Xb, ip, n, U));
   }
   unsigned h_status = 0;
-  if (hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
-    return GPTQ_EHIP;
-  if (hipStreamSynchronize(st) != hipSuccess) return GPTQ_EHIP;
+  GPTQ_HIP(hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st));
+  GPTQ_HIP(hipStreamSynchronize(st));
   if (h_status & ST_NOTSPD) return GPTQ_ENOTSPD;
   return GPTQ_OK;
 }

@@ -466,9 +466,8 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
                                                         codes, g_idx, status));
   }
   unsigned h_status = 0;
-  if (hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st) != hipSuccess)
-    return GPTQ_EHIP;
-  if (hipStreamSynchronize(st) != hipSuccess) return GPTQ_EHIP;
+  GPTQ_HIP(hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st));
+  GPTQ_HIP(hipStreamSynchronize(st));
   if (h_status & ST_BADPERM) return GPTQ_EINVAL;
   if (h_status & ST_NONFINITE) return GPTQ_ENONFINITE;
   return GPTQ_OK;

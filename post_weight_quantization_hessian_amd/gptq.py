@@ -21,11 +21,12 @@ LIB_PATH = os.path.join(HERE, "libgptq.so")
 
 GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTSPD, GPTQ_EHIP, GPTQ_EWORKSPACE, GPTQ_ENONFINITE = range(6)
 GPTQ_FLAG_ACT_ORDER = 1
+GPTQ_FLAG_HESSIAN_OVERWRITE = 2
 
 EXPORTS = {
     "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
     "gptq_hessian_accumulate": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int64,
-                                          C.c_void_p, C.c_size_t, C.c_void_p]),
+                                          C.c_uint32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "gptq_prepare_workspace_bytes": (C.c_size_t, [C.c_int64]),
     "gptq_prepare_hinv": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_double, C.c_uint32,
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -37,7 +38,8 @@ EXPORTS = {
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
     "gptq_version": (C.c_int, []),
-    "gptq_profile_enable": (C.c_int, [C.c_int]),
+    "gptq_last_error_string": (C.c_char_p, []),
+    "gptq_profile_enable": (C.c_int, [C.c_uint32]),
     "gptq_profile_kernel_count": (C.c_int, []),
     "gptq_profile_kernel_name": (C.c_char_p, [C.c_int]),
     "gptq_profile_read": (C.c_int, [C.c_void_p, C.c_void_p]),
@@ -45,6 +47,11 @@ EXPORTS = {
 
 
 def _load():
+    # torch ships its own HIP runtime (same soname as /opt/rocm's). Import it
+    # first so that libgptq binds to that one runtime: loading libgptq first
+    # would map /opt/rocm's copy and torch would then load a second runtime
+    # in the same process, whose device pointers the first cannot use.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libgptq.so is not built ({LIB_PATH}); run "
                           "`python -m post_weight_quantization_hessian_amd.build`")
@@ -63,6 +70,8 @@ class GPTQError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         msg = lib.gptq_status_string(status).decode()
+        if status == GPTQ_EHIP:
+            msg += f" [{lib.gptq_last_error_string().decode()}]"
         super().__init__(f"{where}: {msg} (status {status})")
 
 
@@ -104,8 +113,9 @@ def hessian_workspace_bytes(in_features: int, n_tokens: int) -> int:
     return int(lib.gptq_hessian_workspace_bytes(in_features, n_tokens))
 
 
-def hessian_accumulate(S, X, workspace=None):
-    """S += X^T X (fp64 S [i x i], fp32 X [n x i], unit stride along i)."""
+def hessian_accumulate(S, X, workspace=None, overwrite=False):
+    """S += X^T X, or S = X^T X with ``overwrite`` (fp64 S [i x i], fp32 X
+    [n x i] with unit stride along i)."""
     torch = _torch()
     _need(S, torch.float64, "S", 2)
     _need(X, torch.float32, "X", 2)
@@ -116,7 +126,8 @@ def hessian_accumulate(S, X, workspace=None):
         raise ValueError("X rows must be contiguous")
     if workspace is None:
         workspace = _workspace(hessian_workspace_bytes(i, n), X.device)
-    st = lib.gptq_hessian_accumulate(_ptr(S), i, _ptr(X), n, X.stride(0) if n > 0 else i,
+    flags = GPTQ_FLAG_HESSIAN_OVERWRITE if overwrite else 0
+    st = lib.gptq_hessian_accumulate(_ptr(S), i, _ptr(X), n, X.stride(0) if n > 0 else i, flags,
                                      _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_hessian_accumulate")
     return S
@@ -167,8 +178,10 @@ def quantize_workspace_bytes(rows: int, cols: int, group_size: int) -> int:
     return int(lib.gptq_quantize_workspace_bytes(rows, cols, group_size))
 
 
-def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, workspace=None):
-    """Sweep the fp16 weights W [rows x cols] with the factor U (and perm)."""
+def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, workspace=None,
+                   out=None):
+    """Sweep the fp16 weights W [rows x cols] with the factor U (and perm).
+    ``out`` may be a QuantizedLayer whose tensors are reused."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(U, torch.float32, "U", 2)
@@ -183,11 +196,16 @@ def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, worksp
             raise ValueError("perm must have cols entries")
     ng = -(-cols // group_size) if group_size > 0 else 0
     dev = W.device
-    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    scales = torch.empty((rows, ng), dtype=torch.float16, device=dev)
-    zeros = torch.empty((rows, ng), dtype=torch.float16, device=dev)
-    g_idx = torch.empty(cols, dtype=torch.int32, device=dev)
-    row_loss = torch.empty(rows, dtype=torch.float64, device=dev)
+    if out is not None:
+        codes, scales, zeros, g_idx, row_loss = out.codes, out.scales, out.zeros, out.g_idx, out.row_loss
+        if codes.shape != (rows, cols) or scales.shape != (rows, ng) or row_loss.shape != (rows,):
+            raise ValueError("out tensors have the wrong shape")
+    else:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, ng), dtype=torch.float16, device=dev)
+        zeros = torch.empty((rows, ng), dtype=torch.float16, device=dev)
+        g_idx = torch.empty(cols, dtype=torch.int32, device=dev)
+        row_loss = torch.empty(rows, dtype=torch.float64, device=dev)
     if workspace is None:
         workspace = _workspace(quantize_workspace_bytes(rows, cols, group_size), dev)
     st = lib.gptq_quantize_layer(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
@@ -210,8 +228,22 @@ def fp16_round_host(values):
     return out
 
 
-def profile_enable(on: bool = True):
-    _check(lib.gptq_profile_enable(1 if on else 0), "gptq_profile_enable")
+def kernel_names():
+    return [lib.gptq_profile_kernel_name(k).decode() for k in range(lib.gptq_profile_kernel_count())]
+
+
+def profile_enable(kernels=True):
+    """True: time every kernel; False/None: off; or an iterable of kernel names."""
+    if kernels is True:
+        mask = 0xFFFFFFFF
+    elif not kernels:
+        mask = 0
+    else:
+        names = kernel_names()
+        mask = 0
+        for k in kernels:
+            mask |= 1 << names.index(k)
+    _check(lib.gptq_profile_enable(mask), "gptq_profile_enable")
 
 
 def profile_read() -> dict:

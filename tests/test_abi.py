@@ -98,10 +98,12 @@ def test_invalid_arguments_rejected_on_host():
     assert pw(FAKE, 0, 10, 0.01, 0, NULL, NULL, NULL, 0, NULL) == g.GPTQ_OK
     # hessian
     ha = L.gptq_hessian_accumulate
-    assert ha(NULL, 8, FAKE, 10, 8, NULL, 0, NULL) == g.GPTQ_EINVAL
-    assert ha(FAKE, 8, FAKE, 10, 7, NULL, 0, NULL) == g.GPTQ_EINVAL
-    assert ha(FAKE, 8, NULL, 0, 8, NULL, 0, NULL) == g.GPTQ_OK  # no tokens: no-op
-    assert ha(FAKE, -1, FAKE, 10, 8, NULL, 0, NULL) == g.GPTQ_EINVAL
+    assert ha(NULL, 8, FAKE, 10, 8, 0, NULL, 0, NULL) == g.GPTQ_EINVAL
+    assert ha(FAKE, 8, FAKE, 10, 7, 0, NULL, 0, NULL) == g.GPTQ_EINVAL
+    assert ha(FAKE, 8, NULL, 0, 8, 0, NULL, 0, NULL) == g.GPTQ_OK  # no tokens: no-op
+    assert ha(FAKE, -1, FAKE, 10, 8, 0, NULL, 0, NULL) == g.GPTQ_EINVAL
+    assert ha(FAKE, 8, FAKE, 10, 8, 4, NULL, 0, NULL) == g.GPTQ_EINVAL  # unknown flag
+    assert ha(NULL, 8, FAKE, 0, 8, 2, NULL, 0, NULL) == g.GPTQ_EINVAL  # overwrite needs S
 
 
 def test_profile_api_without_launches():

@@ -78,6 +78,20 @@ def test_hessian_matches_oracle(n, dim, use_ws):
     assert np.array_equal(Sg, Sg.T)
 
 
+def test_hessian_overwrite_ignores_old_contents():
+    say("hessian overwrite")
+    rng = np.random.default_rng(8)
+    for n, dim in [(700, 300), (64, 129)]:  # split and unsplit plans
+        X = rng.standard_normal((n, dim)).astype(np.float32)
+        S = torch.full((dim, dim), float("nan"), dtype=torch.float64, device=DEV)
+        G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
+        Sr, _ = O.hessian_sum(X)
+        np.testing.assert_allclose(S.cpu().numpy(), Sr, rtol=1e-12, atol=1e-9)
+    S = torch.full((50, 50), 3.0, dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, torch.zeros((0, 50), dtype=torch.float32, device=DEV), overwrite=True)
+    assert torch.all(S == 0)
+
+
 def test_hessian_unaligned_rows_and_exact_entries():
     say("hessian strided X")
     rng = np.random.default_rng(5)
