@@ -28,7 +28,8 @@ METRIC = ("quantized weights/sec per layer + XXáµ€/trailing-GEMM % MFMA peak, 1Ã
 DEFAULT_WORKLOAD = "qwen05b_mlp"
 
 # MI355X published peaks
-PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0}
+PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0,
+        "f64_vector": 78.6}
 
 
 def parse():
@@ -51,7 +52,7 @@ def kernel_work(name, wl, plan):
     if name == "hessian_tile":
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
         return f, "flop", "f64_mfma"
-    if name in ("chol_syrk", "chol_trsm", "trtri_update", "trtri_row"):
+    if name in ("chol_syrk", "chol_trsm"):
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
@@ -59,13 +60,27 @@ def kernel_work(name, wl, plan):
                 m = nt - 1 - p
                 if name == "chol_syrk":
                     f += 2 * 128 ** 3 * m * (m + 1) / 2
-                elif name == "chol_trsm":
-                    f += 2 * 128 ** 3 * m
-                elif name == "trtri_update":
-                    f += 2 * 128 ** 3 * m * (p + 1)
                 else:
-                    f += 2 * 128 ** 3 * p
+                    f += 2 * 128 ** 3 * m
         return f, "flop", "f64_mfma"
+    if name in ("trtri_t", "trtri_x"):
+        # X21 = -X22 (L21 X11) at each doubling level, triangular zeros skipped
+        f = 0.0
+        for h in plan:
+            nt = -(-h.dim // 128)
+            hh = 1
+            while hh < nt:
+                for q0 in range(0, nt, 2 * hh):
+                    h2 = min(hh, nt - q0 - hh)
+                    for r in range(max(h2, 0)):
+                        for c in range(hh):
+                            f += 2 * 128 ** 3 * ((hh - c) if name == "trtri_t" else (r + 1))
+                hh *= 2
+        return f, "flop", "f64_mfma"
+    if name == "chol_potrf":
+        # 128x128 diagonal block: Cholesky (n^3/3) and triangular inverse (n^3/3)
+        f = sum(-(-h.dim // 128) for h in plan) * 2 * 128 ** 3 / 3.0
+        return f, "flop", "f64_vector"
     if name == "quant_gemm":
         f = 0.0
         for h in plan:
@@ -224,7 +239,8 @@ def main():
         if unit == "flop":
             achieved = work / per_step_s / 1e12
             peak = PEAK[peak_key]
-            roofline = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            roofline = {"bound": "alu" if peak_key == "f64_vector" else "mfma",
+                        "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                         "frac": achieved / peak, "traffic": None,
                         "kernel": dominant, "precision": peak_key,
                         "launches_per_step": dom_launches / args.steps,

@@ -9,8 +9,9 @@ namespace gptq {
 
 static const char* const kKernelNames[K_COUNT] = {
     "hessian_tile", "hessian_reduce", "prepare_diag", "prepare_perm", "prepare_gather",
-    "chol_potrf", "chol_trsm", "chol_syrk", "trtri_row", "trtri_update", "prepare_uout",
-    "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill"};
+    "chol_potrf", "chol_trsm", "chol_syrk", "trtri_t", "trtri_x", "prepare_uout",
+    "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill",
+    "quant_reduce"};
 
 struct ProfRec {
   int kid;

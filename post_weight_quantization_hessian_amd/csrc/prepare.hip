@@ -89,82 +89,249 @@ __global__ __launch_bounds__(256) void prep_gather_kernel(const double* __restri
 }
 
 // ---------------------------------------------------------------- Cholesky
+//
+// Diagonal 128x128 block of panel p: factor and invert it in LDS, 16 columns
+// at a time. The block is held as the 36 lower 16x16 tiles, each stored
+// column-major with pitch 17 (conflict-free MFMA fragment reads). Per 16-wide
+// step s: one wave factors the 16x16 diagonal tile (no workgroup barrier
+// inside), all threads solve the rows below against it by substitution, and
+// the waves update the trailing tiles with fp64 MFMA. The inverse then takes
+// the eight 16x16 diagonal inverses (one wave each) and assembles the
+// off-diagonal tiles by distance from the diagonal:
+//     X_ij = -X_ii * sum_{k=j}^{i-1} L_ik X_kj.
 
-__device__ inline int pk(int i, int k) { return (i * (i + 1)) / 2 + k; }  // packed lower
+constexpr int PT = 17;        // tile pitch (column-major)
+constexpr int PTS = 16 * PT;  // doubles per tile
+constexpr int NPT = 36;       // lower tiles of an 8x8 tile grid
 
-// Factor the 128x128 diagonal block of panel p in LDS (right-looking), write
-// L11 back, and its inverse (zeros above the diagonal) to Dinv. A pivot that
-// is not positive and finite sets ST_NOTSPD and is replaced by 1.
-__global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K, int64_t ld, int p,
-                                                         double* __restrict__ Dinv,
-                                                         unsigned* __restrict__ status) {
-  __shared__ double Lp[GT * (GT + 1) / 2];
-  __shared__ double Xp[GT * (GT + 1) / 2];
-  const int t = threadIdx.x, ty = t >> 4, tx = t & 15;
-  const int64_t c0 = (int64_t)p * GT;
-  for (int e = t; e < GT * GT; e += 256) {
-    const int i = e >> 7, k = e & 127;
-    if (k <= i) Lp[pk(i, k)] = K[(c0 + i) * ld + c0 + k];
-  }
-  for (int e = t; e < GT * (GT + 1) / 2; e += 256) Xp[e] = 0.0;
-  __syncthreads();
-  bool bad = false;
-  for (int j = 0; j < GT; ++j) {
-    double d = Lp[pk(j, j)];
+__device__ inline int ptile(int I, int K) { return (I * (I + 1) / 2 + K) * PTS; }
+
+// Order the LDS accesses of one wave (they execute in order in hardware).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ inline double readlane_f64(double v, int lane) {
+  union { double d; int i[2]; } a;
+  a.d = v;
+  a.i[0] = __builtin_amdgcn_readlane(a.i[0], lane);
+  a.i[1] = __builtin_amdgcn_readlane(a.i[1], lane);
+  return a.d;
+}
+
+// One wave: in-place Cholesky of the 16x16 tile T (lower part), 1/diag to
+// invd. The tile lives in registers in the MFMA accumulator layout (lane l:
+// column l & 15, rows (l >> 4) + 4m); column j is handed to the other lanes
+// through the 16-entry LDS buffer col.
+__device__ inline void factor16(double* T, double* invd, double* col, int lane, bool& bad) {
+  const int g = lane >> 4, c = lane & 15;
+  double a[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) a[m] = T[c * PT + g + 4 * m];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    double d = readlane_f64(a[j >> 2], 16 * (j & 3) + j);
     if (!(d > 0.0) || !isfinite(d)) {
       bad = true;
       d = 1.0;
     }
     const double ljj = sqrt(d);
-    for (int i = j + 1 + t; i < GT; i += 256) Lp[pk(i, j)] /= ljj;
-    __syncthreads();
-    if (t == 0) Lp[pk(j, j)] = ljj;
-    const int n = GT - 1 - j;
-    for (int r = ty; r < n; r += 16) {
-      const int i = j + 1 + r;
-      const double lij = Lp[pk(i, j)];
-      for (int cc = tx; cc <= r; cc += 16) {
-        const int k = j + 1 + cc;
-        Lp[pk(i, k)] -= lij * Lp[pk(k, j)];
+    const double inv = 1.0 / ljj;
+    if (c == j) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int row = g + 4 * m;
+        if (row > j) a[m] *= inv;
+        else if (row == j) a[m] = ljj;
+        col[row] = row > j ? a[m] : 0.0;
       }
     }
-    __syncthreads();
+    if (lane == 0) invd[j] = inv;
+    wave_lds_sync();
+    // col[] is zero at and above row j, so the rank-1 update needs no
+    // predicate on the lower part; above the diagonal it only touches
+    // entries that are never read.
+    const double ck = col[c];
+    double cr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) cr[m] = col[g + 4 * m];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] -= cr[m] * ck;
+    wave_lds_sync();
   }
-  // X = L^-1, right-looking: row i of X from the accumulated right-hand side,
-  // then remove its contribution from the rows below.
-  for (int i = 0; i < GT; ++i) {
-    const double lii = Lp[pk(i, i)];
-    for (int j = t; j <= i; j += 256) Xp[pk(i, j)] = ((j == i ? 1.0 : 0.0) + Xp[pk(i, j)]) / lii;
-    __syncthreads();
-    for (int r = ty; r < GT - 1 - i; r += 16) {
-      const int m = i + 1 + r;
-      const double lmi = Lp[pk(m, i)];
-      for (int j = tx; j <= i; j += 16) Xp[pk(m, j)] -= lmi * Xp[pk(i, j)];
-    }
-    __syncthreads();
-  }
-  double* D = Dinv + (int64_t)p * GT * GT;
-  for (int e = t; e < GT * GT; e += 256) {
-    const int i = e >> 7, k = e & 127;
-    if (k <= i) {
-      K[(c0 + i) * ld + c0 + k] = Lp[pk(i, k)];
-      D[e] = Xp[pk(i, k)];
-    } else {
-      D[e] = 0.0;
-    }
-  }
-  if (bad && t == 0) atomicOr(status, ST_NOTSPD);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) T[c * PT + g + 4 * m] = a[m];
 }
 
-// L21 = A21 * Dinv^T for row block m below panel p (in place).
-__global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K, int64_t ld, int p,
-                                                        const double* __restrict__ Dinv) {
+// One wave: X = L^-1 for the lower 16x16 tile L (rinv = 1/diag L), written to
+// the tile X (zeros above the diagonal). Row i of X is finished from the
+// accumulated right-hand side, handed over through the LDS buffer rowb, and
+// removed from the rows below.
+__device__ inline void inverse16(const double* L, const double* rinv, double* X, double* rowb,
+                                 int lane) {
+  const int g = lane >> 4, c = lane & 15;
+  double x[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (g == (i & 3)) {
+      double v = 0.0;
+      if (c <= i) v = ((c == i ? 1.0 : 0.0) + x[i >> 2]) * rinv[i];
+      x[i >> 2] = v;
+      rowb[c] = v;
+    }
+    wave_lds_sync();
+    const double xic = rowb[c];
+    double lv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) lv[m] = L[i * PT + g + 4 * m];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const double nv = x[m] - lv[m] * xic;
+      x[m] = (g + 4 * m > i) ? nv : x[m];
+    }
+    wave_lds_sync();
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) X[c * PT + g + 4 * m] = x[m];
+}
+
+__global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K, double* __restrict__ Xb,
+                                                         int64_t ld, int p,
+                                                         unsigned* __restrict__ status) {
+  __shared__ double A[NPT * PTS];
+  __shared__ double X[NPT * PTS];
+  __shared__ double invd[8][16];   // 1 / diag of each 16x16 diagonal tile
+  __shared__ double xbuf[4][16];   // per-wave column / row hand-over buffers
+  __shared__ int bad_any;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t c0 = (int64_t)p * GT;
+  if (t == 0) bad_any = 0;
+  // 64 elements per thread, loaded 16 at a time so the loads overlap
+  for (int e0 = 0; e0 < GT * GT; e0 += 16 * 256) {
+    double v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + u * 256 + t;
+      const int r = e >> 7, c = e & 127;
+      v[u] = c <= r ? K[(c0 + r) * ld + c0 + c] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = e0 + u * 256 + t;
+      const int r = e >> 7, c = e & 127;
+      if (c <= r) A[ptile(r >> 4, c >> 4) + (c & 15) * PT + (r & 15)] = v[u];
+    }
+  }
+  for (int e = t; e < NPT * PTS; e += 256) X[e] = 0.0;
+  __syncthreads();
+
+  bool bad = false;
+  for (int s = 0; s < 8; ++s) {
+    if (wave == 0) factor16(A + ptile(s, s), invd[s], xbuf[0], lane, bad);
+    __syncthreads();
+    // rows below the diagonal tile: x L_ss^T = a  (forward substitution)
+    if (t >= 16 * (s + 1) && t < GT) {
+      double* T = A + ptile(t >> 4, s);
+      const double* Ls = A + ptile(s, s);
+      const int ri = t & 15;
+      double x[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) x[c] = T[c * PT + ri];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        x[c] *= invd[s][c];
+#pragma unroll
+        for (int m = c + 1; m < 16; ++m) x[m] -= x[c] * Ls[c * PT + m];
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) T[c * PT + ri] = x[c];
+    }
+    __syncthreads();
+    // trailing tiles (I, Kc), s < Kc <= I < 8: A_IK -= L_Is L_Ks^T
+    const int m = 7 - s;
+    const int cnt = m * (m + 1) / 2;
+    for (int u = wave; u < cnt; u += 4) {
+      int a = 0;
+      while ((a + 1) * (a + 2) / 2 <= u) ++a;
+      const int I = s + 1 + a, Kc = s + 1 + (u - a * (a + 1) / 2);
+      double* C = A + ptile(I, Kc);
+      const double* Li = A + ptile(I, s);
+      const double* Lk = A + ptile(Kc, s);
+      d4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = C[(lane & 15) * PT + (lane >> 4) + 4 * r];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int q = (lane >> 4) + 4 * kk;
+        const double av = -Li[q * PT + (lane & 15)];
+        const double bv = Lk[q * PT + (lane & 15)];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) C[(lane & 15) * PT + (lane >> 4) + 4 * r] = acc[r];
+    }
+    __syncthreads();
+  }
+  if (bad) atomicOr(&bad_any, 1);
+
+  // inverse: diagonal tiles, then off-diagonal tiles by distance
+  for (int i = wave; i < 8; i += 4)
+    inverse16(A + ptile(i, i), invd[i], X + ptile(i, i), xbuf[wave], lane);
+  __syncthreads();
+  for (int d = 1; d < 8; ++d) {
+    for (int i = d + wave; i < 8; i += 4) {
+      const int j = i - d;
+      d4 acc = d4{0.0, 0.0, 0.0, 0.0};
+      for (int k = j; k < i; ++k) {
+        const double* Lik = A + ptile(i, k);
+        const double* Xkj = X + ptile(k, j);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int q = (lane >> 4) + 4 * kk;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(Lik[q * PT + (lane & 15)],
+                                                     Xkj[(lane & 15) * PT + q], acc, 0, 0, 0);
+        }
+      }
+      const double* Xii = X + ptile(i, i);
+      d4 out = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int q = (lane >> 4) + 4 * kk;
+        out = __builtin_amdgcn_mfma_f64_16x16x4f64(Xii[q * PT + (lane & 15)], acc[kk], out, 0, 0, 0);
+      }
+      double* Xij = X + ptile(i, j);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Xij[(lane & 15) * PT + (lane >> 4) + 4 * r] = -out[r];
+    }
+    __syncthreads();
+  }
+  // L11 back into K (lower), X11 into the diagonal block of Xb (zeros above)
+  for (int e = t; e < GT * GT; e += 256) {
+    const int r = e >> 7, c = e & 127;
+    const int off = ptile(r >> 4, c >> 4) + (c & 15) * PT + (r & 15);
+    if (c <= r) {
+      K[(c0 + r) * ld + c0 + c] = A[off];
+      Xb[(c0 + r) * ld + c0 + c] = X[off];
+    } else {
+      Xb[(c0 + r) * ld + c0 + c] = 0.0;
+    }
+  }
+  if (t == 0 && bad_any) atomicOr(status, ST_NOTSPD);
+}
+
+// L21 = A21 * X11^T for row block m below panel p (in place); X11 = L11^-1
+// is the diagonal block of Xb written by chol_potrf_kernel.
+__global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
+                                                        const double* __restrict__ Xb, int64_t ld,
+                                                        int p) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
   const int64_t c0 = (int64_t)p * GT;
   const int64_t r0 = c0 + GT + (int64_t)blockIdx.x * GT;
   LdTrans64 la{K + r0 * ld + c0, ld, {}};
-  LdTrans64 lb{Dinv + (int64_t)p * GT * GT, GT, {}};
+  LdTrans64 lb{Xb + c0 * ld + c0, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
   gemm64_loop(la, lb, false, GT / GK, sA, sB, acc);
@@ -191,45 +358,70 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, 
 }
 
 // ---------------------------------------------------------------- inverse
+//
+// X = L^-1 by recursive doubling over the 128-tile grid. At level h (a power
+// of two) the tile range is cut into blocks of 2h tiles; in every block the
+// inverses X11 (first h tiles) and X22 (the rest) are complete, and
+//     X21 = -X22 * (L21 * X11)
+// finishes the block. All blocks of a level are independent: one launch for
+// T = L21 X11 and one for X21 = -X22 T, with the triangular zeros of X11 and
+// X22 skipped in the K ranges.
 
-// Step i of the blocked right-looking inverse X = L^-1 (X in Xb, ld ip):
-// X[i][j] = Dinv_i * B[i][j] for j < i (B accumulated in place), X[i][i] = Dinv_i.
-__global__ __launch_bounds__(256) void trtri_row_kernel(double* __restrict__ Xb, int64_t ld, int i,
-                                                        const double* __restrict__ Dinv) {
-  __shared__ double sA[2 * GCH];
-  __shared__ double sB[2 * GCH];
-  const int j = blockIdx.x;
-  const double* D = Dinv + (int64_t)i * GT * GT;
-  double* blk = Xb + (int64_t)i * GT * ld + (int64_t)j * GT;
-  if (j == i) {
-    for (int e = threadIdx.x; e < GT * GT; e += 256) blk[(e >> 7) * ld + (e & 127)] = D[e];
-    return;
-  }
-  LdTrans64 la{D, GT, {}};
-  LdDirect64 lb{blk, ld, {}};
-  d4 acc[4][4];
-  zero_acc(acc);
-  gemm64_loop(la, lb, false, GT / GK, sA, sB, acc);
-  for_each_acc(acc, [&](int r, int c, double v) { blk[r * ld + c] = v; });
+__device__ inline void level_tile(int id, int h, int nt, int& q, int& r, int& c, int64_t& f0,
+                                  int64_t& s0) {
+  const int nq = (nt + 2 * h - 1) / (2 * h);
+  q = id / (h * h);
+  if (q > nq - 1) q = nq - 1;
+  const int rem = id - q * h * h;
+  r = rem / h;
+  c = rem % h;
+  f0 = (int64_t)q * 2 * h;
+  s0 = f0 + h;
 }
 
-// B[m][j] -= L[m][i] * X[i][j] for block rows m > i, block columns j <= i.
-__global__ __launch_bounds__(256) void trtri_update_kernel(double* __restrict__ Xb,
-                                                           const double* __restrict__ K, int64_t ld,
-                                                           int i) {
+__global__ __launch_bounds__(256) void trtri_t_kernel(const double* __restrict__ K,
+                                                      const double* __restrict__ Xb,
+                                                      double* __restrict__ Tb, int64_t ld, int h,
+                                                      int nt) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int ncol = i + 1;
-  const int m = i + 1 + id / ncol;
-  const int j = id % ncol;
-  LdTrans64 la{K + (int64_t)m * GT * ld + (int64_t)i * GT, ld, {}};
-  LdDirect64 lb{Xb + (int64_t)i * GT * ld + (int64_t)j * GT, ld, {}};
+  int q, r, c;
+  int64_t f0, s0;
+  level_tile(xcd_remap(blockIdx.x, gridDim.x), h, nt, q, r, c, f0, s0);
+  // T[r][c] = sum_{k=c}^{h-1} L[s0+r][f0+k] X[f0+k][f0+c]
+  LdTrans64 la{K + (s0 + r) * GT * ld + (f0 + c) * GT, ld, {}};
+  LdDirect64 lb{Xb + (f0 + c) * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop(la, lb, false, GT / GK, sA, sB, acc);
-  double* blk = Xb + (int64_t)m * GT * ld + (int64_t)j * GT;
-  for_each_acc(acc, [&](int r, int c, double v) { blk[r * ld + c] -= v; });
+  gemm64_loop(la, lb, false, (h - c) * (GT / GK), sA, sB, acc);
+  double* out = Tb + (s0 + r) * GT * ld + (f0 + c) * GT;
+  for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
+}
+
+__global__ __launch_bounds__(256) void trtri_x_kernel(double* __restrict__ Xb,
+                                                      const double* __restrict__ Tb, int64_t ld,
+                                                      int h, int nt) {
+  __shared__ double sA[2 * GCH];
+  __shared__ double sB[2 * GCH];
+  int q, r, c;
+  int64_t f0, s0;
+  level_tile(xcd_remap(blockIdx.x, gridDim.x), h, nt, q, r, c, f0, s0);
+  // X[s0+r][f0+c] = -sum_{k=0}^{r} X[s0+r][s0+k] T[s0+k][f0+c]
+  LdTrans64 la{Xb + (s0 + r) * GT * ld + s0 * GT, ld, {}};
+  LdDirect64 lb{Tb + s0 * GT * ld + (f0 + c) * GT, ld, {}};
+  d4 acc[4][4];
+  zero_acc(acc);
+  gemm64_loop(la, lb, false, (r + 1) * (GT / GK), sA, sB, acc);
+  double* out = Xb + (s0 + r) * GT * ld + (f0 + c) * GT;
+  for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = -v; });
+}
+
+static int level_tiles(int h, int nt) {
+  const int nq = (nt + 2 * h - 1) / (2 * h);
+  const int last2 = nt - (nq - 1) * 2 * h - h;  // second-half tiles of the last block
+  int tiles = (nq - 1) * h * h;
+  if (last2 > 0) tiles += last2 * h;
+  return tiles;
 }
 
 // U[j][k] = X[n-1-j][n-1-k] (k >= j), 0 below the diagonal; fp32.
@@ -243,19 +435,13 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
   }
 }
 
-__global__ void fill_kernel(double* __restrict__ p, int64_t n, double v) {
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
-       e += (int64_t)gridDim.x * blockDim.x)
-    p[e] = v;
-}
-
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
 // ---------------------------------------------------------------- layout
 
 struct PrepLayout {
   int64_t n, ip, nt;
-  size_t off_status, off_lam, off_hd, off_K, off_X, off_D, total;
+  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, total;
 };
 
 static PrepLayout prep_layout(int64_t n) {
@@ -274,7 +460,7 @@ static PrepLayout prep_layout(int64_t n) {
   L.off_hd = take(8 * (size_t)n);
   L.off_K = take(8 * (size_t)L.ip * L.ip);
   L.off_X = take(8 * (size_t)L.ip * L.ip);
-  L.off_D = take(8 * (size_t)L.nt * GT * GT);
+  L.off_T = take(L.nt > 1 ? 8 * (size_t)L.ip * L.ip : 8);
   L.total = o;
   return L;
 }
@@ -306,7 +492,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   double* hd = (double*)(base + L.off_hd);
   double* K = (double*)(base + L.off_K);
   double* Xb = (double*)(base + L.off_X);
-  double* Dinv = (double*)(base + L.off_D);
+  double* Tb = (double*)(base + L.off_T);
   const int64_t n = in_features, ip = L.ip;
   const int nt = (int)L.nt;
   const double c = 2.0 / (double)n_tokens_total;
@@ -319,25 +505,17 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   GPTQ_LAUNCH(K_PREP_GATHER, st,
               prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, perm, K));
   for (int p = 0; p < nt; ++p) {
-    GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, ip, p, Dinv, status));
+    GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Xb, ip, p, status));
     const int mt = nt - 1 - p;
     if (mt > 0) {
-      GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, ip, p, Dinv));
+      GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, Xb, ip, p));
       GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<mt * (mt + 1) / 2, 256, 0, st>>>(K, ip, p));
     }
   }
-  {
-    const int64_t cnt = ip * ip;
-    GPTQ_LAUNCH(K_FILL, st,
-                fill_kernel<<<(unsigned)std::min<int64_t>(cdiv(cnt, 256), 65535 * 4), 256, 0, st>>>(
-                    Xb, cnt, 0.0));
-  }
-  for (int i = 0; i < nt; ++i) {
-    GPTQ_LAUNCH(K_TRTRI_ROW, st, trtri_row_kernel<<<i + 1, 256, 0, st>>>(Xb, ip, i, Dinv));
-    if (i + 1 < nt) {
-      const int nb = (nt - 1 - i) * (i + 1);
-      GPTQ_LAUNCH(K_TRTRI_UPDATE, st, trtri_update_kernel<<<nb, 256, 0, st>>>(Xb, K, ip, i));
-    }
+  for (int h = 1; h < nt; h *= 2) {
+    const int tiles = level_tiles(h, nt);
+    GPTQ_LAUNCH(K_TRTRI_ROW, st, trtri_t_kernel<<<tiles, 256, 0, st>>>(K, Xb, Tb, ip, h, nt));
+    GPTQ_LAUNCH(K_TRTRI_UPDATE, st, trtri_x_kernel<<<tiles, 256, 0, st>>>(Xb, Tb, ip, h, nt));
   }
   {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)std::min<int64_t>(n, 65535));

@@ -18,6 +18,7 @@
 namespace gptq {
 
 constexpr int QB = 128;  // sweep block width
+typedef double dbl2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- helpers
 
@@ -115,9 +116,11 @@ constexpr int QU_LD = 160;  // Us row pitch (floats)
 
 __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E, int64_t lde,
                                                      const float* __restrict__ U, int64_t ldu,
+                                                     const uint16_t* __restrict__ W, int64_t ldw,
                                                      int64_t rows, int64_t j0, int bw,
                                                      int64_t ksplit, double* __restrict__ part,
-                                                     int64_t part_stride, bool vecU) {
+                                                     int64_t part_stride,
+                                                     double* __restrict__ wblk, bool vecU) {
   __shared__ float Es[2][64 * QE_LD];
   __shared__ float Us[2][32 * QU_LD];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -206,15 +209,58 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
       __syncthreads();
     }
   }
-  double* P = part + (int64_t)p * part_stride;
+  const int P = gridDim.y;
+  const int col = w * 32 + (lane & 31);
+  if (P == 1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int64_t row = r0 + 32 * i + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+        if (row < rows && col < bw)
+          wblk[row * QB + col] = f16_to_f64(W[row * ldw + j0 + col]) - acc64[i][x];
+      }
+    return;
+  }
+  double* Pp = part + (int64_t)p * part_stride;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
       const int64_t row = r0 + 32 * i + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-      const int col = w * 32 + (lane & 31);
-      if (row < rows) P[row * QB + col] = acc64[i][x];
+      if (row < rows) Pp[row * QB + col] = acc64[i][x];
     }
+}
+
+// wblk = W[:, blk] - sum_p part[p] for the split-K partials, summed in split
+// order (reproducible). Two adjacent columns per thread.
+__global__ __launch_bounds__(256) void q_reduce_kernel(const double* __restrict__ part, int P,
+                                                       int64_t part_stride,
+                                                       const uint16_t* __restrict__ W, int64_t ldw,
+                                                       int64_t rows, int64_t j0, int bw,
+                                                       double* __restrict__ wblk) {
+  const int64_t e2 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair index
+  const int64_t row = e2 / (QB / 2);
+  const int c = (int)(e2 % (QB / 2)) * 2;
+  if (row >= rows) return;
+  const int64_t off = row * QB + c;
+  dbl2_t sum = {0.0, 0.0};
+  for (int q = 0; q < P; q += 4) {
+    dbl2_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = q + u < P ? *reinterpret_cast<const dbl2_t*>(part + (int64_t)(q + u) * part_stride + off)
+                       : dbl2_t{0.0, 0.0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q + u < P) {
+        sum.x += v[u].x;
+        sum.y += v[u].y;
+      }
+  }
+  const uint16_t* wr = W + row * ldw + j0;
+  if (c < bw) wblk[off] = f16_to_f64(wr[c]) - sum.x;
+  if (c + 1 < bw) wblk[off + 1] = f16_to_f64(wr[c + 1]) - sum.y;
 }
 
 // ---------------------------------------------------------------- sweep
@@ -222,25 +268,57 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
 // One block of columns [j0, j0+bw). 16 rows per wave (4 lanes per row).
 template <int GS>
 __global__ __launch_bounds__(256) void q_sweep_kernel(
-    const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ part, int P,
-    int64_t part_stride, const float* __restrict__ U, int64_t ldu, int64_t rows, int64_t j0, int bw,
+    const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
+    const float* __restrict__ U, int64_t ldu, bool vecU, int64_t rows, int64_t j0, int bw,
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
     double* __restrict__ row_loss, unsigned* __restrict__ status) {
-  __shared__ double Us[QB * QB];
+  // U slab plus one zero row of padding: slot addresses run up to 3 columns
+  // past the end of a row (into the next row or the padding) for slots that
+  // are past the block end and never used.
+  __shared__ double Us[QB * QB + QB];
+  __shared__ double rdiag[QB];  // 1 / U[j][j]
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int q4 = lane & 3;
-  const int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 2) + wv * 16 + (lane >> 2);
+  const int nthr = blockDim.x;
+  const int64_t r = (int64_t)blockIdx.x * (nthr >> 2) + wv * 16 + (lane >> 2);
   const bool rv = r < rows;
   const double maxq = (double)((1 << bits) - 1);
 
-  // U slab of this block (upper triangle), zero outside [0, bw).
-  for (int e = t; e < QB * QB; e += blockDim.x) {
-    const int a = e >> 7, c = e & 127;
-    Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] : 0.0;
+  // U slab of this block; U is zero below its diagonal. Zero outside [0, bw).
+  if (vecU && bw == QB) {
+    for (int e0 = 0; e0 < QB * QB / 4; e0 += 8 * nthr) {
+      f4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * nthr + t;  // float4 index
+        const int a = e >> 5, c4 = (e & 31) * 4;
+        v[u] = e < QB * QB / 4 ? *reinterpret_cast<const f4*>(U + (j0 + a) * ldu + j0 + c4)
+                               : f4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = e0 + u * nthr + t;
+        if (e < QB * QB / 4) {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) Us[e * 4 + x] = (double)v[u][x];
+        }
+      }
+    }
+  } else {
+    for (int e = t; e < QB * QB; e += nthr) {
+      const int a = e >> 7, c = e & 127;
+      Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] : 0.0;
+    }
   }
 
-  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk].
+  for (int j = t; j < QB; j += nthr) {
+    rdiag[j] = j < bw ? 1.0 / (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
+    Us[QB * QB + j] = 0.0;
+  }
+
+  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk], formed by
+  // the update GEMM (wblk); the first block reads the weights directly.
   double w[32];
   bool finite = true;
 #pragma unroll
@@ -248,16 +326,19 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
     const int c = 4 * s + q4;
     double v = 0.0;
     if (rv && c < bw) {
-      v = f16_to_f64(W[r * ldw + j0 + c]);
+      if (wblk) {
+        v = wblk[r * QB + c];
+      } else {
+        v = f16_to_f64(W[r * ldw + j0 + c]);
+      }
       finite = finite && isfinite(v);
-      for (int p = 0; p < P; ++p) v -= part[(int64_t)p * part_stride + r * QB + c];
     }
     w[s] = v;
   }
   if (!finite) atomicOr(status, ST_NONFINITE);
   __syncthreads();
 
-  double scale = 1.0, zero = 0.0, loss = 0.0;
+  double scale = 1.0, rscale = 1.0, zero = 0.0, loss = 0.0;
   const int nt4 = (bw + 3) >> 2;
   for (int tt = 0; tt < nt4; ++tt) {
     if (((4 * tt) % GS) == 0) {
@@ -284,6 +365,7 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
       } else {
         zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
       }
+      rscale = 1.0 / scale;
       if (rv && q4 == 0) {
         const int64_t g = (j0 + 4 * tt) / GS;
         scales[r * ldg + g] = sh;
@@ -296,10 +378,10 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
       if (j < bw) {
         // quantize slot 0 (meaningful on the owner lane q4 == jj)
         const double v = w[0];
-        double qf = rint(v / scale) + zero;
+        double qf = rint(v * rscale) + zero;
         qf = fmin(fmax(qf, 0.0), maxq);
         const double dq = scale * (qf - zero);
-        const double e = (v - dq) / Us[j * QB + j];
+        const double e = (v - dq) * rdiag[j];
         double eb;
         if (jj == 0) eb = quad_bcast<0>(e);
         else if (jj == 1) eb = quad_bcast<1>(e);
@@ -310,11 +392,30 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
           E[r * lde + j0 + j] = (float)e;
           loss += e * e;
         }
+        // Slot s holds column 4*(tt+s) + q4; slots past the block end are never
+        // used again. Whole groups of 8 such slots are skipped (uniform tests);
+        // inside a group the reads run past the row end into the next row or
+        // the padding, which only feeds dead slots.
         const double* urow = Us + j * QB + 4 * tt + q4;
-        if (q4 > jj) w[0] -= eb * urow[0];
+        {
+          const double u0 = urow[0];
+          const double nv = w[0] - eb * u0;
+          w[0] = q4 > jj ? nv : w[0];
+        }
 #pragma unroll
-        for (int s = 1; s < 32; ++s)
-          if (s < 32 - tt) w[s] -= eb * urow[4 * s];
+        for (int s = 1; s < 8; ++s) w[s] -= eb * urow[4 * s];
+        if (tt < 24) {
+#pragma unroll
+          for (int s = 8; s < 16; ++s) w[s] -= eb * urow[4 * s];
+        }
+        if (tt < 16) {
+#pragma unroll
+          for (int s = 16; s < 24; ++s) w[s] -= eb * urow[4 * s];
+        }
+        if (tt < 8) {
+#pragma unroll
+          for (int s = 24; s < 32; ++s) w[s] -= eb * urow[4 * s];
+        }
       }
     }
 #pragma unroll
@@ -331,12 +432,13 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
 struct QLayout {
   int64_t rows, cols, lde, ng;
   int pmax;
-  size_t off_status, off_invperm, off_wp, off_codes, off_E, off_part, total;
+  size_t off_status, off_invperm, off_wp, off_codes, off_E, off_part, off_wblk, total;
 };
 
+// Split-K factor of the update GEMM: about 512 workgroups in total.
 static int q_pmax(int64_t rows) {
   const int64_t rt = cdiv(rows, 64);
-  int64_t p = cdiv(2048, rt);
+  int64_t p = cdiv(512, rt);
   if (p > 16) p = 16;
   if (p < 1) p = 1;
   return (int)p;
@@ -361,20 +463,21 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
   L.off_codes = take((size_t)rows * cols);
   L.off_E = take(4 * (size_t)rows * L.lde);
   L.off_part = take(8 * (size_t)L.pmax * rows * QB);
+  L.off_wblk = take(8 * (size_t)rows * QB);
   L.total = o;
   return L;
 }
 
 template <int GS>
 static gptq_status launch_sweep(hipStream_t st, int nw, const uint16_t* Wsrc, int64_t ldws,
-                                const double* part, int P, int64_t pstride, const float* U,
-                                int64_t cols, int64_t rows, int64_t j0, int bw, int bits, float* E,
-                                int64_t lde, uint8_t* codes, int64_t ldc, uint16_t* scales,
-                                uint16_t* zeros, int64_t ldg, double* row_loss, unsigned* status) {
+                                const double* wblk, const float* U, int64_t cols, bool vecU,
+                                int64_t rows, int64_t j0, int bw, int bits, float* E, int64_t lde,
+                                uint8_t* codes, int64_t ldc, uint16_t* scales, uint16_t* zeros,
+                                int64_t ldg, double* row_loss, unsigned* status) {
   const unsigned nblk = (unsigned)cdiv(rows, 16 * nw);
   GPTQ_LAUNCH(K_Q_SWEEP, st,
-              q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, part, P, pstride, U, cols,
-                                                           rows, j0, bw, bits, E, lde, codes, ldc,
+              q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, wblk, U, cols, vecU, rows,
+                                                           j0, bw, bits, E, lde, codes, ldc,
                                                            scales, zeros, ldg, row_loss, status));
   return GPTQ_OK;
 }
@@ -432,29 +535,36 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
     ldws = cols;
     csw = codes_s;
   }
-  const int64_t waves = cdiv(rows, 16);
-  const int nw = waves > 512 ? 4 : (waves > 256 ? 2 : 1);
+  const int nw = 4;
   const bool vecU = (cols % 4 == 0) && ((uintptr_t)U % 16 == 0);
   const int64_t rt = cdiv(rows, 64);
+  double* wblk = (double*)(base + L.off_wblk);
   for (int64_t j0 = 0; j0 < cols; j0 += QB) {
     const int bw = (int)std::min<int64_t>(QB, cols - j0);
-    int P = 0;
+    const double* cur = nullptr;
     if (j0 > 0) {
       int64_t p = L.pmax;
-      if (p > j0 / 32) p = j0 / 32;
+      if (p > j0 / 128) p = j0 / 128;
       const int64_t ks = round_up(cdiv(j0, p), 32);
-      P = (int)cdiv(j0, ks);
+      const int P = (int)cdiv(j0, ks);
       dim3 grid((unsigned)rt, (unsigned)P);
       GPTQ_LAUNCH(K_Q_GEMM, st,
-                  q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, rows, j0, bw, ks, part,
-                                                      pstride, vecU));
+                  q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0, bw,
+                                                      ks, part, pstride, wblk, vecU));
+      if (P > 1) {
+        const int64_t pairs = rows * (QB / 2);
+        GPTQ_LAUNCH(K_Q_REDUCE, st,
+                    q_reduce_kernel<<<(unsigned)cdiv(pairs, 256), 256, 0, st>>>(
+                        part, P, pstride, Wsrc, ldws, rows, j0, bw, wblk));
+      }
+      cur = wblk;
     }
     gptq_status s;
     switch (group_size) {
-      case 16: s = launch_sweep<16>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      case 32: s = launch_sweep<32>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      case 64: s = launch_sweep<64>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      default: s = launch_sweep<128>(st, nw, Wsrc, ldws, part, P, pstride, U, cols, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 16: s = launch_sweep<16>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 32: s = launch_sweep<32>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 64: s = launch_sweep<64>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      default: s = launch_sweep<128>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
     }
     if (s != GPTQ_OK) return s;
   }
