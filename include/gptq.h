@@ -51,6 +51,9 @@ typedef enum {
 /* flags */
 #define GPTQ_FLAG_ACT_ORDER 1u          /* gptq_prepare_hinv: visit columns by descending diag H */
 #define GPTQ_FLAG_HESSIAN_OVERWRITE 2u  /* gptq_hessian_accumulate: S = X^T X instead of S += */
+#define GPTQ_FLAG_NO_SYNC 4u            /* prepare / quantize: return after enqueueing; the
+                                           device-side status stays in the workspace, read
+                                           it with gptq_workspace_status */
 
 /* ---------------------------------------------------------------------------
  * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's
@@ -87,9 +90,15 @@ gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
  *        factor with U^T U = (H[perm][:,perm])^-1, zeros below the diagonal.
  * Computed in fp64 (one Cholesky of the order-reversed permuted Hessian and
  * one triangular inverse), stored as fp32. S is read, never written.
+ * Part of the factorisation runs on a library-owned side stream tied to
+ * `stream` (default priority, created on first use for each caller stream and
+ * kept, ordered against `stream` with events); calls on the same `stream`
+ * from several host threads are serialized while they enqueue.
  * Workspace: gptq_prepare_workspace_bytes(in_features) bytes.
  * Synchronizes `stream` once at the end to read the factorisation status;
  * returns GPTQ_ENOTSPD if a pivot is <= 0 or not finite (U is then garbage).
+ * With GPTQ_FLAG_NO_SYNC it returns after enqueueing (argument errors are
+ * still returned at once) and the status is read by gptq_workspace_status.
  * ------------------------------------------------------------------------- */
 size_t gptq_prepare_workspace_bytes(int64_t in_features);
 gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_tokens_total,
@@ -121,16 +130,25 @@ gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_to
  *   row_loss fp64[rows]: sum_j e_j^2, e_j = (v_j - dequant_j)/U[j,j]; equals
  *            (w-q) H (w-q)^T for the damped, permuted H.
  * Workspace: gptq_quantize_workspace_bytes(rows, cols, group_size) bytes.
- * Synchronizes `stream` at the end; returns GPTQ_ENONFINITE if a weight is
- * NaN/Inf or a scale overflows fp16 (outputs are then unspecified).
+ * perm must be a permutation of 0..cols-1 (checked on the device: GPTQ_EINVAL).
+ * flags: 0 or GPTQ_FLAG_NO_SYNC. Synchronizes `stream` at the end unless
+ * GPTQ_FLAG_NO_SYNC; returns GPTQ_ENONFINITE if a weight is NaN/Inf or a
+ * scale overflows fp16 (outputs are then unspecified).
  * rows == 0 or cols == 0 is a no-op.
  * ------------------------------------------------------------------------- */
 size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int group_size);
 gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
                                 const float* U, const int32_t* perm, int bits, int group_size,
-                                uint8_t* codes, uint16_t* scales, uint16_t* zeros,
-                                int32_t* g_idx, double* row_loss,
+                                uint32_t flags, uint8_t* codes, uint16_t* scales,
+                                uint16_t* zeros, int32_t* g_idx, double* row_loss,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Status of the last gptq_prepare_hinv / gptq_quantize_layer call that used
+ * workspace `ws` (a device pointer): synchronizes `stream` (the stream of that
+ * call), then reads the status word the call left at the start of `ws`.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_workspace_status(const void* ws, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Utilities.

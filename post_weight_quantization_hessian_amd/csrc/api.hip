@@ -11,7 +11,7 @@ static const char* const kKernelNames[K_COUNT] = {
     "hessian_tile", "hessian_reduce", "prepare_diag", "prepare_perm", "prepare_gather",
     "chol_potrf", "chol_trsm", "chol_syrk", "trtri_t", "trtri_x", "prepare_uout",
     "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill",
-    "quant_reduce"};
+    "quant_reduce", "trtri_diag"};
 
 struct ProfRec {
   int kid;
@@ -78,6 +78,15 @@ extern "C" gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int
 }
 
 extern "C" int gptq_version(void) { return 1; }
+
+extern "C" gptq_status gptq_workspace_status(const void* ws, void* stream) {
+  if (!ws) return GPTQ_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned h = 0;
+  GPTQ_HIP(hipMemcpyAsync(&h, ws, sizeof(unsigned), hipMemcpyDeviceToHost, st));
+  GPTQ_HIP(hipStreamSynchronize(st));
+  return status_from_bits(h);
+}
 
 extern "C" const char* gptq_last_error_string(void) {
   if (g_last_error == hipSuccess) return "no error";

@@ -17,11 +17,18 @@ typedef float f16 __attribute__((ext_vector_type(16)));
 // Device status word bits (first word of every workspace).
 enum : unsigned { ST_NOTSPD = 1u, ST_NONFINITE = 2u, ST_BADPERM = 4u };
 
+inline gptq_status status_from_bits(unsigned b) {
+  if (b & ST_BADPERM) return GPTQ_EINVAL;
+  if (b & ST_NOTSPD) return GPTQ_ENOTSPD;
+  if (b & ST_NONFINITE) return GPTQ_ENONFINITE;
+  return GPTQ_OK;
+}
+
 // Kernel classes for the optional HIP-event profiler.
 enum KernelId {
   K_HESS_TILE = 0, K_HESS_REDUCE, K_PREP_DIAG, K_PREP_PERM, K_PREP_GATHER, K_CHOL_POTRF,
   K_CHOL_TRSM, K_CHOL_SYRK, K_TRTRI_ROW, K_TRTRI_UPDATE, K_PREP_UOUT, K_Q_INIT, K_Q_PERMUTE,
-  K_Q_GEMM, K_Q_SWEEP, K_Q_FINALIZE, K_FILL, K_Q_REDUCE, K_COUNT
+  K_Q_GEMM, K_Q_SWEEP, K_Q_FINALIZE, K_FILL, K_Q_REDUCE, K_TRTRI_DIAG, K_COUNT
 };
 
 // Launch bracketing for the profiler (defined in api.hip).

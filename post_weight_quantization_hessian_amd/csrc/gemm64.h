@@ -108,6 +108,28 @@ __device__ inline void zero_acc(d4 (&acc)[4][4]) {
     for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
 }
 
+// C[row][col] += sign * acc for the tile at C (leading dimension ld): all 64
+// old values of the thread are loaded before any store, so the loads overlap
+// (a load-add-store per element would serialize one memory round trip each).
+__device__ inline void acc_update(const d4 (&acc)[4][4], double* C, int64_t ld, double sign) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+  double* base = C + (int64_t)(wm * 64 + (lane >> 4)) * ld + wn * 64 + (lane & 15);
+  double old[4][4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) old[i][j][r] = base[(int64_t)(i * 16 + 4 * r) * ld + j * 16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        base[(int64_t)(i * 16 + 4 * r) * ld + j * 16] = old[i][j][r] + sign * acc[i][j][r];
+}
+
 // Visit the tile's accumulators: f(row, col, value) with tile-local row/col.
 template <class F>
 __device__ inline void for_each_acc(const d4 (&acc)[4][4], F f) {

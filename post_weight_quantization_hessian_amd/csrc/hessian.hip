@@ -90,6 +90,30 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
     return;
   }
   const int64_t fa = (int64_t)a * GT, fb = (int64_t)b * GT;
+  const bool full = fa + GT <= dim && fb + GT <= dim;
+  if (!overwrite && full) {
+    // both triangles: old values of a tile are all loaded before any store
+    acc_update(acc, S + fa * lds + fb, lds, 1.0);
+    if (a != b) {
+      double old[4][4][4];
+      const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+      double* mb = S + (fb + wn * 64 + (lane & 15)) * lds + fa + wm * 64 + (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) old[i][j][r] = mb[(int64_t)(j * 16) * lds + i * 16 + 4 * r];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            mb[(int64_t)(j * 16) * lds + i * 16 + 4 * r] = old[i][j][r] + acc[i][j][r];
+    }
+    return;
+  }
   for_each_acc(acc, [&](int r, int c, double v) {
     const int64_t i = fa + r, j = fb + c;
     if (i < dim && j < dim) {

@@ -8,6 +8,10 @@
 // which is upper triangular with U^T U = Hp^-1. One Cholesky and one
 // triangular inverse, both blocked by 128 in fp64 on MFMA; K is padded to a
 // multiple of 128 with an identity block so no kernel needs edge masks.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "gemm64.h"
 
 namespace gptq {
@@ -121,6 +125,15 @@ __device__ inline double readlane_f64(double v, int lane) {
   return a.d;
 }
 
+// 1/sqrt(d) for d > 0: hardware estimate refined by two Newton steps.
+__device__ inline double rsqrt_f64(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  const double h = 0.5 * d;
+  y = y * fma(-h * y, y, 1.5);
+  y = y * fma(-h * y, y, 1.5);
+  return y;
+}
+
 // One wave: in-place Cholesky of the 16x16 tile T (lower part), 1/diag to
 // invd. The tile lives in registers in the MFMA accumulator layout (lane l:
 // column l & 15, rows (l >> 4) + 4m); column j is handed to the other lanes
@@ -137,8 +150,8 @@ __device__ inline void factor16(double* T, double* invd, double* col, int lane, 
       bad = true;
       d = 1.0;
     }
-    const double ljj = sqrt(d);
-    const double inv = 1.0 / ljj;
+    const double inv = rsqrt_f64(d);
+    const double ljj = d * inv;
     if (c == j) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -197,40 +210,60 @@ __device__ inline void inverse16(const double* L, const double* rinv, double* X,
   for (int m = 0; m < 4; ++m) X[c * PT + g + 4 * m] = x[m];
 }
 
-__global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K, double* __restrict__ Xb,
-                                                         int64_t ld, int p,
+__global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
+                                                         double* __restrict__ Dd, int64_t ld, int p,
                                                          unsigned* __restrict__ status) {
   __shared__ double A[NPT * PTS];
-  __shared__ double X[NPT * PTS];
+  __shared__ double X[8 * PTS];  // inverses of the eight 16x16 diagonal tiles
   __shared__ double invd[8][16];   // 1 / diag of each 16x16 diagonal tile
   __shared__ double xbuf[4][16];   // per-wave column / row hand-over buffers
   __shared__ int bad_any;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t c0 = (int64_t)p * GT;
   if (t == 0) bad_any = 0;
-  // 64 elements per thread, loaded 16 at a time so the loads overlap
-  for (int e0 = 0; e0 < GT * GT; e0 += 16 * 256) {
-    double v[16];
+  // Tile-ordered transfers: thread t always handles element (t >> 4, t & 15)
+  // of a 16x16 tile, so the LDS offset is fixed and the global address moves
+  // by whole tiles; all 36 loads are in flight together.
+  const int er = t >> 4, ec = t & 15;
+  const int lds_off = ec * PT + er;
+  const double* gK = K + (c0 + er) * ld + c0 + ec;
+  {
+    double v[NPT];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = e0 + u * 256 + t;
-      const int r = e >> 7, c = e & 127;
-      v[u] = c <= r ? K[(c0 + r) * ld + c0 + c] : 0.0;
-    }
+    for (int I = 0; I < 8; ++I)
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = e0 + u * 256 + t;
-      const int r = e >> 7, c = e & 127;
-      if (c <= r) A[ptile(r >> 4, c >> 4) + (c & 15) * PT + (r & 15)] = v[u];
-    }
+      for (int Kt = 0; Kt <= I; ++Kt) v[I * (I + 1) / 2 + Kt] = gK[(int64_t)(16 * I) * ld + 16 * Kt];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) A[u * PTS + lds_off] = v[u];
   }
-  for (int e = t; e < NPT * PTS; e += 256) X[e] = 0.0;
   __syncthreads();
 
+  // One 16x16 trailing-tile update C -= L_Is L_Ks^T (one wave, fp64 MFMA).
+  auto syrk_tile = [&](int I, int Kc, int s) {
+    double* C = A + ptile(I, Kc);
+    const double* Li = A + ptile(I, s);
+    const double* Lk = A + ptile(Kc, s);
+    d4 acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = C[(lane & 15) * PT + (lane >> 4) + 4 * r];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int q = (lane >> 4) + 4 * kk;
+      const double av = -Li[q * PT + (lane & 15)];
+      const double bv = Lk[q * PT + (lane & 15)];
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) C[(lane & 15) * PT + (lane >> 4) + 4 * r] = acc[r];
+  };
+
+  // Pipelined 16-wide steps: while wave 0 updates and factors the next
+  // diagonal tile, waves 1-2 update the other trailing tiles and wave 3
+  // inverts the previous diagonal tile.
   bool bad = false;
+  if (wave == 0) factor16(A + ptile(0, 0), invd[0], xbuf[0], lane, bad);
+  __syncthreads();
   for (int s = 0; s < 8; ++s) {
-    if (wave == 0) factor16(A + ptile(s, s), invd[s], xbuf[0], lane, bad);
-    __syncthreads();
     // rows below the diagonal tile: x L_ss^T = a  (forward substitution)
     if (t >= 16 * (s + 1) && t < GT) {
       double* T = A + ptile(t >> 4, s);
@@ -249,36 +282,143 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
       for (int c = 0; c < 16; ++c) T[c * PT + ri] = x[c];
     }
     __syncthreads();
-    // trailing tiles (I, Kc), s < Kc <= I < 8: A_IK -= L_Is L_Ks^T
-    const int m = 7 - s;
-    const int cnt = m * (m + 1) / 2;
-    for (int u = wave; u < cnt; u += 4) {
-      int a = 0;
-      while ((a + 1) * (a + 2) / 2 <= u) ++a;
-      const int I = s + 1 + a, Kc = s + 1 + (u - a * (a + 1) / 2);
-      double* C = A + ptile(I, Kc);
-      const double* Li = A + ptile(I, s);
-      const double* Lk = A + ptile(Kc, s);
-      d4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = C[(lane & 15) * PT + (lane >> 4) + 4 * r];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int q = (lane >> 4) + 4 * kk;
-        const double av = -Li[q * PT + (lane & 15)];
-        const double bv = Lk[q * PT + (lane & 15)];
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+    if (s == 7) break;
+    // trailing tiles (I, Kc), s < Kc <= I < 8; u = 0 is (s+1, s+1)
+    if (wave == 0) {
+      syrk_tile(s + 1, s + 1, s);
+      wave_lds_sync();
+      factor16(A + ptile(s + 1, s + 1), invd[s + 1], xbuf[0], lane, bad);
+    } else if (wave == 3) {
+      inverse16(A + ptile(s, s), invd[s], X + s * PTS, xbuf[3], lane);
+    } else {
+      const int m = 7 - s;
+      const int cnt = m * (m + 1) / 2;
+      for (int u = wave; u < cnt; u += 2) {
+        int a = 0;
+        while ((a + 1) * (a + 2) / 2 <= u) ++a;
+        syrk_tile(s + 1 + a, s + 1 + (u - a * (a + 1) / 2), s);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) C[(lane & 15) * PT + (lane >> 4) + 4 * r] = acc[r];
     }
     __syncthreads();
   }
   if (bad) atomicOr(&bad_any, 1);
+  if (wave == 3) inverse16(A + ptile(7, 7), invd[7], X + 7 * PTS, xbuf[3], lane);
+  __syncthreads();
 
-  // inverse: diagonal tiles, then off-diagonal tiles by distance
-  for (int i = wave; i < 8; i += 4)
-    inverse16(A + ptile(i, i), invd[i], X + ptile(i, i), xbuf[wave], lane);
+  // L11 back into K (lower tiles); the diagonal inverses to Dd (16x16 tiles,
+  // column-major, pitch 16).
+  double* gL = K + (c0 + er) * ld + c0 + ec;
+  for (int I = 0; I < 8; ++I) {
+#pragma unroll
+    for (int Kt = 0; Kt < 8; ++Kt)
+      if (Kt <= I) gL[(int64_t)(16 * I) * ld + 16 * Kt] = A[(I * (I + 1) / 2 + Kt) * PTS + lds_off];
+  }
+  double* D = Dd + (int64_t)p * 8 * 256;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) D[i * 256 + ec * 16 + er] = X[i * PTS + lds_off];
+  if (t == 0 && bad_any) atomicOr(status, ST_NOTSPD);
+}
+
+// L21 = A21 L11^-T for one 128-row block below panel p (in place), by
+// 16-column blocks: with Y_s = (L21[:, s])^T,
+//     Y_s = D_s (A21[:, s]^T - sum_{s'<s} L11[s][s'] Y_s'),   D_s = L11[s][s]^-1,
+// so only the lower 16x16 tiles of L11 and the diagonal inverses are needed.
+// Each wave owns 32 rows; the Y tiles stay in registers in the MFMA
+// accumulator layout, which is also the B-operand layout of the next products.
+__global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
+                                                        const double* __restrict__ Dd, int64_t ld,
+                                                        int p) {
+  __shared__ double Ls[NPT * PTS];
+  __shared__ double Ds[8 * PTS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t c0 = (int64_t)p * GT;
+  const int64_t r0 = c0 + GT + (int64_t)blockIdx.x * GT;
+  {
+    const int er = t >> 4, ec = t & 15;
+    const double* gK = K + (c0 + er) * ld + c0 + ec;
+    double v[NPT];
+#pragma unroll
+    for (int I = 0; I < 8; ++I)
+#pragma unroll
+      for (int Kt = 0; Kt <= I; ++Kt) v[I * (I + 1) / 2 + Kt] = gK[(int64_t)(16 * I) * ld + 16 * Kt];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) Ls[u * PTS + ec * PT + er] = v[u];
+    const double* D = Dd + (int64_t)p * 8 * 256;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) Ds[i * PTS + ec * PT + er] = D[i * 256 + ec * 16 + er];
+  }
+  // this wave's 32 rows, transposed into Y tiles: y[s][rt][r] = A21[row][col] with
+  // row = 32*wave + 16*rt + (lane & 15), col = 16*s + (lane >> 4) + 4*r
+  d4 y[8][2];
+  double* gA = K + (r0 + 32 * wave + (lane & 15)) * ld + c0 + (lane >> 4);
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[s][rt][r] = gA[(int64_t)(16 * rt) * ld + 16 * s + 4 * r];
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      d4 acc = y[s][rt];
+#pragma unroll
+      for (int sp = 0; sp < s; ++sp) {
+        const double* Lt = Ls + ptile(s, sp);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int q = (lane >> 4) + 4 * kk;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-Lt[q * PT + (lane & 15)], y[sp][rt][kk], acc,
+                                                     0, 0, 0);
+        }
+      }
+      const double* Dt = Ds + s * PTS;
+      d4 out = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int q = (lane >> 4) + 4 * kk;
+        out = __builtin_amdgcn_mfma_f64_16x16x4f64(Dt[q * PT + (lane & 15)], acc[kk], out, 0, 0, 0);
+      }
+      y[s][rt] = out;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gA[(int64_t)(16 * rt) * ld + 16 * s + 4 * r] = y[s][rt][r];
+}
+
+// X_pp = L_pp^-1 for every 128x128 diagonal block (one workgroup per block,
+// all blocks at once) from its lower 16x16 tiles and the eight 16x16
+// diagonal inverses: off-diagonal tiles by distance from the diagonal,
+//     X_ij = -X_ii * sum_{k=j}^{i-1} L_ik X_kj.
+// Written to the diagonal block of Xb with zero tiles above.
+__global__ __launch_bounds__(256) void trtri_diag_kernel(const double* __restrict__ K,
+                                                         const double* __restrict__ Dd,
+                                                         double* __restrict__ Xb, int64_t ld) {
+  __shared__ double A[NPT * PTS];
+  __shared__ double X[NPT * PTS];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int p = blockIdx.x;
+  const int64_t c0 = (int64_t)p * GT;
+  const int er = t >> 4, ec = t & 15;
+  const int lds_off = ec * PT + er;
+  {
+    const double* gK = K + (c0 + er) * ld + c0 + ec;
+    double v[NPT];
+#pragma unroll
+    for (int I = 0; I < 8; ++I)
+#pragma unroll
+      for (int Kt = 0; Kt <= I; ++Kt) v[I * (I + 1) / 2 + Kt] = gK[(int64_t)(16 * I) * ld + 16 * Kt];
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) A[u * PTS + lds_off] = v[u];
+    const double* D = Dd + (int64_t)p * 8 * 256;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) X[ptile(i, i) + lds_off] = D[i * 256 + ec * 16 + er];
+  }
   __syncthreads();
   for (int d = 1; d < 8; ++d) {
     for (int i = d + wave; i < 8; i += 4) {
@@ -307,46 +447,37 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
     }
     __syncthreads();
   }
-  // L11 back into K (lower), X11 into the diagonal block of Xb (zeros above)
-  for (int e = t; e < GT * GT; e += 256) {
-    const int r = e >> 7, c = e & 127;
-    const int off = ptile(r >> 4, c >> 4) + (c & 15) * PT + (r & 15);
-    if (c <= r) {
-      K[(c0 + r) * ld + c0 + c] = A[off];
-      Xb[(c0 + r) * ld + c0 + c] = X[off];
-    } else {
-      Xb[(c0 + r) * ld + c0 + c] = 0.0;
-    }
+  double* gX = Xb + (c0 + er) * ld + c0 + ec;
+  for (int I = 0; I < 8; ++I) {
+#pragma unroll
+    for (int Kt = 0; Kt < 8; ++Kt)
+      gX[(int64_t)(16 * I) * ld + 16 * Kt] =
+          Kt <= I ? X[(I * (I + 1) / 2 + Kt) * PTS + lds_off] : 0.0;
   }
-  if (t == 0 && bad_any) atomicOr(status, ST_NOTSPD);
 }
 
-// L21 = A21 * X11^T for row block m below panel p (in place); X11 = L11^-1
-// is the diagonal block of Xb written by chol_potrf_kernel.
-__global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
-                                                        const double* __restrict__ Xb, int64_t ld,
-                                                        int p) {
-  __shared__ double sA[2 * GCH];
-  __shared__ double sB[2 * GCH];
-  const int64_t c0 = (int64_t)p * GT;
-  const int64_t r0 = c0 + GT + (int64_t)blockIdx.x * GT;
-  LdTrans64 la{K + r0 * ld + c0, ld, {}};
-  LdTrans64 lb{Xb + c0 * ld + c0, ld, {}};
-  d4 acc[4][4];
-  zero_acc(acc);
-  gemm64_loop(la, lb, false, GT / GK, sA, sB, acc);
-  for_each_acc(acc, [&](int r, int c, double v) { K[(r0 + r) * ld + c0 + c] = v; });
-}
-
-// Lower tiles of the trailing matrix: K22 -= L21 L21^T (tile (a, b), a >= b).
-__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, int64_t ld, int p) {
+// Lower tiles of the trailing matrix: K22 -= L21 L21^T (tile (a, b), a >= b,
+// in trailing-tile coordinates). part 0: all tiles; 1: the first tile column
+// (b = 0, the next panel); 2: the rest (b >= 1).
+__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, int64_t ld, int p,
+                                                        int part) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  int a = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
-  while (a * (a + 1) / 2 > id) --a;
-  while ((a + 1) * (a + 2) / 2 <= id) ++a;
-  const int b = id - a * (a + 1) / 2;
+  int a, b;
+  if (part == 1) {
+    a = id;
+    b = 0;
+  } else {
+    a = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
+    while (a * (a + 1) / 2 > id) --a;
+    while ((a + 1) * (a + 2) / 2 <= id) ++a;
+    b = id - a * (a + 1) / 2;
+    if (part == 2) {
+      ++a;
+      ++b;
+    }
+  }
   const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
   const int64_t ra = c1 + (int64_t)a * GT, rb = c1 + (int64_t)b * GT;
   LdTrans64 la{K + ra * ld + c0, ld, {}};
@@ -354,7 +485,7 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, 
   d4 acc[4][4];
   zero_acc(acc);
   gemm64_loop(la, lb, a == b, GT / GK, sA, sB, acc);
-  for_each_acc(acc, [&](int r, int c, double v) { K[(ra + r) * ld + rb + c] -= v; });
+  acc_update(acc, K + ra * ld + rb, ld, -1.0);
 }
 
 // ---------------------------------------------------------------- inverse
@@ -437,11 +568,57 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
 
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
+// ---------------------------------------------------------------- side stream
+//
+// One non-blocking side stream (default priority) per device, created on
+// first use and kept for the life of the process, with a ring of events used
+// to order it against the caller's stream. The side stream is restricted to
+// 7/8 of the compute units so that the latency-bound kernels of the critical
+// chain, launched meanwhile on the caller's stream, always find free units.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  std::mutex mu;
+  hipEvent_t events[130] = {};
+  hipEvent_t ev(int i) const { return events[i]; }
+};
+
+static std::mutex g_side_mu;
+static std::map<std::pair<int, hipStream_t>, SideStream*> g_side;
+
+// The side stream serving caller stream `caller` on the current device.
+static SideStream* side_stream(hipStream_t caller) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream*& slot = g_side[std::make_pair(dev, caller)];
+  if (!slot) slot = new SideStream();
+  SideStream& s = *slot;
+  if (!s.stream) {
+    int ncu = 0;
+    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    bool made = false;
+    if (ncu >= 16 && ncu <= 1024) {
+      uint32_t mask[32] = {};
+      for (int cu = 0; cu < ncu; ++cu)
+        if (cu % 8 != 7) mask[cu / 32] |= 1u << (cu % 32);
+      made = hipExtStreamCreateWithCUMask(&s.stream, (uint32_t)((ncu + 31) / 32), mask) ==
+             hipSuccess;
+    }
+    if (!made && hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) {
+      s.stream = nullptr;
+      return nullptr;
+    }
+    for (auto& e : s.events)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+  }
+  return &s;
+}
+
 // ---------------------------------------------------------------- layout
 
 struct PrepLayout {
   int64_t n, ip, nt;
-  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, total;
+  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, off_D, total;
 };
 
 static PrepLayout prep_layout(int64_t n) {
@@ -461,6 +638,7 @@ static PrepLayout prep_layout(int64_t n) {
   L.off_K = take(8 * (size_t)L.ip * L.ip);
   L.off_X = take(8 * (size_t)L.ip * L.ip);
   L.off_T = take(L.nt > 1 ? 8 * (size_t)L.ip * L.ip : 8);
+  L.off_D = take(8 * (size_t)L.nt * 8 * 256);
   L.total = o;
   return L;
 }
@@ -481,7 +659,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   if (in_features == 0) return GPTQ_OK;
   if (!S || !perm || !U || n_tokens_total <= 0 || !(damp >= 0.0) || !std::isfinite(damp))
     return GPTQ_EINVAL;
-  if (flags & ~GPTQ_FLAG_ACT_ORDER) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_ACT_ORDER | GPTQ_FLAG_NO_SYNC)) return GPTQ_EINVAL;
   if (in_features > (int64_t)1 << 20) return GPTQ_EINVAL;
   const PrepLayout L = prep_layout(in_features);
   if (!ws || ws_bytes < L.total) return GPTQ_EWORKSPACE;
@@ -493,6 +671,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   double* K = (double*)(base + L.off_K);
   double* Xb = (double*)(base + L.off_X);
   double* Tb = (double*)(base + L.off_T);
+  double* Dd = (double*)(base + L.off_D);
   const int64_t n = in_features, ip = L.ip;
   const int nt = (int)L.nt;
   const double c = 2.0 / (double)n_tokens_total;
@@ -504,14 +683,43 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                   hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
   GPTQ_LAUNCH(K_PREP_GATHER, st,
               prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, perm, K));
+  // Blocked Cholesky with one step of look-ahead: the caller's stream runs
+  // the chain potrf(p) -> trsm(p) -> update of the next panel's tile column,
+  // while the side stream updates the rest of the trailing matrix (block rows
+  // and columns >= p+2, which potrf/trsm of panel p+1 never touch). The next
+  // panel's column update waits for the previous rest-update, which wrote the
+  // same tiles.
+  SideStream* side = side_stream(st);
+  if (!side) return GPTQ_EHIP;
+  hipStream_t ss = side->stream;
+  std::unique_lock<std::mutex> side_lock(side->mu);  // one enqueuer at a time
+  GPTQ_HIP(hipEventRecord(side->ev(0), st));
+  GPTQ_HIP(hipStreamWaitEvent(ss, side->ev(0), 0));
+  int rest_pending = -1;  // event index of the last rest-update
   for (int p = 0; p < nt; ++p) {
-    GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Xb, ip, p, status));
+    GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, p, status));
     const int mt = nt - 1 - p;
-    if (mt > 0) {
-      GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, Xb, ip, p));
-      GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<mt * (mt + 1) / 2, 256, 0, st>>>(K, ip, p));
+    if (mt == 0) break;
+    GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, Dd, ip, p));
+    if (rest_pending >= 0) GPTQ_HIP(hipStreamWaitEvent(st, side->ev(rest_pending), 0));
+    GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<mt, 256, 0, st>>>(K, ip, p, 1));
+    if (mt > 1) {
+      const int e_trsm = 1 + 2 * (p % 64), e_rest = e_trsm + 1;
+      GPTQ_HIP(hipEventRecord(side->ev(e_trsm), st));
+      GPTQ_HIP(hipStreamWaitEvent(ss, side->ev(e_trsm), 0));
+      GPTQ_LAUNCH(K_CHOL_SYRK, ss,
+                  chol_syrk_kernel<<<(mt - 1) * mt / 2, 256, 0, ss>>>(K, ip, p, 2));
+      GPTQ_HIP(hipEventRecord(side->ev(e_rest), ss));
+      rest_pending = e_rest;
+    } else {
+      rest_pending = -1;
     }
   }
+  // join: everything on the side stream precedes the rest of the call
+  GPTQ_HIP(hipEventRecord(side->ev(129), ss));
+  GPTQ_HIP(hipStreamWaitEvent(st, side->ev(129), 0));
+  side_lock.unlock();
+  GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
   for (int h = 1; h < nt; h *= 2) {
     const int tiles = level_tiles(h, nt);
     GPTQ_LAUNCH(K_TRTRI_ROW, st, trtri_t_kernel<<<tiles, 256, 0, st>>>(K, Xb, Tb, ip, h, nt));
@@ -521,9 +729,6 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)std::min<int64_t>(n, 65535));
     GPTQ_LAUNCH(K_PREP_UOUT, st, prep_uout_kernel<<<grid, 256, 0, st>>>(Xb, ip, n, U));
   }
-  unsigned h_status = 0;
-  GPTQ_HIP(hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st));
-  GPTQ_HIP(hipStreamSynchronize(st));
-  if (h_status & ST_NOTSPD) return GPTQ_ENOTSPD;
-  return GPTQ_OK;
+  if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
+  return gptq_workspace_status(ws, stream);
 }

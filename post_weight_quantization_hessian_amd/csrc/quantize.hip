@@ -22,12 +22,14 @@ typedef double dbl2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- helpers
 
+// Every pattern used here writes every lane, so the "old" operand is the
+// source itself (no extra register initialisation).
 template <int CTRL>
 __device__ inline double dpp_f64(double v) {
   union { double d; int i[2]; } a, b;
   a.d = v;
-  b.i[0] = __builtin_amdgcn_update_dpp(0, a.i[0], CTRL, 0xF, 0xF, false);
-  b.i[1] = __builtin_amdgcn_update_dpp(0, a.i[1], CTRL, 0xF, 0xF, false);
+  b.i[0] = __builtin_amdgcn_update_dpp(a.i[0], a.i[0], CTRL, 0xF, 0xF, false);
+  b.i[1] = __builtin_amdgcn_update_dpp(a.i[1], a.i[1], CTRL, 0xF, 0xF, false);
   return b.d;
 }
 // quad_perm controls: broadcast lane q of the quad; xor 1; xor 2
@@ -265,88 +267,120 @@ __global__ __launch_bounds__(256) void q_reduce_kernel(const double* __restrict_
 
 // ---------------------------------------------------------------- sweep
 //
-// One block of columns [j0, j0+bw). 16 rows per wave (4 lanes per row).
+// One block of columns [j0, j0+bw). A row is held by the 16 lanes of one DPP
+// row: lane q owns columns q, q+16, ..., q+112 (8 fp64 slots); a wave holds
+// 4 rows. Every 16 columns the slots shift down by one, so the live column is
+// always slot 0 of lane j % 16, whose scaled error is broadcast to its row
+// with row_newbcast. Group min/max and the loss are reduced over the row with
+// quad permutes and row rotations.
+template <int N>
+__device__ inline double row_bcast(double v) { return dpp_f64<0x150 + N>(v); }
+__device__ inline double row_ror4(double v) { return dpp_f64<0x124>(v); }
+__device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
+
 template <int GS>
-__global__ __launch_bounds__(256) void q_sweep_kernel(
+__global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
     const float* __restrict__ U, int64_t ldu, bool vecU, int64_t rows, int64_t j0, int bw,
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
     double* __restrict__ row_loss, unsigned* __restrict__ status) {
-  // U slab plus one zero row of padding: slot addresses run up to 3 columns
-  // past the end of a row (into the next row or the padding) for slots that
-  // are past the block end and never used.
+  // U slab plus one row of zero padding: the slot reads of a column run up to
+  // 112 entries past its row end, into the next row or the padding, only for
+  // slots past the block end whose values are never used.
   __shared__ double Us[QB * QB + QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int q4 = lane & 3;
+  const int q = lane & 15;
   const int nthr = blockDim.x;
-  const int64_t r = (int64_t)blockIdx.x * (nthr >> 2) + wv * 16 + (lane >> 2);
+  const int64_t r = (int64_t)blockIdx.x * (nthr >> 4) + wv * 4 + (lane >> 4);
   const bool rv = r < rows;
   const double maxq = (double)((1 << bits) - 1);
 
-  // U slab of this block; U is zero below its diagonal. Zero outside [0, bw).
-  if (vecU && bw == QB) {
-    for (int e0 = 0; e0 < QB * QB / 4; e0 += 8 * nthr) {
-      f4 v[8];
+  // All global loads of the prologue are issued before any is waited on:
+  // this row's current values, the U slab (16 float4 per thread for 256
+  // threads), and the diagonal of the slab.
+  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk], formed by
+  // the update GEMM (wblk); the first block reads the weights directly.
+  double w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * nthr + t;  // float4 index
-        const int a = e >> 5, c4 = (e & 31) * 4;
-        v[u] = e < QB * QB / 4 ? *reinterpret_cast<const f4*>(U + (j0 + a) * ldu + j0 + c4)
-                               : f4{0, 0, 0, 0};
-      }
+  for (int s = 0; s < 8; ++s) {
+    const int c = 16 * s + q;
+    w[s] = (rv && c < bw) ? (wblk ? wblk[r * QB + c] : f16_to_f64(W[r * ldw + j0 + c])) : 0.0;
+  }
+  const bool vec_slab = vecU && bw == QB;
+  constexpr int SLAB4 = QB * QB / 4;       // float4s in the slab
+  constexpr int PER = SLAB4 / 256;         // per thread with 256 threads
+  f4 sv[PER];
+  if (vec_slab) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int e = e0 + u * nthr + t;
-        if (e < QB * QB / 4) {
-#pragma unroll
-          for (int x = 0; x < 4; ++x) Us[e * 4 + x] = (double)v[u][x];
-        }
-      }
-    }
-  } else {
-    for (int e = t; e < QB * QB; e += nthr) {
-      const int a = e >> 7, c = e & 127;
-      Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] : 0.0;
+    for (int u = 0; u < PER; ++u) {
+      const int e = u * nthr + t;
+      const int a = e >> 5, c4 = (e & 31) * 4;
+      sv[u] = e < SLAB4 ? *reinterpret_cast<const f4*>(U + (j0 + a) * ldu + j0 + c4)
+                        : f4{0, 0, 0, 0};
     }
   }
-
   for (int j = t; j < QB; j += nthr) {
     rdiag[j] = j < bw ? 1.0 / (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
     Us[QB * QB + j] = 0.0;
   }
-
-  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk], formed by
-  // the update GEMM (wblk); the first block reads the weights directly.
-  double w[32];
+  __syncthreads();
+  // Row a of the slab is stored divided by U[a][a] (the error broadcast along
+  // a row is then the unscaled residual d, and e = d / U[a][a] leaves the
+  // dependent chain). Entries below the diagonal are zero.
+  if (vec_slab) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = u * nthr + t;
+      if (e < SLAB4) {
+        const int a = e >> 5, c4 = (e & 31) * 4;
+        const double ra = rdiag[a];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Us[e * 4 + x] = c4 + x >= a ? (double)sv[u][x] * ra : 0.0;
+      }
+    }
+    // fewer than 256 threads: the rest of the slab
+    for (int e = PER * nthr + t; e < SLAB4; e += nthr) {
+      const int a = e >> 5, c4 = (e & 31) * 4;
+      const f4 v = *reinterpret_cast<const f4*>(U + (j0 + a) * ldu + j0 + c4);
+      const double ra = rdiag[a];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) Us[e * 4 + x] = c4 + x >= a ? (double)v[x] * ra : 0.0;
+    }
+  } else {
+    for (int e = t; e < QB * QB; e += nthr) {
+      const int a = e >> 7, c = e & 127;
+      Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] * rdiag[a] : 0.0;
+    }
+  }
   bool finite = true;
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    const int c = 4 * s + q4;
-    double v = 0.0;
-    if (rv && c < bw) {
-      if (wblk) {
-        v = wblk[r * QB + c];
-      } else {
-        v = f16_to_f64(W[r * ldw + j0 + c]);
-      }
-      finite = finite && isfinite(v);
-    }
-    w[s] = v;
-  }
+  for (int s = 0; s < 8; ++s) finite = finite && isfinite(w[s]);
   if (!finite) atomicOr(status, ST_NONFINITE);
   __syncthreads();
 
   double scale = 1.0, rscale = 1.0, zero = 0.0, loss = 0.0;
-  const int nt4 = (bw + 3) >> 2;
-  for (int tt = 0; tt < nt4; ++tt) {
-    if (((4 * tt) % GS) == 0) {
+  const int nt16 = (bw + 15) >> 4;
+  // U row of column jc as seen from the slots (slot s holds column
+  // 16*((jc >> 4) + s) + q; slots past the block end are dead and read into
+  // the next row or the padding). Loaded two columns ahead into four
+  // rotating register sets (set = column & 3).
+  double ub[4][8];
+  auto load_row = [&](int jc, double (&uu)[8]) {
+    const double* urow = Us + jc * QB + 16 * (jc >> 4) + q;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) uu[s] = urow[16 * s];
+  };
+  load_row(0, ub[0]);
+  load_row(bw > 1 ? 1 : 0, ub[1]);
+  for (int tt = 0; tt < nt16; ++tt) {
+    if (((16 * tt) % GS) == 0) {
       // grid of the group starting here, from the current values
       double mn = 0.0, mx = 0.0;
 #pragma unroll
-      for (int s = 0; s < GS / 4; ++s) {
-        if (4 * (tt + s) + q4 < bw) {
+      for (int s = 0; s < GS / 16; ++s) {
+        if (16 * (tt + s) + q < bw) {
           mn = fmin(mn, w[s]);
           mx = fmax(mx, w[s]);
         }
@@ -355,6 +389,10 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
       mx = fmax(mx, quad_xor1(mx));
       mn = fmin(mn, quad_xor2(mn));
       mx = fmax(mx, quad_xor2(mx));
+      mn = fmin(mn, row_ror4(mn));
+      mx = fmax(mx, row_ror4(mx));
+      mn = fmin(mn, row_ror8(mn));
+      mx = fmax(mx, row_ror8(mx));
       uint16_t sh = f64_to_f16_rne((mx - mn) / maxq);
       scale = f16_to_f64(sh);
       if ((sh & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
@@ -366,65 +404,73 @@ __global__ __launch_bounds__(256) void q_sweep_kernel(
         zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
       }
       rscale = 1.0 / scale;
-      if (rv && q4 == 0) {
-        const int64_t g = (j0 + 4 * tt) / GS;
+      if (rv && q == 0) {
+        const int64_t g = (j0 + 16 * tt) / GS;
         scales[r * ldg + g] = sh;
         zeros[r * ldg + g] = f64_to_f16_rne(zero);
       }
     }
+    // the residual d and clamped level k of the column this lane owns
+    double d_own = 0.0, k_own = 0.0;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * tt + jj;
+    for (int jj = 0; jj < 16; ++jj) {
+      const int j = 16 * tt + jj;
       if (j < bw) {
-        // quantize slot 0 (meaningful on the owner lane q4 == jj)
+        double (&u)[8] = ub[jj & 3];
+        load_row(j + 2 < bw ? j + 2 : j, ub[(jj + 2) & 3]);
+        // quantize slot 0 (meaningful on the owner lane q == jj):
+        // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
+        // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
         const double v = w[0];
-        double qf = rint(v * rscale) + zero;
-        qf = fmin(fmax(qf, 0.0), maxq);
-        const double dq = scale * (qf - zero);
-        const double e = (v - dq) * rdiag[j];
-        double eb;
-        if (jj == 0) eb = quad_bcast<0>(e);
-        else if (jj == 1) eb = quad_bcast<1>(e);
-        else if (jj == 2) eb = quad_bcast<2>(e);
-        else eb = quad_bcast<3>(e);
-        if (q4 == jj && rv) {
-          codes[r * ldc + j0 + j] = (uint8_t)qf;
-          E[r * lde + j0 + j] = (float)e;
-          loss += e * e;
+        const double k = fmin(fmax(rint(v * rscale), -zero), maxq - zero);
+        const double d = fma(-scale, k, v);
+        double db;
+        switch (jj) {
+          case 0: db = row_bcast<0>(d); break;
+          case 1: db = row_bcast<1>(d); break;
+          case 2: db = row_bcast<2>(d); break;
+          case 3: db = row_bcast<3>(d); break;
+          case 4: db = row_bcast<4>(d); break;
+          case 5: db = row_bcast<5>(d); break;
+          case 6: db = row_bcast<6>(d); break;
+          case 7: db = row_bcast<7>(d); break;
+          case 8: db = row_bcast<8>(d); break;
+          case 9: db = row_bcast<9>(d); break;
+          case 10: db = row_bcast<10>(d); break;
+          case 11: db = row_bcast<11>(d); break;
+          case 12: db = row_bcast<12>(d); break;
+          case 13: db = row_bcast<13>(d); break;
+          case 14: db = row_bcast<14>(d); break;
+          default: db = row_bcast<15>(d); break;
         }
-        // Slot s holds column 4*(tt+s) + q4; slots past the block end are never
-        // used again. Whole groups of 8 such slots are skipped (uniform tests);
-        // inside a group the reads run past the row end into the next row or
-        // the padding, which only feeds dead slots.
-        const double* urow = Us + j * QB + 4 * tt + q4;
-        {
-          const double u0 = urow[0];
-          const double nv = w[0] - eb * u0;
-          w[0] = q4 > jj ? nv : w[0];
-        }
+        d_own = q == jj ? d : d_own;
+        k_own = q == jj ? k : k_own;
+        // later columns: w -= d * U[j][c] / U[j][j]. Slot 0 of the lanes at
+        // or before the pivot is dead (its slab entry, below the diagonal, is
+        // 0); slots past the block end are dead too.
 #pragma unroll
-        for (int s = 1; s < 8; ++s) w[s] -= eb * urow[4 * s];
-        if (tt < 24) {
-#pragma unroll
-          for (int s = 8; s < 16; ++s) w[s] -= eb * urow[4 * s];
-        }
-        if (tt < 16) {
-#pragma unroll
-          for (int s = 16; s < 24; ++s) w[s] -= eb * urow[4 * s];
-        }
-        if (tt < 8) {
-#pragma unroll
-          for (int s = 24; s < 32; ++s) w[s] -= eb * urow[4 * s];
-        }
+        for (int s = 0; s < 8; ++s) w[s] -= db * u[s];
+      }
+    }
+    // codes and scaled errors of this row's 16 columns, one store each
+    {
+      const int c = 16 * tt + q;
+      if (rv && c < bw) {
+        const double e = d_own * rdiag[c];
+        codes[r * ldc + j0 + c] = (uint8_t)(k_own + zero);
+        E[r * lde + j0 + c] = (float)e;
+        loss += e * e;
       }
     }
 #pragma unroll
-    for (int s = 0; s < 31; ++s) w[s] = w[s + 1];
-    w[31] = 0.0;
+    for (int s = 0; s < 7; ++s) w[s] = w[s + 1];
+    w[7] = 0.0;
   }
   loss += quad_xor1(loss);
   loss += quad_xor2(loss);
-  if (rv && q4 == 0) row_loss[r] += loss;
+  loss += row_ror4(loss);
+  loss += row_ror8(loss);
+  if (rv && q == 0) row_loss[r] += loss;
 }
 
 // ---------------------------------------------------------------- layout
@@ -474,7 +520,7 @@ static gptq_status launch_sweep(hipStream_t st, int nw, const uint16_t* Wsrc, in
                                 int64_t rows, int64_t j0, int bw, int bits, float* E, int64_t lde,
                                 uint8_t* codes, int64_t ldc, uint16_t* scales, uint16_t* zeros,
                                 int64_t ldg, double* row_loss, unsigned* status) {
-  const unsigned nblk = (unsigned)cdiv(rows, 16 * nw);
+  const unsigned nblk = (unsigned)cdiv(rows, 4 * nw);
   GPTQ_LAUNCH(K_Q_SWEEP, st,
               q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, wblk, U, cols, vecU, rows,
                                                            j0, bw, bits, E, lde, codes, ldc,
@@ -495,10 +541,12 @@ extern "C" size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int 
 
 extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
                                            const float* U, const int32_t* perm, int bits,
-                                           int group_size, uint8_t* codes, uint16_t* scales,
-                                           uint16_t* zeros, int32_t* g_idx, double* row_loss,
-                                           void* ws, size_t ws_bytes, void* stream) {
+                                           int group_size, uint32_t flags, uint8_t* codes,
+                                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                                           double* row_loss, void* ws, size_t ws_bytes,
+                                           void* stream) {
   if (rows < 0 || cols < 0) return GPTQ_EINVAL;
+  if (flags & ~GPTQ_FLAG_NO_SYNC) return GPTQ_EINVAL;
   if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
   if (rows == 0 || cols == 0) return GPTQ_OK;
   if (!W || !U || !codes || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
@@ -535,7 +583,9 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
     ldws = cols;
     csw = codes_s;
   }
-  const int nw = 4;
+  // 4 rows per wave; 8 waves per workgroup once that still gives >= 256
+  // workgroups, else 4 (the U slab fills most of the LDS: one workgroup per CU)
+  const int nw = cdiv(rows, 32) >= 256 ? 8 : 4;
   const bool vecU = (cols % 4 == 0) && ((uintptr_t)U % 16 == 0);
   const int64_t rt = cdiv(rows, 64);
   double* wblk = (double*)(base + L.off_wblk);
@@ -575,10 +625,6 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
                 q_finalize_kernel<<<grid, 256, 0, st>>>(codes_s, invperm, rows, cols, group_size,
                                                         codes, g_idx, status));
   }
-  unsigned h_status = 0;
-  GPTQ_HIP(hipMemcpyAsync(&h_status, status, sizeof(unsigned), hipMemcpyDeviceToHost, st));
-  GPTQ_HIP(hipStreamSynchronize(st));
-  if (h_status & ST_BADPERM) return GPTQ_EINVAL;
-  if (h_status & ST_NONFINITE) return GPTQ_ENONFINITE;
-  return GPTQ_OK;
+  if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
+  return gptq_workspace_status(ws, stream);
 }

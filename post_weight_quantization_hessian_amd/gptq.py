@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(HERE, "libgptq.so")
 GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTSPD, GPTQ_EHIP, GPTQ_EWORKSPACE, GPTQ_ENONFINITE = range(6)
 GPTQ_FLAG_ACT_ORDER = 1
 GPTQ_FLAG_HESSIAN_OVERWRITE = 2
+GPTQ_FLAG_NO_SYNC = 4
 
 EXPORTS = {
     "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
@@ -32,9 +33,10 @@ EXPORTS = {
                                     C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "gptq_quantize_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int]),
     "gptq_quantize_layer": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
-                                      C.c_void_p, C.c_int, C.c_int, C.c_void_p, C.c_void_p,
-                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
-                                      C.c_void_p]),
+                                      C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_void_p,
+                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                      C.c_size_t, C.c_void_p]),
+    "gptq_workspace_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
     "gptq_version": (C.c_int, []),
@@ -140,8 +142,9 @@ def prepare_workspace_bytes(in_features: int) -> int:
 
 
 def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
-                 workspace=None, out=None):
-    """Damped, optionally act-ordered Hessian -> (perm int32 [i], U fp32 [i x i])."""
+                 workspace=None, out=None, sync: bool = True):
+    """Damped, optionally act-ordered Hessian -> (perm int32 [i], U fp32 [i x i]).
+    ``sync=False`` returns after enqueueing; check with workspace_status()."""
     torch = _torch()
     _need(S, torch.float64, "S", 2)
     i = S.shape[0]
@@ -154,7 +157,7 @@ def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
         perm, U = out
     if workspace is None:
         workspace = _workspace(prepare_workspace_bytes(i), S.device)
-    flags = GPTQ_FLAG_ACT_ORDER if act_order else 0
+    flags = (GPTQ_FLAG_ACT_ORDER if act_order else 0) | (0 if sync else GPTQ_FLAG_NO_SYNC)
     st = lib.gptq_prepare_hinv(_ptr(S), i, int(n_tokens), float(damp), flags, _ptr(perm), _ptr(U),
                                _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_prepare_hinv")
@@ -179,9 +182,10 @@ def quantize_workspace_bytes(rows: int, cols: int, group_size: int) -> int:
 
 
 def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, workspace=None,
-                   out=None):
+                   out=None, sync: bool = True):
     """Sweep the fp16 weights W [rows x cols] with the factor U (and perm).
-    ``out`` may be a QuantizedLayer whose tensors are reused."""
+    ``out`` may be a QuantizedLayer whose tensors are reused; ``sync=False``
+    returns after enqueueing (check with workspace_status())."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(U, torch.float32, "U", 2)
@@ -209,11 +213,18 @@ def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, worksp
     if workspace is None:
         workspace = _workspace(quantize_workspace_bytes(rows, cols, group_size), dev)
     st = lib.gptq_quantize_layer(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
-                                 _ptr(perm), int(bits), int(group_size), _ptr(codes),
+                                 _ptr(perm), int(bits), int(group_size),
+                                 0 if sync else GPTQ_FLAG_NO_SYNC, _ptr(codes),
                                  _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(row_loss),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_quantize_layer")
     return QuantizedLayer(codes, scales, zeros, g_idx, row_loss, bits, group_size)
+
+
+def workspace_status(workspace):
+    """Synchronize the current stream and return the status left in a
+    workspace by an asynchronous prepare_hinv / quantize_layer (raises on error)."""
+    _check(lib.gptq_workspace_status(_ptr(workspace), _stream()), "gptq_workspace_status")
 
 
 # ---------------------------------------------------------------- utilities

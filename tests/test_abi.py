@@ -74,8 +74,8 @@ def test_invalid_arguments_rejected_on_host():
     def q(**kw):
         a = args(**kw)
         return L.gptq_quantize_layer(a["W"], a["rows"], a["cols"], a["ldw"], a["U"], a["perm"],
-                                     a["bits"], a["gs"], a["codes"], a["scales"], a["zeros"],
-                                     a["g_idx"], a["loss"], a["ws"], a["wsb"], NULL)
+                                     a["bits"], a["gs"], a.get("flags", 0), a["codes"], a["scales"],
+                                     a["zeros"], a["g_idx"], a["loss"], a["ws"], a["wsb"], NULL)
     assert q(bits=1) == g.GPTQ_EINVAL
     assert q(bits=9) == g.GPTQ_EINVAL
     assert q(gs=48) == g.GPTQ_EINVAL
@@ -86,7 +86,9 @@ def test_invalid_arguments_rejected_on_host():
     assert q(rows=-1) == g.GPTQ_EINVAL
     assert q(ws=NULL) == g.GPTQ_EWORKSPACE
     assert q(wsb=16) == g.GPTQ_EWORKSPACE
+    assert q(flags=8) == g.GPTQ_EINVAL
     assert q(rows=0) == g.GPTQ_OK and q(cols=0) == g.GPTQ_OK  # empty: no-op
+    assert L.gptq_workspace_status(NULL, NULL) == g.GPTQ_EINVAL
     # prepare
     pw = L.gptq_prepare_hinv
     assert pw(NULL, 8, 10, 0.01, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
@@ -94,6 +96,7 @@ def test_invalid_arguments_rejected_on_host():
     assert pw(FAKE, 8, 10, -0.1, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, float("nan"), 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, 0.01, 8, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, 0.01, 2, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, 0.01, 0, FAKE, FAKE, FAKE, 64, NULL) == g.GPTQ_EWORKSPACE
     assert pw(FAKE, 0, 10, 0.01, 0, NULL, NULL, NULL, 0, NULL) == g.GPTQ_OK
     # hessian
