@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the "
+                         "reference transfer for hardware traffic counters) and exit")
     return ap.parse_args()
 
 
@@ -108,7 +111,17 @@ class HPlan:
 
 # ---------------------------------------------------------------- CPU oracle
 
+CPU_FLOP_BUDGET = 2.5e11   # accumulate sample: tokens x dim^2 x 2 flops
+CPU_FACTOR_DIM = 6144      # larger Hessians are factored on a leading sub-block
+
+
 def cpu_baseline(wl, host_inputs, sample_rows):
+    """The fp64 oracle timed on a bounded sample of one step's work, scaled to
+    the whole step by each phase's operation count: the accumulate on a token
+    sample (x tokens), the damping/act-order/factor on the full Hessian or,
+    above CPU_FACTOR_DIM features, on its leading sub-block (x dim^3), and the
+    strict sweep on a row sample (x rows, x dim^2 when the factor was a
+    sub-block)."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -117,31 +130,34 @@ def cpu_baseline(wl, host_inputs, sample_rows):
         threads = os.cpu_count()
     t_total = 0.0
     sampled = []
-    for hname, (X, W) in host_inputs.items():
-        chunks = [X[s:s + wl.token_chunk] for s in range(0, X.shape[0], wl.token_chunk)]
+    for hname, (Xs, W) in host_inputs.items():
+        dim = Xs.shape[1]
+        n_s = int(min(wl.n_tokens, Xs.shape[0], max(256, CPU_FLOP_BUDGET // (2 * dim * dim))))
         t0 = time.perf_counter()
-        S, n = O.hessian_sum(chunks)
-        t1 = time.perf_counter()
-        H = O.damped_hessian(S, n, wl.damp)
-        perm = O.act_order_perm(H) if wl.act_order else np.arange(H.shape[0])
-        Hp = O.permute_sym(H, perm)
-        U = O.hinv_upper(Hp)
-        t2 = time.perf_counter()
+        S, n = O.hessian_sum([Xs[:n_s]])
+        t_acc = (time.perf_counter() - t0) * wl.n_tokens / n_s
+        d_s = min(dim, CPU_FACTOR_DIM)
+        t0 = time.perf_counter()
+        H = O.damped_hessian(S[:d_s, :d_s], n, wl.damp)
+        perm = O.act_order_perm(H) if wl.act_order else np.arange(d_s)
+        U = O.hinv_upper(O.permute_sym(H, perm))
+        t_fac = (time.perf_counter() - t0) * (dim / d_s) ** 3
         rows = W.shape[0]
         rs = min(rows, sample_rows)
-        Wp = W[:rs].astype(np.float64)[:, perm]
-        ts = 0.0
+        Wp = W[:rs, :d_s].astype(np.float64)[:, perm]
+        t_sw = 0.0
         for bits in wl.bits:
-            t3 = time.perf_counter()
+            t0 = time.perf_counter()
             O.gptq_sweep(Wp, U, bits, wl.group_size)
-            ts += time.perf_counter() - t3
-        t_total += (t1 - t0) + (t2 - t1) + ts * rows / rs
-        sampled.append(f"{hname}: accumulate {X.shape[0]}x{X.shape[1]} + factor "
-                       f"{H.shape[0]} in full, strict sweep on {rs}/{rows} rows "
-                       f"(scaled by rows)")
+            t_sw += (time.perf_counter() - t0) * (rows / rs) * (dim / d_s) ** 2
+        t_total += t_acc + t_fac + t_sw
+        sampled.append(f"{hname}: accumulate {n_s}/{wl.n_tokens} tokens x {dim}, "
+                       f"damp/act-order/factor {d_s}/{dim} features, strict sweep "
+                       f"{rs}/{rows} rows x {d_s} columns x {len(wl.bits)} widths")
     weights = wl.weights_per_step()
     return {"value": weights / t_total, "unit": "weights/s", "cores": int(threads),
-            "kind": "oracle", "sample": "; ".join(sampled),
+            "kind": "oracle", "sample": "; ".join(sampled) + " (each phase scaled to the "
+            "full step by its operation count)",
             "seconds_per_step_extrapolated": t_total}
 
 
@@ -154,45 +170,44 @@ def main():
               "on one MI355X (multi-GPU sharding is design-only).", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": nbytes, "launches": 5}), flush=True)
+        return
     from post_weight_quantization_hessian_amd import synth
     from post_weight_quantization_hessian_amd.workloads import WORKLOADS
     import post_weight_quantization_hessian_amd.gptq as G
+    from post_weight_quantization_hessian_amd.pipeline import LayerGroup
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    # ---- inputs, resident on the device
+    # ---- inputs, resident on the device (host copies kept only for the
+    # oracle's token sample)
     host_inputs = {}
     dev_inputs = {}
     plan = []
     for h in wl.inputs:
+        print(f"[bench] generating {h.name}: {wl.n_tokens} x {h.dim}", file=sys.stderr, flush=True)
         X = synth.activations(wl.wid, h.name, wl.n_tokens, h.dim, kind=h.kind,
                               lognormal_sigma=h.lognormal_sigma)
         Ws = [synth.weights(wl.wid, l.name, l.rows, h.dim, outlier_frac=l.outlier_frac)
               for l in wl.layers_of(h.name)]
         W = np.concatenate(Ws, axis=0)
-        host_inputs[h.name] = (X, W)
-        Xd = torch.from_numpy(X).to(dev)
-        Wd = torch.from_numpy(W).to(dev)
-        chunks = [Xd[s:s + wl.token_chunk] for s in range(0, wl.n_tokens, wl.token_chunk)]
-        S = torch.empty((h.dim, h.dim), dtype=torch.float64, device=dev)
-        hws = torch.empty(max(G.hessian_workspace_bytes(h.dim, c.shape[0]) for c in chunks) or 1,
-                          dtype=torch.uint8, device=dev)
-        pws = torch.empty(G.prepare_workspace_bytes(h.dim), dtype=torch.uint8, device=dev)
-        perm = torch.empty(h.dim, dtype=torch.int32, device=dev)
-        U = torch.empty((h.dim, h.dim), dtype=torch.float32, device=dev)
-        qws = torch.empty(G.quantize_workspace_bytes(W.shape[0], h.dim, wl.group_size),
-                          dtype=torch.uint8, device=dev)
-        outs = [G.QuantizedLayer(
-            torch.empty(W.shape, dtype=torch.uint8, device=dev),
-            torch.empty((W.shape[0], -(-h.dim // wl.group_size)), dtype=torch.float16, device=dev),
-            torch.empty((W.shape[0], -(-h.dim // wl.group_size)), dtype=torch.float16, device=dev),
-            torch.empty(h.dim, dtype=torch.int32, device=dev),
-            torch.empty(W.shape[0], dtype=torch.float64, device=dev), b, wl.group_size)
-            for b in wl.bits]
-        dev_inputs[h.name] = dict(chunks=chunks, W=Wd, S=S, hws=hws, pws=pws, perm=perm, U=U,
-                                  qws=qws, outs=outs)
+        chunks = [torch.from_numpy(X[s:s + wl.token_chunk]).to(dev)
+                  for s in range(0, wl.n_tokens, wl.token_chunk)]
+        host_inputs[h.name] = (X[:min(wl.n_tokens, 16384)].copy(), W)
+        del X
+        grp = LayerGroup(h.dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
+                         bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
+                         damp=wl.damp, device=dev)
+        dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
         plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0]))
     torch.cuda.synchronize()
 
@@ -203,29 +218,21 @@ def main():
 
     def step():
         for h, s in zip(wl.inputs, streams):
-            d = dev_inputs[h.name]
+            chunks, Wd, grp = dev_inputs[h.name]
             with torch.cuda.stream(s):
-                for ci, c in enumerate(d["chunks"]):
-                    G.hessian_accumulate(d["S"], c, workspace=d["hws"], overwrite=(ci == 0))
-                G.prepare_hinv(d["S"], wl.n_tokens, damp=wl.damp, act_order=wl.act_order,
-                               workspace=d["pws"], out=(d["perm"], d["U"]), sync=False)
-                for bi, bits in enumerate(wl.bits):
-                    G.quantize_layer(d["W"], d["U"], d["perm"] if wl.act_order else None,
-                                     bits=bits, group_size=wl.group_size, workspace=d["qws"],
-                                     out=d["outs"][bi], sync=False)
+                grp.enqueue(chunks, Wd)
 
     def check_status():
         for h, s in zip(wl.inputs, streams):
-            d = dev_inputs[h.name]
             with torch.cuda.stream(s):
-                G.workspace_status(d["pws"])
-                G.workspace_status(d["qws"])
+                dev_inputs[h.name][2].check()
 
     # ---- warmup: all kernels timed to find the dominant class
     G.profile_enable(True)
     for _ in range(max(args.warmup, 1)):
         step()
     torch.cuda.synchronize()
+    check_status()
     prof_warm = G.profile_read()
     G.profile_enable(False)
     dominant = max(prof_warm, key=lambda k: prof_warm[k][0])

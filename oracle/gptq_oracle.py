@@ -53,8 +53,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "NotSPD", "NonFinite", "hessian_sum", "hessian_entry", "damped_hessian",
-    "act_order_perm", "permute_sym", "hinv_upper", "fp16_round", "group_grid",
+    "NotSPD", "NonFinite", "hessian_sum", "hessian_entry", "hessian_diag",
+    "damping_lambda", "damped_diagonal", "damped_hessian", "act_order_from_diag", "act_order_perm", "permute_sym", "hinv_upper", "fp16_round", "group_grid",
     "gptq_sweep", "gptq_layer", "rtn_quantize", "dequantize_sweep",
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups",
@@ -108,20 +108,59 @@ def hessian_entry(X, f, g):
     return math.fsum((a * b).tolist())
 
 
-def damped_hessian(S, n_tokens, damp):
-    """H = (2/n) S + damp * mean(diag((2/n) S)) * I   ([CHMC] Schritt 2)."""
+def hessian_diag(chunks):
+    """diag(S) = sum_t X[t,f]^2 for every feature f in fp64, without forming
+    S (the diagonal of ``hessian_sum``; for Hessians too large for the CPU)."""
+    if isinstance(chunks, np.ndarray):
+        chunks = [chunks]
+    d = None
+    n = 0
+    for X in chunks:
+        Xd = np.asarray(X, dtype=np.float32).astype(F64)
+        part = np.einsum("tf,tf->f", Xd, Xd)
+        d = part if d is None else d + part
+        n += Xd.shape[0]
+    return d, n
+
+
+def damping_lambda(diag_S, n_tokens, damp):
+    """lambda = damp * mean(diag((2/n) S))   ([CHMC] Schritt 2)."""
+    if n_tokens <= 0:
+        raise ValueError("n_tokens must be positive")
+    return damp * float(np.mean((2.0 / n_tokens) * np.asarray(diag_S, dtype=F64)))
+
+
+def damped_diagonal(diag_S, n_tokens, damp):
+    """diag of the damped Hessian, (2/n) diag(S) + lambda, and lambda, from
+    diag(S) alone ([CHMC] Schritt 2)."""
+    lam = damping_lambda(diag_S, n_tokens, damp)
+    return (2.0 / n_tokens) * np.asarray(diag_S, dtype=F64) + lam, lam
+
+
+def damped_hessian(S, n_tokens, damp, lam=None):
+    """H = (2/n) S + damp * mean(diag((2/n) S)) * I   ([CHMC] Schritt 2).
+
+    ``lam`` overrides the damping term when S is a principal block of a
+    larger Hessian, whose mean diagonal the block alone does not give."""
     if n_tokens <= 0:
         raise ValueError("n_tokens must be positive")
     H = (2.0 / n_tokens) * np.asarray(S, dtype=F64)
-    lam = damp * float(np.mean(np.diag(H)))
+    if lam is None:
+        lam = damping_lambda(np.diag(S), n_tokens, damp)
     H = H + lam * np.eye(H.shape[0])
     return H
 
 
+def act_order_from_diag(hdiag):
+    """Columns in descending importance = descending diagonal of the damped
+    Hessian, ties kept in index order ([CHMC] Schritt 2 "act-order";
+    [BABAI] 2.3)."""
+    return np.argsort(-np.asarray(hdiag, dtype=F64), kind="stable").astype(np.int64)
+
+
 def act_order_perm(H):
-    """Columns in descending importance = descending diag(H), stable
-    ([CHMC] Schritt 2 "act-order"; [BABAI] 2.3)."""
-    return np.argsort(-np.diag(H), kind="stable").astype(np.int64)
+    """act-order permutation of a full damped Hessian."""
+    return act_order_from_diag(np.diag(H))
 
 
 def permute_sym(H, perm):

@@ -1,0 +1,67 @@
+"""One calibration input and the layers that read it, end to end on the GPU.
+
+Holds every device buffer the three library calls need (the Hessian, the
+workspaces, the act-order permutation, the factor U and one output set per
+bit width), allocated once, and enqueues the whole hot path asynchronously
+on the current stream:
+
+    S  = sum over token chunks of X_c^T X_c        (first chunk overwrites S)
+    perm, U = factor of the damped, act-ordered inverse Hessian
+    codes, scales, zeros, g_idx, row_loss          for every bit width
+
+Layers that read the same input are quantized together by stacking their
+weight rows. Argument marshalling only: every step runs in the HIP library.
+"""
+from __future__ import annotations
+
+from . import gptq as G
+
+
+class LayerGroup:
+    def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
+                 device):
+        import torch
+        self.dim, self.rows = int(dim), int(rows)
+        self.bits, self.group_size = tuple(bits), int(group_size)
+        self.act_order, self.damp = bool(act_order), float(damp)
+        ng = -(-self.dim // self.group_size)
+        self.S = torch.empty((self.dim, self.dim), dtype=torch.float64, device=device)
+        self.hws = torch.empty(max(G.hessian_workspace_bytes(self.dim, max_chunk_tokens), 1),
+                               dtype=torch.uint8, device=device)
+        self.pws = torch.empty(G.prepare_workspace_bytes(self.dim), dtype=torch.uint8,
+                               device=device)
+        self.perm = torch.empty(self.dim, dtype=torch.int32, device=device)
+        self.U = torch.empty((self.dim, self.dim), dtype=torch.float32, device=device)
+        # one quantize workspace per bit width: each call clears the status
+        # word of its workspace, and the statuses are read after the last call
+        self.qws = [torch.empty(G.quantize_workspace_bytes(self.rows, self.dim, self.group_size),
+                                dtype=torch.uint8, device=device) for _ in self.bits]
+        self.outs = [G.QuantizedLayer(
+            torch.empty((self.rows, self.dim), dtype=torch.uint8, device=device),
+            torch.empty((self.rows, ng), dtype=torch.float16, device=device),
+            torch.empty((self.rows, ng), dtype=torch.float16, device=device),
+            torch.empty(self.dim, dtype=torch.int32, device=device),
+            torch.empty(self.rows, dtype=torch.float64, device=device), b, self.group_size)
+            for b in self.bits]
+
+    def enqueue(self, chunks, W):
+        """The whole path for token chunks ``chunks`` (fp32 [n_c x dim] each)
+        and stacked fp16 weights ``W`` [rows x dim], without synchronizing."""
+        n = 0
+        for ci, c in enumerate(chunks):
+            G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0))
+            n += int(c.shape[0])
+        G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
+                       workspace=self.pws, out=(self.perm, self.U), sync=False)
+        for bi, b in enumerate(self.bits):
+            G.quantize_layer(W, self.U, self.perm if self.act_order else None, bits=b,
+                             group_size=self.group_size, workspace=self.qws[bi],
+                             out=self.outs[bi], sync=False)
+        return self.outs
+
+    def check(self):
+        """Synchronize and raise GPTQError if prepare or quantize reported one
+        (a non-SPD Hessian, non-finite values, an invalid permutation)."""
+        G.workspace_status(self.pws)
+        for ws in self.qws:
+            G.workspace_status(ws)

@@ -1,0 +1,202 @@
+"""Full-size parity of the two largest layer workloads, in the launch
+configuration the benchmark times (LayerGroup.enqueue: chunked accumulate
+with overwrite on the first chunk, asynchronous prepare and quantize).
+
+* 8B-shape down projection 4096 x 14336: 131072 calibration tokens in 8192-
+  token chunks, 0.1 % outlier input columns, 3-bit groups of 128, act-order.
+* 70B-shape down projection 8192 x 28672: 65536 tokens with log-normal channel
+  scales, 2-bit and 4-bit groups of 64, act-order.
+
+Their Hessians are out of the oracle's reach as a whole, so it computes what it
+can one piece at a time:
+
+* sampled entries of S, each the exactly rounded sum over all tokens;
+* diag S of every feature, the damping term and the act-order permutation;
+* the trailing 256 x 256 block of U: with U^T U = H_p^-1 and R = U^-1, H_p =
+  R R^T, so that block depends only on the trailing block of H_p, which the
+  oracle forms and factors;
+* the first group of every row: nothing has been propagated into it yet, so
+  its grid and its first column's codes are round-to-nearest of the weights.
+
+and properties of the library's outputs hold at any size:
+
+* U H_p = R^T is lower triangular with diagonal 1/U_jj (sampled rows of U);
+* sum_j e_j^2 = (w - q) H (w - q)^T (the loss identity, sampled rows);
+* codes, zero points and g_idx are valid; a second run is bit-identical.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle as O
+from post_weight_quantization_hessian_amd import synth
+from post_weight_quantization_hessian_amd.workloads import WORKLOADS
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a HIP device", allow_module_level=True)
+
+from post_weight_quantization_hessian_amd.pipeline import LayerGroup  # noqa: E402
+
+DEV = torch.device("cuda:0")
+F64 = np.float64
+
+S_SAMPLES = 40
+TRAIL = 256
+# |(U H_p)[j, k>j]| <= U_TOL (|U| |H_p|)[j, k]: storing U in fp32 alone
+# leaves about 3e-8 (2^-24 per entry).
+U_TOL = 4e-7
+# loss identity with the fp32-stored U: about 1e-7 at the medium shapes
+LOSS_ID_TOL = 1e-4
+HOST_CHUNK = 8192
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def host_chunks(X):
+    return [X[s:s + HOST_CHUNK] for s in range(0, X.shape[0], HOST_CHUNK)]
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("wname", ["llama8b_down", "llama70b_down"])
+def test_fullsize_sampled(wname):
+    wl = WORKLOADS[wname]
+    (h,) = wl.inputs
+    dim, n, gsz = h.dim, wl.n_tokens, wl.group_size
+    t0 = time.time()
+    say(f"{wname}: generating X {n} x {dim}")
+    X = synth.activations(wl.wid, h.name, n, dim, kind=h.kind, lognormal_sigma=h.lognormal_sigma)
+    W = np.concatenate([synth.weights(wl.wid, l.name, l.rows, dim, outlier_frac=l.outlier_frac)
+                        for l in wl.layers_of(h.name)], axis=0)
+    rows = W.shape[0]
+    say(f"{wname}: inputs ready after {time.time() - t0:.0f} s; path run 1")
+    chunks = [torch.from_numpy(X[s:s + wl.token_chunk]).to(DEV)
+              for s in range(0, n, wl.token_chunk)]
+    Wd = torch.from_numpy(W).to(DEV)
+    grp = LayerGroup(dim, rows, max_chunk_tokens=max(c.shape[0] for c in chunks), bits=wl.bits,
+                     group_size=gsz, act_order=wl.act_order, damp=wl.damp, device=DEV)
+    grp.enqueue(chunks, Wd)
+    grp.check()
+    first = dict(S=grp.S.clone(), U=grp.U.clone(), perm=grp.perm.clone(),
+                 outs=[(q.codes.clone(), q.scales.clone(), q.zeros.clone(), q.row_loss.clone())
+                       for q in grp.outs])
+    say(f"{wname}: path run 2 (determinism)")
+    grp.enqueue(chunks, Wd)
+    grp.check()
+    assert torch.equal(first["S"], grp.S) and torch.equal(first["U"], grp.U)
+    assert torch.equal(first["perm"], grp.perm)
+    for (c, s, z, l), q in zip(first["outs"], grp.outs):
+        assert torch.equal(c, q.codes) and torch.equal(s, q.scales)
+        assert torch.equal(z, q.zeros) and torch.equal(l, q.row_loss)
+    del first, chunks
+    torch.cuda.empty_cache()
+
+    S, U = grp.S, grp.U
+    perm = grp.perm.cpu().numpy().astype(np.int64)
+    rng = np.random.default_rng(20240 + wl.wid)
+
+    # ---- S: sampled entries against exactly rounded sums
+    say(f"{wname}: sampled Hessian entries")
+    fs = rng.integers(0, dim, S_SAMPLES)
+    gs_ = rng.integers(0, dim, S_SAMPLES)
+    pairs = list(zip(fs.tolist(), gs_.tolist())) + [(f, f) for f in fs[:8].tolist()]
+    pairs += [(0, dim - 1), (dim - 1, dim - 1), (dim - 1, 0), (0, 0)]
+    fi = torch.tensor([p[0] for p in pairs], device=DEV)
+    gi = torch.tensor([p[1] for p in pairs], device=DEV)
+    Sg = S[fi, gi].cpu().numpy()
+    assert np.array_equal(Sg, S[gi, fi].cpu().numpy()), "S is not exactly symmetric"
+    worst = 0.0
+    for k, (f, g) in enumerate(pairs):
+        exact = O.hessian_entry(X, f, g)
+        mag = float(np.abs(X[:, f].astype(F64) * X[:, g].astype(F64)).sum())
+        err = abs(Sg[k] - exact)
+        assert err <= n * 2.0 ** -53 * mag, (f, g, Sg[k], exact)
+        worst = max(worst, err / mag)
+    assert worst < 1e-13, worst
+
+    # ---- diag, damping, act-order
+    say(f"{wname}: diagonal and act-order")
+    d, nn = O.hessian_diag(host_chunks(X))
+    assert nn == n
+    dg = torch.diagonal(S).cpu().numpy()
+    assert np.max(np.abs(dg - d) / d) < 1e-13
+    hdiag, lam = O.damped_diagonal(d, n, wl.damp)
+    pr = O.act_order_from_diag(hdiag)
+    assert np.array_equal(np.sort(perm), np.arange(dim))
+    for k in np.nonzero(perm != pr)[0]:  # only inside classes of near-equal diagonals
+        assert abs(hdiag[perm[k]] - hdiag[pr[k]]) <= 1e-12 * hdiag[pr[k]], k
+
+    # ---- trailing block of U from the trailing block of H_p alone
+    say(f"{wname}: trailing {TRAIL}x{TRAIL} block of U")
+    assert np.array_equal(perm[-TRAIL:], pr[-TRAIL:])
+    cols_b = pr[-TRAIL:]
+    Sb, _ = O.hessian_sum([c[:, cols_b] for c in host_chunks(X)])
+    Ub = O.hinv_upper(O.damped_hessian(Sb, n, wl.damp, lam=lam))
+    Ug = U[-TRAIL:, -TRAIL:].double().cpu().numpy()
+    rowmax = np.abs(Ub).max(axis=1, keepdims=True)
+    bound = 2.0 ** -23 * np.abs(Ub) + 1e-7 * rowmax
+    assert np.all(np.abs(Ug - Ub) <= bound), float(np.max(np.abs(Ug - Ub) / rowmax))
+
+    # ---- U H_p lower triangular, diagonal 1/U_jj (sampled rows of U)
+    say(f"{wname}: U H_p on sampled rows")
+    Hd = S * (2.0 / n)
+    Hd.diagonal().add_(lam)
+    pt = torch.from_numpy(perm).to(DEV)
+    J = sorted(set([0, 1, dim // 3, dim // 2, dim - TRAIL - 1, dim - 2, dim - 1]
+                   + rng.integers(0, dim, 5).tolist()))
+    Urows = U[J].double()
+    jt = torch.tensor(J, device=DEV)
+    cols = torch.arange(dim, device=DEV)
+    assert torch.all(Urows[cols[None, :] < jt[:, None]] == 0), "U has entries below the diagonal"
+    V = torch.zeros_like(Urows)
+    V[:, pt] = Urows  # back to the original column order
+    Y = (V @ Hd)[:, pt]
+    A = (V.abs() @ Hd.abs())[:, pt]
+    upper = cols[None, :] > jt[:, None]
+    ratio = (Y.abs() / A)[upper]
+    assert float(ratio.max()) <= U_TOL, float(ratio.max())
+    ydiag = Y[torch.arange(len(J), device=DEV), jt]
+    udiag = Urows[torch.arange(len(J), device=DEV), jt]
+    dres = (ydiag - 1.0 / udiag).abs() / A[torch.arange(len(J), device=DEV), jt]
+    assert float(dres.max()) <= U_TOL, float(dres.max())
+
+    # ---- sweep outputs, per bit width
+    Wp = W.astype(F64)[:, pr]
+    g_ref = np.empty(dim, dtype=np.int64)
+    g_ref[pr] = np.arange(dim) // gsz
+    for bi, bits in enumerate(wl.bits):
+        say(f"{wname}: sweep outputs, {bits}-bit")
+        q = grp.outs[bi]
+        codes = q.codes.cpu().numpy().astype(np.int64)
+        scales = q.scales.cpu().numpy().astype(F64)
+        zeros = q.zeros.cpu().numpy().astype(F64)
+        row_loss = q.row_loss.cpu().numpy()
+        maxq = 2 ** bits - 1
+        assert codes.min() >= 0 and codes.max() <= maxq
+        assert np.all(zeros == np.rint(zeros)) and zeros.min() >= 0 and zeros.max() <= maxq
+        assert np.all(np.isfinite(scales)) and np.all(scales > 0)
+        assert np.array_equal(q.g_idx.cpu().numpy().astype(np.int64), g_ref)
+        # first group: round-to-nearest of the untouched weights
+        c_rtn, s_rtn, z_rtn = O.rtn_quantize(Wp[:, :gsz], bits, gsz)
+        assert np.array_equal(scales[:, 0], s_rtn[:, 0])
+        assert np.array_equal(zeros[:, 0], z_rtn[:, 0])
+        assert np.array_equal(codes[:, pr[0]], c_rtn[:, 0])
+        # loss identity on sampled rows
+        R = np.sort(rng.choice(rows, 16, replace=False))
+        deq = O.dequantize_sweep(codes[R][:, pr], scales[R], zeros[R], gsz)
+        D = np.empty((len(R), dim))
+        D[:, pr] = Wp[R] - deq
+        Dt = torch.from_numpy(D).to(DEV)
+        lq = ((Dt @ Hd) * Dt).sum(dim=1).cpu().numpy()
+        rel = np.abs(lq / row_loss[R] - 1.0)
+        say(f"{wname}/{bits}-bit: loss identity max rel {rel.max():.2e}; "
+            f"mean row loss {row_loss.mean():.4e}")
+        assert rel.max() <= LOSS_ID_TOL, rel
+    say(f"{wname}: done after {time.time() - t0:.0f} s")

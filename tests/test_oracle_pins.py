@@ -67,6 +67,39 @@ def test_act_order_hand_example():
     assert O.act_order_perm(H).tolist() == g["perm"]
 
 
+def test_hessian_diag_exact_and_lambda():
+    """diag(S) without forming S: small-integer activations give exact sums
+    (compared with exact rational arithmetic), and the damping term built
+    from it alone equals the one inside the full damped H."""
+    rng = np.random.default_rng(11)
+    X = rng.integers(-8, 9, size=(37, 9)).astype(np.float32)
+    d, n = O.hessian_diag([X[:20], X[20:]])
+    exact = [sum(Fraction(int(v)) ** 2 for v in X[:, f]) for f in range(9)]
+    assert n == 37 and [Fraction(v) for v in d] == exact
+    S, _ = O.hessian_sum(X)
+    lam = O.damping_lambda(d, n, 0.01)
+    H = O.damped_hessian(S, n, 0.01)
+    assert np.array_equal(np.diag(H), (2.0 / n) * np.diag(S) + lam)
+    hd, lam2 = O.damped_diagonal(d, n, 0.01)
+    assert lam2 == lam and np.array_equal(hd, np.diag(H))
+    assert O.act_order_from_diag(hd).tolist() == O.act_order_perm(H).tolist()
+    Hb = O.damped_hessian(S[3:, 3:], n, 0.01, lam=lam)
+    assert np.array_equal(Hb, H[3:, 3:])
+
+
+def test_hinv_upper_trailing_block_depends_on_trailing_hessian_only():
+    """U^T U = H^-1 with U upper means H = R R^T with R = U^-1 upper, so the
+    trailing block of H is R_bb R_bb^T and the trailing block of U is the
+    factor of that block alone: columns swept last see only each other."""
+    X, W, S, n = _rand_problem(4, 40, 300, 5)
+    H = O.damped_hessian(S, n, 0.01)
+    U = O.hinv_upper(H)
+    for k in (1, 7, 16):
+        np.testing.assert_allclose(O.hinv_upper(H[-k:, -k:]), U[-k:, -k:], rtol=1e-9, atol=1e-12)
+    # the leading block does not have this property
+    assert not np.allclose(O.hinv_upper(H[:7, :7]), U[:7, :7], rtol=1e-6)
+
+
 # ---------------------------------------------------------------- factor U
 
 def test_hinv_upper_hand_2x2():
