@@ -41,6 +41,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
+    ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
+                                                              "COPY_WRITE"),
+                    help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of this benchmark, then of --calibrate-copy) into "
+                         "the HBM traffic summary under profiles/ and exit")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (the "
                          "reference transfer for hardware traffic counters) and exit")
@@ -109,6 +114,96 @@ class HPlan:
         self.name, self.dim, self.n, self.rows = name, dim, n, rows
 
 
+# ---------------------------------------------------------------- HBM traffic
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "post_weight_quantization_hessian_amd", "csrc")
+KERNEL_CLASS = {  # device function name -> timing class
+    "hess_tile_kernel": "hessian_tile", "hess_reduce_kernel": "hessian_reduce",
+    "chol_potrf_kernel": "chol_potrf", "chol_trsm_kernel": "chol_trsm",
+    "chol_syrk_kernel": "chol_syrk", "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x",
+    "trtri_diag_kernel": "trtri_diag", "q_gemm_kernel": "quant_gemm",
+    "q_sweep_kernel": "quant_sweep", "q_reduce_kernel": "quant_reduce",
+    "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout"}
+
+
+def source_hash():
+    """sha256 over the HIP sources: counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_path(workload):
+    return os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+
+
+def _pmc_per_class(folder):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    tot = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"]
+            key = next((c for k, c in KERNEL_CLASS.items() if f"::{k}" in name), None)
+            if key is None and "copyBuffer" in name:
+                key = "copy"
+            if key is None:
+                continue
+            v = tot.setdefault(key, [0.0, 0])
+            v[0] += float(r["Counter_Value"])
+            v[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in tot.items()}
+
+
+def counters_summary(args):
+    fetch, write, cfetch, cwrite = (_pmc_per_class(d) for d in args.counters_summary)
+    copy_bytes = 1 << 30
+    # KiB per dispatch that the same counter reads for a plain 1 GiB copy
+    f_fac = copy_bytes / (cfetch["copy"][0] * 1024.0)
+    w_fac = copy_bytes / (cwrite["copy"][0] * 1024.0)
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        if k == "copy":
+            continue
+        fb = fetch[k][0] * 1024.0 * f_fac
+        wb = write[k][0] * 1024.0 * w_fac
+        kernels[k] = {"fetch_kib_per_dispatch": fetch[k][0], "write_kib_per_dispatch": write[k][0],
+                      "dispatches": fetch[k][1], "bytes_per_launch": fb + wb,
+                      "read_bytes_per_launch": fb, "write_bytes_per_launch": wb}
+    out = {"workload": args.workload, "source_sha256": source_hash(),
+           "fetch_scale": f_fac, "write_scale": w_fac,
+           "copy_reference": "bench.py --calibrate-copy 1024 (1 GiB device copy, 5 dispatches)",
+           "commands": [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 "
+                        f"bench.py --workload {args.workload} --steps 2 --warmup 1 "
+                        "--no-cpu-baseline" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                       + [f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o run -- python3 "
+                          "bench.py --calibrate-copy 1024" for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "kernels": kernels}
+    with open(traffic_path(args.workload), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps({k: v["bytes_per_launch"] for k, v in kernels.items()}))
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary,
+    or None when there is none or the sources changed since it was taken."""
+    try:
+        d = json.load(open(traffic_path(workload)))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_sha256") != source_hash() or kernel not in d.get("kernels", {}):
+        return None
+    return d["kernels"][kernel]["bytes_per_launch"]
+
+
 # ---------------------------------------------------------------- CPU oracle
 
 CPU_FLOP_BUDGET = 2.5e11   # accumulate sample: tokens x dim^2 x 2 flops
@@ -165,6 +260,9 @@ def cpu_baseline(wl, host_inputs, sample_rows):
 
 def main():
     args = parse()
+    if args.counters_summary:
+        counters_summary(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the quantizer's hot path is measured "
               "on one MI355X (multi-GPU sharding is design-only).", file=sys.stderr)
@@ -256,6 +354,7 @@ def main():
     dom_ms, dom_launches = prof[dominant]
     work, unit, peak_key = kernel_work(dominant, wl, plan)
     roofline = None
+    traffic = measured_traffic(wl.name, dominant)
     if work is not None and dom_ms > 0:
         per_step_s = dom_ms / 1000.0 / args.steps
         if unit == "flop":
@@ -263,7 +362,7 @@ def main():
             peak = PEAK[peak_key]
             roofline = {"bound": "alu" if peak_key == "f64_vector" else "mfma",
                         "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                        "frac": achieved / peak, "traffic": None,
+                        "frac": achieved / peak, "traffic": traffic,
                         "kernel": dominant, "precision": peak_key,
                         "launches_per_step": dom_launches / args.steps,
                         "avg_launch_ms": dom_ms / max(dom_launches, 1),
@@ -272,7 +371,7 @@ def main():
         else:
             achieved = work / per_step_s / 1e9
             roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"],
-                        "unit": "GB/s", "frac": achieved / PEAK["hbm_gbs"], "traffic": None,
+                        "unit": "GB/s", "frac": achieved / PEAK["hbm_gbs"], "traffic": traffic,
                         "kernel": dominant, "launches_per_step": dom_launches / args.steps,
                         "avg_launch_ms": dom_ms / max(dom_launches, 1)}
 
