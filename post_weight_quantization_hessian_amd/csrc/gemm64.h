@@ -54,7 +54,10 @@ struct LdDirect64 {
 };
 
 // Global [col][k] (row stride ld) -> LDS [k][col] (transposing). In bounds.
-struct LdTrans64 {
+// NEG stores the negated values (a negated operand keeps the epilogue a plain
+// store, so the accumulators never leave the matrix registers).
+template <bool NEG>
+struct LdTrans64T {
   const double* base;
   int64_t ld;
   dbl2 r[4];
@@ -67,36 +70,37 @@ struct LdTrans64 {
     const int col = t >> 1, kh = (t & 1) * 8;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      s[(kh + 2 * q) * GLD + col] = r[q].x;
-      s[(kh + 2 * q + 1) * GLD + col] = r[q].y;
+      s[(kh + 2 * q) * GLD + col] = NEG ? -r[q].x : r[q].x;
+      s[(kh + 2 * q + 1) * GLD + col] = NEG ? -r[q].y : r[q].y;
     }
   }
 };
+using LdTrans64 = LdTrans64T<false>;
 
-// Double-buffered K loop. If `same` the B operand is the A operand (la only).
-template <class LA, class LB>
-__device__ inline void gemm64_loop(LA& la, LB& lb, bool same, int nchunks, double* sA, double* sB,
+// Double-buffered K loop; with SAME the B operand is the A operand (la only).
+// The body is straight-line: every iteration fetches the next chunk (the last
+// one re-fetches its own chunk, in bounds, into the buffer nobody reads any
+// more), so the accumulators stay in the matrix registers across iterations
+// instead of being copied out and back around a branchy loop.
+template <bool SAME, class LA, class LB>
+__device__ inline void gemm64_loop(LA& la, LB& lb, int nchunks, double* sA, double* sB,
                                    d4 (&acc)[4][4]) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
   la.fetch(0, t);
-  if (!same) lb.fetch(0, t);
+  if (!SAME) lb.fetch(0, t);
   la.store(sA, t);
-  if (!same) lb.store(sB, t);
+  if (!SAME) lb.store(sB, t);
   __syncthreads();
   for (int c = 0; c < nchunks; ++c) {
     const int cur = c & 1;
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      la.fetch(c + 1, t);
-      if (!same) lb.fetch(c + 1, t);
-    }
+    const int nx = c + 1 < nchunks ? c + 1 : c;
+    la.fetch(nx, t);
+    if (!SAME) lb.fetch(nx, t);
     const double* a = sA + cur * GCH;
-    const double* b = same ? a : sB + cur * GCH;
+    const double* b = SAME ? a : sB + cur * GCH;
     mfma64_chunk(a, b, acc, wm, wn, lane);
-    if (more) {
-      la.store(sA + (cur ^ 1) * GCH, t);
-      if (!same) lb.store(sB + (cur ^ 1) * GCH, t);
-    }
+    la.store(sA + (cur ^ 1) * GCH, t);
+    if (!SAME) lb.store(sB + (cur ^ 1) * GCH, t);
     __syncthreads();
   }
 }
@@ -128,6 +132,25 @@ __device__ inline void acc_update(const d4 (&acc)[4][4], double* C, int64_t ld, 
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         base[(int64_t)(i * 16 + 4 * r) * ld + j * 16] = old[i][j][r] + sign * acc[i][j][r];
+}
+
+// acc = the tile at C (leading dimension ld), in the accumulator layout;
+// entries at tile-local (row, col) with row >= rows or col >= cols read 0.
+// Loads are clamped into range and all issued before use.
+__device__ inline void acc_load(d4 (&acc)[4][4], const double* C, int64_t ld, int rows, int cols) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + i * 16 + (lane >> 4) + 4 * r;
+        const int col = wn * 64 + j * 16 + (lane & 15);
+        const bool ok = row < rows && col < cols;
+        const double v = C[ok ? (int64_t)row * ld + col : 0];
+        acc[i][j][r] = ok ? v : 0.0;
+      }
 }
 
 // Visit the tile's accumulators: f(row, col, value) with tile-local row/col.

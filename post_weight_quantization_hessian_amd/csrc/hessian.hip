@@ -12,32 +12,44 @@
 
 namespace gptq {
 
-// Global X[token][feature] fp32 -> LDS [k][col] fp64, masked at the token and
-// feature ends; vector loads when the rows are 16-byte aligned.
+// Global X[token][feature] fp32 -> LDS [k][col] fp64, zero outside the token
+// range and the feature range. Branch-free: indices are clamped into range
+// and every load is issued; which values are in range is kept as a mask and
+// applied when the chunk is stored, so the load is waited on only then (one
+// chunk of MFMAs later). With `vec` (rows 16-byte aligned, dim % 4 == 0) each
+// float4 is wholly in or out of range.
+template <bool VEC>
 struct LdX32 {
   const float* X;
   int64_t ldx, t_begin, t_end, dim, f0;
-  bool vec;
   f4 r[2];
+  unsigned ok;  // bit q: value q is in range
   __device__ void fetch(int c, int t) {
     const int64_t tok = t_begin + (int64_t)c * GK + (t >> 4);
+    const bool tok_ok = tok < t_end;
+    const float* row = X + (tok_ok ? tok : t_end - 1) * ldx;
     const int64_t f = f0 + (t & 15) * 8;
-    if (tok < t_end && vec && f + 7 < dim) {
-      const float* p = X + tok * ldx + f;
-      r[0] = *reinterpret_cast<const f4*>(p);
-      r[1] = *reinterpret_cast<const f4*>(p + 4);
+    ok = 0u;
+    if (VEC) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool in = tok_ok && f + 4 * h < dim;
+        r[h] = *reinterpret_cast<const f4*>(row + (in ? f + 4 * h : 0));
+        ok |= in ? 0xFu << (4 * h) : 0u;
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const float v = (tok < t_end && f + q < dim) ? X[tok * ldx + f + q] : 0.0f;
-        r[q >> 2][q & 3] = v;
+        const bool in = tok_ok && f + q < dim;
+        r[q >> 2][q & 3] = row[in ? f + q : 0];
+        ok |= in ? 1u << q : 0u;
       }
     }
   }
   __device__ void store(double* s, int t) const {
     double* d = s + (t >> 4) * GLD + (t & 15) * 8;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) d[q] = (double)r[q >> 2][q & 3];
+    for (int q = 0; q < 8; ++q) d[q] = ((ok >> q) & 1u) ? (double)r[q >> 2][q & 3] : 0.0;
   }
 };
 
@@ -58,11 +70,12 @@ __device__ inline void upper_tile(int id, int nt, int& a, int& b) {
   b = row + (id - start);
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict__ X, int64_t ldx,
                                                         int64_t n_tokens, int64_t dim, int nt,
                                                         int ntiles, int64_t tok_per_split,
                                                         double* __restrict__ S, int64_t lds,
-                                                        double* __restrict__ part, bool vec,
+                                                        double* __restrict__ part,
                                                         bool overwrite) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
@@ -77,53 +90,35 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
   if (t1 > n_tokens) t1 = n_tokens;
   const int nchunks = t1 > t0 ? (int)cdiv(t1 - t0, GK) : 0;
 
+  const int64_t fa = (int64_t)a * GT, fb = (int64_t)b * GT;
+  const int rows = (int)(dim - fa < GT ? dim - fa : GT);
+  const int cols = (int)(dim - fb < GT ? dim - fb : GT);
+  // Accumulating in place starts from the old values of the tile, so the
+  // epilogue is a plain store and the accumulators stay in the matrix
+  // registers through the loop. S is symmetric on entry (every call leaves
+  // it so); the mirror tile is rewritten from the upper one.
   d4 acc[4][4];
-  zero_acc(acc);
+  if (part || overwrite)
+    zero_acc(acc);
+  else
+    acc_load(acc, S + fa * lds + fb, lds, rows, cols);
   if (nchunks > 0) {
-    LdX32 la{X, ldx, t0, t1, dim, (int64_t)a * GT, vec, {}};
-    LdX32 lb{X, ldx, t0, t1, dim, (int64_t)b * GT, vec, {}};
-    gemm64_loop(la, lb, a == b, nchunks, sA, sB, acc);
+    LdX32<VEC> la{X, ldx, t0, t1, dim, fa, {}, 0u};
+    LdX32<VEC> lb{X, ldx, t0, t1, dim, fb, {}, 0u};
+    if (a == b)
+      gemm64_loop<true>(la, lb, nchunks, sA, sB, acc);
+    else
+      gemm64_loop<false>(la, lb, nchunks, sA, sB, acc);
   }
   if (part) {
     double* P = part + ((int64_t)split * ntiles + tile) * (GT * GT);
     for_each_acc(acc, [&](int r, int c, double v) { P[r * GT + c] = v; });
     return;
   }
-  const int64_t fa = (int64_t)a * GT, fb = (int64_t)b * GT;
-  const bool full = fa + GT <= dim && fb + GT <= dim;
-  if (!overwrite && full) {
-    // both triangles: old values of a tile are all loaded before any store
-    acc_update(acc, S + fa * lds + fb, lds, 1.0);
-    if (a != b) {
-      double old[4][4][4];
-      const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-      double* mb = S + (fb + wn * 64 + (lane & 15)) * lds + fa + wm * 64 + (lane >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) old[i][j][r] = mb[(int64_t)(j * 16) * lds + i * 16 + 4 * r];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            mb[(int64_t)(j * 16) * lds + i * 16 + 4 * r] = old[i][j][r] + acc[i][j][r];
-    }
-    return;
-  }
   for_each_acc(acc, [&](int r, int c, double v) {
-    const int64_t i = fa + r, j = fb + c;
-    if (i < dim && j < dim) {
-      if (overwrite) {
-        S[i * lds + j] = v;
-        if (a != b) S[j * lds + i] = v;
-      } else {
-        S[i * lds + j] += v;
-        if (a != b) S[j * lds + i] += v;
-      }
+    if (r < rows && c < cols) {
+      S[(fa + r) * lds + fb + c] = v;
+      if (a != b) S[(fb + c) * lds + fa + r] = v;
     }
   });
 }
@@ -209,13 +204,19 @@ extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, c
     nsplit = 1;
     tps = round_up(n_tokens, GK);
   }
-  const bool vec = (ldx % 4 == 0) && ((uintptr_t)X % 16 == 0);
+  const bool vec = (ldx % 4 == 0) && (in_features % 4 == 0) && ((uintptr_t)X % 16 == 0);
   double* part = nsplit > 1 ? (double*)ws : nullptr;
   const int nblocks = ntiles * nsplit;
-  GPTQ_LAUNCH(K_HESS_TILE, st,
-              hess_tile_kernel<<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt, ntiles, tps,
-                                                        S, in_features, part, vec,
-                                                        overwrite));
+  if (vec)
+    GPTQ_LAUNCH(K_HESS_TILE, st,
+                hess_tile_kernel<true><<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt,
+                                                                ntiles, tps, S, in_features, part,
+                                                                overwrite));
+  else
+    GPTQ_LAUNCH(K_HESS_TILE, st,
+                hess_tile_kernel<false><<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt,
+                                                                 ntiles, tps, S, in_features, part,
+                                                                 overwrite));
   if (part) {
     dim3 grid(GT * GT / 256, ntiles);
     GPTQ_LAUNCH(K_HESS_REDUCE, st,

@@ -13,6 +13,7 @@
 #include <utility>
 
 #include "gemm64.h"
+#include "trtri_order.h"
 
 namespace gptq {
 
@@ -484,7 +485,10 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, 
   LdTrans64 lb{K + rb * ld + c0, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop(la, lb, a == b, GT / GK, sA, sB, acc);
+  if (ra == rb)
+    gemm64_loop<true>(la, lb, GT / GK, sA, sB, acc);
+  else
+    gemm64_loop<false>(la, lb, GT / GK, sA, sB, acc);
   acc_update(acc, K + ra * ld + rb, ld, -1.0);
 }
 
@@ -498,33 +502,21 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, 
 // T = L21 X11 and one for X21 = -X22 T, with the triangular zeros of X11 and
 // X22 skipped in the K ranges.
 
-__device__ inline void level_tile(int id, int h, int nt, int& q, int& r, int& c, int64_t& f0,
-                                  int64_t& s0) {
-  const int nq = (nt + 2 * h - 1) / (2 * h);
-  q = id / (h * h);
-  if (q > nq - 1) q = nq - 1;
-  const int rem = id - q * h * h;
-  r = rem / h;
-  c = rem % h;
-  f0 = (int64_t)q * 2 * h;
-  s0 = f0 + h;
-}
-
 __global__ __launch_bounds__(256) void trtri_t_kernel(const double* __restrict__ K,
                                                       const double* __restrict__ Xb,
                                                       double* __restrict__ Tb, int64_t ld, int h,
                                                       int nt) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
-  int q, r, c;
+  int r, c;
   int64_t f0, s0;
-  level_tile(xcd_remap(blockIdx.x, gridDim.x), h, nt, q, r, c, f0, s0);
+  level_tile_t(blockIdx.x, h, nt, r, c, f0, s0);
   // T[r][c] = sum_{k=c}^{h-1} L[s0+r][f0+k] X[f0+k][f0+c]
   LdTrans64 la{K + (s0 + r) * GT * ld + (f0 + c) * GT, ld, {}};
   LdDirect64 lb{Xb + (f0 + c) * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop(la, lb, false, (h - c) * (GT / GK), sA, sB, acc);
+  gemm64_loop<false>(la, lb, (h - c) * (GT / GK), sA, sB, acc);
   double* out = Tb + (s0 + r) * GT * ld + (f0 + c) * GT;
   for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
 }
@@ -534,25 +526,18 @@ __global__ __launch_bounds__(256) void trtri_x_kernel(double* __restrict__ Xb,
                                                       int h, int nt) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
-  int q, r, c;
+  int r, c;
   int64_t f0, s0;
-  level_tile(xcd_remap(blockIdx.x, gridDim.x), h, nt, q, r, c, f0, s0);
+  level_tile_x(blockIdx.x, h, nt, r, c, f0, s0);
   // X[s0+r][f0+c] = -sum_{k=0}^{r} X[s0+r][s0+k] T[s0+k][f0+c]
-  LdTrans64 la{Xb + (s0 + r) * GT * ld + s0 * GT, ld, {}};
+  // the X22 operand is negated as it is staged, so the result is stored as is
+  LdTrans64T<true> la{Xb + (s0 + r) * GT * ld + s0 * GT, ld, {}};
   LdDirect64 lb{Tb + s0 * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop(la, lb, false, (r + 1) * (GT / GK), sA, sB, acc);
+  gemm64_loop<false>(la, lb, (r + 1) * (GT / GK), sA, sB, acc);
   double* out = Xb + (s0 + r) * GT * ld + (f0 + c) * GT;
-  for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = -v; });
-}
-
-static int level_tiles(int h, int nt) {
-  const int nq = (nt + 2 * h - 1) / (2 * h);
-  const int last2 = nt - (nq - 1) * 2 * h - h;  // second-half tiles of the last block
-  int tiles = (nq - 1) * h * h;
-  if (last2 > 0) tiles += last2 * h;
-  return tiles;
+  for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
 }
 
 // U[j][k] = X[n-1-j][n-1-k] (k >= j), 0 below the diagonal; fp32.

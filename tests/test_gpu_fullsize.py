@@ -119,14 +119,16 @@ def test_fullsize_sampled(wname):
         err = abs(Sg[k] - exact)
         assert err <= n * 2.0 ** -53 * mag, (f, g, Sg[k], exact)
         worst = max(worst, err / mag)
-    assert worst < 1e-13, worst
+    # a running fp64 sum over n terms: worst case n*u (asserted per entry
+    # above), typically sqrt(n)*u, about 4e-14 at 131072 tokens
+    assert worst < 1e-12, worst
 
     # ---- diag, damping, act-order
     say(f"{wname}: diagonal and act-order")
     d, nn = O.hessian_diag(host_chunks(X))
     assert nn == n
     dg = torch.diagonal(S).cpu().numpy()
-    assert np.max(np.abs(dg - d) / d) < 1e-13
+    assert np.max(np.abs(dg - d) / d) < 1e-12  # running sums, as for the entries above
     hdiag, lam = O.damped_diagonal(d, n, wl.damp)
     pr = O.act_order_from_diag(hdiag)
     assert np.array_equal(np.sort(perm), np.arange(dim))
