@@ -26,10 +26,10 @@ import numpy as np
 
 METRIC = ("quantized weights/sec per layer + XXᵀ/trailing-GEMM % MFMA peak, 1×MI355X")
 DEFAULT_WORKLOAD = "qwen05b_mlp"
+CHOL_MERGE_TILES = 512  # the library's threshold for the merged factor + update launch
 
 # MI355X published peaks
-PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0,
-        "f64_vector": 78.6}
+PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0}
 
 
 def parse():
@@ -60,16 +60,29 @@ def kernel_work(name, wl, plan):
     if name == "hessian_tile":
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
         return f, "flop", "f64_mfma"
-    if name in ("chol_syrk", "chol_trsm"):
+    if name in ("chol_syrk", "chol_trsm", "chol_potrf_syrk", "chol_potrf"):
+        # Per panel with m trailing tile rows: trsm m tiles; the next tile
+        # column m tiles (chol_syrk); the rest, r = m(m-1)/2 tiles, either
+        # beside the next diagonal block in one launch (chol_potrf_syrk, while
+        # r <= CHOL_MERGE_TILES; the block's (2/3) 128^3 counted there) or as
+        # its own chol_syrk launch after a chol_potrf one.
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
-            for p in range(nt):
+            if name == "chol_potrf":
+                f += 2 * 128 ** 3 / 3.0  # panel 0
+            for p in range(nt - 1):
                 m = nt - 1 - p
-                if name == "chol_syrk":
-                    f += 2 * 128 ** 3 * m * (m + 1) / 2
-                else:
+                r = m * (m - 1) // 2
+                merged = r <= CHOL_MERGE_TILES
+                if name == "chol_trsm":
                     f += 2 * 128 ** 3 * m
+                elif name == "chol_syrk":
+                    f += 2 * 128 ** 3 * (m + (0 if merged else r))
+                elif name == "chol_potrf_syrk":
+                    f += (2 * 128 ** 3 * r + 2 * 128 ** 3 / 3.0) if merged else 0.0
+                elif not merged:
+                    f += 2 * 128 ** 3 / 3.0
         return f, "flop", "f64_mfma"
     if name in ("trtri_t", "trtri_x"):
         # X21 = -X22 (L21 X11) at each doubling level, triangular zeros skipped
@@ -85,10 +98,6 @@ def kernel_work(name, wl, plan):
                             f += 2 * 128 ** 3 * ((hh - c) if name == "trtri_t" else (r + 1))
                 hh *= 2
         return f, "flop", "f64_mfma"
-    if name == "chol_potrf":
-        # 128x128 diagonal block: Cholesky (n^3/3) and triangular inverse (n^3/3)
-        f = sum(-(-h.dim // 128) for h in plan) * 2 * 128 ** 3 / 3.0
-        return f, "flop", "f64_vector"
     if name == "quant_gemm":
         f = 0.0
         for h in plan:
@@ -120,7 +129,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "post_weight_quantization_hessian_amd", "csrc")
 KERNEL_CLASS = {  # device function name -> timing class
     "hess_tile_kernel": "hessian_tile", "hess_reduce_kernel": "hessian_reduce",
-    "chol_potrf_kernel": "chol_potrf", "chol_trsm_kernel": "chol_trsm",
+    "chol_potrf_syrk_kernel": "chol_potrf_syrk", "chol_potrf_kernel": "chol_potrf",
+    "chol_trsm_kernel": "chol_trsm",
     "chol_syrk_kernel": "chol_syrk", "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x",
     "trtri_diag_kernel": "trtri_diag", "q_gemm_kernel": "quant_gemm",
     "q_sweep_kernel": "quant_sweep", "q_reduce_kernel": "quant_reduce",
@@ -360,7 +370,7 @@ def main():
         if unit == "flop":
             achieved = work / per_step_s / 1e12
             peak = PEAK[peak_key]
-            roofline = {"bound": "alu" if peak_key == "f64_vector" else "mfma",
+            roofline = {"bound": "mfma",
                         "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                         "frac": achieved / peak, "traffic": traffic,
                         "kernel": dominant, "precision": peak_key,

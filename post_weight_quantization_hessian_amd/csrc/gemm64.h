@@ -77,32 +77,33 @@ struct LdTrans64T {
 };
 using LdTrans64 = LdTrans64T<false>;
 
-// Double-buffered K loop; with SAME the B operand is the A operand (la only).
-// The body is straight-line: every iteration fetches the next chunk (the last
-// one re-fetches its own chunk, in bounds, into the buffer nobody reads any
-// more), so the accumulators stay in the matrix registers across iterations
-// instead of being copied out and back around a branchy loop.
-template <bool SAME, class LA, class LB>
+// Double-buffered K loop over nchunks >= 1 chunks. The body is straight-line:
+// every iteration fetches the next chunk (the last one re-fetches its own
+// chunk, in bounds, into the buffer nobody reads any more), and there is one
+// loop form for every tile (a diagonal tile loads its operand twice). A
+// branchy body, or two loop forms in one kernel, made the compiler copy the
+// 64 fp64 accumulators between vector and matrix registers around every
+// chunk, or keep a second copy of them live across the loop.
+template <class LA, class LB>
 __device__ inline void gemm64_loop(LA& la, LB& lb, int nchunks, double* sA, double* sB,
                                    d4 (&acc)[4][4]) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
   la.fetch(0, t);
-  if (!SAME) lb.fetch(0, t);
+  lb.fetch(0, t);
   la.store(sA, t);
-  if (!SAME) lb.store(sB, t);
+  lb.store(sB, t);
   __syncthreads();
-  for (int c = 0; c < nchunks; ++c) {
+  int c = 0;
+  do {
     const int cur = c & 1;
     const int nx = c + 1 < nchunks ? c + 1 : c;
     la.fetch(nx, t);
-    if (!SAME) lb.fetch(nx, t);
-    const double* a = sA + cur * GCH;
-    const double* b = SAME ? a : sB + cur * GCH;
-    mfma64_chunk(a, b, acc, wm, wn, lane);
+    lb.fetch(nx, t);
+    mfma64_chunk(sA + cur * GCH, sB + cur * GCH, acc, wm, wn, lane);
     la.store(sA + (cur ^ 1) * GCH, t);
-    if (!SAME) lb.store(sB + (cur ^ 1) * GCH, t);
+    lb.store(sB + (cur ^ 1) * GCH, t);
     __syncthreads();
-  }
+  } while (++c < nchunks);
 }
 
 __device__ inline void zero_acc(d4 (&acc)[4][4]) {
@@ -112,45 +113,37 @@ __device__ inline void zero_acc(d4 (&acc)[4][4]) {
     for (int j = 0; j < 4; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
 }
 
-// C[row][col] += sign * acc for the tile at C (leading dimension ld): all 64
-// old values of the thread are loaded before any store, so the loads overlap
-// (a load-add-store per element would serialize one memory round trip each).
-__device__ inline void acc_update(const d4 (&acc)[4][4], double* C, int64_t ld, double sign) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
-  double* base = C + (int64_t)(wm * 64 + (lane >> 4)) * ld + wn * 64 + (lane & 15);
-  double old[4][4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) old[i][j][r] = base[(int64_t)(i * 16 + 4 * r) * ld + j * 16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        base[(int64_t)(i * 16 + 4 * r) * ld + j * 16] = old[i][j][r] + sign * acc[i][j][r];
-}
-
-// acc = the tile at C (leading dimension ld), in the accumulator layout;
-// entries at tile-local (row, col) with row >= rows or col >= cols read 0.
-// Loads are clamped into range and all issued before use.
-__device__ inline void acc_load(d4 (&acc)[4][4], const double* C, int64_t ld, int rows, int cols) {
+// acc = the tile at C (leading dimension ld), staged through LDS 64 rows at a
+// time so the values reach the accumulators without a vector-register copy
+// that would stay live across the K loop; entries at tile-local (row, col)
+// with row >= rows or col >= cols read 0. `stage` holds >= 64 * GT doubles
+// and is free on entry; a barrier follows.
+__device__ inline void acc_load_lds(d4 (&acc)[4][4], const double* C, int64_t ld, int rows,
+                                    int cols, double* stage) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int e = 0; e < 32; ++e) {
+      const int idx = e * 256 + t;
+      const int rr = idx >> 7, cc = idx & 127;
+      const int row = 64 * half + rr;
+      const bool ok = row < rows && cc < cols;
+      const double v = C[ok ? (int64_t)row * ld + cc : 0];
+      stage[idx] = ok ? v : 0.0;
+    }
+    __syncthreads();
+    if (wm == half) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + i * 16 + (lane >> 4) + 4 * r;
-        const int col = wn * 64 + j * 16 + (lane & 15);
-        const bool ok = row < rows && col < cols;
-        const double v = C[ok ? (int64_t)row * ld + col : 0];
-        acc[i][j][r] = ok ? v : 0.0;
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = stage[(i * 16 + (lane >> 4) + 4 * r) * GT + wn * 64 + j * 16 + (lane & 15)];
+    }
+    __syncthreads();
+  }
 }
 
 // Visit the tile's accumulators: f(row, col, value) with tile-local row/col.

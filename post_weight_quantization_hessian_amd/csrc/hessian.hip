@@ -13,37 +13,40 @@
 namespace gptq {
 
 // Global X[token][feature] fp32 -> LDS [k][col] fp64, zero outside the token
-// range and the feature range. Branch-free: indices are clamped into range
-// and every load is issued; which values are in range is kept as a mask and
-// applied when the chunk is stored, so the load is waited on only then (one
-// chunk of MFMAs later). With `vec` (rows 16-byte aligned, dim % 4 == 0) each
-// float4 is wholly in or out of range.
+// range and the feature range. Branch-free: the row pointer advances by GK
+// rows per chunk and is clamped to the last row of the range, feature
+// offsets are clamped into the row, every load is issued, and which values
+// are in range is kept as a mask applied when the chunk is stored (so the
+// load is waited on only then, one chunk of MFMAs later). With VEC (rows
+// 16-byte aligned, dim % 4 == 0) each float4 is wholly in or out of range.
 template <bool VEC>
 struct LdX32 {
-  const float* X;
-  int64_t ldx, t_begin, t_end, dim, f0;
+  const float* row0;   // this thread's first token row
+  const float* rlast;  // the last token row of the range (clamp target)
+  int64_t step;        // GK rows
+  int64_t left;        // tokens from this thread's first row to the range end
+  int f;               // this thread's first feature
+  unsigned cols;       // bit q: feature f + q is in range
   f4 r[2];
-  unsigned ok;  // bit q: value q is in range
-  __device__ void fetch(int c, int t) {
-    const int64_t tok = t_begin + (int64_t)c * GK + (t >> 4);
-    const bool tok_ok = tok < t_end;
-    const float* row = X + (tok_ok ? tok : t_end - 1) * ldx;
-    const int64_t f = f0 + (t & 15) * 8;
-    ok = 0u;
+  unsigned ok;         // bit q: value q of the fetched chunk is in range
+  __device__ LdX32(const float* X, int64_t ldx, int64_t t_begin, int64_t t_end, int64_t dim,
+                   int64_t f0, int t)
+      : row0(X + (t_begin + (t >> 4)) * ldx), rlast(X + (t_end - 1) * ldx), step(GK * ldx),
+        left(t_end - t_begin - (t >> 4)), f((int)f0 + (t & 15) * 8), cols(0u), r{}, ok(0u) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cols |= (f + q < dim) ? 1u << q : 0u;
+  }
+  __device__ void fetch(int c, int) {
+    const bool tok_ok = (int64_t)c * GK < left;
+    const float* row = tok_ok ? row0 + c * step : rlast;
+    ok = tok_ok ? cols : 0u;
     if (VEC) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bool in = tok_ok && f + 4 * h < dim;
-        r[h] = *reinterpret_cast<const f4*>(row + (in ? f + 4 * h : 0));
-        ok |= in ? 0xFu << (4 * h) : 0u;
-      }
+      for (int h = 0; h < 2; ++h)
+        r[h] = *reinterpret_cast<const f4*>(row + (((cols >> (4 * h)) & 1u) ? f + 4 * h : 0));
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const bool in = tok_ok && f + q < dim;
-        r[q >> 2][q & 3] = row[in ? f + q : 0];
-        ok |= in ? 1u << q : 0u;
-      }
+      for (int q = 0; q < 8; ++q) r[q >> 2][q & 3] = row[((cols >> q) & 1u) ? f + q : 0];
     }
   }
   __device__ void store(double* s, int t) const {
@@ -70,15 +73,19 @@ __device__ inline void upper_tile(int id, int nt, int& a, int& b) {
   b = row + (id - start);
 }
 
-template <bool VEC>
+// ACC: add to the old values of S in place (the tile starts from them);
+// else the tile starts from zero and overwrites S or writes a partial tile.
+// Every workgroup has at least one token: split ranges all start below
+// n_tokens.
+template <bool VEC, bool ACC>
 __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict__ X, int64_t ldx,
                                                         int64_t n_tokens, int64_t dim, int nt,
                                                         int ntiles, int64_t tok_per_split,
                                                         double* __restrict__ S, int64_t lds,
-                                                        double* __restrict__ part,
-                                                        bool overwrite) {
-  __shared__ double sA[2 * GCH];
-  __shared__ double sB[2 * GCH];
+                                                        double* __restrict__ part) {
+  __shared__ double sAB[4 * GCH];
+  double* sA = sAB;
+  double* sB = sAB + 2 * GCH;
   const int nblocks = gridDim.x;
   const int lin = xcd_remap(blockIdx.x, nblocks);
   const int tile = lin % ntiles;
@@ -88,27 +95,23 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
   const int64_t t0 = (int64_t)split * tok_per_split;
   int64_t t1 = t0 + tok_per_split;
   if (t1 > n_tokens) t1 = n_tokens;
-  const int nchunks = t1 > t0 ? (int)cdiv(t1 - t0, GK) : 0;
+  const int nchunks = (int)cdiv(t1 - t0, GK);
 
   const int64_t fa = (int64_t)a * GT, fb = (int64_t)b * GT;
   const int rows = (int)(dim - fa < GT ? dim - fa : GT);
   const int cols = (int)(dim - fb < GT ? dim - fb : GT);
-  // Accumulating in place starts from the old values of the tile, so the
-  // epilogue is a plain store and the accumulators stay in the matrix
+  // The epilogue is a plain store, so the accumulators stay in the matrix
   // registers through the loop. S is symmetric on entry (every call leaves
   // it so); the mirror tile is rewritten from the upper one.
   d4 acc[4][4];
-  if (part || overwrite)
-    zero_acc(acc);
+  if (ACC)
+    acc_load_lds(acc, S + fa * lds + fb, lds, rows, cols, sAB);
   else
-    acc_load(acc, S + fa * lds + fb, lds, rows, cols);
-  if (nchunks > 0) {
-    LdX32<VEC> la{X, ldx, t0, t1, dim, fa, {}, 0u};
-    LdX32<VEC> lb{X, ldx, t0, t1, dim, fb, {}, 0u};
-    if (a == b)
-      gemm64_loop<true>(la, lb, nchunks, sA, sB, acc);
-    else
-      gemm64_loop<false>(la, lb, nchunks, sA, sB, acc);
+    zero_acc(acc);
+  {
+    LdX32<VEC> la(X, ldx, t0, t1, dim, fa, threadIdx.x);
+    LdX32<VEC> lb(X, ldx, t0, t1, dim, fb, threadIdx.x);
+    gemm64_loop(la, lb, nchunks, sA, sB, acc);
   }
   if (part) {
     double* P = part + ((int64_t)split * ntiles + tile) * (GT * GT);
@@ -207,16 +210,21 @@ extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, c
   const bool vec = (ldx % 4 == 0) && (in_features % 4 == 0) && ((uintptr_t)X % 16 == 0);
   double* part = nsplit > 1 ? (double*)ws : nullptr;
   const int nblocks = ntiles * nsplit;
-  if (vec)
-    GPTQ_LAUNCH(K_HESS_TILE, st,
-                hess_tile_kernel<true><<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt,
-                                                                ntiles, tps, S, in_features, part,
-                                                                overwrite));
-  else
-    GPTQ_LAUNCH(K_HESS_TILE, st,
-                hess_tile_kernel<false><<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, nt,
-                                                                 ntiles, tps, S, in_features, part,
-                                                                 overwrite));
+  // in place only when there is no partial-tile pass (that one adds in the reduce)
+  const bool acc_in_place = !overwrite && !part;
+#define HESS_TILE(V, A)                                                                       \
+  GPTQ_LAUNCH(K_HESS_TILE, st,                                                                 \
+              (hess_tile_kernel<V, A><<<nblocks, 256, 0, st>>>(X, ldx, n_tokens, in_features, \
+                                                               nt, ntiles, tps, S,            \
+                                                               in_features, part)))
+  if (vec) {
+    if (acc_in_place) HESS_TILE(true, true);
+    else HESS_TILE(true, false);
+  } else {
+    if (acc_in_place) HESS_TILE(false, true);
+    else HESS_TILE(false, false);
+  }
+#undef HESS_TILE
   if (part) {
     dim3 grid(GT * GT / 256, ntiles);
     GPTQ_LAUNCH(K_HESS_REDUCE, st,

@@ -8,10 +8,6 @@
 // which is upper triangular with U^T U = Hp^-1. One Cholesky and one
 // triangular inverse, both blocked by 128 in fp64 on MFMA; K is padded to a
 // multiple of 128 with an identity block so no kernel needs edge masks.
-#include <map>
-#include <mutex>
-#include <utility>
-
 #include "gemm64.h"
 #include "trtri_order.h"
 
@@ -110,6 +106,8 @@ constexpr int PTS = 16 * PT;  // doubles per tile
 constexpr int NPT = 36;       // lower tiles of an 8x8 tile grid
 
 __device__ inline int ptile(int I, int K) { return (I * (I + 1) / 2 + K) * PTS; }
+// tile row I of lower tile number u = I (I + 1) / 2 + K (compile-time in unrolled loops)
+__device__ constexpr int tile_row(int u) { return u < 1 ? 0 : u < 3 ? 1 : u < 6 ? 2 : u < 10 ? 3 : u < 15 ? 4 : u < 21 ? 5 : u < 28 ? 6 : 7; }
 
 // Order the LDS accesses of one wave (they execute in order in hardware).
 __device__ inline void wave_lds_sync() {
@@ -180,11 +178,11 @@ __device__ inline void factor16(double* T, double* invd, double* col, int lane, 
 }
 
 // One wave: X = L^-1 for the lower 16x16 tile L (rinv = 1/diag L), written to
-// the tile X (zeros above the diagonal). Row i of X is finished from the
-// accumulated right-hand side, handed over through the LDS buffer rowb, and
-// removed from the rows below.
-__device__ inline void inverse16(const double* L, const double* rinv, double* X, double* rowb,
-                                 int lane) {
+// global memory column-major with pitch 16 (zeros above the diagonal). Row i
+// of X is finished from the accumulated right-hand side, handed over through
+// the LDS buffer rowb, and removed from the rows below.
+__device__ inline void inverse16(const double* L, const double* rinv, double* __restrict__ X,
+                                 double* rowb, int lane) {
   const int g = lane >> 4, c = lane & 15;
   double x[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -208,17 +206,20 @@ __device__ inline void inverse16(const double* L, const double* rinv, double* X,
     wave_lds_sync();
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) X[c * PT + g + 4 * m] = x[m];
+  for (int m = 0; m < 4; ++m) X[c * 16 + g + 4 * m] = x[m];
 }
 
-__global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
-                                                         double* __restrict__ Dd, int64_t ld, int p,
-                                                         unsigned* __restrict__ status) {
-  __shared__ double A[NPT * PTS];
-  __shared__ double X[8 * PTS];  // inverses of the eight 16x16 diagonal tiles
-  __shared__ double invd[8][16];   // 1 / diag of each 16x16 diagonal tile
-  __shared__ double xbuf[4][16];   // per-wave column / row hand-over buffers
-  __shared__ int bad_any;
+// LDS of one diagonal-block factorization (doubles): the 36 tiles, the
+// reciprocal diagonals, the per-wave hand-over buffers and a flag.
+constexpr int POTRF_LDS = NPT * PTS + 8 * 16 + 4 * 16 + 1;
+
+__device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __restrict__ Dd, int64_t ld, int p,
+                            unsigned* __restrict__ status, double* smem) {
+  double* A = smem;
+  double(*invd)[16] = reinterpret_cast<double(*)[16]>(smem + NPT * PTS);  // 1/diag, 8 tiles
+  double(*xbuf)[16] = reinterpret_cast<double(*)[16]>(smem + NPT * PTS + 128);  // hand-over
+  int& bad_any = *reinterpret_cast<int*>(smem + NPT * PTS + 192);
+  double* D = Dd + (int64_t)p * 8 * 256;  // inverted 16x16 diagonal tiles, pitch 16
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t c0 = (int64_t)p * GT;
   if (t == 0) bad_any = 0;
@@ -228,14 +229,19 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
   const int er = t >> 4, ec = t & 15;
   const int lds_off = ec * PT + er;
   const double* gK = K + (c0 + er) * ld + c0 + ec;
-  {
-    double v[NPT];
+  // four batches of 9 tiles in flight: few enough registers that this block
+  // can share a kernel with the fp64 MFMA tile update at two waves per SIMD
 #pragma unroll
-    for (int I = 0; I < 8; ++I)
+  for (int u0 = 0; u0 < NPT; u0 += 9) {
+    double v[9];
 #pragma unroll
-      for (int Kt = 0; Kt <= I; ++Kt) v[I * (I + 1) / 2 + Kt] = gK[(int64_t)(16 * I) * ld + 16 * Kt];
+    for (int u = 0; u < 9; ++u) {
+      const int I = tile_row(u0 + u), Kt = u0 + u - I * (I + 1) / 2;
+      v[u] = gK[(int64_t)(16 * I) * ld + 16 * Kt];
+    }
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) A[u * PTS + lds_off] = v[u];
+    for (int u = 0; u < 9; ++u) A[(u0 + u) * PTS + lds_off] = v[u];
+    __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();
 
@@ -264,6 +270,7 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
   bool bad = false;
   if (wave == 0) factor16(A + ptile(0, 0), invd[0], xbuf[0], lane, bad);
   __syncthreads();
+#pragma unroll 1
   for (int s = 0; s < 8; ++s) {
     // rows below the diagonal tile: x L_ss^T = a  (forward substitution)
     if (t >= 16 * (s + 1) && t < GT) {
@@ -273,11 +280,23 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
       double x[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) x[c] = T[c * PT + ri];
+      // column c of L_ss is read one column ahead (a scheduling barrier per
+      // column keeps all 120 entries from being hoisted into registers)
+      double lc[16], ln[16];
+#pragma unroll
+      for (int m = 1; m < 16; ++m) lc[m] = Ls[m];
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
+        if (c + 1 < 16) {
+#pragma unroll
+          for (int m = c + 2; m < 16; ++m) ln[m] = Ls[(c + 1) * PT + m];
+        }
         x[c] *= invd[s][c];
 #pragma unroll
-        for (int m = c + 1; m < 16; ++m) x[m] -= x[c] * Ls[c * PT + m];
+        for (int m = c + 1; m < 16; ++m) x[m] -= x[c] * lc[m];
+#pragma unroll
+        for (int m = c + 2; m < 16; ++m) lc[m] = ln[m];
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int c = 0; c < 16; ++c) T[c * PT + ri] = x[c];
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
       wave_lds_sync();
       factor16(A + ptile(s + 1, s + 1), invd[s + 1], xbuf[0], lane, bad);
     } else if (wave == 3) {
-      inverse16(A + ptile(s, s), invd[s], X + s * PTS, xbuf[3], lane);
+      inverse16(A + ptile(s, s), invd[s], D + s * 256, xbuf[3], lane);
     } else {
       const int m = 7 - s;
       const int cnt = m * (m + 1) / 2;
@@ -303,20 +322,16 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
     __syncthreads();
   }
   if (bad) atomicOr(&bad_any, 1);
-  if (wave == 3) inverse16(A + ptile(7, 7), invd[7], X + 7 * PTS, xbuf[3], lane);
+  if (wave == 3) inverse16(A + ptile(7, 7), invd[7], D + 7 * 256, xbuf[3], lane);
   __syncthreads();
 
-  // L11 back into K (lower tiles); the diagonal inverses to Dd (16x16 tiles,
-  // column-major, pitch 16).
+  // L11 back into K (lower tiles); the diagonal inverses went to Dd directly.
   double* gL = K + (c0 + er) * ld + c0 + ec;
   for (int I = 0; I < 8; ++I) {
 #pragma unroll
     for (int Kt = 0; Kt < 8; ++Kt)
       if (Kt <= I) gL[(int64_t)(16 * I) * ld + 16 * Kt] = A[(I * (I + 1) / 2 + Kt) * PTS + lds_off];
   }
-  double* D = Dd + (int64_t)p * 8 * 256;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) D[i * 256 + ec * 16 + er] = X[i * PTS + lds_off];
   if (t == 0 && bad_any) atomicOr(status, ST_NOTSPD);
 }
 
@@ -460,11 +475,12 @@ __global__ __launch_bounds__(256) void trtri_diag_kernel(const double* __restric
 // Lower tiles of the trailing matrix: K22 -= L21 L21^T (tile (a, b), a >= b,
 // in trailing-tile coordinates). part 0: all tiles; 1: the first tile column
 // (b = 0, the next panel); 2: the rest (b >= 1).
-__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, int64_t ld, int p,
-                                                        int part) {
-  __shared__ double sA[2 * GCH];
-  __shared__ double sB[2 * GCH];
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
+// One 128x128 tile of the trailing update of panel p, C -= L_a L_b^T (fp64
+// MFMA, K = 128), tile `id` of: part 1, the next panel's tile column (b = 0,
+// a = id); part 2, the rest (tiles a >= b >= 1 of the trailing triangle,
+// row-major). `smem` holds >= 4 * GCH doubles.
+__device__ __forceinline__ void syrk_tile(double* __restrict__ K, int64_t ld, int p, int part, int id,
+                          double* smem) {
   int a, b;
   if (part == 1) {
     a = id;
@@ -474,22 +490,55 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, 
     while (a * (a + 1) / 2 > id) --a;
     while ((a + 1) * (a + 2) / 2 <= id) ++a;
     b = id - a * (a + 1) / 2;
-    if (part == 2) {
-      ++a;
-      ++b;
-    }
+    ++a;
+    ++b;
   }
   const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
   const int64_t ra = c1 + (int64_t)a * GT, rb = c1 + (int64_t)b * GT;
-  LdTrans64 la{K + ra * ld + c0, ld, {}};
+  // the tile starts from C and the first operand is negated as it is
+  // staged, so the epilogue is a plain store
+  LdTrans64T<true> la{K + ra * ld + c0, ld, {}};
   LdTrans64 lb{K + rb * ld + c0, ld, {}};
   d4 acc[4][4];
-  zero_acc(acc);
-  if (ra == rb)
-    gemm64_loop<true>(la, lb, GT / GK, sA, sB, acc);
+  acc_load_lds(acc, K + ra * ld + rb, ld, GT, GT, smem);
+  gemm64_loop(la, lb, GT / GK, smem, smem + 2 * GCH, acc);
+  double* out = K + ra * ld + rb;
+  for_each_acc(acc, [&](int r, int c, double v) { out[r * ld + c] = v; });
+}
+
+// Part `part` of the trailing update of panel p.
+__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, int64_t ld, int p,
+                                                        int part) {
+  __shared__ double smem[4 * GCH];
+  syrk_tile(K, ld, p, part, xcd_remap(blockIdx.x, gridDim.x), smem);
+}
+
+// The diagonal block of panel p alone.
+__global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
+                                                         double* __restrict__ Dd, int64_t ld, int p,
+                                                         unsigned* __restrict__ status) {
+  __shared__ double smem[POTRF_LDS];
+  potrf_block(K, Dd, ld, p, status, smem);
+}
+
+// Workgroup 0 factors the diagonal block of panel q (its tile column is
+// already updated); the others apply the rest of panel q-1's trailing update
+// (part 2), which touches no tile of panel q's column. One launch for two
+// independent pieces of work, so the factor of the next panel runs beside
+// the update instead of after it. The factor's registers limit this kernel
+// to one wave per SIMD, so it is used while the update fits in one round of
+// the GPU (CHOL_MERGE_TILES); larger updates run at two waves per SIMD in
+// their own launch, where the factor is a small fraction of the time.
+constexpr int CHOL_MERGE_TILES = 512;
+constexpr int STEP_LDS = POTRF_LDS > 4 * GCH ? POTRF_LDS : 4 * GCH;
+__global__ __launch_bounds__(256) void chol_potrf_syrk_kernel(double* __restrict__ K,
+                                                              double* __restrict__ Dd, int64_t ld,
+                                                              int q, unsigned* __restrict__ status) {
+  __shared__ double smem[STEP_LDS];
+  if (blockIdx.x == 0)
+    potrf_block(K, Dd, ld, q, status, smem);
   else
-    gemm64_loop<false>(la, lb, GT / GK, sA, sB, acc);
-  acc_update(acc, K + ra * ld + rb, ld, -1.0);
+    syrk_tile(K, ld, q - 1, 2, xcd_remap(blockIdx.x - 1, gridDim.x - 1), smem);
 }
 
 // ---------------------------------------------------------------- inverse
@@ -516,7 +565,7 @@ __global__ __launch_bounds__(256) void trtri_t_kernel(const double* __restrict__
   LdDirect64 lb{Xb + (f0 + c) * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop<false>(la, lb, (h - c) * (GT / GK), sA, sB, acc);
+  gemm64_loop(la, lb, (h - c) * (GT / GK), sA, sB, acc);
   double* out = Tb + (s0 + r) * GT * ld + (f0 + c) * GT;
   for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
 }
@@ -535,7 +584,7 @@ __global__ __launch_bounds__(256) void trtri_x_kernel(double* __restrict__ Xb,
   LdDirect64 lb{Tb + s0 * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop<false>(la, lb, (r + 1) * (GT / GK), sA, sB, acc);
+  gemm64_loop(la, lb, (r + 1) * (GT / GK), sA, sB, acc);
   double* out = Xb + (s0 + r) * GT * ld + (f0 + c) * GT;
   for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
 }
@@ -552,52 +601,6 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
 }
 
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
-
-// ---------------------------------------------------------------- side stream
-//
-// One non-blocking side stream (default priority) per device, created on
-// first use and kept for the life of the process, with a ring of events used
-// to order it against the caller's stream. The side stream is restricted to
-// 7/8 of the compute units so that the latency-bound kernels of the critical
-// chain, launched meanwhile on the caller's stream, always find free units.
-struct SideStream {
-  hipStream_t stream = nullptr;
-  std::mutex mu;
-  hipEvent_t events[130] = {};
-  hipEvent_t ev(int i) const { return events[i]; }
-};
-
-static std::mutex g_side_mu;
-static std::map<std::pair<int, hipStream_t>, SideStream*> g_side;
-
-// The side stream serving caller stream `caller` on the current device.
-static SideStream* side_stream(hipStream_t caller) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStream*& slot = g_side[std::make_pair(dev, caller)];
-  if (!slot) slot = new SideStream();
-  SideStream& s = *slot;
-  if (!s.stream) {
-    int ncu = 0;
-    (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    bool made = false;
-    if (ncu >= 16 && ncu <= 1024) {
-      uint32_t mask[32] = {};
-      for (int cu = 0; cu < ncu; ++cu)
-        if (cu % 8 != 7) mask[cu / 32] |= 1u << (cu % 32);
-      made = hipExtStreamCreateWithCUMask(&s.stream, (uint32_t)((ncu + 31) / 32), mask) ==
-             hipSuccess;
-    }
-    if (!made && hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) {
-      s.stream = nullptr;
-      return nullptr;
-    }
-    for (auto& e : s.events)
-      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
-  }
-  return &s;
-}
 
 // ---------------------------------------------------------------- layout
 
@@ -668,42 +671,24 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                   hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
   GPTQ_LAUNCH(K_PREP_GATHER, st,
               prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, perm, K));
-  // Blocked Cholesky with one step of look-ahead: the caller's stream runs
-  // the chain potrf(p) -> trsm(p) -> update of the next panel's tile column,
-  // while the side stream updates the rest of the trailing matrix (block rows
-  // and columns >= p+2, which potrf/trsm of panel p+1 never touch). The next
-  // panel's column update waits for the previous rest-update, which wrote the
-  // same tiles.
-  SideStream* side = side_stream(st);
-  if (!side) return GPTQ_EHIP;
-  hipStream_t ss = side->stream;
-  std::unique_lock<std::mutex> side_lock(side->mu);  // one enqueuer at a time
-  GPTQ_HIP(hipEventRecord(side->ev(0), st));
-  GPTQ_HIP(hipStreamWaitEvent(ss, side->ev(0), 0));
-  int rest_pending = -1;  // event index of the last rest-update
-  for (int p = 0; p < nt; ++p) {
-    GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, p, status));
+  // Blocked Cholesky, one stream. Per panel p: solve the panel's column
+  // (trsm), update the next panel's tile column, then one launch that
+  // factors the next diagonal block beside the rest of the trailing update.
+  GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
+  for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
-    if (mt == 0) break;
+    const int rest = (mt - 1) * mt / 2;
     GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, Dd, ip, p));
-    if (rest_pending >= 0) GPTQ_HIP(hipStreamWaitEvent(st, side->ev(rest_pending), 0));
     GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<mt, 256, 0, st>>>(K, ip, p, 1));
-    if (mt > 1) {
-      const int e_trsm = 1 + 2 * (p % 64), e_rest = e_trsm + 1;
-      GPTQ_HIP(hipEventRecord(side->ev(e_trsm), st));
-      GPTQ_HIP(hipStreamWaitEvent(ss, side->ev(e_trsm), 0));
-      GPTQ_LAUNCH(K_CHOL_SYRK, ss,
-                  chol_syrk_kernel<<<(mt - 1) * mt / 2, 256, 0, ss>>>(K, ip, p, 2));
-      GPTQ_HIP(hipEventRecord(side->ev(e_rest), ss));
-      rest_pending = e_rest;
+    if (rest <= CHOL_MERGE_TILES) {
+      GPTQ_LAUNCH(K_CHOL_STEP, st,
+                  chol_potrf_syrk_kernel<<<1 + rest, 256, 0, st>>>(K, Dd, ip, p + 1, status));
     } else {
-      rest_pending = -1;
+      GPTQ_LAUNCH(K_CHOL_POTRF, st,
+                  chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, p + 1, status));
+      GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<rest, 256, 0, st>>>(K, ip, p, 2));
     }
   }
-  // join: everything on the side stream precedes the rest of the call
-  GPTQ_HIP(hipEventRecord(side->ev(129), ss));
-  GPTQ_HIP(hipStreamWaitEvent(st, side->ev(129), 0));
-  side_lock.unlock();
   GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
   for (int h = 1; h < nt; h *= 2) {
     const int tiles = level_tiles(h, nt);
