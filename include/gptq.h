@@ -61,7 +61,9 @@ typedef enum {
  *     S[i x i] += X^T X,   X = n_tokens x in_features fp32, row stride ldx,
  * or S = X^T X with flags & GPTQ_FLAG_HESSIAN_OVERWRITE (S's old contents are
  * then never read; with n_tokens == 0 S is set to zero). S is fp64 and
- * symmetric: both triangles are written. The products of two fp32 values are
+ * symmetric: both triangles are written, and when accumulating S must be
+ * symmetric on entry (as every call leaves it; the lower triangle is
+ * rewritten from the upper one). The products of two fp32 values are
  * formed exactly (fp64), only the sums round. Call it once per token chunk
  * (the first with the overwrite flag, or on a zeroed S) and keep the running
  * token count; the normalisation (2/n) is applied by gptq_prepare_hinv.
@@ -90,10 +92,7 @@ gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
  *        factor with U^T U = (H[perm][:,perm])^-1, zeros below the diagonal.
  * Computed in fp64 (one Cholesky of the order-reversed permuted Hessian and
  * one triangular inverse), stored as fp32. S is read, never written.
- * Part of the factorisation runs on a library-owned side stream tied to
- * `stream` (default priority, created on first use for each caller stream and
- * kept, ordered against `stream` with events); calls on the same `stream`
- * from several host threads are serialized while they enqueue.
+ * All work is enqueued on `stream`.
  * Workspace: gptq_prepare_workspace_bytes(in_features) bytes.
  * Synchronizes `stream` once at the end to read the factorisation status;
  * returns GPTQ_ENOTSPD if a pivot is <= 0 or not finite (U is then garbage).
