@@ -60,9 +60,9 @@ def kernel_work(name, wl, plan):
     if name == "hessian_tile":
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
         return f, "flop", "f64_mfma"
-    if name in ("chol_syrk", "chol_trsm", "chol_potrf_syrk", "chol_potrf"):
+    if name in ("chol_syrk", "chol_trsm", "chol_potrf_syrk", "chol_potrf", "chol_col"):
         # Per panel with m trailing tile rows: trsm m tiles; the next tile
-        # column m tiles (chol_syrk); the rest, r = m(m-1)/2 tiles, either
+        # column m tiles (chol_col); the rest, r = m(m-1)/2 tiles, either
         # beside the next diagonal block in one launch (chol_potrf_syrk, while
         # r <= CHOL_MERGE_TILES; the block's (2/3) 128^3 counted there) or as
         # its own chol_syrk launch after a chol_potrf one.
@@ -75,10 +75,10 @@ def kernel_work(name, wl, plan):
                 m = nt - 1 - p
                 r = m * (m - 1) // 2
                 merged = r <= CHOL_MERGE_TILES
-                if name == "chol_trsm":
+                if name in ("chol_trsm", "chol_col"):
                     f += 2 * 128 ** 3 * m
                 elif name == "chol_syrk":
-                    f += 2 * 128 ** 3 * (m + (0 if merged else r))
+                    f += 2 * 128 ** 3 * (0 if merged else r)
                 elif name == "chol_potrf_syrk":
                     f += (2 * 128 ** 3 * r + 2 * 128 ** 3 / 3.0) if merged else 0.0
                 elif not merged:
@@ -130,10 +130,11 @@ CSRC = os.path.join(ROOT, "post_weight_quantization_hessian_amd", "csrc")
 KERNEL_CLASS = {  # device function name -> timing class
     "hess_tile_kernel": "hessian_tile", "hess_reduce_kernel": "hessian_reduce",
     "chol_potrf_syrk_kernel": "chol_potrf_syrk", "chol_potrf_kernel": "chol_potrf",
+    "chol_col_kernel": "chol_col",
     "chol_trsm_kernel": "chol_trsm",
-    "chol_syrk_kernel": "chol_syrk", "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x",
+    "chol_syrk_kernel": "chol_syrk", "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x", "trtri_sum_kernel": "trtri_sum",
     "trtri_diag_kernel": "trtri_diag", "q_gemm_kernel": "quant_gemm",
-    "q_sweep_kernel": "quant_sweep", "q_reduce_kernel": "quant_reduce",
+    "q_sweep_kernel": "quant_sweep",
     "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout"}
 
 
@@ -321,17 +322,20 @@ def main():
 
     # Each calibration input (with the layers that read it) is an independent
     # pipeline; the pipelines are enqueued asynchronously on their own streams
-    # and overlap on the device. Statuses are checked after the timed steps.
-    streams = [torch.cuda.Stream(device=dev) for _ in wl.inputs]
+    # and overlap on the device, the largest Hessian first (its chain of
+    # dependent launches is the longest, so it should not wait for the host
+    # to enqueue the others). Statuses are checked after the timed steps.
+    order = sorted(wl.inputs, key=lambda h: -h.dim)
+    streams = [torch.cuda.Stream(device=dev) for _ in order]
 
     def step():
-        for h, s in zip(wl.inputs, streams):
+        for h, s in zip(order, streams):
             chunks, Wd, grp = dev_inputs[h.name]
             with torch.cuda.stream(s):
                 grp.enqueue(chunks, Wd)
 
     def check_status():
-        for h, s in zip(wl.inputs, streams):
+        for h, s in zip(order, streams):
             with torch.cuda.stream(s):
                 dev_inputs[h.name][2].check()
 

@@ -506,6 +506,64 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ K, int64_t ld, in
   for_each_acc(acc, [&](int r, int c, double v) { out[r * ld + c] = v; });
 }
 
+// The next panel's tile column, C(a, p+1) -= L(a, p) L(p+1, p)^T for every
+// tile row a below panel p, at a finer grain than chol_syrk_kernel because
+// this update is on the critical path of the factorization: one workgroup
+// per 64x64 quadrant (4 per tile), each wave a 32x32 block as 2x2 fp64 MFMA
+// tiles. The operands are read from global memory (they are hot in L2)
+// straight into the MFMA layout, 8 K-steps (32 columns) at a time, double
+// buffered; the accumulators start from C and the row operand is negated.
+// A[m][k] = L[row m][c0 + k], B[k][n] = L[col n][c0 + k]: lane l reads row
+// (l & 15) of its 16-row group at K offset l >> 4.
+__global__ __launch_bounds__(256) void chol_col_kernel(double* __restrict__ K, int64_t ld, int p) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int tile = blockIdx.x >> 2, quad = blockIdx.x & 3;
+  const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
+  const int64_t row0 = c1 + (int64_t)tile * GT + (quad >> 1) * 64 + (w >> 1) * 32;
+  const int64_t col0 = c1 + (quad & 1) * 64 + (w & 1) * 32;
+  const double* ar = K + (row0 + (lane & 15)) * ld + c0 + (lane >> 4);
+  const double* br = K + (col0 + (lane & 15)) * ld + c0 + (lane >> 4);
+  d4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[i][j][r] = K[(row0 + i * 16 + (lane >> 4) + 4 * r) * ld + col0 + j * 16 + (lane & 15)];
+  double a[2][2][8], b[2][2][8];  // [buffer][16-row group][K-step]
+  auto load = [&](int buf, int kb) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        a[buf][g][s] = -ar[(int64_t)(g * 16) * ld + kb * 32 + 4 * s];
+        b[buf][g][s] = br[(int64_t)(g * 16) * ld + kb * 32 + 4 * s];
+      }
+  };
+  load(0, 0);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int cur = kb & 1;
+    if (kb + 1 < 4) load(cur ^ 1, kb + 1);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[cur][i][s], b[cur][j][s], acc[i][j], 0,
+                                                           0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        K[(row0 + i * 16 + (lane >> 4) + 4 * r) * ld + col0 + j * 16 + (lane & 15)] = acc[i][j][r];
+}
+
 // Part `part` of the trailing update of panel p.
 __global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, int64_t ld, int p,
                                                         int part) {
@@ -551,42 +609,117 @@ __global__ __launch_bounds__(256) void chol_potrf_syrk_kernel(double* __restrict
 // T = L21 X11 and one for X21 = -X22 T, with the triangular zeros of X11 and
 // X22 skipped in the K ranges.
 
+// The tile products of a doubling level may be cut along their inner sum
+// into pieces of `ks` tiles: workgroup id covers piece id % np of tile
+// id / np and, with Part, writes its partial 128x128 tile to
+// Part + id * GT * GT; trtri_sum_kernel then adds the pieces of every tile in
+// piece order. With np == 1 and ks >= h a workgroup computes its whole tile
+// and writes it in place. Splitting bounds the serial length of a level at
+// ks tiles when the level has too few tiles to fill the GPU.
 __global__ __launch_bounds__(256) void trtri_t_kernel(const double* __restrict__ K,
                                                       const double* __restrict__ Xb,
-                                                      double* __restrict__ Tb, int64_t ld, int h,
-                                                      int nt) {
+                                                      double* __restrict__ Tb,
+                                                      double* __restrict__ Part, int64_t ld, int h,
+                                                      int nt, int np, int ks) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
+  const int tile = blockIdx.x / np, piece = blockIdx.x % np;
   int r, c;
   int64_t f0, s0;
-  level_tile_t(blockIdx.x, h, nt, r, c, f0, s0);
+  level_tile_t(tile, h, nt, r, c, f0, s0);
   // T[r][c] = sum_{k=c}^{h-1} L[s0+r][f0+k] X[f0+k][f0+c]
-  LdTrans64 la{K + (s0 + r) * GT * ld + (f0 + c) * GT, ld, {}};
-  LdDirect64 lb{Xb + (f0 + c) * GT * ld + (f0 + c) * GT, ld, {}};
+  const int k0 = c + piece * ks;
+  const int k1 = k0 + ks < h ? k0 + ks : h;
+  if (k0 >= k1) return;
+  LdTrans64 la{K + (s0 + r) * GT * ld + (f0 + k0) * GT, ld, {}};
+  LdDirect64 lb{Xb + (f0 + k0) * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop(la, lb, (h - c) * (GT / GK), sA, sB, acc);
-  double* out = Tb + (s0 + r) * GT * ld + (f0 + c) * GT;
-  for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
+  gemm64_loop(la, lb, (k1 - k0) * (GT / GK), sA, sB, acc);
+  if (Part) {
+    double* out = Part + (int64_t)blockIdx.x * GT * GT;
+    for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * GT + cc] = v; });
+  } else {
+    double* out = Tb + (s0 + r) * GT * ld + (f0 + c) * GT;
+    for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
+  }
 }
 
 __global__ __launch_bounds__(256) void trtri_x_kernel(double* __restrict__ Xb,
-                                                      const double* __restrict__ Tb, int64_t ld,
-                                                      int h, int nt) {
+                                                      const double* __restrict__ Tb,
+                                                      double* __restrict__ Part, int64_t ld, int h,
+                                                      int nt, int np, int ks) {
   __shared__ double sA[2 * GCH];
   __shared__ double sB[2 * GCH];
+  const int tile = blockIdx.x / np, piece = blockIdx.x % np;
   int r, c;
   int64_t f0, s0;
-  level_tile_x(blockIdx.x, h, nt, r, c, f0, s0);
+  level_tile_x(tile, h, nt, r, c, f0, s0);
   // X[s0+r][f0+c] = -sum_{k=0}^{r} X[s0+r][s0+k] T[s0+k][f0+c]
+  const int k0 = piece * ks;
+  const int k1 = k0 + ks < r + 1 ? k0 + ks : r + 1;
+  if (k0 >= k1) return;
   // the X22 operand is negated as it is staged, so the result is stored as is
-  LdTrans64T<true> la{Xb + (s0 + r) * GT * ld + s0 * GT, ld, {}};
-  LdDirect64 lb{Tb + s0 * GT * ld + (f0 + c) * GT, ld, {}};
+  LdTrans64T<true> la{Xb + (s0 + r) * GT * ld + (s0 + k0) * GT, ld, {}};
+  LdDirect64 lb{Tb + (s0 + k0) * GT * ld + (f0 + c) * GT, ld, {}};
   d4 acc[4][4];
   zero_acc(acc);
-  gemm64_loop(la, lb, (r + 1) * (GT / GK), sA, sB, acc);
-  double* out = Xb + (s0 + r) * GT * ld + (f0 + c) * GT;
-  for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
+  gemm64_loop(la, lb, (k1 - k0) * (GT / GK), sA, sB, acc);
+  if (Part) {
+    double* out = Part + (int64_t)blockIdx.x * GT * GT;
+    for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * GT + cc] = v; });
+  } else {
+    double* out = Xb + (s0 + r) * GT * ld + (f0 + c) * GT;
+    for_each_acc(acc, [&](int rr, int cc, double v) { out[rr * ld + cc] = v; });
+  }
+}
+
+// Sum of the pieces of every tile of a split level, in piece order, into T
+// (xk false) or X (xk true).
+__global__ __launch_bounds__(256) void trtri_sum_kernel(const double* __restrict__ Part,
+                                                        double* __restrict__ Dst, int64_t ld, int h,
+                                                        int nt, int np, int ks, bool xk) {
+  const int tile = blockIdx.x;
+  int r, c;
+  int64_t f0, s0;
+  if (xk)
+    level_tile_x(tile, h, nt, r, c, f0, s0);
+  else
+    level_tile_t(tile, h, nt, r, c, f0, s0);
+  const int len = xk ? r + 1 : h - c;
+  const int cnt = (len + ks - 1) / ks;
+  const double* src = Part + (int64_t)tile * np * GT * GT;
+  double* dst = Dst + (s0 + r) * GT * ld + (f0 + c) * GT;
+  for (int e = threadIdx.x; e < GT * GT; e += 256) {
+    double v = 0.0;
+    for (int j = 0; j < cnt; ++j) v += src[(int64_t)j * GT * GT + e];
+    dst[(int64_t)(e >> 7) * ld + (e & 127)] = v;
+  }
+}
+
+// Pieces per tile at level h (1: the level is not split): split when the
+// level has too few tiles to fill the GPU twice over and its longest inner
+// sum is long (>= 16 tiles), within a bound on the partial-tile storage;
+// shorter levels do not repay the extra pass over the partial tiles.
+constexpr int TRTRI_KS = 4;
+constexpr int TRTRI_MAX_PIECES = 4096;
+static int trtri_pieces(int h, int nt, bool xk) {
+  const int tiles = level_tiles(h, nt);
+  const int last = level_last_rows(h, nt);
+  const int maxk = xk ? (level_blocks(h, nt) > 1 ? h : (last > 0 ? last : 0)) : h;
+  if (tiles >= 512 || maxk < 16) return 1;
+  const int np = (maxk + TRTRI_KS - 1) / TRTRI_KS;
+  return tiles * np <= TRTRI_MAX_PIECES ? np : 1;
+}
+
+static size_t trtri_part_bytes(int nt) {
+  size_t mx = 0;
+  for (int h = 1; h < nt; h *= 2)
+    for (int xk = 0; xk < 2; ++xk) {
+      const int np = trtri_pieces(h, nt, xk != 0);
+      if (np > 1) mx = std::max(mx, (size_t)level_tiles(h, nt) * np * GT * GT * sizeof(double));
+    }
+  return mx;
 }
 
 // U[j][k] = X[n-1-j][n-1-k] (k >= j), 0 below the diagonal; fp32.
@@ -606,7 +739,7 @@ __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
 struct PrepLayout {
   int64_t n, ip, nt;
-  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, off_D, total;
+  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, off_D, off_P, total;
 };
 
 static PrepLayout prep_layout(int64_t n) {
@@ -627,6 +760,7 @@ static PrepLayout prep_layout(int64_t n) {
   L.off_X = take(8 * (size_t)L.ip * L.ip);
   L.off_T = take(L.nt > 1 ? 8 * (size_t)L.ip * L.ip : 8);
   L.off_D = take(8 * (size_t)L.nt * 8 * 256);
+  L.off_P = take(std::max<size_t>(trtri_part_bytes((int)L.nt), 8));
   L.total = o;
   return L;
 }
@@ -660,6 +794,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   double* Xb = (double*)(base + L.off_X);
   double* Tb = (double*)(base + L.off_T);
   double* Dd = (double*)(base + L.off_D);
+  double* Pt = (double*)(base + L.off_P);
   const int64_t n = in_features, ip = L.ip;
   const int nt = (int)L.nt;
   const double c = 2.0 / (double)n_tokens_total;
@@ -679,7 +814,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     const int mt = nt - 1 - p;
     const int rest = (mt - 1) * mt / 2;
     GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, Dd, ip, p));
-    GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<mt, 256, 0, st>>>(K, ip, p, 1));
+    GPTQ_LAUNCH(K_CHOL_COL, st, chol_col_kernel<<<4 * mt, 256, 0, st>>>(K, ip, p));
     if (rest <= CHOL_MERGE_TILES) {
       GPTQ_LAUNCH(K_CHOL_STEP, st,
                   chol_potrf_syrk_kernel<<<1 + rest, 256, 0, st>>>(K, Dd, ip, p + 1, status));
@@ -692,8 +827,27 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
   for (int h = 1; h < nt; h *= 2) {
     const int tiles = level_tiles(h, nt);
-    GPTQ_LAUNCH(K_TRTRI_ROW, st, trtri_t_kernel<<<tiles, 256, 0, st>>>(K, Xb, Tb, ip, h, nt));
-    GPTQ_LAUNCH(K_TRTRI_UPDATE, st, trtri_x_kernel<<<tiles, 256, 0, st>>>(Xb, Tb, ip, h, nt));
+    const int npt = trtri_pieces(h, nt, false), npx = trtri_pieces(h, nt, true);
+    if (npt > 1) {
+      GPTQ_LAUNCH(K_TRTRI_ROW, st,
+                  trtri_t_kernel<<<tiles * npt, 256, 0, st>>>(K, Xb, Tb, Pt, ip, h, nt, npt,
+                                                              TRTRI_KS));
+      GPTQ_LAUNCH(K_TRTRI_SUM, st,
+                  trtri_sum_kernel<<<tiles, 256, 0, st>>>(Pt, Tb, ip, h, nt, npt, TRTRI_KS, false));
+    } else {
+      GPTQ_LAUNCH(K_TRTRI_ROW, st,
+                  trtri_t_kernel<<<tiles, 256, 0, st>>>(K, Xb, Tb, nullptr, ip, h, nt, 1, h));
+    }
+    if (npx > 1) {
+      GPTQ_LAUNCH(K_TRTRI_UPDATE, st,
+                  trtri_x_kernel<<<tiles * npx, 256, 0, st>>>(Xb, Tb, Pt, ip, h, nt, npx,
+                                                              TRTRI_KS));
+      GPTQ_LAUNCH(K_TRTRI_SUM, st,
+                  trtri_sum_kernel<<<tiles, 256, 0, st>>>(Pt, Xb, ip, h, nt, npx, TRTRI_KS, true));
+    } else {
+      GPTQ_LAUNCH(K_TRTRI_UPDATE, st,
+                  trtri_x_kernel<<<tiles, 256, 0, st>>>(Xb, Tb, nullptr, ip, h, nt, 1, h));
+    }
   }
   {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)std::min<int64_t>(n, 65535));

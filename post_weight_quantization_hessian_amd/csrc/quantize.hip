@@ -234,37 +234,6 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
     }
 }
 
-// wblk = W[:, blk] - sum_p part[p] for the split-K partials, summed in split
-// order (reproducible). Two adjacent columns per thread.
-__global__ __launch_bounds__(256) void q_reduce_kernel(const double* __restrict__ part, int P,
-                                                       int64_t part_stride,
-                                                       const uint16_t* __restrict__ W, int64_t ldw,
-                                                       int64_t rows, int64_t j0, int bw,
-                                                       double* __restrict__ wblk) {
-  const int64_t e2 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair index
-  const int64_t row = e2 / (QB / 2);
-  const int c = (int)(e2 % (QB / 2)) * 2;
-  if (row >= rows) return;
-  const int64_t off = row * QB + c;
-  dbl2_t sum = {0.0, 0.0};
-  for (int q = 0; q < P; q += 4) {
-    dbl2_t v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = q + u < P ? *reinterpret_cast<const dbl2_t*>(part + (int64_t)(q + u) * part_stride + off)
-                       : dbl2_t{0.0, 0.0};
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (q + u < P) {
-        sum.x += v[u].x;
-        sum.y += v[u].y;
-      }
-  }
-  const uint16_t* wr = W + row * ldw + j0;
-  if (c < bw) wblk[off] = f16_to_f64(wr[c]) - sum.x;
-  if (c + 1 < bw) wblk[off + 1] = f16_to_f64(wr[c + 1]) - sum.y;
-}
-
 // ---------------------------------------------------------------- sweep
 //
 // One block of columns [j0, j0+bw). A row is held by the 16 lanes of one DPP
@@ -281,6 +250,7 @@ __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 template <int GS>
 __global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
+    const double* __restrict__ part, int P, int64_t part_stride,
     const float* __restrict__ U, int64_t ldu, bool vecU, int64_t rows, int64_t j0, int bw,
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
@@ -302,11 +272,36 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   // threads), and the diagonal of the slab.
   // Current values of this row's columns: W - E[:, :j0] U[:j0, blk], formed by
   // the update GEMM (wblk); the first block reads the weights directly.
+  // With P > 1 the update GEMM left P split-K partials: they are summed here
+  // in split order (the order a separate reduction would use) and
+  // subtracted from the weights.
   double w[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int c = 16 * s + q;
     w[s] = (rv && c < bw) ? (wblk ? wblk[r * QB + c] : f16_to_f64(W[r * ldw + j0 + c])) : 0.0;
+  }
+  if (P > 1) {
+    double acc[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[s] = 0.0;
+    const double* pr = part + (rv ? r : 0) * QB + q;
+    for (int p0 = 0; p0 < P; p0 += 4) {
+      double v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int pu = p0 + u < P ? p0 + u : p0;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) v[u][s] = pr[(int64_t)pu * part_stride + 16 * s];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (p0 + u < P) acc[s] += v[u][s];
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) w[s] = (rv && 16 * s + q < bw) ? w[s] - acc[s] : 0.0;
   }
   const bool vec_slab = vecU && bw == QB;
   constexpr int SLAB4 = QB * QB / 4;       // float4s in the slab
@@ -516,13 +511,15 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
 
 template <int GS>
 static gptq_status launch_sweep(hipStream_t st, int nw, const uint16_t* Wsrc, int64_t ldws,
-                                const double* wblk, const float* U, int64_t cols, bool vecU,
+                                const double* wblk, const double* part, int P, int64_t pstride,
+                                const float* U, int64_t cols, bool vecU,
                                 int64_t rows, int64_t j0, int bw, int bits, float* E, int64_t lde,
                                 uint8_t* codes, int64_t ldc, uint16_t* scales, uint16_t* zeros,
                                 int64_t ldg, double* row_loss, unsigned* status) {
   const unsigned nblk = (unsigned)cdiv(rows, 4 * nw);
   GPTQ_LAUNCH(K_Q_SWEEP, st,
-              q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, wblk, U, cols, vecU, rows,
+              q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, wblk, part, P, pstride, U,
+                                                           cols, vecU, rows,
                                                            j0, bw, bits, E, lde, codes, ldc,
                                                            scales, zeros, ldg, row_loss, status));
   return GPTQ_OK;
@@ -592,6 +589,7 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
   for (int64_t j0 = 0; j0 < cols; j0 += QB) {
     const int bw = (int)std::min<int64_t>(QB, cols - j0);
     const double* cur = nullptr;
+    int nparts = 0;
     if (j0 > 0) {
       int64_t p = L.pmax;
       if (p > j0 / 128) p = j0 / 128;
@@ -601,20 +599,16 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
       GPTQ_LAUNCH(K_Q_GEMM, st,
                   q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0, bw,
                                                       ks, part, pstride, wblk, vecU));
-      if (P > 1) {
-        const int64_t pairs = rows * (QB / 2);
-        GPTQ_LAUNCH(K_Q_REDUCE, st,
-                    q_reduce_kernel<<<(unsigned)cdiv(pairs, 256), 256, 0, st>>>(
-                        part, P, pstride, Wsrc, ldws, rows, j0, bw, wblk));
-      }
-      cur = wblk;
+      // one split: the GEMM wrote W~ itself; else the sweep sums the partials
+      if (P == 1) cur = wblk;
+      else nparts = P;
     }
     gptq_status s;
     switch (group_size) {
-      case 16: s = launch_sweep<16>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      case 32: s = launch_sweep<32>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      case 64: s = launch_sweep<64>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      default: s = launch_sweep<128>(st, nw, Wsrc, ldws, cur, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 16: s = launch_sweep<16>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 32: s = launch_sweep<32>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 64: s = launch_sweep<64>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      default: s = launch_sweep<128>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
     }
     if (s != GPTQ_OK) return s;
   }
