@@ -133,80 +133,66 @@ __device__ inline double rsqrt_f64(double d) {
   return y;
 }
 
-// One wave: in-place Cholesky of the 16x16 tile T (lower part), 1/diag to
-// invd. The tile lives in registers in the MFMA accumulator layout (lane l:
-// column l & 15, rows (l >> 4) + 4m); column j is handed to the other lanes
-// through the 16-entry LDS buffer col.
-__device__ inline void factor16(double* T, double* invd, double* col, int lane, bool& bad) {
-  const int g = lane >> 4, c = lane & 15;
-  double a[4];
+// One wave: in-place Cholesky of the 16x16 tile T (lower part; column-major,
+// pitch PT), 1/diag to invd. Lane r (of each 16-lane row of the wave) holds
+// row r of the tile in registers; the pivot and the column entries the
+// rank-1 update needs are read from their owner lanes with readlane, so no
+// column passes through LDS. Entries above the diagonal are updated with
+// values that are never read.
+__device__ inline void factor16(double* T, double* invd, int lane, bool& bad) {
+  const int r = lane & 15;
+  double a[16];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) a[m] = T[c * PT + g + 4 * m];
+  for (int k = 0; k < 16; ++k) a[k] = T[k * PT + r];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
-    double d = readlane_f64(a[j >> 2], 16 * (j & 3) + j);
+    double d = readlane_f64(a[j], j);
     if (!(d > 0.0) || !isfinite(d)) {
       bad = true;
       d = 1.0;
     }
     const double inv = rsqrt_f64(d);
     const double ljj = d * inv;
-    if (c == j) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int row = g + 4 * m;
-        if (row > j) a[m] *= inv;
-        else if (row == j) a[m] = ljj;
-        col[row] = row > j ? a[m] : 0.0;
-      }
-    }
+    a[j] = r > j ? a[j] * inv : (r == j ? ljj : a[j]);
     if (lane == 0) invd[j] = inv;
-    wave_lds_sync();
-    // col[] is zero at and above row j, so the rank-1 update needs no
-    // predicate on the lower part; above the diagonal it only touches
-    // entries that are never read.
-    const double ck = col[c];
-    double cr[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) cr[m] = col[g + 4 * m];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] -= cr[m] * ck;
-    wave_lds_sync();
+    for (int k = j + 1; k < 16; ++k) a[k] -= a[j] * readlane_f64(a[j], k);
   }
+  if (lane < 16) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) T[c * PT + g + 4 * m] = a[m];
+    for (int k = 0; k < 16; ++k) T[k * PT + r] = a[k];
+  }
 }
 
-// One wave: X = L^-1 for the lower 16x16 tile L (rinv = 1/diag L), written to
-// global memory column-major with pitch 16 (zeros above the diagonal). Row i
-// of X is finished from the accumulated right-hand side, handed over through
-// the LDS buffer rowb, and removed from the rows below.
+// One wave: X = L^-1 for the lower 16x16 tile L (column-major, pitch PT;
+// rinv = 1/diag L), written to global memory column-major with pitch 16
+// (zeros above the diagonal). Lane c solves column c by forward
+// substitution; the entries of L it needs are read with readlane from a copy
+// of L held one row per lane.
 __device__ inline void inverse16(const double* L, const double* rinv, double* __restrict__ X,
-                                 double* rowb, int lane) {
-  const int g = lane >> 4, c = lane & 15;
-  double x[4] = {0.0, 0.0, 0.0, 0.0};
+                                 int lane) {
+  const int c = lane & 15;
+  double lr[16];  // row c of L
+#pragma unroll
+  for (int k = 0; k < 16; ++k) lr[k] = L[k * PT + c];
+  double x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    if (g == (i & 3)) {
-      double v = 0.0;
-      if (c <= i) v = ((c == i ? 1.0 : 0.0) + x[i >> 2]) * rinv[i];
-      x[i >> 2] = v;
-      rowb[c] = v;
-    }
-    wave_lds_sync();
-    const double xic = rowb[c];
-    double lv[4];
+    double s0 = (i == c) ? 1.0 : 0.0, s1 = 0.0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) lv[m] = L[i * PT + g + 4 * m];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const double nv = x[m] - lv[m] * xic;
-      x[m] = (g + 4 * m > i) ? nv : x[m];
+    for (int k = 0; k < i; ++k) {
+      const double lik = readlane_f64(lr[k], i);
+      if (k & 1)
+        s1 = fma(-lik, x[k], s1);
+      else
+        s0 = fma(-lik, x[k], s0);
     }
-    wave_lds_sync();
+    x[i] = (s0 + s1) * rinv[i];
   }
+  if (lane < 16) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) X[c * 16 + g + 4 * m] = x[m];
+    for (int i = 0; i < 16; ++i) X[c * 16 + i] = x[i];
+  }
 }
 
 // LDS of one diagonal-block factorization (doubles): the 36 tiles, the
@@ -217,7 +203,6 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
                             unsigned* __restrict__ status, double* smem) {
   double* A = smem;
   double(*invd)[16] = reinterpret_cast<double(*)[16]>(smem + NPT * PTS);  // 1/diag, 8 tiles
-  double(*xbuf)[16] = reinterpret_cast<double(*)[16]>(smem + NPT * PTS + 128);  // hand-over
   int& bad_any = *reinterpret_cast<int*>(smem + NPT * PTS + 192);
   double* D = Dd + (int64_t)p * 8 * 256;  // inverted 16x16 diagonal tiles, pitch 16
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -268,7 +253,7 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
   // diagonal tile, waves 1-2 update the other trailing tiles and wave 3
   // inverts the previous diagonal tile.
   bool bad = false;
-  if (wave == 0) factor16(A + ptile(0, 0), invd[0], xbuf[0], lane, bad);
+  if (wave == 0) factor16(A + ptile(0, 0), invd[0], lane, bad);
   __syncthreads();
 #pragma unroll 1
   for (int s = 0; s < 8; ++s) {
@@ -307,9 +292,9 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
     if (wave == 0) {
       syrk_tile(s + 1, s + 1, s);
       wave_lds_sync();
-      factor16(A + ptile(s + 1, s + 1), invd[s + 1], xbuf[0], lane, bad);
+      factor16(A + ptile(s + 1, s + 1), invd[s + 1], lane, bad);
     } else if (wave == 3) {
-      inverse16(A + ptile(s, s), invd[s], D + s * 256, xbuf[3], lane);
+      inverse16(A + ptile(s, s), invd[s], D + s * 256, lane);
     } else {
       const int m = 7 - s;
       const int cnt = m * (m + 1) / 2;
@@ -322,7 +307,7 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
     __syncthreads();
   }
   if (bad) atomicOr(&bad_any, 1);
-  if (wave == 3) inverse16(A + ptile(7, 7), invd[7], D + 7 * 256, xbuf[3], lane);
+  if (wave == 3) inverse16(A + ptile(7, 7), invd[7], D + 7 * 256, lane);
   __syncthreads();
 
   // L11 back into K (lower tiles); the diagonal inverses went to Dd directly.
@@ -675,11 +660,13 @@ __global__ __launch_bounds__(256) void trtri_x_kernel(double* __restrict__ Xb,
 }
 
 // Sum of the pieces of every tile of a split level, in piece order, into T
-// (xk false) or X (xk true).
+// (xk false) or X (xk true). Eight workgroups per tile (16 rows each); each
+// thread sums 4 pairs of adjacent elements, loading up to 8 pieces before
+// adding them.
 __global__ __launch_bounds__(256) void trtri_sum_kernel(const double* __restrict__ Part,
                                                         double* __restrict__ Dst, int64_t ld, int h,
                                                         int nt, int np, int ks, bool xk) {
-  const int tile = blockIdx.x;
+  const int tile = blockIdx.x >> 3, band = blockIdx.x & 7;
   int r, c;
   int64_t f0, s0;
   if (xk)
@@ -690,10 +677,25 @@ __global__ __launch_bounds__(256) void trtri_sum_kernel(const double* __restrict
   const int cnt = (len + ks - 1) / ks;
   const double* src = Part + (int64_t)tile * np * GT * GT;
   double* dst = Dst + (s0 + r) * GT * ld + (f0 + c) * GT;
-  for (int e = threadIdx.x; e < GT * GT; e += 256) {
-    double v = 0.0;
-    for (int j = 0; j < cnt; ++j) v += src[(int64_t)j * GT * GT + e];
-    dst[(int64_t)(e >> 7) * ld + (e & 127)] = v;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = band * 16 * GT + 2 * (u * 256 + threadIdx.x);  // even element of the tile
+    dbl2 sum = {0.0, 0.0};
+    for (int j0 = 0; j0 < cnt; j0 += 8) {
+      dbl2 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = j0 + q < cnt ? j0 + q : j0;
+        v[q] = *reinterpret_cast<const dbl2*>(src + (int64_t)j * GT * GT + e);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + q < cnt) {
+          sum.x += v[q].x;
+          sum.y += v[q].y;
+        }
+    }
+    *reinterpret_cast<dbl2*>(dst + (int64_t)(e >> 7) * ld + (e & 127)) = sum;
   }
 }
 
@@ -833,7 +835,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                   trtri_t_kernel<<<tiles * npt, 256, 0, st>>>(K, Xb, Tb, Pt, ip, h, nt, npt,
                                                               TRTRI_KS));
       GPTQ_LAUNCH(K_TRTRI_SUM, st,
-                  trtri_sum_kernel<<<tiles, 256, 0, st>>>(Pt, Tb, ip, h, nt, npt, TRTRI_KS, false));
+                  trtri_sum_kernel<<<8 * tiles, 256, 0, st>>>(Pt, Tb, ip, h, nt, npt, TRTRI_KS,
+                                                              false));
     } else {
       GPTQ_LAUNCH(K_TRTRI_ROW, st,
                   trtri_t_kernel<<<tiles, 256, 0, st>>>(K, Xb, Tb, nullptr, ip, h, nt, 1, h));
@@ -843,7 +846,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                   trtri_x_kernel<<<tiles * npx, 256, 0, st>>>(Xb, Tb, Pt, ip, h, nt, npx,
                                                               TRTRI_KS));
       GPTQ_LAUNCH(K_TRTRI_SUM, st,
-                  trtri_sum_kernel<<<tiles, 256, 0, st>>>(Pt, Xb, ip, h, nt, npx, TRTRI_KS, true));
+                  trtri_sum_kernel<<<8 * tiles, 256, 0, st>>>(Pt, Xb, ip, h, nt, npx, TRTRI_KS,
+                                                              true));
     } else {
       GPTQ_LAUNCH(K_TRTRI_UPDATE, st,
                   trtri_x_kernel<<<tiles, 256, 0, st>>>(Xb, Tb, nullptr, ip, h, nt, 1, h));
