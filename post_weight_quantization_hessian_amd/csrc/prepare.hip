@@ -320,12 +320,15 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
   if (t == 0 && bad_any) atomicOr(status, ST_NOTSPD);
 }
 
-// L21 = A21 L11^-T for one 128-row block below panel p (in place), by
+// L21 = A21 L11^-T for one 64-row block below panel p (in place), by
 // 16-column blocks: with Y_s = (L21[:, s])^T,
 //     Y_s = D_s (A21[:, s]^T - sum_{s'<s} L11[s][s'] Y_s'),   D_s = L11[s][s]^-1,
 // so only the lower 16x16 tiles of L11 and the diagonal inverses are needed.
-// Each wave owns 32 rows; the Y tiles stay in registers in the MFMA
-// accumulator layout, which is also the B-operand layout of the next products.
+// Each wave owns 16 rows; the Y tiles stay in registers in the MFMA
+// accumulator layout, which is also the B-operand layout of the next
+// products. The sum over s' is kept in four partial accumulators (one per
+// 4-wide K step of the 16x16x4 products) so the dependent chain of each step
+// is s MFMAs long instead of 4s.
 __global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
                                                         const double* __restrict__ Dd, int64_t ld,
                                                         int p) {
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
   __shared__ double Ds[8 * PTS];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t c0 = (int64_t)p * GT;
-  const int64_t r0 = c0 + GT + (int64_t)blockIdx.x * GT;
+  const int64_t r0 = c0 + GT + (int64_t)blockIdx.x * 64;
   {
     const int er = t >> 4, ec = t & 15;
     const double* gK = K + (c0 + er) * ld + c0 + ec;
@@ -348,48 +351,45 @@ __global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
 #pragma unroll
     for (int i = 0; i < 8; ++i) Ds[i * PTS + ec * PT + er] = D[i * 256 + ec * 16 + er];
   }
-  // this wave's 32 rows, transposed into Y tiles: y[s][rt][r] = A21[row][col] with
-  // row = 32*wave + 16*rt + (lane & 15), col = 16*s + (lane >> 4) + 4*r
-  d4 y[8][2];
-  double* gA = K + (r0 + 32 * wave + (lane & 15)) * ld + c0 + (lane >> 4);
+  // this wave's 16 rows, transposed into Y tiles: y[s][r] = A21[row][col] with
+  // row = 16*wave + (lane & 15), col = 16*s + (lane >> 4) + 4*r
+  d4 y[8];
+  double* gA = K + (r0 + 16 * wave + (lane & 15)) * ld + c0 + (lane >> 4);
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) y[s][rt][r] = gA[(int64_t)(16 * rt) * ld + 16 * s + 4 * r];
+    for (int r = 0; r < 4; ++r) y[s][r] = gA[16 * s + 4 * r];
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
+    d4 part[4];
+    part[0] = y[s];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      d4 acc = y[s][rt];
+    for (int kk = 1; kk < 4; ++kk) part[kk] = d4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int sp = 0; sp < s; ++sp) {
-        const double* Lt = Ls + ptile(s, sp);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int q = (lane >> 4) + 4 * kk;
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-Lt[q * PT + (lane & 15)], y[sp][rt][kk], acc,
-                                                     0, 0, 0);
-        }
-      }
-      const double* Dt = Ds + s * PTS;
-      d4 out = d4{0.0, 0.0, 0.0, 0.0};
+    for (int sp = 0; sp < s; ++sp) {
+      const double* Lt = Ls + ptile(s, sp);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int q = (lane >> 4) + 4 * kk;
-        out = __builtin_amdgcn_mfma_f64_16x16x4f64(Dt[q * PT + (lane & 15)], acc[kk], out, 0, 0, 0);
+        part[kk] = __builtin_amdgcn_mfma_f64_16x16x4f64(-Lt[q * PT + (lane & 15)], y[sp][kk],
+                                                        part[kk], 0, 0, 0);
       }
-      y[s][rt] = out;
     }
+    const d4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+    const double* Dt = Ds + s * PTS;
+    d4 out = d4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int q = (lane >> 4) + 4 * kk;
+      out = __builtin_amdgcn_mfma_f64_16x16x4f64(Dt[q * PT + (lane & 15)], acc[kk], out, 0, 0, 0);
+    }
+    y[s] = out;
   }
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gA[(int64_t)(16 * rt) * ld + 16 * s + 4 * r] = y[s][rt][r];
+    for (int r = 0; r < 4; ++r) gA[16 * s + 4 * r] = y[s][r];
 }
 
 // X_pp = L_pp^-1 for every 128x128 diagonal block (one workgroup per block,
@@ -815,7 +815,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
     const int rest = (mt - 1) * mt / 2;
-    GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<mt, 256, 0, st>>>(K, Dd, ip, p));
+    GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<2 * mt, 256, 0, st>>>(K, Dd, ip, p));
     GPTQ_LAUNCH(K_CHOL_COL, st, chol_col_kernel<<<4 * mt, 256, 0, st>>>(K, ip, p));
     if (rest <= CHOL_MERGE_TILES) {
       GPTQ_LAUNCH(K_CHOL_STEP, st,
