@@ -115,6 +115,41 @@ __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(
 
 // Workgroup id remapped so that consecutive logical ids land on the same XCD
 // (hardware dispatches workgroup ids round-robin over the 8 XCDs).
+// DPP moves of an fp64 value (two 32-bit halves). Every pattern used writes
+// every lane, so the "old" operand is the source itself.
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+  union { double d; int i[2]; } a, b;
+  a.d = v;
+  b.i[0] = __builtin_amdgcn_update_dpp(a.i[0], a.i[0], CTRL, 0xF, 0xF, false);
+  b.i[1] = __builtin_amdgcn_update_dpp(a.i[1], a.i[1], CTRL, 0xF, 0xF, false);
+  return b.d;
+}
+// row_newbcast: lane N of each 16-lane row, to the whole row
+template <int N>
+__device__ inline double row_bcast(double v) { return dpp_f64<0x150 + N>(v); }
+// the same for an index that is a constant after loop unrolling
+__device__ inline double row_bcast_i(double v, int n) {
+  switch (n) {
+    case 0: return row_bcast<0>(v);
+    case 1: return row_bcast<1>(v);
+    case 2: return row_bcast<2>(v);
+    case 3: return row_bcast<3>(v);
+    case 4: return row_bcast<4>(v);
+    case 5: return row_bcast<5>(v);
+    case 6: return row_bcast<6>(v);
+    case 7: return row_bcast<7>(v);
+    case 8: return row_bcast<8>(v);
+    case 9: return row_bcast<9>(v);
+    case 10: return row_bcast<10>(v);
+    case 11: return row_bcast<11>(v);
+    case 12: return row_bcast<12>(v);
+    case 13: return row_bcast<13>(v);
+    case 14: return row_bcast<14>(v);
+    default: return row_bcast<15>(v);
+  }
+}
+
 __device__ inline int xcd_remap(int bid, int nblocks) {
   const int nx = 8;
   if (nblocks < nx) return bid;

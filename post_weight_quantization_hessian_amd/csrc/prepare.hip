@@ -156,7 +156,7 @@ __device__ inline void factor16(double* T, double* invd, int lane, bool& bad) {
     a[j] = r > j ? a[j] * inv : (r == j ? ljj : a[j]);
     if (lane == 0) invd[j] = inv;
 #pragma unroll
-    for (int k = j + 1; k < 16; ++k) a[k] -= a[j] * readlane_f64(a[j], k);
+    for (int k = j + 1; k < 16; ++k) a[k] -= a[j] * row_bcast_i(a[j], k);
   }
   if (lane < 16) {
 #pragma unroll
@@ -167,8 +167,8 @@ __device__ inline void factor16(double* T, double* invd, int lane, bool& bad) {
 // One wave: X = L^-1 for the lower 16x16 tile L (column-major, pitch PT;
 // rinv = 1/diag L), written to global memory column-major with pitch 16
 // (zeros above the diagonal). Lane c solves column c by forward
-// substitution; the entries of L it needs are read with readlane from a copy
-// of L held one row per lane.
+// substitution; the entries of L it needs are DPP row broadcasts from a
+// copy of L held one row per lane.
 __device__ inline void inverse16(const double* L, const double* rinv, double* __restrict__ X,
                                  int lane) {
   const int c = lane & 15;
@@ -181,7 +181,7 @@ __device__ inline void inverse16(const double* L, const double* rinv, double* __
     double s0 = (i == c) ? 1.0 : 0.0, s1 = 0.0;
 #pragma unroll
     for (int k = 0; k < i; ++k) {
-      const double lik = readlane_f64(lr[k], i);
+      const double lik = row_bcast_i(lr[k], i);
       if (k & 1)
         s1 = fma(-lik, x[k], s1);
       else
@@ -248,10 +248,47 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
 #pragma unroll
     for (int r = 0; r < 4; ++r) C[(lane & 15) * PT + (lane >> 4) + 4 * r] = acc[r];
   };
+  // Two independent tile updates with their MFMA chains interleaved (the
+  // second is skipped when `two` is false).
+  auto syrk_tile2 = [&](int I1, int K1, int I2, int K2, int s, bool two) {
+    double* C1 = A + ptile(I1, K1);
+    double* C2 = A + ptile(I2, K2);
+    const double* L1i = A + ptile(I1, s);
+    const double* L1k = A + ptile(K1, s);
+    const double* L2i = A + ptile(I2, s);
+    const double* L2k = A + ptile(K2, s);
+    const int off = (lane & 15) * PT + (lane >> 4);
+    d4 a1, a2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      a1[r] = C1[off + 4 * r];
+      a2[r] = C2[off + 4 * r];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int q = (lane >> 4) + 4 * kk;
+      const double x1 = -L1i[q * PT + (lane & 15)], y1 = L1k[q * PT + (lane & 15)];
+      const double x2 = -L2i[q * PT + (lane & 15)], y2 = L2k[q * PT + (lane & 15)];
+      a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(x1, y1, a1, 0, 0, 0);
+      a2 = __builtin_amdgcn_mfma_f64_16x16x4f64(x2, y2, a2, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) C1[off + 4 * r] = a1[r];
+    if (two) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) C2[off + 4 * r] = a2[r];
+    }
+  };
+  auto tile_of = [](int u, int& a, int& b) {
+    a = 0;
+    while ((a + 1) * (a + 2) / 2 <= u) ++a;
+    b = u - a * (a + 1) / 2;
+  };
 
   // Pipelined 16-wide steps: while wave 0 updates and factors the next
-  // diagonal tile, waves 1-2 update the other trailing tiles and wave 3
-  // inverts the previous diagonal tile.
+  // diagonal tile, waves 1-3 update the other trailing tiles two at a time.
+  // The eight 16x16 diagonal inverses are formed at the end (their tiles are
+  // final once factored, and only the next launch reads them).
   bool bad = false;
   if (wave == 0) factor16(A + ptile(0, 0), invd[0], lane, bad);
   __syncthreads();
@@ -293,21 +330,24 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
       syrk_tile(s + 1, s + 1, s);
       wave_lds_sync();
       factor16(A + ptile(s + 1, s + 1), invd[s + 1], lane, bad);
-    } else if (wave == 3) {
-      inverse16(A + ptile(s, s), invd[s], D + s * 256, lane);
     } else {
       const int m = 7 - s;
-      const int cnt = m * (m + 1) / 2;
-      for (int u = wave; u < cnt; u += 2) {
-        int a = 0;
-        while ((a + 1) * (a + 2) / 2 <= u) ++a;
-        syrk_tile(s + 1 + a, s + 1 + (u - a * (a + 1) / 2), s);
+      const int cnt = m * (m + 1) / 2;  // u = 0 is (s+1, s+1), done by wave 0
+      for (int u = wave; u < cnt; u += 6) {
+        const bool two = u + 3 < cnt;
+        int a1, b1, a2, b2;
+        tile_of(u, a1, b1);
+        tile_of(two ? u + 3 : u, a2, b2);
+        syrk_tile2(s + 1 + a1, s + 1 + b1, s + 1 + a2, s + 1 + b2, s, two);
       }
     }
     __syncthreads();
   }
   if (bad) atomicOr(&bad_any, 1);
-  if (wave == 3) inverse16(A + ptile(7, 7), invd[7], D + 7 * 256, lane);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    inverse16(A + ptile(wave + 4 * i, wave + 4 * i), invd[wave + 4 * i], D + (wave + 4 * i) * 256,
+              lane);
   __syncthreads();
 
   // L11 back into K (lower tiles); the diagonal inverses went to Dd directly.

@@ -22,16 +22,6 @@ typedef double dbl2_t __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- helpers
 
-// Every pattern used here writes every lane, so the "old" operand is the
-// source itself (no extra register initialisation).
-template <int CTRL>
-__device__ inline double dpp_f64(double v) {
-  union { double d; int i[2]; } a, b;
-  a.d = v;
-  b.i[0] = __builtin_amdgcn_update_dpp(a.i[0], a.i[0], CTRL, 0xF, 0xF, false);
-  b.i[1] = __builtin_amdgcn_update_dpp(a.i[1], a.i[1], CTRL, 0xF, 0xF, false);
-  return b.d;
-}
 // quad_perm controls: broadcast lane q of the quad; xor 1; xor 2
 template <int Q>
 __device__ inline double quad_bcast(double v) { return dpp_f64<Q * 0x55>(v); }
@@ -242,8 +232,6 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
 // always slot 0 of lane j % 16, whose scaled error is broadcast to its row
 // with row_newbcast. Group min/max and the loss are reduced over the row with
 // quad permutes and row rotations.
-template <int N>
-__device__ inline double row_bcast(double v) { return dpp_f64<0x150 + N>(v); }
 __device__ inline double row_ror4(double v) { return dpp_f64<0x124>(v); }
 __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 
