@@ -27,6 +27,7 @@ import numpy as np
 METRIC = ("quantized weights/sec per layer + XXᵀ/trailing-GEMM % MFMA peak, 1×MI355X")
 DEFAULT_WORKLOAD = "qwen05b_mlp"
 CHOL_MERGE_TILES = 512  # the library's threshold for the merged factor + update launch
+CHOL_FUSE_NT = 48  # the library's bound on panels for the inverse accumulated in the factorization
 
 # MI355X published peaks
 PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0}
@@ -61,26 +62,46 @@ def kernel_work(name, wl, plan):
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
         return f, "flop", "f64_mfma"
     if name in ("chol_syrk", "chol_trsm", "chol_potrf_syrk", "chol_potrf", "chol_col"):
-        # Per panel with m trailing tile rows: trsm m tiles; the next tile
-        # column m tiles (chol_col); the rest, r = m(m-1)/2 tiles, either
-        # beside the next diagonal block in one launch (chol_potrf_syrk, while
-        # r <= CHOL_MERGE_TILES; the block's (2/3) 128^3 counted there) or as
-        # its own chol_syrk launch after a chol_potrf one.
+        # Mirrors the library's launch sequence. Per panel p with m trailing
+        # tile rows: trsm m tiles (a triangular solve with 128 right-hand
+        # sides, 128^3 per tile); the next tile column m tiles (chol_col); the
+        # rest, r = m(m-1)/2 tiles, either beside the next diagonal block in
+        # one launch (chol_potrf_syrk, while r <= CHOL_MERGE_TILES; the
+        # block's (2/3) 128^3 counted there) or as its own chol_syrk launch
+        # after a chol_potrf one. With the inverse accumulated in the
+        # factorization (nt <= CHOL_FUSE_NT), trsm also solves the p + 1
+        # tiles of X's row block p (and the last row block after the loop),
+        # and the m (p + 1) inverse tile updates of the step (2 128^3 each,
+        # half at j = p, where the operand X_pp is triangular) fill the merged
+        # launch up to CHOL_MERGE_TILES background tiles, the rest beside the
+        # column update.
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
+            fused = nt <= CHOL_FUSE_NT
             if name == "chol_potrf":
                 f += 2 * 128 ** 3 / 3.0  # panel 0
+            if name == "chol_trsm" and fused:
+                f += 128 ** 3 * nt  # last row block of X
             for p in range(nt - 1):
                 m = nt - 1 - p
                 r = m * (m - 1) // 2
                 merged = r <= CHOL_MERGE_TILES
-                if name in ("chol_trsm", "chol_col"):
-                    f += 2 * 128 ** 3 * m
+                xt = m * (p + 1) if fused else 0
+                xstep = min(xt, CHOL_MERGE_TILES - r) if merged else 0
+                xcol = xt - xstep
+
+                def xflops(ids):
+                    return sum(2 * 128 ** 3 if i % (p + 1) != p else 128 ** 3 for i in ids)
+                if name == "chol_trsm":
+                    f += 128 ** 3 * (m + ((p + 1) if fused else 0))
+                elif name == "chol_col":
+                    f += 2 * 128 ** 3 * m + xflops(range(xcol))
                 elif name == "chol_syrk":
                     f += 2 * 128 ** 3 * (0 if merged else r)
                 elif name == "chol_potrf_syrk":
-                    f += (2 * 128 ** 3 * r + 2 * 128 ** 3 / 3.0) if merged else 0.0
+                    if merged:
+                        f += 2 * 128 ** 3 * r + 2 * 128 ** 3 / 3.0 + xflops(range(xcol, xt))
                 elif not merged:
                     f += 2 * 128 ** 3 / 3.0
         return f, "flop", "f64_mfma"
@@ -89,7 +110,7 @@ def kernel_work(name, wl, plan):
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
-            hh = 1
+            hh = 1 if nt > CHOL_FUSE_NT else nt
             while hh < nt:
                 for q0 in range(0, nt, 2 * hh):
                     h2 = min(hh, nt - q0 - hh)

@@ -369,9 +369,16 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
 // products. The sum over s' is kept in four partial accumulators (one per
 // 4-wide K step of the 16x16x4 products) so the dependent chain of each step
 // is s MFMAs long instead of 4s.
+//
+// Workgroups from 2 * mt on (when the inverse X = L^-1 is accumulated beside
+// the factorization, as Z = X^T) solve 64 rows each of Z's column block p in
+// place: that block holds B^T with B_j = T_pj = -sum_{k<p} L_pk X_kj for
+// j < p and B_p = I, and X_pj = L_pp^-1 B_j, so each row of it is the same
+// length-128 forward substitution as a row of A21.
 __global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
-                                                        const double* __restrict__ Dd, int64_t ld,
-                                                        int p) {
+                                                        const double* __restrict__ Dd,
+                                                        double* __restrict__ Z, int64_t ld,
+                                                        int p, int mt) {
   __shared__ double Ls[NPT * PTS];
   __shared__ double Ds[8 * PTS];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -392,13 +399,22 @@ __global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
     for (int i = 0; i < 8; ++i) Ds[i * PTS + ec * PT + er] = D[i * 256 + ec * 16 + er];
   }
   // this wave's 16 rows, transposed into Y tiles: y[s][r] = A21[row][col] with
-  // row = 16*wave + (lane & 15), col = 16*s + (lane >> 4) + 4*r
+  // row = 16*wave + (lane & 15), col = 16*s + (lane >> 4) + 4*r; for the
+  // inverse, the same with the rows of Z's column block p in place of A21
+  const bool xpart = (int)blockIdx.x >= 2 * mt;
+  const int64_t row = xpart ? ((int64_t)blockIdx.x - 2 * mt) * 64 + 16 * wave + (lane & 15)
+                            : r0 + 16 * wave + (lane & 15);
+  double* gA = (xpart ? Z : K) + row * ld + c0 + (lane >> 4);
+  const int ident = xpart && row >= c0 ? (int)(row - c0) : -1;  // identity row of B^T
   d4 y[8];
-  double* gA = K + (r0 + 16 * wave + (lane & 15)) * ld + c0 + (lane >> 4);
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) y[s][r] = gA[16 * s + 4 * r];
+    for (int r = 0; r < 4; ++r) {
+      const int k = 16 * s + (lane >> 4) + 4 * r;
+      const double v = gA[16 * s + 4 * r];
+      y[s][r] = ident < 0 ? v : (k == ident ? 1.0 : 0.0);
+    }
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -497,15 +513,29 @@ __global__ __launch_bounds__(256) void trtri_diag_kernel(const double* __restric
   }
 }
 
-// Lower tiles of the trailing matrix: K22 -= L21 L21^T (tile (a, b), a >= b,
-// in trailing-tile coordinates). part 0: all tiles; 1: the first tile column
-// (b = 0, the next panel); 2: the rest (b >= 1).
-// One 128x128 tile of the trailing update of panel p, C -= L_a L_b^T (fp64
-// MFMA, K = 128), tile `id` of: part 1, the next panel's tile column (b = 0,
-// a = id); part 2, the rest (tiles a >= b >= 1 of the trailing triangle,
-// row-major). `smem` holds >= 4 * GCH doubles.
-__device__ __forceinline__ void syrk_tile(double* __restrict__ K, int64_t ld, int p, int part, int id,
-                          double* smem) {
+// C -= A B^T for one 128x128 tile (fp64 MFMA, K = 128): A and B are 128x128
+// blocks with K along their rows (leading dimension ld), C starts from its
+// first `crows` rows (the others from 0). The first operand is negated as it
+// is staged, so the epilogue is a plain store. Every tile update of the
+// factorization and of the fused inverse goes through this one call site
+// per kernel (a second loop form in a kernel costs registers and copies).
+// `smem` holds >= 4 * GCH doubles.
+__device__ __forceinline__ void tile_nt_update(const double* A, const double* B, double* C,
+                                               int64_t ld, int crows, double* smem) {
+  LdTrans64T<true> la{A, ld, {}};
+  LdTrans64 lb{B, ld, {}};
+  d4 acc[4][4];
+  acc_load_lds(acc, C, ld, crows, GT, smem);
+  gemm64_loop(la, lb, GT / GK, smem, smem + 2 * GCH, acc);
+  for_each_acc(acc, [&](int r, int c, double v) { C[r * ld + c] = v; });
+}
+
+// Tile `id` of the trailing update of panel p, C -= L_a L_b^T: part 1, the
+// next panel's tile column (b = 0, a = id); part 2, the rest (tiles
+// a >= b >= 1 of the trailing triangle, row-major), in trailing-tile
+// coordinates. Sets the operands of tile_nt_update.
+__device__ inline void syrk_tile_args(double* K, int64_t ld, int p, int part, int id,
+                                      const double*& A, const double*& B, double*& C) {
   int a, b;
   if (part == 1) {
     a = id;
@@ -520,15 +550,44 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ K, int64_t ld, in
   }
   const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
   const int64_t ra = c1 + (int64_t)a * GT, rb = c1 + (int64_t)b * GT;
-  // the tile starts from C and the first operand is negated as it is
-  // staged, so the epilogue is a plain store
-  LdTrans64T<true> la{K + ra * ld + c0, ld, {}};
-  LdTrans64 lb{K + rb * ld + c0, ld, {}};
-  d4 acc[4][4];
-  acc_load_lds(acc, K + ra * ld + rb, ld, GT, GT, smem);
-  gemm64_loop(la, lb, GT / GK, smem, smem + 2 * GCH, acc);
-  double* out = K + ra * ld + rb;
-  for_each_acc(acc, [&](int r, int c, double v) { out[r * ld + c] = v; });
+  A = K + ra * ld + c0;
+  B = K + rb * ld + c0;
+  C = K + ra * ld + rb;
+}
+
+// One tile of panel p's step of the inverse accumulated beside the
+// factorization, which keeps Z = X^T (upper triangular) for X = L^-1. X is
+// built by block rows: once row block p of X is final,
+//     T_rj -= L_rp X_pj   for every tile row r > p and column j <= p,
+// which leaves T_rj = -sum_{k=j}^{r-1} L_rk X_kj by the time row r is solved
+// (X_rj = L_rr^-1 T_rj). Transposed, the update is Z_jr -= Z_jp L_rp^T, the
+// same product form as the factorization's trailing update. Tile `id` is
+// (r, j) = (p + 1 + id / (p + 1), id % (p + 1)), so the tiles of tile row
+// p + 1, which the next panel solve reads, come first; at j = p the tile is
+// first written and starts from 0. Sets the operands of tile_nt_update.
+__device__ inline void xinv_tile_args(double* K, double* Z, int64_t ld, int p, int id,
+                                      const double*& A, const double*& B, double*& C,
+                                      int& crows) {
+  const int r = p + 1 + id / (p + 1), j = id % (p + 1);
+  const int64_t rr = (int64_t)r * GT, cp = (int64_t)p * GT, cj = (int64_t)j * GT;
+  A = Z + cj * ld + cp;  // Z_jp
+  B = K + rr * ld + cp;  // L_rp
+  C = Z + cj * ld + rr;  // Z_jr
+  crows = j == p ? 0 : GT;
+}
+
+// Background tile `id` of panel p: the first nsyrk ids are tiles of part
+// `part` of the trailing update, the others inverse tiles x0, x0 + 1, ...
+__device__ __forceinline__ void bg_tile(double* K, double* Z, int64_t ld, int p, int part,
+                                        int nsyrk, int x0, int id, double* smem) {
+  const double *A, *B;
+  double* C;
+  int crows = GT;
+  if (id < nsyrk)
+    syrk_tile_args(K, ld, p, part, id, A, B, C);
+  else
+    xinv_tile_args(K, Z, ld, p, x0 + id - nsyrk, A, B, C, crows);
+  tile_nt_update(A, B, C, ld, crows, smem);
 }
 
 // The next panel's tile column, C(a, p+1) -= L(a, p) L(p+1, p)^T for every
@@ -540,7 +599,18 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ K, int64_t ld, in
 // buffered; the accumulators start from C and the row operand is negated.
 // A[m][k] = L[row m][c0 + k], B[k][n] = L[col n][c0 + k]: lane l reads row
 // (l & 15) of its 16-row group at K offset l >> 4.
-__global__ __launch_bounds__(256) void chol_col_kernel(double* __restrict__ K, int64_t ld, int p) {
+//
+// Workgroups from 4 * mt on (when the inverse is accumulated beside the
+// factorization) apply the first inverse tiles of panel p's step, one each.
+__global__ __launch_bounds__(256, 2) void chol_col_kernel(double* __restrict__ K,
+                                                          double* __restrict__ Z, int64_t ld,
+                                                          int p, int mt) {
+  if ((int)blockIdx.x >= 4 * mt) {
+    __shared__ double smem[4 * GCH];
+    const int nx = (int)gridDim.x - 4 * mt;
+    bg_tile(K, Z, ld, p, 2, 0, 0, xcd_remap((int)blockIdx.x - 4 * mt, nx), smem);
+    return;
+  }
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int tile = blockIdx.x >> 2, quad = blockIdx.x & 3;
   const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
@@ -589,11 +659,13 @@ __global__ __launch_bounds__(256) void chol_col_kernel(double* __restrict__ K, i
         K[(row0 + i * 16 + (lane >> 4) + 4 * r) * ld + col0 + j * 16 + (lane & 15)] = acc[i][j][r];
 }
 
-// Part `part` of the trailing update of panel p.
-__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K, int64_t ld, int p,
-                                                        int part) {
+// Part `part` of the trailing update of panel p (nsyrk tiles), then the
+// inverse tiles x0, x0 + 1, ... of panel p's step (the rest of the grid).
+__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K,
+                                                        double* __restrict__ Z, int64_t ld, int p,
+                                                        int part, int nsyrk, int x0) {
   __shared__ double smem[4 * GCH];
-  syrk_tile(K, ld, p, part, xcd_remap(blockIdx.x, gridDim.x), smem);
+  bg_tile(K, Z, ld, p, part, nsyrk, x0, xcd_remap(blockIdx.x, gridDim.x), smem);
 }
 
 // The diagonal block of panel p alone.
@@ -606,7 +678,8 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
 
 // Workgroup 0 factors the diagonal block of panel q (its tile column is
 // already updated); the others apply the rest of panel q-1's trailing update
-// (part 2), which touches no tile of panel q's column. One launch for two
+// (part 2, nsyrk tiles), which touches no tile of panel q's column, and then
+// inverse tiles x0, x0 + 1, ... of panel q-1's step. One launch for two
 // independent pieces of work, so the factor of the next panel runs beside
 // the update instead of after it. The factor's registers limit this kernel
 // to one wave per SIMD, so it is used while the update fits in one round of
@@ -614,14 +687,16 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
 // their own launch, where the factor is a small fraction of the time.
 constexpr int CHOL_MERGE_TILES = 512;
 constexpr int STEP_LDS = POTRF_LDS > 4 * GCH ? POTRF_LDS : 4 * GCH;
-__global__ __launch_bounds__(256) void chol_potrf_syrk_kernel(double* __restrict__ K,
-                                                              double* __restrict__ Dd, int64_t ld,
-                                                              int q, unsigned* __restrict__ status) {
+__global__ __launch_bounds__(256, 2) void chol_potrf_syrk_kernel(double* __restrict__ K,
+                                                              double* __restrict__ Dd,
+                                                              double* __restrict__ Z, int64_t ld,
+                                                              int q, unsigned* __restrict__ status,
+                                                              int nsyrk, int x0) {
   __shared__ double smem[STEP_LDS];
   if (blockIdx.x == 0)
     potrf_block(K, Dd, ld, q, status, smem);
   else
-    syrk_tile(K, ld, q - 1, 2, xcd_remap(blockIdx.x - 1, gridDim.x - 1), smem);
+    bg_tile(K, Z, ld, q - 1, 2, nsyrk, x0, xcd_remap(blockIdx.x - 1, gridDim.x - 1), smem);
 }
 
 // ---------------------------------------------------------------- inverse
@@ -775,9 +850,41 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
   }
 }
 
+// U[j][k] = Z[n-1-k][n-1-j] (k >= j), 0 below the diagonal; fp32. One 64x64
+// tile of U per workgroup, staged through LDS so that the reads of Z and the
+// writes of U both run along rows.
+__global__ __launch_bounds__(256) void prep_uout_z_kernel(const double* __restrict__ Z,
+                                                          int64_t ld, int64_t n,
+                                                          float* __restrict__ U) {
+  __shared__ double tile[64][65];
+  const int64_t j0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const bool below = k0 + 63 < j0;  // the whole tile is below the diagonal
+  if (!below) {
+    for (int a = ty; a < 64; a += 4) {
+      const int64_t k = k0 + a, j = j0 + tx;
+      tile[a][tx] = (k < n && j < n) ? Z[(n - 1 - k) * ld + (n - 1 - j)] : 0.0;
+    }
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t j = j0 + i, k = k0 + tx;
+    if (j < n && k < n) U[j * n + k] = (!below && k >= j) ? (float)tile[tx][i] : 0.0f;
+  }
+}
+
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
 // ---------------------------------------------------------------- layout
+
+// Up to this many 128-column panels the inverse of L is accumulated by block
+// rows inside the factorization's own launches (its tile updates run beside
+// the next panel's column update, its row solves beside the panel solve),
+// which removes the separate triangular inverse from the dependent chain
+// while the factorization is latency-bound. Larger matrices use recursive
+// doubling, whose long inner sums run the MFMA units more efficiently and
+// read each tile once per level instead of once per panel.
+constexpr int CHOL_FUSE_NT = 48;
 
 struct PrepLayout {
   int64_t n, ip, nt;
@@ -800,9 +907,10 @@ static PrepLayout prep_layout(int64_t n) {
   L.off_hd = take(8 * (size_t)n);
   L.off_K = take(8 * (size_t)L.ip * L.ip);
   L.off_X = take(8 * (size_t)L.ip * L.ip);
-  L.off_T = take(L.nt > 1 ? 8 * (size_t)L.ip * L.ip : 8);
+  const bool fused = L.nt <= CHOL_FUSE_NT;
+  L.off_T = take(L.nt > 1 && !fused ? 8 * (size_t)L.ip * L.ip : 8);
   L.off_D = take(8 * (size_t)L.nt * 8 * 256);
-  L.off_P = take(std::max<size_t>(trtri_part_bytes((int)L.nt), 8));
+  L.off_P = take(fused ? 8 : std::max<size_t>(trtri_part_bytes((int)L.nt), 8));
   L.total = o;
   return L;
 }
@@ -851,23 +959,46 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   // Blocked Cholesky, one stream. Per panel p: solve the panel's column
   // (trsm), update the next panel's tile column, then one launch that
   // factors the next diagonal block beside the rest of the trailing update.
+  // With the fused inverse, the panel solve also solves row block p of
+  // X = L^-1, and the column update also applies panel p's step of X.
+  // Panel p's inverse tiles fill the launch with the next diagonal block up
+  // to CHOL_MERGE_TILES background tiles; the first ones (those that do not
+  // fit there, or all when that launch is split) run beside the column
+  // update. Both launches precede the next panel solve, which reads the
+  // first tile row of them.
+  const bool fused = nt <= CHOL_FUSE_NT;
   GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
   for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
     const int rest = (mt - 1) * mt / 2;
-    GPTQ_LAUNCH(K_CHOL_TRSM, st, chol_trsm_kernel<<<2 * mt, 256, 0, st>>>(K, Dd, ip, p));
-    GPTQ_LAUNCH(K_CHOL_COL, st, chol_col_kernel<<<4 * mt, 256, 0, st>>>(K, ip, p));
-    if (rest <= CHOL_MERGE_TILES) {
+    const int xs = fused ? 2 * (p + 1) : 0;   // inverse row-solve workgroups
+    const int xt = fused ? mt * (p + 1) : 0;  // inverse tile updates
+    const bool merged = rest <= CHOL_MERGE_TILES;
+    const int xstep = merged ? std::min(xt, CHOL_MERGE_TILES - rest) : 0;
+    const int xcol = xt - xstep;
+    GPTQ_LAUNCH(K_CHOL_TRSM, st,
+                chol_trsm_kernel<<<2 * mt + xs, 256, 0, st>>>(K, Dd, Xb, ip, p, mt));
+    GPTQ_LAUNCH(K_CHOL_COL, st,
+                chol_col_kernel<<<4 * mt + xcol, 256, 0, st>>>(K, Xb, ip, p, mt));
+    if (merged) {
       GPTQ_LAUNCH(K_CHOL_STEP, st,
-                  chol_potrf_syrk_kernel<<<1 + rest, 256, 0, st>>>(K, Dd, ip, p + 1, status));
+                  chol_potrf_syrk_kernel<<<1 + rest + xstep, 256, 0, st>>>(K, Dd, Xb, ip, p + 1,
+                                                                          status, rest, xcol));
     } else {
       GPTQ_LAUNCH(K_CHOL_POTRF, st,
                   chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, p + 1, status));
-      GPTQ_LAUNCH(K_CHOL_SYRK, st, chol_syrk_kernel<<<rest, 256, 0, st>>>(K, ip, p, 2));
+      GPTQ_LAUNCH(K_CHOL_SYRK, st,
+                  chol_syrk_kernel<<<rest, 256, 0, st>>>(K, Xb, ip, p, 2, rest, 0));
     }
   }
-  GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
-  for (int h = 1; h < nt; h *= 2) {
+  if (fused) {
+    // the last block row of X
+    GPTQ_LAUNCH(K_CHOL_TRSM, st,
+                chol_trsm_kernel<<<2 * nt, 256, 0, st>>>(K, Dd, Xb, ip, nt - 1, 0));
+  } else {
+    GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
+  }
+  for (int h = 1; h < nt && !fused; h *= 2) {
     const int tiles = level_tiles(h, nt);
     const int npt = trtri_pieces(h, nt, false), npx = trtri_pieces(h, nt, true);
     if (npt > 1) {
@@ -893,7 +1024,10 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                   trtri_x_kernel<<<tiles, 256, 0, st>>>(Xb, Tb, nullptr, ip, h, nt, 1, h));
     }
   }
-  {
+  if (fused) {
+    dim3 grid((unsigned)cdiv(n, 64), (unsigned)cdiv(n, 64));
+    GPTQ_LAUNCH(K_PREP_UOUT, st, prep_uout_z_kernel<<<grid, 256, 0, st>>>(Xb, ip, n, U));
+  } else {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)std::min<int64_t>(n, 65535));
     GPTQ_LAUNCH(K_PREP_UOUT, st, prep_uout_kernel<<<grid, 256, 0, st>>>(Xb, ip, n, U));
   }
