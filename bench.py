@@ -26,7 +26,7 @@ import numpy as np
 
 METRIC = ("quantized weights/sec per layer + XXᵀ/trailing-GEMM % MFMA peak, 1×MI355X")
 DEFAULT_WORKLOAD = "qwen05b_mlp"
-CHOL_MERGE_TILES = 512  # the library's threshold for the merged factor + update launch
+CHOL_MERGE_TILES = 504  # the library's threshold for the merged factor + update launch
 CHOL_FUSE_NT = 48  # the library's bound on panels for the inverse accumulated in the factorization
 
 # MI355X published peaks

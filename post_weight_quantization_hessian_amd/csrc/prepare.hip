@@ -681,11 +681,13 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
 // (part 2, nsyrk tiles), which touches no tile of panel q's column, and then
 // inverse tiles x0, x0 + 1, ... of panel q-1's step. One launch for two
 // independent pieces of work, so the factor of the next panel runs beside
-// the update instead of after it. The factor's registers limit this kernel
-// to one wave per SIMD, so it is used while the update fits in one round of
-// the GPU (CHOL_MERGE_TILES); larger updates run at two waves per SIMD in
-// their own launch, where the factor is a small fraction of the time.
-constexpr int CHOL_MERGE_TILES = 512;
+// the update instead of after it. The factor's registers allow this kernel
+// two waves per SIMD only with a few of the factor's values spilled to
+// scratch; one round of the GPU then holds about 2 x 255 tiles beside the
+// factor, and the update goes here while it fits in that round
+// (CHOL_MERGE_TILES); larger updates run in their own launch after the
+// factor, where the factor is a small fraction of the time.
+constexpr int CHOL_MERGE_TILES = 504;
 constexpr int STEP_LDS = POTRF_LDS > 4 * GCH ? POTRF_LDS : 4 * GCH;
 __global__ __launch_bounds__(256, 2) void chol_potrf_syrk_kernel(double* __restrict__ K,
                                                               double* __restrict__ Dd,
