@@ -28,6 +28,7 @@ METRIC = ("quantized weights/sec per layer + XXáµ€/trailing-GEMM % MFMA peak, 1Ã
 DEFAULT_WORKLOAD = "qwen05b_mlp"
 CHOL_MERGE_TILES = 504  # the library's threshold for the merged factor + update launch
 CHOL_FUSE_NT = 48  # the library's bound on panels for the inverse accumulated in the factorization
+QEMB_KMAX = 512  # the library's longest early update-GEMM piece inside a sweep launch
 
 # MI355X published peaks
 PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0}
@@ -120,16 +121,17 @@ def kernel_work(name, wl, plan):
                 hh *= 2
         return f, "flop", "f64_mfma"
     if name == "quant_gemm":
+        # the update GEMM flops that run in q_gemm launches (the rest run
+        # inside the sweep launches, see quant_gemm_split)
         f = 0.0
         for h in plan:
-            for bits in wl.bits:
-                for j0 in range(128, h.dim, 128):
-                    bw = min(128, h.dim - j0)
-                    f += 2.0 * h.rows * j0 * bw
+            f += len(wl.bits) * quant_gemm_split(h.rows, h.dim)[0]
         return f, "flop", "f32_mfma"
     if name == "quant_sweep":
         # bytes per weight: fp16 weight 2 + fp64 update 8 + code 1 + fp32 error 4;
         # plus 4 bytes (fp16 scale + zero) per group and the fp32 U slab per block
+        # (the next block's early update GEMM, run by extra workgroups of the
+        # same launches, is not counted here)
         b = 0.0
         for h in plan:
             for bits in wl.bits:
@@ -137,6 +139,37 @@ def kernel_work(name, wl, plan):
                 b += sum(4 * min(128, h.dim - j0) ** 2 for j0 in range(0, h.dim, 128))
         return b, "byte", "hbm"
     return None, None, None
+
+
+def quant_gemm_split(rows, cols):
+    """(flops in q_gemm launches, flops inside sweep launches) of one layer's
+    update GEMM, W~_b = W_b - E[:, :j0] U[:j0, b]. Mirrors the library: while
+    the sweep leaves CUs idle (4 waves per workgroup, room for at least one
+    GEMM workgroup per 64-row tile beside it), the sum over the errors of
+    blocks before b-1 runs inside the sweep launch of block b-1 (pieces of at
+    most QEMB_KMAX) and only the last 128 columns of K run in a q_gemm launch."""
+    rt = -(-rows // 64)
+    pmax = min(16, max(1, -(-512 // rt)))
+    nw = 8 if -(-rows // 32) >= 256 else 4
+    nsweep = -(-rows // (4 * nw))
+    emb_max = min(pmax, (256 - nsweep) // rt) if nw == 4 else 0
+    ep = 0 if emb_max > 0 else -1
+    fg = fe = 0.0
+    for j0 in range(0, cols, 128):
+        bw = min(128, cols - j0)
+        if j0 > 0:
+            fg += 2.0 * rows * (128 if ep >= 0 else j0) * bw
+        nxt = 0 if emb_max > 0 else -1
+        if emb_max > 0 and j0 > 0 and j0 + 128 < cols:
+            pe = min(emb_max, j0 // 128)
+            ks = -(-(-(-j0 // pe)) // 32) * 32
+            if ks <= QEMB_KMAX:
+                nxt = -(-j0 // ks)
+                fe += 2.0 * rows * j0 * min(128, cols - j0 - 128)
+            else:
+                nxt = -1
+        ep = nxt
+    return fg, fe
 
 
 class HPlan:

@@ -106,21 +106,19 @@ __global__ __launch_bounds__(256) void q_finalize_kernel(const uint8_t* __restri
 constexpr int QE_LD = 34;   // Es row pitch (floats)
 constexpr int QU_LD = 160;  // Us row pitch (floats)
 
-__global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E, int64_t lde,
-                                                     const float* __restrict__ U, int64_t ldu,
-                                                     const uint16_t* __restrict__ W, int64_t ldw,
-                                                     int64_t rows, int64_t j0, int bw,
-                                                     int64_t ksplit, double* __restrict__ part,
-                                                     int64_t part_stride,
-                                                     double* __restrict__ wblk, bool vecU) {
-  __shared__ float Es[2][64 * QE_LD];
-  __shared__ float Us[2][32 * QU_LD];
+// One 64-row workgroup tile of the update GEMM over l in [k_lo, k_hi): with
+// wblk, the whole sum, written as W~ = W - sum into wblk; else the partial
+// sum, written to Pp. 256 threads; `lds` holds QG_LDS floats.
+constexpr int QG_LDS = 2 * 64 * QE_LD + 2 * 32 * QU_LD;
+__device__ __forceinline__ void q_gemm_tile(const float* __restrict__ E, int64_t lde,
+                                            const float* __restrict__ U, int64_t ldu,
+                                            const uint16_t* __restrict__ W, int64_t ldw,
+                                            int64_t rows, int64_t j0, int bw, int64_t r0,
+                                            int64_t k_lo, int64_t k_hi, double* __restrict__ Pp,
+                                            double* __restrict__ wblk, bool vecU, float* lds) {
+  float(*Es)[64 * QE_LD] = reinterpret_cast<float(*)[64 * QE_LD]>(lds);
+  float(*Us)[32 * QU_LD] = reinterpret_cast<float(*)[32 * QU_LD]>(lds + 2 * 64 * QE_LD);
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int64_t r0 = (int64_t)blockIdx.x * 64;
-  const int p = blockIdx.y;
-  const int64_t k_lo = (int64_t)p * ksplit;
-  int64_t k_hi = k_lo + ksplit;
-  if (k_hi > j0) k_hi = j0;
   const int nchunks = k_hi > k_lo ? (int)((k_hi - k_lo) / 32) : 0;
 
   // E loader: row t>>2, 8 floats at (t&3)*8; U loader: row t>>3, 16 floats at (t&7)*16
@@ -201,9 +199,8 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
       __syncthreads();
     }
   }
-  const int P = gridDim.y;
   const int col = w * 32 + (lane & 31);
-  if (P == 1) {
+  if (wblk) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -214,7 +211,6 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
       }
     return;
   }
-  double* Pp = part + (int64_t)p * part_stride;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -222,6 +218,25 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
       const int64_t row = r0 + 32 * i + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
       if (row < rows) Pp[row * QB + col] = acc64[i][x];
     }
+}
+
+// The update GEMM for the block at j0 over l in [k_base, k_end) in pieces of
+// ks (blockIdx.y = piece): the partial of piece p goes to part[p_base + p];
+// with wblk (one piece covering all of l < j0) W~ itself goes to wblk.
+__global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E, int64_t lde,
+                                                     const float* __restrict__ U, int64_t ldu,
+                                                     const uint16_t* __restrict__ W, int64_t ldw,
+                                                     int64_t rows, int64_t j0, int bw,
+                                                     int64_t k_base, int64_t ks, int64_t k_end,
+                                                     double* __restrict__ part,
+                                                     int64_t part_stride, int p_base,
+                                                     double* __restrict__ wblk, bool vecU) {
+  __shared__ float lds[QG_LDS];
+  const int p = blockIdx.y;
+  const int64_t k_lo = k_base + (int64_t)p * ks;
+  const int64_t k_hi = k_lo + ks < k_end ? k_lo + ks : k_end;
+  q_gemm_tile(E, lde, U, ldu, W, ldw, rows, j0, bw, (int64_t)blockIdx.x * 64, k_lo, k_hi,
+              part + (int64_t)(p_base + p) * part_stride, wblk, vecU, lds);
 }
 
 // ---------------------------------------------------------------- sweep
@@ -242,12 +257,27 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     const float* __restrict__ U, int64_t ldu, bool vecU, int64_t rows, int64_t j0, int bw,
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
-    double* __restrict__ row_loss, unsigned* __restrict__ status) {
+    double* __restrict__ row_loss, unsigned* __restrict__ status, int nsweep, int64_t gj0,
+    int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart) {
   // U slab plus one row of zero padding: the slot reads of a column run up to
   // 112 entries past its row end, into the next row or the padding, only for
   // slots past the block end whose values are never used.
   __shared__ double Us[QB * QB + QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
+  if ((int)blockIdx.x >= nsweep) {
+    // workgroups past the sweep's own (256 threads each): the next block's
+    // update GEMM over the errors of the blocks before this one, l < gk_end,
+    // as partials gpart[piece]; they neither read nor write this block
+    const int64_t rt = (rows + 63) / 64;
+    const int idx = (int)blockIdx.x - nsweep;
+    const int piece = (int)(idx / rt);
+    const int64_t k_lo = (int64_t)piece * gks;
+    const int64_t k_hi = k_lo + gks < gk_end ? k_lo + gks : gk_end;
+    q_gemm_tile(E, lde, U, ldu, W, ldw, rows, gj0, gbw, (idx - piece * rt) * 64, k_lo, k_hi,
+                gpart + (int64_t)piece * part_stride, nullptr, vecU,
+                reinterpret_cast<float*>(Us));
+    return;
+  }
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int q = lane & 15;
   const int nthr = blockDim.x;
@@ -491,25 +521,49 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
   L.off_wp = take(2 * (size_t)rows * cols);
   L.off_codes = take((size_t)rows * cols);
   L.off_E = take(4 * (size_t)rows * L.lde);
-  L.off_part = take(8 * (size_t)L.pmax * rows * QB);
+  L.off_part = take(8 * 2 * (size_t)(L.pmax + 1) * rows * QB);
   L.off_wblk = take(8 * (size_t)rows * QB);
   L.total = o;
   return L;
 }
 
+// One sweep launch: nsweep workgroups of 64 * nw threads for the block at j0,
+// then ng workgroups (nw == 4 only) of the next block's early update GEMM.
+struct SweepArgs {
+  int nw, nsweep, ng;
+  const uint16_t* W;
+  int64_t ldw;
+  const double* wblk;
+  const double* part;
+  int P;
+  int64_t pstride;
+  const float* U;
+  int64_t ldu;
+  bool vecU;
+  int64_t rows, j0;
+  int bw, bits;
+  float* E;
+  int64_t lde;
+  uint8_t* codes;
+  int64_t ldc;
+  uint16_t* scales;
+  uint16_t* zeros;
+  int64_t ldg;
+  double* row_loss;
+  unsigned* status;
+  int64_t gj0;
+  int gbw;
+  int64_t gks, gk_end;
+  double* gpart;
+};
+
 template <int GS>
-static gptq_status launch_sweep(hipStream_t st, int nw, const uint16_t* Wsrc, int64_t ldws,
-                                const double* wblk, const double* part, int P, int64_t pstride,
-                                const float* U, int64_t cols, bool vecU,
-                                int64_t rows, int64_t j0, int bw, int bits, float* E, int64_t lde,
-                                uint8_t* codes, int64_t ldc, uint16_t* scales, uint16_t* zeros,
-                                int64_t ldg, double* row_loss, unsigned* status) {
-  const unsigned nblk = (unsigned)cdiv(rows, 4 * nw);
+static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
   GPTQ_LAUNCH(K_Q_SWEEP, st,
-              q_sweep_kernel<GS><<<nblk, 64 * nw, 0, st>>>(Wsrc, ldws, wblk, part, P, pstride, U,
-                                                           cols, vecU, rows,
-                                                           j0, bw, bits, E, lde, codes, ldc,
-                                                           scales, zeros, ldg, row_loss, status));
+              q_sweep_kernel<GS><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(
+                  a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0,
+                  a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg, a.row_loss,
+                  a.status, a.nsweep, a.gj0, a.gbw, a.gks, a.gk_end, a.gpart));
   return GPTQ_OK;
 }
 
@@ -571,32 +625,75 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
   // 4 rows per wave; 8 waves per workgroup once that still gives >= 256
   // workgroups, else 4 (the U slab fills most of the LDS: one workgroup per CU)
   const int nw = cdiv(rows, 32) >= 256 ? 8 : 4;
+  const int nsweep = (int)cdiv(rows, 4 * nw);
   const bool vecU = (cols % 4 == 0) && ((uintptr_t)U % 16 == 0);
   const int64_t rt = cdiv(rows, 64);
   double* wblk = (double*)(base + L.off_wblk);
-  for (int64_t j0 = 0; j0 < cols; j0 += QB) {
+  double* partbuf[2] = {part, part + (int64_t)(L.pmax + 1) * pstride};
+  // When the sweep leaves CUs idle, the update GEMM of block b+1 is split:
+  // the sum over the errors of blocks < b runs in the sweep launch of block b
+  // (pieces 0..ep-1, one workgroup per CU beside the sweep's own, while each
+  // piece stays short: QEMB_KMAX), and only the sum over block b's errors
+  // (piece ep, K = 128) runs between the two sweeps. Otherwise the block's
+  // GEMM runs whole before its sweep.
+  constexpr int64_t QEMB_KMAX = 512;
+  const int emb_max = nw == 4 ? std::min<int64_t>(L.pmax, (256 - nsweep) / rt) : 0;
+  int ep = 0;  // early pieces of the current block's GEMM already computed (-1: none)
+  for (int64_t j0 = 0, b = 0; j0 < cols; j0 += QB, ++b) {
     const int bw = (int)std::min<int64_t>(QB, cols - j0);
+    double* pc = partbuf[b & 1];
+    double* pn = partbuf[(b + 1) & 1];
     const double* cur = nullptr;
     int nparts = 0;
     if (j0 > 0) {
-      int64_t p = L.pmax;
-      if (p > j0 / 128) p = j0 / 128;
-      const int64_t ks = round_up(cdiv(j0, p), 32);
-      const int P = (int)cdiv(j0, ks);
-      dim3 grid((unsigned)rt, (unsigned)P);
-      GPTQ_LAUNCH(K_Q_GEMM, st,
-                  q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0, bw,
-                                                      ks, part, pstride, wblk, vecU));
-      // one split: the GEMM wrote W~ itself; else the sweep sums the partials
-      if (P == 1) cur = wblk;
-      else nparts = P;
+      if (ep >= 0) {
+        dim3 grid((unsigned)rt, 1u);
+        GPTQ_LAUNCH(K_Q_GEMM, st,
+                    q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0,
+                                                        bw, j0 - QB, QB, j0, pc, pstride, ep,
+                                                        ep == 0 ? wblk : nullptr, vecU));
+        if (ep == 0) cur = wblk;
+        else nparts = ep + 1;
+      } else {
+        int64_t p = L.pmax;
+        if (p > j0 / 128) p = j0 / 128;
+        const int64_t ks = round_up(cdiv(j0, p), 32);
+        const int P = (int)cdiv(j0, ks);
+        dim3 grid((unsigned)rt, (unsigned)P);
+        GPTQ_LAUNCH(K_Q_GEMM, st,
+                    q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0,
+                                                        bw, 0, ks, j0, pc, pstride, 0,
+                                                        P == 1 ? wblk : nullptr, vecU));
+        // one split: the GEMM wrote W~ itself; else the sweep sums the partials
+        if (P == 1) cur = wblk;
+        else nparts = P;
+      }
+    }
+    SweepArgs a{nw, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
+                bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status,
+                0, 0, 0, 0, pn};
+    ep = emb_max > 0 ? 0 : -1;
+    if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
+      // next block's sum over l < j0 (the errors of blocks < b)
+      const int64_t pe = std::min<int64_t>(emb_max, j0 / 128);
+      const int64_t ks = round_up(cdiv(j0, pe), 32);
+      if (ks <= QEMB_KMAX) {
+        ep = (int)cdiv(j0, ks);
+        a.ng = (int)(ep * rt);
+        a.gj0 = j0 + QB;
+        a.gbw = (int)std::min<int64_t>(QB, cols - j0 - QB);
+        a.gks = ks;
+        a.gk_end = j0;
+      } else {
+        ep = -1;
+      }
     }
     gptq_status s;
     switch (group_size) {
-      case 16: s = launch_sweep<16>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      case 32: s = launch_sweep<32>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      case 64: s = launch_sweep<64>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
-      default: s = launch_sweep<128>(st, nw, Wsrc, ldws, cur, part, nparts, pstride, U, cols, vecU, rows, j0, bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status); break;
+      case 16: s = launch_sweep<16>(st, a); break;
+      case 32: s = launch_sweep<32>(st, a); break;
+      case 64: s = launch_sweep<64>(st, a); break;
+      default: s = launch_sweep<128>(st, a); break;
     }
     if (s != GPTQ_OK) return s;
   }
