@@ -62,20 +62,20 @@ def kernel_work(name, wl, plan):
     if name == "hessian_tile":
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
         return f, "flop", "f64_mfma"
-    if name in ("chol_syrk", "chol_trsm", "chol_potrf_syrk", "chol_potrf", "chol_col"):
+    if name in ("chol_trsm", "chol_potrf_syrk", "chol_potrf", "chol_col"):
         # Mirrors the library's launch sequence. Per panel p with m trailing
         # tile rows: trsm m tiles (a triangular solve with 128 right-hand
-        # sides, 128^3 per tile); the next tile column m tiles (chol_col); the
-        # rest, r = m(m-1)/2 tiles, either beside the next diagonal block in
-        # one launch (chol_potrf_syrk, while r <= CHOL_MERGE_TILES; the
-        # block's (2/3) 128^3 counted there) or as its own chol_syrk launch
-        # after a chol_potrf one. With the inverse accumulated in the
-        # factorization (nt <= CHOL_FUSE_NT), trsm also solves the p + 1
-        # tiles of X's row block p (and the last row block after the loop),
-        # and the m (p + 1) inverse tile updates of the step (2 128^3 each,
-        # half at j = p, where the operand X_pp is triangular) fill the merged
-        # launch up to CHOL_MERGE_TILES background tiles, the rest beside the
-        # column update.
+        # sides, 128^3 per tile); the next tile column, m tiles (chol_col);
+        # the rest of the trailing update, r = m(m-1)/2 tiles of 2 128^3,
+        # beside the next diagonal block (chol_potrf_syrk, the block's
+        # (2/3) 128^3 counted there) up to CHOL_MERGE_TILES (at least the m-1
+        # tiles of the next column), the others beside the next panel's
+        # column update. With the inverse accumulated in the factorization
+        # (nt <= CHOL_FUSE_NT), trsm also solves the p + 1 tiles of X's row
+        # block p (and the last row block after the loop), and the m (p + 1)
+        # inverse tile updates of the step (2 128^3 each, half at j = p, where
+        # the operand X_pp is triangular) fill the rest of the merged launch,
+        # the others beside the column update.
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
@@ -84,12 +84,13 @@ def kernel_work(name, wl, plan):
                 f += 2 * 128 ** 3 / 3.0  # panel 0
             if name == "chol_trsm" and fused:
                 f += 128 ** 3 * nt  # last row block of X
+            sov = 0
             for p in range(nt - 1):
                 m = nt - 1 - p
                 r = m * (m - 1) // 2
-                merged = r <= CHOL_MERGE_TILES
                 xt = m * (p + 1) if fused else 0
-                xstep = min(xt, CHOL_MERGE_TILES - r) if merged else 0
+                ns = min(r, max(CHOL_MERGE_TILES, m - 1))
+                xstep = min(xt, max(0, CHOL_MERGE_TILES - ns))
                 xcol = xt - xstep
 
                 def xflops(ids):
@@ -97,14 +98,10 @@ def kernel_work(name, wl, plan):
                 if name == "chol_trsm":
                     f += 128 ** 3 * (m + ((p + 1) if fused else 0))
                 elif name == "chol_col":
-                    f += 2 * 128 ** 3 * m + xflops(range(xcol))
-                elif name == "chol_syrk":
-                    f += 2 * 128 ** 3 * (0 if merged else r)
+                    f += 2 * 128 ** 3 * (m + sov) + xflops(range(xcol))
                 elif name == "chol_potrf_syrk":
-                    if merged:
-                        f += 2 * 128 ** 3 * r + 2 * 128 ** 3 / 3.0 + xflops(range(xcol, xt))
-                elif not merged:
-                    f += 2 * 128 ** 3 / 3.0
+                    f += 2 * 128 ** 3 * ns + 2 * 128 ** 3 / 3.0 + xflops(range(xcol, xt))
+                sov = r - ns
         return f, "flop", "f64_mfma"
     if name in ("trtri_t", "trtri_x"):
         # X21 = -X22 (L21 X11) at each doubling level, triangular zeros skipped
@@ -186,7 +183,7 @@ KERNEL_CLASS = {  # device function name -> timing class
     "chol_potrf_syrk_kernel": "chol_potrf_syrk", "chol_potrf_kernel": "chol_potrf",
     "chol_col_kernel": "chol_col",
     "chol_trsm_kernel": "chol_trsm",
-    "chol_syrk_kernel": "chol_syrk", "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x", "trtri_sum_kernel": "trtri_sum",
+    "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x", "trtri_sum_kernel": "trtri_sum",
     "trtri_diag_kernel": "trtri_diag", "q_gemm_kernel": "quant_gemm",
     "q_sweep_kernel": "quant_sweep",
     "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout"}

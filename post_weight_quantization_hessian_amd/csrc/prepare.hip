@@ -302,9 +302,12 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
       double x[16];
 #pragma unroll
       for (int c = 0; c < 16; ++c) x[c] = T[c * PT + ri];
-      // column c of L_ss is read one column ahead (a scheduling barrier per
-      // column keeps all 120 entries from being hoisted into registers)
+      // column c of L_ss and its reciprocal diagonal are read one column
+      // ahead, so no LDS latency sits in the dependent chain (a scheduling
+      // barrier per column keeps all 120 entries from being hoisted into
+      // registers)
       double lc[16], ln[16];
+      double dc = invd[s][0], dn = 0.0;
 #pragma unroll
       for (int m = 1; m < 16; ++m) lc[m] = Ls[m];
 #pragma unroll
@@ -312,12 +315,14 @@ __device__ __forceinline__ void potrf_block(double* __restrict__ K, double* __re
         if (c + 1 < 16) {
 #pragma unroll
           for (int m = c + 2; m < 16; ++m) ln[m] = Ls[(c + 1) * PT + m];
+          dn = invd[s][c + 1];
         }
-        x[c] *= invd[s][c];
+        x[c] *= dc;
 #pragma unroll
         for (int m = c + 1; m < 16; ++m) x[m] -= x[c] * lc[m];
 #pragma unroll
         for (int m = c + 2; m < 16; ++m) lc[m] = ln[m];
+        dc = dn;
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -530,23 +535,25 @@ __device__ __forceinline__ void tile_nt_update(const double* A, const double* B,
   for_each_acc(acc, [&](int r, int c, double v) { C[r * ld + c] = v; });
 }
 
-// Tile `id` of the trailing update of panel p, C -= L_a L_b^T: part 1, the
-// next panel's tile column (b = 0, a = id); part 2, the rest (tiles
-// a >= b >= 1 of the trailing triangle, row-major), in trailing-tile
-// coordinates. Sets the operands of tile_nt_update.
-__device__ inline void syrk_tile_args(double* K, int64_t ld, int p, int part, int id,
+// Tile `id` of the rest of the trailing update of panel p, C -= L_a L_b^T
+// over the tiles a >= b >= 1 of the trailing triangle (mt tile rows, in
+// trailing-tile coordinates; b = 0 is the next panel's column): first the
+// column b = 1 (a = 1 .. mt-1), which the next column update reads, then the
+// tiles a >= b >= 2 row by row. Sets the operands of tile_nt_update.
+__device__ inline void syrk_tile_args(double* K, int64_t ld, int p, int mt, int id,
                                       const double*& A, const double*& B, double*& C) {
   int a, b;
-  if (part == 1) {
-    a = id;
-    b = 0;
+  if (id < mt - 1) {
+    a = 1 + id;
+    b = 1;
   } else {
-    a = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
-    while (a * (a + 1) / 2 > id) --a;
-    while ((a + 1) * (a + 2) / 2 <= id) ++a;
-    b = id - a * (a + 1) / 2;
-    ++a;
-    ++b;
+    const int i2 = id - (mt - 1);
+    a = (int)((sqrt(8.0 * i2 + 1.0) - 1.0) * 0.5);
+    while (a * (a + 1) / 2 > i2) --a;
+    while ((a + 1) * (a + 2) / 2 <= i2) ++a;
+    b = i2 - a * (a + 1) / 2;
+    a += 2;
+    b += 2;
   }
   const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
   const int64_t ra = c1 + (int64_t)a * GT, rb = c1 + (int64_t)b * GT;
@@ -576,22 +583,23 @@ __device__ inline void xinv_tile_args(double* K, double* Z, int64_t ld, int p, i
   crows = j == p ? 0 : GT;
 }
 
-// Background tile `id` of panel p: the first nsyrk ids are tiles of part
-// `part` of the trailing update, the others inverse tiles x0, x0 + 1, ...
-__device__ __forceinline__ void bg_tile(double* K, double* Z, int64_t ld, int p, int part,
-                                        int nsyrk, int x0, int id, double* smem) {
+// Background tile `id`: the first nsyrk ids are the trailing-update tiles
+// s0, s0 + 1, ... of panel ps (mts trailing tile rows), the others the
+// inverse tiles x0, x0 + 1, ... of panel px's step.
+__device__ __forceinline__ void bg_tile(double* K, double* Z, int64_t ld, int ps, int mts, int s0,
+                                        int nsyrk, int px, int x0, int id, double* smem) {
   const double *A, *B;
   double* C;
   int crows = GT;
   if (id < nsyrk)
-    syrk_tile_args(K, ld, p, part, id, A, B, C);
+    syrk_tile_args(K, ld, ps, mts, s0 + id, A, B, C);
   else
-    xinv_tile_args(K, Z, ld, p, x0 + id - nsyrk, A, B, C, crows);
+    xinv_tile_args(K, Z, ld, px, x0 + id - nsyrk, A, B, C, crows);
   tile_nt_update(A, B, C, ld, crows, smem);
 }
 
 // The next panel's tile column, C(a, p+1) -= L(a, p) L(p+1, p)^T for every
-// tile row a below panel p, at a finer grain than chol_syrk_kernel because
+// tile row a below panel p, at a finer grain than the background tiles because
 // this update is on the critical path of the factorization: one workgroup
 // per 64x64 quadrant (4 per tile), each wave a 32x32 block as 2x2 fp64 MFMA
 // tiles. The operands are read from global memory (they are hot in L2)
@@ -600,15 +608,18 @@ __device__ __forceinline__ void bg_tile(double* K, double* Z, int64_t ld, int p,
 // A[m][k] = L[row m][c0 + k], B[k][n] = L[col n][c0 + k]: lane l reads row
 // (l & 15) of its 16-row group at K offset l >> 4.
 //
-// Workgroups from 4 * mt on (when the inverse is accumulated beside the
-// factorization) apply the first inverse tiles of panel p's step, one each.
+// Workgroups from 4 * mt on are background tiles, one each: the trailing-
+// update tiles s0 .. s0 + nsyrk - 1 of panel p-1 that did not fit beside
+// the factor of panel p (none in panel p's column, which this launch
+// updates), then the first inverse tiles of panel p's step.
 __global__ __launch_bounds__(256, 2) void chol_col_kernel(double* __restrict__ K,
                                                           double* __restrict__ Z, int64_t ld,
-                                                          int p, int mt) {
+                                                          int p, int mt, int s0, int nsyrk) {
   if ((int)blockIdx.x >= 4 * mt) {
     __shared__ double smem[4 * GCH];
     const int nx = (int)gridDim.x - 4 * mt;
-    bg_tile(K, Z, ld, p, 2, 0, 0, xcd_remap((int)blockIdx.x - 4 * mt, nx), smem);
+    bg_tile(K, Z, ld, p - 1, mt + 1, s0, nsyrk, p, 0,
+            xcd_remap((int)blockIdx.x - 4 * mt, nx), smem);
     return;
   }
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -659,15 +670,6 @@ __global__ __launch_bounds__(256, 2) void chol_col_kernel(double* __restrict__ K
         K[(row0 + i * 16 + (lane >> 4) + 4 * r) * ld + col0 + j * 16 + (lane & 15)] = acc[i][j][r];
 }
 
-// Part `part` of the trailing update of panel p (nsyrk tiles), then the
-// inverse tiles x0, x0 + 1, ... of panel p's step (the rest of the grid).
-__global__ __launch_bounds__(256) void chol_syrk_kernel(double* __restrict__ K,
-                                                        double* __restrict__ Z, int64_t ld, int p,
-                                                        int part, int nsyrk, int x0) {
-  __shared__ double smem[4 * GCH];
-  bg_tile(K, Z, ld, p, part, nsyrk, x0, xcd_remap(blockIdx.x, gridDim.x), smem);
-}
-
 // The diagonal block of panel p alone.
 __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
                                                          double* __restrict__ Dd, int64_t ld, int p,
@@ -677,28 +679,30 @@ __global__ __launch_bounds__(256) void chol_potrf_kernel(double* __restrict__ K,
 }
 
 // Workgroup 0 factors the diagonal block of panel q (its tile column is
-// already updated); the others apply the rest of panel q-1's trailing update
-// (part 2, nsyrk tiles), which touches no tile of panel q's column, and then
-// inverse tiles x0, x0 + 1, ... of panel q-1's step. One launch for two
-// independent pieces of work, so the factor of the next panel runs beside
-// the update instead of after it. The factor's registers allow this kernel
-// two waves per SIMD only with a few of the factor's values spilled to
-// scratch; one round of the GPU then holds about 2 x 255 tiles beside the
-// factor, and the update goes here while it fits in that round
-// (CHOL_MERGE_TILES); larger updates run in their own launch after the
-// factor, where the factor is a small fraction of the time.
+// already updated); the others are background tiles: the first nsyrk tiles
+// of the rest of panel q-1's trailing update (which touches no tile of panel
+// q's column), then inverse tiles x0, x0 + 1, ... of panel q-1's step. One
+// launch for independent pieces of work, so the factor of the next panel
+// runs beside the update instead of after it. The factor's registers allow
+// this kernel two waves per SIMD only with a few of the factor's values
+// spilled to scratch; one round of the GPU then holds about 2 x 255 tiles
+// beside the factor (CHOL_MERGE_TILES). Trailing-update tiles beyond that
+// round, other than those of the next column, run beside the next column
+// update.
 constexpr int CHOL_MERGE_TILES = 504;
 constexpr int STEP_LDS = POTRF_LDS > 4 * GCH ? POTRF_LDS : 4 * GCH;
 __global__ __launch_bounds__(256, 2) void chol_potrf_syrk_kernel(double* __restrict__ K,
                                                               double* __restrict__ Dd,
                                                               double* __restrict__ Z, int64_t ld,
-                                                              int q, unsigned* __restrict__ status,
+                                                              int q, int mts,
+                                                              unsigned* __restrict__ status,
                                                               int nsyrk, int x0) {
   __shared__ double smem[STEP_LDS];
   if (blockIdx.x == 0)
     potrf_block(K, Dd, ld, q, status, smem);
   else
-    bg_tile(K, Z, ld, q - 1, 2, nsyrk, x0, xcd_remap(blockIdx.x - 1, gridDim.x - 1), smem);
+    bg_tile(K, Z, ld, q - 1, mts, 0, nsyrk, q - 1, x0,
+            xcd_remap(blockIdx.x - 1, gridDim.x - 1), smem);
 }
 
 // ---------------------------------------------------------------- inverse
@@ -963,35 +967,34 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   // factors the next diagonal block beside the rest of the trailing update.
   // With the fused inverse, the panel solve also solves row block p of
   // X = L^-1, and the column update also applies panel p's step of X.
-  // Panel p's inverse tiles fill the launch with the next diagonal block up
-  // to CHOL_MERGE_TILES background tiles; the first ones (those that do not
-  // fit there, or all when that launch is split) run beside the column
-  // update. Both launches precede the next panel solve, which reads the
-  // first tile row of them.
+  // Background tiles of panel p (the rest of its trailing update, then its
+  // step of the inverse, tile row p + 1 first) go beside the next diagonal
+  // block up to CHOL_MERGE_TILES (always the trailing tiles of column p + 2,
+  // which the next column update reads); the inverse tiles that do not fit
+  // run beside panel p's column update (before the next panel solve, which
+  // reads tile row p + 1), the trailing tiles that do not fit beside panel
+  // p+1's column update (before panel p+1's own trailing tiles).
   const bool fused = nt <= CHOL_FUSE_NT;
+  int sov = 0, sov0 = 0;  // trailing tiles of the previous panel for this column update
   GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
   for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
     const int rest = (mt - 1) * mt / 2;
     const int xs = fused ? 2 * (p + 1) : 0;   // inverse row-solve workgroups
     const int xt = fused ? mt * (p + 1) : 0;  // inverse tile updates
-    const bool merged = rest <= CHOL_MERGE_TILES;
-    const int xstep = merged ? std::min(xt, CHOL_MERGE_TILES - rest) : 0;
+    const int ns = std::min(rest, std::max(CHOL_MERGE_TILES, mt - 1));
+    const int xstep = std::min(xt, std::max(0, CHOL_MERGE_TILES - ns));
     const int xcol = xt - xstep;
     GPTQ_LAUNCH(K_CHOL_TRSM, st,
                 chol_trsm_kernel<<<2 * mt + xs, 256, 0, st>>>(K, Dd, Xb, ip, p, mt));
     GPTQ_LAUNCH(K_CHOL_COL, st,
-                chol_col_kernel<<<4 * mt + xcol, 256, 0, st>>>(K, Xb, ip, p, mt));
-    if (merged) {
-      GPTQ_LAUNCH(K_CHOL_STEP, st,
-                  chol_potrf_syrk_kernel<<<1 + rest + xstep, 256, 0, st>>>(K, Dd, Xb, ip, p + 1,
-                                                                          status, rest, xcol));
-    } else {
-      GPTQ_LAUNCH(K_CHOL_POTRF, st,
-                  chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, p + 1, status));
-      GPTQ_LAUNCH(K_CHOL_SYRK, st,
-                  chol_syrk_kernel<<<rest, 256, 0, st>>>(K, Xb, ip, p, 2, rest, 0));
-    }
+                chol_col_kernel<<<4 * mt + sov + xcol, 256, 0, st>>>(K, Xb, ip, p, mt, sov0,
+                                                                     sov));
+    GPTQ_LAUNCH(K_CHOL_STEP, st,
+                chol_potrf_syrk_kernel<<<1 + ns + xstep, 256, 0, st>>>(K, Dd, Xb, ip, p + 1, mt,
+                                                                      status, ns, xcol));
+    sov = rest - ns;
+    sov0 = ns;
   }
   if (fused) {
     // the last block row of X
