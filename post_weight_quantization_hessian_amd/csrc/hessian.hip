@@ -127,26 +127,39 @@ __global__ __launch_bounds__(256) void hess_tile_kernel(const float* __restrict_
 }
 
 // Sum the token-split partials of every tile in split order and add to S.
+// One 64x64 quarter of a tile per workgroup: rows of the partials are read
+// and rows of S written along the row; the mirror S[j][i] is written from an
+// LDS transpose, so its rows are contiguous too.
 __global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restrict__ part, int nsplit,
                                                           int nt, int ntiles, int64_t dim,
                                                           double* __restrict__ S, int64_t lds,
                                                           bool overwrite) {
-  const int tile = blockIdx.y;
+  __shared__ double tr[64][65];
+  const int tile = blockIdx.y, quarter = blockIdx.x;
   int a, b;
   upper_tile(tile, nt, a, b);
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // element within tile
-  if (e >= GT * GT) return;
-  const int r = e / GT, c = e % GT;
-  const int64_t i = (int64_t)a * GT + r, j = (int64_t)b * GT + c;
-  if (i >= dim || j >= dim) return;
-  double s = 0.0;
-  for (int p = 0; p < nsplit; ++p) s += part[((int64_t)p * ntiles + tile) * (GT * GT) + e];
-  if (overwrite) {
-    S[i * lds + j] = s;
-    if (a != b) S[j * lds + i] = s;
-  } else {
-    S[i * lds + j] += s;
-    if (a != b) S[j * lds + i] += s;
+  const int qr = (quarter >> 1) * 64, qc = (quarter & 1) * 64;
+  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int64_t i0 = (int64_t)a * GT + qr, j0 = (int64_t)b * GT + qc;
+  const double* src = part + (int64_t)tile * (GT * GT) + qr * GT + qc;
+  for (int m = 0; m < 16; ++m) {
+    const int r = rg + 4 * m;
+    double s = 0.0;
+    for (int p = 0; p < nsplit; ++p) s += src[(int64_t)p * ntiles * (GT * GT) + r * GT + c];
+    const int64_t i = i0 + r, j = j0 + c;
+    if (i < dim && j < dim) {
+      double* d = S + i * lds + j;
+      s = overwrite ? s : *d + s;
+      *d = s;
+    }
+    tr[r][c] = s;
+  }
+  if (a == b) return;  // a diagonal tile is its own mirror (uniform per workgroup)
+  __syncthreads();
+  for (int m = 0; m < 16; ++m) {
+    const int r = rg + 4 * m;  // row of the mirror block = column of this block
+    const int64_t j = j0 + r, i = i0 + c;
+    if (i < dim && j < dim) S[j * lds + i] = tr[c][r];
   }
 }
 
@@ -226,7 +239,7 @@ extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, c
   }
 #undef HESS_TILE
   if (part) {
-    dim3 grid(GT * GT / 256, ntiles);
+    dim3 grid(4, ntiles);
     GPTQ_LAUNCH(K_HESS_REDUCE, st,
                 hess_reduce_kernel<<<grid, 256, 0, st>>>(part, nsplit, nt, ntiles, in_features, S,
                                                          in_features, overwrite));
