@@ -144,7 +144,9 @@ def quant_gemm_split(rows, cols):
     the sweep leaves CUs idle (4 waves per workgroup, room for at least one
     GEMM workgroup per 64-row tile beside it), the sum over the errors of
     blocks before b-1 runs inside the sweep launch of block b-1 (pieces of at
-    most QEMB_KMAX) and only the last 128 columns of K run in a q_gemm launch."""
+    most QEMB_KMAX) and the sum over block b-1's errors inside the sweep of
+    block b; otherwise (and for a block whose early pieces would be longer)
+    the whole sum runs in a q_gemm launch before the sweep."""
     rt = -(-rows // 64)
     pmax = min(16, max(1, -(-512 // rt)))
     nw = 8 if -(-rows // 32) >= 256 else 4
@@ -155,7 +157,10 @@ def quant_gemm_split(rows, cols):
     for j0 in range(0, cols, 128):
         bw = min(128, cols - j0)
         if j0 > 0:
-            fg += 2.0 * rows * (128 if ep >= 0 else j0) * bw
+            if ep >= 0:
+                fe += 2.0 * rows * 128 * bw
+            else:
+                fg += 2.0 * rows * j0 * bw
         nxt = 0 if emb_max > 0 else -1
         if emb_max > 0 and j0 > 0 and j0 + 128 < cols:
             pe = min(emb_max, j0 // 128)

@@ -257,13 +257,14 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     const float* __restrict__ U, int64_t ldu, bool vecU, int64_t rows, int64_t j0, int bw,
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
-    double* __restrict__ row_loss, unsigned* __restrict__ status, int nsweep, int64_t gj0,
-    int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart) {
+    double* __restrict__ row_loss, unsigned* __restrict__ status, bool late, int nsweep,
+    int64_t gj0, int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart) {
   // U slab plus one row of zero padding: the slot reads of a column run up to
   // 112 entries past its row end, into the next row or the padding, only for
   // slots past the block end whose values are never used.
   __shared__ double Us[QB * QB + QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
+  __shared__ double lt[16][QB];  // the sum over the previous block's errors (late)
   if ((int)blockIdx.x >= nsweep) {
     // workgroups past the sweep's own (256 threads each): the next block's
     // update GEMM over the errors of the blocks before this one, l < gk_end,
@@ -288,21 +289,64 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   // All global loads of the prologue are issued before any is waited on:
   // this row's current values, the U slab (16 float4 per thread for 256
   // threads), and the diagonal of the slab.
-  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk], formed by
-  // the update GEMM (wblk); the first block reads the weights directly.
-  // With P > 1 the update GEMM left P split-K partials: they are summed here
-  // in split order (the order a separate reduction would use) and
-  // subtracted from the weights.
+  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk]. Either
+  // the update GEMM formed them whole (wblk), or it left P split-K partials
+  // of the sum over l < j0 (l < j0 - 128 with `late`), which are added here
+  // in split order, and with `late` (256 threads) the workgroup forms the
+  // sum over the previous block's 128 errors itself, last; the first block
+  // reads the weights directly.
+  //
+  // The late sum, for the workgroup's 16 rows: wave wv takes columns
+  // 32 wv .. 32 wv + 31 as two 16x16 fp32 MFMA tiles over K = 128, summed in
+  // fp32 per 32-wide K chunk and in fp64 across chunks (as the update GEMM
+  // does), and leaves them in lt. v_mfma_f32_16x16x4f32 layout (lane l):
+  // A[m][k]: m = l%16, k = l/16; B[k][n]: n = l%16, k = l/16; D element i:
+  // row 4*(l/16) + i, col l%16.
+  if (late) {
+    const int64_t arow = (int64_t)blockIdx.x * 16 + (lane & 15);
+    const float* ea = E + (arow < rows ? arow : rows - 1) * lde + (j0 - QB) + (lane >> 4);
+    const int n0 = 32 * wv + (lane & 15);
+    const float* ub = U + (j0 - QB + (lane >> 4)) * ldu + j0 + n0;
+    const bool cv0 = n0 < bw, cv1 = n0 + 16 < bw;
+    double dl[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      float av[8], bv0[8], bv1[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int k = 32 * ch + 4 * st;
+        av[st] = ea[k];
+        bv0[st] = cv0 ? ub[(int64_t)k * ldu] : 0.0f;
+        bv1[st] = cv1 ? ub[(int64_t)k * ldu + 16] : 0.0f;
+      }
+      f4 m0 = {0.0f, 0.0f, 0.0f, 0.0f}, m1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv0[st], m0, 0, 0, 0);
+        m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv1[st], m1, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dl[0][i] += (double)m0[i];
+        dl[1][i] += (double)m1[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lt[4 * (lane >> 4) + i][n0] = dl[0][i];
+      lt[4 * (lane >> 4) + i][n0 + 16] = dl[1][i];
+    }
+  }
   double w[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const int c = 16 * s + q;
     w[s] = (rv && c < bw) ? (wblk ? wblk[r * QB + c] : f16_to_f64(W[r * ldw + j0 + c])) : 0.0;
   }
-  if (P > 1) {
-    double acc[8];
+  double acc[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc[s] = 0.0;
+  for (int s = 0; s < 8; ++s) acc[s] = 0.0;
+  if (!wblk && P > 0) {
     const double* pr = part + (rv ? r : 0) * QB + q;
     for (int p0 = 0; p0 < P; p0 += 4) {
       double v[4][8];
@@ -318,8 +362,6 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         for (int s = 0; s < 8; ++s)
           if (p0 + u < P) acc[s] += v[u][s];
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) w[s] = (rv && 16 * s + q < bw) ? w[s] - acc[s] : 0.0;
   }
   const bool vec_slab = vecU && bw == QB;
   constexpr int SLAB4 = QB * QB / 4;       // float4s in the slab
@@ -367,6 +409,13 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] * rdiag[a] : 0.0;
     }
   }
+  // (lt was written before the first barrier above)
+  if (late) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[s] += lt[wv * 4 + (lane >> 4)][16 * s + q];
+  }
+#pragma unroll
+  for (int s = 0; s < 8; ++s) w[s] = (rv && 16 * s + q < bw) ? w[s] - acc[s] : 0.0;
   bool finite = true;
 #pragma unroll
   for (int s = 0; s < 8; ++s) finite = finite && isfinite(w[s]);
@@ -527,8 +576,10 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
   return L;
 }
 
-// One sweep launch: nsweep workgroups of 64 * nw threads for the block at j0,
-// then ng workgroups (nw == 4 only) of the next block's early update GEMM.
+// One sweep launch: nsweep workgroups of 64 * nw threads for the block at j0
+// (with `late`, nw == 4 only, they add the sum over the previous block's
+// errors themselves), then ng workgroups (nw == 4 only) of the next block's
+// early update GEMM.
 struct SweepArgs {
   int nw, nsweep, ng;
   const uint16_t* W;
@@ -551,6 +602,7 @@ struct SweepArgs {
   int64_t ldg;
   double* row_loss;
   unsigned* status;
+  bool late;
   int64_t gj0;
   int gbw;
   int64_t gks, gk_end;
@@ -563,7 +615,7 @@ static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
               q_sweep_kernel<GS><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(
                   a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0,
                   a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg, a.row_loss,
-                  a.status, a.nsweep, a.gj0, a.gbw, a.gks, a.gk_end, a.gpart));
+                  a.status, a.late, a.nsweep, a.gj0, a.gbw, a.gks, a.gk_end, a.gpart));
   return GPTQ_OK;
 }
 
@@ -633,9 +685,9 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
   // When the sweep leaves CUs idle, the update GEMM of block b+1 is split:
   // the sum over the errors of blocks < b runs in the sweep launch of block b
   // (pieces 0..ep-1, one workgroup per CU beside the sweep's own, while each
-  // piece stays short: QEMB_KMAX), and only the sum over block b's errors
-  // (piece ep, K = 128) runs between the two sweeps. Otherwise the block's
-  // GEMM runs whole before its sweep.
+  // piece stays short: QEMB_KMAX), and the sum over block b's errors
+  // (K = 128) is formed by the sweep workgroups of block b+1 themselves.
+  // Otherwise the block's GEMM runs whole before its sweep.
   constexpr int64_t QEMB_KMAX = 512;
   const int emb_max = nw == 4 ? std::min<int64_t>(L.pmax, (256 - nsweep) / rt) : 0;
   int ep = 0;  // early pieces of the current block's GEMM already computed (-1: none)
@@ -645,15 +697,11 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
     double* pn = partbuf[(b + 1) & 1];
     const double* cur = nullptr;
     int nparts = 0;
+    bool late = false;
     if (j0 > 0) {
       if (ep >= 0) {
-        dim3 grid((unsigned)rt, 1u);
-        GPTQ_LAUNCH(K_Q_GEMM, st,
-                    q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0,
-                                                        bw, j0 - QB, QB, j0, pc, pstride, ep,
-                                                        ep == 0 ? wblk : nullptr, vecU));
-        if (ep == 0) cur = wblk;
-        else nparts = ep + 1;
+        late = true;
+        nparts = ep;
       } else {
         int64_t p = L.pmax;
         if (p > j0 / 128) p = j0 / 128;
@@ -670,7 +718,7 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
       }
     }
     SweepArgs a{nw, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
-                bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status,
+                bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, late,
                 0, 0, 0, 0, pn};
     ep = emb_max > 0 ? 0 : -1;
     if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
