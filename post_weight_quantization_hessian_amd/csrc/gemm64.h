@@ -123,14 +123,24 @@ __device__ inline void acc_load_lds(d4 (&acc)[4][4], const double* C, int64_t ld
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
+    // every load is issued before the first LDS store: `stage` is a generic
+    // pointer, so a store between two loads would order them one by one
+    double v[32];
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       const int idx = e * 256 + t;
       const int rr = idx >> 7, cc = idx & 127;
       const int row = 64 * half + rr;
       const bool ok = row < rows && cc < cols;
-      const double v = C[ok ? (int64_t)row * ld + cc : 0];
-      stage[idx] = ok ? v : 0.0;
+      v[e] = C[ok ? (int64_t)row * ld + cc : 0];
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int idx = e * 256 + t;
+      const int rr = idx >> 7, cc = idx & 127;
+      const int row = 64 * half + rr;
+      const bool ok = row < rows && cc < cols;
+      stage[idx] = ok ? v[e] : 0.0;
     }
     __syncthreads();
     if (wm == half) {
