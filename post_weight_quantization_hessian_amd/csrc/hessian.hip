@@ -142,17 +142,34 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restri
   const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
   const int64_t i0 = (int64_t)a * GT + qr, j0 = (int64_t)b * GT + qc;
   const double* src = part + (int64_t)tile * (GT * GT) + qr * GT + qc;
+  // all loads of a split (and of the old S) before any store, so they are in
+  // flight together
+  double acc[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) acc[m] = 0.0;
+  for (int p = 0; p < nsplit; ++p) {
+    double v[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) v[m] = src[(int64_t)p * ntiles * (GT * GT) + (rg + 4 * m) * GT + c];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m] += v[m];
+  }
+  if (!overwrite) {
+    double old[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int64_t i = i0 + rg + 4 * m, j = j0 + c;
+      old[m] = (i < dim && j < dim) ? S[i * lds + j] : 0.0;
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) acc[m] = old[m] + acc[m];
+  }
+#pragma unroll
   for (int m = 0; m < 16; ++m) {
     const int r = rg + 4 * m;
-    double s = 0.0;
-    for (int p = 0; p < nsplit; ++p) s += src[(int64_t)p * ntiles * (GT * GT) + r * GT + c];
     const int64_t i = i0 + r, j = j0 + c;
-    if (i < dim && j < dim) {
-      double* d = S + i * lds + j;
-      s = overwrite ? s : *d + s;
-      *d = s;
-    }
-    tr[r][c] = s;
+    if (i < dim && j < dim) S[i * lds + j] = acc[m];
+    tr[r][c] = acc[m];
   }
   if (a == b) return;  // a diagonal tile is its own mirror (uniform per workgroup)
   __syncthreads();

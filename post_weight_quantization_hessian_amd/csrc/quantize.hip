@@ -259,10 +259,11 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
     double* __restrict__ row_loss, unsigned* __restrict__ status, bool late, int nsweep,
     int64_t gj0, int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart) {
-  // U slab plus one row of zero padding: the slot reads of a column run up to
-  // 112 entries past its row end, into the next row or the padding, only for
-  // slots past the block end whose values are never used.
-  __shared__ double Us[QB * QB + QB];
+  // U slab plus three rows of zero padding: the slot reads of a column run up
+  // to 112 entries past its row end, into the next row or the padding, only
+  // for slots past the block end whose values are never used; rows are read
+  // two columns ahead up to row QB + 1.
+  __shared__ double Us[QB * QB + 3 * QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
   __shared__ double lt[16][QB];  // the sum over the previous block's errors (late)
   if ((int)blockIdx.x >= nsweep) {
@@ -379,6 +380,8 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   for (int j = t; j < QB; j += nthr) {
     rdiag[j] = j < bw ? 1.0 / (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
     Us[QB * QB + j] = 0.0;
+    Us[QB * QB + QB + j] = 0.0;
+    Us[QB * QB + 2 * QB + j] = 0.0;
   }
   __syncthreads();
   // Row a of the slab is stored divided by U[a][a] (the error broadcast along
@@ -435,8 +438,9 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     for (int s = 0; s < 8; ++s) uu[s] = urow[16 * s];
   };
   load_row(0, ub[0]);
-  load_row(bw > 1 ? 1 : 0, ub[1]);
+  load_row(1, ub[1]);
   for (int tt = 0; tt < nt16; ++tt) {
+    const double* ubase = Us + 16 * tt * QB + 16 * tt + q;
     if (((16 * tt) % GS) == 0) {
       // grid of the group starting here, from the current values
       double mn = 0.0, mx = 0.0;
@@ -476,10 +480,17 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     double d_own = 0.0, k_own = 0.0;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-      const int j = 16 * tt + jj;
-      if (j < bw) {
+      if (16 * tt + jj < bw) {
         double (&u)[8] = ub[jj & 3];
-        load_row(j + 2 < bw ? j + 2 : j, ub[(jj + 2) & 3]);
+        {
+          // row 16 tt + jj + 2 at a fixed offset from the group's base (one
+          // address register for the whole group; rows past the block end
+          // are zero rows of the slab or its padding)
+          const int jc = jj + 2;
+          const double* urow = ubase + jc * QB + 16 * (jc >> 4);
+#pragma unroll
+          for (int s = 0; s < 8; ++s) ub[(jj + 2) & 3][s] = urow[16 * s];
+        }
         // quantize slot 0 (meaningful on the owner lane q == jj):
         // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
         // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
