@@ -163,7 +163,7 @@ def quant_gemm_split(rows, cols):
                 fg += 2.0 * rows * j0 * bw
         nxt = 0 if emb_max > 0 else -1
         if emb_max > 0 and j0 > 0 and j0 + 128 < cols:
-            pe = min(emb_max, j0 // 128)
+            pe = min(emb_max, -(-j0 // QEMB_KMAX))
             ks = -(-(-(-j0 // pe)) // 32) * 32
             if ks <= QEMB_KMAX:
                 nxt = -(-j0 // ks)

@@ -733,8 +733,10 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
                 0, 0, 0, 0, pn};
     ep = emb_max > 0 ? 0 : -1;
     if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
-      // next block's sum over l < j0 (the errors of blocks < b)
-      const int64_t pe = std::min<int64_t>(emb_max, j0 / 128);
+      // next block's sum over l < j0 (the errors of blocks < b), in as few
+      // pieces of at most QEMB_KMAX as fit (each piece is one more partial
+      // for the sweep to add)
+      const int64_t pe = std::min<int64_t>(emb_max, cdiv(j0, QEMB_KMAX));
       const int64_t ks = round_up(cdiv(j0, pe), 32);
       if (ks <= QEMB_KMAX) {
         ep = (int)cdiv(j0, ks);
