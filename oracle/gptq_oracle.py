@@ -42,6 +42,10 @@ Readings of what the pages leave open (each listed in the design doc):
 * Rounding is round-half-to-even (rint); codes are clamped to [0, maxq]
   unless ``clip=False`` (the no-clipping regime of [BABAI] 2.3).
 * Act-order: stable argsort of -diag(H) (ties keep the lower index first).
+* Min-pivot order: greedy LDL of the damped H with the smallest Schur
+  diagonal as the next pivot (ties: the higher index first); the sweep runs
+  in the reverse elimination order (so for a diagonal H it equals act-order,
+  ties included).
 * Per-row loss: sum_j e_j^2 with e_j = (w~_j - q_j)/U[j,j]; this equals
   (w-q) H (w-q)^T for the damped, permuted H.
 """
@@ -54,7 +58,7 @@ import numpy as np
 
 __all__ = [
     "NotSPD", "NonFinite", "hessian_sum", "hessian_entry", "hessian_diag",
-    "damping_lambda", "damped_diagonal", "damped_hessian", "act_order_from_diag", "act_order_perm", "permute_sym", "hinv_upper", "fp16_round", "group_grid",
+    "damping_lambda", "damped_diagonal", "damped_hessian", "act_order_from_diag", "act_order_perm", "min_pivot_order", "permute_sym", "hinv_upper", "fp16_round", "group_grid",
     "gptq_sweep", "gptq_layer", "rtn_quantize", "dequantize_sweep",
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups",
@@ -161,6 +165,33 @@ def act_order_from_diag(hdiag):
 def act_order_perm(H):
     """act-order permutation of a full damped Hessian."""
     return act_order_from_diag(np.diag(H))
+
+
+def min_pivot_order(H):
+    """Min-pivot order ([BABAI] 2.3): the LDL factorisation of H taking, at
+    every step, the pivot with the smallest diagonal among the columns not yet
+    eliminated, i.e. the smallest diagonal of the current Schur complement
+    (ties: the higher index first). The pivots D_j of the no-clipping bound
+    are those of the LDL taken from the back of the sweep order, so the sweep
+    takes the columns in the reverse elimination order. Returns the sweep
+    permutation (as act_order_perm does) and the pivots in elimination order.
+    """
+    M = np.array(H, dtype=F64, copy=True)
+    n = M.shape[0]
+    alive = np.ones(n, dtype=bool)
+    elim = np.empty(n, dtype=np.int64)
+    piv = np.empty(n, dtype=F64)
+    for step in range(n):
+        d = np.where(alive, np.diag(M), np.inf)
+        m = d.min()
+        if not (m > 0.0) or not np.isfinite(m):
+            raise NotSPD("non-positive pivot in the min-pivot LDL")
+        p = int(np.nonzero(d == m)[0][-1])
+        elim[step], piv[step] = p, m
+        alive[p] = False
+        col = M[:, p].copy()
+        M -= np.outer(col, col) / m  # Schur complement on the columns still alive
+    return elim[::-1].copy(), piv
 
 
 def permute_sym(H, perm):
@@ -283,8 +314,9 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
 
 
 def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
-               act_order=False, clip=True, block=None):
-    """The whole layer: damping, optional act-order, U, sweep, un-permute.
+               act_order=False, clip=True, block=None, min_pivot=False):
+    """The whole layer: damping, optional act-order (or min-pivot order), U,
+    sweep, un-permute.
 
     Outputs follow the library's layout: codes [rows x cols] in the original
     column order, scales/zeros [rows x groups] with groups in sweep order,
@@ -298,7 +330,12 @@ def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
     if not np.all(np.isfinite(H)):
         raise NonFinite("Hessian is not finite")
     cols = H.shape[0]
-    perm = act_order_perm(H) if act_order else np.arange(cols, dtype=np.int64)
+    if min_pivot:
+        perm = min_pivot_order(H)[0]
+    elif act_order:
+        perm = act_order_perm(H)
+    else:
+        perm = np.arange(cols, dtype=np.int64)
     Hp = permute_sym(H, perm)
     U = hinv_upper(Hp)
     res = gptq_sweep(Wd[:, perm], U, bits, group_size, clip=clip, block=block)

@@ -122,6 +122,61 @@ def test_hinv_upper_properties_and_ldl():
     np.testing.assert_allclose(1.0 / np.diag(U) ** 2, D_rev, rtol=1e-10)
 
 
+def test_min_pivot_diagonal_hessian_is_act_order():
+    """[BABAI] 2.3: act-order (descending diagonal) approximates the min-pivot
+    order by ignoring the off-diagonal terms; on a diagonal H the Schur
+    complement never changes, so the two orders coincide, ties included."""
+    d = np.array([3.0, 1.0, 4.0, 1.0, 5.0, 9.0, 2.0, 6.0, 5.0, 3.0])
+    perm, piv = O.min_pivot_order(np.diag(d))
+    np.testing.assert_array_equal(perm, O.act_order_perm(np.diag(d)))
+    np.testing.assert_array_equal(piv, np.sort(d))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_min_pivot_greedy_schur_brute_force(seed):
+    """[BABAI] 2.3 "smallest diagonal entry at each LDL step": at every step
+    the chosen column has the smallest diagonal of the Schur complement of the
+    columns already eliminated, here computed from scratch by a linear solve
+    (H_ii - H_iS H_SS^-1 H_Si), not by the oracle's rank-1 updates; and the
+    pivots are the LDL diagonal of H taken in elimination order."""
+    rng = np.random.default_rng(100 + seed)
+    n = 7
+    A = rng.standard_normal((n, n)) + 0.5 * rng.standard_normal((n, 1))
+    H = A @ A.T + 0.05 * np.eye(n)
+    perm, piv = O.min_pivot_order(H)
+    elim = perm[::-1]
+    for step in range(n):
+        S = list(elim[:step])
+        rest = [i for i in range(n) if i not in S]
+        if S:
+            HSS = H[np.ix_(S, S)]
+            schur = {i: H[i, i] - H[i, S] @ np.linalg.solve(HSS, H[S, i]) for i in rest}
+        else:
+            schur = {i: H[i, i] for i in rest}
+        best = min(schur.values())
+        assert abs(schur[elim[step]] - best) <= 1e-12 * best
+        assert abs(piv[step] - schur[elim[step]]) <= 1e-10 * best
+    np.testing.assert_allclose(O.ldl_diag(H[np.ix_(elim, elim)]), piv, rtol=1e-10)
+    # and these are Satz 5's D for the sweep order (1/U_jj^2 of the permuted H)
+    U = O.hinv_upper(H[np.ix_(perm, perm)])
+    np.testing.assert_allclose(1.0 / np.diag(U) ** 2, piv[::-1], rtol=1e-9)
+
+
+def test_min_pivot_layer_bound_not_above_act_order_on_example():
+    """[BABAI] 2.3: the min-pivot order targets a smaller trace of D (the
+    bound's pivots) than act-order; on a random correlated Hessian the greedy
+    order's trace is below act-order's and the layer still satisfies Satz 5."""
+    X, W, S, n = _rand_problem(12, 48, 200, 9)
+    H = O.damped_hessian(S, n, 0.01)
+    tr_mp = O.min_pivot_order(H)[1].sum()
+    pa = O.act_order_perm(H)
+    tr_act = O.ldl_diag(H[np.ix_(pa[::-1], pa[::-1])]).sum()
+    assert tr_mp <= tr_act
+    res = O.gptq_layer(W, S, n, bits=2, group_size=16, damp=0.01, min_pivot=True, clip=False)
+    g = np.arange(48) // 16
+    assert np.all(res["row_loss"] <= O.noclip_bound(res["scales"][:, g], res["U"]) * (1 + 1e-12))
+
+
 def test_not_spd_detected():
     rng = np.random.default_rng(4)
     X = rng.standard_normal((5, 12)).astype(np.float32)  # rank 5 < 12
