@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--order", choices=("workload", "min_pivot"), default="workload",
+                    help="column order: the workload's (act-order or none), or the "
+                         "min-pivot order for every input")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
@@ -117,6 +120,14 @@ def kernel_work(name, wl, plan):
                             f += 2 * 128 ** 3 * ((hh - c) if name == "trtri_t" else (r + 1))
                 hh *= 2
         return f, "flop", "f64_mfma"
+    if name == "minpivot_update":
+        # after every full panel of the min-pivot search: A -= P P^T on all
+        # nt(nt+1)/2 lower tiles, 2 128^3 each
+        f = 0.0
+        for h in plan:
+            nt = -(-h.dim // 128)
+            f += 2 * 128 ** 3 * nt * (nt + 1) // 2 * ((h.dim - 1) // 128)
+        return f, "flop", "f64_mfma"
     if name == "quant_gemm":
         # the update GEMM flops that run in q_gemm launches (the rest run
         # inside the sweep launches, see quant_gemm_split)
@@ -191,7 +202,9 @@ KERNEL_CLASS = {  # device function name -> timing class
     "trtri_t_kernel": "trtri_t", "trtri_x_kernel": "trtri_x", "trtri_sum_kernel": "trtri_sum",
     "trtri_diag_kernel": "trtri_diag", "q_gemm_kernel": "quant_gemm",
     "q_sweep_kernel": "quant_sweep",
-    "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout"}
+    "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout",
+    "prep_uout_z_kernel": "prepare_uout", "mp_init_kernel": "minpivot_step",
+    "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update"}
 
 
 def source_hash():
@@ -371,6 +384,7 @@ def main():
         del X
         grp = LayerGroup(h.dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
                          bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
+                         min_pivot=args.order == "min_pivot",
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
         plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0]))
@@ -459,7 +473,7 @@ def main():
             v["frac"] = v["achieved"] / v["peak"]
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.order == "workload":
         sample_rows = args.cpu_sample_rows or 64
         cpu = cpu_baseline(wl, host_inputs, sample_rows)
 
@@ -480,7 +494,9 @@ def main():
                    "layers": [f"{l.name} {l.rows}x{wl.input(l.hessian).dim}" for l in wl.layers],
                    "n_tokens": wl.n_tokens, "token_chunk": wl.token_chunk,
                    "bits": list(wl.bits), "group_size": wl.group_size,
-                   "act_order": wl.act_order, "damp": wl.damp,
+                   "act_order": wl.act_order and args.order == "workload",
+                   "order": "min_pivot" if args.order == "min_pivot" else
+                   ("act_order" if wl.act_order else "none"), "damp": wl.damp,
                    "weights_per_step": weights,
                    "arithmetic": "fp64 Hessian/Cholesky/inverse and sweep, fp32 MFMA lazy update"},
         "roofline": roofline,

@@ -54,6 +54,8 @@ typedef enum {
 #define GPTQ_FLAG_NO_SYNC 4u            /* prepare / quantize: return after enqueueing; the
                                            device-side status stays in the workspace, read
                                            it with gptq_workspace_status */
+#define GPTQ_FLAG_MIN_PIVOT 8u          /* gptq_prepare_hinv: min-pivot order instead of
+                                           act-order (exclusive with GPTQ_FLAG_ACT_ORDER) */
 
 /* ---------------------------------------------------------------------------
  * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's
@@ -86,7 +88,11 @@ gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
  * act-order); The Geometry of LLM Quantization 2.3 (act-order pivoting).
  *   H  = (2/n_tokens_total) * S + damp * mean(diag((2/n) S)) * I
  *   perm (out, int32[i]) = stable order of descending diag H when
- *        flags & GPTQ_FLAG_ACT_ORDER, else the identity;
+ *        flags & GPTQ_FLAG_ACT_ORDER; with GPTQ_FLAG_MIN_PIVOT the min-pivot
+ *        order of The Geometry of LLM Quantization 2.3: the LDL of H that
+ *        takes the smallest diagonal of the current Schur complement as the
+ *        next pivot (ties: the higher index), visited in the reverse of that
+ *        elimination order; else the identity;
  *        perm[k] = original column visited k-th.
  *   U  (out, fp32 [i x i], row-major, ld = in_features) = the upper triangular
  *        factor with U^T U = (H[perm][:,perm])^-1, zeros below the diagonal.

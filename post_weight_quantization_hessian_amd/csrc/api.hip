@@ -11,7 +11,8 @@ static const char* const kKernelNames[K_COUNT] = {
     "hessian_tile", "hessian_reduce", "prepare_diag", "prepare_perm", "prepare_gather",
     "chol_potrf", "chol_trsm", "chol_syrk", "trtri_t", "trtri_x", "prepare_uout",
     "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill",
-    "trtri_diag", "chol_potrf_syrk", "trtri_sum", "chol_col"};
+    "trtri_diag", "chol_potrf_syrk", "trtri_sum", "chol_col", "minpivot_step",
+    "minpivot_update"};
 
 struct ProfRec {
   int kid;

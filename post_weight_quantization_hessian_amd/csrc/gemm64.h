@@ -37,7 +37,9 @@ __device__ inline void mfma64_chunk(const double* __restrict__ As, const double*
 }
 
 // Global [k][col] (row stride ld) -> LDS [k][col]. All in bounds, 16B aligned.
-struct LdDirect64 {
+// NEG stores the negated values.
+template <bool NEG>
+struct LdDirect64T {
   const double* base;
   int64_t ld;
   dbl2 r[4];
@@ -49,9 +51,10 @@ struct LdDirect64 {
   __device__ void store(double* s, int t) const {
     double* d = s + (t >> 4) * GLD + (t & 15) * 8;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<dbl2*>(d + 2 * q) = r[q];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<dbl2*>(d + 2 * q) = NEG ? -r[q] : r[q];
   }
 };
+using LdDirect64 = LdDirect64T<false>;
 
 // Global [col][k] (row stride ld) -> LDS [k][col] (transposing). In bounds.
 // NEG stores the negated values (a negated operand keeps the epilogue a plain

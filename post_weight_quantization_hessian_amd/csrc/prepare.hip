@@ -79,10 +79,11 @@ __global__ __launch_bounds__(256) void prep_gather_kernel(const double* __restri
     for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) row[b] = (a == b) ? 1.0 : 0.0;
     return;
   }
-  const int64_t pa = perm[n - 1 - a];
+  // without perm: H itself in the original order (the min-pivot search)
+  const int64_t pa = perm ? perm[n - 1 - a] : a;
   const double* srow = S + pa * n;
   for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) {
-    const int64_t pb = perm[n - 1 - b];
+    const int64_t pb = perm ? perm[n - 1 - b] : b;
     double v = c * srow[pb];
     if (a == b) v += lam;
     row[b] = v;
@@ -881,6 +882,190 @@ __global__ __launch_bounds__(256) void prep_uout_z_kernel(const double* __restri
 
 __global__ void zero_u32_kernel(unsigned* p) { *p = 0u; }
 
+// ---------------------------------------------------------------- min-pivot
+//
+// The min-pivot order (The Geometry of LLM Quantization 2.3): the LDL of H
+// taking, at every step, the smallest diagonal of the current Schur
+// complement as the next pivot, ties to the higher index; the sweep visits
+// the columns in the reverse elimination order (perm[n-1-j] = j-th pivot).
+// Computed like a blocked pivoted Cholesky, on A = H in the original order
+// (lower triangle, in the factorization's K buffer): one launch per pivot,
+// panels of 128 pivots, and after every full panel one launch of tile
+// updates A -= P P^T over the whole lower triangle (rows of columns already
+// eliminated hold zeros in P, so only live entries change). The order found
+// is then factored again by the ordinary path; this search only decides it.
+//
+// Per pivot j (panel column k = j % 128), with d the Schur diagonal of the
+// live columns (+inf once eliminated) and Pt = P^T [128 x ip]:
+//   p = argmin d (from the previous launch's per-workgroup minima);
+//   Pt[k][p] = sqrt(d_p);  for live i != p:
+//   Pt[k][i] = (A[i][p] - sum_{k'<k} Pt[k'][i] Pt[k'][p]) / sqrt(d_p),
+//   d_i -= Pt[k][i]^2;   eliminated i: Pt[k][i] = 0.
+// Every workgroup reduces the previous minima itself (the same result in all
+// of them, in a fixed order) and leaves the minimum of its own updated
+// entries for the next launch.
+
+struct MinIdx {
+  double v;
+  int i;
+};
+
+// (v, i) before (w, j): smaller value; equal values: the higher index
+__device__ inline bool mp_before(double v, int i, double w, int j) {
+  return v < w || (v == w && i > j);
+}
+
+// Minimum over the wave of (v, i), in every lane (butterfly of lane swaps).
+__device__ inline MinIdx mp_wave_min(double v, int i) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double w = __shfl_xor(v, off);
+    const int j = __shfl_xor(i, off);
+    if (mp_before(w, j, v, i)) {
+      v = w;
+      i = j;
+    }
+  }
+  return MinIdx{v, i};
+}
+
+// Minimum over the block of (v, i) (256 threads); result in every thread.
+__device__ inline MinIdx mp_block_min(double v, int i, double* sv, int* si) {
+  const MinIdx m = mp_wave_min(v, i);
+  const int t = threadIdx.x;
+  if ((t & 63) == 0) {
+    sv[t >> 6] = m.v;
+    si[t >> 6] = m.i;
+  }
+  __syncthreads();
+  MinIdx r{sv[0], si[0]};
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+    if (mp_before(sv[w], si[w], r.v, r.i)) r = MinIdx{sv[w], si[w]};
+  return r;
+}
+
+// d = diag A for the live columns, +inf for the pad; Pt = 0; minima (the
+// second set "none", which a step that found no valid pivot leaves for the
+// next); perm = identity, so that it holds valid indices whatever happens.
+__global__ __launch_bounds__(256) void mp_init_kernel(const double* __restrict__ A, int64_t ld,
+                                                      int64_t n, int64_t ip,
+                                                      double* __restrict__ d,
+                                                      double* __restrict__ Pt,
+                                                      double* __restrict__ mv,
+                                                      int* __restrict__ mi,
+                                                      int32_t* __restrict__ perm) {
+  __shared__ double sv[4];
+  __shared__ int si[4];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double v = INFINITY;
+  if (i < ip) {
+    v = i < n ? A[i * ld + i] : INFINITY;
+    d[i] = v;
+    for (int k = 0; k < GT; ++k) Pt[(int64_t)k * ip + i] = 0.0;
+  }
+  if (i < n) perm[i] = (int32_t)i;
+  const MinIdx m = mp_block_min(v, (int)i, sv, si);
+  if (threadIdx.x == 0) {
+    mv[blockIdx.x] = m.v;
+    mi[blockIdx.x] = m.i;
+    mv[gridDim.x + blockIdx.x] = INFINITY;
+    mi[gridDim.x + blockIdx.x] = -1;
+  }
+}
+
+// Pivot j (column k of its panel). mv_in/mi_in: the previous minima (nwg of
+// them), mv_out/mi_out: this launch's.
+__global__ __launch_bounds__(256) void mp_step_kernel(const double* __restrict__ A, int64_t ld,
+                                                      int64_t n, int64_t ip,
+                                                      double* __restrict__ d,
+                                                      double* __restrict__ Pt, int j, int k,
+                                                      const double* __restrict__ mv_in,
+                                                      const int* __restrict__ mi_in,
+                                                      double* __restrict__ mv_out,
+                                                      int* __restrict__ mi_out,
+                                                      int32_t* __restrict__ perm,
+                                                      unsigned* __restrict__ status) {
+  __shared__ double sv[4];
+  __shared__ int si[4];
+  // every wave reduces the previous minima itself (no barrier needed)
+  const int nwg = gridDim.x, lane = threadIdx.x & 63;
+  double bv = INFINITY;
+  int bi = -1;
+  for (int w = lane; w < nwg; w += 64)
+    if (mp_before(mv_in[w], mi_in[w], bv, bi)) {
+      bv = mv_in[w];
+      bi = mi_in[w];
+    }
+  const MinIdx m = mp_wave_min(bv, bi);
+  const double dp = m.v;
+  const int p = __builtin_amdgcn_readfirstlane(m.i);
+  if (!(dp > 0.0) || !isfinite(dp) || p < 0 || p >= n) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, ST_NOTSPD);
+    return;  // U is garbage after a failed factorization anyway
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) perm[n - 1 - j] = p;
+  // the pivot's panel row, once per workgroup
+  __shared__ double prow[GT];
+  if ((int)threadIdx.x < k) prow[threadIdx.x] = Pt[(int64_t)threadIdx.x * ip + p];
+  __syncthreads();
+  const double rs = 1.0 / sqrt(dp);
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  double v = INFINITY;
+  if (i < n) {
+    const double di = d[i];
+    if (i == p) {
+      Pt[(int64_t)k * ip + i] = dp * rs;
+      d[i] = INFINITY;
+    } else if (di == INFINITY) {
+      Pt[(int64_t)k * ip + i] = 0.0;
+    } else {
+      double c = i > p ? A[i * ld + p] : A[(int64_t)p * ld + i];
+      // the panel's earlier columns at row i, 16 loads in flight at a time
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      const double* pc = Pt + i;
+      int kk = 0;
+      for (; kk + 16 <= k; kk += 16) {
+        double x[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) x[u] = pc[(int64_t)(kk + u) * ip];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u & 3] = fma(x[u], prow[kk + u], acc[u & 3]);
+      }
+      for (; kk < k; ++kk) acc[kk & 3] = fma(pc[(int64_t)kk * ip], prow[kk], acc[kk & 3]);
+      c -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      const double l = c * rs;
+      Pt[(int64_t)k * ip + i] = l;
+      v = di - l * l;
+      d[i] = v;
+    }
+  }
+  const MinIdx mo = mp_block_min(v, (int)i, sv, si);
+  if (threadIdx.x == 0) {
+    mv_out[blockIdx.x] = mo.v;
+    mi_out[blockIdx.x] = mo.i;
+  }
+}
+
+// After a full panel: A -= P P^T on every lower tile (a, b) of the ip grid.
+__global__ __launch_bounds__(256) void mp_update_kernel(double* __restrict__ A, int64_t ld,
+                                                        int64_t ip,
+                                                        const double* __restrict__ Pt) {
+  __shared__ double smem[4 * GCH];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  int a = (int)((sqrt(8.0 * id + 1.0) - 1.0) * 0.5);
+  while (a * (a + 1) / 2 > id) --a;
+  while ((a + 1) * (a + 2) / 2 <= id) ++a;
+  const int b = id - a * (a + 1) / 2;
+  LdDirect64T<true> la{Pt + (int64_t)a * GT, ip, {}};  // -P rows of tile a, k-major
+  LdDirect64 lb{Pt + (int64_t)b * GT, ip, {}};
+  double* C = A + (int64_t)a * GT * ld + (int64_t)b * GT;
+  d4 acc[4][4];
+  acc_load_lds(acc, C, ld, GT, GT, smem);
+  gemm64_loop(la, lb, GT / GK, smem, smem + 2 * GCH, acc);
+  for_each_acc(acc, [&](int r, int c, double v) { C[r * ld + c] = v; });
+}
+
 // ---------------------------------------------------------------- layout
 
 // Up to this many 128-column panels the inverse of L is accumulated by block
@@ -894,7 +1079,9 @@ constexpr int CHOL_FUSE_NT = 48;
 
 struct PrepLayout {
   int64_t n, ip, nt;
-  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, off_D, off_P, total;
+  size_t off_status, off_lam, off_hd, off_K, off_X, off_T, off_D, off_P;
+  size_t off_md, off_mpt, off_mv, off_mi;  // min-pivot search
+  size_t total;
 };
 
 static PrepLayout prep_layout(int64_t n) {
@@ -917,6 +1104,11 @@ static PrepLayout prep_layout(int64_t n) {
   L.off_T = take(L.nt > 1 && !fused ? 8 * (size_t)L.ip * L.ip : 8);
   L.off_D = take(8 * (size_t)L.nt * 8 * 256);
   L.off_P = take(fused ? 8 : std::max<size_t>(trtri_part_bytes((int)L.nt), 8));
+  const int64_t nwg = cdiv(L.ip, 256);
+  L.off_md = take(8 * (size_t)L.ip);
+  L.off_mpt = take(8 * (size_t)GT * L.ip);
+  L.off_mv = take(8 * 2 * (size_t)nwg);
+  L.off_mi = take(4 * 2 * (size_t)nwg);
   L.total = o;
   return L;
 }
@@ -937,7 +1129,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   if (in_features == 0) return GPTQ_OK;
   if (!S || !perm || !U || n_tokens_total <= 0 || !(damp >= 0.0) || !std::isfinite(damp))
     return GPTQ_EINVAL;
-  if (flags & ~(GPTQ_FLAG_ACT_ORDER | GPTQ_FLAG_NO_SYNC)) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_ACT_ORDER | GPTQ_FLAG_MIN_PIVOT | GPTQ_FLAG_NO_SYNC)) return GPTQ_EINVAL;
+  if ((flags & GPTQ_FLAG_ACT_ORDER) && (flags & GPTQ_FLAG_MIN_PIVOT)) return GPTQ_EINVAL;
   if (in_features > (int64_t)1 << 20) return GPTQ_EINVAL;
   const PrepLayout L = prep_layout(in_features);
   if (!ws || ws_bytes < L.total) return GPTQ_EWORKSPACE;
@@ -957,9 +1150,34 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
 
   GPTQ_LAUNCH(K_FILL, st, zero_u32_kernel<<<1, 1, 0, st>>>(status));
   GPTQ_LAUNCH(K_PREP_DIAG, st, prep_diag_kernel<<<1, 1024, 0, st>>>(S, n, c, damp, hd, lam));
-  GPTQ_LAUNCH(K_PREP_PERM, st,
-              prep_perm_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
-                  hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
+  if (flags & GPTQ_FLAG_MIN_PIVOT) {
+    // the order from a pivoted factorization of H in the original order
+    double* md = (double*)(base + L.off_md);
+    double* Pt = (double*)(base + L.off_mpt);
+    double* mv = (double*)(base + L.off_mv);
+    int* mi = (int*)(base + L.off_mi);
+    const int nwg = (int)cdiv(ip, 256);
+    GPTQ_LAUNCH(K_PREP_GATHER, st,
+                prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, nullptr, K));
+    GPTQ_LAUNCH(K_MP_STEP, st,
+                mp_init_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, mv, mi, perm));
+    for (int64_t j = 0; j < n; ++j) {
+      const int k = (int)(j % GT), par = (int)(j & 1);
+      GPTQ_LAUNCH(K_MP_STEP, st,
+                  mp_step_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, (int)j, k,
+                                                      mv + par * nwg, mi + par * nwg,
+                                                      mv + (1 - par) * nwg, mi + (1 - par) * nwg,
+                                                      perm, status));
+      if (k == GT - 1 && j + 1 < n) {
+        const int tiles = (int)(L.nt * (L.nt + 1) / 2);
+        GPTQ_LAUNCH(K_MP_UPDATE, st, mp_update_kernel<<<tiles, 256, 0, st>>>(K, ip, ip, Pt));
+      }
+    }
+  } else {
+    GPTQ_LAUNCH(K_PREP_PERM, st,
+                prep_perm_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
+                    hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
+  }
   GPTQ_LAUNCH(K_PREP_GATHER, st,
               prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, perm, K));
   // Blocked Cholesky, one stream. Per panel p: solve the panel's column

@@ -23,6 +23,7 @@ GPTQ_OK, GPTQ_EINVAL, GPTQ_ENOTSPD, GPTQ_EHIP, GPTQ_EWORKSPACE, GPTQ_ENONFINITE 
 GPTQ_FLAG_ACT_ORDER = 1
 GPTQ_FLAG_HESSIAN_OVERWRITE = 2
 GPTQ_FLAG_NO_SYNC = 4
+GPTQ_FLAG_MIN_PIVOT = 8
 
 EXPORTS = {
     "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
@@ -142,8 +143,9 @@ def prepare_workspace_bytes(in_features: int) -> int:
 
 
 def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
-                 workspace=None, out=None, sync: bool = True):
-    """Damped, optionally act-ordered Hessian -> (perm int32 [i], U fp32 [i x i]).
+                 workspace=None, out=None, sync: bool = True, min_pivot: bool = False):
+    """Damped, optionally act-ordered (or min-pivot-ordered) Hessian ->
+    (perm int32 [i], U fp32 [i x i]).
     ``sync=False`` returns after enqueueing; check with workspace_status()."""
     torch = _torch()
     _need(S, torch.float64, "S", 2)
@@ -157,7 +159,8 @@ def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
         perm, U = out
     if workspace is None:
         workspace = _workspace(prepare_workspace_bytes(i), S.device)
-    flags = (GPTQ_FLAG_ACT_ORDER if act_order else 0) | (0 if sync else GPTQ_FLAG_NO_SYNC)
+    flags = ((GPTQ_FLAG_ACT_ORDER if act_order else 0) | (GPTQ_FLAG_MIN_PIVOT if min_pivot else 0)
+             | (0 if sync else GPTQ_FLAG_NO_SYNC))
     st = lib.gptq_prepare_hinv(_ptr(S), i, int(n_tokens), float(damp), flags, _ptr(perm), _ptr(U),
                                _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_prepare_hinv")

@@ -19,11 +19,14 @@ from . import gptq as G
 
 class LayerGroup:
     def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
-                 device):
+                 device, min_pivot=False):
         import torch
         self.dim, self.rows = int(dim), int(rows)
         self.bits, self.group_size = tuple(bits), int(group_size)
         self.act_order, self.damp = bool(act_order), float(damp)
+        self.min_pivot = bool(min_pivot)  # the min-pivot order instead of act-order
+        if self.min_pivot:
+            self.act_order = False
         ng = -(-self.dim // self.group_size)
         self.S = torch.empty((self.dim, self.dim), dtype=torch.float64, device=device)
         self.hws = torch.empty(max(G.hessian_workspace_bytes(self.dim, max_chunk_tokens), 1),
@@ -52,9 +55,11 @@ class LayerGroup:
             G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0))
             n += int(c.shape[0])
         G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
-                       workspace=self.pws, out=(self.perm, self.U), sync=False)
+                       workspace=self.pws, out=(self.perm, self.U), sync=False,
+                       min_pivot=self.min_pivot)
         for bi, b in enumerate(self.bits):
-            G.quantize_layer(W, self.U, self.perm if self.act_order else None, bits=b,
+            G.quantize_layer(W, self.U, self.perm if (self.act_order or self.min_pivot) else None,
+                             bits=b,
                              group_size=self.group_size, workspace=self.qws[bi],
                              out=self.outs[bi], sync=False)
         return self.outs

@@ -95,7 +95,9 @@ def test_invalid_arguments_rejected_on_host():
     assert pw(FAKE, 8, 0, 0.01, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, -0.1, 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, float("nan"), 0, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
-    assert pw(FAKE, 8, 10, 0.01, 8, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, 0.01, 16, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    # act-order and min-pivot are exclusive
+    assert pw(FAKE, 8, 10, 0.01, 9, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, 0.01, 2, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, 0.01, 0, FAKE, FAKE, FAKE, 64, NULL) == g.GPTQ_EWORKSPACE
     assert pw(FAKE, 0, 10, 0.01, 0, NULL, NULL, NULL, 0, NULL) == g.GPTQ_OK

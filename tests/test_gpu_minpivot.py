@@ -1,0 +1,117 @@
+"""GPU parity of the min-pivot order (The Geometry of LLM Quantization 2.3,
+the smallest Schur diagonal as the next LDL pivot, the sweep in the reverse
+elimination order), through the C ABI.
+
+The order is an argmin per step, decided in fp64 on both sides but from sums
+taken in different orders, so it is checked as what must hold: every GPU
+pivot is a smallest live Schur diagonal of the oracle's exact-order recursion
+(within 1e-10 relative), and the GPU order equals the oracle's unless a step
+has a near tie. U and the layer outputs are then compared as for act-order.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.parity_util import compare_layer, to_numpy_layer
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a HIP device", allow_module_level=True)
+
+import post_weight_quantization_hessian_amd.gptq as G  # noqa: E402
+
+DEV = torch.device("cuda:0")
+REL = 1e-10
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def check_greedy(H, perm):
+    """Every pivot of the order a smallest live Schur diagonal (within REL);
+    returns whether some step had a near tie (then another order is valid)."""
+    n = H.shape[0]
+    assert np.array_equal(np.sort(perm), np.arange(n))
+    M = np.array(H, dtype=np.float64, copy=True)
+    alive = np.ones(n, dtype=bool)
+    near_tie = False
+    for p in perm[::-1]:
+        d = np.where(alive, np.diag(M), np.inf)
+        m = d.min()
+        assert alive[p] and M[p, p] <= m * (1 + REL), (p, M[p, p], m)
+        second = np.partition(d, 1)[1] if alive.sum() > 1 else np.inf
+        near_tie |= second <= m * (1 + REL)
+        col = M[:, p].copy()
+        M -= np.outer(col, col) / col[p]
+        alive[p] = False
+    return near_tie
+
+
+def hessian(dim, seed, lognormal=True):
+    rng = np.random.default_rng(seed)
+    scale = rng.lognormal(0, 1, dim) if lognormal else 1.0
+    X = ((rng.standard_normal((2 * dim + 50, dim)) + 0.6 * rng.standard_normal((2 * dim + 50, 1)))
+         * scale).astype(np.float32)
+    return O.hessian_sum(X), X
+
+
+@pytest.mark.parametrize("dim", [1, 7, 130, 257, 576, 700])
+def test_minpivot_order_and_factor(dim):
+    say(f"min-pivot prepare dim={dim}")
+    (Sr, n), _ = hessian(dim, 500 + dim)
+    S = torch.from_numpy(Sr).to(DEV)
+    perm, U = G.prepare_hinv(S, n, damp=0.01, min_pivot=True)
+    pg = perm.cpu().numpy().astype(np.int64)
+    H = O.damped_hessian(Sr, n, 0.01)
+    near_tie = check_greedy(H, pg)
+    pr, _ = O.min_pivot_order(H)
+    if not near_tie:
+        assert np.array_equal(pg, pr)
+    Ur = O.hinv_upper(O.permute_sym(H, pg))
+    Ug = U.cpu().numpy().astype(np.float64)
+    assert np.all(np.tril(Ug, -1) == 0)
+    err = np.max(np.abs(Ug - Ur)) / np.max(np.abs(Ur))
+    assert err < 2e-6, err
+
+
+def test_minpivot_diagonal_hessian_equals_act_order():
+    """On a diagonal H the min-pivot order is act-order, ties included."""
+    say("min-pivot diagonal H")
+    d = np.repeat(np.array([3.0, 1.0, 4.0, 1.5, 5.0, 9.0, 2.0, 6.0]), 40)  # ties
+    S = torch.from_numpy(np.diag(d)).to(DEV)
+    p_mp, _ = G.prepare_hinv(S, 2, damp=0.0, min_pivot=True)
+    p_act, _ = G.prepare_hinv(S, 2, damp=0.0, act_order=True)
+    assert torch.equal(p_mp, p_act)
+
+
+@pytest.mark.parametrize("rows,cols,bits,gs", [(40, 300, 4, 64), (96, 576, 3, 128)])
+def test_minpivot_layer_end_to_end(rows, cols, bits, gs):
+    say(f"min-pivot layer {rows}x{cols}")
+    (Sr, n), X = hessian(cols, 900 + cols, lognormal=False)
+    rng = np.random.default_rng(cols)
+    W = (0.02 * rng.standard_t(4, size=(rows, cols))).astype(np.float16)
+    S = torch.from_numpy(Sr).to(DEV)
+    perm, U = G.prepare_hinv(S, n, damp=0.01, min_pivot=True)
+    q = G.quantize_layer(torch.from_numpy(W).to(DEV), U, perm, bits=bits, group_size=gs)
+    torch.cuda.synchronize()
+    ref = O.gptq_layer(W, Sr, n, bits=bits, group_size=gs, damp=0.01, min_pivot=True)
+    assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    compare_layer(to_numpy_layer(q), ref, name=f"minpivot{rows}x{cols}")
+
+
+def test_minpivot_flag_errors():
+    say("min-pivot flags and non-SPD")
+    S = torch.eye(64, dtype=torch.float64, device=DEV)
+    with pytest.raises(G.GPTQError) as ei:
+        G.prepare_hinv(S, 10, act_order=True, min_pivot=True)
+    assert ei.value.status == G.GPTQ_EINVAL
+    Z = torch.zeros((200, 200), dtype=torch.float64, device=DEV)
+    with pytest.raises(G.GPTQError) as ei:
+        G.prepare_hinv(Z, 10, damp=0.0, min_pivot=True)
+    assert ei.value.status == G.GPTQ_ENOTSPD
