@@ -115,3 +115,49 @@ def test_minpivot_flag_errors():
     with pytest.raises(G.GPTQError) as ei:
         G.prepare_hinv(Z, 10, damp=0.0, min_pivot=True)
     assert ei.value.status == G.GPTQ_ENOTSPD
+
+
+def test_minpivot_qwen_down_shape_sampled():
+    """The 4864-feature down-projection input of the Qwen-shape workload
+    (2048 SiLU-gated tokens): the oracle's cubic greedy is out of reach, so
+    the first 48 pivots are checked against Schur diagonals computed from
+    scratch (a solve with the eliminated block), and U against H_p on
+    sampled rows (U H_p = U^-T is lower triangular with diagonal 1/U_jj)."""
+    from post_weight_quantization_hessian_amd import synth
+    from post_weight_quantization_hessian_amd.workloads import WORKLOADS
+    wl = WORKLOADS["qwen05b_mlp"]
+    h = wl.input("down_in")
+    say("min-pivot 4864-feature Hessian")
+    X = synth.activations(wl.wid, h.name, wl.n_tokens, h.dim, kind=h.kind)
+    Xd = torch.from_numpy(X).to(DEV)
+    S = torch.zeros((h.dim, h.dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, Xd, overwrite=True)
+    perm, U = G.prepare_hinv(S, wl.n_tokens, damp=wl.damp, min_pivot=True)
+    pg = perm.cpu().numpy().astype(np.int64)
+    assert np.array_equal(np.sort(pg), np.arange(h.dim))
+    H = O.damped_hessian(S.cpu().numpy(), wl.n_tokens, wl.damp)
+    elim = pg[::-1]
+    for s in range(48):
+        E = elim[:s]
+        alive = np.ones(h.dim, dtype=bool)
+        alive[E] = False
+        if s:
+            Y = np.linalg.solve(H[np.ix_(E, E)], H[E, :])
+            schur = np.diag(H) - np.einsum("ij,ij->j", H[E, :], Y)
+        else:
+            schur = np.diag(H).copy()
+        m = schur[alive].min()
+        assert schur[elim[s]] <= m * (1 + REL), (s, schur[elim[s]], m)
+    Hp = torch.from_numpy(O.permute_sym(H, pg)).to(DEV)
+    rng = np.random.default_rng(7)
+    J = sorted(set([0, 1, h.dim // 2, h.dim - 2, h.dim - 1] + rng.integers(0, h.dim, 6).tolist()))
+    Ur = U[J].double()
+    Y = Ur @ Hp
+    A = Ur.abs() @ Hp.abs()
+    cols = torch.arange(h.dim, device=DEV)
+    jt = torch.tensor(J, device=DEV)
+    upper = cols[None, :] > jt[:, None]
+    assert float((Y.abs() / A)[upper].max()) <= 4e-7
+    ud = Ur[torch.arange(len(J), device=DEV), jt]
+    yd = Y[torch.arange(len(J), device=DEV), jt]
+    assert float(((yd - 1.0 / ud).abs() / A[torch.arange(len(J), device=DEV), jt]).max()) <= 4e-7
