@@ -56,6 +56,9 @@ typedef enum {
                                            it with gptq_workspace_status */
 #define GPTQ_FLAG_MIN_PIVOT 8u          /* gptq_prepare_hinv: min-pivot order instead of
                                            act-order (exclusive with GPTQ_FLAG_ACT_ORDER) */
+#define GPTQ_FLAG_NO_CLIP 16u           /* gptq_quantize_layer: levels not clamped to the grid
+                                           (the no-clipping regime of Satz 5); stored codes
+                                           saturate to [0, 255] */
 
 /* ---------------------------------------------------------------------------
  * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's
@@ -136,7 +139,11 @@ gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_to
  *            (w-q) H (w-q)^T for the damped, permuted H.
  * Workspace: gptq_quantize_workspace_bytes(rows, cols, group_size) bytes.
  * perm must be a permutation of 0..cols-1 (checked on the device: GPTQ_EINVAL).
- * flags: 0 or GPTQ_FLAG_NO_SYNC. Synchronizes `stream` at the end unless
+ * flags: 0, GPTQ_FLAG_NO_SYNC, GPTQ_FLAG_NO_CLIP (The Geometry of LLM
+ * Quantization 2.3, the no-clipping regime of Satz 5: code = rint(v/scale) +
+ * zero without the clamp; the errors, the propagation and row_loss use that
+ * unclamped code, the stored byte is it saturated to [0, 255]). Synchronizes
+ * `stream` at the end unless
  * GPTQ_FLAG_NO_SYNC; returns GPTQ_ENONFINITE if a weight is NaN/Inf or a
  * scale overflows fp16 (outputs are then unspecified).
  * rows == 0 or cols == 0 is a no-op.

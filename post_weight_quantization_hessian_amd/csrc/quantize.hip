@@ -257,7 +257,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     const float* __restrict__ U, int64_t ldu, bool vecU, int64_t rows, int64_t j0, int bw,
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
-    double* __restrict__ row_loss, unsigned* __restrict__ status, bool late, int nsweep,
+    double* __restrict__ row_loss, unsigned* __restrict__ status, bool clip, bool late, int nsweep,
     int64_t gj0, int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart) {
   // U slab plus three rows of zero padding: the slot reads of a column run up
   // to 112 entries past its row end, into the next row or the padding, only
@@ -426,6 +426,10 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   __syncthreads();
 
   double scale = 1.0, rscale = 1.0, zero = 0.0, loss = 0.0;
+  // range of the level k = code - zero: [-zero, maxq - zero], or unbounded
+  // without clipping (the no-clipping regime of The Geometry of LLM
+  // Quantization 2.3, whose codes are stored saturated to [0, 255])
+  double klo = -1e300, khi = 1e300;
   const int nt16 = (bw + 15) >> 4;
   // U row of column jc as seen from the slots (slot s holds column
   // 16*((jc >> 4) + s) + q; slots past the block end are dead and read into
@@ -470,6 +474,8 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
       }
       rscale = 1.0 / scale;
+      klo = clip ? -zero : -1e300;
+      khi = clip ? maxq - zero : 1e300;
       if (rv && q == 0) {
         const int64_t g = (j0 + 16 * tt) / GS;
         scales[r * ldg + g] = sh;
@@ -495,7 +501,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
         // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
         const double v = w[0];
-        const double k = fmin(fmax(rint(v * rscale), -zero), maxq - zero);
+        const double k = fmin(fmax(rint(v * rscale), klo), khi);
         const double d = fma(-scale, k, v);
         double db;
         switch (jj) {
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       const int c = 16 * tt + q;
       if (rv && c < bw) {
         const double e = d_own * rdiag[c];
-        codes[r * ldc + j0 + c] = (uint8_t)(k_own + zero);
+        codes[r * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero, 0.0), 255.0);
         E[r * lde + j0 + c] = (float)e;
         loss += e * e;
       }
@@ -613,7 +619,7 @@ struct SweepArgs {
   int64_t ldg;
   double* row_loss;
   unsigned* status;
-  bool late;
+  bool clip, late;
   int64_t gj0;
   int gbw;
   int64_t gks, gk_end;
@@ -626,7 +632,7 @@ static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
               q_sweep_kernel<GS><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(
                   a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0,
                   a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg, a.row_loss,
-                  a.status, a.late, a.nsweep, a.gj0, a.gbw, a.gks, a.gk_end, a.gpart));
+                  a.status, a.clip, a.late, a.nsweep, a.gj0, a.gbw, a.gks, a.gk_end, a.gpart));
   return GPTQ_OK;
 }
 
@@ -648,7 +654,8 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
                                            double* row_loss, void* ws, size_t ws_bytes,
                                            void* stream) {
   if (rows < 0 || cols < 0) return GPTQ_EINVAL;
-  if (flags & ~GPTQ_FLAG_NO_SYNC) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_NO_SYNC | GPTQ_FLAG_NO_CLIP)) return GPTQ_EINVAL;
+  const bool clip = !(flags & GPTQ_FLAG_NO_CLIP);
   if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
   if (rows == 0 || cols == 0) return GPTQ_OK;
   if (!W || !U || !codes || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
@@ -729,8 +736,8 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
       }
     }
     SweepArgs a{nw, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
-                bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, late,
-                0, 0, 0, 0, pn};
+                bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, clip,
+                late, 0, 0, 0, 0, pn};
     ep = emb_max > 0 ? 0 : -1;
     if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
       // next block's sum over l < j0 (the errors of blocks < b), in as few

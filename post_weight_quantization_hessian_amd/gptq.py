@@ -24,6 +24,7 @@ GPTQ_FLAG_ACT_ORDER = 1
 GPTQ_FLAG_HESSIAN_OVERWRITE = 2
 GPTQ_FLAG_NO_SYNC = 4
 GPTQ_FLAG_MIN_PIVOT = 8
+GPTQ_FLAG_NO_CLIP = 16
 
 EXPORTS = {
     "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
@@ -185,10 +186,11 @@ def quantize_workspace_bytes(rows: int, cols: int, group_size: int) -> int:
 
 
 def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, workspace=None,
-                   out=None, sync: bool = True):
+                   out=None, sync: bool = True, clip: bool = True):
     """Sweep the fp16 weights W [rows x cols] with the factor U (and perm).
     ``out`` may be a QuantizedLayer whose tensors are reused; ``sync=False``
-    returns after enqueueing (check with workspace_status())."""
+    returns after enqueueing (check with workspace_status()); ``clip=False``
+    is the no-clipping regime (stored codes saturate to [0, 255])."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(U, torch.float32, "U", 2)
@@ -217,7 +219,8 @@ def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, worksp
         workspace = _workspace(quantize_workspace_bytes(rows, cols, group_size), dev)
     st = lib.gptq_quantize_layer(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
                                  _ptr(perm), int(bits), int(group_size),
-                                 0 if sync else GPTQ_FLAG_NO_SYNC, _ptr(codes),
+                                 (0 if sync else GPTQ_FLAG_NO_SYNC)
+                                 | (0 if clip else GPTQ_FLAG_NO_CLIP), _ptr(codes),
                                  _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(row_loss),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_quantize_layer")
