@@ -129,6 +129,38 @@ __device__ inline double dpp_f64(double v) {
 // row_newbcast: lane N of each 16-lane row, to the whole row
 template <int N>
 __device__ inline double row_bcast(double v) { return dpp_f64<0x150 + N>(v); }
+// row_newbcast whose result also depends on `dep` (it is the "old" operand,
+// which a full-mask broadcast never uses): keeps the compiler from hoisting
+// the broadcast above the computation of dep
+template <int N>
+__device__ inline double row_bcast_dep(double v, double dep) {
+  union { double d; int i[2]; } a, b, o;
+  a.d = v;
+  o.d = dep;
+  b.i[0] = __builtin_amdgcn_update_dpp(o.i[0], a.i[0], 0x150 + N, 0xF, 0xF, false);
+  b.i[1] = __builtin_amdgcn_update_dpp(o.i[1], a.i[1], 0x150 + N, 0xF, 0xF, false);
+  return b.d;
+}
+__device__ inline double row_bcast_dep_i(double v, double dep, int n) {
+  switch (n) {
+    case 0: return row_bcast_dep<0>(v, dep);
+    case 1: return row_bcast_dep<1>(v, dep);
+    case 2: return row_bcast_dep<2>(v, dep);
+    case 3: return row_bcast_dep<3>(v, dep);
+    case 4: return row_bcast_dep<4>(v, dep);
+    case 5: return row_bcast_dep<5>(v, dep);
+    case 6: return row_bcast_dep<6>(v, dep);
+    case 7: return row_bcast_dep<7>(v, dep);
+    case 8: return row_bcast_dep<8>(v, dep);
+    case 9: return row_bcast_dep<9>(v, dep);
+    case 10: return row_bcast_dep<10>(v, dep);
+    case 11: return row_bcast_dep<11>(v, dep);
+    case 12: return row_bcast_dep<12>(v, dep);
+    case 13: return row_bcast_dep<13>(v, dep);
+    case 14: return row_bcast_dep<14>(v, dep);
+    default: return row_bcast_dep<15>(v, dep);
+  }
+}
 // the same for an index that is a constant after loop unrolling
 __device__ inline double row_bcast_i(double v, int n) {
   switch (n) {

@@ -180,9 +180,12 @@ __device__ inline void inverse16(const double* L, const double* rinv, double* __
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     double s0 = (i == c) ? 1.0 : 0.0, s1 = 0.0;
+    // the broadcasts of row i wait for x[i-1]: otherwise all 120 of them are
+    // hoisted to the top and held in registers at once
+    const double dep = i > 0 ? x[i - 1] : 0.0;
 #pragma unroll
     for (int k = 0; k < i; ++k) {
-      const double lik = row_bcast_i(lr[k], i);
+      const double lik = row_bcast_dep_i(lr[k], dep, i);
       if (k & 1)
         s1 = fma(-lik, x[k], s1);
       else
