@@ -425,30 +425,43 @@ __global__ __launch_bounds__(256) void chol_trsm_kernel(double* __restrict__ K,
       y[s][r] = ident < 0 ? v : (k == ident ? 1.0 : 0.0);
     }
   __syncthreads();
+  // The LDS operands of step s+1 (its L11 tiles, negated, and D_s+1) are
+  // read while step s multiplies, so no product waits for an LDS read.
+  double ops[2][36];
+  auto load_ops = [&](int s, double (&o)[36]) {
+#pragma unroll
+    for (int sp = 0; sp < 7; ++sp)
+      if (sp < s) {
+        const double* Lt = Ls + ptile(s, sp);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) o[4 * sp + kk] = -Lt[((lane >> 4) + 4 * kk) * PT + (lane & 15)];
+      }
+    const double* Dt = Ds + s * PTS;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) o[32 + kk] = Dt[((lane >> 4) + 4 * kk) * PT + (lane & 15)];
+  };
+  load_ops(0, ops[0]);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
+    if (s + 1 < 8) load_ops(s + 1, ops[(s + 1) & 1]);
+    // keeps the reads above this step's products (the scheduler would sink
+    // each one next to its use)
+    __builtin_amdgcn_sched_barrier(0);
+    const double(&o)[36] = ops[s & 1];
     d4 part[4];
     part[0] = y[s];
 #pragma unroll
     for (int kk = 1; kk < 4; ++kk) part[kk] = d4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int sp = 0; sp < s; ++sp) {
-      const double* Lt = Ls + ptile(s, sp);
+    for (int sp = 0; sp < s; ++sp)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int q = (lane >> 4) + 4 * kk;
-        part[kk] = __builtin_amdgcn_mfma_f64_16x16x4f64(-Lt[q * PT + (lane & 15)], y[sp][kk],
-                                                        part[kk], 0, 0, 0);
-      }
-    }
+      for (int kk = 0; kk < 4; ++kk)
+        part[kk] = __builtin_amdgcn_mfma_f64_16x16x4f64(o[4 * sp + kk], y[sp][kk], part[kk], 0, 0, 0);
     const d4 acc = (part[0] + part[1]) + (part[2] + part[3]);
-    const double* Dt = Ds + s * PTS;
     d4 out = d4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int q = (lane >> 4) + 4 * kk;
-      out = __builtin_amdgcn_mfma_f64_16x16x4f64(Dt[q * PT + (lane & 15)], acc[kk], out, 0, 0, 0);
-    }
+    for (int kk = 0; kk < 4; ++kk)
+      out = __builtin_amdgcn_mfma_f64_16x16x4f64(o[32 + kk], acc[kk], out, 0, 0, 0);
     y[s] = out;
   }
 #pragma unroll
