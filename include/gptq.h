@@ -59,6 +59,8 @@ typedef enum {
 #define GPTQ_FLAG_NO_CLIP 16u           /* gptq_quantize_layer: levels not clamped to the grid
                                            (the no-clipping regime of Satz 5); stored codes
                                            saturate to [0, 255] */
+#define GPTQ_FLAG_HESSIAN_SPLIT8 32u    /* gptq_hessian_accumulate: X^T X from int8 digit
+                                           slices on the int8 matrix cores (see Step 1) */
 
 /* ---------------------------------------------------------------------------
  * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's
@@ -79,8 +81,23 @@ typedef enum {
  * (results are bitwise reproducible either way for a given ws choice).
  * in_features == 0, or n_tokens == 0 without the overwrite flag, is a no-op.
  * Asynchronous on `stream`.
+ *
+ * With GPTQ_FLAG_HESSIAN_SPLIT8 the products are formed on the int8 matrix
+ * cores instead (error-free slicing of a matrix product into integer slice
+ * products, after Ozaki, Ogita, Oishi and Rump). Per call, column f of X
+ * gets the scale 2^e_f, the smallest power of two above max_k |x_kf|, and
+ * each value is rounded to the nearest multiple of 2^(e_f - 30) (ties to
+ * even); that fixed-point value is cut into four signed int8 digits and
+ * every digit-pair product is summed exactly in int32, then in fp64. The
+ * result is X~^T X~ for the rounded X~ (|x~ - x| <= 2^(e_f - 31)), up to the
+ * fp64 additions. A column holding NaN or Inf gives NaN in its row and
+ * column of S. The workspace is then required: ws_bytes >=
+ * gptq_hessian_split8_workspace_bytes(in_features, n_tokens), else
+ * GPTQ_EWORKSPACE (it holds the digit planes, 4 * in_features * n_tokens
+ * bytes rounded up to tiles, and any token-split partial tiles).
  * ------------------------------------------------------------------------- */
 size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_tokens);
+size_t gptq_hessian_split8_workspace_bytes(int64_t in_features, int64_t n_tokens);
 gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
                                     const float* X, int64_t n_tokens, int64_t ldx,
                                     uint32_t flags, void* ws, size_t ws_bytes, void* stream);

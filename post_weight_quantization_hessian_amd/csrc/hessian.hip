@@ -198,6 +198,318 @@ static void hess_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit,
   nsplit = (int)cdiv(n, tps);
 }
 
+// ---------------------------------------------------------------- split8
+//
+// Digit-sliced route on the int8 matrix cores (the error-free splitting of a
+// matrix product into exactly computed integer slice products, Ozaki, Ogita,
+// Oishi and Rump; here applied to X^T X). Per call, activation column f gets
+// the power-of-two scale 2^e_f with max_k |x_kf| < 2^e_f, and every value of
+// the column becomes the integer m = rint(x * 2^(30 - e_f)), |m| < 2^30,
+// written as m = d0*2^24 + d1*2^16 + d2*2^8 + d3 with signed-byte digits
+// d1..d3 in [-128, 127] and |d0| <= 64. Then
+//   x_kf x_kg = 2^(e_f + e_g - 60) * sum_{a,b} d_a d_b 2^(48 - 8(a + b)),
+// and for every digit order s = a + b the sum T_s = sum_{a+b=s} D_a^T D_b over
+// the tokens is an exact int32 product on v_mfma_i32_32x32x32_i8 (at most
+// 4 * 2^14 per token, 16384 tokens per workgroup). Each T_s is added into
+// fp64 accumulators once it is complete. What this represents exactly is x
+// rounded to 30 fractional bits of its column's scale: an error of at most
+// 2^(e_f - 31) per value, no other error than the fp64 additions.
+
+constexpr int H8_KB = 64;               // tokens per staged chunk
+constexpr int H8_LD = 80;               // LDS row pitch in bytes (conflict-free 16 B reads)
+constexpr int H8_TN = 64;               // workgroup tile: 128 rows x 64 columns of S
+constexpr int H8_ABUF = 4 * GT * H8_LD;     // one chunk of A: 4 digit planes x 128 rows
+constexpr int H8_BBUF = 4 * H8_TN * H8_LD;  // one chunk of B: 4 digit planes x 64 rows
+constexpr int H8_GRP = 8;               // tiles are visited in 8x8 groups (L2 reuse)
+constexpr int H8_MAXTOK = 16384;        // tokens per workgroup (int32 range of T_s)
+constexpr int H8_BAD = 0x40000000;      // exponent of a column holding NaN/Inf
+
+typedef int i4v __attribute__((ext_vector_type(4)));
+typedef int i16v __attribute__((ext_vector_type(16)));
+
+__global__ void h8_zero_kernel(unsigned* __restrict__ p, int64_t count) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = 0u;
+}
+
+// colmax[f] = max over the call's tokens of the bits of |x_kf| (as unsigned,
+// which orders non-negative floats; NaN/Inf give bits >= 0x7f800000).
+// Grid (cdiv(dim, 256), cdiv(n, 256)).
+__global__ __launch_bounds__(256) void h8_colmax_kernel(const float* __restrict__ X, int64_t ldx,
+                                                        int64_t n, int64_t dim,
+                                                        unsigned* __restrict__ colmax) {
+  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (f >= dim) return;
+  const int64_t k0 = (int64_t)blockIdx.y * 256;
+  const int64_t k1 = k0 + 256 < n ? k0 + 256 : n;
+  unsigned m = 0u;
+  for (int64_t k = k0; k < k1; ++k) {
+    const unsigned b = __float_as_uint(X[k * ldx + f]) & 0x7fffffffu;
+    m = b > m ? b : m;
+  }
+  atomicMax(colmax + f, m);
+}
+
+__device__ inline int h8_exponent(unsigned bits) {
+  if (bits >= 0x7f800000u) return H8_BAD;
+  if (bits == 0u) return 0;
+  int e;
+  (void)frexpf(__uint_as_float(bits), &e);  // max = mant * 2^e, mant in [0.5, 1)
+  return e;
+}
+
+// Digit planes dig[a][f][k] (a = 0..3, f < dpad, k < npad; int8, tokens
+// contiguous), zero outside the token and feature range and in columns
+// holding NaN/Inf. Workgroup: 64 features x 64 tokens; thread t takes
+// feature t % 64 and 16 consecutive tokens. Blocks with blockIdx.x == 0 also
+// write the column exponents. Grid (npad / 64, dpad / 64).
+__global__ __launch_bounds__(256) void h8_split_kernel(const float* __restrict__ X, int64_t ldx,
+                                                       int64_t n, int64_t dim,
+                                                       const unsigned* __restrict__ colmax,
+                                                       int* __restrict__ exps,
+                                                       int8_t* __restrict__ dig, int64_t dpad,
+                                                       int64_t npad) {
+  const int r = threadIdx.x & 63, tg = threadIdx.x >> 6;
+  const int64_t f = (int64_t)blockIdx.y * 64 + r;
+  const int64_t k0 = (int64_t)blockIdx.x * 64 + tg * 16;
+  const int e = f < dim ? h8_exponent(colmax[f]) : 0;
+  if (blockIdx.x == 0 && tg == 0) exps[f] = e;
+  const bool live = f < dim && e != H8_BAD;
+  float x[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) x[q] = (live && k0 + q < n) ? X[(k0 + q) * ldx + f] : 0.0f;
+  unsigned w[4][4];  // [digit][token quad], little-endian bytes
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) w[a][qq] = 0u;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    int m = __float2int_rn(ldexpf(x[q], 30 - e));
+    int d[4];
+#pragma unroll
+    for (int a = 3; a >= 1; --a) {
+      d[a] = (int)(signed char)(m & 0xff);
+      m = (m - d[a]) >> 8;
+    }
+    d[0] = m;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) w[a][q >> 2] |= ((unsigned)d[a] & 0xffu) << (8 * (q & 3));
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    uint4 v = make_uint4(w[a][0], w[a][1], w[a][2], w[a][3]);
+    *reinterpret_cast<uint4*>(dig + ((int64_t)a * dpad + f) * npad + k0) = v;
+  }
+}
+
+// 128-tile of a launch slot: the upper triangle of 128x128 tiles is visited
+// in groups of 8x8 tiles (row-major over the triangle of groups, row-major
+// inside a group), so that the workgroups resident on one XCD share operand
+// rows in its L2; each tile is two slots (its left and right 64 columns).
+// Slots of a group that fall below the diagonal or outside the matrix have
+// no tile.
+__device__ inline bool h8_tile_of(int id, int nt, int& a, int& b, int& half) {
+  const int ng = (nt + H8_GRP - 1) / H8_GRP;
+  half = id & 1;
+  id >>= 1;
+  int ga, gb;
+  upper_tile(id / (H8_GRP * H8_GRP), ng, ga, gb);
+  const int loc = id % (H8_GRP * H8_GRP);
+  a = ga * H8_GRP + loc / H8_GRP;
+  b = gb * H8_GRP + loc % H8_GRP;
+  return a <= b && b < nt;
+}
+
+// 128 rows x 64 columns of an upper 128-tile of S (a <= b) for one token
+// split per workgroup: four waves, each 64 x 32 (two v_mfma_i32_32x32x32_i8
+// tiles). Every 64-token chunk stages all four digit planes of the rows and
+// of the columns in LDS, and all 16 digit pairs are multiplied from there;
+// each digit order s = a + b has its own int32 accumulators for the whole
+// token range (7 orders x 2 tiles x 16 = 224 registers), combined in fp64 at
+// the end. v_mfma_i32_32x32x32_i8 operands (lane l): 16 int8 of row l%32 of A
+// (of column l%32 of B) over the tokens 16*(l/32) .. +15 of the 32-token step;
+// A and B are loaded alike, so the pairing of their k indices inside the
+// instruction is the same for both. D reg x: row 8*(x/4) + 4*(l/32) + x%4,
+// col l%32. The next chunk is loaded into registers while the current one
+// is multiplied, and two chunks alternate in LDS.
+__global__ __launch_bounds__(256, 1) void h8_tile_kernel(const int8_t* __restrict__ dig, int64_t dpad,
+                                                         int64_t npad, const int* __restrict__ exps,
+                                                         int64_t n_tokens, int64_t dim, int nt,
+                                                         int nslots, int64_t tok_per_split,
+                                                         double* __restrict__ S, int64_t lds,
+                                                         double* __restrict__ part, bool acc_old) {
+  __shared__ __attribute__((aligned(16))) int8_t sm[2][H8_ABUF + H8_BBUF];
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int slot = lin % nslots;
+  const int split = lin / nslots;
+  int ta, tb, half;
+  if (!h8_tile_of(slot, nt, ta, tb, half)) return;  // uniform per workgroup
+  const int64_t fa = (int64_t)ta * GT, fb = (int64_t)tb * GT + half * H8_TN;
+  const int64_t t0 = (int64_t)split * tok_per_split;
+  int64_t t1 = t0 + tok_per_split;
+  const int64_t tend = round_up(n_tokens, H8_KB);
+  if (t1 > tend) t1 = tend;
+  const int nst = (int)((t1 - t0) / H8_KB);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
+  const int lrow = tid >> 2, lch = tid & 3;  // row lrow (+64), 16-byte chunk lch
+  const int64_t plane = dpad * npad;
+  const int8_t* gA = dig + (fa + lrow) * npad + t0 + lch * 16;
+  const int8_t* gB = dig + (fb + lrow) * npad + t0 + lch * 16;
+  const int64_t row64 = 64 * npad;
+  i4v ra[8], rb[4];
+  auto fetch = [&](int k) {
+    if (k > nst - 1) k = nst - 1;  // past the end: reload the last chunk (never used)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[2 * q] = *reinterpret_cast<const i4v*>(gA + q * plane + k * H8_KB);
+      ra[2 * q + 1] = *reinterpret_cast<const i4v*>(gA + q * plane + row64 + k * H8_KB);
+      rb[q] = *reinterpret_cast<const i4v*>(gB + q * plane + k * H8_KB);
+    }
+  };
+  auto stash = [&](int buf) {
+    int8_t* A = sm[buf] + lrow * H8_LD + lch * 16;
+    int8_t* B = sm[buf] + H8_ABUF + lrow * H8_LD + lch * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<i4v*>(A + q * (GT * H8_LD)) = ra[2 * q];
+      *reinterpret_cast<i4v*>(A + q * (GT * H8_LD) + 64 * H8_LD) = ra[2 * q + 1];
+      *reinterpret_cast<i4v*>(B + q * (H8_TN * H8_LD)) = rb[q];
+    }
+  };
+  i16v acc[7][2];
+#pragma unroll
+  for (int o = 0; o < 7; ++o)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[o][i][x] = 0;
+  const int arow = (wr * 64 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
+  const int brow = H8_ABUF + (wc * 32 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
+  fetch(0);
+  stash(0);
+  fetch(1);
+  __syncthreads();
+  for (int k = 0; k < nst; ++k) {
+    const int8_t* base = sm[k & 1];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      i4v av[4][2], bv[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q][0] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + kh * 32);
+        av[q][1] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + 32 * H8_LD +
+                                                 kh * 32);
+        bv[q] = *reinterpret_cast<const i4v*>(base + q * (H8_TN * H8_LD) + brow + kh * 32);
+      }
+#pragma unroll
+      for (int da = 0; da < 4; ++da)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            acc[da + db][i] =
+                __builtin_amdgcn_mfma_i32_32x32x32_i8(av[da][i], bv[db], acc[da + db][i], 0, 0, 0);
+    }
+    // unconditional, so that the load counters stay in issue order on every
+    // path (after the last chunk this fills the idle buffer)
+    stash((k + 1) & 1);
+    fetch(k + 2);
+    __syncthreads();
+  }
+  // S_fg = 2^(e_f + e_g - 60) * sum_s 2^(48 - 8 s) T_s, smallest terms first
+  const int ec = exps[fb + wc * 32 + (lane & 31)];
+  const int canon = ta * nt - ta * (ta - 1) / 2 + (tb - ta);  // row-major triangle order
+  const int ntiles = nt * (nt + 1) / 2;
+  double* P = part ? part + ((int64_t)split * ntiles + canon) * (GT * GT) : nullptr;
+  const int c = wc * 32 + (lane & 31);  // column inside this workgroup's 64
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int r = wr * 64 + i * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+      const int er = exps[fa + r];
+      double t = (double)acc[6][i][x];
+#pragma unroll
+      for (int o = 5; o >= 0; --o) t += __builtin_ldexp((double)acc[o][i][x], 48 - 8 * o);
+      const double v = (er == H8_BAD || ec == H8_BAD) ? __builtin_nan("")
+                                                      : __builtin_ldexp(t, er + ec - 60);
+      if (P) {
+        P[r * GT + half * H8_TN + c] = v;
+      } else if (fa + r < dim && fb + c < dim) {
+        double* d = S + (fa + r) * lds + fb + c;
+        const double o = acc_old ? *d + v : v;
+        *d = o;
+        // a diagonal 128-tile is written whole by its two halves (the two
+        // triangles are exact integer sums, so they agree bit for bit)
+        if (ta != tb) S[(fb + c) * lds + fa + r] = o;
+      }
+    }
+}
+
+static void h8_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit, int64_t& tps) {
+  nt = (int)cdiv(dim, GT);
+  ntiles = nt * (nt + 1) / 2;
+  int64_t want = cdiv(1024, ntiles);
+  int64_t cap_tok = n / 512;
+  if (want > cap_tok) want = cap_tok;
+  if (want > 64) want = 64;
+  if (want < cdiv(n, H8_MAXTOK)) want = cdiv(n, H8_MAXTOK);
+  if (want < 1) want = 1;
+  tps = round_up(cdiv(n, want), H8_KB);
+  nsplit = (int)cdiv(n, tps);
+}
+
+struct H8Layout {
+  int64_t dpad, npad, off_exps, off_dig, off_part, total;
+  int nt, ntiles, nsplit, nslots;
+  int64_t tps;
+  H8Layout(int64_t dim, int64_t n) {
+    h8_plan(dim, n, nt, ntiles, nsplit, tps);
+    const int ng = (int)cdiv(nt, H8_GRP);
+    nslots = ng * (ng + 1) / 2 * H8_GRP * H8_GRP * 2;
+    dpad = round_up(dim, GT);
+    npad = round_up(n, H8_KB);
+    off_exps = round_up(dpad * 4, 256);
+    off_dig = off_exps + round_up(dpad * 4, 256);
+    off_part = off_dig + round_up(4 * dpad * npad, 256);
+    total = off_part + (nsplit > 1 ? (int64_t)nsplit * ntiles * GT * GT * 8 : 0);
+  }
+};
+
+static gptq_status hess_split8(double* S, int64_t dim, const float* X, int64_t n, int64_t ldx,
+                               bool overwrite, void* ws, size_t ws_bytes, hipStream_t st) {
+  H8Layout L(dim, n);
+  if (!ws || ws_bytes < (size_t)L.total) return GPTQ_EWORKSPACE;
+  char* base = (char*)ws;
+  unsigned* colmax = (unsigned*)base;
+  int* exps = (int*)(base + L.off_exps);
+  int8_t* dig = (int8_t*)(base + L.off_dig);
+  double* part = L.nsplit > 1 ? (double*)(base + L.off_part) : nullptr;
+  GPTQ_LAUNCH(K_FILL, st,
+              h8_zero_kernel<<<(unsigned)std::min<int64_t>(cdiv(dim, 256), 4096), 256, 0, st>>>(
+                  colmax, dim));
+  GPTQ_LAUNCH(K_HESS_DIGITS, st,
+              h8_colmax_kernel<<<dim3((unsigned)cdiv(dim, 256), (unsigned)cdiv(n, 256)), 256, 0,
+                                 st>>>(X, ldx, n, dim, colmax));
+  GPTQ_LAUNCH(K_HESS_DIGITS, st,
+              h8_split_kernel<<<dim3((unsigned)(L.npad / 64), (unsigned)(L.dpad / 64)), 256, 0,
+                                st>>>(X, ldx, n, dim, colmax, exps, dig, L.dpad, L.npad));
+  const int nblocks = L.nslots * L.nsplit;
+  GPTQ_LAUNCH(K_HESS_SPLIT8, st,
+              h8_tile_kernel<<<nblocks, 256, 0, st>>>(dig, L.dpad, L.npad, exps, n, dim, L.nt,
+                                                      L.nslots, L.tps, S, dim, part,
+                                                      !overwrite));
+  if (part) {
+    dim3 grid(4, L.ntiles);
+    GPTQ_LAUNCH(K_HESS_REDUCE, st,
+                hess_reduce_kernel<<<grid, 256, 0, st>>>(part, L.nsplit, L.nt, L.ntiles, dim, S,
+                                                         dim, overwrite));
+  }
+  return GPTQ_OK;
+}
+
 }  // namespace gptq
 
 using namespace gptq;
@@ -211,11 +523,17 @@ extern "C" size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_to
   return (size_t)nsplit * ntiles * GT * GT * sizeof(double);
 }
 
+extern "C" size_t gptq_hessian_split8_workspace_bytes(int64_t in_features, int64_t n_tokens) {
+  if (in_features <= 0 || n_tokens <= 0) return 0;
+  if (in_features > (int64_t)1 << 20) return 0;
+  return (size_t)H8Layout(in_features, n_tokens).total;
+}
+
 extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, const float* X,
                                                int64_t n_tokens, int64_t ldx, uint32_t flags,
                                                void* ws, size_t ws_bytes, void* stream) {
   if (in_features < 0 || n_tokens < 0) return GPTQ_EINVAL;
-  if (flags & ~GPTQ_FLAG_HESSIAN_OVERWRITE) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_HESSIAN_OVERWRITE | GPTQ_FLAG_HESSIAN_SPLIT8)) return GPTQ_EINVAL;
   const bool overwrite = (flags & GPTQ_FLAG_HESSIAN_OVERWRITE) != 0;
   if (in_features == 0 || (n_tokens == 0 && !overwrite)) return GPTQ_OK;
   if (!S) return GPTQ_EINVAL;
@@ -229,6 +547,8 @@ extern "C" gptq_status gptq_hessian_accumulate(double* S, int64_t in_features, c
     return GPTQ_OK;
   }
   if (!X || ldx < in_features) return GPTQ_EINVAL;
+  if (flags & GPTQ_FLAG_HESSIAN_SPLIT8)
+    return hess_split8(S, in_features, X, n_tokens, ldx, overwrite, ws, ws_bytes, st);
   int nt, ntiles, nsplit;
   int64_t tps;
   hess_plan(in_features, n_tokens, nt, ntiles, nsplit, tps);

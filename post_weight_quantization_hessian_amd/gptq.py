@@ -25,9 +25,11 @@ GPTQ_FLAG_HESSIAN_OVERWRITE = 2
 GPTQ_FLAG_NO_SYNC = 4
 GPTQ_FLAG_MIN_PIVOT = 8
 GPTQ_FLAG_NO_CLIP = 16
+GPTQ_FLAG_HESSIAN_SPLIT8 = 32
 
 EXPORTS = {
     "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
+    "gptq_hessian_split8_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
     "gptq_hessian_accumulate": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int64,
                                           C.c_uint32, C.c_void_p, C.c_size_t, C.c_void_p]),
     "gptq_prepare_workspace_bytes": (C.c_size_t, [C.c_int64]),
@@ -117,9 +119,15 @@ def hessian_workspace_bytes(in_features: int, n_tokens: int) -> int:
     return int(lib.gptq_hessian_workspace_bytes(in_features, n_tokens))
 
 
-def hessian_accumulate(S, X, workspace=None, overwrite=False):
+def hessian_split8_workspace_bytes(in_features: int, n_tokens: int) -> int:
+    return int(lib.gptq_hessian_split8_workspace_bytes(in_features, n_tokens))
+
+
+def hessian_accumulate(S, X, workspace=None, overwrite=False, split8=False):
     """S += X^T X, or S = X^T X with ``overwrite`` (fp64 S [i x i], fp32 X
-    [n x i] with unit stride along i)."""
+    [n x i] with unit stride along i). ``split8``: products from int8 digit
+    slices on the int8 matrix cores (X rounded per column to 30 fractional
+    bits of a power-of-two scale)."""
     torch = _torch()
     _need(S, torch.float64, "S", 2)
     _need(X, torch.float32, "X", 2)
@@ -129,8 +137,11 @@ def hessian_accumulate(S, X, workspace=None, overwrite=False):
     if X.stride(1) != 1:
         raise ValueError("X rows must be contiguous")
     if workspace is None:
-        workspace = _workspace(hessian_workspace_bytes(i, n), X.device)
+        nb = hessian_split8_workspace_bytes(i, n) if split8 else hessian_workspace_bytes(i, n)
+        workspace = _workspace(nb, X.device)
     flags = GPTQ_FLAG_HESSIAN_OVERWRITE if overwrite else 0
+    if split8:
+        flags |= GPTQ_FLAG_HESSIAN_SPLIT8
     st = lib.gptq_hessian_accumulate(_ptr(S), i, _ptr(X), n, X.stride(0) if n > 0 else i, flags,
                                      _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_hessian_accumulate")
