@@ -31,7 +31,8 @@ CHOL_FUSE_NT = 48  # the library's bound on panels for the inverse accumulated i
 QEMB_KMAX = 512  # the library's longest early update-GEMM piece inside a sweep launch
 
 # MI355X published peaks
-PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "hbm_gbs": 8000.0}
+PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "i8_mfma": 5000.0,
+        "hbm_gbs": 8000.0}
 
 
 def parse():
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--order", choices=("workload", "min_pivot"), default="workload",
                     help="column order: the workload's (act-order or none), or the "
                          "min-pivot order for every input")
+    ap.add_argument("--hessian", choices=("auto", "exact", "split8"), default="auto",
+                    help="Hessian products: exact fp64, int8 digit slices, or split8 from "
+                         "2048 input features on (auto)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
@@ -63,8 +67,16 @@ def kernel_work(name, wl, plan):
     """Algorithmic flops (or bytes) of all launches of one kernel class in a
     step, with the unit and the roofline it is priced against."""
     if name == "hessian_tile":
-        f = sum(h.n * h.dim * (h.dim + 1) for h in plan)  # symmetric half, mul+add = 2
+        f = sum(h.n * h.dim * (h.dim + 1) for h in plan if not h.split8)  # symmetric half
         return f, "flop", "f64_mfma"
+    if name == "hessian_split8":
+        # the 16 digit-pair products of the symmetric half, int8 multiply + add
+        f = sum(16 * h.n * h.dim * (h.dim + 1) for h in plan if h.split8)
+        return f, "op", "i8_mfma"
+    if name == "hessian_digits":
+        # column maxima (read X), digit planes (read X, write 4 int8 per value)
+        b = sum(12 * h.n * h.dim for h in plan if h.split8)
+        return b, "byte", "hbm"
     if name in ("chol_trsm", "chol_potrf_syrk", "chol_potrf", "chol_col"):
         # Mirrors the library's launch sequence. Per panel p with m trailing
         # tile rows: trsm m tiles (a triangular solve with 128 right-hand
@@ -186,8 +198,9 @@ def quant_gemm_split(rows, cols):
 
 
 class HPlan:
-    def __init__(self, name, dim, n, rows):
+    def __init__(self, name, dim, n, rows, split8=False):
         self.name, self.dim, self.n, self.rows = name, dim, n, rows
+        self.split8 = split8
 
 
 # ---------------------------------------------------------------- HBM traffic
@@ -204,7 +217,9 @@ KERNEL_CLASS = {  # device function name -> timing class
     "q_sweep_kernel": "quant_sweep",
     "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout",
     "prep_uout_z_kernel": "prepare_uout", "mp_init_kernel": "minpivot_step",
-    "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update"}
+    "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update",
+    "h8_tile_kernel": "hessian_split8", "h8_colmax_kernel": "hessian_digits",
+    "h8_split_kernel": "hessian_digits"}
 
 
 def source_hash():
@@ -384,10 +399,10 @@ def main():
         del X
         grp = LayerGroup(h.dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
                          bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
-                         min_pivot=args.order == "min_pivot",
+                         min_pivot=args.order == "min_pivot", hessian=args.hessian,
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
-        plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0]))
+        plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0], split8=grp.split8))
     torch.cuda.synchronize()
 
     # Each calibration input (with the layers that read it) is an independent
@@ -441,11 +456,12 @@ def main():
     traffic = measured_traffic(wl.name, dominant)
     if work is not None and dom_ms > 0:
         per_step_s = dom_ms / 1000.0 / args.steps
-        if unit == "flop":
+        if unit in ("flop", "op"):
             achieved = work / per_step_s / 1e12
             peak = PEAK[peak_key]
             roofline = {"bound": "mfma",
-                        "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                        "achieved": achieved, "peak": peak,
+                        "unit": "TFLOP/s" if unit == "flop" else "TOP/s",
                         "frac": achieved / peak, "traffic": traffic,
                         "kernel": dominant, "precision": peak_key,
                         "launches_per_step": dom_launches / args.steps,
@@ -467,9 +483,9 @@ def main():
         w, u, pk = kernel_work(k, wl, plan)
         if w is not None and v["ms_per_step"] > 0:
             rate = w / (v["ms_per_step"] / 1000.0)
-            v["achieved"] = rate / (1e12 if u == "flop" else 1e9)
-            v["unit"] = "TFLOP/s" if u == "flop" else "GB/s"
-            v["peak"] = PEAK[pk] if u == "flop" else PEAK["hbm_gbs"]
+            v["achieved"] = rate / (1e9 if u == "byte" else 1e12)
+            v["unit"] = {"flop": "TFLOP/s", "op": "TOP/s", "byte": "GB/s"}[u]
+            v["peak"] = PEAK["hbm_gbs"] if u == "byte" else PEAK[pk]
             v["frac"] = v["achieved"] / v["peak"]
 
     cpu = None
@@ -488,7 +504,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": "i8+f64" if any(h.split8 for h in plan) else "f64",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.notes,
                    "layers": [f"{l.name} {l.rows}x{wl.input(l.hessian).dim}" for l in wl.layers],
@@ -498,7 +514,10 @@ def main():
                    "order": "min_pivot" if args.order == "min_pivot" else
                    ("act_order" if wl.act_order else "none"), "damp": wl.damp,
                    "weights_per_step": weights,
-                   "arithmetic": "fp64 Hessian/Cholesky/inverse and sweep, fp32 MFMA lazy update"},
+                   "hessian": {h.name: ("split8" if h.split8 else "exact") for h in plan},
+                   "arithmetic": "Hessian: exact fp64 products, or (split8) int8 digit-slice "
+                                 "products summed exactly in int32 and combined in fp64; "
+                                 "fp64 Cholesky/inverse and sweep, fp32 MFMA lazy update"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": breakdown,

@@ -5,7 +5,8 @@ workspaces, the act-order permutation, the factor U and one output set per
 bit width), allocated once, and enqueues the whole hot path asynchronously
 on the current stream:
 
-    S  = sum over token chunks of X_c^T X_c        (first chunk overwrites S)
+    S  = sum over token chunks of X_c^T X_c        (first chunk overwrites S;
+         exact fp64 products, or int8 digit slices on the matrix cores)
     perm, U = factor of the damped, act-ordered inverse Hessian
     codes, scales, zeros, g_idx, row_loss          for every bit width
 
@@ -16,10 +17,24 @@ from __future__ import annotations
 
 from . import gptq as G
 
+# "auto" takes the int8 digit-slice Hessian from this many input features on:
+# below it the fp64 kernel is as fast (few tiles, and the slicing costs three
+# extra launches)
+SPLIT8_MIN_DIM = 2048
+
+
+def hessian_mode(mode, dim):
+    """'exact' | 'split8' | 'auto' -> True when the layer uses split8."""
+    if mode == "auto":
+        return dim >= SPLIT8_MIN_DIM
+    if mode not in ("exact", "split8"):
+        raise ValueError(f"hessian mode {mode!r}")
+    return mode == "split8"
+
 
 class LayerGroup:
     def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
-                 device, min_pivot=False):
+                 device, min_pivot=False, hessian="exact"):
         import torch
         self.dim, self.rows = int(dim), int(rows)
         self.bits, self.group_size = tuple(bits), int(group_size)
@@ -29,8 +44,10 @@ class LayerGroup:
             self.act_order = False
         ng = -(-self.dim // self.group_size)
         self.S = torch.empty((self.dim, self.dim), dtype=torch.float64, device=device)
-        self.hws = torch.empty(max(G.hessian_workspace_bytes(self.dim, max_chunk_tokens), 1),
-                               dtype=torch.uint8, device=device)
+        self.split8 = hessian_mode(hessian, self.dim)
+        hb = (G.hessian_split8_workspace_bytes if self.split8 else G.hessian_workspace_bytes)(
+            self.dim, max_chunk_tokens)
+        self.hws = torch.empty(max(hb, 1), dtype=torch.uint8, device=device)
         self.pws = torch.empty(G.prepare_workspace_bytes(self.dim), dtype=torch.uint8,
                                device=device)
         self.perm = torch.empty(self.dim, dtype=torch.int32, device=device)
@@ -52,7 +69,8 @@ class LayerGroup:
         and stacked fp16 weights ``W`` [rows x dim], without synchronizing."""
         n = 0
         for ci, c in enumerate(chunks):
-            G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0))
+            G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0),
+                                 split8=self.split8)
             n += int(c.shape[0])
         G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
                        workspace=self.pws, out=(self.perm, self.U), sync=False,

@@ -1,0 +1,82 @@
+"""Test-side definitions for the digit-sliced int8 Hessian (split8).
+
+The library documents what split8 computes: per call (token chunk), column f
+of X gets the scale 2^e_f, the smallest power of two above max_k |x_kf|, and
+each value is rounded to the nearest multiple of 2^(e_f - 30) (ties to even);
+S += X~^T X~ for that fixed-point X~. These helpers restate that definition
+on the host, independently of the HIP code, and sum X~^T X~ exactly: with
+m = rint(x 2^(30 - e)) = hi 2^15 + lo (|hi| < 2^15, 0 <= lo < 2^15), every
+product of halves is an integer below 2^30 and every sum over fewer than 2^23
+tokens an integer below 2^53, so fp64 matrix products of the halves are
+exact; only the final combination rounds (twice, relative 2^-53 each).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def col_exponent(X):
+    """e_f with max_k |x_kf| = m 2^e_f, m in [0.5, 1) (0 for a zero column)."""
+    X = np.asarray(X)
+    mx = np.abs(X).max(axis=0).astype(np.float64)  # exact in X's own type
+    return np.frexp(mx)[1].astype(np.int64)
+
+
+def fixed_point_ints(X, e=None):
+    """(m, e): X~ = m 2^(e - 30), m integer (int64), |m| < 2^30. ``e`` may be
+    given (the exponents of the full call when X holds some of its columns)."""
+    e = col_exponent(X) if e is None else np.asarray(e, dtype=np.int64)
+    m = np.rint(np.ldexp(np.asarray(X, dtype=np.float64), (30 - e)[None, :])).astype(np.int64)
+    assert np.abs(m).max(initial=0) < 2 ** 30
+    return m, e
+
+
+def _halves(m):
+    hi = m >> 15
+    lo = m - (hi << 15)
+    return hi.astype(np.float64), lo.astype(np.float64)
+
+
+def fixed_point_gram(X, cols_a=None, cols_b=None, e=None):
+    """(X~^T X~ restricted to cols_a x cols_b, |X~|^T |X~| on the same block)
+    for one call's X. Exact integer sums; requires fewer than 2^23 tokens."""
+    X = np.asarray(X)
+    assert X.shape[0] < 2 ** 23
+    m, e = fixed_point_ints(X, e)
+    ca = np.arange(X.shape[1]) if cols_a is None else np.asarray(cols_a)
+    cb = ca if cols_b is None else np.asarray(cols_b)
+    ha, la = _halves(m[:, ca])
+    hb, lb = _halves(m[:, cb])
+    T = (ha.T @ hb) * 2.0 ** 30 + ((ha.T @ lb) + (la.T @ hb)) * 2.0 ** 15 + la.T @ lb
+    scale = np.ldexp(1.0, e[ca][:, None] + e[cb][None, :] - 60)
+    am = np.abs(m).astype(np.float64)
+    mag = (am[:, ca].T @ am[:, cb]) * scale
+    return T * scale, mag
+
+
+def fixed_point_diag(X, e=None, block=1024):
+    """diag(X~^T X~) for one call's X, exact integer sums then one rounding
+    (column blocks, to bound the temporaries)."""
+    X = np.asarray(X)
+    e = col_exponent(X) if e is None else np.asarray(e, dtype=np.int64)
+    out = np.empty(X.shape[1])
+    for c0 in range(0, X.shape[1], block):
+        m, eb = fixed_point_ints(X[:, c0:c0 + block], e[c0:c0 + block])
+        hi, lo = _halves(m)
+        d = (hi * hi).sum(axis=0) * 2.0 ** 30 + 2.0 * (hi * lo).sum(axis=0) * 2.0 ** 15 \
+            + (lo * lo).sum(axis=0)
+        out[c0:c0 + block] = d * np.ldexp(1.0, 2 * eb - 60)
+    return out
+
+
+def rounding_bound(X, cols_a=None, cols_b=None, e=None):
+    """Bound on |X~^T X~ - X^T X| for one call: |x~ - x| <= 2^(e_f - 31), so
+    2^-31 (s_f sum|x_g| + s_g sum|x_f|) + n 2^-62 s_f s_g."""
+    X = np.asarray(X, dtype=np.float64)
+    ca = np.arange(X.shape[1]) if cols_a is None else np.asarray(cols_a)
+    cb = ca if cols_b is None else np.asarray(cols_b)
+    s = np.ldexp(1.0, col_exponent(X) if e is None else np.asarray(e, dtype=np.int64))
+    a = np.abs(X).sum(axis=0)
+    n = X.shape[0]
+    return 2.0 ** -31 * (s[ca][:, None] * a[cb][None, :] + s[cb][None, :] * a[ca][:, None]) \
+        + n * 2.0 ** -62 * np.outer(s[ca], s[cb])

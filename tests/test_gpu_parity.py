@@ -11,6 +11,7 @@ import pytest
 
 import oracle as O
 from post_weight_quantization_hessian_amd import synth
+from post_weight_quantization_hessian_amd.pipeline import hessian_mode
 from post_weight_quantization_hessian_amd.workloads import WORKLOADS
 from tests.parity_util import compare_layer, to_numpy_layer
 
@@ -30,13 +31,13 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_hessian(Xs, dim, use_ws=True):
+def gpu_hessian(Xs, dim, use_ws=True, split8=False):
     S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
     n = 0
     for X in Xs:
         Xd = torch.from_numpy(X).to(DEV)
         ws = None if use_ws else torch.empty(1, dtype=torch.uint8, device=DEV)
-        G.hessian_accumulate(S, Xd, workspace=ws)
+        G.hessian_accumulate(S, Xd, workspace=ws, split8=split8)
         n += X.shape[0]
     return S, n
 
@@ -239,14 +240,27 @@ def workload_inputs(wl, hname):
 
 
 def run_workload_input(wl, hname, block):
+    """The Hessian mode is the benchmark's ("auto": the int8 digit-slice
+    products from 2048 features on); the oracle's S is exact either way."""
     X, W = workload_inputs(wl, hname)
     chunks = [X[s:s + wl.token_chunk] for s in range(0, X.shape[0], wl.token_chunk)]
-    S, n = gpu_hessian(chunks, X.shape[1])
+    split8 = hessian_mode("auto", X.shape[1])
+    S, n = gpu_hessian(chunks, X.shape[1], split8=split8)
     perm, U = G.prepare_hinv(S, n, damp=wl.damp, act_order=wl.act_order)
     Sr, nr = O.hessian_sum(chunks)
     H = O.damped_hessian(Sr, nr, wl.damp)
     pr = O.act_order_perm(H) if wl.act_order else np.arange(H.shape[0])
-    assert np.array_equal(perm.cpu().numpy(), pr)
+    pg = perm.cpu().numpy().astype(np.int64)
+    if split8:
+        # diag S rounds X per column (relative error far below 1e-7): the
+        # order may differ only between near-equal diagonals, and the
+        # reference then sweeps in the library's (equally valid) order
+        hd = np.diag(H)
+        assert np.array_equal(np.sort(pg), np.arange(len(pg)))
+        for k in np.nonzero(pg != pr)[0]:
+            assert abs(hd[pg[k]] - hd[pr[k]]) <= 1e-7 * hd[pr[k]], k
+        pr = pg
+    assert np.array_equal(pg, pr)
     Ur = O.hinv_upper(O.permute_sym(H, pr))
     Wd = torch.from_numpy(W).to(DEV)
     for bits in wl.bits:

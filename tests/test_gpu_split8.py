@@ -26,6 +26,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 import post_weight_quantization_hessian_amd.gptq as G  # noqa: E402
 from post_weight_quantization_hessian_amd import synth  # noqa: E402
 from tests.parity_util import compare_layer, to_numpy_layer  # noqa: E402
+from tests.split8_ref import fixed_point_gram, rounding_bound  # noqa: E402
 
 DEV = torch.device("cuda:0")
 U53 = 2.0 ** -53
@@ -34,39 +35,6 @@ U53 = 2.0 ** -53
 def say(msg):
     print(f"[case] {msg}", flush=True)
     sys.stdout.flush()
-
-
-def col_exponent(X):
-    mx = np.abs(X.astype(np.float64)).max(axis=0)
-    return np.frexp(mx)[1].astype(np.int64)  # mx = m 2^e, m in [0.5, 1); 0 -> 0
-
-
-def fixed_point_gram(X):
-    """(S~, |X~|^T |X~|) for the per-column fixed-point X~, exact up to two
-    fp64 additions per entry."""
-    e = col_exponent(X)
-    m = np.rint(np.ldexp(X.astype(np.float64), (30 - e)[None, :])).astype(np.int64)
-    assert np.abs(m).max() < 2 ** 30
-    hi = m >> 15
-    lo = m - (hi << 15)
-    HH = hi.T @ hi
-    HL = hi.T @ lo
-    LL = lo.T @ lo
-    T = HH.astype(np.float64) * 2.0 ** 30 + (HL + HL.T).astype(np.float64) * 2.0 ** 15 \
-        + LL.astype(np.float64)
-    scale = np.ldexp(1.0, (e[:, None] + e[None, :] - 60))
-    am = np.abs(m).astype(np.float64)
-    mag = (am.T @ am) * scale
-    return T * scale, mag
-
-
-def rounding_bound(X):
-    """The bound on |S~ - S| implied by rounding X to X~ (one call)."""
-    s = np.ldexp(1.0, col_exponent(X))
-    a = np.abs(X.astype(np.float64)).sum(axis=0)
-    n = X.shape[0]
-    return 2.0 ** -31 * (s[:, None] * a[None, :] + s[None, :] * a[:, None]) \
-        + n * 2.0 ** -62 * np.outer(s, s)
 
 
 def skewed_inputs(n, dim, seed):

@@ -1,0 +1,82 @@
+"""CPU pins of the test-side split8 definitions (tests/split8_ref.py), checked
+against exact rational arithmetic, so that the GPU tests that use them
+compare the library with the documented fixed-point Gram matrix and not with
+a restatement of their own mistakes."""
+from fractions import Fraction
+
+import numpy as np
+
+from tests import split8_ref as R8
+
+
+def _inputs(seed, n=40, d=5):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((n, d)) * np.exp(3.0 * rng.standard_normal(d))[None, :]
+    X[:, 2] = 0.0
+    X[7, 3] = 2.0 ** 5  # the column maximum is a power of two
+    X[:, 3] = np.clip(X[:, 3], -2.0 ** 5, 2.0 ** 5)
+    return X.astype(np.float32)
+
+
+def _exact_fixed_point(X):
+    """X~ as Fractions, from the definition: 2^e the smallest power of two
+    above the column maximum, x rounded to a multiple of 2^(e - 30), ties to
+    even."""
+    n, d = X.shape
+    out = [[None] * d for _ in range(n)]
+    for f in range(d):
+        col = [Fraction(float(v)) for v in X[:, f]]
+        mx = max(abs(v) for v in col)
+        e = 0
+        if mx > 0:
+            while Fraction(2) ** e <= mx:
+                e += 1
+            while Fraction(2) ** (e - 1) > mx:
+                e -= 1
+        step = Fraction(2) ** (e - 30)
+        for k, v in enumerate(col):
+            q = v / step
+            fl = q.numerator // q.denominator
+            r = q - fl
+            m = fl + (1 if (r > Fraction(1, 2) or (r == Fraction(1, 2) and fl % 2)) else 0)
+            assert abs(m) < 2 ** 30
+            out[k][f] = m * step
+    return out
+
+
+def test_fixed_point_gram_is_the_exact_sum():
+    X = _inputs(1)
+    Xt = _exact_fixed_point(X)
+    n, d = X.shape
+    S, mag = R8.fixed_point_gram(X)
+    for f in range(d):
+        for g in range(d):
+            ex = sum(Xt[k][f] * Xt[k][g] for k in range(n))
+            assert abs(Fraction(float(S[f, g])) - ex) <= Fraction(2.0 ** -51) * Fraction(mag[f, g])
+    dg = R8.fixed_point_diag(X)
+    assert np.array_equal(dg, np.diag(S))
+    m, e = R8.fixed_point_ints(X)
+    assert e[2] == 0 and np.all(m[:, 2] == 0)
+    assert e[3] == 6  # max 2^5 -> scale 2^6
+
+
+def test_rounding_bound_holds_exactly():
+    for seed in (2, 3):
+        X = _inputs(seed)
+        Xt = _exact_fixed_point(X)
+        n, d = X.shape
+        B = R8.rounding_bound(X)
+        for f in range(d):
+            for g in range(d):
+                fixed = sum(Xt[k][f] * Xt[k][g] for k in range(n))
+                exact = sum(Fraction(float(X[k, f])) * Fraction(float(X[k, g])) for k in range(n))
+                assert abs(fixed - exact) <= Fraction(float(B[f, g]))
+
+
+def test_subset_with_given_exponents_matches_full():
+    X = _inputs(4, n=64, d=9)
+    S, _ = R8.fixed_point_gram(X)
+    cols = np.array([8, 0, 3])
+    e = R8.col_exponent(X)[cols]
+    Ss, _ = R8.fixed_point_gram(X[:, cols], e=e)
+    assert np.array_equal(Ss, S[np.ix_(cols, cols)])
