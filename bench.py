@@ -47,7 +47,7 @@ def parse():
                          "min-pivot order for every input")
     ap.add_argument("--hessian", choices=("auto", "exact", "split8"), default="auto",
                     help="Hessian products: exact fp64, int8 digit slices, or split8 from "
-                         "2048 input features on (auto)")
+                         "256 input features on (auto)")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",

@@ -235,18 +235,26 @@ __global__ void h8_zero_kernel(unsigned* __restrict__ p, int64_t count) {
 
 // colmax[f] = max over the call's tokens of the bits of |x_kf| (as unsigned,
 // which orders non-negative floats; NaN/Inf give bits >= 0x7f800000).
-// Grid (cdiv(dim, 256), cdiv(n, 256)).
+// Workgroup: 64 features x 64 tokens, thread t takes feature t % 64 and 16
+// tokens of each 64-token block it visits. Grid (cdiv(dim, 64), up to
+// 65535), the token blocks strided by the grid's y extent.
 __global__ __launch_bounds__(256) void h8_colmax_kernel(const float* __restrict__ X, int64_t ldx,
                                                         int64_t n, int64_t dim,
                                                         unsigned* __restrict__ colmax) {
-  const int64_t f = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t f = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
   if (f >= dim) return;
-  const int64_t k0 = (int64_t)blockIdx.y * 256;
-  const int64_t k1 = k0 + 256 < n ? k0 + 256 : n;
   unsigned m = 0u;
-  for (int64_t k = k0; k < k1; ++k) {
-    const unsigned b = __float_as_uint(X[k * ldx + f]) & 0x7fffffffu;
-    m = b > m ? b : m;
+  for (int64_t k0 = (int64_t)blockIdx.y * 64 + (threadIdx.x >> 6) * 16; k0 < n;
+       k0 += (int64_t)gridDim.y * 64) {
+    const int cnt = n - k0 < 16 ? (int)(n - k0) : 16;
+    unsigned v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = q < cnt ? __float_as_uint(X[(k0 + q) * ldx + f]) : 0u;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const unsigned b = v[q] & 0x7fffffffu;
+      m = b > m ? b : m;
+    }
   }
   atomicMax(colmax + f, m);
 }
@@ -323,18 +331,19 @@ __device__ inline bool h8_tile_of(int id, int nt, int& a, int& b, int& half) {
 }
 
 // 128 rows x 64 columns of an upper 128-tile of S (a <= b) for one token
-// split per workgroup: four waves, each 64 x 32 (two v_mfma_i32_32x32x32_i8
-// tiles). Every 64-token chunk stages all four digit planes of the rows and
-// of the columns in LDS, and all 16 digit pairs are multiplied from there;
-// each digit order s = a + b has its own int32 accumulators for the whole
-// token range (7 orders x 2 tiles x 16 = 224 registers), combined in fp64 at
-// the end. v_mfma_i32_32x32x32_i8 operands (lane l): 16 int8 of row l%32 of A
-// (of column l%32 of B) over the tokens 16*(l/32) .. +15 of the 32-token step;
-// A and B are loaded alike, so the pairing of their k indices inside the
-// instruction is the same for both. D reg x: row 8*(x/4) + 4*(l/32) + x%4,
-// col l%32. The next chunk is loaded into registers while the current one
-// is multiplied, and two chunks alternate in LDS.
-__global__ __launch_bounds__(256, 1) void h8_tile_kernel(const int8_t* __restrict__ dig, int64_t dpad,
+// split per workgroup: eight waves (two per SIMD), each a 32 x 32
+// v_mfma_i32_32x32x32_i8 tile. Every 64-token chunk stages all four digit
+// planes of the rows and of the columns in LDS, and all 16 digit pairs are
+// multiplied from there; each digit order s = a + b has its own int32
+// accumulator for the whole token range (7 orders x 16 = 112 registers),
+// combined in fp64 at the end. v_mfma_i32_32x32x32_i8 operands (lane l): 16
+// int8 of row l%32 of A (of column l%32 of B) over the tokens 16*(l/32) ..
+// +15 of the 32-token step; A and B are loaded alike, so the pairing of their
+// k indices inside the instruction is the same for both. D reg x: row
+// 8*(x/4) + 4*(l/32) + x%4, col l%32. The next chunk is loaded into
+// registers while the current one is multiplied, and two chunks alternate in
+// LDS.
+__global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restrict__ dig, int64_t dpad,
                                                          int64_t npad, const int* __restrict__ exps,
                                                          int64_t n_tokens, int64_t dim, int nt,
                                                          int nslots, int64_t tok_per_split,
@@ -353,39 +362,35 @@ __global__ __launch_bounds__(256, 1) void h8_tile_kernel(const int8_t* __restric
   if (t1 > tend) t1 = tend;
   const int nst = (int)((t1 - t0) / H8_KB);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
-  const int lrow = tid >> 2, lch = tid & 3;  // row lrow (+64), 16-byte chunk lch
+  // loads: A row lrow of all four planes; B row lrow % 64 of planes
+  // 2 (lrow / 64) and 2 (lrow / 64) + 1; 16-byte chunk lch of the 64 tokens
+  const int lrow = tid >> 2, lch = tid & 3;
+  const int brw = lrow & 63, bpl = (lrow >> 6) * 2;
   const int64_t plane = dpad * npad;
   const int8_t* gA = dig + (fa + lrow) * npad + t0 + lch * 16;
-  const int8_t* gB = dig + (fb + lrow) * npad + t0 + lch * 16;
-  const int64_t row64 = 64 * npad;
-  i4v ra[8], rb[4];
+  const int8_t* gB = dig + bpl * plane + (fb + brw) * npad + t0 + lch * 16;
+  i4v ra[4], rb[2];
   auto fetch = [&](int k) {
     if (k > nst - 1) k = nst - 1;  // past the end: reload the last chunk (never used)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ra[2 * q] = *reinterpret_cast<const i4v*>(gA + q * plane + k * H8_KB);
-      ra[2 * q + 1] = *reinterpret_cast<const i4v*>(gA + q * plane + row64 + k * H8_KB);
-      rb[q] = *reinterpret_cast<const i4v*>(gB + q * plane + k * H8_KB);
-    }
+    for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const i4v*>(gA + q * plane + k * H8_KB);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) rb[q] = *reinterpret_cast<const i4v*>(gB + q * plane + k * H8_KB);
   };
   auto stash = [&](int buf) {
     int8_t* A = sm[buf] + lrow * H8_LD + lch * 16;
-    int8_t* B = sm[buf] + H8_ABUF + lrow * H8_LD + lch * 16;
+    int8_t* B = sm[buf] + H8_ABUF + bpl * (H8_TN * H8_LD) + brw * H8_LD + lch * 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<i4v*>(A + q * (GT * H8_LD)) = ra[2 * q];
-      *reinterpret_cast<i4v*>(A + q * (GT * H8_LD) + 64 * H8_LD) = ra[2 * q + 1];
-      *reinterpret_cast<i4v*>(B + q * (H8_TN * H8_LD)) = rb[q];
-    }
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<i4v*>(A + q * (GT * H8_LD)) = ra[q];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<i4v*>(B + q * (H8_TN * H8_LD)) = rb[q];
   };
-  i16v acc[7][2];
+  i16v acc[7];
 #pragma unroll
   for (int o = 0; o < 7; ++o)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int x = 0; x < 16; ++x) acc[o][i][x] = 0;
-  const int arow = (wr * 64 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
+    for (int x = 0; x < 16; ++x) acc[o][x] = 0;
+  const int arow = (wr * 32 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
   const int brow = H8_ABUF + (wc * 32 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
   fetch(0);
   stash(0);
@@ -395,22 +400,19 @@ __global__ __launch_bounds__(256, 1) void h8_tile_kernel(const int8_t* __restric
     const int8_t* base = sm[k & 1];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      i4v av[4][2], bv[4];
+      i4v av[4], bv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        av[q][0] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + kh * 32);
-        av[q][1] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + 32 * H8_LD +
-                                                 kh * 32);
+        av[q] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + kh * 32);
         bv[q] = *reinterpret_cast<const i4v*>(base + q * (H8_TN * H8_LD) + brow + kh * 32);
       }
+      // row-major over (a, b): two products into the same order are at
+      // least three instructions apart
 #pragma unroll
       for (int da = 0; da < 4; ++da)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            acc[da + db][i] =
-                __builtin_amdgcn_mfma_i32_32x32x32_i8(av[da][i], bv[db], acc[da + db][i], 0, 0, 0);
+          acc[da + db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[da], bv[db], acc[da + db], 0, 0, 0);
     }
     // unconditional, so that the load counters stay in issue order on every
     // path (after the last chunk this fills the idle buffer)
@@ -419,33 +421,31 @@ __global__ __launch_bounds__(256, 1) void h8_tile_kernel(const int8_t* __restric
     __syncthreads();
   }
   // S_fg = 2^(e_f + e_g - 60) * sum_s 2^(48 - 8 s) T_s, smallest terms first
-  const int ec = exps[fb + wc * 32 + (lane & 31)];
+  const int c = wc * 32 + (lane & 31);  // column inside this workgroup's 64
+  const int ec = exps[fb + c];
   const int canon = ta * nt - ta * (ta - 1) / 2 + (tb - ta);  // row-major triangle order
   const int ntiles = nt * (nt + 1) / 2;
   double* P = part ? part + ((int64_t)split * ntiles + canon) * (GT * GT) : nullptr;
-  const int c = wc * 32 + (lane & 31);  // column inside this workgroup's 64
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int x = 0; x < 16; ++x) {
+    const int r = wr * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+    const int er = exps[fa + r];
+    double t = (double)acc[6][x];
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int r = wr * 64 + i * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-      const int er = exps[fa + r];
-      double t = (double)acc[6][i][x];
-#pragma unroll
-      for (int o = 5; o >= 0; --o) t += __builtin_ldexp((double)acc[o][i][x], 48 - 8 * o);
-      const double v = (er == H8_BAD || ec == H8_BAD) ? __builtin_nan("")
-                                                      : __builtin_ldexp(t, er + ec - 60);
-      if (P) {
-        P[r * GT + half * H8_TN + c] = v;
-      } else if (fa + r < dim && fb + c < dim) {
-        double* d = S + (fa + r) * lds + fb + c;
-        const double o = acc_old ? *d + v : v;
-        *d = o;
-        // a diagonal 128-tile is written whole by its two halves (the two
-        // triangles are exact integer sums, so they agree bit for bit)
-        if (ta != tb) S[(fb + c) * lds + fa + r] = o;
-      }
+    for (int o = 5; o >= 0; --o) t += __builtin_ldexp((double)acc[o][x], 48 - 8 * o);
+    const double v = (er == H8_BAD || ec == H8_BAD) ? __builtin_nan("")
+                                                    : __builtin_ldexp(t, er + ec - 60);
+    if (P) {
+      P[r * GT + half * H8_TN + c] = v;
+    } else if (fa + r < dim && fb + c < dim) {
+      double* d = S + (fa + r) * lds + fb + c;
+      const double o = acc_old ? *d + v : v;
+      *d = o;
+      // a diagonal 128-tile is written whole by its two halves (the two
+      // triangles are exact integer sums, so they agree bit for bit)
+      if (ta != tb) S[(fb + c) * lds + fa + r] = o;
     }
+  }
 }
 
 static void h8_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit, int64_t& tps) {
@@ -491,14 +491,15 @@ static gptq_status hess_split8(double* S, int64_t dim, const float* X, int64_t n
               h8_zero_kernel<<<(unsigned)std::min<int64_t>(cdiv(dim, 256), 4096), 256, 0, st>>>(
                   colmax, dim));
   GPTQ_LAUNCH(K_HESS_DIGITS, st,
-              h8_colmax_kernel<<<dim3((unsigned)cdiv(dim, 256), (unsigned)cdiv(n, 256)), 256, 0,
-                                 st>>>(X, ldx, n, dim, colmax));
+              h8_colmax_kernel<<<dim3((unsigned)cdiv(dim, 64),
+                                      (unsigned)std::min<int64_t>(cdiv(n, 64), 65535)),
+                                 256, 0, st>>>(X, ldx, n, dim, colmax));
   GPTQ_LAUNCH(K_HESS_DIGITS, st,
               h8_split_kernel<<<dim3((unsigned)(L.npad / 64), (unsigned)(L.dpad / 64)), 256, 0,
                                 st>>>(X, ldx, n, dim, colmax, exps, dig, L.dpad, L.npad));
   const int nblocks = L.nslots * L.nsplit;
   GPTQ_LAUNCH(K_HESS_SPLIT8, st,
-              h8_tile_kernel<<<nblocks, 256, 0, st>>>(dig, L.dpad, L.npad, exps, n, dim, L.nt,
+              h8_tile_kernel<<<nblocks, 512, 0, st>>>(dig, L.dpad, L.npad, exps, n, dim, L.nt,
                                                       L.nslots, L.tps, S, dim, part,
                                                       !overwrite));
   if (part) {

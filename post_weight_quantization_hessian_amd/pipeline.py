@@ -17,10 +17,10 @@ from __future__ import annotations
 
 from . import gptq as G
 
-# "auto" takes the int8 digit-slice Hessian from this many input features on:
-# below it the fp64 kernel is as fast (few tiles, and the slicing costs three
-# extra launches)
-SPLIT8_MIN_DIM = 2048
+# "auto" takes the int8 digit-slice Hessian from this many input features on
+# (measured faster from 256 features at 2048 tokens; below, a handful of
+# tiles, either is a few microseconds)
+SPLIT8_MIN_DIM = 256
 
 
 def hessian_mode(mode, dim):

@@ -241,7 +241,7 @@ def workload_inputs(wl, hname):
 
 def run_workload_input(wl, hname, block):
     """The Hessian mode is the benchmark's ("auto": the int8 digit-slice
-    products from 2048 features on); the oracle's S is exact either way."""
+    products from 256 features on); the oracle's S is exact either way."""
     X, W = workload_inputs(wl, hname)
     chunks = [X[s:s + wl.token_chunk] for s in range(0, X.shape[0], wl.token_chunk)]
     split8 = hessian_mode("auto", X.shape[1])
