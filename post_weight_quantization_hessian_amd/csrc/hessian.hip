@@ -216,7 +216,7 @@ static void hess_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit,
 // 2^(e_f - 31) per value, no other error than the fp64 additions.
 
 constexpr int H8_KB = 64;               // tokens per staged chunk
-constexpr int H8_LD = 80;               // LDS row pitch in bytes (conflict-free 16 B reads)
+constexpr int H8_LD = 64;               // LDS row pitch in bytes, 16-byte chunks swizzled
 constexpr int H8_TN = 64;               // workgroup tile: 128 rows x 64 columns of S
 constexpr int H8_ABUF = 4 * GT * H8_LD;     // one chunk of A: 4 digit planes x 128 rows
 constexpr int H8_BBUF = 4 * H8_TN * H8_LD;  // one chunk of B: 4 digit planes x 64 rows
@@ -377,9 +377,14 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
 #pragma unroll
     for (int q = 0; q < 2; ++q) rb[q] = *reinterpret_cast<const i4v*>(gB + q * plane + k * H8_KB);
   };
+  // LDS rows of 64 bytes; chunk c of row r sits at position c ^ ((r >> 2) & 3).
+  // Stores (four lanes per row, 16 lanes = 4 consecutive rows) cover 64
+  // distinct banks, and so do operand reads (16 consecutive rows at one
+  // chunk: row r mod 4 picks the 16-bank quarter, the swizzle the 4 banks)
   auto stash = [&](int buf) {
-    int8_t* A = sm[buf] + lrow * H8_LD + lch * 16;
-    int8_t* B = sm[buf] + H8_ABUF + bpl * (H8_TN * H8_LD) + brw * H8_LD + lch * 16;
+    int8_t* A = sm[buf] + lrow * H8_LD + ((lch ^ ((lrow >> 2) & 3)) << 4);
+    int8_t* B = sm[buf] + H8_ABUF + bpl * (H8_TN * H8_LD) + brw * H8_LD +
+                ((lch ^ ((brw >> 2) & 3)) << 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<i4v*>(A + q * (GT * H8_LD)) = ra[q];
 #pragma unroll
@@ -390,8 +395,12 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
   for (int o = 0; o < 7; ++o)
 #pragma unroll
     for (int x = 0; x < 16; ++x) acc[o][x] = 0;
-  const int arow = (wr * 32 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
-  const int brow = H8_ABUF + (wc * 32 + (lane & 31)) * H8_LD + (lane >> 5) * 16;
+  // operand rows: wr*32 + l%32 (A), wc*32 + l%32 (B); both have the same
+  // swizzle, (l%32 >> 2) & 3, since 32-row offsets leave bits 2-3 alone
+  const int sw = ((lane & 31) >> 2) & 3;
+  const int arow = (wr * 32 + (lane & 31)) * H8_LD;
+  const int brow = H8_ABUF + (wc * 32 + (lane & 31)) * H8_LD;
+  const int koff[2] = {(((lane >> 5) + 0) ^ sw) << 4, (((lane >> 5) + 2) ^ sw) << 4};
   fetch(0);
   stash(0);
   fetch(1);
@@ -403,11 +412,9 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
       i4v av[4], bv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        av[q] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + kh * 32);
-        bv[q] = *reinterpret_cast<const i4v*>(base + q * (H8_TN * H8_LD) + brow + kh * 32);
+        av[q] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + koff[kh]);
+        bv[q] = *reinterpret_cast<const i4v*>(base + q * (H8_TN * H8_LD) + brow + koff[kh]);
       }
-      // row-major over (a, b): two products into the same order are at
-      // least three instructions apart
 #pragma unroll
       for (int da = 0; da < 4; ++da)
 #pragma unroll
