@@ -71,6 +71,21 @@ def test_split8_matches_fixed_point_and_oracle(n, dim):
     assert np.all(np.abs(Sg - Sx) <= rounding_bound(X) + 32 * U53 * mag)
 
 
+def test_split8_strided_rows():
+    """X as a column slice of a wider array (row stride > in_features)."""
+    say("split8 strided X")
+    n, dim, ld = 777, 300, 333
+    big = skewed_inputs(n, ld, 9)
+    X = big[:, :dim]
+    Xd = torch.from_numpy(big).to(DEV)[:, :dim]
+    assert Xd.stride(0) == ld
+    S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, Xd, overwrite=True, split8=True)
+    torch.cuda.synchronize()
+    St, mag = fixed_point_gram(np.ascontiguousarray(X))
+    assert np.all(np.abs(S.cpu().numpy() - St) <= 32 * U53 * mag)
+
+
 def test_split8_accumulates_calls_with_their_own_scales():
     say("split8 accumulate over three calls")
     dim = 300
