@@ -455,10 +455,13 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
   }
 }
 
+// Token splits: only while the tile halves (one workgroup each, one
+// workgroup per CU) number fewer than two rounds of the GPU, and whenever a
+// workgroup would otherwise take more than H8_MAXTOK tokens.
 static void h8_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit, int64_t& tps) {
   nt = (int)cdiv(dim, GT);
   ntiles = nt * (nt + 1) / 2;
-  int64_t want = cdiv(1024, ntiles);
+  int64_t want = cdiv(512, 2 * ntiles);
   int64_t cap_tok = n / 512;
   if (want > cap_tok) want = cap_tok;
   if (want > 64) want = 64;
