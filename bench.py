@@ -469,9 +469,10 @@ def main():
                         "frac": achieved / peak, "traffic": traffic,
                         "kernel": dominant, "precision": peak_key,
                         "launches_per_step": dom_launches,
-                        "avg_launch_ms": dom_ms / max(dom_launches, 1),
-                        "frac_vs_bf16_dense": achieved / PEAK["bf16_mfma"],
-                        "frac_vs_f32_mfma": achieved / PEAK["f32_mfma"]}
+                        "avg_launch_ms": dom_ms / max(dom_launches, 1)}
+            if unit == "flop":
+                roofline["frac_vs_bf16_dense"] = achieved / PEAK["bf16_mfma"]
+                roofline["frac_vs_f32_mfma"] = achieved / PEAK["f32_mfma"]
         else:
             achieved = work / per_step_s / 1e9
             roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK["hbm_gbs"],
@@ -482,7 +483,6 @@ def main():
     breakdown = {k: {"ms_per_step": v[0] / max(args.warmup, 1),
                      "launches_per_step": v[1] / max(args.warmup, 1)}
                  for k, v in prof_warm.items() if v[1] > 0}
-    phases = {}
     for k, v in breakdown.items():
         w, u, pk = kernel_work(k, wl, plan)
         if w is not None and v["ms_per_step"] > 0:
@@ -491,6 +491,28 @@ def main():
             v["unit"] = {"flop": "TFLOP/s", "op": "TOP/s", "byte": "GB/s"}[u]
             v["peak"] = PEAK["hbm_gbs"] if u == "byte" else PEAK[pk]
             v["frac"] = v["achieved"] / v["peak"]
+    # X^T X of the int8 digit-slice Hessian as the flops of the product it
+    # stands for (n i (i+1), symmetric half): its rate against the fp64 MFMA
+    # peak, the instruction the exact products use
+    if "hessian_split8" in breakdown and breakdown["hessian_split8"]["ms_per_step"] > 0:
+        xf = sum(h.n * h.dim * (h.dim + 1) for h in plan if h.split8)
+        eq = xf / (breakdown["hessian_split8"]["ms_per_step"] / 1000.0) / 1e12
+        breakdown["hessian_split8"]["xxt_tflops"] = eq
+        breakdown["hessian_split8"]["xxt_frac_vs_f64_mfma"] = eq / PEAK["f64_mfma"]
+        if roofline is not None and roofline.get("kernel") == "hessian_split8":
+            xeq = xf / per_step_s / 1e12
+            roofline["xxt_tflops"] = xeq
+            roofline["xxt_frac_vs_f64_mfma"] = xeq / PEAK["f64_mfma"]
+    # device time per phase (kernel classes summed; the inputs' streams
+    # overlap, so these add up to more than the step) and weights per second
+    # of the quantize phase alone, U given
+    phase_of = {"hessian": "accumulate", "prepare": "prepare", "chol": "prepare",
+                "trtri": "prepare", "minpivot": "prepare", "quant": "quantize"}
+    phase_ms = {"accumulate": 0.0, "prepare": 0.0, "quantize": 0.0}
+    for k, v in breakdown.items():
+        ph = phase_of.get(k.split("_")[0])
+        if ph:
+            phase_ms[ph] += v["ms_per_step"]
 
     cpu = None
     if not args.no_cpu_baseline and args.order == "workload":
@@ -525,6 +547,9 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": breakdown,
+        "phases_device_ms_per_step": phase_ms,
+        "quantize_only_weights_per_s": (weights / (phase_ms["quantize"] / 1000.0)
+                                        if phase_ms["quantize"] > 0 else None),
     }
     print(json.dumps(out), flush=True)
 
