@@ -58,6 +58,16 @@ def test_workspace_sizes():
     assert p >= 2 * 640 * 640 * 8
     assert g.hessian_workspace_bytes(576, 2048) > 0
     assert g.hessian_workspace_bytes(28672, 65536) == 0  # enough tiles, no split
+    # split8: column maxima and exponents, four int8 digit planes padded to
+    # 128 features x 64 tokens, and partial tiles only when split
+    assert g.hessian_split8_workspace_bytes(0, 2048) == 0
+    assert g.hessian_split8_workspace_bytes(64, 0) == 0
+    s = g.hessian_split8_workspace_bytes(4864, 2048)  # 741 tiles: no token split
+    assert 4 * 4864 * 2048 <= s <= 4 * 4864 * 2048 + 2 * 256 + 8 * 4992 + 4 * 4992 * 2048
+    assert s == g.hessian_split8_workspace_bytes(4864, 2048)
+    # more than 16384 tokens per call always splits, so partial tiles appear
+    big = g.hessian_split8_workspace_bytes(1024, 40000)
+    assert big > 4 * 1024 * 40000 + 3 * 36 * 128 * 128 * 8 - 1
 
 
 FAKE = C.c_void_p(0x10000)  # never dereferenced: validation fails first
@@ -109,6 +119,12 @@ def test_invalid_arguments_rejected_on_host():
     assert ha(FAKE, -1, FAKE, 10, 8, 0, NULL, 0, NULL) == g.GPTQ_EINVAL
     assert ha(FAKE, 8, FAKE, 10, 8, 4, NULL, 0, NULL) == g.GPTQ_EINVAL  # unknown flag
     assert ha(NULL, 8, FAKE, 0, 8, 2, NULL, 0, NULL) == g.GPTQ_EINVAL  # overwrite needs S
+    assert ha(FAKE, 8, FAKE, 10, 8, 64, NULL, 0, NULL) == g.GPTQ_EINVAL  # unknown flag
+    # split8 needs its workspace (checked before any launch)
+    assert ha(FAKE, 8, FAKE, 10, 8, 32, NULL, 0, NULL) == g.GPTQ_EWORKSPACE
+    need = g.hessian_split8_workspace_bytes(8, 10)
+    assert ha(FAKE, 8, FAKE, 10, 8, 32, FAKE, need - 1, NULL) == g.GPTQ_EWORKSPACE
+    assert ha(FAKE, 8, FAKE, 10, 7, 32, FAKE, need, NULL) == g.GPTQ_EINVAL  # ldx < i
 
 
 def test_profile_api_without_launches():
