@@ -48,6 +48,14 @@ Readings of what the pages leave open (each listed in the design doc):
   ties included).
 * Per-row loss: sum_j e_j^2 with e_j = (w~_j - q_j)/U[j,j]; this equals
   (w-q) H (w-q)^T for the damped, permuted H.
+* SSQR ([BABAI] 3, "Skalengerechte SpQR"; the page names the scheme and its
+  binary search, and prints no rule): a weight whose level would fall
+  outside [0, maxq] is an outlier and is kept as its current value rounded to
+  fp16 (only that rounding error propagates); one factor alpha per layer
+  multiplies every group's min-max scale, scale = fp16(alpha * (xmax -
+  xmin)/maxq), with the zero point of the unscaled grid, so the grid shrinks
+  about 0; the search bisects alpha for the smallest value whose outlier
+  fraction is at most the target.
 """
 from __future__ import annotations
 
@@ -61,7 +69,7 @@ __all__ = [
     "damping_lambda", "damped_diagonal", "damped_hessian", "act_order_from_diag", "act_order_perm", "min_pivot_order", "permute_sym", "hinv_upper", "fp16_round", "group_grid",
     "gptq_sweep", "gptq_layer", "rtn_quantize", "dequantize_sweep",
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
-    "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups",
+    "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups", "group_grid_ssqr", "ssqr_search",
 ]
 
 F64 = np.float64
@@ -238,6 +246,35 @@ def group_grid(V, bits):
     return scale, zero
 
 
+def group_grid_ssqr(V, bits, alpha):
+    """SSQR grid: the min-max step times ``alpha`` (fp16-rounded), the zero
+    point of the unscaled grid. Degenerate (scale 1, zero 0) when
+    xmax == xmin or either step rounds to fp16 zero."""
+    maxq = (1 << bits) - 1
+    V = np.asarray(V, dtype=F64)
+    xmin = np.minimum(V.min(axis=1), 0.0)
+    xmax = np.maximum(V.max(axis=1), 0.0)
+    step = (xmax - xmin) / maxq
+    with np.errstate(over="ignore"):
+        s1 = fp16_round(step)
+        scale = fp16_round(alpha * step)
+    if not (np.all(np.isfinite(s1)) and np.all(np.isfinite(scale))):
+        raise NonFinite("group scale overflows fp16")
+    degenerate = (xmax == xmin) | (s1 == 0.0) | (scale == 0.0)
+    zero = np.clip(np.rint(-xmin / np.where(degenerate, 1.0, s1)), 0, maxq)
+    return np.where(degenerate, 1.0, scale), np.where(degenerate, 0.0, zero)
+
+
+def _quantize_ssqr(v, scale, zero, maxq):
+    """(stored code, dequantized value, outlier mask): the level outside
+    [0, maxq] makes an outlier, kept as fp16(v); its stored code is the
+    clamped one."""
+    code = np.rint(v / scale) + zero
+    out = (code < 0) | (code > maxq)
+    dq = np.where(out, fp16_round(v), scale * (code - zero))
+    return np.clip(code, 0, maxq), dq, out
+
+
 def _quantize(v, scale, zero, maxq, clip):
     q = np.rint(v / scale) + zero
     if clip:
@@ -256,7 +293,7 @@ def num_groups(cols, group_size):
 # --------------------------------------------------------------------------
 
 def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
-               block=None):
+               block=None, ssqr_alpha=None):
     """Sweep the columns of Wp (already in sweep order) with the factor U.
 
     Strict form (``block=None``): after column j is rounded, its scaled error
@@ -265,7 +302,9 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
     update reaches only the block; the remaining columns receive
     E[:, block] @ U[block, rest] when the block ends — the same sums in
     another order. ``static_grid=(scales, zeros)`` [rows x groups] fixes the
-    grid instead of taking it at each group start.
+    grid instead of taking it at each group start. ``ssqr_alpha`` runs the
+    SSQR rule (grid step times alpha, out-of-grid levels kept as fp16
+    outliers) and adds ``outlier`` (bool) and ``outlier_vals`` [rows x cols].
 
     Returns dict with codes (sweep order, int64), scales, zeros
     [rows x groups], E [rows x cols], row_loss [rows], deq (dequantized).
@@ -287,20 +326,27 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
     scales = np.zeros((rows, ng), dtype=F64)
     zeros = np.zeros((rows, ng), dtype=F64)
     loss = np.zeros(rows, dtype=F64)
+    ssqr = ssqr_alpha is not None
+    outl = np.zeros((rows, cols), dtype=bool)
     step = cols if block is None else block
     for j0 in range(0, cols, step):
         j1 = min(j0 + step, cols)
         for j in range(j0, j1):
             g = j // gs
             if j % gs == 0:
-                if static_grid is None:
+                if ssqr:
+                    s, z = group_grid_ssqr(W[:, j:min(j + gs, cols)], bits, ssqr_alpha)
+                elif static_grid is None:
                     s, z = group_grid(W[:, j:min(j + gs, cols)], bits)
                 else:
                     s = np.asarray(static_grid[0], dtype=F64)[:, g]
                     z = np.asarray(static_grid[1], dtype=F64)[:, g]
                 scales[:, g] = s
                 zeros[:, g] = z
-            q, dq = _quantize(W[:, j], scales[:, g], zeros[:, g], maxq, clip)
+            if ssqr:
+                q, dq, outl[:, j] = _quantize_ssqr(W[:, j], scales[:, g], zeros[:, g], maxq)
+            else:
+                q, dq = _quantize(W[:, j], scales[:, g], zeros[:, g], maxq, clip)
             codes[:, j] = q.astype(np.int64)
             deq[:, j] = dq
             e = (W[:, j] - dq) / U[j, j]
@@ -309,12 +355,17 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
             W[:, j + 1:j1] -= np.outer(e, U[j, j + 1:j1])
         if j1 < cols:
             W[:, j1:] -= E[:, j0:j1] @ U[j0:j1, j1:]
-    return {"codes": codes, "scales": scales, "zeros": zeros, "E": E,
-            "row_loss": loss, "deq": deq}
+    res = {"codes": codes, "scales": scales, "zeros": zeros, "E": E,
+           "row_loss": loss, "deq": deq}
+    if ssqr:
+        res["outlier"] = outl
+        res["outlier_vals"] = np.where(outl, deq, 0.0)
+    return res
 
 
 def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
-               act_order=False, clip=True, block=None, min_pivot=False):
+               act_order=False, clip=True, block=None, min_pivot=False,
+               ssqr_alpha=None):
     """The whole layer: damping, optional act-order (or min-pivot order), U,
     sweep, un-permute.
 
@@ -338,14 +389,49 @@ def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
         perm = np.arange(cols, dtype=np.int64)
     Hp = permute_sym(H, perm)
     U = hinv_upper(Hp)
-    res = gptq_sweep(Wd[:, perm], U, bits, group_size, clip=clip, block=block)
+    res = gptq_sweep(Wd[:, perm], U, bits, group_size, clip=clip, block=block,
+                     ssqr_alpha=ssqr_alpha)
     codes = np.empty_like(res["codes"])
     codes[:, perm] = res["codes"]
+    if ssqr_alpha is not None:  # outliers back to the original column order
+        for key in ("outlier", "outlier_vals"):
+            a = np.empty_like(res[key])
+            a[:, perm] = res[key]
+            res[key] = a
     g_idx = np.empty(cols, dtype=np.int64)
     g_idx[perm] = np.arange(cols) // group_size
     res.update({"codes_sweep": res["codes"], "codes": codes, "g_idx": g_idx,
                 "perm": perm, "U": U, "Hp": Hp})
     return res
+
+
+def ssqr_search(Wp, U, bits, group_size, target, *, iters=12, lo=1.0 / 64, hi=1.0,
+                block=None):
+    """[BABAI] 3 (SSQR): bisection on the layer's scale factor alpha for the
+    smallest alpha whose outlier fraction is at most ``target``. The upper
+    end is tried first; if even it exceeds the target it is returned. Each
+    probe is a full sweep (outliers depend on the propagated values).
+    Returns (alpha, the sweep at alpha, the probes [(alpha, fraction)])."""
+    Wp = np.asarray(Wp, dtype=F64)
+    n = Wp.size
+
+    def probe(a):
+        r = gptq_sweep(Wp, U, bits, group_size, block=block, ssqr_alpha=a)
+        return r, float(r["outlier"].sum()) / n
+
+    best, f = probe(hi)
+    probes = [(hi, f)]
+    if f > target:
+        return hi, best, probes
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        r, f = probe(mid)
+        probes.append((mid, f))
+        if f <= target:
+            hi, best = mid, r
+        else:
+            lo = mid
+    return hi, best, probes
 
 
 def dequantize_sweep(codes_sweep, scales, zeros, group_size):

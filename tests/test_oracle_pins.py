@@ -414,3 +414,106 @@ def test_generator_deterministic_and_chunk_independent():
     assert w1.dtype == np.float16 and np.array_equal(w1, w2)
     sd = w1.astype(np.float64).std(axis=1)
     np.testing.assert_allclose(sd, 0.02, rtol=0.01)
+
+
+# ---------------------------------------------------------------- SSQR
+
+def _ssqr_element(v, xmin, xmax, bits, alpha):
+    """One weight under the SSQR rule, from its group's range, with Python
+    floats and numpy's fp16 (the reading: step times alpha, zero point of the
+    unscaled step, out-of-grid levels kept as fp16)."""
+    maxq = (1 << bits) - 1
+    step = (xmax - xmin) / maxq
+    s1 = float(np.float16(step))
+    sc = float(np.float16(alpha * step))
+    if xmax == xmin or s1 == 0.0 or sc == 0.0:
+        sc, zero = 1.0, 0.0
+    else:
+        zero = min(max(float(np.rint(-xmin / s1)), 0.0), float(maxq))
+    code = float(np.rint(v / sc)) + zero
+    if code < 0 or code > maxq:
+        return True, float(np.float16(v)), sc, zero
+    return False, sc * (code - zero), sc, zero
+
+
+@pytest.mark.parametrize("alpha", [1.0, 0.6, 0.25])
+def test_ssqr_diagonal_hessian_elementwise(alpha):
+    """Diagonal H: nothing propagates, so every weight follows the rule on
+    its own group's range."""
+    rng = np.random.default_rng(7)
+    W = (0.02 * rng.standard_t(4, size=(6, 160))).astype(np.float16)
+    S = np.diag(rng.uniform(0.5, 2.0, 160)) * 100
+    res = O.gptq_layer(W, S, 100, bits=3, group_size=64, ssqr_alpha=alpha)
+    Wd = W.astype(np.float64)
+    for r in range(6):
+        for j in range(160):
+            g0 = (j // 64) * 64
+            grp = Wd[r, g0:g0 + 64]
+            out, dq, sc, zero = _ssqr_element(Wd[r, j], min(grp.min(), 0.0), max(grp.max(), 0.0),
+                                              3, alpha)
+            assert res["outlier"][r, j] == out
+            assert res["deq"][r, j] == dq
+            assert res["scales"][r, j // 64] == sc and res["zeros"][r, j // 64] == zero
+            if out:
+                assert res["outlier_vals"][r, j] == dq
+
+
+def test_ssqr_all_outliers_is_lossless():
+    """A grid far finer than every weight: all weights are outliers, each is
+    kept exactly (fp16 inputs), nothing propagates, and the loss is 0 for any
+    H."""
+    X, _, S, n = _rand_problem(8, 96, 200, 8)
+    rng = np.random.default_rng(4)
+    W = (rng.choice([-1, 1], size=(8, 96)) * rng.uniform(0.01, 0.05, (8, 96))).astype(np.float16)
+    res = O.gptq_layer(W, S, n, bits=4, group_size=32, act_order=True, ssqr_alpha=1e-4)
+    assert res["outlier"].all()
+    assert np.array_equal(res["outlier_vals"], W.astype(np.float64))
+    assert np.all(res["row_loss"] == 0.0)
+
+
+def test_ssqr_loss_identity_and_outlier_values():
+    """With some outliers: sum e^2 = (w - deq) H (w - deq)^T, and every
+    outlier's value is an fp16 number."""
+    X, W, S, n = _rand_problem(11, 60, 128, 10)
+    res = O.gptq_layer(W, S, n, bits=3, group_size=32, act_order=True, ssqr_alpha=0.45)
+    assert 0 < res["outlier"].sum() < res["outlier"].size
+    perm = res["perm"]
+    D = W.astype(np.float64)[:, perm] - res["deq"]
+    np.testing.assert_allclose(res["row_loss"], O.loss_quadratic(D, res["Hp"]), rtol=1e-10)
+    v = res["outlier_vals"][res["outlier"]]
+    assert np.array_equal(v, v.astype(np.float16).astype(np.float64))
+
+
+def test_ssqr_alpha_one_rows_without_outliers_equal_gptq():
+    """alpha = 1 is the min-max grid: a row with no outlier took no clamped
+    level either, so it equals the plain sweep in codes, grid and loss."""
+    X, W, S, n = _rand_problem(12, 60, 128, 24)
+    a = O.gptq_layer(W, S, n, bits=2, group_size=32, ssqr_alpha=1.0)
+    b = O.gptq_layer(W, S, n, bits=2, group_size=32)
+    clean = ~a["outlier"].any(axis=1)
+    assert clean.sum() >= 1
+    for key in ("codes", "scales", "zeros", "row_loss"):
+        assert np.array_equal(a[key][clean], b[key][clean]), key
+
+
+def test_ssqr_search_bisection():
+    """The returned alpha meets the target; the probes keep the bisection
+    invariant (every failing probe below every passing one is not required,
+    but each probe halves the interval around the returned value)."""
+    X, W, S, n = _rand_problem(13, 60, 128, 16)
+    H = O.damped_hessian(S, n, 0.01)
+    U = O.hinv_upper(H)
+    Wp = W.astype(np.float64)
+    target = 0.02
+    alpha, best, probes = O.ssqr_search(Wp, U, 3, 32, target, iters=10)
+    assert best["outlier"].mean() <= target
+    assert probes[0][0] == 1.0
+    lo, hi = 1.0 / 64, 1.0
+    for a, f in probes[1:]:
+        assert a == 0.5 * (lo + hi)
+        if f <= target:
+            hi = a
+        else:
+            lo = a
+    assert alpha == hi and hi - lo == (1.0 - 1.0 / 64) / 2 ** 10
+    assert any(f > target for _, f in probes)  # the target was binding
