@@ -173,6 +173,48 @@ gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, i
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * SSQR — The Geometry of LLM Quantization, section 3 ("Skalengerechte SpQR":
+ * outliers that would overflow the grid are kept as sparse floating-point
+ * values; a binary search on the scales meets a target outlier density).
+ * The page prints no rule; the one taken here:
+ *   step_g = fp16(alpha * (xmax - xmin) / maxq) for every group (xmin/xmax as
+ *   in the plain grid), zero point = that of the unscaled grid (so the grid
+ *   shrinks about 0 for alpha < 1); a weight whose level rint(v/step) + zero
+ *   falls outside [0, maxq] is an outlier: it is kept as fp16(v) (its current,
+ *   error-updated value) and only that fp16 rounding error propagates; its
+ *   stored code is the clamped level. alpha = 1 is the min-max grid.
+ * gptq_quantize_layer_ssqr: as gptq_quantize_layer (same workspace), plus
+ *   alpha       in (0, 16], else GPTQ_EINVAL;
+ *   outlier_mask (out, u8 [rows x cols], original column order): 1 = outlier;
+ *   outlier_vals (out, fp16 bits [rows x cols]): fp16(v) at outliers, 0 else;
+ *   n_outliers  (host, may be NULL): the count, read after a synchronize
+ *               (GPTQ_EINVAL with GPTQ_FLAG_NO_SYNC).
+ *   GPTQ_FLAG_NO_CLIP is not accepted (the rule above replaces clipping).
+ * gptq_ssqr_search: bisection on alpha in [alpha_lo, alpha_hi] (0 < lo < hi
+ *   <= 16) for the smallest alpha whose outlier fraction (count / (rows *
+ *   cols)) is at most target (in [0, 1]): alpha_hi is tried first and, if it
+ *   already exceeds the target, returned; else iters (<= 60) midpoints are
+ *   tried, keeping hi at the passing ones. Each probe is one full sweep into
+ *   the output buffers, synchronized to read its count; on return they hold
+ *   the sweep at *alpha_out (host), and *n_outliers (host, may be NULL) its
+ *   count. flags must be 0.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_quantize_layer_ssqr(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                     const float* U, const int32_t* perm, int bits,
+                                     int group_size, uint32_t flags, double alpha,
+                                     uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                     int32_t* g_idx, double* row_loss, uint8_t* outlier_mask,
+                                     uint16_t* outlier_vals, uint64_t* n_outliers, void* ws,
+                                     size_t ws_bytes, void* stream);
+gptq_status gptq_ssqr_search(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                             const float* U, const int32_t* perm, int bits, int group_size,
+                             uint32_t flags, double target, int iters, double alpha_lo,
+                             double alpha_hi, double* alpha_out, uint8_t* codes,
+                             uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                             double* row_loss, uint8_t* outlier_mask, uint16_t* outlier_vals,
+                             uint64_t* n_outliers, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Status of the last gptq_prepare_hinv / gptq_quantize_layer call that used
  * workspace `ws` (a device pointer): synchronizes `stream` (the stream of that
  * call), then reads the status word the call left at the start of `ws`.

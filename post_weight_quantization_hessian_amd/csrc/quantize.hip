@@ -35,10 +35,14 @@ __device__ inline double quad_xor2(double v) { return dpp_f64<0x4E>(v); }
 __global__ void q_init_kernel(double* __restrict__ row_loss, int64_t rows,
                               const int32_t* __restrict__ perm, int32_t* __restrict__ invperm,
                               int32_t* __restrict__ g_idx, int64_t cols, int gs,
-                              unsigned* __restrict__ status) {
+                              unsigned* __restrict__ status,
+                              unsigned long long* __restrict__ ocount) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t nthr = (int64_t)gridDim.x * blockDim.x;
-  if (tid == 0) *status = 0u;
+  if (tid == 0) {
+    *status = 0u;
+    *ocount = 0ull;
+  }
   for (int64_t r = tid; r < rows; r += nthr) row_loss[r] = 0.0;
   for (int64_t k = tid; k < cols; k += nthr) {
     if (perm) invperm[k] = -1;
@@ -250,7 +254,12 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
 __device__ inline double row_ror4(double v) { return dpp_f64<0x124>(v); }
 __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 
-template <int GS>
+// SSQR (The Geometry of LLM Quantization, section 3): the group's step is
+// alpha times the min-max one, with the zero point of the unscaled step, and
+// a level outside [0, maxq] makes an outlier: its current value is kept as
+// fp16 (mask 1, value in ovals at the original column, only the fp16
+// rounding propagates) and its stored code is the clamped one.
+template <int GS, bool SSQR>
 __global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
     const double* __restrict__ part, int P, int64_t part_stride,
@@ -258,7 +267,9 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     int bits, float* __restrict__ E, int64_t lde, uint8_t* __restrict__ codes, int64_t ldc,
     uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros, int64_t ldg,
     double* __restrict__ row_loss, unsigned* __restrict__ status, bool clip, bool late, int nsweep,
-    int64_t gj0, int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart) {
+    int64_t gj0, int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart, double alpha,
+    uint8_t* __restrict__ omask, uint16_t* __restrict__ ovals, const int32_t* __restrict__ operm,
+    int64_t cols, unsigned long long* __restrict__ ocount) {
   // U slab plus three rows of zero padding: the slot reads of a column run up
   // to 112 entries past its row end, into the next row or the padding, only
   // for slots past the block end whose values are never used; rows are read
@@ -426,6 +437,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   __syncthreads();
 
   double scale = 1.0, rscale = 1.0, zero = 0.0, loss = 0.0;
+  double nout = 0.0;  // SSQR: outliers of this lane's columns
   // range of the level k = code - zero: [-zero, maxq - zero], or unbounded
   // without clipping (the no-clipping regime of The Geometry of LLM
   // Quantization 2.3, whose codes are stored saturated to [0, 255])
@@ -466,12 +478,18 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       uint16_t sh = f64_to_f16_rne((mx - mn) / maxq);
       scale = f16_to_f64(sh);
       if ((sh & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
-      if (mx == mn || scale == 0.0) {
+      // SSQR: the step used is fp16(alpha * step); the zero point comes from
+      // the unscaled one (scale, here), so the grid shrinks about 0
+      const uint16_t sha = SSQR ? f64_to_f16_rne(alpha * ((mx - mn) / maxq)) : sh;
+      const double scale_a = SSQR ? f16_to_f64(sha) : scale;
+      if (mx == mn || scale == 0.0 || scale_a == 0.0) {
         scale = 1.0;
         sh = 0x3c00;
         zero = 0.0;
       } else {
         zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
+        scale = scale_a;
+        sh = sha;
       }
       rscale = 1.0 / scale;
       klo = clip ? -zero : -1e300;
@@ -482,8 +500,11 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         zeros[r * ldg + g] = f64_to_f16_rne(zero);
       }
     }
-    // the residual d and clamped level k of the column this lane owns
+    // the residual d and clamped level k of the column this lane owns (SSQR:
+    // whether it is an outlier, and its fp16 value)
     double d_own = 0.0, k_own = 0.0;
+    bool o_own = false;
+    uint16_t h_own = 0;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       if (16 * tt + jj < bw) {
@@ -501,8 +522,16 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
         // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
         const double v = w[0];
-        const double k = fmin(fmax(rint(v * rscale), klo), khi);
-        const double d = fma(-scale, k, v);
+        const double kr = rint(v * rscale);
+        const double k = fmin(fmax(kr, klo), khi);
+        double d = fma(-scale, k, v);
+        bool out = false;
+        uint16_t vh = 0;
+        if (SSQR) {
+          out = kr < klo || kr > khi;
+          vh = f64_to_f16_rne(v);
+          if (out) d = v - f16_to_f64(vh);
+        }
         double db;
         switch (jj) {
           case 0: db = row_bcast<0>(d); break;
@@ -524,6 +553,10 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         }
         d_own = q == jj ? d : d_own;
         k_own = q == jj ? k : k_own;
+        if (SSQR) {
+          o_own = q == jj ? out : o_own;
+          h_own = q == jj ? vh : h_own;
+        }
         // later columns: w -= d * U[j][c] / U[j][j]. Slot 0 of the lanes at
         // or before the pivot is dead (its slab entry, below the diagonal, is
         // 0); slots past the block end are dead too.
@@ -539,6 +572,14 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         codes[r * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero, 0.0), 255.0);
         E[r * lde + j0 + c] = (float)e;
         loss += e * e;
+        if (SSQR) {
+          const int64_t oc = operm ? (int64_t)operm[j0 + c] : j0 + c;
+          if (oc >= 0 && oc < cols) {  // a bad permutation is reported elsewhere
+            omask[r * cols + oc] = o_own ? 1 : 0;
+            ovals[r * cols + oc] = o_own ? h_own : (uint16_t)0;
+          }
+          nout += o_own ? 1.0 : 0.0;
+        }
       }
     }
 #pragma unroll
@@ -550,6 +591,13 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   loss += row_ror4(loss);
   loss += row_ror8(loss);
   if (rv && q == 0) row_loss[r] += loss;
+  if (SSQR) {
+    nout += quad_xor1(nout);
+    nout += quad_xor2(nout);
+    nout += row_ror4(nout);
+    nout += row_ror8(nout);
+    if (rv && q == 0 && nout > 0.0) atomicAdd(ocount, (unsigned long long)nout);
+  }
 }
 
 // ---------------------------------------------------------------- layout
@@ -557,7 +605,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
 struct QLayout {
   int64_t rows, cols, lde, ng;
   int pmax;
-  size_t off_status, off_invperm, off_wp, off_codes, off_E, off_part, off_wblk, total;
+  size_t off_status, off_count, off_invperm, off_wp, off_codes, off_E, off_part, off_wblk, total;
 };
 
 // Split-K factor of the update GEMM: about 512 workgroups in total.
@@ -583,6 +631,7 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
     return at;
   };
   L.off_status = take(4);
+  L.off_count = take(8);
   L.off_invperm = take(4 * (size_t)cols);
   L.off_wp = take(2 * (size_t)rows * cols);
   L.off_codes = take((size_t)rows * cols);
@@ -624,15 +673,27 @@ struct SweepArgs {
   int gbw;
   int64_t gks, gk_end;
   double* gpart;
+  // SSQR (alpha > 0): outputs at the original columns, outlier counter
+  double alpha;
+  uint8_t* omask;
+  uint16_t* ovals;
+  const int32_t* operm;
+  int64_t cols;
+  unsigned long long* ocount;
 };
 
 template <int GS>
 static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
-  GPTQ_LAUNCH(K_Q_SWEEP, st,
-              q_sweep_kernel<GS><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(
-                  a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0,
-                  a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg, a.row_loss,
-                  a.status, a.clip, a.late, a.nsweep, a.gj0, a.gbw, a.gks, a.gk_end, a.gpart));
+#define Q_SWEEP(SS)                                                                            \
+  GPTQ_LAUNCH(K_Q_SWEEP, st,                                                                   \
+              (q_sweep_kernel<GS, SS><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(                  \
+                  a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0, \
+                  a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg,          \
+                  a.row_loss, a.status, a.clip, a.late, a.nsweep, a.gj0, a.gbw, a.gks,         \
+                  a.gk_end, a.gpart, a.alpha, a.omask, a.ovals, a.operm, a.cols, a.ocount)))
+  if (a.alpha > 0.0) Q_SWEEP(true);
+  else Q_SWEEP(false);
+#undef Q_SWEEP
   return GPTQ_OK;
 }
 
@@ -647,24 +708,18 @@ extern "C" size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int 
   return q_layout(rows, cols, group_size).total;
 }
 
-extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
-                                           const float* U, const int32_t* perm, int bits,
-                                           int group_size, uint32_t flags, uint8_t* codes,
-                                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
-                                           double* row_loss, void* ws, size_t ws_bytes,
-                                           void* stream) {
-  if (rows < 0 || cols < 0) return GPTQ_EINVAL;
-  if (flags & ~(GPTQ_FLAG_NO_SYNC | GPTQ_FLAG_NO_CLIP)) return GPTQ_EINVAL;
-  const bool clip = !(flags & GPTQ_FLAG_NO_CLIP);
-  if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
-  if (rows == 0 || cols == 0) return GPTQ_OK;
-  if (!W || !U || !codes || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
-  if (cols > (int64_t)1 << 20 || rows > (int64_t)1 << 26) return GPTQ_EINVAL;
+// The whole sweep of a layer; alpha > 0 runs the SSQR rule with its outputs.
+// Arguments are validated by the callers; returns after enqueueing.
+static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                    const float* U, const int32_t* perm, int bits, int group_size,
+                                    bool clip, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                    int32_t* g_idx, double* row_loss, double alpha,
+                                    uint8_t* omask, uint16_t* ovals, void* ws,
+                                    hipStream_t st) {
   const QLayout L = q_layout(rows, cols, group_size);
-  if (!ws || ws_bytes < L.total) return GPTQ_EWORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
   unsigned* status = (unsigned*)(base + L.off_status);
+  unsigned long long* ocount = (unsigned long long*)(base + L.off_count);
   int32_t* invperm = (int32_t*)(base + L.off_invperm);
   uint16_t* Wp = (uint16_t*)(base + L.off_wp);
   uint8_t* codes_s = (uint8_t*)(base + L.off_codes);
@@ -677,7 +732,7 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
     const unsigned nb = (unsigned)std::min<int64_t>(cdiv(n, 256), 4096);
     GPTQ_LAUNCH(K_Q_INIT, st,
                 q_init_kernel<<<nb, 256, 0, st>>>(row_loss, rows, perm, invperm, g_idx, cols,
-                                                  group_size, status));
+                                                  group_size, status, ocount));
   }
   const uint16_t* Wsrc = W;
   int64_t ldws = ldw;
@@ -737,7 +792,7 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
     }
     SweepArgs a{nw, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
                 bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, clip,
-                late, 0, 0, 0, 0, pn};
+                late, 0, 0, 0, 0, pn, alpha, omask, ovals, perm, cols, ocount};
     ep = emb_max > 0 ? 0 : -1;
     if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
       // next block's sum over l < j0 (the errors of blocks < b), in as few
@@ -772,6 +827,143 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
                 q_finalize_kernel<<<grid, 256, 0, st>>>(codes_s, invperm, rows, cols, group_size,
                                                         codes, g_idx, status));
   }
+  return GPTQ_OK;
+}
+
+static gptq_status quantize_check(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                  const float* U, int bits, int group_size, const uint8_t* codes,
+                                  const uint16_t* scales, const uint16_t* zeros,
+                                  const double* row_loss) {
+  if (rows < 0 || cols < 0) return GPTQ_EINVAL;
+  if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
+  if (rows == 0 || cols == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
+  if (cols > (int64_t)1 << 20 || rows > (int64_t)1 << 26) return GPTQ_EINVAL;
+  return GPTQ_OK;
+}
+
+extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                           const float* U, const int32_t* perm, int bits,
+                                           int group_size, uint32_t flags, uint8_t* codes,
+                                           uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                                           double* row_loss, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  if (flags & ~(GPTQ_FLAG_NO_SYNC | GPTQ_FLAG_NO_CLIP)) return GPTQ_EINVAL;
+  gptq_status c = quantize_check(W, rows, cols, ldw, U, bits, group_size, codes, scales, zeros,
+                                 row_loss);
+  if (c != GPTQ_OK || rows == 0 || cols == 0) return c;
+  if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
+  c = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size,
+                       !(flags & GPTQ_FLAG_NO_CLIP), codes, scales, zeros, g_idx, row_loss, 0.0,
+                       nullptr, nullptr, ws, (hipStream_t)stream);
+  if (c != GPTQ_OK) return c;
   if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
   return gptq_workspace_status(ws, stream);
+}
+
+// SSQR: the outlier count of the last sweep on this workspace (synchronizes).
+static gptq_status ssqr_count(void* ws, int64_t rows, int64_t cols, int gs, hipStream_t st,
+                              uint64_t* n) {
+  const QLayout L = q_layout(rows, cols, gs);
+  unsigned long long h = 0;
+  GPTQ_HIP(hipMemcpyAsync(&h, (char*)ws + L.off_count, sizeof(h), hipMemcpyDeviceToHost, st));
+  GPTQ_HIP(hipStreamSynchronize(st));
+  *n = (uint64_t)h;
+  return GPTQ_OK;
+}
+
+extern "C" gptq_status gptq_quantize_layer_ssqr(const uint16_t* W, int64_t rows, int64_t cols,
+                                                int64_t ldw, const float* U, const int32_t* perm,
+                                                int bits, int group_size, uint32_t flags,
+                                                double alpha, uint8_t* codes, uint16_t* scales,
+                                                uint16_t* zeros, int32_t* g_idx,
+                                                double* row_loss, uint8_t* outlier_mask,
+                                                uint16_t* outlier_vals, uint64_t* n_outliers,
+                                                void* ws, size_t ws_bytes, void* stream) {
+  if (flags & ~GPTQ_FLAG_NO_SYNC) return GPTQ_EINVAL;
+  if (!(alpha > 0.0 && alpha <= 16.0)) return GPTQ_EINVAL;
+  if ((flags & GPTQ_FLAG_NO_SYNC) && n_outliers) return GPTQ_EINVAL;
+  gptq_status c = quantize_check(W, rows, cols, ldw, U, bits, group_size, codes, scales, zeros,
+                                 row_loss);
+  if (c != GPTQ_OK) return c;
+  if (rows == 0 || cols == 0) {
+    if (n_outliers) *n_outliers = 0;
+    return GPTQ_OK;
+  }
+  if (!outlier_mask || !outlier_vals) return GPTQ_EINVAL;
+  if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  c = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size, true, codes, scales, zeros,
+                       g_idx, row_loss, alpha, outlier_mask, outlier_vals, ws, st);
+  if (c != GPTQ_OK) return c;
+  if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
+  if (n_outliers) {
+    c = ssqr_count(ws, rows, cols, group_size, st, n_outliers);
+    if (c != GPTQ_OK) return c;
+  }
+  return gptq_workspace_status(ws, stream);
+}
+
+extern "C" gptq_status gptq_ssqr_search(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                        const float* U, const int32_t* perm, int bits,
+                                        int group_size, uint32_t flags, double target, int iters,
+                                        double alpha_lo, double alpha_hi, double* alpha_out,
+                                        uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                        int32_t* g_idx, double* row_loss, uint8_t* outlier_mask,
+                                        uint16_t* outlier_vals, uint64_t* n_outliers, void* ws,
+                                        size_t ws_bytes, void* stream) {
+  if (flags != 0) return GPTQ_EINVAL;
+  if (!(target >= 0.0 && target <= 1.0) || iters < 0 || iters > 60) return GPTQ_EINVAL;
+  if (!(alpha_lo > 0.0 && alpha_lo < alpha_hi && alpha_hi <= 16.0)) return GPTQ_EINVAL;
+  if (!alpha_out) return GPTQ_EINVAL;
+  gptq_status c = quantize_check(W, rows, cols, ldw, U, bits, group_size, codes, scales, zeros,
+                                 row_loss);
+  if (c != GPTQ_OK) return c;
+  if (rows == 0 || cols == 0) {
+    *alpha_out = alpha_hi;
+    if (n_outliers) *n_outliers = 0;
+    return GPTQ_OK;
+  }
+  if (!outlier_mask || !outlier_vals) return GPTQ_EINVAL;
+  if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  const double n = (double)rows * (double)cols;
+  // every probe is a full sweep into the caller's outputs; the outputs are
+  // left from the returned alpha (swept again at the end if the last probe
+  // was another one)
+  auto probe = [&](double a, uint64_t* cnt) -> gptq_status {
+    gptq_status r = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size, true, codes,
+                                     scales, zeros, g_idx, row_loss, a, outlier_mask,
+                                     outlier_vals, ws, st);
+    if (r != GPTQ_OK) return r;
+    r = ssqr_count(ws, rows, cols, group_size, st, cnt);
+    if (r != GPTQ_OK) return r;
+    return gptq_workspace_status(ws, stream);
+  };
+  double lo = alpha_lo, hi = alpha_hi, last = hi;
+  uint64_t cnt = 0, best = 0;
+  c = probe(hi, &cnt);
+  if (c != GPTQ_OK) return c;
+  best = cnt;
+  if ((double)cnt / n <= target) {
+    for (int it = 0; it < iters; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      c = probe(mid, &cnt);
+      if (c != GPTQ_OK) return c;
+      last = mid;
+      if ((double)cnt / n <= target) {
+        hi = mid;
+        best = cnt;
+      } else {
+        lo = mid;
+      }
+    }
+    if (last != hi) {
+      c = probe(hi, &cnt);
+      if (c != GPTQ_OK) return c;
+    }
+  }
+  *alpha_out = hi;
+  if (n_outliers) *n_outliers = best;
+  return GPTQ_OK;
 }

@@ -40,6 +40,16 @@ EXPORTS = {
                                       C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_void_p,
                                       C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                       C.c_size_t, C.c_void_p]),
+    "gptq_quantize_layer_ssqr": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                           C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_uint32,
+                                           C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "gptq_ssqr_search": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
+                                   C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_double, C.c_int,
+                                   C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "gptq_workspace_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
@@ -236,6 +246,80 @@ def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, worksp
                                  _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_quantize_layer")
     return QuantizedLayer(codes, scales, zeros, g_idx, row_loss, bits, group_size)
+
+
+@dataclass
+class SSQRLayer:
+    layer: QuantizedLayer
+    outlier_mask: object  # uint8 [rows x cols], original column order, 1 = outlier
+    outlier_vals: object  # fp16  [rows x cols], the outlier's value (0 elsewhere)
+    n_outliers: int
+    alpha: float
+
+
+def _ssqr_args(W, U, perm, group_size):
+    torch = _torch()
+    _need(W, torch.float16, "W", 2)
+    _need(U, torch.float32, "U", 2)
+    rows, cols = W.shape
+    if U.shape != (cols, cols) or not U.is_contiguous():
+        raise ValueError("U must be a contiguous [cols x cols] tensor")
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    if perm is not None:
+        _need(perm, torch.int32, "perm", 1)
+        if perm.numel() != cols:
+            raise ValueError("perm must have cols entries")
+    ng = -(-cols // group_size) if group_size > 0 else 0
+    dev = W.device
+    outs = dict(codes=torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                scales=torch.empty((rows, ng), dtype=torch.float16, device=dev),
+                zeros=torch.empty((rows, ng), dtype=torch.float16, device=dev),
+                g_idx=torch.empty(cols, dtype=torch.int32, device=dev),
+                row_loss=torch.empty(rows, dtype=torch.float64, device=dev),
+                mask=torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+                vals=torch.empty((rows, cols), dtype=torch.float16, device=dev))
+    ws = _workspace(quantize_workspace_bytes(rows, cols, group_size), dev)
+    return rows, cols, outs, ws
+
+
+def quantize_layer_ssqr(W, U, perm=None, bits: int = 4, group_size: int = 128,
+                        alpha: float = 1.0) -> SSQRLayer:
+    """The sweep under the SSQR rule at scale factor ``alpha`` (synchronous):
+    out-of-grid levels kept as fp16 outliers, reported as a dense mask and
+    values in the original column order."""
+    rows, cols, o, ws = _ssqr_args(W, U, perm, group_size)
+    n = C.c_uint64(0)
+    st = lib.gptq_quantize_layer_ssqr(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols,
+                                      _ptr(U), _ptr(perm), int(bits), int(group_size), 0,
+                                      float(alpha), _ptr(o["codes"]), _ptr(o["scales"]),
+                                      _ptr(o["zeros"]), _ptr(o["g_idx"]), _ptr(o["row_loss"]),
+                                      _ptr(o["mask"]), _ptr(o["vals"]), C.byref(n), _ptr(ws),
+                                      ws.numel(), _stream())
+    _check(st, "gptq_quantize_layer_ssqr")
+    q = QuantizedLayer(o["codes"], o["scales"], o["zeros"], o["g_idx"], o["row_loss"], bits,
+                       group_size)
+    return SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(alpha))
+
+
+def ssqr_search(W, U, perm=None, bits: int = 4, group_size: int = 128, target: float = 0.01,
+                iters: int = 12, alpha_lo: float = 1.0 / 64, alpha_hi: float = 1.0) -> SSQRLayer:
+    """Bisection on the SSQR scale factor for the smallest alpha in
+    [alpha_lo, alpha_hi] whose outlier fraction is at most ``target``; the
+    result holds the sweep at that alpha."""
+    rows, cols, o, ws = _ssqr_args(W, U, perm, group_size)
+    n = C.c_uint64(0)
+    a = C.c_double(0.0)
+    st = lib.gptq_ssqr_search(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
+                              _ptr(perm), int(bits), int(group_size), 0, float(target),
+                              int(iters), float(alpha_lo), float(alpha_hi), C.byref(a),
+                              _ptr(o["codes"]), _ptr(o["scales"]), _ptr(o["zeros"]),
+                              _ptr(o["g_idx"]), _ptr(o["row_loss"]), _ptr(o["mask"]),
+                              _ptr(o["vals"]), C.byref(n), _ptr(ws), ws.numel(), _stream())
+    _check(st, "gptq_ssqr_search")
+    q = QuantizedLayer(o["codes"], o["scales"], o["zeros"], o["g_idx"], o["row_loss"], bits,
+                       group_size)
+    return SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(a.value))
 
 
 def workspace_status(workspace):

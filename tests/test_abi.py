@@ -127,6 +127,39 @@ def test_invalid_arguments_rejected_on_host():
     assert ha(FAKE, 8, FAKE, 10, 7, 32, FAKE, need, NULL) == g.GPTQ_EINVAL  # ldx < i
 
 
+def test_ssqr_arguments_rejected_on_host():
+    L = g.lib
+    C_ = C
+    n = C_.c_uint64(0)
+    a = C_.c_double(0.0)
+    q = L.gptq_quantize_layer_ssqr
+
+    def qs(alpha=0.5, flags=0, mask=FAKE, cnt=None, ws=FAKE, wsb=1 << 40):
+        return q(FAKE, 4, 8, 8, FAKE, NULL, 4, 16, flags, alpha, FAKE, FAKE, FAKE, NULL, FAKE,
+                 mask, FAKE, C_.byref(n) if cnt is None else cnt, ws, wsb, NULL)
+    assert qs(alpha=0.0) == g.GPTQ_EINVAL
+    assert qs(alpha=17.0) == g.GPTQ_EINVAL
+    assert qs(alpha=float("nan")) == g.GPTQ_EINVAL
+    assert qs(flags=g.GPTQ_FLAG_NO_CLIP) == g.GPTQ_EINVAL  # its own rule replaces clipping
+    assert qs(flags=g.GPTQ_FLAG_NO_SYNC) == g.GPTQ_EINVAL  # a count needs a synchronize
+    assert qs(mask=NULL) == g.GPTQ_EINVAL
+    assert qs(ws=NULL, wsb=0) == g.GPTQ_EWORKSPACE
+    s = L.gptq_ssqr_search
+
+    def ss(target=0.01, iters=8, lo=0.1, hi=1.0, flags=0, aout=None):
+        return s(FAKE, 4, 8, 8, FAKE, NULL, 4, 16, flags, target, iters, lo, hi,
+                 C_.byref(a) if aout is None else aout, FAKE, FAKE, FAKE, NULL, FAKE, FAKE,
+                 FAKE, C_.byref(n), FAKE, 1 << 40, NULL)
+    assert ss(target=-0.1) == g.GPTQ_EINVAL
+    assert ss(target=1.5) == g.GPTQ_EINVAL
+    assert ss(iters=61) == g.GPTQ_EINVAL
+    assert ss(lo=0.0) == g.GPTQ_EINVAL
+    assert ss(lo=1.0, hi=0.5) == g.GPTQ_EINVAL
+    assert ss(hi=17.0) == g.GPTQ_EINVAL
+    assert ss(flags=g.GPTQ_FLAG_NO_SYNC) == g.GPTQ_EINVAL
+    assert ss(aout=NULL) == g.GPTQ_EINVAL
+
+
 def test_profile_api_without_launches():
     g.profile_enable(True)
     r = g.profile_read()

@@ -1,0 +1,136 @@
+"""GPU: SSQR (The Geometry of LLM Quantization, section 3) against the oracle.
+
+Through the C ABI: the full path (Hessian, prepare, SSQR sweep) at fixed
+scale factors, with and without act-order, on ragged shapes; the outlier
+mask and values element by element; the all-outlier case (lossless); the
+bisection search against the oracle's; and the Qwen down projection's full
+shape at the alpha the search picks.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a HIP device", allow_module_level=True)
+
+import post_weight_quantization_hessian_amd.gptq as G  # noqa: E402
+from post_weight_quantization_hessian_amd import synth  # noqa: E402
+from tests.parity_util import compare_layer, to_numpy_layer  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def problem(rows, cols, n, seed):
+    rng = np.random.default_rng(seed)
+    X = (rng.standard_normal((n, cols)) + 0.8 * rng.standard_normal((n, 1))).astype(np.float32)
+    W = (0.02 * rng.standard_t(4, size=(rows, cols))).astype(np.float16)
+    return W, X
+
+
+def gpu_factor(X, act_order):
+    dim = X.shape[1]
+    S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
+    perm, U = G.prepare_hinv(S, X.shape[0], damp=0.01, act_order=act_order)
+    return perm if act_order else None, U
+
+
+def compare_ssqr(res, ref, name):
+    mask = res.outlier_mask.cpu().numpy().astype(bool)
+    vals = res.outlier_vals.cpu().numpy().astype(np.float64)
+    agree = float(np.mean(mask == ref["outlier"]))
+    say(f"{name}: outliers gpu {int(mask.sum())} oracle {int(ref['outlier'].sum())} "
+        f"mask agreement {agree:.6f}")
+    assert res.n_outliers == int(mask.sum())
+    assert agree >= 0.999
+    both = mask & ref["outlier"]
+    assert np.array_equal(vals[both], ref["outlier_vals"][both])
+    assert np.all(vals[~mask] == 0.0)
+    compare_layer(to_numpy_layer(res.layer), ref, name=name)
+
+
+@pytest.mark.parametrize("rows,cols,bits,gs,act,alpha", [
+    (64, 576, 4, 128, False, 0.5),
+    (37, 333, 3, 32, True, 0.7),
+    (130, 260, 2, 64, True, 1.0),
+    (200, 640, 4, 64, False, 0.3),
+    (1, 129, 4, 128, True, 0.6),
+])
+def test_ssqr_fixed_alpha_matches_oracle(rows, cols, bits, gs, act, alpha):
+    say(f"ssqr {rows}x{cols} b{bits} g{gs} act={act} alpha={alpha}")
+    W, X = problem(rows, cols, 2 * cols + 7, rows * 31 + cols)
+    perm, U = gpu_factor(X, act)
+    res = G.quantize_layer_ssqr(torch.from_numpy(W).to(DEV), U, perm, bits=bits, group_size=gs,
+                                alpha=alpha)
+    Sr, n = O.hessian_sum(X)
+    ref = O.gptq_layer(W, Sr, n, bits=bits, group_size=gs, act_order=act, block=128,
+                       ssqr_alpha=alpha)
+    if act:
+        assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    compare_ssqr(res, ref, f"ssqr {rows}x{cols}")
+
+
+def test_ssqr_all_outliers_lossless():
+    say("ssqr all outliers")
+    rng = np.random.default_rng(4)
+    rows, cols = 48, 256
+    W = (rng.choice([-1, 1], size=(rows, cols)) * rng.uniform(0.01, 0.05, (rows, cols))
+         ).astype(np.float16)
+    _, X = problem(rows, cols, 600, 5)
+    perm, U = gpu_factor(X, True)
+    res = G.quantize_layer_ssqr(torch.from_numpy(W).to(DEV), U, perm, bits=4, group_size=64,
+                                alpha=1e-4)
+    assert res.n_outliers == rows * cols
+    assert torch.all(res.outlier_mask == 1)
+    assert torch.equal(res.outlier_vals.cpu(), torch.from_numpy(W))
+    assert torch.all(res.layer.row_loss == 0.0)
+
+
+def test_ssqr_search_matches_oracle():
+    say("ssqr search 96x384, target 2 %")
+    W, X = problem(96, 384, 900, 21)
+    perm, U = gpu_factor(X, True)
+    res = G.ssqr_search(torch.from_numpy(W).to(DEV), U, perm, bits=3, group_size=64, target=0.02,
+                        iters=10)
+    Sr, n = O.hessian_sum(X)
+    H = O.damped_hessian(Sr, n, 0.01)
+    pr = O.act_order_perm(H)
+    Ur = O.hinv_upper(O.permute_sym(H, pr))
+    alpha, best, probes = O.ssqr_search(W.astype(np.float64)[:, pr], Ur, 3, 64, 0.02, iters=10,
+                                        block=128)
+    say(f"gpu alpha {res.alpha} ({res.n_outliers} outliers), oracle alpha {alpha} "
+        f"({int(best['outlier'].sum())}); probes {probes}")
+    assert res.n_outliers <= 0.02 * W.size
+    assert res.alpha == alpha
+    ref = O.gptq_layer(W, Sr, n, bits=3, group_size=64, act_order=True, block=128,
+                       ssqr_alpha=res.alpha)
+    compare_ssqr(res, ref, "ssqr search result")
+
+
+def test_ssqr_qwen_down_projection_full_shape():
+    """896 x 4864 (the Qwen2.5-0.5B down projection), SiLU-gated activations:
+    the GPU search for 1 % outliers, then the oracle's lazy sweep at that
+    alpha."""
+    say("ssqr qwen down 896x4864, target 1 %")
+    rows, dim, n = 896, 4864, 2048
+    X = synth.activations(1, "down_in", n, dim, kind="silu_gated")
+    W = synth.weights(1, "down_proj", rows, dim)
+    perm, U = gpu_factor(X, False)
+    res = G.ssqr_search(torch.from_numpy(W).to(DEV), U, None, bits=4, group_size=128,
+                        target=0.01, iters=8)
+    say(f"alpha {res.alpha}, outliers {res.n_outliers} ({res.n_outliers / W.size:.4%})")
+    assert res.n_outliers <= 0.01 * W.size
+    Sr, nr = O.hessian_sum(X)
+    ref = O.gptq_layer(W, Sr, nr, bits=4, group_size=128, block=128, ssqr_alpha=res.alpha)
+    compare_ssqr(res, ref, "ssqr qwen down")
