@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--hessian", choices=("auto", "exact", "split8"), default="auto",
                     help="Hessian products: exact fp64, int8 digit slices, or split8 from "
                          "256 input features on (auto)")
+    ap.add_argument("--ssqr", type=float, default=None, metavar="TARGET",
+                    help="quantize with SSQR instead: bisection on the scale factor for at "
+                         "most this outlier fraction (every probe is a full sweep)")
+    ap.add_argument("--ssqr-iters", type=int, default=12)
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
@@ -63,9 +67,11 @@ def parse():
 
 # ---------------------------------------------------------------- algorithmic work
 
-def kernel_work(name, wl, plan):
+def kernel_work(name, wl, plan, sweeps=1.0):
     """Algorithmic flops (or bytes) of all launches of one kernel class in a
-    step, with the unit and the roofline it is priced against."""
+    step, with the unit and the roofline it is priced against. ``sweeps``:
+    full sweeps per layer and bit width in a step (the SSQR search runs
+    several; measured from the sweep launches)."""
     if name == "hessian_tile":
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan if not h.split8)  # symmetric half
         return f, "flop", "f64_mfma"
@@ -146,7 +152,7 @@ def kernel_work(name, wl, plan):
         f = 0.0
         for h in plan:
             f += len(wl.bits) * quant_gemm_split(h.rows, h.dim)[0]
-        return f, "flop", "f32_mfma"
+        return f * sweeps, "flop", "f32_mfma"
     if name == "quant_sweep":
         # bytes per weight: fp16 weight 2 + fp64 update 8 + code 1 + fp32 error 4;
         # plus 4 bytes (fp16 scale + zero) per group and the fp32 U slab per block
@@ -157,7 +163,7 @@ def kernel_work(name, wl, plan):
             for bits in wl.bits:
                 b += h.rows * h.dim * 15 + h.rows * (-(-h.dim // wl.group_size)) * 4
                 b += sum(4 * min(128, h.dim - j0) ** 2 for j0 in range(0, h.dim, 128))
-        return b, "byte", "hbm"
+        return b * sweeps, "byte", "hbm"
     return None, None, None
 
 
@@ -413,11 +419,16 @@ def main():
     order = sorted(wl.inputs, key=lambda h: -h.dim)
     streams = [torch.cuda.Stream(device=dev) for _ in order]
 
+    ssqr_last = {}
+
     def step():
         for h, s in zip(order, streams):
             chunks, Wd, grp = dev_inputs[h.name]
             with torch.cuda.stream(s):
-                grp.enqueue(chunks, Wd)
+                if args.ssqr is None:
+                    grp.enqueue(chunks, Wd)
+                else:
+                    ssqr_last[h.name] = grp.ssqr(chunks, Wd, args.ssqr, args.ssqr_iters)
 
     def check_status():
         for h, s in zip(order, streams):
@@ -433,6 +444,12 @@ def main():
     prof_warm = G.profile_read()
     G.profile_enable(False)
     dominant = max(prof_warm, key=lambda k: prof_warm[k][0])
+    # sweeps per layer and bit width in a step: one, or the SSQR search's
+    # probes (sweep launches over the launches of one sweep of every layer)
+    sweeps = 1.0
+    if args.ssqr is not None:
+        per_sweep = sum(len(wl.bits) * -(-h.dim // 128) for h in plan)
+        sweeps = prof_warm["quant_sweep"][1] / max(args.warmup, 1) / per_sweep
 
     # ---- timed steps: the dominant kernel's launches of the last step are
     # bracketed by HIP events on their stream (an event pair per launch sits
@@ -455,7 +472,7 @@ def main():
     value = weights * args.steps / elapsed
 
     dom_ms, dom_launches = prof[dominant]
-    work, unit, peak_key = kernel_work(dominant, wl, plan)
+    work, unit, peak_key = kernel_work(dominant, wl, plan, sweeps)
     roofline = None
     traffic = measured_traffic(wl.name, dominant)
     if work is not None and dom_ms > 0:
@@ -484,7 +501,7 @@ def main():
                      "launches_per_step": v[1] / max(args.warmup, 1)}
                  for k, v in prof_warm.items() if v[1] > 0}
     for k, v in breakdown.items():
-        w, u, pk = kernel_work(k, wl, plan)
+        w, u, pk = kernel_work(k, wl, plan, sweeps)
         if w is not None and v["ms_per_step"] > 0:
             rate = w / (v["ms_per_step"] / 1000.0)
             v["achieved"] = rate / (1e9 if u == "byte" else 1e12)
@@ -515,7 +532,7 @@ def main():
             phase_ms[ph] += v["ms_per_step"]
 
     cpu = None
-    if not args.no_cpu_baseline and args.order == "workload":
+    if not args.no_cpu_baseline and args.order == "workload" and args.ssqr is None:
         sample_rows = args.cpu_sample_rows or 64
         cpu = cpu_baseline(wl, host_inputs, sample_rows)
 
@@ -545,6 +562,11 @@ def main():
                                  "products summed exactly in int32 and combined in fp64; "
                                  "fp64 Cholesky/inverse and sweep, fp32 MFMA lazy update"},
         "roofline": roofline,
+        "ssqr": None if args.ssqr is None else {
+            "target": args.ssqr, "iters": args.ssqr_iters, "sweeps_per_search": sweeps,
+            "result": {k: [{"bits": r.layer.bits, "alpha": r.alpha,
+                            "outlier_fraction": r.n_outliers / r.outlier_mask.numel()}
+                           for r in v] for k, v in ssqr_last.items()}},
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "phases_device_ms_per_step": phase_ms,

@@ -44,6 +44,7 @@ class LayerGroup:
             self.act_order = False
         ng = -(-self.dim // self.group_size)
         self.S = torch.empty((self.dim, self.dim), dtype=torch.float64, device=device)
+        self._swept = False  # quantize workspaces hold a status once enqueue ran
         self.split8 = hessian_mode(hessian, self.dim)
         hb = (G.hessian_split8_workspace_bytes if self.split8 else G.hessian_workspace_bytes)(
             self.dim, max_chunk_tokens)
@@ -64,9 +65,7 @@ class LayerGroup:
             torch.empty(self.rows, dtype=torch.float64, device=device), b, self.group_size)
             for b in self.bits]
 
-    def enqueue(self, chunks, W):
-        """The whole path for token chunks ``chunks`` (fp32 [n_c x dim] each)
-        and stacked fp16 weights ``W`` [rows x dim], without synchronizing."""
+    def _factor(self, chunks):
         n = 0
         for ci, c in enumerate(chunks):
             G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0),
@@ -75,6 +74,12 @@ class LayerGroup:
         G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
                        workspace=self.pws, out=(self.perm, self.U), sync=False,
                        min_pivot=self.min_pivot)
+
+    def enqueue(self, chunks, W):
+        """The whole path for token chunks ``chunks`` (fp32 [n_c x dim] each)
+        and stacked fp16 weights ``W`` [rows x dim], without synchronizing."""
+        self._factor(chunks)
+        self._swept = True
         for bi, b in enumerate(self.bits):
             G.quantize_layer(W, self.U, self.perm if (self.act_order or self.min_pivot) else None,
                              bits=b,
@@ -82,9 +87,19 @@ class LayerGroup:
                              out=self.outs[bi], sync=False)
         return self.outs
 
+    def ssqr(self, chunks, W, target, iters=12):
+        """Hessian and factor as in enqueue, then at every bit width the SSQR
+        search for a target outlier fraction (synchronous: every probe reads
+        its outlier count). Returns one SSQRLayer per bit width."""
+        self._factor(chunks)
+        perm = self.perm if (self.act_order or self.min_pivot) else None
+        return [G.ssqr_search(W, self.U, perm, bits=b, group_size=self.group_size,
+                              target=target, iters=iters) for b in self.bits]
+
     def check(self):
         """Synchronize and raise GPTQError if prepare or quantize reported one
         (a non-SPD Hessian, non-finite values, an invalid permutation)."""
         G.workspace_status(self.pws)
-        for ws in self.qws:
-            G.workspace_status(ws)
+        if self._swept:  # (the SSQR search checks its own sweeps)
+            for ws in self.qws:
+                G.workspace_status(ws)
