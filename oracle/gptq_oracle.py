@@ -56,6 +56,14 @@ Readings of what the pages leave open (each listed in the design doc):
   xmin)/maxq), with the zero point of the unscaled grid, so the grid shrinks
   about 0; the search bisects alpha for the smallest value whose outlier
   fraction is at most the target.
+* HPTQ ([BABAI] 3, Huffman-coded PTQ; named, no rule printed): inliers and
+  outliers share one unbounded integer grid, the group step alpha * (xmax -
+  xmin)/maxq (fp16) with levels k = rint(v/step) relative to 0 (no zero
+  point, no clipping); the layer's levels are Huffman-coded with one
+  codebook; bits per weight = (the Huffman-coded length of all levels + 16 per
+  group step) / weights (a single distinct level costs 1 bit per weight); the
+  search bisects alpha for the smallest value meeting a bits-per-weight
+  budget.
 """
 from __future__ import annotations
 
@@ -70,6 +78,7 @@ __all__ = [
     "gptq_sweep", "gptq_layer", "rtn_quantize", "dequantize_sweep",
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups", "group_grid_ssqr", "ssqr_search",
+    "group_step_hptq", "huffman_lengths", "hptq_bits_per_weight", "hptq_search",
 ]
 
 F64 = np.float64
@@ -265,6 +274,52 @@ def group_grid_ssqr(V, bits, alpha):
     return np.where(degenerate, 1.0, scale), np.where(degenerate, 0.0, zero)
 
 
+def group_step_hptq(V, bits, alpha):
+    """HPTQ step of a group: fp16(alpha * (xmax - xmin)/maxq), 1 when
+    degenerate (xmax == xmin or the step rounds to fp16 zero)."""
+    maxq = (1 << bits) - 1
+    V = np.asarray(V, dtype=F64)
+    xmin = np.minimum(V.min(axis=1), 0.0)
+    xmax = np.maximum(V.max(axis=1), 0.0)
+    with np.errstate(over="ignore"):
+        step = fp16_round(alpha * (xmax - xmin) / maxq)
+    if not np.all(np.isfinite(step)):
+        raise NonFinite("group scale overflows fp16")
+    return np.where((xmax == xmin) | (step == 0.0), 1.0, step)
+
+
+def huffman_lengths(counts):
+    """Code length of every symbol of a Huffman code for ``counts`` (dict
+    symbol -> count > 0), by repeatedly merging the two lightest subtrees. A
+    single symbol gets length 1. Every Huffman code has the same total
+    length sum(count * length), the optimum over prefix codes."""
+    import heapq
+    syms = sorted(counts)
+    if len(syms) == 1:
+        return {syms[0]: 1}
+    length = {s_: 0 for s_ in syms}
+    heap = [(counts[s_], i, [s_]) for i, s_ in enumerate(syms)]
+    heapq.heapify(heap)
+    nxt = len(syms)
+    while len(heap) > 1:
+        c1, _, a = heapq.heappop(heap)
+        c2, _, b = heapq.heappop(heap)
+        for s_ in a + b:
+            length[s_] += 1
+        heapq.heappush(heap, (c1 + c2, nxt, a + b))
+        nxt += 1
+    return length
+
+
+def hptq_bits_per_weight(levels, n_groups_total):
+    """(Huffman-coded bits of all levels + 16 per group step) / weights."""
+    levels = np.asarray(levels).ravel()
+    vals, cnt = np.unique(levels, return_counts=True)
+    ln = huffman_lengths({int(v): int(c) for v, c in zip(vals, cnt)})
+    total = sum(int(c) * ln[int(v)] for v, c in zip(vals, cnt))
+    return (total + 16.0 * n_groups_total) / levels.size
+
+
 def _quantize_ssqr(v, scale, zero, maxq):
     """(stored code, dequantized value, outlier mask): the level outside
     [0, maxq] makes an outlier, kept as fp16(v); its stored code is the
@@ -293,7 +348,7 @@ def num_groups(cols, group_size):
 # --------------------------------------------------------------------------
 
 def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
-               block=None, ssqr_alpha=None):
+               block=None, ssqr_alpha=None, hptq_alpha=None):
     """Sweep the columns of Wp (already in sweep order) with the factor U.
 
     Strict form (``block=None``): after column j is rounded, its scaled error
@@ -305,6 +360,8 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
     grid instead of taking it at each group start. ``ssqr_alpha`` runs the
     SSQR rule (grid step times alpha, out-of-grid levels kept as fp16
     outliers) and adds ``outlier`` (bool) and ``outlier_vals`` [rows x cols].
+    ``hptq_alpha`` runs the HPTQ grid (step times alpha, unbounded levels
+    relative to 0); ``codes`` are then those levels and ``zeros`` are 0.
 
     Returns dict with codes (sweep order, int64), scales, zeros
     [rows x groups], E [rows x cols], row_loss [rows], deq (dequantized).
@@ -334,7 +391,10 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
         for j in range(j0, j1):
             g = j // gs
             if j % gs == 0:
-                if ssqr:
+                if hptq_alpha is not None:
+                    s = group_step_hptq(W[:, j:min(j + gs, cols)], bits, hptq_alpha)
+                    z = np.zeros(rows)
+                elif ssqr:
                     s, z = group_grid_ssqr(W[:, j:min(j + gs, cols)], bits, ssqr_alpha)
                 elif static_grid is None:
                     s, z = group_grid(W[:, j:min(j + gs, cols)], bits)
@@ -345,6 +405,8 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
                 zeros[:, g] = z
             if ssqr:
                 q, dq, outl[:, j] = _quantize_ssqr(W[:, j], scales[:, g], zeros[:, g], maxq)
+            elif hptq_alpha is not None:
+                q, dq = _quantize(W[:, j], scales[:, g], zeros[:, g], maxq, False)
             else:
                 q, dq = _quantize(W[:, j], scales[:, g], zeros[:, g], maxq, clip)
             codes[:, j] = q.astype(np.int64)
@@ -365,7 +427,7 @@ def gptq_sweep(Wp, U, bits, group_size, *, clip=True, static_grid=None,
 
 def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
                act_order=False, clip=True, block=None, min_pivot=False,
-               ssqr_alpha=None):
+               ssqr_alpha=None, hptq_alpha=None):
     """The whole layer: damping, optional act-order (or min-pivot order), U,
     sweep, un-permute.
 
@@ -390,7 +452,7 @@ def gptq_layer(W_fp16, S, n_tokens, *, bits, group_size, damp=0.01,
     Hp = permute_sym(H, perm)
     U = hinv_upper(Hp)
     res = gptq_sweep(Wd[:, perm], U, bits, group_size, clip=clip, block=block,
-                     ssqr_alpha=ssqr_alpha)
+                     ssqr_alpha=ssqr_alpha, hptq_alpha=hptq_alpha)
     codes = np.empty_like(res["codes"])
     codes[:, perm] = res["codes"]
     if ssqr_alpha is not None:  # outliers back to the original column order
@@ -428,6 +490,36 @@ def ssqr_search(Wp, U, bits, group_size, target, *, iters=12, lo=1.0 / 64, hi=1.
         r, f = probe(mid)
         probes.append((mid, f))
         if f <= target:
+            hi, best = mid, r
+        else:
+            lo = mid
+    return hi, best, probes
+
+
+def hptq_search(Wp, U, bits, group_size, budget, *, iters=12, lo=1.0 / 64, hi=1.0,
+                block=None):
+    """[BABAI] 3 (HPTQ): bisection on the layer's scale factor alpha for the
+    smallest alpha whose Huffman-coded bits per weight are at most
+    ``budget`` (the same probe order as ssqr_search). Returns (alpha, the
+    sweep at alpha with its "bpw", the probes [(alpha, bpw)])."""
+    Wp = np.asarray(Wp, dtype=F64)
+    rows, cols = Wp.shape
+    ngt = rows * num_groups(cols, group_size)
+
+    def probe(a):
+        r = gptq_sweep(Wp, U, bits, group_size, block=block, hptq_alpha=a)
+        r["bpw"] = hptq_bits_per_weight(r["codes"], ngt)
+        return r, r["bpw"]
+
+    best, f = probe(hi)
+    probes = [(hi, f)]
+    if f > budget:
+        return hi, best, probes
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        r, f = probe(mid)
+        probes.append((mid, f))
+        if f <= budget:
             hi, best = mid, r
         else:
             lo = mid

@@ -517,3 +517,79 @@ def test_ssqr_search_bisection():
             lo = a
     assert alpha == hi and hi - lo == (1.0 - 1.0 / 64) / 2 ** 10
     assert any(f > target for _, f in probes)  # the target was binding
+
+
+# ---------------------------------------------------------------- HPTQ
+
+def test_huffman_lengths_dyadic_and_single():
+    assert O.huffman_lengths({0: 8, 1: 4, 2: 2, 3: 1, 4: 1}) == {0: 1, 1: 2, 2: 3, 3: 4, 4: 4}
+    assert O.huffman_lengths({7: 5}) == {7: 1}
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_huffman_total_is_the_prefix_code_optimum(seed):
+    """Brute force over every length vector that a prefix code can have
+    (Kraft: sum 2^-l <= 1): the Huffman total is the minimum."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    k = int(rng.integers(2, 6))
+    counts = {i: int(c) for i, c in enumerate(rng.integers(1, 40, k))}
+    ln = O.huffman_lengths(counts)
+    assert sum(Fraction(1, 2 ** ln[s]) for s in counts) <= 1
+    huff = sum(counts[s] * ln[s] for s in counts)
+    best = min(sum(counts[s] * l for s, l in zip(counts, ls))
+               for ls in itertools.product(range(1, k + 1), repeat=k)
+               if sum(Fraction(1, 2 ** l) for l in ls) <= 1)
+    assert huff == best
+
+
+def test_hptq_bits_per_weight_hand_example():
+    # levels 0, 0, 0, 1 in one group: one bit each, plus a 16-bit step
+    assert O.hptq_bits_per_weight(np.array([[0, 0, 0, 1]]), 1) == (4 + 16) / 4
+
+
+def test_hptq_diagonal_hessian_elementwise():
+    """Diagonal H: every level is rint(v / step) on its group's step, the
+    step fp16(alpha (xmax - xmin)/maxq); unbounded, relative to 0."""
+    rng = np.random.default_rng(8)
+    W = (0.02 * rng.standard_t(4, size=(5, 130))).astype(np.float16)
+    S = np.diag(rng.uniform(0.5, 2.0, 130)) * 100
+    alpha = 0.3
+    res = O.gptq_layer(W, S, 100, bits=4, group_size=64, hptq_alpha=alpha)
+    Wd = W.astype(np.float64)
+    for r in range(5):
+        for j in range(130):
+            g0 = (j // 64) * 64
+            grp = Wd[r, g0:g0 + 64]
+            xmin, xmax = min(grp.min(), 0.0), max(grp.max(), 0.0)
+            step = float(np.float16(alpha * (xmax - xmin) / 15))
+            lvl = float(np.rint(Wd[r, j] / step))
+            assert res["codes"][r, j] == lvl and res["deq"][r, j] == step * lvl
+    assert np.all(res["zeros"] == 0.0)
+    assert res["codes"].max() > 15 or res["codes"].min() < 0  # unbounded at alpha < 1
+
+
+def test_hptq_loss_identity():
+    X, W, S, n = _rand_problem(9, 70, 150, 31)
+    res = O.gptq_layer(W, S, n, bits=3, group_size=32, act_order=True, hptq_alpha=0.5)
+    perm = res["perm"]
+    D = W.astype(np.float64)[:, perm] - res["deq"]
+    np.testing.assert_allclose(res["row_loss"], O.loss_quadratic(D, res["Hp"]), rtol=1e-10)
+
+
+def test_hptq_search_bisection():
+    X, W, S, n = _rand_problem(13, 64, 160, 17)
+    H = O.damped_hessian(S, n, 0.01)
+    U = O.hinv_upper(H)
+    budget = 3.5
+    alpha, best, probes = O.hptq_search(W.astype(np.float64), U, 4, 32, budget, iters=10,
+                                        lo=0.25, hi=4.0)
+    assert best["bpw"] <= budget
+    lo, hi = 0.25, 4.0
+    for a, f in probes[1:]:
+        assert a == 0.5 * (lo + hi)
+        if f <= budget:
+            hi = a
+        else:
+            lo = a
+    assert alpha == hi and any(f > budget for _, f in probes)
