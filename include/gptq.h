@@ -215,6 +215,45 @@ gptq_status gptq_ssqr_search(const uint16_t* W, int64_t rows, int64_t cols, int6
                              uint64_t* n_outliers, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * HPTQ — The Geometry of LLM Quantization, section 3 (Huffman-coded PTQ:
+ * inliers and outliers in one unbounded integer grid, the integers Huffman
+ * coded to meet a compression budget). The page prints no rule; the one
+ * taken here:
+ *   step_g = fp16(alpha * (xmax - xmin) / maxq) (xmin/xmax and maxq = 2^bits
+ *   - 1 as in the plain grid), level k = rint(v / step) relative to 0, no
+ *   zero point and no clipping (the no-clipping sweep on this grid);
+ *   bits per weight = (the total length of a Huffman code for all levels of
+ *   the call, one codebook, a single distinct level costing 1 bit per weight,
+ *   + 16 per group step) / (rows * cols).
+ * gptq_quantize_layer_hptq: as gptq_quantize_layer (same workspace), with
+ *   alpha   in (0, 16], else GPTQ_EINVAL;
+ *   levels  (out, int16 [rows x cols], original column order): k; a level
+ *           beyond the int16 range is reported as GPTQ_ENONFINITE;
+ *   scales  (out, fp16 [rows x ceil(cols/gs)], groups in sweep order): steps;
+ *   zeros   (out, same shape): 0 for every group;
+ *   bpw     (host, may be NULL): bits per weight, read after a synchronize
+ *           (GPTQ_EINVAL with GPTQ_FLAG_NO_SYNC).
+ * gptq_hptq_search: bisection on alpha in [alpha_lo, alpha_hi] (0 < lo < hi
+ *   <= 16) for the smallest alpha whose bits per weight are at most budget
+ *   (> 0), in the probe order of gptq_ssqr_search; on return the outputs hold
+ *   the sweep at *alpha_out (host) and *bpw_out (host, may be NULL) its bits
+ *   per weight. flags must be 0.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_quantize_layer_hptq(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                     const float* U, const int32_t* perm, int bits,
+                                     int group_size, uint32_t flags, double alpha,
+                                     int16_t* levels, uint16_t* scales, uint16_t* zeros,
+                                     int32_t* g_idx, double* row_loss, double* bpw, void* ws,
+                                     size_t ws_bytes, void* stream);
+gptq_status gptq_hptq_search(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                             const float* U, const int32_t* perm, int bits, int group_size,
+                             uint32_t flags, double budget, int iters, double alpha_lo,
+                             double alpha_hi, double* alpha_out, int16_t* levels,
+                             uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
+                             double* row_loss, double* bpw_out, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
  * Status of the last gptq_prepare_hinv / gptq_quantize_layer call that used
  * workspace `ws` (a device pointer): synchronizes `stream` (the stream of that
  * call), then reads the status word the call left at the start of `ws`.

@@ -89,13 +89,43 @@ __global__ __launch_bounds__(256) void q_finalize_kernel(const uint8_t* __restri
       const int32_t k = invperm[m];
       if (k < 0 || k >= cols) {
         if (r == 0) atomicOr(status, ST_BADPERM);
-        codes[r * cols + m] = 0;
+        if (codes) codes[r * cols + m] = 0;
         continue;
       }
-      codes[r * cols + m] = codes_s[r * cols + k];
+      if (codes) codes[r * cols + m] = codes_s[r * cols + k];
       if (r == 0 && g_idx) g_idx[m] = k / gs;
     }
   }
+}
+
+__global__ void q_fill_u32_kernel(unsigned* __restrict__ p, int64_t count) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = 0u;
+}
+
+// Histogram of int16 levels into hist[level + 32768] (65536 bins): levels in
+// [-1024, 1023] are counted in LDS first, the others straight in global
+// memory. Each thread takes 16 consecutive levels.
+constexpr int QH_LDS = 2048;
+__global__ __launch_bounds__(256) void q_hist_kernel(const int16_t* __restrict__ lv, int64_t n,
+                                                     unsigned* __restrict__ hist) {
+  __shared__ unsigned h[QH_LDS];
+  for (int i = threadIdx.x; i < QH_LDS; i += blockDim.x) h[i] = 0u;
+  __syncthreads();
+  const int64_t e0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int64_t e = e0 + u;
+    if (e < n) {
+      const int k = lv[e];
+      if (k >= -QH_LDS / 2 && k < QH_LDS / 2) atomicAdd(&h[k + QH_LDS / 2], 1u);
+      else atomicAdd(&hist[k + 32768], 1u);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < QH_LDS; i += blockDim.x)
+    if (h[i]) atomicAdd(&hist[i - QH_LDS / 2 + 32768], h[i]);
 }
 
 // ---------------------------------------------------------------- update GEMM
@@ -254,12 +284,16 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
 __device__ inline double row_ror4(double v) { return dpp_f64<0x124>(v); }
 __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 
-// SSQR (The Geometry of LLM Quantization, section 3): the group's step is
-// alpha times the min-max one, with the zero point of the unscaled step, and
-// a level outside [0, maxq] makes an outlier: its current value is kept as
-// fp16 (mask 1, value in ovals at the original column, only the fp16
+// MODE 1, SSQR (The Geometry of LLM Quantization, section 3): the group's
+// step is alpha times the min-max one, with the zero point of the unscaled
+// step, and a level outside [0, maxq] makes an outlier: its current value is
+// kept as fp16 (mask 1, value in ovals at the original column, only the fp16
 // rounding propagates) and its stored code is the clamped one.
-template <int GS, bool SSQR>
+// MODE 2, HPTQ (same section): one unbounded grid, step alpha times the
+// min-max one, zero point 0, no clipping (the caller passes clip = false);
+// the level k goes to ovals (int16 bits) at the original column, and a level
+// beyond the int16 range is reported (ST_NONFINITE).
+template <int GS, int MODE>
 __global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
     const double* __restrict__ part, int P, int64_t part_stride,
@@ -270,6 +304,8 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     int64_t gj0, int gbw, int64_t gks, int64_t gk_end, double* __restrict__ gpart, double alpha,
     uint8_t* __restrict__ omask, uint16_t* __restrict__ ovals, const int32_t* __restrict__ operm,
     int64_t cols, unsigned long long* __restrict__ ocount) {
+  constexpr bool SSQR = MODE == 1;
+  constexpr bool HPTQ = MODE == 2;
   // U slab plus three rows of zero padding: the slot reads of a column run up
   // to 112 entries past its row end, into the next row or the padding, only
   // for slots past the block end whose values are never used; rows are read
@@ -480,14 +516,15 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       if ((sh & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
       // SSQR: the step used is fp16(alpha * step); the zero point comes from
       // the unscaled one (scale, here), so the grid shrinks about 0
-      const uint16_t sha = SSQR ? f64_to_f16_rne(alpha * ((mx - mn) / maxq)) : sh;
-      const double scale_a = SSQR ? f16_to_f64(sha) : scale;
-      if (mx == mn || scale == 0.0 || scale_a == 0.0) {
+      const uint16_t sha = (SSQR || HPTQ) ? f64_to_f16_rne(alpha * ((mx - mn) / maxq)) : sh;
+      const double scale_a = (SSQR || HPTQ) ? f16_to_f64(sha) : scale;
+      if ((sha & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
+      if (mx == mn || (!HPTQ && scale == 0.0) || scale_a == 0.0) {
         scale = 1.0;
         sh = 0x3c00;
         zero = 0.0;
       } else {
-        zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
+        zero = HPTQ ? 0.0 : fmin(fmax(rint(-mn / scale), 0.0), maxq);
         scale = scale_a;
         sh = sha;
       }
@@ -572,13 +609,19 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         codes[r * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero, 0.0), 255.0);
         E[r * lde + j0 + c] = (float)e;
         loss += e * e;
-        if (SSQR) {
+        if (SSQR || HPTQ) {
           const int64_t oc = operm ? (int64_t)operm[j0 + c] : j0 + c;
           if (oc >= 0 && oc < cols) {  // a bad permutation is reported elsewhere
-            omask[r * cols + oc] = o_own ? 1 : 0;
-            ovals[r * cols + oc] = o_own ? h_own : (uint16_t)0;
+            if (SSQR) {
+              omask[r * cols + oc] = o_own ? 1 : 0;
+              ovals[r * cols + oc] = o_own ? h_own : (uint16_t)0;
+            } else {
+              const double kc = fmin(fmax(k_own, -32768.0), 32767.0);
+              if (kc != k_own) atomicOr(status, ST_NONFINITE);
+              ovals[r * cols + oc] = (uint16_t)(int16_t)kc;
+            }
           }
-          nout += o_own ? 1.0 : 0.0;
+          if (SSQR) nout += o_own ? 1.0 : 0.0;
         }
       }
     }
@@ -605,7 +648,8 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
 struct QLayout {
   int64_t rows, cols, lde, ng;
   int pmax;
-  size_t off_status, off_count, off_invperm, off_wp, off_codes, off_E, off_part, off_wblk, total;
+  size_t off_status, off_count, off_hist, off_invperm, off_wp, off_codes, off_E, off_part, off_wblk,
+      total;
 };
 
 // Split-K factor of the update GEMM: about 512 workgroups in total.
@@ -632,6 +676,7 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
   };
   L.off_status = take(4);
   L.off_count = take(8);
+  L.off_hist = take(4 * 65536);
   L.off_invperm = take(4 * (size_t)cols);
   L.off_wp = take(2 * (size_t)rows * cols);
   L.off_codes = take((size_t)rows * cols);
@@ -673,7 +718,8 @@ struct SweepArgs {
   int gbw;
   int64_t gks, gk_end;
   double* gpart;
-  // SSQR (alpha > 0): outputs at the original columns, outlier counter
+  // SSQR (mode 1) / HPTQ (mode 2): outputs at the original columns
+  int mode;
   double alpha;
   uint8_t* omask;
   uint16_t* ovals;
@@ -691,8 +737,9 @@ static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
                   a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg,          \
                   a.row_loss, a.status, a.clip, a.late, a.nsweep, a.gj0, a.gbw, a.gks,         \
                   a.gk_end, a.gpart, a.alpha, a.omask, a.ovals, a.operm, a.cols, a.ocount)))
-  if (a.alpha > 0.0) Q_SWEEP(true);
-  else Q_SWEEP(false);
+  if (a.mode == 1) Q_SWEEP(1);
+  else if (a.mode == 2) Q_SWEEP(2);
+  else Q_SWEEP(0);
 #undef Q_SWEEP
   return GPTQ_OK;
 }
@@ -713,7 +760,7 @@ extern "C" size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int 
 static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
                                     const float* U, const int32_t* perm, int bits, int group_size,
                                     bool clip, uint8_t* codes, uint16_t* scales, uint16_t* zeros,
-                                    int32_t* g_idx, double* row_loss, double alpha,
+                                    int32_t* g_idx, double* row_loss, int mode, double alpha,
                                     uint8_t* omask, uint16_t* ovals, void* ws,
                                     hipStream_t st) {
   const QLayout L = q_layout(rows, cols, group_size);
@@ -736,7 +783,7 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
   }
   const uint16_t* Wsrc = W;
   int64_t ldws = ldw;
-  uint8_t* csw = codes;  // sweep-order codes
+  uint8_t* csw = codes ? codes : codes_s;  // sweep-order codes (HPTQ: none returned)
   if (perm) {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(cols, 256), 16),
               (unsigned)std::min<int64_t>(rows, 65535));
@@ -792,7 +839,7 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
     }
     SweepArgs a{nw, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
                 bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, clip,
-                late, 0, 0, 0, 0, pn, alpha, omask, ovals, perm, cols, ocount};
+                late, 0, 0, 0, 0, pn, mode, alpha, omask, ovals, perm, cols, ocount};
     ep = emb_max > 0 ? 0 : -1;
     if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
       // next block's sum over l < j0 (the errors of blocks < b), in as few
@@ -854,7 +901,7 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
   if (c != GPTQ_OK || rows == 0 || cols == 0) return c;
   if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
   c = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size,
-                       !(flags & GPTQ_FLAG_NO_CLIP), codes, scales, zeros, g_idx, row_loss, 0.0,
+                       !(flags & GPTQ_FLAG_NO_CLIP), codes, scales, zeros, g_idx, row_loss, 0, 0.0,
                        nullptr, nullptr, ws, (hipStream_t)stream);
   if (c != GPTQ_OK) return c;
   if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
@@ -894,7 +941,7 @@ extern "C" gptq_status gptq_quantize_layer_ssqr(const uint16_t* W, int64_t rows,
   if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   c = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size, true, codes, scales, zeros,
-                       g_idx, row_loss, alpha, outlier_mask, outlier_vals, ws, st);
+                       g_idx, row_loss, 1, alpha, outlier_mask, outlier_vals, ws, st);
   if (c != GPTQ_OK) return c;
   if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
   if (n_outliers) {
@@ -933,7 +980,7 @@ extern "C" gptq_status gptq_ssqr_search(const uint16_t* W, int64_t rows, int64_t
   // was another one)
   auto probe = [&](double a, uint64_t* cnt) -> gptq_status {
     gptq_status r = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size, true, codes,
-                                     scales, zeros, g_idx, row_loss, a, outlier_mask,
+                                     scales, zeros, g_idx, row_loss, 1, a, outlier_mask,
                                      outlier_vals, ws, st);
     if (r != GPTQ_OK) return r;
     r = ssqr_count(ws, rows, cols, group_size, st, cnt);
@@ -965,5 +1012,133 @@ extern "C" gptq_status gptq_ssqr_search(const uint16_t* W, int64_t rows, int64_t
   }
   *alpha_out = hi;
   if (n_outliers) *n_outliers = best;
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- HPTQ
+//
+// Bits per weight of a level array: the histogram (device), then on the host
+// the total length of a Huffman code for it, which is the sum of the weights
+// of all merged subtrees (a single distinct level costs 1 bit each), plus 16
+// bits per group step.
+#include <functional>
+#include <queue>
+#include <vector>
+
+static gptq_status hptq_bpw(const int16_t* levels, int64_t rows, int64_t cols, int gs, void* ws,
+                            hipStream_t st, double* bpw) {
+  const QLayout L = q_layout(rows, cols, gs);
+  unsigned* hist = (unsigned*)((char*)ws + L.off_hist);
+  const int64_t n = rows * cols;
+  GPTQ_LAUNCH(K_FILL, st, q_fill_u32_kernel<<<64, 256, 0, st>>>(hist, 65536));
+  GPTQ_LAUNCH(K_Q_FINALIZE, st,
+              q_hist_kernel<<<(unsigned)cdiv(n, 256 * 16), 256, 0, st>>>(levels, n, hist));
+  std::vector<unsigned> h(65536);
+  GPTQ_HIP(hipMemcpyAsync(h.data(), hist, 65536 * sizeof(unsigned), hipMemcpyDeviceToHost, st));
+  GPTQ_HIP(hipStreamSynchronize(st));
+  std::priority_queue<uint64_t, std::vector<uint64_t>, std::greater<uint64_t>> pq;
+  for (unsigned c : h)
+    if (c) pq.push(c);
+  uint64_t total = 0;
+  if (pq.size() == 1) total = pq.top();
+  while (pq.size() > 1) {
+    const uint64_t a = pq.top();
+    pq.pop();
+    const uint64_t b = pq.top();
+    pq.pop();
+    total += a + b;
+    pq.push(a + b);
+  }
+  *bpw = ((double)total + 16.0 * (double)rows * (double)cdiv(cols, gs)) / (double)n;
+  return GPTQ_OK;
+}
+
+extern "C" gptq_status gptq_quantize_layer_hptq(const uint16_t* W, int64_t rows, int64_t cols,
+                                                int64_t ldw, const float* U, const int32_t* perm,
+                                                int bits, int group_size, uint32_t flags,
+                                                double alpha, int16_t* levels, uint16_t* scales,
+                                                uint16_t* zeros, int32_t* g_idx,
+                                                double* row_loss, double* bpw, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  if (flags & ~GPTQ_FLAG_NO_SYNC) return GPTQ_EINVAL;
+  if (!(alpha > 0.0 && alpha <= 16.0)) return GPTQ_EINVAL;
+  if ((flags & GPTQ_FLAG_NO_SYNC) && bpw) return GPTQ_EINVAL;
+  if (rows < 0 || cols < 0) return GPTQ_EINVAL;
+  if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
+  if (rows == 0 || cols == 0) {
+    if (bpw) *bpw = 0.0;
+    return GPTQ_OK;
+  }
+  if (!W || !U || !levels || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
+  if (cols > (int64_t)1 << 20 || rows > (int64_t)1 << 26) return GPTQ_EINVAL;
+  if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  gptq_status c = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size, false, nullptr,
+                                   scales, zeros, g_idx, row_loss, 2, alpha, nullptr,
+                                   (uint16_t*)levels, ws, st);
+  if (c != GPTQ_OK) return c;
+  if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
+  if (bpw) {
+    c = hptq_bpw(levels, rows, cols, group_size, ws, st, bpw);
+    if (c != GPTQ_OK) return c;
+  }
+  return gptq_workspace_status(ws, stream);
+}
+
+extern "C" gptq_status gptq_hptq_search(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                                        const float* U, const int32_t* perm, int bits,
+                                        int group_size, uint32_t flags, double budget, int iters,
+                                        double alpha_lo, double alpha_hi, double* alpha_out,
+                                        int16_t* levels, uint16_t* scales, uint16_t* zeros,
+                                        int32_t* g_idx, double* row_loss, double* bpw_out,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  if (flags != 0) return GPTQ_EINVAL;
+  if (!(budget > 0.0) || iters < 0 || iters > 60) return GPTQ_EINVAL;
+  if (!(alpha_lo > 0.0 && alpha_lo < alpha_hi && alpha_hi <= 16.0)) return GPTQ_EINVAL;
+  if (!alpha_out) return GPTQ_EINVAL;
+  if (rows < 0 || cols < 0) return GPTQ_EINVAL;
+  if (bits < 2 || bits > 8 || !valid_gs(group_size)) return GPTQ_EINVAL;
+  if (rows == 0 || cols == 0) {
+    *alpha_out = alpha_hi;
+    if (bpw_out) *bpw_out = 0.0;
+    return GPTQ_OK;
+  }
+  if (!W || !U || !levels || !scales || !zeros || !row_loss || ldw < cols) return GPTQ_EINVAL;
+  if (cols > (int64_t)1 << 20 || rows > (int64_t)1 << 26) return GPTQ_EINVAL;
+  if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  auto probe = [&](double a, double* b) -> gptq_status {
+    gptq_status r = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size, false,
+                                     nullptr, scales, zeros, g_idx, row_loss, 2, a, nullptr,
+                                     (uint16_t*)levels, ws, st);
+    if (r != GPTQ_OK) return r;
+    r = hptq_bpw(levels, rows, cols, group_size, ws, st, b);
+    if (r != GPTQ_OK) return r;
+    return gptq_workspace_status(ws, stream);
+  };
+  double lo = alpha_lo, hi = alpha_hi, last = hi, b = 0.0, best = 0.0;
+  gptq_status c = probe(hi, &b);
+  if (c != GPTQ_OK) return c;
+  best = b;
+  if (b <= budget) {
+    for (int it = 0; it < iters; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      c = probe(mid, &b);
+      if (c != GPTQ_OK) return c;
+      last = mid;
+      if (b <= budget) {
+        hi = mid;
+        best = b;
+      } else {
+        lo = mid;
+      }
+    }
+    if (last != hi) {
+      c = probe(hi, &b);
+      if (c != GPTQ_OK) return c;
+    }
+  }
+  *alpha_out = hi;
+  if (bpw_out) *bpw_out = best;
   return GPTQ_OK;
 }

@@ -50,6 +50,16 @@ EXPORTS = {
                                    C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "gptq_quantize_layer_hptq": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                           C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_uint32,
+                                           C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                           C.c_size_t, C.c_void_p]),
+    "gptq_hptq_search": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
+                                   C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_double, C.c_int,
+                                   C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
+                                   C.c_size_t, C.c_void_p]),
     "gptq_workspace_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
@@ -320,6 +330,57 @@ def ssqr_search(W, U, perm=None, bits: int = 4, group_size: int = 128, target: f
     q = QuantizedLayer(o["codes"], o["scales"], o["zeros"], o["g_idx"], o["row_loss"], bits,
                        group_size)
     return SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(a.value))
+
+
+@dataclass
+class HPTQLayer:
+    levels: object     # int16 [rows x cols], original column order
+    scales: object     # fp16  [rows x groups], groups in sweep order (the steps)
+    g_idx: object      # int32 [cols]
+    row_loss: object   # fp64  [rows]
+    bpw: float         # Huffman-coded bits per weight, with 16 per group step
+    alpha: float
+
+
+def _hptq_args(W, U, perm, group_size):
+    rows, cols, o, ws = _ssqr_args(W, U, perm, group_size)
+    torch = _torch()
+    o["levels"] = torch.empty((rows, cols), dtype=torch.int16, device=W.device)
+    return rows, cols, o, ws
+
+
+def quantize_layer_hptq(W, U, perm=None, bits: int = 4, group_size: int = 128,
+                        alpha: float = 1.0) -> HPTQLayer:
+    """The no-clipping sweep on the HPTQ grid at scale factor ``alpha``
+    (synchronous), with its Huffman-coded bits per weight."""
+    rows, cols, o, ws = _hptq_args(W, U, perm, group_size)
+    b = C.c_double(0.0)
+    st = lib.gptq_quantize_layer_hptq(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols,
+                                      _ptr(U), _ptr(perm), int(bits), int(group_size), 0,
+                                      float(alpha), _ptr(o["levels"]), _ptr(o["scales"]),
+                                      _ptr(o["zeros"]), _ptr(o["g_idx"]), _ptr(o["row_loss"]),
+                                      C.byref(b), _ptr(ws), ws.numel(), _stream())
+    _check(st, "gptq_quantize_layer_hptq")
+    return HPTQLayer(o["levels"], o["scales"], o["g_idx"], o["row_loss"], float(b.value),
+                     float(alpha))
+
+
+def hptq_search(W, U, perm=None, bits: int = 4, group_size: int = 128, budget: float = 4.0,
+                iters: int = 12, alpha_lo: float = 1.0 / 16, alpha_hi: float = 4.0) -> HPTQLayer:
+    """Bisection on the HPTQ scale factor for the smallest alpha in
+    [alpha_lo, alpha_hi] whose bits per weight are at most ``budget``."""
+    rows, cols, o, ws = _hptq_args(W, U, perm, group_size)
+    b = C.c_double(0.0)
+    a = C.c_double(0.0)
+    st = lib.gptq_hptq_search(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
+                              _ptr(perm), int(bits), int(group_size), 0, float(budget),
+                              int(iters), float(alpha_lo), float(alpha_hi), C.byref(a),
+                              _ptr(o["levels"]), _ptr(o["scales"]), _ptr(o["zeros"]),
+                              _ptr(o["g_idx"]), _ptr(o["row_loss"]), C.byref(b), _ptr(ws),
+                              ws.numel(), _stream())
+    _check(st, "gptq_hptq_search")
+    return HPTQLayer(o["levels"], o["scales"], o["g_idx"], o["row_loss"], float(b.value),
+                     float(a.value))
 
 
 def workspace_status(workspace):

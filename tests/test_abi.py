@@ -160,6 +160,34 @@ def test_ssqr_arguments_rejected_on_host():
     assert ss(aout=NULL) == g.GPTQ_EINVAL
 
 
+def test_hptq_arguments_rejected_on_host():
+    L = g.lib
+    b = C.c_double(0.0)
+    a = C.c_double(0.0)
+    q = L.gptq_quantize_layer_hptq
+
+    def qh(alpha=0.5, flags=0, lv=FAKE, bp=None, ws=FAKE, wsb=1 << 40):
+        return q(FAKE, 4, 8, 8, FAKE, NULL, 4, 16, flags, alpha, lv, FAKE, FAKE, NULL, FAKE,
+                 C.byref(b) if bp is None else bp, ws, wsb, NULL)
+    assert qh(alpha=0.0) == g.GPTQ_EINVAL
+    assert qh(alpha=16.5) == g.GPTQ_EINVAL
+    assert qh(flags=g.GPTQ_FLAG_NO_CLIP) == g.GPTQ_EINVAL
+    assert qh(flags=g.GPTQ_FLAG_NO_SYNC) == g.GPTQ_EINVAL  # bits per weight need a sync
+    assert qh(lv=NULL) == g.GPTQ_EINVAL
+    assert qh(ws=NULL, wsb=0) == g.GPTQ_EWORKSPACE
+    s = L.gptq_hptq_search
+
+    def hs(budget=3.0, iters=8, lo=0.1, hi=1.0, flags=0, aout=None):
+        return s(FAKE, 4, 8, 8, FAKE, NULL, 4, 16, flags, budget, iters, lo, hi,
+                 C.byref(a) if aout is None else aout, FAKE, FAKE, FAKE, NULL, FAKE,
+                 C.byref(b), FAKE, 1 << 40, NULL)
+    assert hs(budget=0.0) == g.GPTQ_EINVAL
+    assert hs(iters=-1) == g.GPTQ_EINVAL
+    assert hs(lo=0.5, hi=0.5) == g.GPTQ_EINVAL
+    assert hs(flags=1) == g.GPTQ_EINVAL
+    assert hs(aout=NULL) == g.GPTQ_EINVAL
+
+
 def test_profile_api_without_launches():
     g.profile_enable(True)
     r = g.profile_read()
