@@ -52,6 +52,9 @@ def parse():
                     help="quantize with SSQR instead: bisection on the scale factor for at "
                          "most this outlier fraction (every probe is a full sweep)")
     ap.add_argument("--ssqr-iters", type=int, default=12)
+    ap.add_argument("--hptq", type=float, default=None, metavar="BUDGET",
+                    help="quantize with HPTQ instead: bisection on the scale factor for at "
+                         "most this many Huffman-coded bits per weight")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
@@ -420,15 +423,20 @@ def main():
     streams = [torch.cuda.Stream(device=dev) for _ in order]
 
     ssqr_last = {}
+    hptq_last = {}
+    if args.ssqr is not None and args.hptq is not None:
+        raise SystemExit("--ssqr and --hptq are exclusive")
 
     def step():
         for h, s in zip(order, streams):
             chunks, Wd, grp = dev_inputs[h.name]
             with torch.cuda.stream(s):
-                if args.ssqr is None:
-                    grp.enqueue(chunks, Wd)
-                else:
+                if args.ssqr is not None:
                     ssqr_last[h.name] = grp.ssqr(chunks, Wd, args.ssqr, args.ssqr_iters)
+                elif args.hptq is not None:
+                    hptq_last[h.name] = grp.hptq(chunks, Wd, args.hptq, args.ssqr_iters)
+                else:
+                    grp.enqueue(chunks, Wd)
 
     def check_status():
         for h, s in zip(order, streams):
@@ -447,7 +455,7 @@ def main():
     # sweeps per layer and bit width in a step: one, or the SSQR search's
     # probes (sweep launches over the launches of one sweep of every layer)
     sweeps = 1.0
-    if args.ssqr is not None:
+    if args.ssqr is not None or args.hptq is not None:
         per_sweep = sum(len(wl.bits) * -(-h.dim // 128) for h in plan)
         sweeps = prof_warm["quant_sweep"][1] / max(args.warmup, 1) / per_sweep
 
@@ -532,7 +540,8 @@ def main():
             phase_ms[ph] += v["ms_per_step"]
 
     cpu = None
-    if not args.no_cpu_baseline and args.order == "workload" and args.ssqr is None:
+    if (not args.no_cpu_baseline and args.order == "workload" and args.ssqr is None
+            and args.hptq is None):
         sample_rows = args.cpu_sample_rows or 64
         cpu = cpu_baseline(wl, host_inputs, sample_rows)
 
@@ -567,6 +576,11 @@ def main():
             "result": {k: [{"bits": r.layer.bits, "alpha": r.alpha,
                             "outlier_fraction": r.n_outliers / r.outlier_mask.numel()}
                            for r in v] for k, v in ssqr_last.items()}},
+        "hptq": None if args.hptq is None else {
+            "budget_bits_per_weight": args.hptq, "iters": args.ssqr_iters,
+            "sweeps_per_search": sweeps,
+            "result": {k: [{"alpha": r.alpha, "bits_per_weight": r.bpw} for r in v]
+                       for k, v in hptq_last.items()}},
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "phases_device_ms_per_step": phase_ms,

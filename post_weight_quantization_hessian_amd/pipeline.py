@@ -96,6 +96,15 @@ class LayerGroup:
         return [G.ssqr_search(W, self.U, perm, bits=b, group_size=self.group_size,
                               target=target, iters=iters) for b in self.bits]
 
+    def hptq(self, chunks, W, budget, iters=12):
+        """Hessian and factor as in enqueue, then at every bit width the HPTQ
+        search for a bits-per-weight budget (synchronous). Returns one
+        HPTQLayer per bit width."""
+        self._factor(chunks)
+        perm = self.perm if (self.act_order or self.min_pivot) else None
+        return [G.hptq_search(W, self.U, perm, bits=b, group_size=self.group_size,
+                              budget=budget, iters=iters) for b in self.bits]
+
     def check(self):
         """Synchronize and raise GPTQError if prepare or quantize reported one
         (a non-SPD Hessian, non-finite values, an invalid permutation)."""
