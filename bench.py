@@ -228,7 +228,7 @@ KERNEL_CLASS = {  # device function name -> timing class
     "prep_uout_z_kernel": "prepare_uout", "mp_init_kernel": "minpivot_step",
     "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update",
     "h8_tile_kernel": "hessian_split8", "h8_colmax_kernel": "hessian_digits",
-    "h8_split_kernel": "hessian_digits"}
+    "h8_split_kernel": "hessian_digits", "q_hist_kernel": "quant_hist"}
 
 
 def source_hash():

@@ -1031,7 +1031,7 @@ static gptq_status hptq_bpw(const int16_t* levels, int64_t rows, int64_t cols, i
   unsigned* hist = (unsigned*)((char*)ws + L.off_hist);
   const int64_t n = rows * cols;
   GPTQ_LAUNCH(K_FILL, st, q_fill_u32_kernel<<<64, 256, 0, st>>>(hist, 65536));
-  GPTQ_LAUNCH(K_Q_FINALIZE, st,
+  GPTQ_LAUNCH(K_Q_HIST, st,
               q_hist_kernel<<<(unsigned)cdiv(n, 256 * 16), 256, 0, st>>>(levels, n, hist));
   std::vector<unsigned> h(65536);
   GPTQ_HIP(hipMemcpyAsync(h.data(), hist, 65536 * sizeof(unsigned), hipMemcpyDeviceToHost, st));
