@@ -109,6 +109,18 @@ __host__ __device__ inline double f16_to_f64(uint16_t h) {
   return s ? -v : v;
 }
 
+// The nearest-even binary16 value of a double, as a double: x scaled by a
+// power of two so that one fp16 unit in the last place is 1 (2^(e-10) for
+// the binade 2^e, 2^-24 below the normal range), rounded to an integer
+// (ties to even), scaled back; beyond the largest finite fp16 value the
+// result is infinite. Exact: the scalings are by powers of two.
+__device__ inline double f16_round_f64(double x) {
+  const int e = (int)((__double_as_longlong(x) >> 52) & 0x7ff) - 1023;
+  const int u = e - 10 > -24 ? e - 10 : -24;
+  const double r = __builtin_ldexp(__builtin_rint(__builtin_ldexp(x, -u)), u);
+  return __builtin_fabs(r) > 65504.0 ? __builtin_copysign(__builtin_inf(), x) : r;
+}
+
 // ---------------------------------------------------------------- misc
 
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

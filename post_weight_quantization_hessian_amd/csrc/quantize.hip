@@ -541,7 +541,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     // whether it is an outlier, and its fp16 value)
     double d_own = 0.0, k_own = 0.0;
     bool o_own = false;
-    uint16_t h_own = 0;
+    double h_own = 0.0;  // SSQR: the column's value rounded to fp16
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
       if (16 * tt + jj < bw) {
@@ -563,11 +563,11 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         const double k = fmin(fmax(kr, klo), khi);
         double d = fma(-scale, k, v);
         bool out = false;
-        uint16_t vh = 0;
+        double vh = 0.0;
         if (SSQR) {
           out = kr < klo || kr > khi;
-          vh = f64_to_f16_rne(v);
-          if (out) d = v - f16_to_f64(vh);
+          vh = f16_round_f64(v);
+          if (out) d = v - vh;
         }
         double db;
         switch (jj) {
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
           if (oc >= 0 && oc < cols) {  // a bad permutation is reported elsewhere
             if (SSQR) {
               omask[r * cols + oc] = o_own ? 1 : 0;
-              ovals[r * cols + oc] = o_own ? h_own : (uint16_t)0;
+              ovals[r * cols + oc] = o_own ? f64_to_f16_rne(h_own) : (uint16_t)0;
             } else {
               const double kc = fmin(fmax(k_own, -32768.0), 32767.0);
               if (kc != k_own) atomicOr(status, ST_NONFINITE);
