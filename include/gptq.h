@@ -94,7 +94,9 @@ typedef enum {
  * column of S. The workspace is then required: ws_bytes >=
  * gptq_hessian_split8_workspace_bytes(in_features, n_tokens), else
  * GPTQ_EWORKSPACE (it holds the digit planes, 4 * in_features * n_tokens
- * bytes rounded up to tiles, and any token-split partial tiles).
+ * bytes rounded up to tiles, and any token-split partial tiles). A call whose
+ * tiles and token splits would exceed one launch grid (2^31 - 1 workgroups)
+ * is rejected with GPTQ_EINVAL.
  * ------------------------------------------------------------------------- */
 size_t gptq_hessian_workspace_bytes(int64_t in_features, int64_t n_tokens);
 size_t gptq_hessian_split8_workspace_bytes(int64_t in_features, int64_t n_tokens);

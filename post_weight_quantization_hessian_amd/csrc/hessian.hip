@@ -491,6 +491,7 @@ struct H8Layout {
 static gptq_status hess_split8(double* S, int64_t dim, const float* X, int64_t n, int64_t ldx,
                                bool overwrite, void* ws, size_t ws_bytes, hipStream_t st) {
   H8Layout L(dim, n);
+  if ((int64_t)L.nslots * L.nsplit > INT32_MAX) return GPTQ_EINVAL;  // one launch grid
   if (!ws || ws_bytes < (size_t)L.total) return GPTQ_EWORKSPACE;
   char* base = (char*)ws;
   unsigned* colmax = (unsigned*)base;
