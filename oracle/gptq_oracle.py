@@ -64,6 +64,16 @@ Readings of what the pages leave open (each listed in the design doc):
   group step) / weights (a single distinct level costs 1 bit per weight); the
   search bisects alpha for the smallest value meeting a bits-per-weight
   budget.
+* CHMC frontend ([CHMC] Schritt 1-3): c_j = (1/n) sum_t x_tj^2 plus 0.05 *
+  mean(c); W~ = W diag(sqrt c); a rank-r approximation of W~ by randomized
+  subspace iteration (Halko, Martinsson, Tropp 2011, Algorithm 4.4) with q = r
+  sketch columns, niter = 5 power iterations and a Gaussian sketch passed in
+  (any orthonormal basis of each iterate's span: the result depends on the
+  spans only), then the SVD of the small projected matrix; stored factors
+  A = fp16(U S) and B = fp16(V^T diag(1/sqrt c)); the residual R = W - A B
+  is swept like GPTQ (act-order, damped H) with one grid per group of gs
+  consecutive output channels (rows) and column; r from the page's bit
+  budget formula.
 """
 from __future__ import annotations
 
@@ -79,6 +89,8 @@ __all__ = [
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups", "group_grid_ssqr", "ssqr_search",
     "group_step_hptq", "huffman_lengths", "hptq_bits_per_weight", "hptq_search",
+    "chmc_energies", "chmc_rank", "randomized_lowrank", "chmc_lowrank", "gptq_sweep_outgroups",
+    "chmc_layer",
 ]
 
 F64 = np.float64
@@ -524,6 +536,117 @@ def hptq_search(Wp, U, bits, group_size, budget, *, iters=12, lo=1.0 / 64, hi=1.
         else:
             lo = mid
     return hi, best, probes
+
+
+# --------------------------------------------------------------------------
+# CHMC frontend ([CHMC] "Methodik", Schritt 1-3)
+# --------------------------------------------------------------------------
+
+def chmc_energies(S_diag, n_tokens, lam=0.05):
+    """Schritt 1: damped activation energies c_j = (1/n) sum_t x_tj^2 +
+    lam * mean(c)."""
+    c = np.asarray(S_diag, dtype=F64) / n_tokens
+    return c + lam * c.mean()
+
+
+def chmc_rank(o, i, bits, group_size, bpw_target):
+    """Schritt 3: the largest rank whose fp16 factors (16 r (o + i)), b-bit
+    residual codes and one 16-bit scale per output group and column fit the
+    budget: floor((BPW o i - b o i - 16 ceil(o/gs) i) / (16 (o + i)))."""
+    r = (bpw_target * o * i - bits * o * i - 16 * num_groups(o, group_size) * i) // (16 * (o + i))
+    return int(max(0, min(r, min(o, i))))
+
+
+def _orth(Y):
+    return np.linalg.qr(Y, mode="reduced")[0]
+
+
+def randomized_lowrank(A, Omega, niter):
+    """Randomized subspace iteration (Halko, Martinsson, Tropp 2011,
+    Algorithm 4.4): Q = orth(A Omega), then niter times Q = orth(A orth(A^T
+    Q)); B = Q^T A = Ub S Vt (SVD), U = Q Ub. Returns (U, S, Vt)."""
+    A = np.asarray(A, dtype=F64)
+    Q = _orth(A @ Omega)
+    for _ in range(niter):
+        Q = _orth(A @ _orth(A.T @ Q))
+    Ub, S, Vt = np.linalg.svd(Q.T @ A, full_matrices=False)
+    return Q @ Ub, S, Vt
+
+
+def chmc_lowrank(W, c, Omega, niter=5):
+    """Schritt 1: the low-rank part of W in the norm weighted by sqrt(c), as
+    fp16 factors A = U S [o x r] and B = V^T diag(1/sqrt c) [r x i]."""
+    sc = np.sqrt(np.asarray(c, dtype=F64))
+    U, S, Vt = randomized_lowrank(np.asarray(W, dtype=F64) * sc[None, :], Omega, niter)
+    return fp16_round(U * S[None, :]), fp16_round(Vt / sc[None, :])
+
+
+def gptq_sweep_outgroups(Rp, U, bits, row_group):
+    """Schritt 2 with the page's grouping: the strict GPTQ sweep of Rp (sweep
+    order) where each column gets one grid per group of ``row_group``
+    consecutive rows, from the group's current values of that column.
+    Returns codes [rows x cols], scales/zeros [groups x cols] (sweep order),
+    E, row_loss and deq."""
+    R = np.array(Rp, dtype=F64, copy=True)
+    rows, cols = R.shape
+    U = np.asarray(U, dtype=F64)
+    maxq = (1 << bits) - 1
+    ng = num_groups(rows, row_group)
+    codes = np.zeros((rows, cols), dtype=np.int64)
+    deq = np.zeros((rows, cols))
+    E = np.zeros((rows, cols))
+    scales = np.zeros((ng, cols))
+    zeros = np.zeros((ng, cols))
+    loss = np.zeros(rows)
+    for j in range(cols):
+        s_col = np.empty(rows)
+        z_col = np.empty(rows)
+        for g in range(ng):
+            r0, r1 = g * row_group, min((g + 1) * row_group, rows)
+            s, z = group_grid(R[r0:r1, j][None, :], bits)
+            scales[g, j], zeros[g, j] = s[0], z[0]
+            s_col[r0:r1], z_col[r0:r1] = s[0], z[0]
+        q, dq = _quantize(R[:, j], s_col, z_col, maxq, True)
+        codes[:, j] = q.astype(np.int64)
+        deq[:, j] = dq
+        e = (R[:, j] - dq) / U[j, j]
+        E[:, j] = e
+        loss += e * e
+        R[:, j + 1:] -= np.outer(e, U[j, j + 1:])
+    return {"codes": codes, "scales": scales, "zeros": zeros, "E": E, "row_loss": loss,
+            "deq": deq}
+
+
+def chmc_layer(W_fp16, S, n_tokens, Omega, *, bits=4, group_size=128, bpw_target=4.2875,
+               damp=0.01, act_order=True, niter=5, rank=None):
+    """The CHMC layer: energies, rank from the budget (or ``rank``), the
+    low-rank fp16 factors from the first r columns of the sketch Omega
+    [i x >= r], the residual swept with output-channel groups. Codes and
+    scales/zeros come back in the original column order; row_loss is the
+    residual sweep's (its H-weighted error)."""
+    W = np.asarray(W_fp16)
+    if W.dtype != np.float16:
+        raise TypeError("W must be fp16")
+    Wd = W.astype(F64)
+    o, i = Wd.shape
+    c = chmc_energies(np.diag(S), n_tokens)
+    r = chmc_rank(o, i, bits, group_size, bpw_target) if rank is None else int(rank)
+    if r > 0:
+        A, B = chmc_lowrank(Wd, c, np.asarray(Omega, dtype=F64)[:, :r], niter)
+    else:
+        A, B = np.zeros((o, 0)), np.zeros((0, i))
+    R = Wd - A @ B
+    H = damped_hessian(S, n_tokens, damp)
+    perm = act_order_perm(H) if act_order else np.arange(i)
+    U = hinv_upper(permute_sym(H, perm))
+    res = gptq_sweep_outgroups(R[:, perm], U, bits, group_size)
+    out = {"A": A, "B": B, "rank": r, "c": c, "R": R, "perm": perm, "U": U,
+           "row_loss": res["row_loss"]}
+    for key in ("codes", "scales", "zeros", "deq"):
+        a = np.empty_like(res[key])
+        a[:, perm] = res[key]
+        out[key] = a
+    return out
 
 
 def dequantize_sweep(codes_sweep, scales, zeros, group_size):

@@ -593,3 +593,76 @@ def test_hptq_search_bisection():
         else:
             lo = a
     assert alpha == hi and any(f > budget for _, f in probes)
+
+
+# ---------------------------------------------------------------- CHMC frontend
+
+def test_chmc_rank_worked_example():
+    """[CHMC] Schritt 3 states r = 2 for 576 x 576 at 4.2875 bits."""
+    g = GOLD["chmc_rank_576"]
+    assert O.chmc_rank(g["o"], g["i"], g["bits"], g["gs"], g["bpw_target"]) == g["rank"]
+    # the budget of the rank it returns fits, one more rank does not
+    o, i = g["o"], g["i"]
+    used = lambda r: (16 * r * (o + i) + 4 * o * i + 16 * O.num_groups(o, 128) * i) / (o * i)
+    assert used(2) <= 4.2875 < used(3)
+
+
+def test_chmc_energies_from_activations():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((200, 9)).astype(np.float32)
+    S, n = O.hessian_sum(X)
+    c = O.chmc_energies(np.diag(S), n)
+    c0 = np.mean(X.astype(np.float64) ** 2, axis=0)
+    np.testing.assert_allclose(c, c0 + 0.05 * c0.mean(), rtol=1e-13)
+
+
+def test_randomized_lowrank_exact_on_low_rank_and_matches_svd():
+    """A matrix of rank <= q is reproduced exactly; with a clear spectral gap
+    the rank-q result equals the library's truncated SVD."""
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((60, 4)) @ rng.standard_normal((4, 50))
+    U, S, Vt = O.randomized_lowrank(A, rng.standard_normal((50, 4)), 2)
+    np.testing.assert_allclose(U @ np.diag(S) @ Vt, A, atol=1e-12 * np.abs(A).max())
+    Ut, St, Vtt = np.linalg.svd(rng.standard_normal((80, 80)) @ np.diag(0.5 ** np.arange(80)) @
+                                rng.standard_normal((80, 70)), full_matrices=False)
+    B = (Ut[:, :10] * (np.array([100.0] * 3 + [1e-3] * 7))) @ Vtt[:10]
+    B += 1e-6 * rng.standard_normal(B.shape)
+    U, S, Vt = O.randomized_lowrank(B, rng.standard_normal((70, 3)), 5)
+    u, s, vt = np.linalg.svd(B)
+    ref = u[:, :3] @ np.diag(s[:3]) @ vt[:3]
+    np.testing.assert_allclose(U @ np.diag(S) @ Vt, ref, atol=1e-9 * np.abs(ref).max())
+    np.testing.assert_allclose(S, s[:3], rtol=1e-10)
+
+
+def test_outgroup_sweep_diagonal_hessian_is_columnwise_rtn():
+    """Diagonal H: nothing propagates; each column is rounded on one grid per
+    group of rows, from that group's values of the column."""
+    rng = np.random.default_rng(6)
+    R = 0.02 * rng.standard_t(4, size=(200, 30))
+    U = np.diag(rng.uniform(0.5, 2.0, 30))
+    res = O.gptq_sweep_outgroups(R, U, 4, 64)
+    for j in range(30):
+        for g0 in range(0, 200, 64):
+            v = R[g0:g0 + 64, j]
+            xmin, xmax = min(v.min(), 0.0), max(v.max(), 0.0)
+            sc = float(np.float16((xmax - xmin) / 15))
+            z = min(max(float(np.rint(-xmin / sc)), 0.0), 15.0)
+            q = np.clip(np.rint(v / sc) + z, 0, 15)
+            assert np.array_equal(res["codes"][g0:g0 + 64, j], q)
+            assert res["scales"][g0 // 64, j] == sc and res["zeros"][g0 // 64, j] == z
+
+
+def test_chmc_layer_loss_identity_and_reconstruction():
+    """The residual sweep obeys the loss identity with the damped H, and
+    W = A B + R exactly in fp64 for the stored fp16 factors."""
+    X, W, S, n = _rand_problem(70, 96, 300, 41)
+    rng = np.random.default_rng(42)
+    res = O.chmc_layer(W, S, n, rng.standard_normal((96, 8)), bits=4, group_size=32, rank=3)
+    assert res["A"].shape == (70, 3) and res["B"].shape == (3, 96)
+    assert np.array_equal(res["A"], res["A"].astype(np.float16).astype(np.float64))
+    np.testing.assert_allclose(res["A"] @ res["B"] + res["R"], W.astype(np.float64), atol=1e-15)
+    H = O.damped_hessian(S, n, 0.01)
+    perm = res["perm"]
+    D = (res["R"] - res["deq"])[:, perm]
+    np.testing.assert_allclose(res["row_loss"], O.loss_quadratic(D, O.permute_sym(H, perm)),
+                               rtol=1e-10)
