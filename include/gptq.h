@@ -278,6 +278,63 @@ gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int64_t n);
 int gptq_version(void);
 
 /* ---------------------------------------------------------------------------
+ * CHMC frontend — CHMC article, "Methodik. Was ist CHMC", Schritt 1-3: the
+ * weight is split into a low-rank part, kept as two fp16 factors, and a
+ * residual quantized by the GPTQ sweep with one grid per group of output
+ * channels (rows) and column.
+ *   energies  c_j = S_jj / n + 0.05 * mean_k(S_kk / n) (activation energy,
+ *             damped by 5 % of its mean);
+ *   low rank  of W~ = W diag(sqrt c) by randomized subspace iteration
+ *             (Halko, Martinsson and Tropp 2011, Algorithm 4.4) from the
+ *             caller's sketch omega with 5 power iterations, then the SVD of
+ *             the r x i projection: W~ ~ Ul diag(s) V^T;
+ *             A = fp16(Ul diag(s)) [rows x r], B = fp16(V^T diag(1/sqrt c)) [r x cols];
+ *   residual  R = W - A B (fp64 from the fp16 factors), swept in the order
+ *             perm with the factor U of gptq_prepare_hinv: column j gets, per
+ *             group of group_size rows, the min-max asymmetric grid of the
+ *             group's current values (fp16 scale, integer zero point), and its
+ *             scaled errors propagate along row j of U.
+ * gptq_chmc_rank: the largest r whose factors (16 r (rows + cols) bits),
+ *   bits-bit codes and one 16-bit scale per row group and column fit
+ *   bpw_target bits per weight: floor((bpw rows cols - bits rows cols - 16
+ *   ceil(rows/gs) cols) / (16 (rows + cols))), clamped to [0, min(rows, cols)];
+ *   0 for invalid arguments.
+ * gptq_chmc_workspace_bytes: workspace for gptq_chmc_layer (0 if rank is not
+ *   in [0, 64] or a size is not positive): about 3 rows*cols fp64 matrices.
+ * gptq_chmc_layer:
+ *   W       (in, fp16 bits, device, [rows x cols] row stride ldw >= cols);
+ *   S       (in, fp64, device, [cols x cols]) the Hessian sum X^T X over
+ *           n_tokens (> 0) tokens (only its diagonal is read here);
+ *   U, perm (in, device) from gptq_prepare_hinv: U fp32 [cols x cols] upper,
+ *           sweep order; perm int32 [cols] a permutation (NULL = identity);
+ *           a perm that is not one is reported as GPTQ_EINVAL;
+ *   omega   (in, fp64, device, [cols x rank] row-major) the Gaussian sketch;
+ *   rank    in [0, min(64, rows, cols)] (0: no low-rank part; omega, A, B
+ *           may then be NULL); bits in [2, 8]; group_size 32, 64 or 128;
+ *   flags   0 or GPTQ_FLAG_NO_SYNC;
+ *   A       (out, fp16 bits [rows x rank]), B (out, fp16 bits [rank x cols]);
+ *           each component is determined up to a common sign of its column
+ *           of A and row of B;
+ *   codes   (out, u8 [rows x cols], original column order);
+ *   scales, zeros (out, fp16 bits [ceil(rows/group_size) x cols], original
+ *           column order): the grid of each row group and column;
+ *   row_loss (out, fp64 [rows]): sum over columns of the squared scaled
+ *           errors of the residual sweep.
+ *   Returns GPTQ_ENOTSPD when the sketch loses rank (the weighted W has
+ *   rank below r), GPTQ_ENONFINITE for a NaN/Inf weight or energy or an
+ *   fp16 overflow of a scale; with GPTQ_FLAG_NO_SYNC the status is read later
+ *   with gptq_workspace_status. Calls on one workspace must not overlap.
+ * ------------------------------------------------------------------------- */
+int gptq_chmc_rank(int64_t rows, int64_t cols, int bits, int group_size, double bpw_target);
+size_t gptq_chmc_workspace_bytes(int64_t rows, int64_t cols, int rank);
+gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
+                            const double* S, int64_t n_tokens, const float* U,
+                            const int32_t* perm, const double* omega, int rank, int bits,
+                            int group_size, uint32_t flags, uint16_t* A, uint16_t* B,
+                            uint8_t* codes, uint16_t* scales, uint16_t* zeros, double* row_loss,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Optional kernel timing (process-wide, not thread-safe). gptq_profile_enable
  * takes a bit mask of kernel ids (bit k = kernel id k; 0 turns timing off,
  * 0xFFFFFFFF times every kernel). Each launch of a selected kernel is then

@@ -12,7 +12,8 @@ static const char* const kKernelNames[K_COUNT] = {
     "chol_potrf", "chol_trsm", "chol_syrk", "trtri_t", "trtri_x", "prepare_uout",
     "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill",
     "trtri_diag", "chol_potrf_syrk", "trtri_sum", "chol_col", "minpivot_step",
-    "minpivot_update", "hessian_digits", "hessian_split8", "quant_hist"};
+    "minpivot_update", "hessian_digits", "hessian_split8", "quant_hist", "chmc_front",
+    "chmc_update", "chmc_sweep"};
 
 struct ProfRec {
   int kid;

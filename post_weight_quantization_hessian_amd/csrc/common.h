@@ -29,7 +29,8 @@ enum KernelId {
   K_HESS_TILE = 0, K_HESS_REDUCE, K_PREP_DIAG, K_PREP_PERM, K_PREP_GATHER, K_CHOL_POTRF,
   K_CHOL_TRSM, K_CHOL_SYRK, K_TRTRI_ROW, K_TRTRI_UPDATE, K_PREP_UOUT, K_Q_INIT, K_Q_PERMUTE,
   K_Q_GEMM, K_Q_SWEEP, K_Q_FINALIZE, K_FILL, K_TRTRI_DIAG, K_CHOL_STEP, K_TRTRI_SUM, K_CHOL_COL, K_MP_STEP,
-  K_MP_UPDATE, K_HESS_DIGITS, K_HESS_SPLIT8, K_Q_HIST, K_COUNT
+  K_MP_UPDATE, K_HESS_DIGITS, K_HESS_SPLIT8, K_Q_HIST, K_CH_FRONT, K_CH_UPDATE, K_CH_SWEEP,
+  K_COUNT
 };
 
 // Launch bracketing for the profiler (defined in api.hip).

@@ -60,6 +60,13 @@ EXPORTS = {
                                    C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "gptq_chmc_rank": (C.c_int, [C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_double]),
+    "gptq_chmc_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int]),
+    "gptq_chmc_layer": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
+                                  C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                  C.c_int, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                  C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                  C.c_void_p]),
     "gptq_workspace_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
@@ -381,6 +388,85 @@ def hptq_search(W, U, perm=None, bits: int = 4, group_size: int = 128, budget: f
     _check(st, "gptq_hptq_search")
     return HPTQLayer(o["levels"], o["scales"], o["g_idx"], o["row_loss"], float(b.value),
                      float(a.value))
+
+
+@dataclass
+class CHMCLayer:
+    A: object          # fp16 [rows x rank]
+    B: object          # fp16 [rank x cols]
+    codes: object      # uint8 [rows x cols], original column order
+    scales: object     # fp16 [row groups x cols], original column order
+    zeros: object      # fp16 [row groups x cols]
+    row_loss: object   # fp64 [rows]
+    rank: int
+    bits: int
+    group_size: int
+
+    def dequantize(self):
+        """A B + the dequantized residual, fp64 [rows x cols]."""
+        torch = _torch()
+        g = torch.arange(self.codes.shape[0], device=self.codes.device) // self.group_size
+        s = self.scales.double()[g]
+        z = self.zeros.double()[g]
+        res = s * (self.codes.double() - z)
+        if self.rank > 0:
+            res = res + self.A.double() @ self.B.double()
+        return res
+
+
+def chmc_rank(rows: int, cols: int, bits: int = 4, group_size: int = 128,
+              bpw_target: float = 4.2875) -> int:
+    return int(lib.gptq_chmc_rank(rows, cols, bits, group_size, bpw_target))
+
+
+def chmc_workspace_bytes(rows: int, cols: int, rank: int) -> int:
+    return int(lib.gptq_chmc_workspace_bytes(rows, cols, rank))
+
+
+def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_size: int = 128,
+               bpw_target: float = 4.2875, sync: bool = True, workspace=None) -> CHMCLayer:
+    """The CHMC layer on the device: energies from diag(S), the rank-``rank``
+    fp16 factors of W from the sketch ``omega`` (fp64 [cols x >= rank]; its
+    first ``rank`` columns are used), the residual swept with one grid per
+    group of ``group_size`` output rows and column. ``rank`` defaults to the
+    largest that fits ``bpw_target``."""
+    torch = _torch()
+    _need(W, torch.float16, "W", 2)
+    _need(S, torch.float64, "S", 2)
+    _need(U, torch.float32, "U", 2)
+    rows, cols = W.shape
+    if W.stride(1) != 1:
+        raise ValueError("W must have unit column stride")
+    r = chmc_rank(rows, cols, bits, group_size, bpw_target) if rank is None else int(rank)
+    om = None
+    if r > 0:
+        _need(omega, torch.float64, "omega", 2)
+        if omega.shape[0] != cols or omega.shape[1] < r:
+            raise ValueError("omega must be [cols x >= rank]")
+        om = omega[:, :r].contiguous()
+    if perm is not None:
+        _need(perm, torch.int32, "perm", 1)
+    if tuple(S.shape) != (cols, cols) or not S.is_contiguous():
+        raise ValueError("S must be a contiguous [cols x cols] tensor")
+    if tuple(U.shape) != (cols, cols) or not U.is_contiguous():
+        raise ValueError("U must be a contiguous [cols x cols] tensor")
+    dev = W.device
+    ng = -(-rows // group_size)
+    A = torch.empty((rows, r), dtype=torch.float16, device=dev)
+    B = torch.empty((r, cols), dtype=torch.float16, device=dev)
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    scales = torch.empty((ng, cols), dtype=torch.float16, device=dev)
+    zeros = torch.empty((ng, cols), dtype=torch.float16, device=dev)
+    row_loss = torch.empty(rows, dtype=torch.float64, device=dev)
+    nb = chmc_workspace_bytes(rows, cols, r)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    st = lib.gptq_chmc_layer(_ptr(W), rows, cols, W.stride(0), _ptr(S), int(n_tokens), _ptr(U),
+                             _ptr(perm), _ptr(om), r, int(bits), int(group_size),
+                             0 if sync else GPTQ_FLAG_NO_SYNC, _ptr(A), _ptr(B), _ptr(codes),
+                             _ptr(scales), _ptr(zeros), _ptr(row_loss), _ptr(ws), ws.numel(),
+                             _stream())
+    _check(st, "gptq_chmc_layer")
+    return CHMCLayer(A, B, codes, scales, zeros, row_loss, r, int(bits), int(group_size))
 
 
 def workspace_status(workspace):

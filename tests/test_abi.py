@@ -188,6 +188,39 @@ def test_hptq_arguments_rejected_on_host():
     assert hs(aout=NULL) == g.GPTQ_EINVAL
 
 
+def test_chmc_host_checks():
+    """Rank formula against the oracle's, workspace sizes and the argument
+    checks of gptq_chmc_layer (rejected before anything is enqueued)."""
+    import oracle as O
+    L = g.lib
+    for shape in [(576, 576), (896, 4864), (4864, 896), (37, 129), (1, 1), (8192, 28672)]:
+        for bits, gs, bpw in [(4, 128, 4.2875), (3, 64, 3.5), (2, 32, 8.0), (4, 128, 4.0)]:
+            assert g.chmc_rank(*shape, bits, gs, bpw) == O.chmc_rank(*shape, bits, gs, bpw)
+    assert g.chmc_rank(576, 576, 4, 128, 4.2875) == 2
+    assert g.chmc_workspace_bytes(576, 576, 2) >= 3 * 8 * 576 * 576
+    assert g.chmc_workspace_bytes(576, 576, 65) == 0
+    assert g.chmc_workspace_bytes(37, 129, 0) >= 3 * 8 * 37 * 129  # no low-rank part
+    assert g.chmc_workspace_bytes(0, 576, 2) == 0
+    f = L.gptq_chmc_layer
+
+    def ch(rows=64, cols=128, ldw=128, n=100, perm=NULL, om=FAKE, rank=2, bits=4, gs=64,
+           flags=0, A=FAKE, B=FAKE, ws=FAKE, wsb=1 << 40):
+        return f(FAKE, rows, cols, ldw, FAKE, n, FAKE, perm, om, rank, bits, gs, flags, A, B,
+                 FAKE, FAKE, FAKE, FAKE, ws, wsb, NULL)
+    assert ch(rank=65) == g.GPTQ_EINVAL
+    assert ch(rank=-1) == g.GPTQ_EINVAL
+    assert ch(rows=1, rank=2) == g.GPTQ_EINVAL
+    assert ch(bits=1) == g.GPTQ_EINVAL
+    assert ch(gs=100) == g.GPTQ_EINVAL
+    assert ch(n=0) == g.GPTQ_EINVAL
+    assert ch(ldw=127) == g.GPTQ_EINVAL
+    assert ch(flags=1) == g.GPTQ_EINVAL
+    assert ch(om=NULL) == g.GPTQ_EINVAL
+    assert ch(A=NULL) == g.GPTQ_EINVAL
+    assert ch(ws=NULL, wsb=0) == g.GPTQ_EWORKSPACE
+    assert ch(wsb=g.chmc_workspace_bytes(64, 128, 2) - 1) == g.GPTQ_EWORKSPACE
+
+
 def test_profile_api_without_launches():
     g.profile_enable(True)
     r = g.profile_read()

@@ -1,0 +1,188 @@
+"""GPU: the CHMC frontend (CHMC article, Methodik, Schritt 1-3) against the
+oracle's chmc_layer.
+
+Through the C ABI: the GPU Hessian and factor, then gptq_chmc_layer with a
+seeded Gaussian sketch. The fp16 factors A and B must equal the oracle's up to
+the sign of each component (an fp16 rounding tie may land one ulp apart);
+codes, per-row-group scales and zero points and the loss of the residual
+sweep meet the sweep's parity bar. Shapes: the page's worked size (576 x 576
+at 4.2875 bits per weight, rank 2), ragged rows, columns and groups, no
+low-rank part, the largest rank, and the Qwen2.5-0.5B down projection at
+full size; error paths: a weight of too low rank and a bad permutation.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.parity_util import CODE_AGREE, LOSS_RTOL, SCALE_AGREE, SCALE_RTOL
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a HIP device", allow_module_level=True)
+
+import post_weight_quantization_hessian_amd.gptq as G  # noqa: E402
+from post_weight_quantization_hessian_amd import synth  # noqa: E402
+
+DEV = torch.device("cuda:0")
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def problem(rows, cols, n, seed, lowrank=0):
+    rng = np.random.default_rng(seed)
+    X = (rng.standard_normal((n, cols)) * np.exp(0.5 * rng.standard_normal(cols))[None, :]
+         + 0.8 * rng.standard_normal((n, 1))).astype(np.float32)
+    W = 0.02 * rng.standard_t(4, size=(rows, cols))
+    if lowrank:
+        W += 0.05 * rng.standard_normal((rows, lowrank)) @ rng.standard_normal((lowrank, cols))
+    return W.astype(np.float16), X
+
+
+def gpu_inputs(X, act_order):
+    dim = X.shape[1]
+    S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
+    perm, U = G.prepare_hinv(S, X.shape[0], damp=0.01, act_order=act_order)
+    return S, (perm if act_order else None), U
+
+
+def compare_factor(gpu, ref, name):
+    g = gpu.cpu().numpy().astype(np.float64)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    if g.size == 0:
+        return
+    exact = float(np.mean(g == ref))
+    ulp = np.abs(np.spacing(ref.astype(np.float16)).astype(np.float64))
+    near = bool(np.all(np.abs(g - ref) <= ulp))
+    say(f"{name}: exact {exact:.6f}, within one ulp {near}")
+    assert exact >= 0.999 and near
+
+
+def compare_chmc(res, ref, name):
+    r = ref["rank"]
+    assert res.rank == r
+    if r > 0:
+        Ag = res.A.cpu().numpy().astype(np.float64)
+        sgn = np.sign(np.sum(Ag * ref["A"], axis=0))
+        sgn[sgn == 0] = 1.0
+        compare_factor(res.A * torch.from_numpy(sgn).to(DEV).half()[None, :], ref["A"],
+                       f"{name} A")
+        compare_factor(res.B * torch.from_numpy(sgn).to(DEV).half()[:, None], ref["B"],
+                       f"{name} B")
+    codes = res.codes.cpu().numpy().astype(np.int64)
+    agree = float(np.mean(codes == ref["codes"]))
+    sc = res.scales.cpu().numpy().astype(np.float64)
+    s_ok = float(np.mean(np.abs(sc - ref["scales"]) <= SCALE_RTOL * np.abs(ref["scales"])))
+    z_ok = float(np.mean(res.zeros.cpu().numpy().astype(np.float64) == ref["zeros"]))
+    lg, lr = float(res.row_loss.sum().item()), float(ref["row_loss"].sum())
+    say(f"{name}: rank {r} codes {agree:.6f} scales {s_ok:.6f} zeros {z_ok:.6f} "
+        f"loss gpu {lg:.6e} oracle {lr:.6e}")
+    assert agree >= CODE_AGREE and s_ok >= SCALE_AGREE and z_ok >= SCALE_AGREE
+    assert abs(lg - lr) <= LOSS_RTOL * lr
+
+
+def run_case(rows, cols, n, bits, gs, act, rank, seed, lowrank=0, bpw=4.2875):
+    W, X = problem(rows, cols, n, seed, lowrank)
+    S, perm, U = gpu_inputs(X, act)
+    om = np.random.default_rng(seed + 1).standard_normal((cols, max(rank or 0, 64)))
+    Sr, nr = O.hessian_sum(X)
+    ref = O.chmc_layer(W, Sr, nr, om, bits=bits, group_size=gs, bpw_target=bpw, act_order=act,
+                       rank=rank)
+    if act:
+        assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    res = G.chmc_layer(torch.from_numpy(W).to(DEV), S, n, U, perm, torch.from_numpy(om).to(DEV),
+                       rank=rank, bits=bits, group_size=gs, bpw_target=bpw)
+    return res, ref
+
+
+def test_chmc_page_example_576():
+    """576 x 576 at 4.2875 bits per weight: rank 2 from the budget."""
+    say("chmc 576x576 b4 g128 act, rank from the budget")
+    res, ref = run_case(576, 576, 1300, 4, 128, True, None, 11, lowrank=3)
+    assert ref["rank"] == 2
+    compare_chmc(res, ref, "chmc 576")
+
+
+@pytest.mark.parametrize("rows,cols,n,bits,gs,act,rank", [
+    (200, 333, 700, 3, 64, False, 5),
+    (37, 129, 300, 2, 32, True, 0),
+    (130, 260, 600, 4, 128, True, 64),
+    (300, 128, 400, 4, 32, True, 3),
+])
+def test_chmc_ragged_matches_oracle(rows, cols, n, bits, gs, act, rank):
+    say(f"chmc {rows}x{cols} b{bits} g{gs} act={act} rank={rank}")
+    res, ref = run_case(rows, cols, n, bits, gs, act, rank, rows * 7 + cols, lowrank=2)
+    compare_chmc(res, ref, f"chmc {rows}x{cols}")
+
+
+def test_chmc_qwen_down_projection_full_shape():
+    """896 x 4864 (the Qwen2.5-0.5B down projection), SiLU-gated activations,
+    rank from the 4.2875-bit budget (7). The oracle's factors in full; its
+    residual sweep for one sampled row group (row groups are independent:
+    each has its own grids and rows), compared with that group of the GPU
+    result."""
+    say("chmc qwen down 896x4864")
+    rows, dim, n, gs = 896, 4864, 2048, 128
+    X = synth.activations(1, "down_in", n, dim, kind="silu_gated")
+    W = synth.weights(1, "down_proj", rows, dim)
+    S, perm, U = gpu_inputs(X, True)
+    om = np.random.default_rng(5).standard_normal((dim, 64))
+    res = G.chmc_layer(torch.from_numpy(W).to(DEV), S, n, U, perm, torch.from_numpy(om).to(DEV))
+    Sr, nr = O.hessian_sum(X)
+    r = O.chmc_rank(rows, dim, 4, gs, 4.2875)
+    assert r == 7 and res.rank == r
+    c = O.chmc_energies(np.diag(Sr), nr)
+    A, B = O.chmc_lowrank(W.astype(np.float64), c, om[:, :r], 5)
+    ref = {"rank": r, "A": A, "B": B}
+    H = O.damped_hessian(Sr, nr, 0.01)
+    pr = O.act_order_perm(H)
+    assert np.array_equal(perm.cpu().numpy(), pr)
+    Ur = O.hinv_upper(O.permute_sym(H, pr))
+    g = 3
+    rs = slice(g * gs, (g + 1) * gs)
+    R = W.astype(np.float64)[rs] - A[rs] @ B
+    sw = O.gptq_sweep_outgroups(R[:, pr], Ur, 4, gs)
+    for key in ("codes", "scales", "zeros"):
+        a = np.empty_like(sw[key])
+        a[:, pr] = sw[key]
+        ref[key] = a
+    ref["row_loss"] = sw["row_loss"]
+    sub = G.CHMCLayer(res.A, res.B, res.codes[rs], res.scales[g:g + 1], res.zeros[g:g + 1],
+                      res.row_loss[rs], r, 4, gs)
+    compare_chmc(sub, ref, f"chmc qwen down, row group {g}")
+
+
+def test_chmc_rank_matches_oracle():
+    for shape in [(576, 576), (896, 4864), (4864, 896), (37, 129), (1, 1)]:
+        for bits, gs, bpw in [(4, 128, 4.2875), (3, 64, 3.5), (2, 32, 8.0), (4, 128, 4.0)]:
+            assert G.chmc_rank(*shape, bits, gs, bpw) == O.chmc_rank(*shape, bits, gs, bpw)
+
+
+def test_chmc_low_rank_weight_is_rejected():
+    say("chmc zero weight, rank 2: the sketch loses rank")
+    _, X = problem(64, 128, 300, 3)
+    S, perm, U = gpu_inputs(X, True)
+    W = torch.zeros((64, 128), dtype=torch.float16, device=DEV)
+    om = torch.from_numpy(np.random.default_rng(1).standard_normal((128, 2))).to(DEV)
+    with pytest.raises(G.GPTQError) as e:
+        G.chmc_layer(W, S, 300, U, perm, om, rank=2)
+    assert e.value.status == G.GPTQ_ENOTSPD
+
+
+def test_chmc_bad_permutation_is_rejected():
+    say("chmc duplicate entry in perm")
+    W, X = problem(64, 128, 300, 4)
+    S, perm, U = gpu_inputs(X, True)
+    bad = perm.clone()
+    bad[5] = bad[6]
+    om = torch.from_numpy(np.random.default_rng(1).standard_normal((128, 2))).to(DEV)
+    with pytest.raises(G.GPTQError) as e:
+        G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, bad, om, rank=2)
+    assert e.value.status == G.GPTQ_EINVAL
