@@ -31,7 +31,7 @@ CHOL_FUSE_NT = 48  # the library's bound on panels for the inverse accumulated i
 QEMB_KMAX = 512  # the library's longest early update-GEMM piece inside a sweep launch
 
 # MI355X published peaks
-PEAK = {"f64_mfma": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "i8_mfma": 5000.0,
+PEAK = {"f64_mfma": 78.6, "f64_vec": 78.6, "f32_mfma": 157.3, "bf16_mfma": 2500.0, "i8_mfma": 5000.0,
         "hbm_gbs": 8000.0}
 
 
@@ -55,6 +55,10 @@ def parse():
     ap.add_argument("--hptq", type=float, default=None, metavar="BUDGET",
                     help="quantize with HPTQ instead: bisection on the scale factor for at "
                          "most this many Huffman-coded bits per weight")
+    ap.add_argument("--chmc", type=float, default=None, metavar="BPW",
+                    help="quantize with the CHMC frontend instead: per layer, the fp16 "
+                         "low-rank factors of the largest rank that fits BPW bits per weight "
+                         "and the residual swept with one grid per output-row group")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="rows per layer group for the oracle sample (0 = auto)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH",
@@ -70,11 +74,25 @@ def parse():
 
 # ---------------------------------------------------------------- algorithmic work
 
+def chmc_flops(plan, bits_n, in_block):
+    """fp64 multiply-adds (2 flops each) of the CHMC residual sweep: the lazy
+    update of block b (at j0) is rows x j0 x bw, the in-block propagation rows
+    x bw (bw - 1) / 2; per bit width."""
+    f = 0.0
+    for h in plan:
+        for j0 in range(0, h.dim, 128):
+            bw = min(128, h.dim - j0)
+            f += 2.0 * h.rows * (bw * (bw - 1) / 2.0 if in_block else j0 * bw)
+    return f * bits_n
+
+
 def kernel_work(name, wl, plan, sweeps=1.0):
     """Algorithmic flops (or bytes) of all launches of one kernel class in a
     step, with the unit and the roofline it is priced against. ``sweeps``:
     full sweeps per layer and bit width in a step (the SSQR search runs
     several; measured from the sweep launches)."""
+    if name in ("chmc_update", "chmc_sweep"):
+        return chmc_flops(plan, len(wl.bits), name == "chmc_sweep"), "flop", "f64_vec"
     if name == "hessian_tile":
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan if not h.split8)  # symmetric half
         return f, "flop", "f64_mfma"
@@ -228,7 +246,14 @@ KERNEL_CLASS = {  # device function name -> timing class
     "prep_uout_z_kernel": "prepare_uout", "mp_init_kernel": "minpivot_step",
     "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update",
     "h8_tile_kernel": "hessian_split8", "h8_colmax_kernel": "hessian_digits",
-    "h8_split_kernel": "hessian_digits", "q_hist_kernel": "quant_hist"}
+    "h8_split_kernel": "hessian_digits", "q_hist_kernel": "quant_hist",
+    "ch_update_kernel": "chmc_update", "ch_sweep_kernel": "chmc_sweep",
+    "ch_gemm_nn": "chmc_front", "ch_gemm_tn": "chmc_front", "ch_sum_kernel": "chmc_front",
+    "ch_chol_inv_kernel": "chmc_front", "ch_jacobi_kernel": "chmc_front",
+    "ch_energy_kernel": "chmc_front", "ch_scale_kernel": "chmc_front",
+    "ch_factor_kernel": "chmc_front", "ch_resid_kernel": "chmc_front",
+    "ch_perm_count_kernel": "chmc_front", "ch_perm_check_kernel": "chmc_front",
+    "ch_zero_kernel": "fill"}
 
 
 def source_hash():
@@ -395,6 +420,7 @@ def main():
     host_inputs = {}
     dev_inputs = {}
     plan = []
+    layer_rows = {}
     for h in wl.inputs:
         print(f"[bench] generating {h.name}: {wl.n_tokens} x {h.dim}", file=sys.stderr, flush=True)
         X = synth.activations(wl.wid, h.name, wl.n_tokens, h.dim, kind=h.kind,
@@ -412,6 +438,7 @@ def main():
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
         plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0], split8=grp.split8))
+        layer_rows[h.name] = [(l.name, l.rows) for l in wl.layers_of(h.name)]
     torch.cuda.synchronize()
 
     # Each calibration input (with the layers that read it) is an independent
@@ -424,8 +451,14 @@ def main():
 
     ssqr_last = {}
     hptq_last = {}
-    if args.ssqr is not None and args.hptq is not None:
-        raise SystemExit("--ssqr and --hptq are exclusive")
+    chmc_last = {}
+    if sum(a is not None for a in (args.ssqr, args.hptq, args.chmc)) > 1:
+        raise SystemExit("--ssqr, --hptq and --chmc are exclusive")
+    omegas = {}
+    if args.chmc is not None:  # the sketch the method draws: seeded Gaussian per input
+        for h in order:
+            rng = np.random.default_rng(1000 + h.dim)
+            omegas[h.name] = torch.from_numpy(rng.standard_normal((h.dim, 64))).to(dev)
 
     def step():
         for h, s in zip(order, streams):
@@ -435,6 +468,9 @@ def main():
                     ssqr_last[h.name] = grp.ssqr(chunks, Wd, args.ssqr, args.ssqr_iters)
                 elif args.hptq is not None:
                     hptq_last[h.name] = grp.hptq(chunks, Wd, args.hptq, args.ssqr_iters)
+                elif args.chmc is not None:
+                    chmc_last[h.name] = grp.chmc(chunks, Wd, layer_rows[h.name], args.chmc,
+                                                 omegas[h.name])
                 else:
                     grp.enqueue(chunks, Wd)
 
@@ -488,7 +524,7 @@ def main():
         if unit in ("flop", "op"):
             achieved = work / per_step_s / 1e12
             peak = PEAK[peak_key]
-            roofline = {"bound": "mfma",
+            roofline = {"bound": "alu" if peak_key == "f64_vec" else "mfma",
                         "achieved": achieved, "peak": peak,
                         "unit": "TFLOP/s" if unit == "flop" else "TOP/s",
                         "frac": achieved / peak, "traffic": traffic,
@@ -532,7 +568,8 @@ def main():
     # overlap, so these add up to more than the step) and weights per second
     # of the quantize phase alone, U given
     phase_of = {"hessian": "accumulate", "prepare": "prepare", "chol": "prepare",
-                "trtri": "prepare", "minpivot": "prepare", "quant": "quantize"}
+                "trtri": "prepare", "minpivot": "prepare", "quant": "quantize",
+                "chmc": "quantize"}
     phase_ms = {"accumulate": 0.0, "prepare": 0.0, "quantize": 0.0}
     for k, v in breakdown.items():
         ph = phase_of.get(k.split("_")[0])
@@ -541,7 +578,7 @@ def main():
 
     cpu = None
     if (not args.no_cpu_baseline and args.order == "workload" and args.ssqr is None
-            and args.hptq is None):
+            and args.hptq is None and args.chmc is None):
         sample_rows = args.cpu_sample_rows or 64
         cpu = cpu_baseline(wl, host_inputs, sample_rows)
 
@@ -581,6 +618,9 @@ def main():
             "sweeps_per_search": sweeps,
             "result": {k: [{"alpha": r.alpha, "bits_per_weight": r.bpw} for r in v]
                        for k, v in hptq_last.items()}},
+        "chmc": None if args.chmc is None else {
+            "bpw_target": args.chmc, "sketch": "seeded Gaussian [in_features x rank]",
+            "rank": {name: r for v in chmc_last.values() for name, r in v}},
         "cpu_baseline": cpu,
         "kernels": breakdown,
         "phases_device_ms_per_step": phase_ms,

@@ -14,9 +14,10 @@
 // orth() is CholeskyQR2 (Y^T Y = R^T R, Y R^-1, twice): the iteration depends
 // only on the span of each iterate, so any orthonormal basis gives the same
 // Q Uh up to the signs of its columns.
-// Sizes are those of a layer with a small rank (r <= 64): the products run as
-// one wave per output row with the r sketch columns across its lanes, the
-// long sums split over workgroups; everything is fp64.
+// Sizes are those of a layer with a small rank (r <= 64): the products with a
+// long inner dimension run as wave dot products (W~ times a thin matrix) or
+// one thread per column (W~^T times a thin matrix, the sum over rows split
+// over workgroups), the short ones one wave per row; everything is fp64.
 #include "common.h"
 
 namespace gptq {
@@ -103,25 +104,76 @@ __global__ __launch_bounds__(256) void ch_gemm_nn(const double* __restrict__ A, 
   C[row * q + lane] = acc;
 }
 
-// C [k x q] = A^T B, A [m x k] (ld lda), B [m x q] (ld q): one wave per row
-// of C (a column of A), lane = column of C. blockIdx.y = slice s of the sum
-// over m (rows [s mc, (s+1) mc)); with one slice the result goes to C, else
-// to part[s] (k x q each), summed in slice order by ch_sum_kernel.
+// C [m x q] = A [m x k] (ld lda) B [k x q] (ld q) for a long k: one wave per
+// row of C, the lanes across k (coalesced reads of the row of A), 8 columns
+// of C per blockIdx.y (q0 = 8 y), each summed over the wave at the end.
+__global__ __launch_bounds__(256) void ch_rowdot_kernel(const double* __restrict__ A,
+                                                        int64_t lda,
+                                                        const double* __restrict__ B, int64_t m,
+                                                        int64_t k, int q,
+                                                        double* __restrict__ C) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int q0 = blockIdx.y * 8;
+  if (row >= m) return;  // whole waves leave together
+  const int nq = q - q0 < 8 ? q - q0 : 8;
+  double acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+  const double* a = A + row * lda;
+  for (int64_t kk = lane; kk < k; kk += 64) {
+    const double av = a[kk];
+    const double* bk = B + kk * q + q0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < nq) acc[j] = fma(av, bk[j], acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    double v = acc[j];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    acc[j] = v;
+  }
+  if (lane < nq) {
+    double v = acc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j)
+      if (lane == j) v = acc[j];
+    C[row * q + q0 + lane] = v;
+  }
+}
+
+// C [k x q] = A^T B, A [m x k] (ld lda), B [m x q] (ld q): one thread per
+// column of A (coalesced across the workgroup), 8 columns of C per
+// blockIdx.z (q0 = 8 z); blockIdx.y = slice s of the sum over m (rows
+// [s mc, (s+1) mc)); with one slice the result goes to C, else to part[s]
+// (k x q each), summed in slice order by ch_sum_kernel.
 __global__ __launch_bounds__(256) void ch_gemm_tn(const double* __restrict__ A, int64_t lda,
                                                   const double* __restrict__ B, int64_t m,
                                                   int64_t k, int q, int64_t mc,
                                                   double* __restrict__ C,
                                                   double* __restrict__ part) {
-  const int64_t col = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (col >= k || lane >= q) return;
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int q0 = blockIdx.z * 8;
+  if (col >= k) return;
+  const int nq = q - q0 < 8 ? q - q0 : 8;
   const int64_t m0 = (int64_t)blockIdx.y * mc;
   const int64_t m1 = m0 + mc < m ? m0 + mc : m;
-  double acc = 0.0;
-#pragma unroll 4
-  for (int64_t r = m0; r < m1; ++r) acc = fma(A[r * lda + col], B[r * q + lane], acc);
+  double acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0;
+  for (int64_t r = m0; r < m1; ++r) {
+    const double av = A[r * lda + col];
+    const double* br = B + r * q + q0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < nq) acc[j] = fma(av, br[j], acc[j]);
+  }
   double* out = gridDim.y == 1 ? C : part + (int64_t)blockIdx.y * k * q;
-  out[col * q + lane] = acc;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < nq) out[col * q + q0 + j] = acc[j];
 }
 
 __global__ void ch_sum_kernel(const double* __restrict__ part, int ns, int64_t n,
@@ -355,119 +407,140 @@ __global__ __launch_bounds__(256) void ch_update_kernel(const double* __restrict
   }
 }
 
-// The sweep of the block [j0, j0 + bw) with one grid per group of G = 8 RPS
-// output channels (rows) and column: one workgroup of 1024 threads per
-// group; thread t holds column t % 128 of the block for the RPS rows of row
-// set t / 128, starting from Res[:, perm[j]] minus the np partial updates.
-// For each column the 8 threads of that column reduce the group's range
-// through LDS, quantize their rows and publish the scaled errors; every
-// later column of the block subtracts error * U[j][c]. Codes and grids go to
-// the original column perm[j], the errors to E in sweep order, and the
-// squared errors are added to row_loss (set on the first block).
-template <int RPS>
-__global__ __launch_bounds__(1024) void ch_sweep_kernel(
+// binary16 bits of a double that is exactly representable in binary16 and
+// not negative (a grid step): exponent and the top 10 fraction bits, or the
+// subnormal count of 2^-24; infinity gives 0x7c00.
+__device__ inline uint16_t f16_bits_of_exact(double x) {
+  if (!(x < 65536.0)) return 0x7c00;
+  const long long b = __double_as_longlong(x);
+  const int e = (int)((b >> 52) & 0x7ff) - 1023;
+  if (e >= -14) return (uint16_t)(((e + 15) << 10) | (int)((b >> 42) & 0x3ff));
+  return (uint16_t)(x * 16777216.0);  // 2^24: subnormal (or zero) count
+}
+
+// The sweep of the block [j0, j0 + bw) with one grid per group of G output
+// channels (rows) and column: one workgroup of 8 G threads per group; thread
+// (row lr = t / 8, slice cs = t % 8) holds the columns 8 s + cs (s < 16) of
+// its row, starting from Res[row][perm[j]] minus the np partial updates.
+// For column jj = 8 s + c the owners are the lanes with cs = c: each wave
+// reduces its rows' range with lane shuffles and one barrier joins the G / 8
+// wave ranges; every owner quantizes its own row, and its scaled error
+// reaches the other slices of the row by a shuffle among the row's 8 lanes,
+// which subtract error * U[jj][col] from their later columns. Codes, errors
+// and grids stay in registers until the block is done; codes and grids go to
+// the original column perm[j], the errors to E in sweep order, the squared
+// errors to row_loss (set on the first block).
+template <int G>
+__global__ __launch_bounds__(8 * G) void ch_sweep_kernel(
     const double* __restrict__ Res, int64_t rows, int64_t cols, int64_t j0, int bw,
     const double* __restrict__ part, int np, int64_t pstride, const float* __restrict__ U,
     const int32_t* __restrict__ perm, int bits, double* __restrict__ E,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
     double* __restrict__ row_loss, unsigned* __restrict__ status) {
-  constexpr int G = 8 * RPS;
+  constexpr int NT = 8 * G, NW = NT / 64;
   __shared__ float Us[CH_QB][CH_QB + 1];
-  __shared__ double mm[2][8];
-  __shared__ double el[G];
-  __shared__ double ls[G];
-  const int t = threadIdx.x, c = t & 127, rs = t >> 7;
+  __shared__ double mm[2][2][NW];
+  const int t = threadIdx.x, cs = t & 7, lr = t >> 3, wv = t >> 6, lane = t & 63;
   const int64_t grp = blockIdx.x;
-  const int64_t g0 = grp * G;
-  const int64_t r0 = g0 + rs * RPS;
+  const int64_t row = grp * G + lr;
+  const bool rv = row < rows;
   const double maxq = (double)((1 << bits) - 1);
-  if (t < G) ls[t] = 0.0;
-  for (int e = t; e < CH_QB * CH_QB; e += 1024) {
+  for (int e = t; e < CH_QB * CH_QB; e += NT) {
     const int a = e >> 7, b = e & 127;
     Us[a][b] = (a < bw && b < bw) ? U[(j0 + a) * cols + j0 + b] : 0.0f;
   }
-  const bool cv = c < bw;
-  const int64_t jc = j0 + c;
-  int64_t oc = cv ? (perm ? (int64_t)perm[jc] : jc) : 0;
-  if (oc < 0 || oc >= cols) oc = 0;  // reported as ST_BADPERM before the sweep
-  double w[RPS];
+  double w[16];
 #pragma unroll
-  for (int q = 0; q < RPS; ++q) {
-    const int64_t row = r0 + q;
+  for (int s = 0; s < 16; ++s) {
+    const int col = 8 * s + cs;
     double v = 0.0;
-    if (cv && row < rows) {
+    if (col < bw && rv) {
+      int64_t oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
+      if (oc < 0 || oc >= cols) oc = 0;  // reported as ST_BADPERM before the sweep
       v = Res[row * cols + oc];
-      for (int p = 0; p < np; ++p) v -= part[(int64_t)p * pstride + row * CH_QB + c];
+      for (int p = 0; p < np; ++p) v -= part[(int64_t)p * pstride + row * CH_QB + col];
     }
-    w[q] = v;
+    w[s] = v;
   }
+  uint32_t kq[4] = {0u, 0u, 0u, 0u};          // codes of the own columns, 8 bits each
+  uint32_t sb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // their fp16 steps
+  uint32_t zb[4] = {0u, 0u, 0u, 0u};          // their zero points
+  double lsum = 0.0;
   __syncthreads();
-  for (int jj = 0; jj < bw; ++jj) {
-    if (c == jj) {
-      double mn = 0.0, mx = 0.0;  // the range includes 0
 #pragma unroll
-      for (int q = 0; q < RPS; ++q)
-        if (r0 + q < rows) {
-          mn = fmin(mn, w[q]);
-          mx = fmax(mx, w[q]);
-        }
-      mm[0][rs] = mn;
-      mm[1][rs] = mx;
-    }
-    __syncthreads();
-    if (c == jj) {
-      double mn = mm[0][0], mx = mm[1][0];
+  for (int s = 0; s < 16; ++s) {
+    for (int c = 0; c < 8; ++c) {
+      const int jj = 8 * s + c;
+      if (jj >= bw) break;  // uniform
+      const bool own = cs == c;
+      double mn = (own && rv) ? fmin(w[s], 0.0) : 0.0;  // the range includes 0
+      double mx = (own && rv) ? fmax(w[s], 0.0) : 0.0;
 #pragma unroll
-      for (int k = 1; k < 8; ++k) {
-        mn = fmin(mn, mm[0][k]);
-        mx = fmax(mx, mm[1][k]);
+      for (int off = 8; off < 64; off <<= 1) {
+        mn = fmin(mn, __shfl_xor(mn, off, 64));
+        mx = fmax(mx, __shfl_xor(mx, off, 64));
       }
-      uint16_t sh = f64_to_f16_rne((mx - mn) / maxq);
-      double scale = f16_to_f64(sh), zero;
-      if ((sh & 0x7fff) >= 0x7c00) atomicOr(status, ST_NONFINITE);
-      if (mx == mn || scale == 0.0) {
-        scale = 1.0;
-        sh = 0x3c00;
-        zero = 0.0;
-      } else {
-        zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
+      const int buf = jj & 1;
+      if (lane == c) {
+        mm[buf][0][wv] = mn;
+        mm[buf][1][wv] = mx;
       }
-      const double rd = 1.0 / (double)Us[jj][jj];
-      if (rs == 0) {
-        scales[grp * cols + oc] = sh;
-        zeros[grp * cols + oc] = f64_to_f16_rne(zero);
-      }
+      __syncthreads();
+      mn = mm[buf][0][0];
+      mx = mm[buf][1][0];
 #pragma unroll
-      for (int q = 0; q < RPS; ++q) {
-        const int64_t row = r0 + q;
-        const double v = w[q];
+      for (int k = 1; k < NW; ++k) {
+        mn = fmin(mn, mm[buf][0][k]);
+        mx = fmax(mx, mm[buf][1][k]);
+      }
+      double scale = f16_round_f64((mx - mn) / maxq), zero = 0.0;
+      if (!(scale <= 65504.0) && t == 0) atomicOr(status, ST_NONFINITE);
+      if (mx == mn || scale == 0.0) scale = 1.0;
+      else zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
+      double e = 0.0;
+      if (own) {
+        const double v = w[s];
         const double k = fmin(fmax(rint(v / scale) + zero, 0.0), maxq);
-        const double e = (v - scale * (k - zero)) * rd;
-        double ev = 0.0;
-        if (row < rows) {
-          codes[row * cols + oc] = (uint8_t)k;
-          E[row * cols + jc] = e;
-          ls[rs * RPS + q] += e * e;
-          ev = e;
-        }
-        el[rs * RPS + q] = ev;
+        if (rv) e = (v - scale * (k - zero)) / (double)Us[jj][jj];
+        kq[s >> 2] |= (uint32_t)k << (8 * (s & 3));
+        sb[s >> 1] |= (uint32_t)f16_bits_of_exact(scale) << (16 * (s & 1));
+        zb[s >> 2] |= (uint32_t)zero << (8 * (s & 3));
+        w[s] = e;
+        lsum = fma(e, e, lsum);
       }
-    }
-    __syncthreads();
-    if (c > jj && cv) {
-      const double u = (double)Us[jj][c];
+      const double eb = __shfl(e, (lane & ~7) | c, 64);
+      if (cs > c) w[s] -= eb * (double)Us[jj][8 * s + cs];
 #pragma unroll
-      for (int q = 0; q < RPS; ++q) w[q] -= el[rs * RPS + q] * u;
+      for (int s2 = s + 1; s2 < 16; ++s2) w[s2] -= eb * (double)Us[jj][8 * s2 + cs];
     }
   }
-  __syncthreads();
-  if (t < G && g0 + t < rows) row_loss[g0 + t] = (j0 == 0 ? 0.0 : row_loss[g0 + t]) + ls[t];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int col = 8 * s + cs;
+    if (col < bw) {
+      int64_t oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
+      if (oc < 0 || oc >= cols) oc = 0;
+      if (rv) {
+        codes[row * cols + oc] = (uint8_t)(kq[s >> 2] >> (8 * (s & 3)));
+        E[row * cols + j0 + col] = w[s];
+      }
+      if (lr == 0) {
+        scales[grp * cols + oc] = (uint16_t)(sb[s >> 1] >> (16 * (s & 1)));
+        zeros[grp * cols + oc] = f64_to_f16_rne((double)((zb[s >> 2] >> (8 * (s & 3))) & 0xff));
+      }
+    }
+  }
+  // the row's loss: its 8 slices in a fixed order
+  lsum += __shfl_xor(lsum, 1, 64);
+  lsum += __shfl_xor(lsum, 2, 64);
+  lsum += __shfl_xor(lsum, 4, 64);
+  if (cs == 0 && rv) row_loss[row] = (j0 == 0 ? 0.0 : row_loss[row]) + lsum;
 }
 
 // Sum over m of A^T B in ns slices: the slice count that gives about 512
 // workgroups (each slice at least 64 rows long).
 inline int ch_slices(int64_t m, int64_t k) {
-  const int64_t wg = std::max<int64_t>(1, cdiv(k, 4));
+  const int64_t wg = std::max<int64_t>(1, cdiv(k, 256));
   int64_t s = cdiv(512, wg);
   s = std::min<int64_t>(s, std::max<int64_t>(1, m / 64));
   return (int)std::max<int64_t>(1, std::min<int64_t>(s, 64));
@@ -585,7 +658,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
                      double* C) -> gptq_status {
     const int ns = ch_slices(m, k);
     const int64_t mc = cdiv(m, ns);
-    dim3 grid(rowsg(k), (unsigned)ns);
+    dim3 grid((unsigned)cdiv(k, 256), (unsigned)ns, (unsigned)cdiv(r, 8));
     GPTQ_LAUNCH(K_CH_FRONT, st,
                 ch_gemm_tn<<<grid, 256, 0, st>>>(Am, lda, Bm, m, k, r, mc, C, Tp));
     if (ns > 1)
@@ -614,12 +687,13 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   if (r > 0) {
     GPTQ_LAUNCH(K_CH_FRONT, st,
                 ch_scale_kernel<<<grid1(o * i), 256, 0, st>>>(W, ldw, o, i, sc, Wt));
-    GPTQ_LAUNCH(K_CH_FRONT, st, ch_gemm_nn<<<rowsg(o), 256, 0, st>>>(Wt, i, omega, o, i, r, Y));
+    const dim3 gro(rowsg(o), (unsigned)cdiv(r, 8));
+    GPTQ_LAUNCH(K_CH_FRONT, st, ch_rowdot_kernel<<<gro, 256, 0, st>>>(Wt, i, omega, o, i, r, Y));
     CH_TRY(orth(Y, o, Q));
     for (int it = 0; it < CH_NITER; ++it) {
       CH_TRY(gemm_tn(Wt, i, Q, o, i, Z));  // Z = W~^T Q [i x r]
       CH_TRY(orth(Z, i, Zq));
-      GPTQ_LAUNCH(K_CH_FRONT, st, ch_gemm_nn<<<rowsg(o), 256, 0, st>>>(Wt, i, Zq, o, i, r, Y));
+      GPTQ_LAUNCH(K_CH_FRONT, st, ch_rowdot_kernel<<<gro, 256, 0, st>>>(Wt, i, Zq, o, i, r, Y));
       CH_TRY(orth(Y, o, Q));
     }
     CH_TRY(gemm_tn(Wt, i, Q, o, i, Z));
@@ -647,14 +721,14 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
       GPTQ_LAUNCH(K_CH_UPDATE, st,
                   ch_update_kernel<<<grid, 256, 0, st>>>(E, U, o, i, j0, bw, ks, part, L.pstride));
     }
-#define CH_SWEEP(RPS)                                                                           \
+#define CH_SWEEP(GS)                                                                            \
   GPTQ_LAUNCH(K_CH_SWEEP, st,                                                                    \
-              ch_sweep_kernel<RPS><<<ngr, 1024, 0, st>>>(Res, o, i, j0, bw, part, np, L.pstride, \
+              ch_sweep_kernel<GS><<<ngr, 8 * GS, 0, st>>>(Res, o, i, j0, bw, part, np, L.pstride, \
                                                          U, perm, bits, E, codes, scales, zeros, \
                                                          row_loss, status))
-    if (group_size == 32) CH_SWEEP(4);
-    else if (group_size == 64) CH_SWEEP(8);
-    else CH_SWEEP(16);
+    if (group_size == 32) CH_SWEEP(32);
+    else if (group_size == 64) CH_SWEEP(64);
+    else CH_SWEEP(128);
 #undef CH_SWEEP
   }
   if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;

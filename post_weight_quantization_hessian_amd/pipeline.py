@@ -32,6 +32,11 @@ def hessian_mode(mode, dim):
     return mode == "split8"
 
 
+def torch_empty_bytes(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 class LayerGroup:
     def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
                  device, min_pivot=False, hessian="exact"):
@@ -67,10 +72,12 @@ class LayerGroup:
 
     def _factor(self, chunks):
         n = 0
+        self.n = 0
         for ci, c in enumerate(chunks):
             G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0),
                                  split8=self.split8)
             n += int(c.shape[0])
+        self.n = n
         G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
                        workspace=self.pws, out=(self.perm, self.U), sync=False,
                        min_pivot=self.min_pivot)
@@ -105,10 +112,37 @@ class LayerGroup:
         return [G.hptq_search(W, self.U, perm, bits=b, group_size=self.group_size,
                               budget=budget, iters=iters) for b in self.bits]
 
+    def chmc(self, chunks, W, layers, bpw, omega):
+        """Hessian and factor as in enqueue, then the CHMC layer (CHMC article,
+        Methodik, Schritt 1-3) for each layer of the stack ``W`` (``layers``:
+        (name, rows) in stacking order) and bit width, the rank from the budget
+        ``bpw``, without synchronizing. Returns [(name, rank)]."""
+        self._factor(chunks)
+        perm = self.perm if (self.act_order or self.min_pivot) else None
+        if not hasattr(self, "cws"):
+            self.cws = {}
+        out, r0 = [], 0
+        for name, rows in layers:
+            for b in self.bits:
+                r = G.chmc_rank(rows, self.dim, b, self.group_size, bpw)
+                key = (name, b)
+                if key not in self.cws:
+                    self.cws[key] = torch_empty_bytes(G.chmc_workspace_bytes(rows, self.dim, r),
+                                                      W.device)
+                G.chmc_layer(W[r0:r0 + rows], self.S, self.n, self.U, perm, omega, rank=r,
+                             bits=b, group_size=self.group_size, bpw_target=bpw, sync=False,
+                             workspace=self.cws[key])
+            out.append((name, r))
+            r0 += rows
+        self._chmc = True
+        return out
+
     def check(self):
         """Synchronize and raise GPTQError if prepare or quantize reported one
         (a non-SPD Hessian, non-finite values, an invalid permutation)."""
         G.workspace_status(self.pws)
+        for ws in getattr(self, "cws", {}).values():
+            G.workspace_status(ws)
         if self._swept:  # (the SSQR search checks its own sweeps)
             for ws in self.qws:
                 G.workspace_status(ws)
