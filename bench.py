@@ -487,13 +487,18 @@ def main():
     check_status()
     prof_warm = G.profile_read()
     G.profile_enable(False)
-    dominant = max(prof_warm, key=lambda k: prof_warm[k][0])
     # sweeps per layer and bit width in a step: one, or the SSQR search's
     # probes (sweep launches over the launches of one sweep of every layer)
     sweeps = 1.0
     if args.ssqr is not None or args.hptq is not None:
         per_sweep = sum(len(wl.bits) * -(-h.dim // 128) for h in plan)
         sweeps = prof_warm["quant_sweep"][1] / max(args.warmup, 1) / per_sweep
+    # the dominant kernel: the most device time among the classes with a work
+    # model (the status fills and init kernels have none; on launch-bound
+    # shapes their event times also carry the host's submission gaps)
+    modelled = [k for k in prof_warm
+                if prof_warm[k][1] > 0 and kernel_work(k, wl, plan, sweeps)[0] is not None]
+    dominant = max(modelled or list(prof_warm), key=lambda k: prof_warm[k][0])
 
     # ---- timed steps: the dominant kernel's launches of the last step are
     # bracketed by HIP events on their stream (an event pair per launch sits

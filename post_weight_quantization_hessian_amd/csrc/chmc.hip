@@ -26,6 +26,7 @@ constexpr int CH_RMAX = 64;   // rank (sketch columns) at most
 constexpr int CH_NITER = 5;   // power iterations (CHMC article, Schritt 1)
 constexpr int CH_QB = 128;    // sweep block width
 constexpr int CH_KS = 256;    // shortest K piece of the block update
+constexpr int CH_RP = 2;      // rows per lane in the residual sweep (1 and 4 measured slower)
 
 __global__ void ch_zero_kernel(unsigned* __restrict__ p, int64_t n) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
@@ -419,53 +420,71 @@ __device__ inline uint16_t f16_bits_of_exact(double x) {
 }
 
 // The sweep of the block [j0, j0 + bw) with one grid per group of G output
-// channels (rows) and column: one workgroup of 8 G threads per group; thread
-// (row lr = t / 8, slice cs = t % 8) holds the columns 8 s + cs (s < 16) of
-// its row, starting from Res[row][perm[j]] minus the np partial updates.
-// For column jj = 8 s + c the owners are the lanes with cs = c: each wave
-// reduces its rows' range with lane shuffles and one barrier joins the G / 8
-// wave ranges; every owner quantizes its own row, and its scaled error
-// reaches the other slices of the row by a shuffle among the row's 8 lanes,
-// which subtract error * U[jj][col] from their later columns. Codes, errors
-// and grids stay in registers until the block is done; codes and grids go to
-// the original column perm[j], the errors to E in sweep order, the squared
-// errors to row_loss (set on the first block).
-template <int G>
-__global__ __launch_bounds__(8 * G) void ch_sweep_kernel(
+// channels (rows) and column: one workgroup of 8 G / RP threads per group;
+// thread (row set lr = t / 8, slice cs = t % 8) holds the columns 8 s + cs
+// (s < 16) of its RP rows lr RP .. lr RP + RP - 1, starting from
+// Res[row][perm[j]] minus the np partial updates. For column jj = 8 s + c
+// the owners are the lanes with cs = c: each wave reduces its rows' range
+// with lane shuffles and one barrier joins the wave ranges; every owner
+// quantizes its own rows, and their scaled errors reach the other slices of
+// the rows by a shuffle among the 8 lanes, which subtract error * U[jj][col]
+// from their later columns. The grid arithmetic is the same in every wave,
+// so fewer, fuller waves (RP rows per lane) issue less of it. Codes, errors
+// and grids stay in registers until the block is done; codes and grids go
+// to the original column perm[j], the errors to E in sweep order, the
+// squared errors to row_loss (set on the first block).
+template <int G, int RP>
+__global__ __launch_bounds__(8 * G / RP) void ch_sweep_kernel(
     const double* __restrict__ Res, int64_t rows, int64_t cols, int64_t j0, int bw,
     const double* __restrict__ part, int np, int64_t pstride, const float* __restrict__ U,
     const int32_t* __restrict__ perm, int bits, double* __restrict__ E,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
     double* __restrict__ row_loss, unsigned* __restrict__ status) {
-  constexpr int NT = 8 * G, NW = NT / 64;
+  constexpr int NT = 8 * G / RP, NW = NT / 64;
+  static_assert(NT % 64 == 0, "whole waves");
   __shared__ float Us[CH_QB][CH_QB + 1];
   __shared__ double mm[2][2][NW];
   const int t = threadIdx.x, cs = t & 7, lr = t >> 3, wv = t >> 6, lane = t & 63;
   const int64_t grp = blockIdx.x;
-  const int64_t row = grp * G + lr;
-  const bool rv = row < rows;
+  const int64_t row0 = grp * G + (int64_t)lr * RP;
+  bool rv[RP];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) rv[p] = row0 + p < rows;
   const double maxq = (double)((1 << bits) - 1);
   for (int e = t; e < CH_QB * CH_QB; e += NT) {
     const int a = e >> 7, b = e & 127;
     Us[a][b] = (a < bw && b < bw) ? U[(j0 + a) * cols + j0 + b] : 0.0f;
   }
-  double w[16];
+  double w[RP][16];
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const int col = 8 * s + cs;
-    double v = 0.0;
-    if (col < bw && rv) {
-      int64_t oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
+    int64_t oc = 0;
+    if (col < bw) {
+      oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
       if (oc < 0 || oc >= cols) oc = 0;  // reported as ST_BADPERM before the sweep
-      v = Res[row * cols + oc];
-      for (int p = 0; p < np; ++p) v -= part[(int64_t)p * pstride + row * CH_QB + col];
     }
-    w[s] = v;
+#pragma unroll
+    for (int p = 0; p < RP; ++p) {
+      double v = 0.0;
+      if (col < bw && rv[p]) {
+        const int64_t row = row0 + p;
+        v = Res[row * cols + oc];
+        for (int q = 0; q < np; ++q) v -= part[(int64_t)q * pstride + row * CH_QB + col];
+      }
+      w[p][s] = v;
+    }
   }
-  uint32_t kq[4] = {0u, 0u, 0u, 0u};          // codes of the own columns, 8 bits each
+  uint32_t kq[RP][4];                          // codes of the own columns, 8 bits each
   uint32_t sb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // their fp16 steps
   uint32_t zb[4] = {0u, 0u, 0u, 0u};          // their zero points
-  double lsum = 0.0;
+  double lsum[RP];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    lsum[p] = 0.0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kq[p][q] = 0u;
+  }
   __syncthreads();
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
@@ -473,8 +492,13 @@ __global__ __launch_bounds__(8 * G) void ch_sweep_kernel(
       const int jj = 8 * s + c;
       if (jj >= bw) break;  // uniform
       const bool own = cs == c;
-      double mn = (own && rv) ? fmin(w[s], 0.0) : 0.0;  // the range includes 0
-      double mx = (own && rv) ? fmax(w[s], 0.0) : 0.0;
+      double mn = 0.0, mx = 0.0;  // the range includes 0
+#pragma unroll
+      for (int p = 0; p < RP; ++p)
+        if (own && rv[p]) {
+          mn = fmin(mn, w[p][s]);
+          mx = fmax(mx, w[p][s]);
+        }
 #pragma unroll
       for (int off = 8; off < 64; off <<= 1) {
         mn = fmin(mn, __shfl_xor(mn, off, 64));
@@ -497,21 +521,39 @@ __global__ __launch_bounds__(8 * G) void ch_sweep_kernel(
       if (!(scale <= 65504.0) && t == 0) atomicOr(status, ST_NONFINITE);
       if (mx == mn || scale == 0.0) scale = 1.0;
       else zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
-      double e = 0.0;
+      double e[RP];
+      const double ujj = (double)Us[jj][jj];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        e[p] = 0.0;
+        if (own) {
+          const double v = w[p][s];
+          const double k = fmin(fmax(rint(v / scale) + zero, 0.0), maxq);
+          if (rv[p]) e[p] = (v - scale * (k - zero)) / ujj;
+          kq[p][s >> 2] |= (uint32_t)k << (8 * (s & 3));
+          w[p][s] = e[p];
+          lsum[p] = fma(e[p], e[p], lsum[p]);
+        }
+      }
       if (own) {
-        const double v = w[s];
-        const double k = fmin(fmax(rint(v / scale) + zero, 0.0), maxq);
-        if (rv) e = (v - scale * (k - zero)) / (double)Us[jj][jj];
-        kq[s >> 2] |= (uint32_t)k << (8 * (s & 3));
         sb[s >> 1] |= (uint32_t)f16_bits_of_exact(scale) << (16 * (s & 1));
         zb[s >> 2] |= (uint32_t)zero << (8 * (s & 3));
-        w[s] = e;
-        lsum = fma(e, e, lsum);
       }
-      const double eb = __shfl(e, (lane & ~7) | c, 64);
-      if (cs > c) w[s] -= eb * (double)Us[jj][8 * s + cs];
+      const int src = (lane & ~7) | c;
+      double eb[RP];
 #pragma unroll
-      for (int s2 = s + 1; s2 < 16; ++s2) w[s2] -= eb * (double)Us[jj][8 * s2 + cs];
+      for (int p = 0; p < RP; ++p) eb[p] = __shfl(e[p], src, 64);
+      if (cs > c) {
+        const double u = (double)Us[jj][8 * s + cs];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) w[p][s] -= eb[p] * u;
+      }
+#pragma unroll
+      for (int s2 = s + 1; s2 < 16; ++s2) {
+        const double u = (double)Us[jj][8 * s2 + cs];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) w[p][s2] -= eb[p] * u;
+      }
     }
   }
 #pragma unroll
@@ -520,21 +562,28 @@ __global__ __launch_bounds__(8 * G) void ch_sweep_kernel(
     if (col < bw) {
       int64_t oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
       if (oc < 0 || oc >= cols) oc = 0;
-      if (rv) {
-        codes[row * cols + oc] = (uint8_t)(kq[s >> 2] >> (8 * (s & 3)));
-        E[row * cols + j0 + col] = w[s];
-      }
+#pragma unroll
+      for (int p = 0; p < RP; ++p)
+        if (rv[p]) {
+          const int64_t row = row0 + p;
+          codes[row * cols + oc] = (uint8_t)(kq[p][s >> 2] >> (8 * (s & 3)));
+          E[row * cols + j0 + col] = w[p][s];
+        }
       if (lr == 0) {
         scales[grp * cols + oc] = (uint16_t)(sb[s >> 1] >> (16 * (s & 1)));
         zeros[grp * cols + oc] = f64_to_f16_rne((double)((zb[s >> 2] >> (8 * (s & 3))) & 0xff));
       }
     }
   }
-  // the row's loss: its 8 slices in a fixed order
-  lsum += __shfl_xor(lsum, 1, 64);
-  lsum += __shfl_xor(lsum, 2, 64);
-  lsum += __shfl_xor(lsum, 4, 64);
-  if (cs == 0 && rv) row_loss[row] = (j0 == 0 ? 0.0 : row_loss[row]) + lsum;
+  // each row's loss: its 8 slices in a fixed order
+#pragma unroll
+  for (int p = 0; p < RP; ++p) {
+    double l = lsum[p];
+    l += __shfl_xor(l, 1, 64);
+    l += __shfl_xor(l, 2, 64);
+    l += __shfl_xor(l, 4, 64);
+    if (cs == 0 && rv[p]) row_loss[row0 + p] = (j0 == 0 ? 0.0 : row_loss[row0 + p]) + l;
+  }
 }
 
 // Sum over m of A^T B in ns slices: the slice count that gives about 512
@@ -723,7 +772,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
     }
 #define CH_SWEEP(GS)                                                                            \
   GPTQ_LAUNCH(K_CH_SWEEP, st,                                                                    \
-              ch_sweep_kernel<GS><<<ngr, 8 * GS, 0, st>>>(Res, o, i, j0, bw, part, np, L.pstride, \
+              ch_sweep_kernel<GS, CH_RP><<<ngr, 8 * GS / CH_RP, 0, st>>>(Res, o, i, j0, bw, part, np, L.pstride, \
                                                          U, perm, bits, E, codes, scales, zeros, \
                                                          row_loss, status))
     if (group_size == 32) CH_SWEEP(32);
