@@ -164,7 +164,23 @@ __global__ __launch_bounds__(256) void ch_gemm_tn(const double* __restrict__ A, 
   double acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-  for (int64_t r = m0; r < m1; ++r) {
+  // four rows per step, their loads issued together (the sums keep the row
+  // order)
+  int64_t r = m0;
+  for (; r + 4 <= m1; r += 4) {
+    double av[4], bv[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = A[(r + u) * lda + col];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[u][j] = j < nq ? B[(r + u) * q + q0 + j] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fma(av[u], bv[u][j], acc[j]);
+  }
+  for (; r < m1; ++r) {
     const double av = A[r * lda + col];
     const double* br = B + r * q + q0;
 #pragma unroll
@@ -182,6 +198,7 @@ __global__ void ch_sum_kernel(const double* __restrict__ part, int ns, int64_t n
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
        e += (int64_t)gridDim.x * blockDim.x) {
     double s = 0.0;
+#pragma unroll 8
     for (int p = 0; p < ns; ++p) s += part[(int64_t)p * n + e];
     C[e] = s;
   }
