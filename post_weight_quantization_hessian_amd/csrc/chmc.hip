@@ -79,14 +79,16 @@ __global__ __launch_bounds__(1024) void ch_energy_kernel(const double* __restric
   }
 }
 
-// Wt[r][j] = W[r][j] * sc[j] (fp64, ld i).
+// Wt[r][j] = W[r][j] * sc[j] (fp64, ld i); a NaN/Inf weight sets ST_NONFINITE.
 __global__ void ch_scale_kernel(const uint16_t* __restrict__ W, int64_t ldw, int64_t o,
                                 int64_t i, const double* __restrict__ sc,
-                                double* __restrict__ Wt) {
+                                double* __restrict__ Wt, unsigned* __restrict__ status) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < o * i;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t r = e / i, j = e - r * i;
-    Wt[e] = f16_to_f64(W[r * ldw + j]) * sc[j];
+    const double v = f16_to_f64(W[r * ldw + j]);
+    if (!isfinite(v)) atomicOr(status, ST_NONFINITE);
+    Wt[e] = v * sc[j];
   }
 }
 
@@ -208,7 +210,8 @@ __global__ void ch_sum_kernel(const double* __restrict__ part, int ns, int64_t n
 // wave, the matrices in LDS: right-looking Cholesky by rows (lane = column),
 // then every lane back-substitutes its column of the inverse. A pivot that
 // is not above 1e-15 of its diagonal entry of G (the sketch has lost rank:
-// the weighted W has rank below q) or not finite sets ST_NOTSPD.
+// the weighted W has rank below q) sets ST_NOTSPD, a pivot that is not
+// finite (a NaN or Inf weight) ST_NONFINITE.
 __global__ __launch_bounds__(64) void ch_chol_inv_kernel(const double* __restrict__ G, int q,
                                                          double* __restrict__ Rinv,
                                                          unsigned* __restrict__ status) {
@@ -217,11 +220,13 @@ __global__ __launch_bounds__(64) void ch_chol_inv_kernel(const double* __restric
   const int l = threadIdx.x;
   for (int e = l; e < q * q; e += 64) a[e / q][e % q] = G[e];
   __syncthreads();
-  bool bad = false;
+  bool bad = false, nonfin = false;
   for (int k = 0; k < q; ++k) {
     const double piv = a[k][k];
-    const bool ok = piv > 1e-15 * G[k * q + k] && isfinite(piv);
-    bad = bad || !ok;
+    const bool fin = isfinite(piv) && isfinite(G[k * q + k]);
+    const bool ok = fin && piv > 1e-15 * G[k * q + k];
+    bad = bad || (fin && !ok);
+    nonfin = nonfin || !fin;
     const double rkk = sqrt(ok ? piv : 1.0);
     __syncthreads();
     if (l > k && l < q) a[k][l] /= rkk;  // row k of R, right of the diagonal
@@ -232,6 +237,7 @@ __global__ __launch_bounds__(64) void ch_chol_inv_kernel(const double* __restric
     __syncthreads();
   }
   if (l == 0 && bad) atomicOr(status, ST_NOTSPD);
+  if (l == 0 && nonfin) atomicOr(status, ST_NONFINITE);
   // column l of R^-1 (upper triangular) by back substitution
   if (l < q) {
     for (int r = l; r >= 0; --r) {
@@ -752,7 +758,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   } while (0)
   if (r > 0) {
     GPTQ_LAUNCH(K_CH_FRONT, st,
-                ch_scale_kernel<<<grid1(o * i), 256, 0, st>>>(W, ldw, o, i, sc, Wt));
+                ch_scale_kernel<<<grid1(o * i), 256, 0, st>>>(W, ldw, o, i, sc, Wt, status));
     const dim3 gro(rowsg(o), (unsigned)cdiv(r, 8));
     GPTQ_LAUNCH(K_CH_FRONT, st, ch_rowdot_kernel<<<gro, 256, 0, st>>>(Wt, i, omega, o, i, r, Y));
     CH_TRY(orth(Y, o, Q));

@@ -186,3 +186,15 @@ def test_chmc_bad_permutation_is_rejected():
     with pytest.raises(G.GPTQError) as e:
         G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, bad, om, rank=2)
     assert e.value.status == G.GPTQ_EINVAL
+
+
+@pytest.mark.parametrize("rank", [0, 2])
+def test_chmc_nonfinite_weight_is_reported(rank):
+    say(f"chmc NaN weight, rank {rank}")
+    W, X = problem(64, 128, 300, 6)
+    S, perm, U = gpu_inputs(X, True)
+    W[3, 17] = np.nan
+    om = torch.from_numpy(np.random.default_rng(1).standard_normal((128, 2))).to(DEV)
+    with pytest.raises(G.GPTQError) as e:
+        G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, perm, om, rank=rank)
+    assert e.value.status == G.GPTQ_ENONFINITE
