@@ -517,6 +517,20 @@ def main():
     check_status()
 
     ms_per_step = 1000.0 * elapsed / args.steps
+    # the spread: five more steps, each alone between two synchronizations
+    # (after the timed steps, so the K-step figure above is untouched)
+    reps = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        reps.append(1000.0 * (time.perf_counter() - t1))
+    check_status()
+    reps.sort()
+    step_repeats = {"n": len(reps), "median_ms": reps[len(reps) // 2], "min_ms": reps[0],
+                    "max_ms": reps[-1],
+                    "note": "single steps, each between two device synchronizations"}
     weights = wl.weights_per_step()
     value = weights * args.steps / elapsed
 
@@ -627,6 +641,7 @@ def main():
             "bpw_target": args.chmc, "sketch": "seeded Gaussian [in_features x rank]",
             "rank": {name: r for v in chmc_last.values() for name, r in v}},
         "cpu_baseline": cpu,
+        "step_repeats": step_repeats,
         "kernels": breakdown,
         "phases_device_ms_per_step": phase_ms,
         "quantize_only_weights_per_s": (weights / (phase_ms["quantize"] / 1000.0)
