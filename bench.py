@@ -382,7 +382,29 @@ def cpu_baseline(wl, host_inputs, sample_rows):
     return {"value": weights / t_total, "unit": "weights/s", "cores": int(threads),
             "kind": "oracle", "sample": "; ".join(sampled) + " (each phase scaled to the "
             "full step by its operation count)",
-            "seconds_per_step_extrapolated": t_total}
+            "seconds_per_step_extrapolated": t_total, "cpu_model": host_cpu_model(),
+            "blas": numpy_blas()}
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def numpy_blas():
+    """The BLAS NumPy was built against (name and version), as NumPy reports it."""
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg["Build Dependencies"]["blas"]
+        return f"{b.get('name')} {b.get('version')}"
+    except Exception:  # older NumPy or an unexpected layout: not essential
+        return None
 
 
 # ---------------------------------------------------------------- main
