@@ -474,6 +474,7 @@ __global__ __launch_bounds__(8 * G / RP) void ch_sweep_kernel(
 #pragma unroll
   for (int p = 0; p < RP; ++p) rv[p] = row0 + p < rows;
   const double maxq = (double)((1 << bits) - 1);
+  const double rmaxq = 1.0 / maxq;
   for (int e = t; e < CH_QB * CH_QB; e += NT) {
     const int a = e >> 7, b = e & 127;
     Us[a][b] = (a < bw && b < bw) ? U[(j0 + a) * cols + j0 + b] : 0.0f;
@@ -515,6 +516,7 @@ __global__ __launch_bounds__(8 * G / RP) void ch_sweep_kernel(
       const int jj = 8 * s + c;
       if (jj >= bw) break;  // uniform
       const bool own = cs == c;
+      const double rd = 1.0 / (double)Us[jj][jj];  // off the chain: depends on jj only
       double mn = 0.0, mx = 0.0;  // the range includes 0
 #pragma unroll
       for (int p = 0; p < RP; ++p)
@@ -540,19 +542,20 @@ __global__ __launch_bounds__(8 * G / RP) void ch_sweep_kernel(
         mn = fmin(mn, mm[buf][0][k]);
         mx = fmax(mx, mm[buf][1][k]);
       }
-      double scale = f16_round_f64((mx - mn) / maxq), zero = 0.0;
+      double scale = f16_round_f64((mx - mn) * rmaxq), zero = 0.0;
       if (!(scale <= 65504.0) && t == 0) atomicOr(status, ST_NONFINITE);
-      if (mx == mn || scale == 0.0) scale = 1.0;
-      else zero = fmin(fmax(rint(-mn / scale), 0.0), maxq);
+      const bool degen = mx == mn || scale == 0.0;
+      if (degen) scale = 1.0;
+      const double rs = 1.0 / scale;
+      if (!degen) zero = fmin(fmax(rint(-mn * rs), 0.0), maxq);
       double e[RP];
-      const double ujj = (double)Us[jj][jj];
 #pragma unroll
       for (int p = 0; p < RP; ++p) {
         e[p] = 0.0;
         if (own) {
           const double v = w[p][s];
-          const double k = fmin(fmax(rint(v / scale) + zero, 0.0), maxq);
-          if (rv[p]) e[p] = (v - scale * (k - zero)) / ujj;
+          const double k = fmin(fmax(rint(v * rs) + zero, 0.0), maxq);
+          if (rv[p]) e[p] = (v - scale * (k - zero)) * rd;
           kq[p][s >> 2] |= (uint32_t)k << (8 * (s & 3));
           w[p][s] = e[p];
           lsum[p] = fma(e[p], e[p], lsum[p]);
