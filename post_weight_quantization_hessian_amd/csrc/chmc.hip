@@ -25,7 +25,7 @@ namespace gptq {
 constexpr int CH_RMAX = 64;   // rank (sketch columns) at most
 constexpr int CH_NITER = 5;   // power iterations (CHMC article, Schritt 1)
 constexpr int CH_QB = 128;    // sweep block width
-constexpr int CH_KS = 256;    // shortest K piece of the block update
+constexpr int CH_KS = 64;     // shortest K piece of the block update
 constexpr int CH_RP = 2;      // rows per lane in the residual sweep (1 and 4 measured slower)
 
 __global__ void ch_zero_kernel(unsigned* __restrict__ p, int64_t n) {
@@ -623,7 +623,7 @@ inline int ch_slices(int64_t m, int64_t k) {
 
 struct CHLayout {
   size_t status, cnt, c, sc, wt, y, q, q1, z, zq, gm, rinv, mm, uh, sig, ul, vz, res, e, tpart,
-      part, total;
+      part, psum, total;
   int pmax;
   int64_t pstride;
   CHLayout(int64_t o, int64_t i, int r) {
@@ -659,9 +659,10 @@ struct CHLayout {
     tp = std::max<int64_t>(tp, (int64_t)ch_slices(o, i) * i * r);
     tpart = take(8 * tp);
     const int64_t rt = cdiv(o, 64);
-    pmax = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(i, CH_KS), cdiv(512, rt)));
+    pmax = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(i, CH_KS), cdiv(1024, rt)));
     pstride = o * CH_QB;
     part = take(8 * (size_t)pmax * pstride);
+    psum = take(8 * (size_t)pstride);
     total = p;
   }
 };
@@ -713,6 +714,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   double *sig = (double*)(b + L.sig), *Ul = (double*)(b + L.ul), *Vz = (double*)(b + L.vz);
   double *Res = (double*)(b + L.res), *E = (double*)(b + L.e), *Tp = (double*)(b + L.tpart);
   double* part = (double*)(b + L.part);
+  double* psum = (double*)(b + L.psum);
   const int64_t o = rows, i = cols;
   const int r = rank;
   auto grid1 = [](int64_t n) {
@@ -788,6 +790,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   for (int64_t j0 = 0; j0 < i; j0 += CH_QB) {
     const int bw = (int)std::min<int64_t>(CH_QB, i - j0);
     int np = 0;
+    const double* upd = part;
     if (j0 > 0) {
       const int64_t p0 = std::min<int64_t>(L.pmax, cdiv(j0, CH_KS));
       const int64_t ks = round_up(cdiv(j0, p0), 32);
@@ -795,10 +798,18 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
       dim3 grid(rt, (unsigned)np);
       GPTQ_LAUNCH(K_CH_UPDATE, st,
                   ch_update_kernel<<<grid, 256, 0, st>>>(E, U, o, i, j0, bw, ks, part, L.pstride));
+      // the pieces summed in piece order, all values at once, so that the
+      // sweep reads one update per value
+      if (np > 1) {
+        GPTQ_LAUNCH(K_CH_UPDATE, st,
+                    ch_sum_kernel<<<grid1(L.pstride), 256, 0, st>>>(part, np, L.pstride, psum));
+        upd = psum;
+        np = 1;
+      }
     }
 #define CH_SWEEP(GS)                                                                            \
   GPTQ_LAUNCH(K_CH_SWEEP, st,                                                                    \
-              ch_sweep_kernel<GS, CH_RP><<<ngr, 8 * GS / CH_RP, 0, st>>>(Res, o, i, j0, bw, part, np, L.pstride, \
+              ch_sweep_kernel<GS, CH_RP><<<ngr, 8 * GS / CH_RP, 0, st>>>(Res, o, i, j0, bw, upd, np, L.pstride, \
                                                          U, perm, bits, E, codes, scales, zeros, \
                                                          row_loss, status))
     if (group_size == 32) CH_SWEEP(32);
