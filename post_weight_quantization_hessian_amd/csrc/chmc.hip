@@ -446,13 +446,15 @@ __device__ inline uint16_t f16_bits_of_exact(double x) {
 // channels (rows) and column: one workgroup of 8 G / RP threads per group;
 // thread (row set lr = t / 8, slice cs = t % 8) holds the columns 8 s + cs
 // (s < 16) of its RP rows lr RP .. lr RP + RP - 1, starting from
-// Res[row][perm[j]] minus the np partial updates. For column jj = 8 s + c
+// Res[row][perm[j]] minus the np update sums. For column jj = 8 s + c
 // the owners are the lanes with cs = c: each wave reduces its rows' range
 // with lane shuffles and one barrier joins the wave ranges; every owner
 // quantizes its own rows, and their scaled errors reach the other slices of
 // the rows by a shuffle among the 8 lanes, which subtract error * U[jj][col]
 // from their later columns. The grid arithmetic is the same in every wave,
-// so fewer, fuller waves (RP rows per lane) issue less of it. Codes, errors
+// so fewer, fuller waves (RP rows per lane) issue less of it; the step and
+// U[jj][jj] enter as reciprocals (one division per column each, the latter
+// off the row chain), as in the GPTQ sweep. Codes, errors
 // and grids stay in registers until the block is done; codes and grids go
 // to the original column perm[j], the errors to E in sweep order, the
 // squared errors to row_loss (set on the first block).
