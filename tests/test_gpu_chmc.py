@@ -198,3 +198,39 @@ def test_chmc_nonfinite_weight_is_reported(rank):
     with pytest.raises(G.GPTQError) as e:
         G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, perm, om, rank=rank)
     assert e.value.status == G.GPTQ_ENONFINITE
+
+
+def test_chmc_square_2048_g64_sampled():
+    """2048 x 2048 (the TinyLlama attention output shape), 3 bits, groups of
+    64 output rows, act-order, rank from a 3.5-bit budget: the oracle's
+    factors in full and its residual sweep for one sampled row group."""
+    rows = cols = 2048
+    n, gs, bits, bpw = 2048, 64, 3, 3.5
+    say("chmc 2048x2048 b3 g64, sampled row group")
+    W, X = problem(rows, cols, n, 77, lowrank=4)
+    S, perm, U = gpu_inputs(X, True)
+    om = np.random.default_rng(78).standard_normal((cols, 64))
+    res = G.chmc_layer(torch.from_numpy(W).to(DEV), S, n, U, perm, torch.from_numpy(om).to(DEV),
+                       bits=bits, group_size=gs, bpw_target=bpw)
+    Sr, nr = O.hessian_sum(X)
+    r = O.chmc_rank(rows, cols, bits, gs, bpw)
+    assert r > 0 and res.rank == r
+    c = O.chmc_energies(np.diag(Sr), nr)
+    A, B = O.chmc_lowrank(W.astype(np.float64), c, om[:, :r], 5)
+    ref = {"rank": r, "A": A, "B": B}
+    H = O.damped_hessian(Sr, nr, 0.01)
+    pr = O.act_order_perm(H)
+    assert np.array_equal(perm.cpu().numpy(), pr)
+    Ur = O.hinv_upper(O.permute_sym(H, pr))
+    g = 17
+    rs = slice(g * gs, (g + 1) * gs)
+    R = W.astype(np.float64)[rs] - A[rs] @ B
+    sw = O.gptq_sweep_outgroups(R[:, pr], Ur, bits, gs)
+    for key in ("codes", "scales", "zeros"):
+        a = np.empty_like(sw[key])
+        a[:, pr] = sw[key]
+        ref[key] = a
+    ref["row_loss"] = sw["row_loss"]
+    sub = G.CHMCLayer(res.A, res.B, res.codes[rs], res.scales[g:g + 1], res.zeros[g:g + 1],
+                      res.row_loss[rs], r, bits, gs)
+    compare_chmc(sub, ref, f"chmc 2048, row group {g}")
