@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--hessian", choices=("auto", "exact", "split8"), default="auto",
                     help="Hessian products: exact fp64, int8 digit slices, or split8 from "
                          "256 input features on (auto)")
+    ap.add_argument("--no-clip", action="store_true",
+                    help="the no-clipping sweep: levels are not clamped to [0, maxq]")
     ap.add_argument("--ssqr", type=float, default=None, metavar="TARGET",
                     help="quantize with SSQR instead: bisection on the scale factor for at "
                          "most this outlier fraction (every probe is a full sweep)")
@@ -457,6 +459,7 @@ def main():
         grp = LayerGroup(h.dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
                          bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
                          min_pivot=args.order == "min_pivot", hessian=args.hessian,
+                         clip=not args.no_clip,
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
         plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0], split8=grp.split8))
@@ -619,7 +622,7 @@ def main():
 
     cpu = None
     if (not args.no_cpu_baseline and args.order == "workload" and args.ssqr is None
-            and args.hptq is None and args.chmc is None):
+            and args.hptq is None and args.chmc is None and not args.no_clip):
         sample_rows = args.cpu_sample_rows or 64
         cpu = cpu_baseline(wl, host_inputs, sample_rows)
 
@@ -641,6 +644,7 @@ def main():
                    "n_tokens": wl.n_tokens, "token_chunk": wl.token_chunk,
                    "bits": list(wl.bits), "group_size": wl.group_size,
                    "act_order": wl.act_order and args.order == "workload",
+                   "clip": not args.no_clip,
                    "order": "min_pivot" if args.order == "min_pivot" else
                    ("act_order" if wl.act_order else "none"), "damp": wl.damp,
                    "weights_per_step": weights,

@@ -39,12 +39,13 @@ def torch_empty_bytes(nbytes, device):
 
 class LayerGroup:
     def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
-                 device, min_pivot=False, hessian="exact"):
+                 device, min_pivot=False, hessian="exact", clip=True):
         import torch
         self.dim, self.rows = int(dim), int(rows)
         self.bits, self.group_size = tuple(bits), int(group_size)
         self.act_order, self.damp = bool(act_order), float(damp)
         self.min_pivot = bool(min_pivot)  # the min-pivot order instead of act-order
+        self.clip = bool(clip)  # False: the no-clipping sweep (codes may leave [0, maxq])
         if self.min_pivot:
             self.act_order = False
         ng = -(-self.dim // self.group_size)
@@ -91,7 +92,7 @@ class LayerGroup:
             G.quantize_layer(W, self.U, self.perm if (self.act_order or self.min_pivot) else None,
                              bits=b,
                              group_size=self.group_size, workspace=self.qws[bi],
-                             out=self.outs[bi], sync=False)
+                             out=self.outs[bi], sync=False, clip=self.clip)
         return self.outs
 
     def ssqr(self, chunks, W, target, iters=12):
