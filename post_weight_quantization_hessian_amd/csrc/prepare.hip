@@ -40,29 +40,37 @@ __global__ __launch_bounds__(1024) void prep_diag_kernel(const double* __restric
 
 // perm[rank(k)] = k with rank(k) = #{j : hd[j] > hd[k] or (hd[j] == hd[k] and
 // j < k)}: the stable order of descending damped diagonal. Identity if !act.
+// 16 lanes per key, each counting every 16th j of the staged tiles, the 16
+// counts summed with lane shuffles: n/16 workgroups of 16 keys, so that a few
+// thousand features fill the GPU.
 __global__ __launch_bounds__(256) void prep_perm_kernel(const double* __restrict__ hd, int64_t n,
                                                         bool act, int32_t* __restrict__ perm) {
   __shared__ double tile[1024];
-  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (!act) {
-    if (k < n) perm[k] = (int32_t)k;
+  const int kl = threadIdx.x >> 4, jl = threadIdx.x & 15;
+  const int64_t k = (int64_t)blockIdx.x * 16 + kl;
+  if (!act) {  // uniform
+    if (k < n && jl == 0) perm[k] = (int32_t)k;
     return;
   }
   const double mine = k < n ? hd[k] : 0.0;
-  int64_t rank = 0;
+  int rank = 0;  // < n < 2^31 (perm is int32)
   for (int64_t j0 = 0; j0 < n; j0 += 1024) {
-    const int64_t m = (n - j0) < 1024 ? (n - j0) : 1024;
+    const int m = (int)((n - j0) < 1024 ? (n - j0) : 1024);
     __syncthreads();
     for (int q = threadIdx.x; q < m; q += blockDim.x) tile[q] = hd[j0 + q];
     __syncthreads();
     if (k < n) {
-      for (int q = 0; q < m; ++q) {
+      for (int q = jl; q < m; q += 16) {
         const double v = tile[q];
         rank += (v > mine) || (v == mine && j0 + q < k);
       }
     }
   }
-  if (k < n) perm[rank] = (int32_t)k;
+  rank += __shfl_xor(rank, 1, 16);
+  rank += __shfl_xor(rank, 2, 16);
+  rank += __shfl_xor(rank, 4, 16);
+  rank += __shfl_xor(rank, 8, 16);
+  if (k < n && jl == 0) perm[rank] = (int32_t)k;
 }
 
 // Lower triangle of K (ip x ip, ld ip): K[a][b] = H[p_a][p_b], p_x = perm[n-1-x],
@@ -1191,7 +1199,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     }
   } else {
     GPTQ_LAUNCH(K_PREP_PERM, st,
-                prep_perm_kernel<<<(unsigned)cdiv(n, 256), 256, 0, st>>>(
+                prep_perm_kernel<<<(unsigned)cdiv(n, 16), 256, 0, st>>>(
                     hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
   }
   GPTQ_LAUNCH(K_PREP_GATHER, st,
