@@ -234,3 +234,21 @@ def test_chmc_square_2048_g64_sampled():
     sub = G.CHMCLayer(res.A, res.B, res.codes[rs], res.scales[g:g + 1], res.zeros[g:g + 1],
                       res.row_loss[rs], r, bits, gs)
     compare_chmc(sub, ref, f"chmc 2048, row group {g}")
+
+
+def test_chmc_strided_weight_matches_contiguous():
+    """W given as a column slice of a wider matrix (row stride > cols): the
+    same results as the contiguous copy, bit for bit."""
+    say("chmc strided W (ldw 300 > cols 256)")
+    W, X = problem(96, 256, 600, 9, lowrank=2)
+    S, perm, U = gpu_inputs(X, True)
+    om = torch.from_numpy(np.random.default_rng(2).standard_normal((256, 4))).to(DEV)
+    wide = torch.zeros((96, 300), dtype=torch.float16, device=DEV)
+    wide[:, 17:17 + 256] = torch.from_numpy(W).to(DEV)
+    Ws = wide[:, 17:17 + 256]
+    assert Ws.stride(0) == 300
+    a = G.chmc_layer(Ws, S, 600, U, perm, om, rank=4, group_size=32)
+    b = G.chmc_layer(torch.from_numpy(W).to(DEV), S, 600, U, perm, om, rank=4, group_size=32)
+    for x, y in ((a.A, b.A), (a.B, b.B), (a.codes, b.codes), (a.scales, b.scales),
+                 (a.zeros, b.zeros), (a.row_loss, b.row_loss)):
+        assert torch.equal(x, y)
