@@ -252,3 +252,25 @@ def test_chmc_strided_weight_matches_contiguous():
     for x, y in ((a.A, b.A), (a.B, b.B), (a.codes, b.codes), (a.scales, b.scales),
                  (a.zeros, b.zeros), (a.row_loss, b.row_loss)):
         assert torch.equal(x, y)
+
+
+def test_chmc_no_sync_reports_through_the_workspace():
+    """With GPTQ_FLAG_NO_SYNC the call returns after enqueueing; the status
+    is read from the workspace afterwards (a bad permutation here)."""
+    say("chmc no-sync: status from the workspace")
+    W, X = problem(64, 128, 300, 10)
+    S, perm, U = gpu_inputs(X, True)
+    om = torch.from_numpy(np.random.default_rng(3).standard_normal((128, 2))).to(DEV)
+    ws = torch.empty(G.chmc_workspace_bytes(64, 128, 2), dtype=torch.uint8, device=DEV)
+    good = G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, perm, om, rank=2, sync=False,
+                        workspace=ws)
+    G.workspace_status(ws)  # no error
+    ref = G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, perm, om, rank=2)
+    assert torch.equal(good.codes, ref.codes) and torch.equal(good.A, ref.A)
+    bad = perm.clone()
+    bad[1] = bad[0]  # a repeated entry
+    G.chmc_layer(torch.from_numpy(W).to(DEV), S, 300, U, bad, om, rank=2, sync=False,
+                 workspace=ws)
+    with pytest.raises(G.GPTQError) as e:
+        G.workspace_status(ws)
+    assert e.value.status == G.GPTQ_EINVAL
