@@ -320,6 +320,13 @@ int gptq_version(void);
  *           column order): the grid of each row group and column;
  *   row_loss (out, fp64 [rows]): sum over columns of the squared scaled
  *           errors of the residual sweep.
+ *   u_stream (may be NULL): a HIP stream on which U and perm are still being
+ *           produced (gptq_prepare_hinv enqueued there before this call).
+ *           The frontend, which reads only W, diag S and omega, starts at
+ *           once on `stream`; the permutation check and the sweep wait for
+ *           the work enqueued on u_stream up to this call. NULL: U and perm
+ *           are ready in stream order. S must be complete in `stream` order
+ *           either way.
  *   Returns GPTQ_ENOTSPD when the sketch loses rank (the weighted W has
  *   rank below r), GPTQ_ENONFINITE for a NaN/Inf weight or energy or an
  *   fp16 overflow of a scale; with GPTQ_FLAG_NO_SYNC the status is read later
@@ -332,7 +339,7 @@ gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t cols, int64
                             const int32_t* perm, const double* omega, int rank, int bits,
                             int group_size, uint32_t flags, uint16_t* A, uint16_t* B,
                             uint8_t* codes, uint16_t* scales, uint16_t* zeros, double* row_loss,
-                            void* ws, size_t ws_bytes, void* stream);
+                            void* ws, size_t ws_bytes, void* stream, void* u_stream);
 
 /* ---------------------------------------------------------------------------
  * Optional kernel timing (process-wide, not thread-safe). gptq_profile_enable

@@ -694,7 +694,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
                                        int bits, int group_size, uint32_t flags, uint16_t* A,
                                        uint16_t* B, uint8_t* codes, uint16_t* scales,
                                        uint16_t* zeros, double* row_loss, void* ws,
-                                       size_t ws_bytes, void* stream) {
+                                       size_t ws_bytes, void* stream, void* u_stream) {
   if (flags & ~GPTQ_FLAG_NO_SYNC) return GPTQ_EINVAL;
   if (rows <= 0 || cols <= 0 || n_tokens <= 0) return GPTQ_EINVAL;
   if (bits < 2 || bits > 8) return GPTQ_EINVAL;
@@ -724,12 +724,6 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   };
   auto rowsg = [](int64_t m) { return (unsigned)cdiv(m, 4); };
   GPTQ_LAUNCH(K_FILL, st, ch_zero_kernel<<<1, 64, 0, st>>>(status, 1));
-  if (perm) {
-    GPTQ_LAUNCH(K_FILL, st, ch_zero_kernel<<<grid1(i), 256, 0, st>>>(cnt, i));
-    GPTQ_LAUNCH(K_CH_FRONT, st,
-                ch_perm_count_kernel<<<grid1(i), 256, 0, st>>>(perm, i, cnt, status));
-    GPTQ_LAUNCH(K_CH_FRONT, st, ch_perm_check_kernel<<<grid1(i), 256, 0, st>>>(cnt, i, status));
-  }
   GPTQ_LAUNCH(K_CH_FRONT, st,
               ch_energy_kernel<<<1, 1024, 0, st>>>(S, i, 1.0 / (double)n_tokens, c, sc, status));
   // C [k x r] = A^T B over m rows, split in slices when that fills the chip
@@ -787,6 +781,24 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
 #undef CH_TRY
   GPTQ_LAUNCH(K_CH_FRONT, st,
               ch_resid_kernel<<<grid1(o * i), 256, 0, st>>>(W, ldw, o, i, A, B, r, Res, status));
+  // U and perm are read from here on: with u_stream, wait for the work
+  // enqueued on it before this call (the frontend above does not need U and
+  // overlaps with it)
+  if (u_stream && u_stream != stream) {
+    hipEvent_t ev;
+    GPTQ_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    hipError_t e1 = hipEventRecord(ev, (hipStream_t)u_stream);
+    hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, ev, 0) : e1;
+    hipError_t e3 = hipEventDestroy(ev);
+    GPTQ_HIP(e2);
+    GPTQ_HIP(e3);
+  }
+  if (perm) {
+    GPTQ_LAUNCH(K_FILL, st, ch_zero_kernel<<<grid1(i), 256, 0, st>>>(cnt, i));
+    GPTQ_LAUNCH(K_CH_FRONT, st,
+                ch_perm_count_kernel<<<grid1(i), 256, 0, st>>>(perm, i, cnt, status));
+    GPTQ_LAUNCH(K_CH_FRONT, st, ch_perm_check_kernel<<<grid1(i), 256, 0, st>>>(cnt, i, status));
+  }
   const unsigned ngr = (unsigned)cdiv(o, group_size);
   const unsigned rt = (unsigned)cdiv(o, 64);
   for (int64_t j0 = 0; j0 < i; j0 += CH_QB) {

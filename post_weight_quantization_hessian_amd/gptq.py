@@ -66,7 +66,7 @@ EXPORTS = {
                                   C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int, C.c_int,
                                   C.c_int, C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
-                                  C.c_void_p]),
+                                  C.c_void_p, C.c_void_p]),
     "gptq_workspace_status": (C.c_int, [C.c_void_p, C.c_void_p]),
     "gptq_status_string": (C.c_char_p, [C.c_int]),
     "gptq_fp16_round_host": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64]),
@@ -424,12 +424,15 @@ def chmc_workspace_bytes(rows: int, cols: int, rank: int) -> int:
 
 
 def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_size: int = 128,
-               bpw_target: float = 4.2875, sync: bool = True, workspace=None) -> CHMCLayer:
+               bpw_target: float = 4.2875, sync: bool = True, workspace=None,
+               u_stream=None) -> CHMCLayer:
     """The CHMC layer on the device: energies from diag(S), the rank-``rank``
     fp16 factors of W from the sketch ``omega`` (fp64 [cols x >= rank]; its
     first ``rank`` columns are used), the residual swept with one grid per
     group of ``group_size`` output rows and column. ``rank`` defaults to the
-    largest that fits ``bpw_target``."""
+    largest that fits ``bpw_target``. ``u_stream``: a torch stream on which U and
+    perm are still being produced; the frontend then overlaps with that work
+    and only the sweep waits for it."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(S, torch.float64, "S", 2)
@@ -464,7 +467,9 @@ def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_s
                              _ptr(perm), _ptr(om), r, int(bits), int(group_size),
                              0 if sync else GPTQ_FLAG_NO_SYNC, _ptr(A), _ptr(B), _ptr(codes),
                              _ptr(scales), _ptr(zeros), _ptr(row_loss), _ptr(ws), ws.numel(),
-                             _stream())
+                             _stream(),
+                             C.c_void_p(u_stream.cuda_stream) if u_stream is not None
+                             else C.c_void_p(0))
     _check(st, "gptq_chmc_layer")
     return CHMCLayer(A, B, codes, scales, zeros, row_loss, r, int(bits), int(group_size))
 

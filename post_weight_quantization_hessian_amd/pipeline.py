@@ -117,25 +117,45 @@ class LayerGroup:
         """Hessian and factor as in enqueue, then the CHMC layer (CHMC article,
         Methodik, Schritt 1-3) for each layer of the stack ``W`` (``layers``:
         (name, rows) in stacking order) and bit width, the rank from the budget
-        ``bpw``, without synchronizing. Returns [(name, rank)]."""
-        self._factor(chunks)
-        perm = self.perm if (self.act_order or self.min_pivot) else None
-        if not hasattr(self, "cws"):
+        ``bpw``, without synchronizing. The CHMC calls run on a side stream
+        forked once S is complete: their frontends (which need only diag S and
+        W) overlap with the factorization, and their sweeps wait for U.
+        Returns [(name, rank)]."""
+        import torch
+        n = 0
+        for ci, c in enumerate(chunks):
+            G.hessian_accumulate(self.S, c, workspace=self.hws, overwrite=(ci == 0),
+                                 split8=self.split8)
+            n += int(c.shape[0])
+        self.n = n
+        main = torch.cuda.current_stream()
+        if not hasattr(self, "cstream"):
+            self.cstream = torch.cuda.Stream(device=W.device)
             self.cws = {}
+        fork = torch.cuda.Event()
+        fork.record(main)
+        G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
+                       workspace=self.pws, out=(self.perm, self.U), sync=False,
+                       min_pivot=self.min_pivot)
+        perm = self.perm if (self.act_order or self.min_pivot) else None
         out, r0 = [], 0
-        for name, rows in layers:
-            for b in self.bits:
-                r = G.chmc_rank(rows, self.dim, b, self.group_size, bpw)
-                key = (name, b)
-                if key not in self.cws:
-                    self.cws[key] = torch_empty_bytes(G.chmc_workspace_bytes(rows, self.dim, r),
-                                                      W.device)
-                G.chmc_layer(W[r0:r0 + rows], self.S, self.n, self.U, perm, omega, rank=r,
-                             bits=b, group_size=self.group_size, bpw_target=bpw, sync=False,
-                             workspace=self.cws[key])
-            out.append((name, r))
-            r0 += rows
-        self._chmc = True
+        with torch.cuda.stream(self.cstream):
+            self.cstream.wait_event(fork)
+            for name, rows in layers:
+                for b in self.bits:
+                    r = G.chmc_rank(rows, self.dim, b, self.group_size, bpw)
+                    key = (name, b)
+                    if key not in self.cws:
+                        self.cws[key] = torch_empty_bytes(
+                            G.chmc_workspace_bytes(rows, self.dim, r), W.device)
+                    G.chmc_layer(W[r0:r0 + rows], self.S, self.n, self.U, perm, omega, rank=r,
+                                 bits=b, group_size=self.group_size, bpw_target=bpw,
+                                 sync=False, workspace=self.cws[key], u_stream=main)
+                out.append((name, r))
+                r0 += rows
+            join = torch.cuda.Event()
+            join.record(self.cstream)
+        main.wait_event(join)
         return out
 
     def check(self):

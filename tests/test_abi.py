@@ -206,7 +206,7 @@ def test_chmc_host_checks():
     def ch(rows=64, cols=128, ldw=128, n=100, perm=NULL, om=FAKE, rank=2, bits=4, gs=64,
            flags=0, A=FAKE, B=FAKE, ws=FAKE, wsb=1 << 40):
         return f(FAKE, rows, cols, ldw, FAKE, n, FAKE, perm, om, rank, bits, gs, flags, A, B,
-                 FAKE, FAKE, FAKE, FAKE, ws, wsb, NULL)
+                 FAKE, FAKE, FAKE, FAKE, ws, wsb, NULL, NULL)
     assert ch(rank=65) == g.GPTQ_EINVAL
     assert ch(rank=-1) == g.GPTQ_EINVAL
     assert ch(rows=1, rank=2) == g.GPTQ_EINVAL

@@ -274,3 +274,33 @@ def test_chmc_no_sync_reports_through_the_workspace():
     with pytest.raises(G.GPTQError) as e:
         G.workspace_status(ws)
     assert e.value.status == G.GPTQ_EINVAL
+
+
+def test_chmc_frontend_overlaps_the_factorization():
+    """prepare_hinv enqueued on one stream, the CHMC call on another with
+    u_stream = the first: the frontend runs at once, the sweep waits for U;
+    the results equal those of the call made after U is ready, bit for bit."""
+    say("chmc with u_stream: overlap with prepare")
+    W, X = problem(256, 1024, 2100, 12, lowrank=3)
+    dim, n = 1024, 2100
+    S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
+    om = torch.from_numpy(np.random.default_rng(4).standard_normal((dim, 8))).to(DEV)
+    Wd = torch.from_numpy(W).to(DEV)
+    perm0, U0 = G.prepare_hinv(S, n, damp=0.01, act_order=True)
+    ref = G.chmc_layer(Wd, S, n, U0, perm0, om, rank=8, group_size=64)
+    perm = torch.empty(dim, dtype=torch.int32, device=DEV)
+    U = torch.empty((dim, dim), dtype=torch.float32, device=DEV)
+    pws = torch.empty(G.prepare_workspace_bytes(dim), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        G.prepare_hinv(S, n, damp=0.01, act_order=True, workspace=pws, out=(perm, U),
+                       sync=False)
+    with torch.cuda.stream(s2):
+        res = G.chmc_layer(Wd, S, n, U, perm, om, rank=8, group_size=64, u_stream=s1)
+    torch.cuda.synchronize()
+    G.workspace_status(pws)
+    for x, y in ((res.A, ref.A), (res.B, ref.B), (res.codes, ref.codes),
+                 (res.scales, ref.scales), (res.zeros, ref.zeros), (res.row_loss, ref.row_loss)):
+        assert torch.equal(x, y)
