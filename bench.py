@@ -25,7 +25,7 @@ import time
 import numpy as np
 
 METRIC = ("quantized weights/sec per layer + XXᵀ/trailing-GEMM % MFMA peak, 1×MI355X")
-DEFAULT_WORKLOAD = "qwen05b_mlp"
+DEFAULT_WORKLOAD = "llama70b_down"
 CHOL_MERGE_TILES = 504  # the library's threshold for the merged factor + update launch
 CHOL_FUSE_NT = 48  # the library's bound on panels for the inverse accumulated in the factorization
 QEMB_KMAX = 512  # the library's longest early update-GEMM piece inside a sweep launch
@@ -86,6 +86,14 @@ def chmc_flops(plan, bits_n, in_block):
             bw = min(128, h.dim - j0)
             f += 2.0 * h.rows * (bw * (bw - 1) / 2.0 if in_block else j0 * bw)
     return f * bits_n
+
+
+def chmc_bpw(o, i, r, bits, gs):
+    """Stored bits per weight of a CHMC layer: fp16 factors 16 r (o + i), the
+    b-bit residual codes, per output group and column an fp16 scale and a
+    zero point in [0, 2^b - 1] (b bits)."""
+    ng = -(-o // gs)
+    return (16 * r * (o + i) + bits * o * i + (16 + bits) * ng * i) / (o * i)
 
 
 def kernel_work(name, wl, plan, sweeps=1.0):
@@ -433,7 +441,7 @@ def main():
     from post_weight_quantization_hessian_amd import synth
     from post_weight_quantization_hessian_amd.workloads import WORKLOADS
     import post_weight_quantization_hessian_amd.gptq as G
-    from post_weight_quantization_hessian_amd.pipeline import LayerGroup
+    from post_weight_quantization_hessian_amd.pipeline import CHMC_DAMP, LayerGroup
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -646,7 +654,8 @@ def main():
                    "act_order": wl.act_order and args.order == "workload",
                    "clip": not args.no_clip,
                    "order": "min_pivot" if args.order == "min_pivot" else
-                   ("act_order" if wl.act_order else "none"), "damp": wl.damp,
+                   ("act_order" if wl.act_order else "none"),
+                   "damp": CHMC_DAMP if args.chmc is not None else wl.damp,
                    "weights_per_step": weights,
                    "hessian": {h.name: ("split8" if h.split8 else "exact") for h in plan},
                    "arithmetic": "Hessian: exact fp64 products, or (split8) int8 digit-slice "
@@ -665,7 +674,11 @@ def main():
                        for k, v in hptq_last.items()}},
         "chmc": None if args.chmc is None else {
             "bpw_target": args.chmc, "sketch": "seeded Gaussian [in_features x rank]",
-            "rank": {name: r for v in chmc_last.values() for name, r in v}},
+            "damp": CHMC_DAMP,
+            "layers": [{"layer": name, "bits": b, "rank": q.rank,
+                        "bits_per_weight": chmc_bpw(q.codes.shape[0], q.codes.shape[1], q.rank,
+                                                    b, q.group_size)}
+                       for v in chmc_last.values() for name, b, q in v]},
         "cpu_baseline": cpu,
         "step_repeats": step_repeats,
         "kernels": breakdown,

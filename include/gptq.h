@@ -26,8 +26,10 @@
  *   - Fp16 values (weights, scales, zero points) travel as uint16_t bit
  *     patterns (IEEE binary16).
  *   - No exception crosses the ABI. Calls on different streams with disjoint
- *     buffers are independent; the optional profiler (gptq_profile_*) is a
- *     process-wide switch and is not thread-safe.
+ *     buffers are independent and may come from different host threads. The
+ *     optional profiler (gptq_profile_*) is the only state kept across calls:
+ *     a process-wide switch and one shared record, both guarded, so it is
+ *     thread-safe too.
  */
 #ifndef GPTQ_H
 #define GPTQ_H
@@ -295,10 +297,12 @@ int gptq_version(void);
  *             group's current values (fp16 scale, integer zero point), and its
  *             scaled errors propagate along row j of U.
  * gptq_chmc_rank: the largest r whose factors (16 r (rows + cols) bits),
- *   bits-bit codes and one 16-bit scale per row group and column fit
- *   bpw_target bits per weight: floor((bpw rows cols - bits rows cols - 16
- *   ceil(rows/gs) cols) / (16 (rows + cols))), clamped to [0, min(rows, cols)];
- *   0 for invalid arguments.
+ *   bits-bit codes, one 16-bit scale per row group and column and that
+ *   group's zero point (an integer in [0, 2^bits - 1], counted at bits bits)
+ *   fit bpw_target bits per weight: floor((bpw rows cols - bits rows cols -
+ *   (16 + bits) ceil(rows/gs) cols) / (16 (rows + cols))), clamped to
+ *   [0, min(rows, cols, 64)] (64 is the largest rank gptq_chmc_layer takes; a
+ *   smaller rank stays under the budget); 0 for invalid arguments.
  * gptq_chmc_workspace_bytes: workspace for gptq_chmc_layer (0 if rank is not
  *   in [0, 64] or a size is not positive): about 3 rows*cols fp64 matrices.
  * gptq_chmc_layer:
@@ -342,7 +346,7 @@ gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t cols, int64
                             void* ws, size_t ws_bytes, void* stream, void* u_stream);
 
 /* ---------------------------------------------------------------------------
- * Optional kernel timing (process-wide, not thread-safe). gptq_profile_enable
+ * Optional kernel timing (process-wide, thread-safe). gptq_profile_enable
  * takes a bit mask of kernel ids (bit k = kernel id k; 0 turns timing off,
  * 0xFFFFFFFF times every kernel). Each launch of a selected kernel is then
  * bracketed by two HIP events recorded on the stream it is launched on.

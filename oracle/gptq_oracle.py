@@ -71,9 +71,10 @@ Readings of what the pages leave open (each listed in the design doc):
   (any orthonormal basis of each iterate's span: the result depends on the
   spans only), then the SVD of the small projected matrix; stored factors
   A = fp16(U S) and B = fp16(V^T diag(1/sqrt c)); the residual R = W - A B
-  is swept like GPTQ (act-order, damped H) with one grid per group of gs
-  consecutive output channels (rows) and column; r from the page's bit
-  budget formula.
+  is swept like GPTQ (act-order, H damped with 0.05 as in Anhang A) with one
+  grid per group of gs consecutive output channels (rows) and column; r from
+  the page's bit budget formula with the residual grid's zero point counted
+  at b bits per output group and column (the page counts only the scales).
 """
 from __future__ import annotations
 
@@ -89,7 +90,7 @@ __all__ = [
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups", "group_grid_ssqr", "ssqr_search",
     "group_step_hptq", "huffman_lengths", "hptq_bits_per_weight", "hptq_search",
-    "chmc_energies", "chmc_rank", "randomized_lowrank", "chmc_lowrank", "gptq_sweep_outgroups",
+    "CHMC_DAMP", "chmc_energies", "chmc_bits", "chmc_rank", "randomized_lowrank", "chmc_lowrank", "gptq_sweep_outgroups",
     "chmc_layer",
 ]
 
@@ -542,19 +543,37 @@ def hptq_search(Wp, U, bits, group_size, budget, *, iters=12, lo=1.0 / 64, hi=1.
 # CHMC frontend ([CHMC] "Methodik", Schritt 1-3)
 # --------------------------------------------------------------------------
 
-def chmc_energies(S_diag, n_tokens, lam=0.05):
+# Anhang A of the CHMC article: the CHMC v6 quantization runs with dampening
+# 0.05, both for the activation energies (Schritt 1) and for the Hessian of the
+# residual's GPTQ step (Schritt 2).
+CHMC_DAMP = 0.05
+
+
+def chmc_energies(S_diag, n_tokens, lam=CHMC_DAMP):
     """Schritt 1: damped activation energies c_j = (1/n) sum_t x_tj^2 +
     lam * mean(c)."""
     c = np.asarray(S_diag, dtype=F64) / n_tokens
     return c + lam * c.mean()
 
 
-def chmc_rank(o, i, bits, group_size, bpw_target):
-    """Schritt 3: the largest rank whose fp16 factors (16 r (o + i)), b-bit
-    residual codes and one 16-bit scale per output group and column fit the
-    budget: floor((BPW o i - b o i - 16 ceil(o/gs) i) / (16 (o + i)))."""
-    r = (bpw_target * o * i - bits * o * i - 16 * num_groups(o, group_size) * i) // (16 * (o + i))
-    return int(max(0, min(r, min(o, i))))
+def chmc_bits(o, i, r, bits, group_size):
+    """Schritt 3's count of the stored bits of a CHMC layer: fp16 factors
+    16 r (o + i), b-bit residual codes, one 16-bit scale per output group and
+    column, plus that group's zero point of the asymmetric grid (an integer in
+    [0, maxq]: b bits), which the page's formula has no term for."""
+    ng = num_groups(o, group_size)
+    return 16 * r * (o + i) + bits * o * i + (16 + bits) * ng * i
+
+
+def chmc_rank(o, i, bits, group_size, bpw_target, max_rank=None):
+    """Schritt 3: the largest rank whose layer (chmc_bits) fits the budget,
+    floor((BPW o i - b o i - (16 + b) ceil(o/gs) i) / (16 (o + i))), within
+    [0, min(o, i)] and at most ``max_rank`` when given (a smaller rank stays
+    under the budget, which the page only asks not to exceed)."""
+    ng = num_groups(o, group_size)
+    r = (bpw_target * o * i - bits * o * i - (16 + bits) * ng * i) // (16 * (o + i))
+    r = int(max(0, min(r, min(o, i))))
+    return r if max_rank is None else min(r, int(max_rank))
 
 
 def _orth(Y):
@@ -618,7 +637,7 @@ def gptq_sweep_outgroups(Rp, U, bits, row_group):
 
 
 def chmc_layer(W_fp16, S, n_tokens, Omega, *, bits=4, group_size=128, bpw_target=4.2875,
-               damp=0.01, act_order=True, niter=5, rank=None):
+               damp=CHMC_DAMP, act_order=True, niter=5, rank=None, max_rank=None):
     """The CHMC layer: energies, rank from the budget (or ``rank``), the
     low-rank fp16 factors from the first r columns of the sketch Omega
     [i x >= r], the residual swept with output-channel groups. Codes and
@@ -630,7 +649,8 @@ def chmc_layer(W_fp16, S, n_tokens, Omega, *, bits=4, group_size=128, bpw_target
     Wd = W.astype(F64)
     o, i = Wd.shape
     c = chmc_energies(np.diag(S), n_tokens)
-    r = chmc_rank(o, i, bits, group_size, bpw_target) if rank is None else int(rank)
+    r = (chmc_rank(o, i, bits, group_size, bpw_target, max_rank) if rank is None
+         else int(rank))
     if r > 0:
         A, B = chmc_lowrank(Wd, c, np.asarray(Omega, dtype=F64)[:, :r], niter)
     else:

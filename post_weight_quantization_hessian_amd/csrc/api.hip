@@ -1,5 +1,6 @@
 // Status strings, the fp16 rounding utility and the optional HIP-event
 // kernel profiler of the GPTQ library.
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -20,14 +21,20 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 
-static uint32_t g_prof_mask = 0u;
+// The kernel-timing hooks are the library's only state that outlives a call.
+// The mask is atomic; the start events of launches in flight are per thread
+// (a begin and its end always come from the same call, on one thread); the
+// finished records are shared and guarded by a mutex, so calls from several
+// host threads on several streams may be timed together.
+static std::atomic<uint32_t> g_prof_mask{0u};
 static thread_local hipError_t g_last_error = hipSuccess;
 
 void note_hip_error(hipError_t e) { g_last_error = e; }
-static std::vector<ProfRec> g_prof;
-static std::vector<hipEvent_t> g_open;  // per-launch start events pending an end
+static std::mutex g_prof_mutex;
+static std::vector<ProfRec> g_prof;  // guarded by g_prof_mutex
+static thread_local std::vector<hipEvent_t> g_open;  // start events pending an end
 
-static bool selected(int kid) { return (g_prof_mask >> kid) & 1u; }
+static bool selected(int kid) { return (g_prof_mask.load(std::memory_order_relaxed) >> kid) & 1u; }
 
 // A null start event marks a launch whose start could not be recorded; the
 // matching prof_end then records nothing.
@@ -54,6 +61,7 @@ void prof_end(int kid, hipStream_t s) {
     return;
   }
   (void)hipEventRecord(b, s);
+  std::lock_guard<std::mutex> lock(g_prof_mutex);
   g_prof.push_back({kid, a, b});
 }
 
@@ -96,7 +104,7 @@ extern "C" const char* gptq_last_error_string(void) {
 }
 
 extern "C" gptq_status gptq_profile_enable(uint32_t kernel_mask) {
-  g_prof_mask = kernel_mask;
+  g_prof_mask.store(kernel_mask, std::memory_order_relaxed);
   return GPTQ_OK;
 }
 
@@ -113,8 +121,13 @@ extern "C" gptq_status gptq_profile_read(double* totals_ms, int64_t* launches) {
     totals_ms[k] = 0.0;
     launches[k] = 0;
   }
+  std::vector<ProfRec> recs;
+  {
+    std::lock_guard<std::mutex> lock(g_prof_mutex);
+    recs.swap(g_prof);
+  }
   gptq_status st = GPTQ_OK;
-  for (auto& r : g_prof) {
+  for (auto& r : recs) {
     if (hipEventSynchronize(r.b) != hipSuccess) st = GPTQ_EHIP;
     float ms = 0.0f;
     if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
@@ -126,6 +139,5 @@ extern "C" gptq_status gptq_profile_read(double* totals_ms, int64_t* launches) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
   }
-  g_prof.clear();
   return st;
 }

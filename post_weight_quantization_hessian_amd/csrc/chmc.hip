@@ -676,11 +676,14 @@ using namespace gptq;
 extern "C" int gptq_chmc_rank(int64_t rows, int64_t cols, int bits, int group_size,
                               double bpw_target) {
   if (rows <= 0 || cols <= 0 || bits < 2 || bits > 8 || group_size <= 0) return 0;
+  // Schritt 3's budget with the residual grid's zero point (bits bits per
+  // output group and column) counted beside its fp16 scale
   const double o = (double)rows, i = (double)cols;
   const double r = std::floor((bpw_target * o * i - bits * o * i -
-                               16.0 * (double)cdiv(rows, group_size) * i) / (16.0 * (o + i)));
+                               (16.0 + bits) * (double)cdiv(rows, group_size) * i) /
+                              (16.0 * (o + i)));
   if (!(r > 0.0)) return 0;
-  return (int)std::min<double>(r, (double)std::min(rows, cols));
+  return (int)std::min<double>(r, (double)std::min<int64_t>(std::min(rows, cols), CH_RMAX));
 }
 
 extern "C" size_t gptq_chmc_workspace_bytes(int64_t rows, int64_t cols, int rank) {

@@ -402,16 +402,19 @@ class CHMCLayer:
     bits: int
     group_size: int
 
-    def dequantize(self):
-        """A B + the dequantized residual, fp64 [rows x cols]."""
-        torch = _torch()
-        g = torch.arange(self.codes.shape[0], device=self.codes.device) // self.group_size
-        s = self.scales.double()[g]
-        z = self.zeros.double()[g]
-        res = s * (self.codes.double() - z)
-        if self.rank > 0:
-            res = res + self.A.double() @ self.B.double()
-        return res
+
+def chmc_outputs(rows: int, cols: int, rank: int, bits: int, group_size: int,
+                 device) -> CHMCLayer:
+    """Uninitialized output buffers of one CHMC layer call (for ``out=``)."""
+    torch = _torch()
+    ng = -(-rows // group_size)
+    return CHMCLayer(torch.empty((rows, rank), dtype=torch.float16, device=device),
+                     torch.empty((rank, cols), dtype=torch.float16, device=device),
+                     torch.empty((rows, cols), dtype=torch.uint8, device=device),
+                     torch.empty((ng, cols), dtype=torch.float16, device=device),
+                     torch.empty((ng, cols), dtype=torch.float16, device=device),
+                     torch.empty(rows, dtype=torch.float64, device=device),
+                     int(rank), int(bits), int(group_size))
 
 
 def chmc_rank(rows: int, cols: int, bits: int = 4, group_size: int = 128,
@@ -425,14 +428,15 @@ def chmc_workspace_bytes(rows: int, cols: int, rank: int) -> int:
 
 def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_size: int = 128,
                bpw_target: float = 4.2875, sync: bool = True, workspace=None,
-               u_stream=None) -> CHMCLayer:
+               u_stream=None, out: CHMCLayer | None = None) -> CHMCLayer:
     """The CHMC layer on the device: energies from diag(S), the rank-``rank``
     fp16 factors of W from the sketch ``omega`` (fp64 [cols x >= rank]; its
     first ``rank`` columns are used), the residual swept with one grid per
     group of ``group_size`` output rows and column. ``rank`` defaults to the
     largest that fits ``bpw_target``. ``u_stream``: a torch stream on which U and
     perm are still being produced; the frontend then overlaps with that work
-    and only the sweep waits for it."""
+    and only the sweep waits for it. ``out``: buffers from chmc_outputs of the
+    same shape, rank, bits and group size to write into."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(S, torch.float64, "S", 2)
@@ -454,13 +458,13 @@ def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_s
     if tuple(U.shape) != (cols, cols) or not U.is_contiguous():
         raise ValueError("U must be a contiguous [cols x cols] tensor")
     dev = W.device
-    ng = -(-rows // group_size)
-    A = torch.empty((rows, r), dtype=torch.float16, device=dev)
-    B = torch.empty((r, cols), dtype=torch.float16, device=dev)
-    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-    scales = torch.empty((ng, cols), dtype=torch.float16, device=dev)
-    zeros = torch.empty((ng, cols), dtype=torch.float16, device=dev)
-    row_loss = torch.empty(rows, dtype=torch.float64, device=dev)
+    if out is None:
+        out = chmc_outputs(rows, cols, r, bits, group_size, dev)
+    elif (out.rank, out.bits, out.group_size) != (r, int(bits), int(group_size)) or \
+            tuple(out.codes.shape) != (rows, cols) or tuple(out.A.shape) != (rows, r):
+        raise ValueError("out does not match this call's shape, rank, bits or group size")
+    A, B, codes, scales, zeros, row_loss = (out.A, out.B, out.codes, out.scales, out.zeros,
+                                            out.row_loss)
     nb = chmc_workspace_bytes(rows, cols, r)
     ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
     st = lib.gptq_chmc_layer(_ptr(W), rows, cols, W.stride(0), _ptr(S), int(n_tokens), _ptr(U),
@@ -471,7 +475,7 @@ def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_s
                              C.c_void_p(u_stream.cuda_stream) if u_stream is not None
                              else C.c_void_p(0))
     _check(st, "gptq_chmc_layer")
-    return CHMCLayer(A, B, codes, scales, zeros, row_loss, r, int(bits), int(group_size))
+    return out
 
 
 def workspace_status(workspace):

@@ -17,6 +17,11 @@ from __future__ import annotations
 
 from . import gptq as G
 
+# The CHMC article's quantization damps the Hessian of the residual's GPTQ
+# step with 0.05 (Anhang A, "dampening 0.05"; the same lambda as the
+# activation energies of Schritt 1).
+CHMC_DAMP = 0.05
+
 # "auto" takes the int8 digit-slice Hessian from this many input features on
 # (measured faster from 256 features at 2048 tokens; below, a handful of
 # tiles, either is a few microseconds)
@@ -113,14 +118,16 @@ class LayerGroup:
         return [G.hptq_search(W, self.U, perm, bits=b, group_size=self.group_size,
                               budget=budget, iters=iters) for b in self.bits]
 
-    def chmc(self, chunks, W, layers, bpw, omega):
-        """Hessian and factor as in enqueue, then the CHMC layer (CHMC article,
+    def chmc(self, chunks, W, layers, bpw, omega, damp=CHMC_DAMP):
+        """Hessian, then the factor of H damped with ``damp`` (the CHMC
+        article's 0.05 by default), then the CHMC layer (CHMC article,
         Methodik, Schritt 1-3) for each layer of the stack ``W`` (``layers``:
         (name, rows) in stacking order) and bit width, the rank from the budget
         ``bpw``, without synchronizing. The CHMC calls run on a side stream
         forked once S is complete: their frontends (which need only diag S and
-        W) overlap with the factorization, and their sweeps wait for U.
-        Returns [(name, rank)]."""
+        W) overlap with the factorization, and their sweeps wait for U. The
+        outputs live in buffers of this group (one set per layer and bit
+        width, reused by later calls). Returns [(name, bits, CHMCLayer)]."""
         import torch
         n = 0
         for ci, c in enumerate(chunks):
@@ -132,9 +139,10 @@ class LayerGroup:
         if not hasattr(self, "cstream"):
             self.cstream = torch.cuda.Stream(device=W.device)
             self.cws = {}
+            self.couts = {}
         fork = torch.cuda.Event()
         fork.record(main)
-        G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
+        G.prepare_hinv(self.S, n, damp=damp, act_order=self.act_order,
                        workspace=self.pws, out=(self.perm, self.U), sync=False,
                        min_pivot=self.min_pivot)
         perm = self.perm if (self.act_order or self.min_pivot) else None
@@ -144,14 +152,17 @@ class LayerGroup:
             for name, rows in layers:
                 for b in self.bits:
                     r = G.chmc_rank(rows, self.dim, b, self.group_size, bpw)
-                    key = (name, b)
+                    key = (name, b, r)
                     if key not in self.cws:
                         self.cws[key] = torch_empty_bytes(
                             G.chmc_workspace_bytes(rows, self.dim, r), W.device)
+                        self.couts[key] = G.chmc_outputs(rows, self.dim, r, b, self.group_size,
+                                                         W.device)
                     G.chmc_layer(W[r0:r0 + rows], self.S, self.n, self.U, perm, omega, rank=r,
                                  bits=b, group_size=self.group_size, bpw_target=bpw,
-                                 sync=False, workspace=self.cws[key], u_stream=main)
-                out.append((name, r))
+                                 sync=False, workspace=self.cws[key], u_stream=main,
+                                 out=self.couts[key])
+                    out.append((name, b, self.couts[key]))
                 r0 += rows
             join = torch.cuda.Event()
             join.record(self.cstream)

@@ -195,8 +195,24 @@ def test_chmc_host_checks():
     L = g.lib
     for shape in [(576, 576), (896, 4864), (4864, 896), (37, 129), (1, 1), (8192, 28672)]:
         for bits, gs, bpw in [(4, 128, 4.2875), (3, 64, 3.5), (2, 32, 8.0), (4, 128, 4.0)]:
-            assert g.chmc_rank(*shape, bits, gs, bpw) == O.chmc_rank(*shape, bits, gs, bpw)
+            assert g.chmc_rank(*shape, bits, gs, bpw) == O.chmc_rank(*shape, bits, gs, bpw,
+                                                                       max_rank=64)
     assert g.chmc_rank(576, 576, 4, 128, 4.2875) == 2
+    # every layer shape and bit width of the workloads at the page's budget:
+    # the rank fits the layer call's limit (64) and its workspace query
+    from post_weight_quantization_hessian_amd.workloads import WORKLOADS
+    for wl in WORKLOADS.values():
+        for lay in wl.layers:
+            cols = wl.input(lay.hessian).dim
+            for bits in wl.bits:
+                r = g.chmc_rank(lay.rows, cols, bits, wl.group_size, 4.2875)
+                assert 0 <= r <= 64
+                assert r == min(64, O.chmc_rank(lay.rows, cols, bits, wl.group_size, 4.2875))
+                if r > 0:  # (at 4 bits and 64-row groups even rank 0 is over)
+                    assert O.chmc_bits(lay.rows, cols, r, bits, wl.group_size) <= \
+                        4.2875 * lay.rows * cols
+                if lay.rows * cols <= 1 << 24:
+                    assert g.chmc_workspace_bytes(lay.rows, cols, r) > 0
     assert g.chmc_workspace_bytes(576, 576, 2) >= 3 * 8 * 576 * 576
     assert g.chmc_workspace_bytes(576, 576, 65) == 0
     assert g.chmc_workspace_bytes(37, 129, 0) >= 3 * 8 * 37 * 129  # no low-rank part

@@ -48,9 +48,13 @@ def test_hessian_work_is_the_symmetric_half():
 
 def test_default_workload_and_peaks():
     wl = W.WORKLOADS[bench.DEFAULT_WORKLOAD] if hasattr(W, "WORKLOADS") else None
-    assert bench.DEFAULT_WORKLOAD == "qwen05b_mlp"
+    # the largest single-GPU workload: the 70B-shape down projection
+    assert bench.DEFAULT_WORKLOAD == "llama70b_down"
     assert bench.PEAK["hbm_gbs"] == 8000.0
     assert bench.PEAK["f64_mfma"] == 78.6 and bench.PEAK["f32_mfma"] == 157.3
     assert bench.PEAK["i8_mfma"] == 5000.0 and bench.PEAK["bf16_mfma"] == 2500.0
     if wl is not None:
-        assert wl.weights_per_step() == (4864 * 896 * 2 + 896 * 4864) * len(wl.bits)
+        assert wl.weights_per_step() == 8192 * 28672 * 2  # 2-bit and 4-bit
+        sizes = {n: sum(l.rows * w.input(l.hessian).dim for l in w.layers)
+                 for n, w in W.WORKLOADS.items()}
+        assert max(sizes, key=sizes.get) == bench.DEFAULT_WORKLOAD

@@ -49,7 +49,7 @@ def gpu_inputs(X, act_order):
     dim = X.shape[1]
     S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
     G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
-    perm, U = G.prepare_hinv(S, X.shape[0], damp=0.01, act_order=act_order)
+    perm, U = G.prepare_hinv(S, X.shape[0], damp=O.CHMC_DAMP, act_order=act_order)
     return S, (perm if act_order else None), U
 
 
@@ -124,7 +124,7 @@ def test_chmc_ragged_matches_oracle(rows, cols, n, bits, gs, act, rank):
 
 def test_chmc_qwen_down_projection_full_shape():
     """896 x 4864 (the Qwen2.5-0.5B down projection), SiLU-gated activations,
-    rank from the 4.2875-bit budget (7). The oracle's factors in full; its
+    rank from the 4.2875-bit budget (6). The oracle's factors in full; its
     residual sweep for one sampled row group (row groups are independent:
     each has its own grids and rows), compared with that group of the GPU
     result."""
@@ -137,11 +137,11 @@ def test_chmc_qwen_down_projection_full_shape():
     res = G.chmc_layer(torch.from_numpy(W).to(DEV), S, n, U, perm, torch.from_numpy(om).to(DEV))
     Sr, nr = O.hessian_sum(X)
     r = O.chmc_rank(rows, dim, 4, gs, 4.2875)
-    assert r == 7 and res.rank == r
+    assert r == 6 and res.rank == r
     c = O.chmc_energies(np.diag(Sr), nr)
     A, B = O.chmc_lowrank(W.astype(np.float64), c, om[:, :r], 5)
     ref = {"rank": r, "A": A, "B": B}
-    H = O.damped_hessian(Sr, nr, 0.01)
+    H = O.damped_hessian(Sr, nr, O.CHMC_DAMP)
     pr = O.act_order_perm(H)
     assert np.array_equal(perm.cpu().numpy(), pr)
     Ur = O.hinv_upper(O.permute_sym(H, pr))
@@ -162,7 +162,8 @@ def test_chmc_qwen_down_projection_full_shape():
 def test_chmc_rank_matches_oracle():
     for shape in [(576, 576), (896, 4864), (4864, 896), (37, 129), (1, 1)]:
         for bits, gs, bpw in [(4, 128, 4.2875), (3, 64, 3.5), (2, 32, 8.0), (4, 128, 4.0)]:
-            assert G.chmc_rank(*shape, bits, gs, bpw) == O.chmc_rank(*shape, bits, gs, bpw)
+            assert G.chmc_rank(*shape, bits, gs, bpw) == O.chmc_rank(*shape, bits, gs, bpw,
+                                                                       max_rank=64)
 
 
 def test_chmc_low_rank_weight_is_rejected():
@@ -213,12 +214,12 @@ def test_chmc_square_2048_g64_sampled():
     res = G.chmc_layer(torch.from_numpy(W).to(DEV), S, n, U, perm, torch.from_numpy(om).to(DEV),
                        bits=bits, group_size=gs, bpw_target=bpw)
     Sr, nr = O.hessian_sum(X)
-    r = O.chmc_rank(rows, cols, bits, gs, bpw)
+    r = O.chmc_rank(rows, cols, bits, gs, bpw, max_rank=64)
     assert r > 0 and res.rank == r
     c = O.chmc_energies(np.diag(Sr), nr)
     A, B = O.chmc_lowrank(W.astype(np.float64), c, om[:, :r], 5)
     ref = {"rank": r, "A": A, "B": B}
-    H = O.damped_hessian(Sr, nr, 0.01)
+    H = O.damped_hessian(Sr, nr, O.CHMC_DAMP)
     pr = O.act_order_perm(H)
     assert np.array_equal(perm.cpu().numpy(), pr)
     Ur = O.hinv_upper(O.permute_sym(H, pr))
@@ -287,7 +288,7 @@ def test_chmc_frontend_overlaps_the_factorization():
     G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
     om = torch.from_numpy(np.random.default_rng(4).standard_normal((dim, 8))).to(DEV)
     Wd = torch.from_numpy(W).to(DEV)
-    perm0, U0 = G.prepare_hinv(S, n, damp=0.01, act_order=True)
+    perm0, U0 = G.prepare_hinv(S, n, damp=O.CHMC_DAMP, act_order=True)
     ref = G.chmc_layer(Wd, S, n, U0, perm0, om, rank=8, group_size=64)
     perm = torch.empty(dim, dtype=torch.int32, device=DEV)
     U = torch.empty((dim, dim), dtype=torch.float32, device=DEV)
@@ -295,7 +296,7 @@ def test_chmc_frontend_overlaps_the_factorization():
     torch.cuda.synchronize()
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     with torch.cuda.stream(s1):
-        G.prepare_hinv(S, n, damp=0.01, act_order=True, workspace=pws, out=(perm, U),
+        G.prepare_hinv(S, n, damp=O.CHMC_DAMP, act_order=True, workspace=pws, out=(perm, U),
                        sync=False)
     with torch.cuda.stream(s2):
         res = G.chmc_layer(Wd, S, n, U, perm, om, rank=8, group_size=64, u_stream=s1)
@@ -304,3 +305,49 @@ def test_chmc_frontend_overlaps_the_factorization():
     for x, y in ((res.A, ref.A), (res.B, ref.B), (res.codes, ref.codes),
                  (res.scales, ref.scales), (res.zeros, ref.zeros), (res.row_loss, ref.row_loss)):
         assert torch.equal(x, y)
+
+
+def test_chmc_pipeline_two_streams_equals_serial_calls():
+    """LayerGroup.chmc (the benchmark's configuration: Hessian, factor on the
+    calling stream, the CHMC calls forked onto a side stream that overlaps the
+    factorization, outputs in the group's buffers) against a serial run of the
+    same library calls, bit for bit, twice in a row (the buffers are reused),
+    with every status read through check()."""
+    from post_weight_quantization_hessian_amd.pipeline import CHMC_DAMP, LayerGroup
+    say("chmc pipeline fork/join against serial calls")
+    dim, n, gs, bpw = 640, 1500, 64, 4.2875
+    layers = [("a", 192), ("b", 70)]
+    rng = np.random.default_rng(31)
+    X = (rng.standard_normal((n, dim)) * np.exp(0.5 * rng.standard_normal(dim))[None, :]
+         + 0.8 * rng.standard_normal((n, 1))).astype(np.float32)
+    W = np.concatenate([(0.02 * rng.standard_t(4, size=(r, dim))
+                         + 0.05 * rng.standard_normal((r, 2)) @ rng.standard_normal((2, dim)))
+                        .astype(np.float16) for _, r in layers], axis=0)
+    Wd = torch.from_numpy(W).to(DEV)
+    chunks = [torch.from_numpy(X[:700]).to(DEV), torch.from_numpy(X[700:]).to(DEV)]
+    om = torch.from_numpy(rng.standard_normal((dim, 64))).to(DEV)
+    grp = LayerGroup(dim, W.shape[0], max_chunk_tokens=800, bits=(4, 3), group_size=gs,
+                     act_order=True, damp=0.01, device=DEV)
+    # serial reference: the same calls, one after the other on one stream
+    S = torch.empty((dim, dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, chunks[0], overwrite=True)
+    G.hessian_accumulate(S, chunks[1])
+    perm, U = G.prepare_hinv(S, n, damp=CHMC_DAMP, act_order=True)
+    ref, r0 = {}, 0
+    for name, rows in layers:
+        for b in (4, 3):
+            ref[(name, b)] = G.chmc_layer(Wd[r0:r0 + rows], S, n, U, perm, om, bits=b,
+                                          group_size=gs, bpw_target=bpw)
+        r0 += rows
+    for rep in range(2):
+        out = grp.chmc(chunks, Wd, layers, bpw, om)
+        grp.check()
+        torch.cuda.synchronize()
+        assert torch.equal(grp.S, S) and torch.equal(grp.U, U) and torch.equal(grp.perm, perm)
+        assert [(nm, b) for nm, b, _ in out] == list(ref)
+        for name, b, q in out:
+            e = ref[(name, b)]
+            assert q.rank == e.rank > 0
+            for x, y in ((q.A, e.A), (q.B, e.B), (q.codes, e.codes), (q.scales, e.scales),
+                         (q.zeros, e.zeros), (q.row_loss, e.row_loss)):
+                assert torch.equal(x, y), (rep, name, b)

@@ -598,13 +598,34 @@ def test_hptq_search_bisection():
 # ---------------------------------------------------------------- CHMC frontend
 
 def test_chmc_rank_worked_example():
-    """[CHMC] Schritt 3 states r = 2 for 576 x 576 at 4.2875 bits."""
+    """[CHMC] Teil 4 reports rank 2 for a 576 x 576 layer at the 4.2875-bit
+    budget of Schritt 3 / Anhang A."""
     g = GOLD["chmc_rank_576"]
     assert O.chmc_rank(g["o"], g["i"], g["bits"], g["gs"], g["bpw_target"]) == g["rank"]
-    # the budget of the rank it returns fits, one more rank does not
+    # the budget of the rank it returns fits, one more rank does not: factors,
+    # codes, one fp16 scale and one b-bit zero point per output group and column
     o, i = g["o"], g["i"]
-    used = lambda r: (16 * r * (o + i) + 4 * o * i + 16 * O.num_groups(o, 128) * i) / (o * i)
+    ng = -(-o // 128)
+    used = lambda r: (16 * r * (o + i) + 4 * o * i + (16 + 4) * ng * i) / (o * i)
     assert used(2) <= 4.2875 < used(3)
+    assert O.chmc_bits(o, i, 2, 4, 128) == used(2) * o * i
+    # the page's own formula, without the zero points, also gives 2 here
+    assert int((4.2875 * o * i - 4 * o * i - 16 * ng * i) // (16 * (o + i))) == 2
+
+
+def test_chmc_rank_budget_and_cap():
+    """Every returned rank fits the budget and one more does not (unless
+    capped); the cap only lowers it."""
+    for o, i, b, gs, bpw in [(4864, 896, 4, 128, 4.2875), (2048, 5632, 3, 128, 4.2875),
+                             (8192, 28672, 2, 64, 4.2875), (37, 129, 2, 32, 8.0),
+                             (100, 100, 4, 128, 4.0)]:
+        r = O.chmc_rank(o, i, b, gs, bpw)
+        assert 0 <= r <= min(o, i)
+        if r > 0:
+            assert O.chmc_bits(o, i, r, b, gs) <= bpw * o * i
+        if r < min(o, i):
+            assert O.chmc_bits(o, i, r + 1, b, gs) > bpw * o * i
+        assert O.chmc_rank(o, i, b, gs, bpw, max_rank=64) == min(r, 64)
 
 
 def test_chmc_energies_from_activations():
@@ -634,6 +655,46 @@ def test_randomized_lowrank_exact_on_low_rank_and_matches_svd():
     np.testing.assert_allclose(S, s[:3], rtol=1e-10)
 
 
+def test_chmc_lowrank_minimizes_the_sqrt_c_weighted_norm():
+    """Schritt 1: W_lr minimizes ||(W - W_lr) diag(sqrt c)||_F over rank r.
+    By Eckart-Young that minimizer is the truncated SVD of W diag(sqrt c),
+    scaled back by diag(1/sqrt c). Built here from the library SVD with a
+    spectral gap (so the randomized iteration reaches it) and strongly uneven
+    energies (so that weighting by c, weighting rows, or leaving B unscaled
+    gives a visibly different product)."""
+    rng = np.random.default_rng(8)
+    o, i, r = 48, 40, 3
+    c = np.exp(3.0 * rng.standard_normal(i))  # energies over ~4 decades
+    sc = np.sqrt(c)
+    Qa, _ = np.linalg.qr(rng.standard_normal((o, o)))
+    Qb, _ = np.linalg.qr(rng.standard_normal((i, i)))
+    # W diag(sqrt c) with a gap 4 -> 0.5 at r = 3: five power iterations
+    # bring the sketch's span within (0.5/4)^11 ~ 1e-10 of the top three
+    sv = np.concatenate([[9.0, 6.0, 4.0], rng.uniform(0.3, 0.5, i - 3)])
+    Wt = (Qa[:, :i] * sv) @ Qb.T
+    W = Wt / sc[None, :]
+    A, B = O.chmc_lowrank(W, c, rng.standard_normal((i, r)), 5)
+    u, s, vt = np.linalg.svd(W * sc[None, :], full_matrices=False)
+    ref = (u[:, :r] * s[:r]) @ vt[:r] / sc[None, :]
+    AB = A @ B
+    # fp16 factors: each entry of A B within a few fp16 ulps of the products
+    tol = 4 * 2.0 ** -11 * (np.abs(A) @ np.abs(B))
+    assert np.all(np.abs(AB - ref) <= tol)
+    werr = lambda M: np.linalg.norm((W - M) * sc[None, :])
+    # the weighted error is the optimum's (up to fp16 factors) ...
+    assert werr(AB) <= werr(ref) + 4 * 2.0 ** -11 * np.linalg.norm(ref * sc[None, :])
+    # ... and clearly below that of the unweighted truncation, or of the
+    # other weightings a slip could produce (those differ by 12 % and more;
+    # the fp16 factors move the error by about 1e-6 of it)
+    uu, su, vtu = np.linalg.svd(W, full_matrices=False)
+    plain = (uu[:, :r] * su[:r]) @ vtu[:r]
+    u2, s2, vt2 = np.linalg.svd(W * c[None, :], full_matrices=False)
+    by_c = (u2[:, :r] * s2[:r]) @ vt2[:r] / c[None, :]
+    unscaled_b = (u[:, :r] * s[:r]) @ vt[:r]
+    for wrong in (plain, by_c, unscaled_b):
+        assert werr(AB) < 0.95 * werr(wrong)
+
+
 def test_outgroup_sweep_diagonal_hessian_is_columnwise_rtn():
     """Diagonal H: nothing propagates; each column is rounded on one grid per
     group of rows, from that group's values of the column."""
@@ -661,7 +722,8 @@ def test_chmc_layer_loss_identity_and_reconstruction():
     assert res["A"].shape == (70, 3) and res["B"].shape == (3, 96)
     assert np.array_equal(res["A"], res["A"].astype(np.float16).astype(np.float64))
     np.testing.assert_allclose(res["A"] @ res["B"] + res["R"], W.astype(np.float64), atol=1e-15)
-    H = O.damped_hessian(S, n, 0.01)
+    assert O.CHMC_DAMP == 0.05  # Anhang A: dampening 0.05
+    H = O.damped_hessian(S, n, 0.05)
     perm = res["perm"]
     D = (res["R"] - res["deq"])[:, perm]
     np.testing.assert_allclose(res["row_loss"], O.loss_quadratic(D, O.permute_sym(H, perm)),
