@@ -219,6 +219,32 @@ gptq_status gptq_ssqr_search(const uint16_t* W, int64_t rows, int64_t cols, int6
                              uint64_t* n_outliers, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gptq_ssqr_outliers_csr — the storage of SSQR's outliers (The Geometry of LLM
+ * Quantization, section 3: the weights that would overflow the grid are kept
+ * sparse, in floating point). Compacts the dense outlier_mask / outlier_vals
+ * of a gptq_quantize_layer_ssqr or gptq_ssqr_search call into compressed
+ * sparse rows:
+ *   mask     (in, u8 [rows x cols], device, contiguous): nonzero = outlier;
+ *   vals     (in, fp16 bits [rows x cols], device, contiguous);
+ *   row_ptr  (out, int64 [rows + 1], device): row r's entries are
+ *            [row_ptr[r], row_ptr[r + 1]); row_ptr[rows] = their count;
+ *   col_idx  (out, int32 [capacity], device): columns, increasing in a row;
+ *   csr_vals (out, fp16 bits [capacity], device): vals at those columns;
+ *   capacity entries the caller provides (the n_outliers of the SSQR call
+ *            suffices); when the count exceeds it, row_ptr is still written,
+ *            col_idx / csr_vals are left untouched and the call returns
+ *            GPTQ_EINVAL (without GPTQ_FLAG_NO_SYNC; with it, compare
+ *            row_ptr[rows] with capacity afterwards);
+ *   flags    0 or GPTQ_FLAG_NO_SYNC; nnz (host, may be NULL, must be NULL
+ *            with GPTQ_FLAG_NO_SYNC): the count, read after a synchronize.
+ *   Needs no workspace. rows, cols >= 0, cols < 2^31.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_ssqr_outliers_csr(const uint8_t* mask, const uint16_t* vals, int64_t rows,
+                                   int64_t cols, int64_t* row_ptr, int32_t* col_idx,
+                                   uint16_t* csr_vals, int64_t capacity, uint32_t flags,
+                                   int64_t* nnz, void* stream);
+
+/* ---------------------------------------------------------------------------
  * HPTQ — The Geometry of LLM Quantization, section 3 (Huffman-coded PTQ:
  * inliers and outliers in one unbounded integer grid, the integers Huffman
  * coded to meet a compression budget). The page prints no rule; the one

@@ -89,6 +89,7 @@ __all__ = [
     "gptq_sweep", "gptq_layer", "rtn_quantize", "dequantize_sweep",
     "babai_nearest_plane", "brute_force_cvp", "ldl_diag", "noclip_bound",
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups", "group_grid_ssqr", "ssqr_search",
+    "ssqr_csr", "bpw_ssqr",
     "group_step_hptq", "huffman_lengths", "hptq_bits_per_weight", "hptq_search",
     "CHMC_DAMP", "chmc_energies", "chmc_bits", "chmc_rank", "randomized_lowrank", "chmc_lowrank", "gptq_sweep_outgroups",
     "chmc_layer",
@@ -507,6 +508,33 @@ def ssqr_search(Wp, U, bits, group_size, target, *, iters=12, lo=1.0 / 64, hi=1.
         else:
             lo = mid
     return hi, best, probes
+
+
+def ssqr_csr(outlier, outlier_vals):
+    """[BABAI] 3 (SSQR keeps its outliers sparse, in floating point): the
+    outliers of a sweep as compressed sparse rows, row by row in increasing
+    column order. Returns row offsets [rows + 1] (row r's entries are
+    row_ptr[r]:row_ptr[r+1]), their columns and their values."""
+    m = np.asarray(outlier) != 0
+    v = np.asarray(outlier_vals)
+    row_ptr = [0]
+    cols, vals = [], []
+    for r in range(m.shape[0]):
+        for c in range(m.shape[1]):
+            if m[r, c]:
+                cols.append(c)
+                vals.append(v[r, c])
+        row_ptr.append(len(cols))
+    return (np.array(row_ptr, dtype=np.int64), np.array(cols, dtype=np.int64),
+            np.array(vals, dtype=v.dtype))
+
+
+def bpw_ssqr(o, i, bits, group_size, n_outliers):
+    """Bits per weight of an SSQR layer stored as b-bit codes, an fp16 scale
+    and zero point per (row, group), and its outliers in compressed sparse
+    rows (32-bit column and fp16 value per outlier, 64-bit row offsets)."""
+    return (bits * o * i + 32 * o * num_groups(i, group_size) + 48 * n_outliers
+            + 64 * (o + 1)) / (o * i)
 
 
 def hptq_search(Wp, U, bits, group_size, budget, *, iters=12, lo=1.0 / 64, hi=1.0,

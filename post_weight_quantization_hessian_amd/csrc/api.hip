@@ -14,7 +14,7 @@ static const char* const kKernelNames[K_COUNT] = {
     "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill",
     "trtri_diag", "chol_potrf_syrk", "trtri_sum", "chol_col", "minpivot_step",
     "minpivot_update", "hessian_digits", "hessian_split8", "quant_hist", "chmc_front",
-    "chmc_update", "chmc_sweep"};
+    "chmc_update", "chmc_sweep", "ssqr_csr"};
 
 struct ProfRec {
   int kid;

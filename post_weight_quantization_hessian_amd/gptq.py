@@ -50,6 +50,9 @@ EXPORTS = {
                                    C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "gptq_ssqr_outliers_csr": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
+                                         C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
+                                         C.c_uint32, C.c_void_p, C.c_void_p]),
     "gptq_quantize_layer_hptq": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
                                            C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_uint32,
                                            C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
@@ -272,6 +275,54 @@ class SSQRLayer:
     outlier_vals: object  # fp16  [rows x cols], the outlier's value (0 elsewhere)
     n_outliers: int
     alpha: float
+    # the stored form of the outliers: compressed sparse rows
+    row_ptr: object = None   # int64 [rows + 1]
+    col_idx: object = None   # int32 [n_outliers], increasing within a row
+    csr_vals: object = None  # fp16  [n_outliers]
+
+    @property
+    def bits_per_weight(self) -> float:
+        """Stored bits per weight: the b-bit codes, an fp16 scale and zero
+        point per (row, group), and the outliers in CSR form (32-bit column
+        index and fp16 value each, 64-bit row offsets)."""
+        rows, cols = self.layer.codes.shape
+        ng = -(-cols // self.layer.group_size)
+        bits = (self.layer.bits * rows * cols + 32 * rows * ng + 48 * self.n_outliers
+                + 64 * (rows + 1))
+        return bits / (rows * cols)
+
+
+def ssqr_outliers_csr(mask, vals, capacity=None, sync: bool = True):
+    """Compressed sparse rows of a dense outlier mask and values (the device
+    compaction of gptq_ssqr_outliers_csr). ``capacity`` defaults to the
+    number of set mask entries counted on the device (one synchronize).
+    Returns (row_ptr int64 [rows + 1], col_idx int32 [nnz], vals fp16 [nnz])."""
+    torch = _torch()
+    _need(mask, torch.uint8, "mask", 2)
+    _need(vals, torch.float16, "vals", 2)
+    if mask.shape != vals.shape or not (mask.is_contiguous() and vals.is_contiguous()):
+        raise ValueError("mask and vals must be contiguous and of one shape")
+    rows, cols = mask.shape
+    dev = mask.device
+    if capacity is None:
+        capacity = int((mask != 0).sum().item())
+    row_ptr = torch.empty(rows + 1, dtype=torch.int64, device=dev)
+    col_idx = torch.empty(max(int(capacity), 1), dtype=torch.int32, device=dev)
+    out = torch.empty(max(int(capacity), 1), dtype=torch.float16, device=dev)
+    nnz = C.c_int64(0)
+    st = lib.gptq_ssqr_outliers_csr(_ptr(mask), _ptr(vals), rows, cols, _ptr(row_ptr),
+                                    _ptr(col_idx), _ptr(out), int(capacity),
+                                    0 if sync else GPTQ_FLAG_NO_SYNC,
+                                    C.byref(nnz) if sync else None, _stream())
+    _check(st, "gptq_ssqr_outliers_csr")
+    n = int(nnz.value) if sync else int(capacity)
+    return row_ptr, col_idx[:n], out[:n]
+
+
+def _with_csr(layer: SSQRLayer) -> SSQRLayer:
+    layer.row_ptr, layer.col_idx, layer.csr_vals = ssqr_outliers_csr(
+        layer.outlier_mask, layer.outlier_vals, capacity=layer.n_outliers)
+    return layer
 
 
 def _ssqr_args(W, U, perm, group_size):
@@ -304,7 +355,8 @@ def quantize_layer_ssqr(W, U, perm=None, bits: int = 4, group_size: int = 128,
                         alpha: float = 1.0) -> SSQRLayer:
     """The sweep under the SSQR rule at scale factor ``alpha`` (synchronous):
     out-of-grid levels kept as fp16 outliers, reported as a dense mask and
-    values in the original column order."""
+    values in the original column order and compacted on the device into
+    compressed sparse rows (their stored form)."""
     rows, cols, o, ws = _ssqr_args(W, U, perm, group_size)
     n = C.c_uint64(0)
     st = lib.gptq_quantize_layer_ssqr(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols,
@@ -316,7 +368,7 @@ def quantize_layer_ssqr(W, U, perm=None, bits: int = 4, group_size: int = 128,
     _check(st, "gptq_quantize_layer_ssqr")
     q = QuantizedLayer(o["codes"], o["scales"], o["zeros"], o["g_idx"], o["row_loss"], bits,
                        group_size)
-    return SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(alpha))
+    return _with_csr(SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(alpha)))
 
 
 def ssqr_search(W, U, perm=None, bits: int = 4, group_size: int = 128, target: float = 0.01,
@@ -336,7 +388,7 @@ def ssqr_search(W, U, perm=None, bits: int = 4, group_size: int = 128, target: f
     _check(st, "gptq_ssqr_search")
     q = QuantizedLayer(o["codes"], o["scales"], o["zeros"], o["g_idx"], o["row_loss"], bits,
                        group_size)
-    return SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(a.value))
+    return _with_csr(SSQRLayer(q, o["mask"], o["vals"], int(n.value), float(a.value)))
 
 
 @dataclass

@@ -243,3 +243,24 @@ def test_profile_api_without_launches():
     g.profile_enable(False)
     assert "quant_sweep" in r and "hessian_tile" in r
     assert all(v == (0.0, 0) for v in r.values())
+
+
+def test_ssqr_csr_host_checks():
+    """gptq_ssqr_outliers_csr rejects bad arguments before any launch."""
+    f = g.lib.gptq_ssqr_outliers_csr
+    n = C.c_int64(0)
+
+    def call(mask=FAKE, vals=FAKE, rows=4, cols=8, rp=FAKE, ci=FAKE, cv=FAKE, cap=3, flags=0,
+             nnz=None):
+        return f(mask, vals, rows, cols, rp, ci, cv, cap, flags, nnz, NULL)
+    assert call(rp=NULL) == g.GPTQ_EINVAL
+    assert call(rows=-1) == g.GPTQ_EINVAL
+    assert call(cols=-1) == g.GPTQ_EINVAL
+    assert call(cap=-1) == g.GPTQ_EINVAL
+    assert call(cols=1 << 31) == g.GPTQ_EINVAL
+    assert call(mask=NULL) == g.GPTQ_EINVAL
+    assert call(vals=NULL) == g.GPTQ_EINVAL
+    assert call(ci=NULL) == g.GPTQ_EINVAL
+    assert call(cv=NULL) == g.GPTQ_EINVAL
+    assert call(flags=1) == g.GPTQ_EINVAL
+    assert call(flags=g.GPTQ_FLAG_NO_SYNC, nnz=C.byref(n)) == g.GPTQ_EINVAL

@@ -315,7 +315,7 @@ def test_chmc_pipeline_two_streams_equals_serial_calls():
     with every status read through check()."""
     from post_weight_quantization_hessian_amd.pipeline import CHMC_DAMP, LayerGroup
     say("chmc pipeline fork/join against serial calls")
-    dim, n, gs, bpw = 640, 1500, 64, 4.2875
+    dim, n, gs, bpw = 640, 1500, 64, 5.0  # ranks 6, 15, 1, 5
     layers = [("a", 192), ("b", 70)]
     rng = np.random.default_rng(31)
     X = (rng.standard_normal((n, dim)) * np.exp(0.5 * rng.standard_normal(dim))[None, :]

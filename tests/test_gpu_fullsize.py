@@ -7,8 +7,15 @@ with overwrite on the first chunk, asynchronous prepare and quantize).
 * 70B-shape down projection 8192 x 28672: 65536 tokens with log-normal channel
   scales, 2-bit and 4-bit groups of 64, act-order.
 
-Their Hessians are out of the oracle's reach as a whole, so it computes what it
-can one piece at a time:
+The oracle's own results for 64 seeded rows of every layer and bit width are
+stored under tests/golden/ (written by tests/golden/make_fullsize_goldens.py,
+which calls only the seeded generator and the oracle: the whole S over all
+tokens, the damped H, act-order, U = chol(inv(H_p))^T and the strict sweep of
+those rows). The GPU's act-order must equal the stored one, and its codes,
+scales, zero points and row losses on those rows meet the parity bar against
+the stored ones (CHMC article, Methodik, Schritt 2).
+
+Beside that, the oracle computes what it can on the box one piece at a time:
 
 * sampled entries of S, each the exactly rounded sum over all tokens;
 * diag S of every feature, the damping term and the act-order permutation;
@@ -30,6 +37,7 @@ and properties of the library's outputs hold at any size:
 * sum_j e_j^2 = (w - q) H (w - q)^T (the loss identity, sampled rows);
 * codes, zero points and g_idx are valid; a second run is bit-identical.
 """
+import os
 import sys
 import time
 
@@ -48,6 +56,9 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 from post_weight_quantization_hessian_amd.pipeline import LayerGroup  # noqa: E402
 from tests import split8_ref as R8  # noqa: E402
+from tests.parity_util import CODE_AGREE, compare_layer, first_divergence  # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 DEV = torch.device("cuda:0")
 F64 = np.float64
@@ -212,6 +223,28 @@ def test_fullsize_sampled(wname):
     udiag = Urows[torch.arange(len(J), device=DEV), jt]
     dres = (ydiag - 1.0 / udiag).abs() / A[torch.arange(len(J), device=DEV), jt]
     assert float(dres.max()) <= U_TOL, float(dres.max())
+
+    # ---- the oracle's stored sweep of 64 sampled rows (whole-Hessian oracle)
+    gold = np.load(os.path.join(GOLDEN, f"fullsize_{wname}.npz"))
+    assert int(gold["n_rows_total"]) == rows and int(gold["group_size"]) == gsz
+    assert tuple(gold["bits"].tolist()) == tuple(wl.bits)
+    assert np.array_equal(perm, gold["perm"].astype(np.int64)), "act-order differs from the oracle's"
+    sel = gold["rows"].astype(np.int64)
+    for bi, bits in enumerate(wl.bits):
+        q = grp.outs[bi]
+        gpu = dict(codes=q.codes[sel].cpu().numpy().astype(np.int64),
+                   scales=q.scales[sel].cpu().numpy().astype(F64),
+                   zeros=q.zeros[sel].cpu().numpy().astype(F64),
+                   row_loss=q.row_loss[sel].cpu().numpy())
+        ref = dict(codes=gold[f"codes_{bits}"].astype(np.int64),
+                   scales=gold[f"scales_{bits}"].astype(F64),
+                   zeros=gold[f"zeros_{bits}"].astype(F64),
+                   row_loss=gold[f"row_loss_{bits}"])
+        rep = compare_layer(gpu, ref, name=f"{wname} {bits}-bit, {len(sel)} oracle rows")
+        fd = first_divergence(gpu["codes"][:, pr], ref["codes"][:, pr])
+        say(f"{wname}/{bits}-bit: rows with a differing code {int((fd < dim).sum())}, "
+            f"first divergence (sweep order) min {int(fd.min())}")
+        assert rep["codes_agree"] >= CODE_AGREE
 
     # ---- sweep outputs, per bit width
     Wp = W.astype(F64)[:, pr]

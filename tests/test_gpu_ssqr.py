@@ -58,6 +58,33 @@ def compare_ssqr(res, ref, name):
     assert np.array_equal(vals[both], ref["outlier_vals"][both])
     assert np.all(vals[~mask] == 0.0)
     compare_layer(to_numpy_layer(res.layer), ref, name=name)
+    compare_csr(res, ref, name)
+
+
+def compare_csr(res, ref, name):
+    """The stored (CSR) outliers against the oracle's, element by element:
+    every row whose outlier set agrees with the oracle's (all rows, at 100 %
+    mask agreement) has the same columns and fp16 values, in column order."""
+    rp_r, ci_r, cv_r = O.ssqr_csr(ref["outlier"], ref["outlier_vals"])
+    rp = res.row_ptr.cpu().numpy()
+    ci = res.col_idx.cpu().numpy().astype(np.int64)
+    cv = res.csr_vals.cpu().numpy().astype(np.float64)
+    assert rp[0] == 0 and rp[-1] == res.n_outliers == len(ci) == len(cv)
+    mask = res.outlier_mask.cpu().numpy().astype(bool)
+    same = np.all(mask == ref["outlier"], axis=1)
+    say(f"{name}: CSR {len(ci)} entries, {int(same.sum())}/{len(same)} rows with the "
+        f"oracle's outlier set")
+    for r in np.nonzero(same)[0]:
+        a, b = rp[r], rp[r + 1]
+        ar, br = rp_r[r], rp_r[r + 1]
+        assert b - a == br - ar, r
+        assert np.array_equal(ci[a:b], ci_r[ar:br]), r
+        assert np.array_equal(cv[a:b], cv_r[ar:br]), r
+    if same.all():
+        assert np.array_equal(rp, rp_r)
+    rows, cols = mask.shape
+    assert res.bits_per_weight == O.bpw_ssqr(rows, cols, res.layer.bits, res.layer.group_size,
+                                             res.n_outliers)
 
 
 @pytest.mark.parametrize("rows,cols,bits,gs,act,alpha", [
@@ -134,3 +161,42 @@ def test_ssqr_qwen_down_projection_full_shape():
     Sr, nr = O.hessian_sum(X)
     ref = O.gptq_layer(W, Sr, nr, bits=4, group_size=128, block=128, ssqr_alpha=res.alpha)
     compare_ssqr(res, ref, "ssqr qwen down")
+
+
+@pytest.mark.parametrize("rows,cols,dens", [(5, 1, 1.0), (70, 333, 0.02), (3, 64, 0.0),
+                                            (1500, 130, 0.5), (0, 10, 0.0), (4, 0, 0.0)])
+def test_ssqr_csr_compaction_edge_cases(rows, cols, dens):
+    """gptq_ssqr_outliers_csr on seeded masks: empty rows and layers, one
+    column, a ragged last 64-column chunk, more than 1024 rows (several scan
+    rounds); against the oracle's CSR of the same mask, element by element."""
+    say(f"csr compaction {rows}x{cols} density {dens}")
+    rng = np.random.default_rng(rows * 7 + cols)
+    m = (rng.random((rows, cols)) < dens).astype(np.uint8)
+    v = np.where(m, rng.uniform(-3, 3, (rows, cols)), 0.0).astype(np.float16)
+    rp, ci, cv = G.ssqr_outliers_csr(torch.from_numpy(m).to(DEV), torch.from_numpy(v).to(DEV))
+    rp_r, ci_r, cv_r = O.ssqr_csr(m, v)
+    assert np.array_equal(rp.cpu().numpy(), rp_r)
+    assert np.array_equal(ci.cpu().numpy().astype(np.int64), ci_r)
+    assert np.array_equal(cv.cpu().numpy(), cv_r)
+
+
+def test_ssqr_csr_capacity_too_small_is_reported():
+    """A capacity below the count: GPTQ_EINVAL, row offsets still complete,
+    the entry arrays untouched."""
+    say("csr compaction, capacity too small")
+    rng = np.random.default_rng(3)
+    m = (rng.random((40, 100)) < 0.1).astype(np.uint8)
+    v = np.where(m, 1.0, 0.0).astype(np.float16)
+    n = int(m.sum())
+    md, vd = torch.from_numpy(m).to(DEV), torch.from_numpy(v).to(DEV)
+    row_ptr = torch.empty(41, dtype=torch.int64, device=DEV)
+    ci = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    cv = torch.zeros(n, dtype=torch.float16, device=DEV)
+    import ctypes as C
+    nnz = C.c_int64(0)
+    st = G.lib.gptq_ssqr_outliers_csr(G._ptr(md), G._ptr(vd), 40, 100, G._ptr(row_ptr),
+                                      G._ptr(ci), G._ptr(cv), n - 1, 0, C.byref(nnz),
+                                      G._stream())
+    assert st == G.GPTQ_EINVAL and nnz.value == n
+    assert np.array_equal(row_ptr.cpu().numpy(), O.ssqr_csr(m, v)[0])
+    assert torch.all(ci == -7)

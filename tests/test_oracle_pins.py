@@ -728,3 +728,31 @@ def test_chmc_layer_loss_identity_and_reconstruction():
     D = (res["R"] - res["deq"])[:, perm]
     np.testing.assert_allclose(res["row_loss"], O.loss_quadratic(D, O.permute_sym(H, perm)),
                                rtol=1e-10)
+
+
+def test_ssqr_csr_hand_example():
+    """Compressed sparse rows of a small outlier set, written out by hand
+    (rows with no outlier, several per row, first and last columns)."""
+    g = GOLD["ssqr_csr"]
+    rp, ci, cv = O.ssqr_csr(np.array(g["mask"], dtype=np.uint8), np.array(g["vals"]))
+    assert rp.tolist() == g["row_ptr"] and ci.tolist() == g["col_idx"]
+    assert cv.tolist() == g["csr_vals"]
+    nr, nc = np.array(g["mask"]).shape
+    assert O.bpw_ssqr(nr, nc, g["bits"], g["gs"], len(g["col_idx"])) == g["bpw"]
+
+
+def test_ssqr_csr_matches_library_sparse_matrix():
+    """On random masks (values nonzero at every outlier, as an outlier's fp16
+    value is far from 0) the CSR equals scipy's compressed sparse row form of
+    the masked dense matrix."""
+    sp = pytest.importorskip("scipy.sparse")
+    rng = np.random.default_rng(12)
+    for rows, cols, dens in [(7, 130, 0.05), (1, 1, 1.0), (9, 64, 0.0), (33, 200, 0.3)]:
+        m = rng.random((rows, cols)) < dens
+        v = np.where(m, rng.choice([-1.0, 1.0], (rows, cols)) * rng.uniform(1, 2, (rows, cols)),
+                     0.0).astype(np.float16)
+        rp, ci, cv = O.ssqr_csr(m.astype(np.uint8), v)
+        ref = sp.csr_matrix(v.astype(np.float64))
+        ref.sort_indices()
+        assert np.array_equal(rp, ref.indptr) and np.array_equal(ci, ref.indices)
+        assert np.array_equal(cv.astype(np.float64), ref.data)
