@@ -177,6 +177,29 @@ gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int64_t cols, i
                                 void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gptq_quantize_layer_noalloc — for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): gptq_quantize_layer with the same arguments, flags,
+ * outputs and statuses, minus the workspace. Its scratch is one fixed array
+ * of the library in device memory, 64 MiB per device, which each device
+ * holds from the first call there until the process ends; the call itself
+ * allocates nothing.
+ *   - A layer whose workspace (gptq_quantize_workspace_bytes) exceeds 64 MiB
+ *     is rejected with GPTQ_EWORKSPACE before anything is enqueued (896 x
+ *     4864 at groups of 128 fits; 9728 x 896 does not).
+ *   - `stream` must belong to the current device (else GPTQ_EINVAL).
+ *   - Every call on a device shares that device's array and leaves its
+ *     contents there; each call clears what it needs cleared, so calls one
+ *     after the other are fine, but calls that overlap in time on one device
+ *     (other streams, other host threads) race and give wrong results.
+ * ------------------------------------------------------------------------- */
+gptq_status gptq_quantize_layer_noalloc(const uint16_t* W, int64_t rows, int64_t cols,
+                                        int64_t ldw, const float* U, const int32_t* perm,
+                                        int bits, int group_size, uint32_t flags,
+                                        uint8_t* codes, uint16_t* scales, uint16_t* zeros,
+                                        int32_t* g_idx, double* row_loss, void* stream);
+
+/* ---------------------------------------------------------------------------
  * SSQR — The Geometry of LLM Quantization, section 3 ("Skalengerechte SpQR":
  * outliers that would overflow the grid are kept as sparse floating-point
  * values; a binary search on the scales meets a target outlier density).

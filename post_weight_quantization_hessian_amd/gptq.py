@@ -50,6 +50,10 @@ EXPORTS = {
                                    C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "gptq_quantize_layer_noalloc": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64,
+                                              C.c_void_p, C.c_void_p, C.c_int, C.c_int,
+                                              C.c_uint32, C.c_void_p, C.c_void_p, C.c_void_p,
+                                              C.c_void_p, C.c_void_p, C.c_void_p]),
     "gptq_ssqr_outliers_csr": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64,
                                          C.c_void_p, C.c_void_p, C.c_void_p, C.c_int64,
                                          C.c_uint32, C.c_void_p, C.c_void_p]),

@@ -264,3 +264,25 @@ def test_ssqr_csr_host_checks():
     assert call(cv=NULL) == g.GPTQ_EINVAL
     assert call(flags=1) == g.GPTQ_EINVAL
     assert call(flags=g.GPTQ_FLAG_NO_SYNC, nnz=C.byref(n)) == g.GPTQ_EINVAL
+
+
+def test_noalloc_host_checks():
+    """gptq_quantize_layer_noalloc: the argument checks of gptq_quantize_layer,
+    then a layer whose workspace exceeds the 64 MiB array is rejected, all
+    before any HIP call."""
+    f = g.lib.gptq_quantize_layer_noalloc
+
+    def call(rows=4, cols=8, ldw=8, bits=4, gs=16, flags=0, W=FAKE, U=FAKE, codes=FAKE):
+        return f(W, rows, cols, ldw, U, NULL, bits, gs, flags, codes, FAKE, FAKE, NULL, FAKE,
+                 NULL)
+    assert call(bits=1) == g.GPTQ_EINVAL
+    assert call(gs=100) == g.GPTQ_EINVAL
+    assert call(ldw=7) == g.GPTQ_EINVAL
+    assert call(W=NULL) == g.GPTQ_EINVAL
+    assert call(codes=NULL) == g.GPTQ_EINVAL
+    assert call(flags=1) == g.GPTQ_EINVAL
+    assert call(rows=0) == g.GPTQ_OK  # an empty layer: nothing to do
+    assert g.quantize_workspace_bytes(9728, 896, 128) > 64 << 20
+    assert call(rows=9728, cols=896, ldw=896, gs=128) == g.GPTQ_EWORKSPACE
+    assert g.quantize_workspace_bytes(4096, 14336, 128) > 64 << 20
+    assert call(rows=4096, cols=14336, ldw=14336, gs=128) == g.GPTQ_EWORKSPACE
