@@ -267,9 +267,11 @@ __device__ inline int h8_exponent(unsigned bits) {
   return e;
 }
 
-// Digit planes dig[a][f][k] (a = 0..3, f < dpad, k < npad; int8, tokens
-// contiguous), zero outside the token and feature range and in columns
-// holding NaN/Inf. Workgroup: 64 features x 64 tokens; thread t takes
+// Digits of feature f, 64-token chunk c (c < npad / 64) and plane a (0..3)
+// at dig[((f * (npad / 64) + c) * 4 + a) * 64 + k % 64] (int8): the four
+// planes of one feature and chunk are one contiguous 256-byte block, so that
+// the tile kernel's loads of a chunk use whole cache lines. Zero outside the
+// token and feature range and in columns holding NaN/Inf. Workgroup: 64 features x 64 tokens; thread t takes
 // feature t % 64 and 16 consecutive tokens. Blocks with blockIdx.x == 0 also
 // write the column exponents. Grid (npad / 64, dpad / 64).
 __global__ __launch_bounds__(256) void h8_split_kernel(const float* __restrict__ X, int64_t ldx,
@@ -308,7 +310,8 @@ __global__ __launch_bounds__(256) void h8_split_kernel(const float* __restrict__
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     uint4 v = make_uint4(w[a][0], w[a][1], w[a][2], w[a][3]);
-    *reinterpret_cast<uint4*>(dig + ((int64_t)a * dpad + f) * npad + k0) = v;
+    *reinterpret_cast<uint4*>(dig + ((f * (npad / H8_KB) + blockIdx.x) * 4 + a) * H8_KB +
+                              tg * 16) = v;
   }
 }
 
@@ -366,16 +369,20 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
   // 2 (lrow / 64) and 2 (lrow / 64) + 1; 16-byte chunk lch of the 64 tokens
   const int lrow = tid >> 2, lch = tid & 3;
   const int brw = lrow & 63, bpl = (lrow >> 6) * 2;
-  const int64_t plane = dpad * npad;
-  const int8_t* gA = dig + (fa + lrow) * npad + t0 + lch * 16;
-  const int8_t* gB = dig + bpl * plane + (fb + brw) * npad + t0 + lch * 16;
+  // one chunk of a feature: 4 planes x 64 tokens, contiguous (256 bytes)
+  constexpr int CHB = 4 * H8_KB;
+  const int64_t nchk = npad / H8_KB;
+  const int8_t* gA = dig + ((fa + lrow) * nchk + t0 / H8_KB) * CHB + lch * 16;
+  const int8_t* gB = dig + ((fb + brw) * nchk + t0 / H8_KB) * CHB + bpl * H8_KB + lch * 16;
   i4v ra[4], rb[2];
   auto fetch = [&](int k) {
     if (k > nst - 1) k = nst - 1;  // past the end: reload the last chunk (never used)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ra[q] = *reinterpret_cast<const i4v*>(gA + q * plane + k * H8_KB);
+    for (int q = 0; q < 4; ++q)
+      ra[q] = *reinterpret_cast<const i4v*>(gA + (int64_t)k * CHB + q * H8_KB);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) rb[q] = *reinterpret_cast<const i4v*>(gB + q * plane + k * H8_KB);
+    for (int q = 0; q < 2; ++q)
+      rb[q] = *reinterpret_cast<const i4v*>(gB + (int64_t)k * CHB + q * H8_KB);
   };
   // LDS rows of 64 bytes; chunk c of row r sits at position c ^ ((r >> 2) & 3).
   // Stores (four lanes per row, 16 lanes = 4 consecutive rows) cover 64

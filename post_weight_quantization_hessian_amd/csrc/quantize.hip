@@ -13,6 +13,8 @@
 // the register window shifts by one slot every 4 columns so the live column
 // is always slot 0, and the scaled error of the live column is broadcast to
 // the quad with a DPP quad permute. Group min/max reductions also use DPP.
+#include <type_traits>
+
 #include "common.h"
 
 namespace gptq {
@@ -282,6 +284,36 @@ __global__ __launch_bounds__(256) void q_gemm_kernel(const float* __restrict__ E
 // with row_newbcast. Group min/max and the loss are reduced over the row with
 // quad permutes and row rotations.
 __device__ inline double row_ror4(double v) { return dpp_f64<0x124>(v); }
+// row_newbcast of lane N as a plain DPP move (no "old" operand to keep)
+template <int N>
+__device__ inline double row_bcast_mov(double v) {
+  union { double d; int i[2]; } a, b;
+  a.d = v;
+  b.i[0] = __builtin_amdgcn_mov_dpp(a.i[0], 0x150 + N, 0xF, 0xF, false);
+  b.i[1] = __builtin_amdgcn_mov_dpp(a.i[1], 0x150 + N, 0xF, 0xF, false);
+  return b.d;
+}
+// the same for a lane index that is a constant after loop unrolling
+__device__ inline double row_bcast_mov_i(double v, int n) {
+  switch (n) {
+    case 0: return row_bcast_mov<0>(v);
+    case 1: return row_bcast_mov<1>(v);
+    case 2: return row_bcast_mov<2>(v);
+    case 3: return row_bcast_mov<3>(v);
+    case 4: return row_bcast_mov<4>(v);
+    case 5: return row_bcast_mov<5>(v);
+    case 6: return row_bcast_mov<6>(v);
+    case 7: return row_bcast_mov<7>(v);
+    case 8: return row_bcast_mov<8>(v);
+    case 9: return row_bcast_mov<9>(v);
+    case 10: return row_bcast_mov<10>(v);
+    case 11: return row_bcast_mov<11>(v);
+    case 12: return row_bcast_mov<12>(v);
+    case 13: return row_bcast_mov<13>(v);
+    case 14: return row_bcast_mov<14>(v);
+    default: return row_bcast_mov<15>(v);
+  }
+}
 __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 
 // MODE 1, SSQR (The Geometry of LLM Quantization, section 3): the group's
@@ -433,7 +465,10 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   __syncthreads();
   // Row a of the slab is stored divided by U[a][a] (the error broadcast along
   // a row is then the unscaled residual d, and e = d / U[a][a] leaves the
-  // dependent chain). Entries below the diagonal are zero.
+  // dependent chain). Entries on and below the diagonal are zero: a column's
+  // own update (its diagonal term) is left out, so the slot holding the
+  // column keeps the value it was quantized from until the tile ends, when
+  // its code and error are formed from it again.
   if (vec_slab) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -442,7 +477,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         const int a = e >> 5, c4 = (e & 31) * 4;
         const double ra = rdiag[a];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) Us[e * 4 + x] = c4 + x >= a ? (double)sv[u][x] * ra : 0.0;
+        for (int x = 0; x < 4; ++x) Us[e * 4 + x] = c4 + x > a ? (double)sv[u][x] * ra : 0.0;
       }
     }
     // fewer than 256 threads: the rest of the slab
@@ -451,12 +486,12 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       const f4 v = *reinterpret_cast<const f4*>(U + (j0 + a) * ldu + j0 + c4);
       const double ra = rdiag[a];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) Us[e * 4 + x] = c4 + x >= a ? (double)v[x] * ra : 0.0;
+      for (int x = 0; x < 4; ++x) Us[e * 4 + x] = c4 + x > a ? (double)v[x] * ra : 0.0;
     }
   } else {
     for (int e = t; e < QB * QB; e += nthr) {
       const int a = e >> 7, c = e & 127;
-      Us[e] = (a < bw && c < bw && c >= a) ? (double)U[(j0 + a) * ldu + j0 + c] * rdiag[a] : 0.0;
+      Us[e] = (a < bw && c < bw && c > a) ? (double)U[(j0 + a) * ldu + j0 + c] * rdiag[a] : 0.0;
     }
   }
   // (lt was written before the first barrier above)
@@ -537,74 +572,68 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         zeros[r * ldg + g] = f64_to_f16_rne(zero);
       }
     }
-    // the residual d and clamped level k of the column this lane owns (SSQR:
-    // whether it is an outlier, and its fp16 value)
-    double d_own = 0.0, k_own = 0.0;
-    bool o_own = false;
-    double h_own = 0.0;  // SSQR: the column's value rounded to fp16
+    // The 16 columns of the tile. Slot s of lane q holds column
+    // 16 (tt + s) + q; in a full block only slots s < 8 - tt are inside it
+    // (NS live slots), and only those are loaded and updated. Every lane
+    // rounds its slot 0 each column, the owner's (lane jj's) residual is
+    // broadcast to its row, and later columns take the update; the owner's
+    // own slot is left as it was (zero diagonal of the slab).
+    auto tile = [&](auto ns_c, auto full_c) {
+      constexpr int NS = decltype(ns_c)::value;
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      if (16 * tt + jj < bw) {
-        double (&u)[8] = ub[jj & 3];
-        {
-          // row 16 tt + jj + 2 at a fixed offset from the group's base (one
-          // address register for the whole group; rows past the block end
-          // are zero rows of the slab or its padding)
-          const int jc = jj + 2;
-          const double* urow = ubase + jc * QB + 16 * (jc >> 4);
+      for (int jj = 0; jj < 16; ++jj) {
+        if (FULL || 16 * tt + jj < bw) {
+          double (&u)[8] = ub[jj & 3];
+          {
+            // row 16 tt + jj + 2 at a fixed offset from the tile's base (one
+            // address register for the whole tile; rows past the block end
+            // are zero rows of the slab or its padding)
+            const int jc = jj + 2;
+            const double* urow = ubase + jc * QB + 16 * (jc >> 4);
 #pragma unroll
-          for (int s = 0; s < 8; ++s) ub[(jj + 2) & 3][s] = urow[16 * s];
-        }
-        // quantize slot 0 (meaningful on the owner lane q == jj):
-        // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
-        // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
-        const double v = w[0];
-        const double kr = rint(v * rscale);
-        const double k = fmin(fmax(kr, klo), khi);
-        double d = fma(-scale, k, v);
-        bool out = false;
-        double vh = 0.0;
-        if (SSQR) {
-          out = kr < klo || kr > khi;
-          vh = f16_round_f64(v);
-          if (out) d = v - vh;
-        }
-        double db;
-        switch (jj) {
-          case 0: db = row_bcast<0>(d); break;
-          case 1: db = row_bcast<1>(d); break;
-          case 2: db = row_bcast<2>(d); break;
-          case 3: db = row_bcast<3>(d); break;
-          case 4: db = row_bcast<4>(d); break;
-          case 5: db = row_bcast<5>(d); break;
-          case 6: db = row_bcast<6>(d); break;
-          case 7: db = row_bcast<7>(d); break;
-          case 8: db = row_bcast<8>(d); break;
-          case 9: db = row_bcast<9>(d); break;
-          case 10: db = row_bcast<10>(d); break;
-          case 11: db = row_bcast<11>(d); break;
-          case 12: db = row_bcast<12>(d); break;
-          case 13: db = row_bcast<13>(d); break;
-          case 14: db = row_bcast<14>(d); break;
-          default: db = row_bcast<15>(d); break;
-        }
-        d_own = q == jj ? d : d_own;
-        k_own = q == jj ? k : k_own;
-        if (SSQR) {
-          o_own = q == jj ? out : o_own;
-          h_own = q == jj ? vh : h_own;
-        }
-        // later columns: w -= d * U[j][c] / U[j][j]. Slot 0 of the lanes at
-        // or before the pivot is dead (its slab entry, below the diagonal, is
-        // 0); slots past the block end are dead too.
+            for (int s = 0; s < NS; ++s) ub[(jj + 2) & 3][s] = urow[16 * s];
+          }
+          // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
+          // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
+          const double v = w[0];
+          const double kr = rint(v * rscale);
+          double d = fma(-scale, fmin(fmax(kr, klo), khi), v);
+          if (SSQR && (kr < klo || kr > khi)) d = v - f16_round_f64(v);
+          const double db = row_bcast_mov_i(d, jj);
+          // later columns: w -= d * U[j][c] / U[j][j] (zero for this column
+          // and the ones before it)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) w[s] -= db * u[s];
+          for (int s = 0; s < NS; ++s) w[s] = fma(-db, u[s], w[s]);
+        }
       }
+    };
+    if (bw == QB) {
+      switch (8 - tt) {
+        case 8: tile(std::integral_constant<int, 8>{}, std::true_type{}); break;
+        case 7: tile(std::integral_constant<int, 7>{}, std::true_type{}); break;
+        case 6: tile(std::integral_constant<int, 6>{}, std::true_type{}); break;
+        case 5: tile(std::integral_constant<int, 5>{}, std::true_type{}); break;
+        case 4: tile(std::integral_constant<int, 4>{}, std::true_type{}); break;
+        case 3: tile(std::integral_constant<int, 3>{}, std::true_type{}); break;
+        case 2: tile(std::integral_constant<int, 2>{}, std::true_type{}); break;
+        default: tile(std::integral_constant<int, 1>{}, std::true_type{}); break;
+      }
+    } else {
+      tile(std::integral_constant<int, 8>{}, std::false_type{});
     }
-    // codes and scaled errors of this row's 16 columns, one store each
+    // codes and scaled errors of this row's 16 columns, one store each: slot
+    // 0 still holds the value the lane's column was quantized from
     {
       const int c = 16 * tt + q;
       if (rv && c < bw) {
+        const double v = w[0];
+        const double kr = rint(v * rscale);
+        const double k_own = fmin(fmax(kr, klo), khi);
+        double d_own = fma(-scale, k_own, v);
+        const bool o_own = SSQR && (kr < klo || kr > khi);
+        const double h_own = SSQR ? f16_round_f64(v) : 0.0;
+        if (o_own) d_own = v - h_own;
         const double e = d_own * rdiag[c];
         codes[r * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero, 0.0), 255.0);
         E[r * lde + j0 + c] = (float)e;

@@ -230,6 +230,8 @@ def test_fullsize_sampled(wname):
     assert tuple(gold["bits"].tolist()) == tuple(wl.bits)
     assert np.array_equal(perm, gold["perm"].astype(np.int64)), "act-order differs from the oracle's"
     sel = gold["rows"].astype(np.int64)
+    g_gold = np.empty(dim, dtype=np.int64)
+    g_gold[gold["perm"].astype(np.int64)] = np.arange(dim) // gsz
     for bi, bits in enumerate(wl.bits):
         q = grp.outs[bi]
         gpu = dict(codes=q.codes[sel].cpu().numpy().astype(np.int64),
@@ -239,7 +241,7 @@ def test_fullsize_sampled(wname):
         ref = dict(codes=gold[f"codes_{bits}"].astype(np.int64),
                    scales=gold[f"scales_{bits}"].astype(F64),
                    zeros=gold[f"zeros_{bits}"].astype(F64),
-                   row_loss=gold[f"row_loss_{bits}"])
+                   row_loss=gold[f"row_loss_{bits}"], g_idx=g_gold)
         rep = compare_layer(gpu, ref, name=f"{wname} {bits}-bit, {len(sel)} oracle rows")
         fd = first_divergence(gpu["codes"][:, pr], ref["codes"][:, pr])
         say(f"{wname}/{bits}-bit: rows with a differing code {int((fd < dim).sum())}, "
