@@ -329,6 +329,41 @@ gptq_status gptq_fp16_round_host(const double* in, uint16_t* out, int64_t n);
 int gptq_version(void);
 
 /* ---------------------------------------------------------------------------
+ * HPTQ code stream — the stored form of HPTQ's levels (The Geometry of LLM
+ * Quantization, section 3: the integer levels are Huffman-coded).
+ * gptq_hptq_encode: levels (in, int16 [rows x cols], device, row-major, e.g.
+ *   the levels of gptq_quantize_layer_hptq) as one bit stream, rows in order,
+ *   each row's levels in column order:
+ *   - code lengths: a Huffman code of the call's level histogram (the two
+ *     lightest subtrees merged first; ties to the subtree made earlier, the
+ *     leaves in increasing level order); a single distinct level costs 1 bit;
+ *   - codes: the canonical code of those lengths (levels ordered by length,
+ *     then value; the first code 0, each next one the previous plus one,
+ *     shifted left by the growth in length), most significant bit first;
+ *   - bit b of the stream is bit 31 - b % 32 of words[b / 32];
+ *   code_len (out, host [65536], may be NULL): the length of level v at
+ *     v + 32768, 0 for levels that do not occur;
+ *   words (out, device uint32 [capacity_words]); row_bit (out, device int64
+ *     [rows + 1]): the stream position of each row's first code, row_bit[rows]
+ *     = *total_bits (out, host). A capacity below ceil(total / 32) words is
+ *     GPTQ_EINVAL with row_bit and *total_bits still set; a code longer than 63
+ *     bits is GPTQ_EINVAL. Synchronizes `stream`.
+ * gptq_hptq_decode: the inverse (one device thread per row): words [nwords],
+ *   row_bit and code_len from gptq_hptq_encode; levels (out, device int16
+ *   [rows x cols]). A stream that does not decode is GPTQ_EINVAL.
+ *   Synchronizes `stream`.
+ * Workspace (both): gptq_hptq_code_workspace_bytes() bytes (about 1 MB).
+ * ------------------------------------------------------------------------- */
+size_t gptq_hptq_code_workspace_bytes(void);
+gptq_status gptq_hptq_encode(const int16_t* levels, int64_t rows, int64_t cols,
+                             uint8_t* code_len, uint32_t* words, int64_t capacity_words,
+                             int64_t* row_bit, int64_t* total_bits, void* ws, size_t ws_bytes,
+                             void* stream);
+gptq_status gptq_hptq_decode(const uint32_t* words, int64_t nwords, const int64_t* row_bit,
+                             int64_t rows, int64_t cols, const uint8_t* code_len,
+                             int16_t* levels, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * CHMC frontend — CHMC article, "Methodik. Was ist CHMC", Schritt 1-3: the
  * weight is split into a low-rank part, kept as two fp16 factors, and a
  * residual quantized by the GPTQ sweep with one grid per group of output

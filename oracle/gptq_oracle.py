@@ -91,6 +91,7 @@ __all__ = [
     "loss_quadratic", "bpw_gptq", "bpw_page", "num_groups", "group_grid_ssqr", "ssqr_search",
     "ssqr_csr", "bpw_ssqr",
     "group_step_hptq", "huffman_lengths", "hptq_bits_per_weight", "hptq_search",
+    "huffman_canonical", "huffman_encode", "huffman_decode",
     "CHMC_DAMP", "chmc_energies", "chmc_bits", "chmc_rank", "randomized_lowrank", "chmc_lowrank", "gptq_sweep_outgroups",
     "chmc_layer",
 ]
@@ -323,6 +324,67 @@ def huffman_lengths(counts):
         heapq.heappush(heap, (c1 + c2, nxt, a + b))
         nxt += 1
     return length
+
+
+def huffman_canonical(lengths):
+    """Canonical prefix code for code lengths ``lengths`` (dict symbol ->
+    length >= 1): symbols in order of (length, symbol value); the first gets
+    code 0, each next one the previous code plus one, shifted left by the
+    growth in length. Returns dict symbol -> (code, length)."""
+    order = sorted(lengths, key=lambda s_: (lengths[s_], s_))
+    codes = {}
+    code, prev = 0, lengths[order[0]]
+    for i, s_ in enumerate(order):
+        ln = lengths[s_]
+        if i > 0:
+            code = (code + 1) << (ln - prev)
+        codes[s_] = (code, ln)
+        prev = ln
+    return codes
+
+
+def huffman_encode(levels, lengths):
+    """[BABAI] 3 (HPTQ stores the integer levels Huffman-coded): the levels
+    [rows x cols] in row-major order as one bit stream of their canonical
+    codes, most significant code bit first; bit b of the stream is bit
+    31 - b % 32 of 32-bit word b // 32. Returns (words uint32, row_bit int64
+    [rows + 1] with the stream position of each row's first code, total
+    bits)."""
+    lv = np.asarray(levels)
+    codes = huffman_canonical(lengths)
+    bits = []
+    row_bit = [0]
+    for r in range(lv.shape[0]):
+        for v in lv[r].tolist():
+            code, ln = codes[int(v)]
+            bits.extend((code >> (ln - 1 - i)) & 1 for i in range(ln))
+        row_bit.append(len(bits))
+    nw = (len(bits) + 31) // 32
+    words = np.zeros(nw, dtype=np.uint64)
+    for b, bit in enumerate(bits):
+        if bit:
+            words[b // 32] |= np.uint64(1) << np.uint64(31 - b % 32)
+    return words.astype(np.uint32), np.array(row_bit, dtype=np.int64), len(bits)
+
+
+def huffman_decode(words, row_bit, rows, cols, lengths):
+    """Inverse of huffman_encode: read each row's bits from row_bit[r] and
+    match codes bit by bit against the canonical code."""
+    codes = huffman_canonical(lengths)
+    inv = {(c, ln): s_ for s_, (c, ln) in codes.items()}
+    w = np.asarray(words, dtype=np.uint64)
+    out = np.zeros((rows, cols), dtype=np.int64)
+    for r in range(rows):
+        b = int(row_bit[r])
+        for j in range(cols):
+            code, ln = 0, 0
+            while (code, ln) not in inv:
+                bit = int((w[b // 32] >> np.uint64(31 - b % 32)) & np.uint64(1))
+                code, ln, b = (code << 1) | bit, ln + 1, b + 1
+                if ln > 64:
+                    raise ValueError("not a code of this prefix code")
+            out[r, j] = inv[(code, ln)]
+    return out
 
 
 def hptq_bits_per_weight(levels, n_groups_total):

@@ -1,6 +1,7 @@
 // Status strings, the fp16 rounding utility and the optional HIP-event
 // kernel profiler of the GPTQ library.
 #include <atomic>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -14,7 +15,7 @@ static const char* const kKernelNames[K_COUNT] = {
     "quant_init", "quant_permute", "quant_gemm", "quant_sweep", "quant_finalize", "fill",
     "trtri_diag", "chol_potrf_syrk", "trtri_sum", "chol_col", "minpivot_step",
     "minpivot_update", "hessian_digits", "hessian_split8", "quant_hist", "chmc_front",
-    "chmc_update", "chmc_sweep", "ssqr_csr"};
+    "chmc_update", "chmc_sweep", "ssqr_csr", "hptq_code"};
 
 struct ProfRec {
   int kid;
@@ -70,7 +71,12 @@ void prof_end(int kid, hipStream_t s) {
 using namespace gptq;
 
 extern "C" const char* gptq_status_string(gptq_status status) {
-  switch (status) {
+  // a C caller may pass any int: read it without an enum-typed load (outside
+  // the enumerators' range that load is undefined in C++)
+  int code = 0;
+  static_assert(sizeof(code) == sizeof(status), "gptq_status is int-sized");
+  std::memcpy(&code, &status, sizeof code);
+  switch (code) {
     case GPTQ_OK: return "ok";
     case GPTQ_EINVAL: return "invalid argument";
     case GPTQ_ENOTSPD: return "damped Hessian is not positive definite";

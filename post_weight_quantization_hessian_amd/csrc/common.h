@@ -30,7 +30,7 @@ enum KernelId {
   K_CHOL_TRSM, K_CHOL_SYRK, K_TRTRI_ROW, K_TRTRI_UPDATE, K_PREP_UOUT, K_Q_INIT, K_Q_PERMUTE,
   K_Q_GEMM, K_Q_SWEEP, K_Q_FINALIZE, K_FILL, K_TRTRI_DIAG, K_CHOL_STEP, K_TRTRI_SUM, K_CHOL_COL, K_MP_STEP,
   K_MP_UPDATE, K_HESS_DIGITS, K_HESS_SPLIT8, K_Q_HIST, K_CH_FRONT, K_CH_UPDATE, K_CH_SWEEP,
-  K_SP_CSR, K_COUNT
+  K_SP_CSR, K_HF, K_COUNT
 };
 
 // Launch bracketing for the profiler (defined in api.hip).

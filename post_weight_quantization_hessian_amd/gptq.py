@@ -67,6 +67,12 @@ EXPORTS = {
                                    C.c_double, C.c_double, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                    C.c_size_t, C.c_void_p]),
+    "gptq_hptq_code_workspace_bytes": (C.c_size_t, []),
+    "gptq_hptq_encode": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                   C.c_int64, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t,
+                                   C.c_void_p]),
+    "gptq_hptq_decode": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p, C.c_int64, C.c_int64,
+                                   C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "gptq_chmc_rank": (C.c_int, [C.c_int64, C.c_int64, C.c_int, C.c_int, C.c_double]),
     "gptq_chmc_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64, C.c_int]),
     "gptq_chmc_layer": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_int64, C.c_void_p,
@@ -403,6 +409,60 @@ class HPTQLayer:
     row_loss: object   # fp64  [rows]
     bpw: float         # Huffman-coded bits per weight, with 16 per group step
     alpha: float
+
+
+@dataclass
+class HPTQStream:
+    words: object      # uint32 [ceil(total_bits / 32)] on the device
+    row_bit: object    # int64 [rows + 1] on the device
+    code_len: object   # numpy uint8 [65536]: length of level v at v + 32768
+    total_bits: int
+    shape: tuple
+
+
+def hptq_encode(levels) -> HPTQStream:
+    """The Huffman code stream of an int16 level matrix (gptq_hptq_encode)."""
+    torch = _torch()
+    import numpy as np
+    _need(levels, torch.int16, "levels", 2)
+    if not levels.is_contiguous():
+        raise ValueError("levels must be contiguous")
+    rows, cols = levels.shape
+    dev = levels.device
+    ws = _workspace(int(lib.gptq_hptq_code_workspace_bytes()), dev)
+    row_bit = torch.empty(rows + 1, dtype=torch.int64, device=dev)
+    clen = np.zeros(65536, dtype=np.uint8)
+    total = C.c_int64(0)
+
+    def call(words, cap):
+        return lib.gptq_hptq_encode(_ptr(levels), rows, cols, clen.ctypes.data_as(C.c_void_p),
+                                    _ptr(words), cap, _ptr(row_bit), C.byref(total), _ptr(ws),
+                                    ws.numel(), _stream())
+    # first the size (a capacity of 0 returns the total with GPTQ_EINVAL),
+    # then the stream
+    st = call(None, 0)
+    nw = -(-int(total.value) // 32)
+    words = torch.zeros(max(nw, 1), dtype=torch.int32, device=dev)
+    if nw > 0:
+        if st != GPTQ_EINVAL:
+            _check(st, "gptq_hptq_encode")
+        st = call(words, nw)
+    _check(st, "gptq_hptq_encode")
+    return HPTQStream(words[:nw], row_bit, clen, int(total.value), (rows, cols))
+
+
+def hptq_decode(s: HPTQStream):
+    """The levels back from a code stream (gptq_hptq_decode)."""
+    torch = _torch()
+    rows, cols = s.shape
+    dev = s.row_bit.device
+    ws = _workspace(int(lib.gptq_hptq_code_workspace_bytes()), dev)
+    out = torch.empty((rows, cols), dtype=torch.int16, device=dev)
+    st = lib.gptq_hptq_decode(_ptr(s.words), s.words.numel(), _ptr(s.row_bit), rows, cols,
+                              s.code_len.ctypes.data_as(C.c_void_p), _ptr(out), _ptr(ws),
+                              ws.numel(), _stream())
+    _check(st, "gptq_hptq_decode")
+    return out
 
 
 def _hptq_args(W, U, perm, group_size):

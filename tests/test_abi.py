@@ -286,3 +286,25 @@ def test_noalloc_host_checks():
     assert call(rows=9728, cols=896, ldw=896, gs=128) == g.GPTQ_EWORKSPACE
     assert g.quantize_workspace_bytes(4096, 14336, 128) > 64 << 20
     assert call(rows=4096, cols=14336, ldw=14336, gs=128) == g.GPTQ_EWORKSPACE
+
+
+def test_hptq_code_host_checks():
+    """gptq_hptq_encode / gptq_hptq_decode reject bad calls before any launch."""
+    enc, dec = g.lib.gptq_hptq_encode, g.lib.gptq_hptq_decode
+    wsb = g.lib.gptq_hptq_code_workspace_bytes()
+    assert 0 < wsb < 4 << 20
+    n = C.c_int64(0)
+    clen = (C.c_uint8 * 65536)()
+    assert enc(FAKE, -1, 4, None, FAKE, 1, FAKE, C.byref(n), FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert enc(NULL, 4, 4, None, FAKE, 1, FAKE, C.byref(n), FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert enc(FAKE, 4, 4, None, FAKE, 1, NULL, C.byref(n), FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert enc(FAKE, 4, 4, None, FAKE, 1, FAKE, None, FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert enc(FAKE, 4, 4, None, NULL, 1, FAKE, C.byref(n), FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert enc(FAKE, 4, 4, None, FAKE, 1, FAKE, C.byref(n), FAKE, wsb - 1, NULL) == \
+        g.GPTQ_EWORKSPACE
+    assert dec(FAKE, 1, FAKE, 4, 4, None, FAKE, FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert dec(FAKE, -1, FAKE, 4, 4, clen, FAKE, FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert dec(NULL, 1, FAKE, 4, 4, clen, FAKE, FAKE, wsb, NULL) == g.GPTQ_EINVAL
+    assert dec(FAKE, 1, FAKE, 4, 4, clen, FAKE, FAKE, 0, NULL) == g.GPTQ_EWORKSPACE
+    clen[5] = 64  # longer than the 63 bits a code may have
+    assert dec(FAKE, 1, FAKE, 4, 4, clen, FAKE, FAKE, wsb, NULL) == g.GPTQ_EINVAL

@@ -122,3 +122,63 @@ def test_hptq_qwen_down_projection_full_shape():
     Sr, nr = O.hessian_sum(X)
     ref = O.gptq_layer(W, Sr, nr, bits=4, group_size=128, block=128, hptq_alpha=res.alpha)
     compare_hptq(res, ref, 128, "hptq qwen down")
+
+
+def _check_stream(lv_dev, name, bit_exact=True):
+    """gptq_hptq_encode / gptq_hptq_decode on a level matrix: the code
+    lengths are a Huffman code of its histogram (the oracle's, same tie
+    rule), the stream equals the oracle's canonical encoding bit for bit,
+    and decoding gives the levels back."""
+    lv = lv_dev.cpu().numpy().astype(np.int64)
+    s = G.hptq_encode(lv_dev)
+    vals, cnt = np.unique(lv, return_counts=True)
+    ref_len = O.huffman_lengths({int(v): int(c) for v, c in zip(vals, cnt)})
+    lib_len = {int(v): int(s.code_len[int(v) + 32768]) for v in vals}
+    assert int(np.count_nonzero(s.code_len)) == len(vals)
+    assert lib_len == ref_len
+    total = sum(int(c) * ref_len[int(v)] for v, c in zip(vals, cnt))
+    say(f"{name}: {len(vals)} distinct levels, {total} bits ({total / lv.size:.4f} per level)")
+    assert s.total_bits == total
+    if bit_exact:
+        words, row_bit, tb = O.huffman_encode(lv, lib_len)
+        assert tb == total
+        assert np.array_equal(s.row_bit.cpu().numpy(), row_bit)
+        assert np.array_equal(s.words.cpu().numpy().view(np.uint32), words)
+    back = G.hptq_decode(s)
+    assert torch.equal(back, lv_dev)
+
+
+def test_hptq_code_stream_matches_oracle_and_round_trips():
+    say("hptq code stream 150x333")
+    W, X = problem(150, 333, 800, 91)
+    perm, U = gpu_factor(X, True)
+    res = G.quantize_layer_hptq(torch.from_numpy(W).to(DEV), U, perm, bits=3, group_size=32,
+                                alpha=0.8)
+    _check_stream(res.levels, "hptq 150x333")
+
+
+@pytest.mark.parametrize("shape,spread", [((1, 1), 0), ((3, 70), 0), ((40, 129), 3),
+                                          ((1500, 64), 40), ((7, 100), 3000)])
+def test_hptq_code_stream_edge_cases(shape, spread):
+    """One level only (1 bit each), a single row, ragged widths, more than
+    1024 rows (several scan rounds), levels beyond the LDS histogram range."""
+    say(f"hptq code stream {shape} spread {spread}")
+    rng = np.random.default_rng(shape[0] * 31 + spread)
+    lv = np.rint(rng.standard_normal(shape) * spread).astype(np.int16)
+    _check_stream(torch.from_numpy(lv).to(DEV), f"stream {shape}")
+
+
+def test_hptq_code_stream_full_shape_round_trip():
+    """The 896 x 4864 down projection at the search's alpha: the stream size
+    is the Huffman part of the bits per weight, and it decodes to the levels."""
+    say("hptq code stream 896x4864")
+    rows, dim, n = 896, 4864, 2048
+    X = synth.activations(1, "down_in", n, dim, kind="silu_gated")
+    W = synth.weights(1, "down_proj", rows, dim)
+    perm, U = gpu_factor(X, False)
+    res = G.hptq_search(torch.from_numpy(W).to(DEV), U, None, bits=4, group_size=128,
+                        budget=3.125, iters=6)
+    _check_stream(res.levels, "hptq 896x4864", bit_exact=False)
+    s = G.hptq_encode(res.levels)
+    ngt = rows * O.num_groups(dim, 128)
+    assert abs((s.total_bits + 16.0 * ngt) / (rows * dim) - res.bpw) <= 1e-12

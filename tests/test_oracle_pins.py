@@ -756,3 +756,37 @@ def test_ssqr_csr_matches_library_sparse_matrix():
         ref.sort_indices()
         assert np.array_equal(rp, ref.indptr) and np.array_equal(ci, ref.indices)
         assert np.array_equal(cv.astype(np.float64), ref.data)
+
+
+def test_huffman_stream_hand_example():
+    """Canonical codes and the bit stream of a small level matrix, by hand."""
+    g = GOLD["huffman_stream"]
+    lengths = {int(k): v for k, v in g["lengths"].items()}
+    codes = O.huffman_canonical(lengths)
+    assert {k: list(v) for k, v in codes.items()} == {int(k): v for k, v in g["codes"].items()}
+    words, row_bit, total = O.huffman_encode(np.array(g["levels"]), lengths)
+    assert words.tolist() == g["words"] and row_bit.tolist() == g["row_bit"]
+    assert total == g["total_bits"]
+    dec = O.huffman_decode(words, row_bit, 2, 3, lengths)
+    assert dec.tolist() == g["levels"]
+
+
+def test_huffman_canonical_code_is_prefix_free_and_round_trips():
+    rng = np.random.default_rng(17)
+    for n_sym in (1, 2, 3, 9, 40):
+        lv = rng.integers(-n_sym // 2, n_sym - n_sym // 2, size=(7, 53))
+        lv = np.where(rng.random(lv.shape) < 0.6, 0, lv)
+        vals, cnt = np.unique(lv, return_counts=True)
+        lengths = O.huffman_lengths({int(v): int(c) for v, c in zip(vals, cnt)})
+        codes = O.huffman_canonical(lengths)
+        strs = {s: format(c, f"0{ln}b") for s, (c, ln) in codes.items()}
+        for a in strs:
+            assert len(strs[a]) == lengths[a]
+            for b in strs:
+                if a != b:
+                    assert not strs[b].startswith(strs[a]), (a, b)
+        if len(codes) > 1:  # a complete code: Kraft sum exactly 1
+            assert sum(Fraction(1, 2 ** ln) for _, ln in codes.values()) == 1
+        words, row_bit, total = O.huffman_encode(lv, lengths)
+        assert total == sum(int(c) * lengths[int(v)] for v, c in zip(vals, cnt))
+        assert np.array_equal(O.huffman_decode(words, row_bit, *lv.shape, lengths), lv)
