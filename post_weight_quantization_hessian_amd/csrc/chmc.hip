@@ -26,7 +26,6 @@ constexpr int CH_RMAX = 64;   // rank (sketch columns) at most
 constexpr int CH_NITER = 5;   // power iterations (CHMC article, Schritt 1)
 constexpr int CH_QB = 128;    // sweep block width
 constexpr int CH_KS = 64;     // shortest K piece of the block update
-constexpr int CH_RP = 2;      // rows per lane in the residual sweep (1 and 4 measured slower)
 
 __global__ void ch_zero_kernel(unsigned* __restrict__ p, int64_t n) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
@@ -349,28 +348,64 @@ __global__ void ch_factor_kernel(const double* __restrict__ Ul, const double* __
   }
 }
 
-// Res[row][j] = W[row][j] - sum_k A[row][k] B[k][j] (fp64 from the fp16 values).
-__global__ void ch_resid_kernel(const uint16_t* __restrict__ W, int64_t ldw, int64_t o, int64_t i,
-                                const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-                                int r, double* __restrict__ Res, unsigned* __restrict__ status) {
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < o * i;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = e / i, j = e - row * i;
-    double acc = 0.0;
-    for (int k = 0; k < r; ++k)
-      acc = fma(f16_to_f64(A[row * r + k]), f16_to_f64(B[k * i + j]), acc);
-    const double v = f16_to_f64(W[row * ldw + j]) - acc;
-    if (!isfinite(v)) atomicOr(status, ST_NONFINITE);
-    Res[e] = v;
+// The residual, stored by column (rows contiguous, the sweep's lane order):
+//   ResT[j][row] = W[row][j] - sum_k A[row][k] B[k][j]   (fp64 from fp16).
+// One workgroup per 64 x 64 tile: the tile's rows of A and columns of B are
+// staged in LDS, W is read along its rows (all 16 loads of a thread issued
+// together), the tile is turned in LDS and ResT written along its columns.
+__global__ __launch_bounds__(256) void ch_resid_kernel(const uint16_t* __restrict__ W, int64_t ldw,
+                                                       int64_t o, int64_t i,
+                                                       const uint16_t* __restrict__ A,
+                                                       const uint16_t* __restrict__ B, int r,
+                                                       double* __restrict__ ResT,
+                                                       unsigned* __restrict__ status) {
+  __shared__ double T[64][65];
+  __shared__ double As[64][CH_RMAX + 1];
+  __shared__ double Bs[CH_RMAX][64];
+  const int t = threadIdx.x, tx = t & 63, ty = t >> 6;
+  const int64_t row0 = (int64_t)blockIdx.y * 64, j0 = (int64_t)blockIdx.x * 64;
+  const int64_t j = j0 + tx;
+  for (int e = t; e < 64 * r; e += 256) {
+    const int rr = e / r, k = e - rr * r;
+    As[rr][k] = row0 + rr < o ? f16_to_f64(A[(row0 + rr) * r + k]) : 0.0;
   }
+  for (int e = t; e < 64 * r; e += 256) {
+    const int k = e >> 6, c = e & 63;
+    Bs[k][c] = j0 + c < i ? f16_to_f64(B[(int64_t)k * i + j0 + c]) : 0.0;
+  }
+  double wv[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int64_t row = row0 + ty + 4 * m;
+    wv[m] = (row < o && j < i) ? f16_to_f64(W[row * ldw + j]) : 0.0;
+  }
+  __syncthreads();
+  bool bad = false;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int rr = ty + 4 * m;
+    double acc = 0.0;
+    for (int k = 0; k < r; ++k) acc = fma(As[rr][k], Bs[k][tx], acc);
+    const double v = wv[m] - acc;
+    if (row0 + rr < o && j < i) bad |= !isfinite(v);
+    T[rr][tx] = v;
+  }
+  if (bad) atomicOr(status, ST_NONFINITE);
+  __syncthreads();
+  const int64_t row = row0 + tx;
+  for (int jj = ty; jj < 64; jj += 4)
+    if (row < o && j0 + jj < i) ResT[(j0 + jj) * o + row] = T[tx][jj];
 }
 
 // Lazy update of the block [j0, j0 + bw) (sweep order) over the errors of
 // columns [k_lo, k_hi), k_lo = blockIdx.y * ks, k_hi <= j0:
-//   part[y][row][c] = sum_k E[row][k] U[k][j0 + c]    (c < 128; 0 beyond bw)
-// A workgroup forms 64 rows x 128 columns, thread (ty, tx) the rows 4 ty..4 ty+3
-// and the columns tx + 16 b, through 16-deep LDS stages of E and U.
-__global__ __launch_bounds__(256) void ch_update_kernel(const double* __restrict__ E,
+//   part[y][c][row] = sum_k ET[k][row] U[k][j0 + c]    (c < 128; 0 beyond bw)
+// (errors and partial sums stored by column, rows contiguous)
+// A workgroup forms 64 rows x 128 columns, thread (tc, tr) = (t / 16, t % 16)
+// the rows tr + 16 b and the columns 8 tc .. 8 tc + 7, through 16-deep LDS
+// stages of E and U; loads and stores run along the rows (16 consecutive
+// rows per column in each wave access).
+__global__ __launch_bounds__(256) void ch_update_kernel(const double* __restrict__ ET,
                                                         const float* __restrict__ U,
                                                         int64_t rows, int64_t cols, int64_t j0,
                                                         int bw, int64_t ks,
@@ -378,23 +413,23 @@ __global__ __launch_bounds__(256) void ch_update_kernel(const double* __restrict
                                                         int64_t pstride) {
   __shared__ double Es[16][64];
   __shared__ float Us[16][CH_QB];
-  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  const int t = threadIdx.x, tr = t & 15, tc = t >> 4;
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int64_t k_lo = (int64_t)blockIdx.y * ks;
   const int64_t k_hi = k_lo + ks < j0 ? k_lo + ks : j0;
-  double acc[4][8];
+  double acc[4][8];  // [row tr + 16 b][column 8 tc + a]
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
+    for (int a = 0; a < 8; ++a) acc[b][a] = 0.0;
   for (int64_t k0 = k_lo; k0 < k_hi; k0 += 16) {
     {
-      const int rr = t >> 2, kk = (t & 3) * 4;
-      const int64_t row = r0 + rr;
+      const int kk = t >> 4;
+      const int64_t k = k0 + kk;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const int64_t k = k0 + kk + x;
-        Es[kk + x][rr] = (row < rows && k < k_hi) ? E[row * cols + k] : 0.0;
+        const int64_t row = r0 + tr + 16 * x;
+        Es[kk][tr + 16 * x] = (row < rows && k < k_hi) ? ET[k * rows + row] : 0.0;
       }
     }
     {
@@ -411,23 +446,47 @@ __global__ __launch_bounds__(256) void ch_update_kernel(const double* __restrict
     for (int kk = 0; kk < 16; ++kk) {
       double e[4], u[8];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) e[a] = Es[kk][ty * 4 + a];
+      for (int b = 0; b < 4; ++b) e[b] = Es[kk][tr + 16 * b];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) u[b] = (double)Us[kk][tx + 16 * b];
+      for (int a = 0; a < 8; ++a) u[a] = (double)Us[kk][8 * tc + a];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = fma(e[a], u[b], acc[a][b]);
+        for (int a = 0; a < 8; ++a) acc[b][a] = fma(e[b], u[a], acc[b][a]);
     }
     __syncthreads();
   }
   double* out = part + (int64_t)blockIdx.y * pstride;
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t row = r0 + ty * 4 + a;
+  for (int b = 0; b < 4; ++b) {
+    const int64_t row = r0 + tr + 16 * b;
     if (row < rows)
 #pragma unroll
-      for (int b = 0; b < 8; ++b) out[row * CH_QB + tx + 16 * b] = acc[a][b];
+      for (int a = 0; a < 8; ++a) out[(int64_t)(8 * tc + a) * rows + row] = acc[b][a];
+  }
+}
+
+// The block's current values for the sweep, by block column:
+//   cur[c][row] = ResT[perm[j0 + c]][row] - sum_q part[q][c][row]
+// (the update pieces summed in piece order; 0 for c >= bw).
+__global__ void ch_cur_kernel(const double* __restrict__ part, int np, int64_t pstride,
+                              const double* __restrict__ ResT, int64_t rows, int64_t cols,
+                              const int32_t* __restrict__ perm, int64_t j0, int bw,
+                              double* __restrict__ cur) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < pstride;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int c = (int)(e / rows);
+    const int64_t row = e - (int64_t)c * rows;
+    double v = 0.0;
+    if (c < bw) {
+      int64_t oc = perm ? (int64_t)perm[j0 + c] : j0 + c;
+      if (oc < 0 || oc >= cols) oc = 0;  // reported as ST_BADPERM before the sweep
+      double sum = 0.0;
+#pragma unroll 8
+      for (int q = 0; q < np; ++q) sum += part[(int64_t)q * pstride + e];
+      v = ResT[oc * rows + row] - sum;
+    }
+    cur[e] = v;
   }
 }
 
@@ -443,109 +502,219 @@ __device__ inline uint16_t f16_bits_of_exact(double x) {
 }
 
 // The sweep of the block [j0, j0 + bw) with one grid per group of G output
-// channels (rows) and column: one workgroup of 8 G / RP threads per group;
-// thread (row set lr = t / 8, slice cs = t % 8) holds the columns 8 s + cs
-// (s < 16) of its RP rows lr RP .. lr RP + RP - 1, starting from
-// Res[row][perm[j]] minus the np update sums. For column jj = 8 s + c
-// the owners are the lanes with cs = c: each wave reduces its rows' range
-// with lane shuffles and one barrier joins the wave ranges; every owner
-// quantizes its own rows, and their scaled errors reach the other slices of
-// the rows by a shuffle among the 8 lanes, which subtract error * U[jj][col]
-// from their later columns. The grid arithmetic is the same in every wave,
-// so fewer, fuller waves (RP rows per lane) issue less of it; the step and
-// U[jj][jj] enter as reciprocals (one division per column each, the latter
-// off the row chain), as in the GPTQ sweep. Codes, errors
-// and grids stay in registers until the block is done; codes and grids go
-// to the original column perm[j], the errors to E in sweep order, the
-// squared errors to row_loss (set on the first block).
-template <int G, int RP>
-__global__ __launch_bounds__(8 * G / RP) void ch_sweep_kernel(
-    const double* __restrict__ Res, int64_t rows, int64_t cols, int64_t j0, int bw,
-    const double* __restrict__ part, int np, int64_t pstride, const float* __restrict__ U,
-    const int32_t* __restrict__ perm, int bits, double* __restrict__ E,
+// channels (rows) and column, starting from the residual ResT[perm[j]][row]
+// (first block) or from cur, the residual less the update sum of the
+// earlier blocks (by block column, from ch_cur_kernel); codes and grids go to the
+// original column perm[j], the scaled errors to ET[j][row] (sweep order,
+// by column like the residual and the update sums), the squared errors
+// to row_loss (set on the first block). The step and U[j][j] enter as
+// reciprocals, as in the GPTQ sweep.
+//
+// One workgroup of four waves per group of G rows (lane l: rows l + 64 p,
+// p < RP; for G = 32 the upper half of the wave holds zeros, which the range
+// contains anyway), the block's columns in four stripes of 32 (wave w:
+// columns 32 w .. 32 w + 31, in registers). The block is swept in sub-blocks
+// of 16 columns, each by the wave that holds it, in a loop that is not
+// unrolled: the column under way is always register 0 of the sub-block, and
+// the update of the later columns moves each one register down (an fma into
+// the next lower register), so the loop body is the same for every column.
+// A single wave runs the column chain, so its time is about the count of
+// instructions issued per column: the group's range is one reduction over
+// the wave in DPP moves (no LDS), every lane quantizes its own rows, and
+// codes, errors and grids go to LDS as they are (conversions and global
+// stores wait for the end of the block). The sub-block's errors then reach
+// the later columns: the other waves apply them while the next sub-block is
+// swept, one barrier per sub-block (two error buffers). The U slab stays
+// fp32 in LDS, as stored. Errors go to ET from LDS one sub-block later,
+// codes and grids after the block (without a permutation, four codes of a
+// row per store).
+constexpr int CH_SB = 16;  // columns per sub-block
+
+template <int CTRL, int RM>
+__device__ inline double ch_dpp(double v) {
+  union { double d; int i[2]; } a, b;
+  a.d = v;
+  if constexpr (RM == 0xF) {  // every lane written
+    b.i[0] = __builtin_amdgcn_mov_dpp(a.i[0], CTRL, RM, 0xF, false);
+    b.i[1] = __builtin_amdgcn_mov_dpp(a.i[1], CTRL, RM, 0xF, false);
+  } else {
+    b.i[0] = __builtin_amdgcn_update_dpp(a.i[0], a.i[0], CTRL, RM, 0xF, false);
+    b.i[1] = __builtin_amdgcn_update_dpp(a.i[1], a.i[1], CTRL, RM, 0xF, false);
+  }
+  return b.d;
+}
+__device__ inline double ch_lane63(double v) {
+  union { double d; int i[2]; } a;
+  a.d = v;
+  a.i[0] = __builtin_amdgcn_readlane(a.i[0], 63);
+  a.i[1] = __builtin_amdgcn_readlane(a.i[1], 63);
+  return a.d;
+}
+// min and max over the 64 lanes of the wave, returned uniform: the four
+// 16-lane rows reduce in quad and row rotations, rows 1 and 3 then take
+// the last lane of rows 0 and 2, rows 2 and 3 the last lane of row 1, so
+// that lane 63 holds the whole wave's result (rows left out by a row mask
+// keep their value, which min and max leave unchanged)
+__device__ inline void ch_wave_minmax(double& mn, double& mx) {
+  mn = fmin(mn, ch_dpp<0xB1, 0xF>(mn));  // quad_perm [1,0,3,2]
+  mx = fmax(mx, ch_dpp<0xB1, 0xF>(mx));
+  mn = fmin(mn, ch_dpp<0x4E, 0xF>(mn));  // quad_perm [2,3,0,1]
+  mx = fmax(mx, ch_dpp<0x4E, 0xF>(mx));
+  mn = fmin(mn, ch_dpp<0x124, 0xF>(mn)); // row_ror 4
+  mx = fmax(mx, ch_dpp<0x124, 0xF>(mx));
+  mn = fmin(mn, ch_dpp<0x128, 0xF>(mn)); // row_ror 8
+  mx = fmax(mx, ch_dpp<0x128, 0xF>(mx));
+  mn = fmin(mn, ch_dpp<0x142, 0xA>(mn)); // row_bcast 15 into rows 1, 3
+  mx = fmax(mx, ch_dpp<0x142, 0xA>(mx));
+  mn = fmin(mn, ch_dpp<0x143, 0xC>(mn)); // row_bcast 31 into rows 2, 3
+  mx = fmax(mx, ch_dpp<0x143, 0xC>(mx));
+  mn = ch_lane63(mn);
+  mx = ch_lane63(mx);
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
+    const double* __restrict__ ResT, int64_t rows, int64_t cols, int64_t j0, int bw,
+    const double* __restrict__ cur, const float* __restrict__ U,
+    const int32_t* __restrict__ perm, int bits, double* __restrict__ ET,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
     double* __restrict__ row_loss, unsigned* __restrict__ status) {
-  constexpr int NT = 8 * G / RP, NW = NT / 64;
-  static_assert(NT % 64 == 0, "whole waves");
-  __shared__ float Us[CH_QB][CH_QB + 1];
-  __shared__ double mm[2][2][NW];
-  const int t = threadIdx.x, cs = t & 7, lr = t >> 3, wv = t >> 6, lane = t & 63;
+  constexpr int RP = G >= 64 ? G / 64 : 1;  // rows per lane
+  constexpr int NC = CH_QB / 4;             // columns per wave
+  constexpr int KPT = CH_SB * G / 256;      // errors per thread in the ET copy
+  // the U slab, row-major (fp32 as stored); the shifted update of the last
+  // columns reads up to CH_SB - 1 entries past a row's end (zeros at the end)
+  __shared__ float Us[CH_QB * CH_QB + CH_SB];
+  __shared__ double Es[2][CH_SB][G];  // a sub-block's errors, [column][row]
+  __shared__ double Rd[CH_QB];        // 1 / U[jb][jb]
+  __shared__ uint8_t Ks[CH_QB][G];    // the block's codes, [column][row]
+  __shared__ double Sd[CH_QB], Zd[CH_QB];  // its grids: step, zero point
+  __shared__ int Pm[CH_QB];           // original column of each block column
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t grp = blockIdx.x;
-  const int64_t row0 = grp * G + (int64_t)lr * RP;
   bool rv[RP];
+  int64_t row[RP];
 #pragma unroll
-  for (int p = 0; p < RP; ++p) rv[p] = row0 + p < rows;
+  for (int p = 0; p < RP; ++p) {
+    const int lr = lane + 64 * p;
+    row[p] = grp * G + lr;
+    rv[p] = lr < G && row[p] < rows;
+  }
   const double maxq = (double)((1 << bits) - 1);
   const double rmaxq = 1.0 / maxq;
-  for (int e = t; e < CH_QB * CH_QB; e += NT) {
-    const int a = e >> 7, b = e & 127;
-    Us[a][b] = (a < bw && b < bw) ? U[(j0 + a) * cols + j0 + b] : 0.0f;
-  }
-  double w[RP][16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int col = 8 * s + cs;
+  // every load of the prologue is issued before its first use (each round
+  // trip to memory costs about a microsecond)
+  if (t < CH_QB) {
     int64_t oc = 0;
-    if (col < bw) {
-      oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
+    if (t < bw) {
+      oc = perm ? (int64_t)perm[j0 + t] : j0 + t;
       if (oc < 0 || oc >= cols) oc = 0;  // reported as ST_BADPERM before the sweep
     }
+    Pm[t] = (int)oc;
+    Rd[t] = t < bw ? 1.0 / (double)U[(j0 + t) * cols + j0 + t] : 0.0;
+  }
+  if (t < CH_SB) Us[CH_QB * CH_QB + t] = 0.0f;
+  if (bw == CH_QB && (cols & 3) == 0) {
+    // 16 float4 per thread, row a = e / 32 of the slab
+    float4 v[16];
 #pragma unroll
-    for (int p = 0; p < RP; ++p) {
-      double v = 0.0;
-      if (col < bw && rv[p]) {
-        const int64_t row = row0 + p;
-        v = Res[row * cols + oc];
-        for (int q = 0; q < np; ++q) v -= part[(int64_t)q * pstride + row * CH_QB + col];
+    for (int u = 0; u < 16; ++u) {
+      const int e = t + 256 * u, a = e >> 5, b4 = e & 31;
+      v[u] = *reinterpret_cast<const float4*>(U + (j0 + a) * cols + j0 + 4 * b4);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) reinterpret_cast<float4*>(Us)[t + 256 * u] = v[u];
+  } else {
+#pragma unroll 1
+    for (int e0 = 0; e0 < CH_QB * CH_QB; e0 += 16 * 256) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int e = e0 + t + 256 * u, a = e >> 7, b = e & 127;
+        v[u] = (a < bw && b < bw) ? U[(j0 + a) * cols + j0 + b] : 0.0f;
       }
-      w[p][s] = v;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) Us[e0 + t + 256 * u] = v[u];
     }
   }
-  uint32_t kq[RP][4];                          // codes of the own columns, 8 bits each
-  uint32_t sb[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // their fp16 steps
-  uint32_t zb[4] = {0u, 0u, 0u, 0u};          // their zero points
-  double lsum[RP];
+  __syncthreads();
+  // current values of the wave's 32 columns (zero for rows outside the group)
+  double w[RP][NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int col = NC * wv + c;
+    const double* src = cur ? cur + (int64_t)col * rows : ResT + (int64_t)Pm[col] * rows;
+#pragma unroll
+    for (int p = 0; p < RP; ++p) w[p][c] = (col < bw && rv[p]) ? src[row[p]] : 0.0;
+  }
+  double lsum[RP], loss0[RP];  // this block's squared errors; the earlier blocks'
 #pragma unroll
   for (int p = 0; p < RP; ++p) {
     lsum[p] = 0.0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) kq[p][q] = 0u;
+    loss0[p] = (j0 > 0 && wv == 0 && rv[p]) ? row_loss[row[p]] : 0.0;
   }
-  __syncthreads();
+  bool bad = false;
+
+  // the errors of sub-block sb applied to this wave's columns LO .. HI - 1
+  // (all of them after the sub-block); the U row and the errors of step
+  // k + 1 are read before the products of step k, so no product waits for LDS
+  auto apply = [&](int sb, auto lo_c, auto hi_c) {
+    constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value, NU = HI - LO;
+    const double* es = &Es[sb & 1][0][0];
+    const int kn = min(CH_SB, bw - CH_SB * sb);
+    const float* ub = Us + (CH_SB * sb) * CH_QB + NC * wv + LO;
+    float un[NU];
+    double en[RP];
 #pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    for (int c = 0; c < 8; ++c) {
-      const int jj = 8 * s + c;
-      if (jj >= bw) break;  // uniform
-      const bool own = cs == c;
-      const double rd = 1.0 / (double)Us[jj][jj];  // off the chain: depends on jj only
+    for (int c = 0; c < NU; ++c) un[c] = ub[c];
+#pragma unroll
+    for (int p = 0; p < RP; ++p) en[p] = lane + 64 * p < G ? es[lane + 64 * p] : 0.0;
+#pragma unroll 2
+    for (int k = 0; k < kn; ++k) {
+      float uc[NU];
+      double ev[RP];
+#pragma unroll
+      for (int c = 0; c < NU; ++c) uc[c] = un[c];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) ev[p] = en[p];
+      const int kx = k + 1 < kn ? k + 1 : k;
+#pragma unroll
+      for (int c = 0; c < NU; ++c) un[c] = ub[kx * CH_QB + c];
+#pragma unroll
+      for (int p = 0; p < RP; ++p) en[p] = lane + 64 * p < G ? es[kx * G + lane + 64 * p] : 0.0;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < NU; ++c) {
+        const double u = (double)uc[c];
+#pragma unroll
+        for (int p = 0; p < RP; ++p) w[p][LO + c] = fma(-ev[p], u, w[p][LO + c]);
+      }
+    }
+  };
+
+  // the sweep of sub-block sb by its wave, the registers H .. H + 15
+  auto sweep = [&](int sb, auto half_c) {
+    constexpr int H = decltype(half_c)::value * CH_SB;
+    double* es = &Es[sb & 1][0][0];
+    const int jbeg = CH_SB * sb, jend = min(jbeg + CH_SB, bw);
+    for (int jb = jbeg; jb < jend; ++jb) {
+      // this column's row of U and 1 / U[jb][jb] are read first, so the LDS
+      // latency passes during the range reduction
+      const float* ur = Us + jb * CH_QB + jb + 1;  // columns jb + 1 .. jb + 15
+      float uu[CH_SB - 1];
+#pragma unroll
+      for (int c = 0; c < CH_SB - 1; ++c) uu[c] = ur[c];
+      const double rd = Rd[jb];
+      __builtin_amdgcn_sched_barrier(0);
       double mn = 0.0, mx = 0.0;  // the range includes 0
 #pragma unroll
-      for (int p = 0; p < RP; ++p)
-        if (own && rv[p]) {
-          mn = fmin(mn, w[p][s]);
-          mx = fmax(mx, w[p][s]);
-        }
-#pragma unroll
-      for (int off = 8; off < 64; off <<= 1) {
-        mn = fmin(mn, __shfl_xor(mn, off, 64));
-        mx = fmax(mx, __shfl_xor(mx, off, 64));
+      for (int p = 0; p < RP; ++p) {
+        mn = fmin(mn, w[p][H]);
+        mx = fmax(mx, w[p][H]);
       }
-      const int buf = jj & 1;
-      if (lane == c) {
-        mm[buf][0][wv] = mn;
-        mm[buf][1][wv] = mx;
-      }
-      __syncthreads();
-      mn = mm[buf][0][0];
-      mx = mm[buf][1][0];
-#pragma unroll
-      for (int k = 1; k < NW; ++k) {
-        mn = fmin(mn, mm[buf][0][k]);
-        mx = fmax(mx, mm[buf][1][k]);
-      }
+      ch_wave_minmax(mn, mx);
       double scale = f16_round_f64((mx - mn) * rmaxq), zero = 0.0;
-      if (!(scale <= 65504.0) && t == 0) atomicOr(status, ST_NONFINITE);
+      bad |= !(scale <= 65504.0);
       const bool degen = mx == mn || scale == 0.0;
       if (degen) scale = 1.0;
       const double rs = 1.0 / scale;
@@ -553,64 +722,108 @@ __global__ __launch_bounds__(8 * G / RP) void ch_sweep_kernel(
       double e[RP];
 #pragma unroll
       for (int p = 0; p < RP; ++p) {
-        e[p] = 0.0;
-        if (own) {
-          const double v = w[p][s];
-          const double k = fmin(fmax(rint(v * rs) + zero, 0.0), maxq);
-          if (rv[p]) e[p] = (v - scale * (k - zero)) * rd;
-          kq[p][s >> 2] |= (uint32_t)k << (8 * (s & 3));
-          w[p][s] = e[p];
-          lsum[p] = fma(e[p], e[p], lsum[p]);
+        const double v = w[p][H];
+        const double k = fmin(fmax(rint(v * rs) + zero, 0.0), maxq);
+        e[p] = rv[p] ? (v - scale * (k - zero)) * rd : 0.0;
+        lsum[p] = fma(e[p], e[p], lsum[p]);
+        if (lane + 64 * p < G) {
+          es[(jb - jbeg) * G + lane + 64 * p] = e[p];
+          Ks[jb][lane + 64 * p] = (uint8_t)k;
         }
       }
-      if (own) {
-        sb[s >> 1] |= (uint32_t)f16_bits_of_exact(scale) << (16 * (s & 1));
-        zb[s >> 2] |= (uint32_t)zero << (8 * (s & 3));
+      if (lane == 0) {
+        Sd[jb] = scale;
+        Zd[jb] = zero;
       }
-      const int src = (lane & ~7) | c;
-      double eb[RP];
+      // the sub-block's later columns, each one register down
 #pragma unroll
-      for (int p = 0; p < RP; ++p) eb[p] = __shfl(e[p], src, 64);
-      if (cs > c) {
-        const double u = (double)Us[jj][8 * s + cs];
+      for (int c = 0; c < CH_SB - 1; ++c)
 #pragma unroll
-        for (int p = 0; p < RP; ++p) w[p][s] -= eb[p] * u;
+        for (int p = 0; p < RP; ++p) w[p][H + c] = fma(-e[p], (double)uu[c], w[p][H + c + 1]);
+    }
+  };
+
+  // errors of sub-block sb from LDS to ET (sweep order): thread t takes row
+  // t % G of the columns KPT (t / G) .. KPT (t / G) + KPT - 1
+  auto store_e = [&](int sb) {
+    const int r = t % G, k0 = KPT * (t / G);
+    const int64_t gr = grp * G + r;
+    const int kn = min(CH_SB, bw - CH_SB * sb);
+    if (gr < rows) {
+      const double* es = &Es[sb & 1][0][0];
+      double* dst = ET + (j0 + CH_SB * sb) * rows + gr;
+#pragma unroll
+      for (int k = 0; k < KPT; ++k)
+        if (k0 + k < kn) dst[(k0 + k) * rows] = es[(k0 + k) * G + r];
+    }
+  };
+
+  const int nsb = (bw + CH_SB - 1) / CH_SB;
+  for (int sb = 0; sb < nsb; ++sb) {
+    const int owner = sb >> 1;
+    if (sb > 0) store_e(sb - 1);
+    if (wv == owner) {
+      if (sb & 1) {
+        if (sb > 0) apply(sb - 1, std::integral_constant<int, CH_SB>{},
+                          std::integral_constant<int, NC>{});
+        sweep(sb, std::integral_constant<int, 1>{});
+      } else {
+        if (sb > 0) apply(sb - 1, std::integral_constant<int, 0>{},
+                          std::integral_constant<int, CH_SB>{});
+        sweep(sb, std::integral_constant<int, 0>{});
+        if (sb > 0) apply(sb - 1, std::integral_constant<int, CH_SB>{},
+                          std::integral_constant<int, NC>{});
       }
-#pragma unroll
-      for (int s2 = s + 1; s2 < 16; ++s2) {
-        const double u = (double)Us[jj][8 * s2 + cs];
-#pragma unroll
-        for (int p = 0; p < RP; ++p) w[p][s2] -= eb[p] * u;
+    } else if (sb > 0 && wv > owner) {
+      apply(sb - 1, std::integral_constant<int, 0>{}, std::integral_constant<int, NC>{});
+    }
+    __syncthreads();
+  }
+  store_e(nsb - 1);
+  // codes and grids to the original columns
+  if (!perm && bw == CH_QB && (cols & 3) == 0 && ((uintptr_t)codes & 3) == 0) {
+    // four consecutive columns of a row per store: lane = column quad
+    const int q = t & 31;
+#pragma unroll 4
+    for (int r = t >> 5; r < G; r += 8) {
+      const int64_t gr = grp * G + r;
+      const uint32_t v = (uint32_t)Ks[4 * q][r] | ((uint32_t)Ks[4 * q + 1][r] << 8) |
+                         ((uint32_t)Ks[4 * q + 2][r] << 16) | ((uint32_t)Ks[4 * q + 3][r] << 24);
+      if (gr < rows) *reinterpret_cast<uint32_t*>(codes + gr * cols + j0 + 4 * q) = v;
+    }
+  } else {
+    // lane = block column: without a permutation 64 consecutive bytes of a row
+    const int jb = t & (CH_QB - 1);
+    if (jb < bw) {
+      const int64_t oc = Pm[jb];
+#pragma unroll 4
+      for (int r = t >> 7; r < G; r += 2) {
+        const int64_t gr = grp * G + r;
+        if (gr < rows) codes[gr * cols + oc] = Ks[jb][r];
       }
     }
   }
-#pragma unroll
-  for (int s = 0; s < 16; ++s) {
-    const int col = 8 * s + cs;
-    if (col < bw) {
-      int64_t oc = perm ? (int64_t)perm[j0 + col] : j0 + col;
-      if (oc < 0 || oc >= cols) oc = 0;
-#pragma unroll
-      for (int p = 0; p < RP; ++p)
-        if (rv[p]) {
-          const int64_t row = row0 + p;
-          codes[row * cols + oc] = (uint8_t)(kq[p][s >> 2] >> (8 * (s & 3)));
-          E[row * cols + j0 + col] = w[p][s];
-        }
-      if (lr == 0) {
-        scales[grp * cols + oc] = (uint16_t)(sb[s >> 1] >> (16 * (s & 1)));
-        zeros[grp * cols + oc] = f64_to_f16_rne((double)((zb[s >> 2] >> (8 * (s & 3))) & 0xff));
-      }
-    }
+  if (t < bw) {
+    const int64_t oc = Pm[t];
+    scales[grp * cols + oc] = f16_bits_of_exact(Sd[t]);
+    zeros[grp * cols + oc] = f64_to_f16_rne(Zd[t]);
   }
-  // each row's loss: its 8 slices in a fixed order
+  if (bad && lane == 0) atomicOr(status, ST_NONFINITE);
+  // each row's loss over the block: the four waves' sums (each over the
+  // columns it swept, in column order), added in wave order
+  __syncthreads();  // Es[0] is read by the E copy above
 #pragma unroll
-  for (int p = 0; p < RP; ++p) {
-    double l = lsum[p];
-    l += __shfl_xor(l, 1, 64);
-    l += __shfl_xor(l, 2, 64);
-    l += __shfl_xor(l, 4, 64);
-    if (cs == 0 && rv[p]) row_loss[row0 + p] = (j0 == 0 ? 0.0 : row_loss[row0 + p]) + l;
+  for (int p = 0; p < RP; ++p)
+    if (lane + 64 * p < G) Es[0][wv][lane + 64 * p] = lsum[p];
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int p = 0; p < RP; ++p)
+      if (rv[p]) {
+        const int lr = lane + 64 * p;
+        const double l = ((Es[0][0][lr] + Es[0][1][lr]) + Es[0][2][lr]) + Es[0][3][lr];
+        row_loss[row[p]] = loss0[p] + l;
+      }
   }
 }
 
@@ -783,7 +996,8 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   }
 #undef CH_TRY
   GPTQ_LAUNCH(K_CH_FRONT, st,
-              ch_resid_kernel<<<grid1(o * i), 256, 0, st>>>(W, ldw, o, i, A, B, r, Res, status));
+              ch_resid_kernel<<<dim3((unsigned)cdiv(i, 64), (unsigned)cdiv(o, 64)), 256, 0, st>>>(
+                  W, ldw, o, i, A, B, r, Res, status));
   // U and perm are read from here on: with u_stream, wait for the work
   // enqueued on it before this call (the frontend above does not need U and
   // overlaps with it)
@@ -806,29 +1020,26 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   const unsigned rt = (unsigned)cdiv(o, 64);
   for (int64_t j0 = 0; j0 < i; j0 += CH_QB) {
     const int bw = (int)std::min<int64_t>(CH_QB, i - j0);
-    int np = 0;
-    const double* upd = part;
+    const double* cur = nullptr;  // the block's current values, after the first block
     if (j0 > 0) {
       const int64_t p0 = std::min<int64_t>(L.pmax, cdiv(j0, CH_KS));
       const int64_t ks = round_up(cdiv(j0, p0), 32);
-      np = (int)cdiv(j0, ks);
+      const int np = (int)cdiv(j0, ks);
       dim3 grid(rt, (unsigned)np);
       GPTQ_LAUNCH(K_CH_UPDATE, st,
                   ch_update_kernel<<<grid, 256, 0, st>>>(E, U, o, i, j0, bw, ks, part, L.pstride));
-      // the pieces summed in piece order, all values at once, so that the
-      // sweep reads one update per value
-      if (np > 1) {
-        GPTQ_LAUNCH(K_CH_UPDATE, st,
-                    ch_sum_kernel<<<grid1(L.pstride), 256, 0, st>>>(part, np, L.pstride, psum));
-        upd = psum;
-        np = 1;
-      }
+      // the pieces summed in piece order and taken from the residual, all
+      // values at once, so that the sweep reads one value per entry
+      GPTQ_LAUNCH(K_CH_UPDATE, st,
+                  ch_cur_kernel<<<grid1(L.pstride), 256, 0, st>>>(part, np, L.pstride, Res, o, i,
+                                                                  perm, j0, bw, psum));
+      cur = psum;
     }
 #define CH_SWEEP(GS)                                                                            \
   GPTQ_LAUNCH(K_CH_SWEEP, st,                                                                    \
-              ch_sweep_kernel<GS, CH_RP><<<ngr, 8 * GS / CH_RP, 0, st>>>(Res, o, i, j0, bw, upd, np, L.pstride, \
-                                                         U, perm, bits, E, codes, scales, zeros, \
-                                                         row_loss, status))
+              ch_sweep_rows_kernel<GS><<<ngr, 256, 0, st>>>(Res, o, i, j0, bw, cur, U, perm,      \
+                                                             bits, E, codes, scales, zeros,      \
+                                                             row_loss, status))
     if (group_size == 32) CH_SWEEP(32);
     else if (group_size == 64) CH_SWEEP(64);
     else CH_SWEEP(128);

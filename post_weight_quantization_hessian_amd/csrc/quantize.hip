@@ -325,7 +325,7 @@ __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 // min-max one, zero point 0, no clipping (the caller passes clip = false);
 // the level k goes to ovals (int16 bits) at the original column, and a level
 // beyond the int16 range is reported (ST_NONFINITE).
-template <int GS, int MODE>
+template <int GS, int MODE, int RPL>
 __global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
     const double* __restrict__ part, int P, int64_t part_stride,
@@ -341,10 +341,11 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   // U slab plus three rows of zero padding: the slot reads of a column run up
   // to 112 entries past its row end, into the next row or the padding, only
   // for slots past the block end whose values are never used; rows are read
-  // two columns ahead up to row QB + 1.
+  // two columns ahead up to row QB + 1. With `late`, the sum over the
+  // previous block's errors (16 RPL rows x 128 columns) is left in the front
+  // of this array before the slab is staged.
   __shared__ double Us[QB * QB + 3 * QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
-  __shared__ double lt[16][QB];  // the sum over the previous block's errors (late)
   if ((int)blockIdx.x >= nsweep) {
     // workgroups past the sweep's own (256 threads each): the next block's
     // update GEMM over the errors of the blocks before this one, l < gk_end,
@@ -362,87 +363,23 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int q = lane & 15;
   const int nthr = blockDim.x;
-  const int64_t r = (int64_t)blockIdx.x * (nthr >> 4) + wv * 4 + (lane >> 4);
-  const bool rv = r < rows;
+  // the workgroup's rows: 4 per wave and row slot p (16 lanes each), RPL
+  // slots; local row lr[p] = 4 RPL wv + 4 p + lane / 16
+  const int64_t wg_row0 = (int64_t)blockIdx.x * ((nthr >> 4) * RPL);
+  int lr[RPL];
+  int64_t r[RPL];
+  bool rv[RPL];
+#pragma unroll
+  for (int p = 0; p < RPL; ++p) {
+    lr[p] = 4 * RPL * wv + 4 * p + (lane >> 4);
+    r[p] = wg_row0 + lr[p];
+    rv[p] = r[p] < rows;
+  }
   const double maxq = (double)((1 << bits) - 1);
 
   // All global loads of the prologue are issued before any is waited on:
-  // this row's current values, the U slab (16 float4 per thread for 256
-  // threads), and the diagonal of the slab.
-  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk]. Either
-  // the update GEMM formed them whole (wblk), or it left P split-K partials
-  // of the sum over l < j0 (l < j0 - 128 with `late`), which are added here
-  // in split order, and with `late` (256 threads) the workgroup forms the
-  // sum over the previous block's 128 errors itself, last; the first block
-  // reads the weights directly.
-  //
-  // The late sum, for the workgroup's 16 rows: wave wv takes columns
-  // 32 wv .. 32 wv + 31 as two 16x16 fp32 MFMA tiles over K = 128, summed in
-  // fp32 per 32-wide K chunk and in fp64 across chunks (as the update GEMM
-  // does), and leaves them in lt. v_mfma_f32_16x16x4f32 layout (lane l):
-  // A[m][k]: m = l%16, k = l/16; B[k][n]: n = l%16, k = l/16; D element i:
-  // row 4*(l/16) + i, col l%16.
-  if (late) {
-    const int64_t arow = (int64_t)blockIdx.x * 16 + (lane & 15);
-    const float* ea = E + (arow < rows ? arow : rows - 1) * lde + (j0 - QB) + (lane >> 4);
-    const int n0 = 32 * wv + (lane & 15);
-    const float* ub = U + (j0 - QB + (lane >> 4)) * ldu + j0 + n0;
-    const bool cv0 = n0 < bw, cv1 = n0 + 16 < bw;
-    double dl[2][4] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      float av[8], bv0[8], bv1[8];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int k = 32 * ch + 4 * st;
-        av[st] = ea[k];
-        bv0[st] = cv0 ? ub[(int64_t)k * ldu] : 0.0f;
-        bv1[st] = cv1 ? ub[(int64_t)k * ldu + 16] : 0.0f;
-      }
-      f4 m0 = {0.0f, 0.0f, 0.0f, 0.0f}, m1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv0[st], m0, 0, 0, 0);
-        m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], bv1[st], m1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dl[0][i] += (double)m0[i];
-        dl[1][i] += (double)m1[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lt[4 * (lane >> 4) + i][n0] = dl[0][i];
-      lt[4 * (lane >> 4) + i][n0 + 16] = dl[1][i];
-    }
-  }
-  double w[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int c = 16 * s + q;
-    w[s] = (rv && c < bw) ? (wblk ? wblk[r * QB + c] : f16_to_f64(W[r * ldw + j0 + c])) : 0.0;
-  }
-  double acc[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) acc[s] = 0.0;
-  if (!wblk && P > 0) {
-    const double* pr = part + (rv ? r : 0) * QB + q;
-    for (int p0 = 0; p0 < P; p0 += 4) {
-      double v[4][8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int pu = p0 + u < P ? p0 + u : p0;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) v[u][s] = pr[(int64_t)pu * part_stride + 16 * s];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          if (p0 + u < P) acc[s] += v[u][s];
-    }
-  }
+  // the U slab (16 float4 per thread for 256 threads), this row's current
+  // values, the split-K partials, then the operands of the late sum.
   const bool vec_slab = vecU && bw == QB;
   constexpr int SLAB4 = QB * QB / 4;       // float4s in the slab
   constexpr int PER = SLAB4 / 256;         // per thread with 256 threads
@@ -456,6 +393,103 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
                         : f4{0, 0, 0, 0};
     }
   }
+  // Current values of this row's columns: W - E[:, :j0] U[:j0, blk]. Either
+  // the update GEMM formed them whole (wblk), or it left P split-K partials
+  // of the sum over l < j0 (l < j0 - 128 with `late`), which are added here
+  // in split order, and with `late` (256 threads) the workgroup forms the
+  // sum over the previous block's 128 errors itself, last; the first block
+  // reads the weights directly.
+  double w[RPL][8];
+#pragma unroll
+  for (int p = 0; p < RPL; ++p)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int c = 16 * s + q;
+      w[p][s] = (rv[p] && c < bw)
+                    ? (wblk ? wblk[r[p] * QB + c] : f16_to_f64(W[r[p] * ldw + j0 + c]))
+                    : 0.0;
+    }
+  double acc[RPL][8];
+#pragma unroll
+  for (int p = 0; p < RPL; ++p)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[p][s] = 0.0;
+  if (!wblk && P > 0) {
+    constexpr int PR = RPL == 1 ? 4 : 2;  // partials per round
+#pragma unroll
+    for (int p = 0; p < RPL; ++p) {
+      const double* pr = part + (rv[p] ? r[p] : 0) * QB + q;
+      for (int p0 = 0; p0 < P; p0 += PR) {
+        double v[PR][8];
+#pragma unroll
+        for (int u = 0; u < PR; ++u) {
+          const int pu = p0 + u < P ? p0 + u : p0;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) v[u][s] = pr[(int64_t)pu * part_stride + 16 * s];
+        }
+#pragma unroll
+        for (int u = 0; u < PR; ++u)
+#pragma unroll
+          for (int s = 0; s < 8; ++s)
+            if (p0 + u < P) acc[p][s] += v[u][s];
+      }
+    }
+  }
+  // The late sum, for the workgroup's 16 RPL rows: wave wv takes columns
+  // 32 wv .. 32 wv + 31 as 16x16 fp32 MFMA tiles over K = 128 (all operands
+  // loaded first), summed in fp32 per 32-wide K chunk and in fp64 across
+  // chunks (as the update GEMM does), and leaves them in the front of Us.
+  // v_mfma_f32_16x16x4f32 layout (lane l): A[m][k]: m = l%16, k = l/16;
+  // B[k][n]: n = l%16, k = l/16; D element i: row 4*(l/16) + i, col l%16.
+  double* lt = Us;  // [16 RPL][QB]
+  if (late) {
+    const int n0 = 32 * wv + (lane & 15);
+    const float* ub = U + (j0 - QB + (lane >> 4)) * ldu + j0 + n0;
+    const bool cv0 = n0 < bw, cv1 = n0 + 16 < bw;
+    double dl[RPL][2][4];
+#pragma unroll
+    for (int rt = 0; rt < RPL; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dl[rt][0][i] = dl[rt][1][i] = 0.0;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      float av[RPL][8], bv0[8], bv1[8];
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const int k = 32 * ch + 4 * st;
+        bv0[st] = cv0 ? ub[(int64_t)k * ldu] : 0.0f;
+        bv1[st] = cv1 ? ub[(int64_t)k * ldu + 16] : 0.0f;
+      }
+#pragma unroll
+      for (int rt = 0; rt < RPL; ++rt) {
+        const int64_t arow = wg_row0 + 16 * rt + (lane & 15);
+        const float* ea = E + (arow < rows ? arow : rows - 1) * lde + (j0 - QB) + (lane >> 4);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) av[rt][st] = ea[32 * ch + 4 * st];
+      }
+#pragma unroll
+      for (int rt = 0; rt < RPL; ++rt) {
+        f4 m0 = {0.0f, 0.0f, 0.0f, 0.0f}, m1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          m0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[rt][st], bv0[st], m0, 0, 0, 0);
+          m1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av[rt][st], bv1[st], m1, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dl[rt][0][i] += (double)m0[i];
+          dl[rt][1][i] += (double)m1[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < RPL; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lt[(16 * rt + 4 * (lane >> 4) + i) * QB + n0] = dl[rt][0][i];
+        lt[(16 * rt + 4 * (lane >> 4) + i) * QB + n0 + 16] = dl[rt][1][i];
+      }
+  }
   for (int j = t; j < QB; j += nthr) {
     rdiag[j] = j < bw ? 1.0 / (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
     Us[QB * QB + j] = 0.0;
@@ -463,6 +497,13 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     Us[QB * QB + 2 * QB + j] = 0.0;
   }
   __syncthreads();
+  if (late) {
+#pragma unroll
+    for (int p = 0; p < RPL; ++p)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) acc[p][s] += lt[lr[p] * QB + 16 * s + q];
+    __syncthreads();  // the slab overwrites lt
+  }
   // Row a of the slab is stored divided by U[a][a] (the error broadcast along
   // a row is then the unscaled residual d, and e = d / U[a][a] leaves the
   // dependent chain). Entries on and below the diagonal are zero: a column's
@@ -494,30 +535,35 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       Us[e] = (a < bw && c < bw && c > a) ? (double)U[(j0 + a) * ldu + j0 + c] * rdiag[a] : 0.0;
     }
   }
-  // (lt was written before the first barrier above)
-  if (late) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc[s] += lt[wv * 4 + (lane >> 4)][16 * s + q];
-  }
-#pragma unroll
-  for (int s = 0; s < 8; ++s) w[s] = (rv && 16 * s + q < bw) ? w[s] - acc[s] : 0.0;
   bool finite = true;
 #pragma unroll
-  for (int s = 0; s < 8; ++s) finite = finite && isfinite(w[s]);
+  for (int p = 0; p < RPL; ++p)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] - acc[p][s] : 0.0;
+      finite = finite && isfinite(w[p][s]);
+    }
   if (!finite) atomicOr(status, ST_NONFINITE);
   __syncthreads();
 
-  double scale = 1.0, rscale = 1.0, zero = 0.0, loss = 0.0;
-  double nout = 0.0;  // SSQR: outliers of this lane's columns
+  double scale[RPL], rscale[RPL], zero[RPL], loss[RPL];
+  double nout[RPL];  // SSQR: outliers of this lane's columns
   // range of the level k = code - zero: [-zero, maxq - zero], or unbounded
   // without clipping (the no-clipping regime of The Geometry of LLM
   // Quantization 2.3, whose codes are stored saturated to [0, 255])
-  double klo = -1e300, khi = 1e300;
+  double klo[RPL], khi[RPL];
+#pragma unroll
+  for (int p = 0; p < RPL; ++p) {
+    scale[p] = rscale[p] = 1.0;
+    zero[p] = loss[p] = nout[p] = 0.0;
+    klo[p] = -1e300;
+    khi[p] = 1e300;
+  }
   const int nt16 = (bw + 15) >> 4;
   // U row of column jc as seen from the slots (slot s holds column
   // 16*((jc >> 4) + s) + q; slots past the block end are dead and read into
   // the next row or the padding). Loaded two columns ahead into four
-  // rotating register sets (set = column & 3).
+  // rotating register sets (set = column & 3); shared by the RPL rows.
   double ub[4][8];
   auto load_row = [&](int jc, double (&uu)[8]) {
     const double* urow = Us + jc * QB + 16 * (jc >> 4) + q;
@@ -530,46 +576,52 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     const double* ubase = Us + 16 * tt * QB + 16 * tt + q;
     if (((16 * tt) % GS) == 0) {
       // grid of the group starting here, from the current values
-      double mn = 0.0, mx = 0.0;
 #pragma unroll
-      for (int s = 0; s < GS / 16; ++s) {
-        if (16 * (tt + s) + q < bw) {
-          mn = fmin(mn, w[s]);
-          mx = fmax(mx, w[s]);
+      for (int p = 0; p < RPL; ++p) {
+        double mn = 0.0, mx = 0.0;
+#pragma unroll
+        for (int s = 0; s < GS / 16; ++s) {
+          if (16 * (tt + s) + q < bw) {
+            mn = fmin(mn, w[p][s]);
+            mx = fmax(mx, w[p][s]);
+          }
         }
-      }
-      mn = fmin(mn, quad_xor1(mn));
-      mx = fmax(mx, quad_xor1(mx));
-      mn = fmin(mn, quad_xor2(mn));
-      mx = fmax(mx, quad_xor2(mx));
-      mn = fmin(mn, row_ror4(mn));
-      mx = fmax(mx, row_ror4(mx));
-      mn = fmin(mn, row_ror8(mn));
-      mx = fmax(mx, row_ror8(mx));
-      uint16_t sh = f64_to_f16_rne((mx - mn) / maxq);
-      scale = f16_to_f64(sh);
-      if ((sh & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
-      // SSQR: the step used is fp16(alpha * step); the zero point comes from
-      // the unscaled one (scale, here), so the grid shrinks about 0
-      const uint16_t sha = (SSQR || HPTQ) ? f64_to_f16_rne(alpha * ((mx - mn) / maxq)) : sh;
-      const double scale_a = (SSQR || HPTQ) ? f16_to_f64(sha) : scale;
-      if ((sha & 0x7fff) >= 0x7c00 && rv) atomicOr(status, ST_NONFINITE);
-      if (mx == mn || (!HPTQ && scale == 0.0) || scale_a == 0.0) {
-        scale = 1.0;
-        sh = 0x3c00;
-        zero = 0.0;
-      } else {
-        zero = HPTQ ? 0.0 : fmin(fmax(rint(-mn / scale), 0.0), maxq);
-        scale = scale_a;
-        sh = sha;
-      }
-      rscale = 1.0 / scale;
-      klo = clip ? -zero : -1e300;
-      khi = clip ? maxq - zero : 1e300;
-      if (rv && q == 0) {
-        const int64_t g = (j0 + 16 * tt) / GS;
-        scales[r * ldg + g] = sh;
-        zeros[r * ldg + g] = f64_to_f16_rne(zero);
+        mn = fmin(mn, quad_xor1(mn));
+        mx = fmax(mx, quad_xor1(mx));
+        mn = fmin(mn, quad_xor2(mn));
+        mx = fmax(mx, quad_xor2(mx));
+        mn = fmin(mn, row_ror4(mn));
+        mx = fmax(mx, row_ror4(mx));
+        mn = fmin(mn, row_ror8(mn));
+        mx = fmax(mx, row_ror8(mx));
+        uint16_t sh = f64_to_f16_rne((mx - mn) / maxq);
+        double sc = f16_to_f64(sh);
+        if ((sh & 0x7fff) >= 0x7c00 && rv[p]) atomicOr(status, ST_NONFINITE);
+        // SSQR: the step used is fp16(alpha * step); the zero point comes
+        // from the unscaled one (sc, here), so the grid shrinks about 0
+        const uint16_t sha = (SSQR || HPTQ) ? f64_to_f16_rne(alpha * ((mx - mn) / maxq)) : sh;
+        const double scale_a = (SSQR || HPTQ) ? f16_to_f64(sha) : sc;
+        if ((sha & 0x7fff) >= 0x7c00 && rv[p]) atomicOr(status, ST_NONFINITE);
+        double z;
+        if (mx == mn || (!HPTQ && sc == 0.0) || scale_a == 0.0) {
+          sc = 1.0;
+          sh = 0x3c00;
+          z = 0.0;
+        } else {
+          z = HPTQ ? 0.0 : fmin(fmax(rint(-mn / sc), 0.0), maxq);
+          sc = scale_a;
+          sh = sha;
+        }
+        scale[p] = sc;
+        zero[p] = z;
+        rscale[p] = 1.0 / sc;
+        klo[p] = clip ? -z : -1e300;
+        khi[p] = clip ? maxq - z : 1e300;
+        if (rv[p] && q == 0) {
+          const int64_t g = (j0 + 16 * tt) / GS;
+          scales[r[p] * ldg + g] = sh;
+          zeros[r[p] * ldg + g] = f64_to_f16_rne(z);
+        }
       }
     }
     // The 16 columns of the tile. Slot s of lane q holds column
@@ -577,7 +629,8 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     // (NS live slots), and only those are loaded and updated. Every lane
     // rounds its slot 0 each column, the owner's (lane jj's) residual is
     // broadcast to its row, and later columns take the update; the owner's
-    // own slot is left as it was (zero diagonal of the slab).
+    // own slot is left as it was (zero diagonal of the slab). The RPL rows'
+    // chains are independent and interleave.
     auto tile = [&](auto ns_c, auto full_c) {
       constexpr int NS = decltype(ns_c)::value;
       constexpr bool FULL = decltype(full_c)::value;
@@ -594,17 +647,23 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
 #pragma unroll
             for (int s = 0; s < NS; ++s) ub[(jj + 2) & 3][s] = urow[16 * s];
           }
-          // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
-          // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
-          const double v = w[0];
-          const double kr = rint(v * rscale);
-          double d = fma(-scale, fmin(fmax(kr, klo), khi), v);
-          if (SSQR && (kr < klo || kr > khi)) d = v - f16_round_f64(v);
-          const double db = row_bcast_mov_i(d, jj);
+          double db[RPL];
+#pragma unroll
+          for (int p = 0; p < RPL; ++p) {
+            // code = clamp(rint(v/s) + z, 0, maxq) = k + z with
+            // k = clamp(rint(v/s), -z, maxq - z), dequantized s * k
+            const double v = w[p][0];
+            const double kr = rint(v * rscale[p]);
+            double d = fma(-scale[p], fmin(fmax(kr, klo[p]), khi[p]), v);
+            if (SSQR && (kr < klo[p] || kr > khi[p])) d = v - f16_round_f64(v);
+            db[p] = row_bcast_mov_i(d, jj);
+          }
           // later columns: w -= d * U[j][c] / U[j][j] (zero for this column
           // and the ones before it)
 #pragma unroll
-          for (int s = 0; s < NS; ++s) w[s] = fma(-db, u[s], w[s]);
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int p = 0; p < RPL; ++p) w[p][s] = fma(-db[p], u[s], w[p][s]);
         }
       }
     };
@@ -626,49 +685,60 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     // 0 still holds the value the lane's column was quantized from
     {
       const int c = 16 * tt + q;
-      if (rv && c < bw) {
-        const double v = w[0];
-        const double kr = rint(v * rscale);
-        const double k_own = fmin(fmax(kr, klo), khi);
-        double d_own = fma(-scale, k_own, v);
-        const bool o_own = SSQR && (kr < klo || kr > khi);
-        const double h_own = SSQR ? f16_round_f64(v) : 0.0;
-        if (o_own) d_own = v - h_own;
-        const double e = d_own * rdiag[c];
-        codes[r * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero, 0.0), 255.0);
-        E[r * lde + j0 + c] = (float)e;
-        loss += e * e;
-        if (SSQR || HPTQ) {
-          const int64_t oc = operm ? (int64_t)operm[j0 + c] : j0 + c;
-          if (oc >= 0 && oc < cols) {  // a bad permutation is reported elsewhere
-            if (SSQR) {
-              omask[r * cols + oc] = o_own ? 1 : 0;
-              ovals[r * cols + oc] = o_own ? f64_to_f16_rne(h_own) : (uint16_t)0;
-            } else {
-              const double kc = fmin(fmax(k_own, -32768.0), 32767.0);
-              if (kc != k_own) atomicOr(status, ST_NONFINITE);
-              ovals[r * cols + oc] = (uint16_t)(int16_t)kc;
+#pragma unroll
+      for (int p = 0; p < RPL; ++p) {
+        if (rv[p] && c < bw) {
+          const double v = w[p][0];
+          const double kr = rint(v * rscale[p]);
+          const double k_own = fmin(fmax(kr, klo[p]), khi[p]);
+          double d_own = fma(-scale[p], k_own, v);
+          const bool o_own = SSQR && (kr < klo[p] || kr > khi[p]);
+          const double h_own = SSQR ? f16_round_f64(v) : 0.0;
+          if (o_own) d_own = v - h_own;
+          const double e = d_own * rdiag[c];
+          codes[r[p] * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero[p], 0.0), 255.0);
+          E[r[p] * lde + j0 + c] = (float)e;
+          loss[p] += e * e;
+          if (SSQR || HPTQ) {
+            const int64_t oc = operm ? (int64_t)operm[j0 + c] : j0 + c;
+            if (oc >= 0 && oc < cols) {  // a bad permutation is reported elsewhere
+              if (SSQR) {
+                omask[r[p] * cols + oc] = o_own ? 1 : 0;
+                ovals[r[p] * cols + oc] = o_own ? f64_to_f16_rne(h_own) : (uint16_t)0;
+              } else {
+                const double kc = fmin(fmax(k_own, -32768.0), 32767.0);
+                if (kc != k_own) atomicOr(status, ST_NONFINITE);
+                ovals[r[p] * cols + oc] = (uint16_t)(int16_t)kc;
+              }
             }
+            if (SSQR) nout[p] += o_own ? 1.0 : 0.0;
           }
-          if (SSQR) nout += o_own ? 1.0 : 0.0;
         }
       }
     }
 #pragma unroll
-    for (int s = 0; s < 7; ++s) w[s] = w[s + 1];
-    w[7] = 0.0;
+    for (int p = 0; p < RPL; ++p) {
+#pragma unroll
+      for (int s = 0; s < 7; ++s) w[p][s] = w[p][s + 1];
+      w[p][7] = 0.0;
+    }
   }
-  loss += quad_xor1(loss);
-  loss += quad_xor2(loss);
-  loss += row_ror4(loss);
-  loss += row_ror8(loss);
-  if (rv && q == 0) row_loss[r] += loss;
-  if (SSQR) {
-    nout += quad_xor1(nout);
-    nout += quad_xor2(nout);
-    nout += row_ror4(nout);
-    nout += row_ror8(nout);
-    if (rv && q == 0 && nout > 0.0) atomicAdd(ocount, (unsigned long long)nout);
+#pragma unroll
+  for (int p = 0; p < RPL; ++p) {
+    double l = loss[p];
+    l += quad_xor1(l);
+    l += quad_xor2(l);
+    l += row_ror4(l);
+    l += row_ror8(l);
+    if (rv[p] && q == 0) row_loss[r[p]] += l;
+    if (SSQR) {
+      double no = nout[p];
+      no += quad_xor1(no);
+      no += quad_xor2(no);
+      no += row_ror4(no);
+      no += row_ror8(no);
+      if (rv[p] && q == 0 && no > 0.0) atomicAdd(ocount, (unsigned long long)no);
+    }
   }
 }
 
@@ -721,7 +791,7 @@ static QLayout q_layout(int64_t rows, int64_t cols, int gs) {
 // errors themselves), then ng workgroups (nw == 4 only) of the next block's
 // early update GEMM.
 struct SweepArgs {
-  int nw, nsweep, ng;
+  int nw, rpl, nsweep, ng;
   const uint16_t* W;
   int64_t ldw;
   const double* wblk;
@@ -759,16 +829,20 @@ struct SweepArgs {
 
 template <int GS>
 static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
-#define Q_SWEEP(SS)                                                                            \
+#define Q_SWEEP(SS, RP)                                                                        \
   GPTQ_LAUNCH(K_Q_SWEEP, st,                                                                   \
-              (q_sweep_kernel<GS, SS><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(                  \
+              (q_sweep_kernel<GS, SS, RP><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(              \
                   a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0, \
                   a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg,          \
                   a.row_loss, a.status, a.clip, a.late, a.nsweep, a.gj0, a.gbw, a.gks,         \
                   a.gk_end, a.gpart, a.alpha, a.omask, a.ovals, a.operm, a.cols, a.ocount)))
-  if (a.mode == 1) Q_SWEEP(1);
-  else if (a.mode == 2) Q_SWEEP(2);
-  else Q_SWEEP(0);
+  if (a.rpl == 2) {  // the plain sweep only (the SSQR/HPTQ state of two rows spills)
+    Q_SWEEP(0, 2);
+  } else {
+    if (a.mode == 1) Q_SWEEP(1, 1);
+    else if (a.mode == 2) Q_SWEEP(2, 1);
+    else Q_SWEEP(0, 1);
+  }
 #undef Q_SWEEP
   return GPTQ_OK;
 }
@@ -823,10 +897,17 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
     ldws = cols;
     csw = codes_s;
   }
-  // 4 rows per wave; 8 waves per workgroup once that still gives >= 256
-  // workgroups, else 4 (the U slab fills most of the LDS: one workgroup per CU)
+  // 4 rows per wave and row slot; 8 waves per workgroup once that still
+  // gives >= 256 workgroups, else 4 (the U slab fills most of the LDS: one
+  // workgroup per CU). Two row slots per lane group (their dependent chains
+  // interleave) when one slot would need more than one round of workgroups:
+  // 9728 rows, 45.5 -> 36.8 us per launch. (With 4 waves, where the launch
+  // also carries the early update GEMM, two slots measured 35 % slower: the
+  // split-K partials are loaded per row. The SSQR and HPTQ state of two rows
+  // does not fit the registers.)
   const int nw = cdiv(rows, 32) >= 256 ? 8 : 4;
-  const int nsweep = (int)cdiv(rows, 4 * nw);
+  const int rpl = (mode == 0 && nw == 8 && cdiv(rows, 32) > 256) ? 2 : 1;
+  const int nsweep = (int)cdiv(rows, 4 * nw * rpl);
   const bool vecU = (cols % 4 == 0) && ((uintptr_t)U % 16 == 0);
   const int64_t rt = cdiv(rows, 64);
   double* wblk = (double*)(base + L.off_wblk);
@@ -866,7 +947,7 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
         else nparts = P;
       }
     }
-    SweepArgs a{nw, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
+    SweepArgs a{nw, rpl, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
                 bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, clip,
                 late, 0, 0, 0, 0, pn, mode, alpha, omask, ovals, perm, cols, ocount};
     ep = emb_max > 0 ? 0 : -1;
