@@ -129,8 +129,9 @@ __host__ __device__ inline int64_t round_up(int64_t a, int64_t b) { return cdiv(
 
 // Workgroup id remapped so that consecutive logical ids land on the same XCD
 // (hardware dispatches workgroup ids round-robin over the 8 XCDs).
-// DPP moves of an fp64 value (two 32-bit halves). Every pattern used writes
-// every lane, so the "old" operand is the source itself.
+// DPP moves of an fp64 value (two 32-bit halves: the quad and row patterns
+// exist for 32-bit moves only). Every pattern used writes every lane, so the
+// "old" operand is the source itself.
 template <int CTRL>
 __device__ inline double dpp_f64(double v) {
   union { double d; int i[2]; } a, b;
@@ -139,20 +140,19 @@ __device__ inline double dpp_f64(double v) {
   b.i[1] = __builtin_amdgcn_update_dpp(a.i[1], a.i[1], CTRL, 0xF, 0xF, false);
   return b.d;
 }
-// row_newbcast: lane N of each 16-lane row, to the whole row
+// row_newbcast: lane N of each 16-lane row, to the whole row. It is the one
+// DPP pattern that also exists for 64-bit moves, so this is a single
+// v_mov_b64_dpp rather than a move of each 32-bit half.
 template <int N>
-__device__ inline double row_bcast(double v) { return dpp_f64<0x150 + N>(v); }
+__device__ inline double row_bcast(double v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + N, 0xF, 0xF, false);
+}
 // row_newbcast whose result also depends on `dep` (it is the "old" operand,
 // which a full-mask broadcast never uses): keeps the compiler from hoisting
 // the broadcast above the computation of dep
 template <int N>
 __device__ inline double row_bcast_dep(double v, double dep) {
-  union { double d; int i[2]; } a, b, o;
-  a.d = v;
-  o.d = dep;
-  b.i[0] = __builtin_amdgcn_update_dpp(o.i[0], a.i[0], 0x150 + N, 0xF, 0xF, false);
-  b.i[1] = __builtin_amdgcn_update_dpp(o.i[1], a.i[1], 0x150 + N, 0xF, 0xF, false);
-  return b.d;
+  return __builtin_amdgcn_update_dpp(dep, v, 0x150 + N, 0xF, 0xF, false);
 }
 __device__ inline double row_bcast_dep_i(double v, double dep, int n) {
   switch (n) {

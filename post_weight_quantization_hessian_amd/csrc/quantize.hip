@@ -287,11 +287,7 @@ __device__ inline double row_ror4(double v) { return dpp_f64<0x124>(v); }
 // row_newbcast of lane N as a plain DPP move (no "old" operand to keep)
 template <int N>
 __device__ inline double row_bcast_mov(double v) {
-  union { double d; int i[2]; } a, b;
-  a.d = v;
-  b.i[0] = __builtin_amdgcn_mov_dpp(a.i[0], 0x150 + N, 0xF, 0xF, false);
-  b.i[1] = __builtin_amdgcn_mov_dpp(a.i[1], 0x150 + N, 0xF, 0xF, false);
-  return b.d;
+  return row_bcast<N>(v);
 }
 // the same for a lane index that is a constant after loop unrolling
 __device__ inline double row_bcast_mov_i(double v, int n) {
