@@ -257,7 +257,12 @@ KERNEL_CLASS = {  # device function name -> timing class
     "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update",
     "h8_tile_kernel": "hessian_split8", "h8_colmax_kernel": "hessian_digits",
     "h8_split_kernel": "hessian_digits", "q_hist_kernel": "quant_hist",
-    "ch_update_kernel": "chmc_update", "ch_sweep_kernel": "chmc_sweep",
+    "ch_update_kernel": "chmc_update", "ch_cur_kernel": "chmc_update",
+    "ch_sweep_rows_kernel": "chmc_sweep", "ch_rowdot_kernel": "chmc_front",
+    "hf_hist_kernel": "hptq_code", "hf_rowbits_kernel": "hptq_code",
+    "hf_scan_kernel": "hptq_code", "hf_encode_kernel": "hptq_code",
+    "hf_decode_kernel": "hptq_code", "hf_zero_kernel": "hptq_code",
+    "sp_count_kernel": "ssqr_csr", "sp_scan_kernel": "ssqr_csr", "sp_fill_kernel": "ssqr_csr",
     "ch_gemm_nn": "chmc_front", "ch_gemm_tn": "chmc_front", "ch_sum_kernel": "chmc_front",
     "ch_chol_inv_kernel": "chmc_front", "ch_jacobi_kernel": "chmc_front",
     "ch_energy_kernel": "chmc_front", "ch_scale_kernel": "chmc_front",
