@@ -271,14 +271,25 @@ KERNEL_CLASS = {  # device function name -> timing class
     "ch_zero_kernel": "fill"}
 
 
-def source_hash():
-    """sha256 over the HIP sources: counters taken on other sources are stale."""
+def _code_only(text):
+    """The source without its comments and blank-line differences (a comment
+    edit does not change a kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
+def source_hash(csrc=None):
+    """sha256 over the HIP sources' code: counters taken on other code are
+    stale."""
     import hashlib
+    csrc = csrc or CSRC
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
+    for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 

@@ -9,10 +9,12 @@
 // (E = the scaled errors of all earlier columns), the same sums as the
 // right-looking update, formed once per block by an fp32-MFMA GEMM whose
 // K-chunks are accumulated in fp64. Inside the block the sweep runs in fp64
-// registers: 4 lanes per row, lane q of a quad owns columns q, q+4, q+8, ...;
-// the register window shifts by one slot every 4 columns so the live column
-// is always slot 0, and the scaled error of the live column is broadcast to
-// the quad with a DPP quad permute. Group min/max reductions also use DPP.
+// registers: 16 lanes (one DPP row) per row, lane q owning the columns q,
+// q + 16, ..., q + 112 (8 slots); the register window shifts by one slot
+// every 16 columns so the live column is always slot 0 of lane j % 16, whose
+// residual is broadcast to its row with row_newbcast (one 64-bit DPP move).
+// Group min/max and the loss are reduced over the row with quad permutes and
+// row rotations.
 #include <type_traits>
 
 #include "common.h"
