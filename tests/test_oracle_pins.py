@@ -496,6 +496,45 @@ def test_ssqr_alpha_one_rows_without_outliers_equal_gptq():
         assert np.array_equal(a[key][clean], b[key][clean]), key
 
 
+def test_ssqr_outliers_nested_and_zero_fixed_in_alpha():
+    """The reading's grid shrinks about 0 as alpha falls, with the zero point
+    of the unscaled grid: on a diagonal H (values do not move) every outlier
+    at a larger alpha is still one at a smaller alpha, and the stored zero
+    points do not depend on alpha. A factor applied the wrong way round, or
+    a zero point taken from the scaled step, fails one of the two."""
+    rng = np.random.default_rng(21)
+    W = (0.02 * rng.standard_t(4, size=(6, 192))).astype(np.float16)
+    S = np.diag(rng.uniform(0.5, 2.0, 192)) * 100
+    prev = None
+    zeros = None
+    for alpha in (1.0, 0.8, 0.55, 0.3, 0.15):
+        res = O.gptq_layer(W, S, 100, bits=3, group_size=64, ssqr_alpha=alpha)
+        out = res["outlier"]
+        if prev is not None:
+            assert np.all(out[prev]), alpha
+            assert out.sum() > prev.sum(), alpha
+        if zeros is None:
+            zeros = res["zeros"].copy()
+        assert np.array_equal(res["zeros"], zeros), alpha
+        prev = out
+
+
+def test_hptq_unbounded_grid_error_bound():
+    """One unbounded grid: on a diagonal H every weight is within half a step
+    of its dequantized value (no clamp ever adds error), also at alpha < 1
+    where levels leave [0, maxq]; a clamp anywhere would break the bound."""
+    rng = np.random.default_rng(22)
+    W = (0.02 * rng.standard_t(4, size=(5, 192))).astype(np.float16)
+    S = np.diag(rng.uniform(0.5, 2.0, 192)) * 100
+    Wd = W.astype(np.float64)
+    for alpha in (1.0, 0.5, 0.2):
+        res = O.gptq_layer(W, S, 100, bits=3, group_size=64, hptq_alpha=alpha)
+        step = np.repeat(res["scales"], 64, axis=1)
+        assert np.all(np.abs(Wd - res["deq"]) <= 0.5 * step + 1e-300), alpha
+        if alpha < 1.0:
+            assert res["codes"].max() > 7 or res["codes"].min() < 0, alpha
+
+
 def test_ssqr_search_bisection():
     """The returned alpha meets the target; the probes keep the bisection
     invariant (every failing probe below every passing one is not required,
