@@ -64,6 +64,11 @@ Readings of what the pages leave open (each listed in the design doc):
   group step) / weights (a single distinct level costs 1 bit per weight); the
   search bisects alpha for the smallest value meeting a bits-per-weight
   budget.
+* SSQR's and HPTQ's exact grid rules (the alpha factor on the fp16-rounded
+  min-max step) are readings of pages that print no rule: their tests pin
+  what the readings claim (alpha = 1 is the plain grid, the all-outlier
+  limit, nested outliers with a zero point fixed in alpha, one unbounded
+  grid); the rules beyond that are parity unpinned.
 * CHMC frontend ([CHMC] Schritt 1-3): c_j = (1/n) sum_t x_tj^2 plus 0.05 *
   mean(c); W~ = W diag(sqrt c); a rank-r approximation of W~ by randomized
   subspace iteration (Halko, Martinsson, Tropp 2011, Algorithm 4.4) with q = r
