@@ -254,7 +254,8 @@ KERNEL_CLASS = {  # device function name -> timing class
     "q_sweep_kernel": "quant_sweep",
     "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout",
     "prep_uout_z_kernel": "prepare_uout", "mp_init_kernel": "minpivot_step",
-    "mp_step_kernel": "minpivot_step", "mp_update_kernel": "minpivot_update",
+    "mp_step_kernel": "minpivot_step", "mp_panel_kernel": "minpivot_step",
+    "mp_update_kernel": "minpivot_update",
     "h8_tile_kernel": "hessian_split8", "h8_colmax_kernel": "hessian_digits",
     "h8_split_kernel": "hessian_digits", "q_hist_kernel": "quant_hist",
     "ch_update_kernel": "chmc_update", "ch_cur_kernel": "chmc_update",

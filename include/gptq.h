@@ -128,6 +128,11 @@ gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
  * returns GPTQ_ENOTSPD if a pivot is <= 0 or not finite (U is then garbage).
  * With GPTQ_FLAG_NO_SYNC it returns after enqueueing (argument errors are
  * still returned at once) and the status is read by gptq_workspace_status.
+ * The min-pivot search of up to 8192 features runs as one cooperative launch
+ * per 128 pivots whose workgroups wait for each other with bounded waits: if
+ * one of them waits for about a second (the device held by other work), the
+ * call reports GPTQ_ENOTSPD as well. Where a cooperative launch of that size
+ * is not possible, and above 8192 features, it runs as one launch per pivot.
  * ------------------------------------------------------------------------- */
 size_t gptq_prepare_workspace_bytes(int64_t in_features);
 gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_tokens_total,

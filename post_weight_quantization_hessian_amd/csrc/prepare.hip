@@ -954,6 +954,7 @@ __device__ inline MinIdx mp_wave_min(double v, int i) {
 }
 
 // Minimum over the block of (v, i) (256 threads); result in every thread.
+template <int NW = 4>
 __device__ inline MinIdx mp_block_min(double v, int i, double* sv, int* si) {
   const MinIdx m = mp_wave_min(v, i);
   const int t = threadIdx.x;
@@ -964,7 +965,7 @@ __device__ inline MinIdx mp_block_min(double v, int i, double* sv, int* si) {
   __syncthreads();
   MinIdx r{sv[0], si[0]};
 #pragma unroll
-  for (int w = 1; w < 4; ++w)
+  for (int w = 1; w < NW; ++w)
     if (mp_before(sv[w], si[w], r.v, r.i)) r = MinIdx{sv[w], si[w]};
   return r;
 }
@@ -1071,6 +1072,253 @@ __global__ __launch_bounds__(256) void mp_step_kernel(const double* __restrict__
   }
 }
 
+// The pivots of one panel (up to 128) in one cooperative launch, for
+// searches whose columns fit few workgroups: the same step as
+// mp_step_kernel, with no launch between two pivots. Each workgroup owns
+// MP_T columns and keeps their entries of the panel's Pt rows in LDS
+// (128 x MP_T fp64), so the dot product of a step reads LDS; the entries
+// also go to Pt in global memory for the tile update after the panel.
+//
+// What one workgroup tells the others travels in tagged 64-bit words: the
+// tag j + 1 of step j in the upper half beside 32 bits of payload, each word
+// written and read whole with agent-scope atomics (no fences), so a reader
+// that sees the tag it waits for sees that step's payload.
+//  - slot: the minimum of the workgroup's columns after step j (value low
+//    and high words, column index): three words.
+//  - candidate: the Pt entries, rows 0..k, of that minimum's column (low
+//    and high word each), which are the pivot row of step j + 1 if that
+//    column wins.
+// Every wave of every workgroup polls all slots of step j - 1 (one lane per
+// workgroup) until each holds the tag j, takes the minimum from what it
+// read, then reads the winner's candidate (waiting for its tags too).
+// Both tables have two halves, by the parity of j: half j & 1 is written
+// again only at step j + 2, which needs every workgroup's slot of step j +
+// 1, published after it read half j & 1. Every wait is bounded: a wave that
+// gives up ends the search with ST_NOTSPD, and so does every wave that then
+// waits for it.
+constexpr int MP_T = 128;                 // columns per workgroup
+constexpr long MP_SPIN = 1L << 20;        // polls before a wait gives up
+
+__global__ void zero_u64_kernel(uint64_t* __restrict__ p, int count) {
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < count; k += gridDim.x * blockDim.x)
+    p[k] = 0;
+}
+
+// Minimum over the wave of (v, i), the result uniform: lane moves inside
+// quads and rows (DPP), a swizzle across the two row pairs of each half,
+// then the two halves' results read from lanes 0 and 32. The order is a
+// strict total one on distinct indices, so the result is the same as that of
+// any other reduction order.
+template <int CTRL>
+__device__ inline void mp_dpp_step(double& v, int& i) {
+  const double w = dpp_f64<CTRL>(v);
+  const int j = __builtin_amdgcn_update_dpp(i, i, CTRL, 0xF, 0xF, false);
+  const bool b = mp_before(w, j, v, i);
+  v = b ? w : v;
+  i = b ? j : i;
+}
+__device__ inline MinIdx mp_wave_min_u(double v, int i) {
+  mp_dpp_step<0xB1>(v, i);   // quad_perm [1,0,3,2]
+  mp_dpp_step<0x4E>(v, i);   // quad_perm [2,3,0,1]
+  mp_dpp_step<0x141>(v, i);  // row_half_mirror: the other quad of each 8 lanes
+  mp_dpp_step<0x140>(v, i);  // row_mirror: the other 8 lanes of each row
+  {
+    // lane ^ 16 inside each 32 lanes (swizzle, bitmask mode)
+    constexpr int SW = 0x1F | (0x10 << 10);
+    const int lo = __builtin_amdgcn_ds_swizzle(__double2loint(v), SW);
+    const int hi = __builtin_amdgcn_ds_swizzle(__double2hiint(v), SW);
+    const int j = __builtin_amdgcn_ds_swizzle(i, SW);
+    const double w = __hiloint2double(hi, lo);
+    const bool b = mp_before(w, j, v, i);
+    v = b ? w : v;
+    i = b ? j : i;
+  }
+  const double a = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 0),
+                                    __builtin_amdgcn_readlane(__double2loint(v), 0));
+  const int ai = __builtin_amdgcn_readlane(i, 0);
+  const double c = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), 32),
+                                    __builtin_amdgcn_readlane(__double2loint(v), 32));
+  const int ci = __builtin_amdgcn_readlane(i, 32);
+  return mp_before(c, ci, a, ai) ? MinIdx{c, ci} : MinIdx{a, ai};
+}
+
+// A tagged word: the tag above 32 bits of payload.
+__device__ inline uint64_t mp_word(unsigned tag, unsigned payload) {
+  return ((uint64_t)tag << 32) | payload;
+}
+__device__ inline void mp_put(uint64_t* w, unsigned tag, unsigned payload) {
+  __hip_atomic_store(w, mp_word(tag, payload), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t mp_get(const uint64_t* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline bool mp_tagged(uint64_t w, unsigned tag) { return (unsigned)(w >> 32) == tag; }
+
+__global__ __launch_bounds__(MP_T) void mp_panel_kernel(const double* __restrict__ A, int64_t ld,
+                                                        int64_t n, int64_t ip,
+                                                        double* __restrict__ d,
+                                                        double* __restrict__ Pt, int j0, int kn,
+                                                        const double* __restrict__ mv0,
+                                                        const int* __restrict__ mi0, int nprev,
+                                                        uint64_t* __restrict__ slots,
+                                                        uint64_t* __restrict__ cands,
+                                                        int32_t* __restrict__ perm,
+                                                        unsigned* __restrict__ status) {
+  constexpr int NW = MP_T / 64;
+  __shared__ double pts[GT][MP_T];  // this workgroup's entries of the panel's Pt rows
+  __shared__ double prow[GT];
+  __shared__ double sv[NW];
+  __shared__ int si[NW];
+  __shared__ int fail[NW];
+  __shared__ unsigned st0;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int nwg = gridDim.x;
+  // a failed step earlier on the stream: the order is garbage already, and
+  // the slots of its last step may never have been written
+  if (t == 0) st0 = *status;
+  __syncthreads();
+  if (st0 & ST_NOTSPD) return;
+  const int64_t i = (int64_t)blockIdx.x * MP_T + t;
+  double di = i < n ? d[i] : INFINITY;
+  // j0 is the first column of a panel, so panel column k = j - j0
+  for (int k = 0; k < kn; ++k) {
+    const int j = j0 + k;
+    // the minima of step j - 1: mp_init's (written before this launch) for
+    // the first pivot, else the slots
+    double bv = INFINITY;
+    int bi = -1;
+    bool ok = true;
+    if (j == 0) {
+      for (int w = lane; w < nprev; w += 64)
+        if (mp_before(mv0[w], mi0[w], bv, bi)) {
+          bv = mv0[w];
+          bi = mi0[w];
+        }
+    } else if (lane < nwg) {
+      const uint64_t* sl = slots + ((size_t)((j - 1) & 1) * nwg + lane) * 4;
+      uint64_t w0, w1, w2;
+      long spins = 0;
+      for (;;) {
+        w0 = mp_get(sl);
+        w1 = mp_get(sl + 1);
+        w2 = mp_get(sl + 2);
+        if (mp_tagged(w0, j) && mp_tagged(w1, j) && mp_tagged(w2, j)) break;
+        if (++spins > MP_SPIN) {
+          ok = false;
+          break;
+        }
+      }
+      bv = __hiloint2double((int)(unsigned)w1, (int)(unsigned)w0);
+      bi = (int)(unsigned)w2;
+    }
+    const MinIdx m = mp_wave_min_u(bv, bi);
+    const double dp = m.v;
+    const int p = m.i;
+    bool good = __all(ok) && dp > 0.0 && isfinite(dp) && p >= 0 && p < n;
+    // the pivot's entries of this panel's earlier rows (its workgroup's
+    // candidate of step j - 1), and A's entry (i, p), loaded together from
+    // addresses valid in every lane (what a lane does not need is unused)
+    const int pc = good ? p : 0;
+    const int64_t ic = i < n ? i : pc;
+    double c = ic > pc ? A[ic * ld + pc] : A[(int64_t)pc * ld + ic];
+    if (good && t < k) {
+      const uint64_t* cw = cands + (((size_t)((j - 1) & 1) * nwg + pc / MP_T) * GT + t) * 2;
+      uint64_t lo, hi;
+      long spins = 0;
+      for (;;) {
+        lo = mp_get(cw);
+        hi = mp_get(cw + 1);
+        if (mp_tagged(lo, j) && mp_tagged(hi, j)) break;
+        if (++spins > MP_SPIN) {
+          good = false;
+          break;
+        }
+      }
+      prow[t] = __hiloint2double((int)(unsigned)hi, (int)(unsigned)lo);
+    }
+    good = __all(good);
+    if (lane == 0) fail[wv] = !good;
+    __syncthreads();
+    bool stop = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) stop |= fail[w] != 0;
+    if (stop) {
+      if (t == 0) atomicOr(status, ST_NOTSPD);
+      break;  // the same decision in every wave of the workgroup
+    }
+    if (blockIdx.x == 0 && t == 0) perm[n - 1 - j] = p;
+    const double rs = 1.0 / sqrt(dp);
+    double v = INFINITY;
+    if (i < n) {
+      double l;
+      if (i == p) {
+        l = dp * rs;
+        di = INFINITY;
+      } else if (di == INFINITY) {
+        l = 0.0;
+      } else {
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int q = 0; q < k; ++q) acc[q & 3] = fma(pts[q][t], prow[q], acc[q & 3]);
+        c -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        l = c * rs;
+        di -= l * l;
+        v = di;
+      }
+      pts[k][t] = l;
+      Pt[(int64_t)k * ip + i] = l;
+    }
+    const MinIdx mw = mp_wave_min_u(v, (int)i);
+    if (lane == 0) {
+      sv[wv] = mw.v;
+      si[wv] = mw.i;
+    }
+    __syncthreads();
+    MinIdx r{sv[0], si[0]};
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+      if (mp_before(sv[w], si[w], r.v, r.i)) r = MinIdx{sv[w], si[w]};
+    const unsigned tag = (unsigned)j + 1;
+    if (k + 1 < kn && t <= k) {
+      // the candidate's column, rows 0..k (the next step of this launch
+      // reads it; a launch starts at a panel's first row and reads none)
+      const double x = pts[t][r.i - (int)blockIdx.x * MP_T];
+      uint64_t* cw = cands + (((size_t)(j & 1) * nwg + blockIdx.x) * GT + t) * 2;
+      mp_put(cw, tag, (unsigned)__double2loint(x));
+      mp_put(cw + 1, tag, (unsigned)__double2hiint(x));
+    }
+    if (t == 0) {
+      uint64_t* sl = slots + ((size_t)(j & 1) * nwg + blockIdx.x) * 4;
+      mp_put(sl, tag, (unsigned)__double2loint(r.v));
+      mp_put(sl + 1, tag, (unsigned)__double2hiint(r.v));
+      mp_put(sl + 2, tag, (unsigned)r.i);
+    }
+  }
+  if (i < n) d[i] = di;
+}
+
+// The panel launches serve searches up to this many workgroups (MP_T columns
+// each): their barrier costs grow with the workgroup count, the per-pivot
+// launches' cost does not.
+constexpr int MP_PANEL_MAX_WG = 64;  // one polling lane per workgroup
+constexpr int MP_SLOT_WORDS = 2 * MP_PANEL_MAX_WG * 4;
+constexpr int MP_CAND_WORDS = 2 * MP_PANEL_MAX_WG * GT * 2;
+
+// Whether nwg workgroups of mp_panel_kernel can all be resident at once on
+// the current device (a cooperative launch needs that).
+static bool mp_panel_fits(int nwg) {
+  int dev = 0, coop = 0, ncu = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+      !coop)
+    return false;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)mp_panel_kernel, MP_T, 0) !=
+      hipSuccess)
+    return false;
+  return (int64_t)per * ncu >= nwg;
+}
+
 // After a full panel: A -= P P^T on every lower tile (a, b) of the ip grid.
 __global__ __launch_bounds__(256) void mp_update_kernel(double* __restrict__ A, int64_t ld,
                                                         int64_t ip,
@@ -1104,7 +1352,7 @@ constexpr int CHOL_FUSE_NT = 48;
 struct PrepLayout {
   int64_t n, ip, nt;
   size_t off_status, off_lam, off_hd, off_K, off_X, off_T, off_D, off_P;
-  size_t off_md, off_mpt, off_mv, off_mi;  // min-pivot search
+  size_t off_md, off_mpt, off_mv, off_mi, off_mslot, off_mcand;  // min-pivot search
   size_t total;
 };
 
@@ -1133,6 +1381,8 @@ static PrepLayout prep_layout(int64_t n) {
   L.off_mpt = take(8 * (size_t)GT * L.ip);
   L.off_mv = take(8 * 2 * (size_t)nwg);
   L.off_mi = take(4 * 2 * (size_t)nwg);
+  L.off_mslot = take(MP_SLOT_WORDS * 8);
+  L.off_mcand = take(MP_CAND_WORDS * 8);
   L.total = o;
   return L;
 }
@@ -1180,19 +1430,41 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     double* Pt = (double*)(base + L.off_mpt);
     double* mv = (double*)(base + L.off_mv);
     int* mi = (int*)(base + L.off_mi);
+    uint64_t* mslot = (uint64_t*)(base + L.off_mslot);
+    uint64_t* mcand = (uint64_t*)(base + L.off_mcand);
     const int nwg = (int)cdiv(ip, 256);
+    const int nwgp = (int)cdiv(ip, MP_T);
+    const bool panel = nwgp <= MP_PANEL_MAX_WG && mp_panel_fits(nwgp);
     GPTQ_LAUNCH(K_PREP_GATHER, st,
                 prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, nullptr, K));
     GPTQ_LAUNCH(K_MP_STEP, st,
                 mp_init_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, mv, mi, perm));
-    for (int64_t j = 0; j < n; ++j) {
-      const int k = (int)(j % GT), par = (int)(j & 1);
-      GPTQ_LAUNCH(K_MP_STEP, st,
-                  mp_step_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, (int)j, k,
-                                                      mv + par * nwg, mi + par * nwg,
-                                                      mv + (1 - par) * nwg, mi + (1 - par) * nwg,
-                                                      perm, status));
-      if (k == GT - 1 && j + 1 < n) {
+    if (panel) {  // no tag of an earlier call may match
+      GPTQ_LAUNCH(K_FILL, st, zero_u64_kernel<<<1, 256, 0, st>>>(mslot, MP_SLOT_WORDS));
+      GPTQ_LAUNCH(K_FILL, st, zero_u64_kernel<<<64, 256, 0, st>>>(mcand, MP_CAND_WORDS));
+    }
+    for (int64_t j0 = 0; j0 < n; j0 += GT) {
+      const int kn = (int)std::min<int64_t>(GT, n - j0);
+      if (panel) {
+        // the first pivot reads the minima of mp_init (nwg of them), the
+        // others the slots of the step before
+        int j0i = (int)j0, nprev = nwg, knv = kn;
+        int64_t ldv = ip, nv = n, ipv = ip;
+        void* args[] = {&K, &ldv, &nv, &ipv, &md, &Pt, &j0i, &knv, &mv, &mi, &nprev,
+                        &mslot, &mcand, &perm, &status};
+        GPTQ_LAUNCH(K_MP_STEP, st,
+                    GPTQ_HIP(hipLaunchCooperativeKernel((const void*)mp_panel_kernel,
+                                                        dim3(nwgp), dim3(MP_T), args, 0, st)));
+      } else {
+        for (int64_t j = j0; j < j0 + kn; ++j) {
+          const int k = (int)(j - j0), par = (int)(j & 1);
+          GPTQ_LAUNCH(K_MP_STEP, st,
+                      mp_step_kernel<<<nwg, 256, 0, st>>>(
+                          K, ip, n, ip, md, Pt, (int)j, k, mv + par * nwg, mi + par * nwg,
+                          mv + (1 - par) * nwg, mi + (1 - par) * nwg, perm, status));
+        }
+      }
+      if (j0 + kn < n) {
         const int tiles = (int)(L.nt * (L.nt + 1) / 2);
         GPTQ_LAUNCH(K_MP_UPDATE, st, mp_update_kernel<<<tiles, 256, 0, st>>>(K, ip, ip, Pt));
       }

@@ -117,12 +117,52 @@ def test_minpivot_flag_errors():
     assert ei.value.status == G.GPTQ_ENOTSPD
 
 
+def check_sampled(S, n_tokens, damp, perm, U, steps):
+    """A large min-pivot search, where the oracle's cubic greedy is out of
+    reach: the pivots at the given steps are checked against Schur diagonals
+    computed from scratch (a solve with the block eliminated before them),
+    and U against H_p on sampled rows (U H_p = U^-T is lower triangular with
+    diagonal 1/U_jj)."""
+    dim = S.shape[0]
+    pg = perm.cpu().numpy().astype(np.int64)
+    assert np.array_equal(np.sort(pg), np.arange(dim))
+    H = O.damped_hessian(S.cpu().numpy(), n_tokens, damp)
+    elim = pg[::-1]
+    for s in steps:
+        E = elim[:s]
+        alive = np.ones(dim, dtype=bool)
+        alive[E] = False
+        if s:
+            Y = np.linalg.solve(H[np.ix_(E, E)], H[E, :])
+            schur = np.diag(H) - np.einsum("ij,ij->j", H[E, :], Y)
+        else:
+            schur = np.diag(H).copy()
+        m = schur[alive].min()
+        assert schur[elim[s]] <= m * (1 + REL), (s, schur[elim[s]], m)
+    Hp = torch.from_numpy(O.permute_sym(H, pg)).to(DEV)
+    del H
+    rng = np.random.default_rng(7)
+    J = sorted(set([0, 1, dim // 2, dim - 2, dim - 1] + rng.integers(0, dim, 6).tolist()))
+    Ur = U[J].double()
+    Y = Ur @ Hp
+    A = Ur.abs() @ Hp.abs()
+    cols = torch.arange(dim, device=DEV)
+    jt = torch.tensor(J, device=DEV)
+    upper = cols[None, :] > jt[:, None]
+    assert float((Y.abs() / A)[upper].max()) <= 4e-7
+    ud = Ur[torch.arange(len(J), device=DEV), jt]
+    yd = Y[torch.arange(len(J), device=DEV), jt]
+    assert float(((yd - 1.0 / ud).abs() / A[torch.arange(len(J), device=DEV), jt]).max()) <= 4e-7
+
+
+# the first panel of pivots whole, then steps on both sides of the next two
+# panel boundaries (the tile update of A between panels)
+STEPS = list(range(48)) + [126, 127, 128, 129, 130, 200, 254, 255, 256, 257, 300]
+
+
 def test_minpivot_qwen_down_shape_sampled():
     """The 4864-feature down-projection input of the Qwen-shape workload
-    (2048 SiLU-gated tokens): the oracle's cubic greedy is out of reach, so
-    the first 48 pivots are checked against Schur diagonals computed from
-    scratch (a solve with the eliminated block), and U against H_p on
-    sampled rows (U H_p = U^-T is lower triangular with diagonal 1/U_jj)."""
+    (2048 SiLU-gated tokens); the search runs as one launch per panel."""
     from post_weight_quantization_hessian_amd import synth
     from post_weight_quantization_hessian_amd.workloads import WORKLOADS
     wl = WORKLOADS["qwen05b_mlp"]
@@ -133,31 +173,18 @@ def test_minpivot_qwen_down_shape_sampled():
     S = torch.zeros((h.dim, h.dim), dtype=torch.float64, device=DEV)
     G.hessian_accumulate(S, Xd, overwrite=True)
     perm, U = G.prepare_hinv(S, wl.n_tokens, damp=wl.damp, min_pivot=True)
-    pg = perm.cpu().numpy().astype(np.int64)
-    assert np.array_equal(np.sort(pg), np.arange(h.dim))
-    H = O.damped_hessian(S.cpu().numpy(), wl.n_tokens, wl.damp)
-    elim = pg[::-1]
-    for s in range(48):
-        E = elim[:s]
-        alive = np.ones(h.dim, dtype=bool)
-        alive[E] = False
-        if s:
-            Y = np.linalg.solve(H[np.ix_(E, E)], H[E, :])
-            schur = np.diag(H) - np.einsum("ij,ij->j", H[E, :], Y)
-        else:
-            schur = np.diag(H).copy()
-        m = schur[alive].min()
-        assert schur[elim[s]] <= m * (1 + REL), (s, schur[elim[s]], m)
-    Hp = torch.from_numpy(O.permute_sym(H, pg)).to(DEV)
-    rng = np.random.default_rng(7)
-    J = sorted(set([0, 1, h.dim // 2, h.dim - 2, h.dim - 1] + rng.integers(0, h.dim, 6).tolist()))
-    Ur = U[J].double()
-    Y = Ur @ Hp
-    A = Ur.abs() @ Hp.abs()
-    cols = torch.arange(h.dim, device=DEV)
-    jt = torch.tensor(J, device=DEV)
-    upper = cols[None, :] > jt[:, None]
-    assert float((Y.abs() / A)[upper].max()) <= 4e-7
-    ud = Ur[torch.arange(len(J), device=DEV), jt]
-    yd = Y[torch.arange(len(J), device=DEV), jt]
-    assert float(((yd - 1.0 / ud).abs() / A[torch.arange(len(J), device=DEV), jt]).max()) <= 4e-7
+    check_sampled(S, wl.n_tokens, wl.damp, perm, U, STEPS)
+
+
+def test_minpivot_wide_sampled():
+    """8320 features: more columns than the panel launches serve, so the
+    search runs as one launch per pivot."""
+    dim = 8320
+    say(f"min-pivot {dim}-feature Hessian")
+    rng = np.random.default_rng(8320)
+    X = (rng.standard_normal((3000, dim)) * rng.lognormal(0, 1, dim)).astype(np.float32)
+    Xd = torch.from_numpy(X).to(DEV)
+    S = torch.zeros((dim, dim), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, Xd, overwrite=True)
+    perm, U = G.prepare_hinv(S, 3000, damp=0.01, min_pivot=True)
+    check_sampled(S, 3000, 0.01, perm, U, STEPS)
