@@ -551,12 +551,12 @@ __global__ __launch_bounds__(256) void trtri_diag_kernel(const double* __restric
 // per kernel (a second loop form in a kernel costs registers and copies).
 // `smem` holds >= 4 * GCH doubles.
 __device__ __forceinline__ void tile_nt_update(const double* A, const double* B, double* C,
-                                               int64_t ld, int crows, double* smem) {
+                                               int64_t ld, int crows, int kch, double* smem) {
   LdTrans64T<true> la{A, ld, {}};
   LdTrans64 lb{B, ld, {}};
   d4 acc[4][4];
   acc_load_lds(acc, C, ld, crows, GT, smem);
-  gemm64_loop(la, lb, GT / GK, smem, smem + 2 * GCH, acc);
+  gemm64_loop(la, lb, kch, smem, smem + 2 * GCH, acc);
   for_each_acc(acc, [&](int r, int c, double v) { C[r * ld + c] = v; });
 }
 
@@ -564,8 +564,11 @@ __device__ __forceinline__ void tile_nt_update(const double* A, const double* B,
 // over the tiles a >= b >= 1 of the trailing triangle (mt tile rows, in
 // trailing-tile coordinates; b = 0 is the next panel's column): first the
 // column b = 1 (a = 1 .. mt-1), which the next column update reads, then the
-// tiles a >= b >= 2 row by row. Sets the operands of tile_nt_update.
-__device__ inline void syrk_tile_args(double* K, int64_t ld, int p, int mt, int id,
+// tiles a >= b >= 2 row by row. With kp = 2 the tile takes panels p - 1 and
+// p at once (K = 256: the two panels' columns are adjacent; the products
+// enter the accumulators in the same order as two separate updates, so the
+// result is the same). Sets the operands of tile_nt_update.
+__device__ inline void syrk_tile_args(double* K, int64_t ld, int p, int mt, int id, int kp,
                                       const double*& A, const double*& B, double*& C) {
   int a, b;
   if (id < mt - 1) {
@@ -582,8 +585,9 @@ __device__ inline void syrk_tile_args(double* K, int64_t ld, int p, int mt, int 
   }
   const int64_t c0 = (int64_t)p * GT, c1 = c0 + GT;
   const int64_t ra = c1 + (int64_t)a * GT, rb = c1 + (int64_t)b * GT;
-  A = K + ra * ld + c0;
-  B = K + rb * ld + c0;
+  const int64_t k0 = c0 - (int64_t)(kp - 1) * GT;
+  A = K + ra * ld + k0;
+  B = K + rb * ld + k0;
   C = K + ra * ld + rb;
 }
 
@@ -609,18 +613,21 @@ __device__ inline void xinv_tile_args(double* K, double* Z, int64_t ld, int p, i
 }
 
 // Background tile `id`: the first nsyrk ids are the trailing-update tiles
-// s0, s0 + 1, ... of panel ps (mts trailing tile rows), the others the
-// inverse tiles x0, x0 + 1, ... of panel px's step.
+// s0, s0 + 1, ... of panel ps (mts trailing tile rows; kps panels ending at
+// ps), the others the inverse tiles x0, x0 + 1, ... of panel px's step.
 __device__ __forceinline__ void bg_tile(double* K, double* Z, int64_t ld, int ps, int mts, int s0,
-                                        int nsyrk, int px, int x0, int id, double* smem) {
+                                        int nsyrk, int kps, int px, int x0, int id,
+                                        double* smem) {
   const double *A, *B;
   double* C;
-  int crows = GT;
-  if (id < nsyrk)
-    syrk_tile_args(K, ld, ps, mts, s0 + id, A, B, C);
-  else
+  int crows = GT, kch = GT / GK;
+  if (id < nsyrk) {
+    syrk_tile_args(K, ld, ps, mts, s0 + id, kps, A, B, C);
+    kch *= kps;
+  } else {
     xinv_tile_args(K, Z, ld, px, x0 + id - nsyrk, A, B, C, crows);
-  tile_nt_update(A, B, C, ld, crows, smem);
+  }
+  tile_nt_update(A, B, C, ld, crows, kch, smem);
 }
 
 // The next panel's tile column, C(a, p+1) -= L(a, p) L(p+1, p)^T for every
@@ -639,11 +646,12 @@ __device__ __forceinline__ void bg_tile(double* K, double* Z, int64_t ld, int ps
 // updates), then the first inverse tiles of panel p's step.
 __global__ __launch_bounds__(256, 2) void chol_col_kernel(double* __restrict__ K,
                                                           double* __restrict__ Z, int64_t ld,
-                                                          int p, int mt, int s0, int nsyrk) {
+                                                          int p, int mt, int s0, int nsyrk,
+                                                          int kps) {
   if ((int)blockIdx.x >= 4 * mt) {
     __shared__ double smem[4 * GCH];
     const int nx = (int)gridDim.x - 4 * mt;
-    bg_tile(K, Z, ld, p - 1, mt + 1, s0, nsyrk, p, 0,
+    bg_tile(K, Z, ld, p - 1, mt + 1, s0, nsyrk, kps, p, 0,
             xcd_remap((int)blockIdx.x - 4 * mt, nx), smem);
     return;
   }
@@ -721,12 +729,12 @@ __global__ __launch_bounds__(256, 2) void chol_potrf_syrk_kernel(double* __restr
                                                               double* __restrict__ Z, int64_t ld,
                                                               int q, int mts,
                                                               unsigned* __restrict__ status,
-                                                              int nsyrk, int x0) {
+                                                              int nsyrk, int x0, int kps) {
   __shared__ double smem[STEP_LDS];
   if (blockIdx.x == 0)
     potrf_block(K, Dd, ld, q, status, smem);
   else
-    bg_tile(K, Z, ld, q - 1, mts, 0, nsyrk, q - 1, x0,
+    bg_tile(K, Z, ld, q - 1, mts, 0, nsyrk, kps, q - 1, x0,
             xcd_remap(blockIdx.x - 1, gridDim.x - 1), smem);
 }
 
@@ -1488,12 +1496,20 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   // run beside panel p's column update (before the next panel solve, which
   // reads tile row p + 1), the trailing tiles that do not fit beside panel
   // p+1's column update (before panel p+1's own trailing tiles).
+  // Without the fused inverse (large matrices, where these tiles are most of
+  // the work), the trailing update goes two panels at a time: an even panel
+  // updates only column p + 2, which the next column update reads, and the
+  // odd panel after it applies both panels to the rest at once (K = 256),
+  // so each such tile is read and written once per two panels.
   const bool fused = nt <= CHOL_FUSE_NT;
   int sov = 0, sov0 = 0;  // trailing tiles of the previous panel for this column update
+  int kpo = 1;            // panels those tiles take
   GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
   for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
-    const int rest = (mt - 1) * mt / 2;
+    const bool col_only = !fused && p % 2 == 0;
+    const int kp = !fused && p % 2 == 1 ? 2 : 1;
+    const int rest = col_only ? mt - 1 : (mt - 1) * mt / 2;
     const int xs = fused ? 2 * (p + 1) : 0;   // inverse row-solve workgroups
     const int xt = fused ? mt * (p + 1) : 0;  // inverse tile updates
     const int ns = std::min(rest, std::max(CHOL_MERGE_TILES, mt - 1));
@@ -1503,12 +1519,13 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                 chol_trsm_kernel<<<2 * mt + xs, 256, 0, st>>>(K, Dd, Xb, ip, p, mt));
     GPTQ_LAUNCH(K_CHOL_COL, st,
                 chol_col_kernel<<<4 * mt + sov + xcol, 256, 0, st>>>(K, Xb, ip, p, mt, sov0,
-                                                                     sov));
+                                                                     sov, kpo));
     GPTQ_LAUNCH(K_CHOL_STEP, st,
                 chol_potrf_syrk_kernel<<<1 + ns + xstep, 256, 0, st>>>(K, Dd, Xb, ip, p + 1, mt,
-                                                                      status, ns, xcol));
+                                                                      status, ns, xcol, kp));
     sov = rest - ns;
     sov0 = ns;
+    kpo = kp;
   }
   if (fused) {
     // the last block row of X
