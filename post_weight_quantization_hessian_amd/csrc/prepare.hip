@@ -1356,6 +1356,8 @@ __global__ __launch_bounds__(256) void mp_update_kernel(double* __restrict__ A, 
 // doubling, whose long inner sums run the MFMA units more efficiently and
 // read each tile once per level instead of once per panel.
 constexpr int CHOL_FUSE_NT = 48;
+// panels per trailing update without the fused inverse
+constexpr int CHOL_GROUP = 4;
 
 struct PrepLayout {
   int64_t n, ip, nt;
@@ -1497,18 +1499,22 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   // reads tile row p + 1), the trailing tiles that do not fit beside panel
   // p+1's column update (before panel p+1's own trailing tiles).
   // Without the fused inverse (large matrices, where these tiles are most of
-  // the work), the trailing update goes two panels at a time: an even panel
-  // updates only column p + 2, which the next column update reads, and the
-  // odd panel after it applies both panels to the rest at once (K = 256),
-  // so each such tile is read and written once per two panels.
+  // the work), the trailing update goes CHOL_GROUP panels at a time: panel
+  // p = g0 + r of a group starting at g0 updates only column p + 2, which
+  // the next column update reads, with panels g0 .. p (K = 128 (r + 1));
+  // the group's last panel applies all of them to the rest at once, so each
+  // such tile is read and written once per group. (Column c gets the
+  // group's panels up to c - 2 at panel c - 2, and the panels after that
+  // from the column updates; a group cut short by the end leaves no tile.)
   const bool fused = nt <= CHOL_FUSE_NT;
   int sov = 0, sov0 = 0;  // trailing tiles of the previous panel for this column update
   int kpo = 1;            // panels those tiles take
   GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
   for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
-    const bool col_only = !fused && p % 2 == 0;
-    const int kp = !fused && p % 2 == 1 ? 2 : 1;
+    const int r = p % CHOL_GROUP;
+    const bool col_only = !fused && r < CHOL_GROUP - 1;
+    const int kp = fused ? 1 : r + 1;
     const int rest = col_only ? mt - 1 : (mt - 1) * mt / 2;
     const int xs = fused ? 2 * (p + 1) : 0;   // inverse row-solve workgroups
     const int xt = fused ? mt * (p + 1) : 0;  // inverse tile updates
