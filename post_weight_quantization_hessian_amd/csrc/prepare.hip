@@ -74,23 +74,32 @@ __global__ __launch_bounds__(256) void prep_perm_kernel(const double* __restrict
 }
 
 // Lower triangle of K (ip x ip, ld ip): K[a][b] = H[p_a][p_b], p_x = perm[n-1-x],
-// H = c*S + lam*I; the padding a, b >= n is the identity. One row per block.
-__global__ __launch_bounds__(256) void prep_gather_kernel(const double* __restrict__ S, int64_t n,
-                                                          int64_t ip, double c,
-                                                          const double* __restrict__ lam_p,
-                                                          const int32_t* __restrict__ perm,
-                                                          double* __restrict__ K) {
-  const int64_t a = blockIdx.x;
+// H = c*S + lam*I; the padding a, b >= n is the identity. GATHER_SPLIT
+// blocks per row, each a contiguous range of b; the blocks of one row are
+// consecutive after the XCD remap, so they run on one XCD and the scattered
+// reads of the permuted S row are served from its L2 (with one block per row,
+// the rows in flight did not fit the L2s and most reads of a row went to
+// memory again).
+constexpr int GATHER_SPLIT = 8;
+__global__ __launch_bounds__(1024) void prep_gather_kernel(const double* __restrict__ S, int64_t n,
+                                                           int64_t ip, double c,
+                                                           const double* __restrict__ lam_p,
+                                                           const int32_t* __restrict__ perm,
+                                                           double* __restrict__ K) {
+  const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t a = lin / GATHER_SPLIT;
+  const int q = (int)(lin % GATHER_SPLIT);
+  const int64_t lo = (a + 1) * q / GATHER_SPLIT, hi = (a + 1) * (q + 1) / GATHER_SPLIT;
   const double lam = *lam_p;
   double* row = K + a * ip;
   if (a >= n) {
-    for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) row[b] = (a == b) ? 1.0 : 0.0;
+    for (int64_t b = lo + threadIdx.x; b < hi; b += blockDim.x) row[b] = (a == b) ? 1.0 : 0.0;
     return;
   }
   // without perm: H itself in the original order (the min-pivot search)
   const int64_t pa = perm ? perm[n - 1 - a] : a;
   const double* srow = S + pa * n;
-  for (int64_t b = threadIdx.x; b <= a; b += blockDim.x) {
+  for (int64_t b = lo + threadIdx.x; b < hi; b += blockDim.x) {
     const int64_t pb = perm ? perm[n - 1 - b] : b;
     double v = c * srow[pb];
     if (a == b) v += lam;
@@ -1446,7 +1455,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     const int nwgp = (int)cdiv(ip, MP_T);
     const bool panel = nwgp <= MP_PANEL_MAX_WG && mp_panel_fits(nwgp);
     GPTQ_LAUNCH(K_PREP_GATHER, st,
-                prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, nullptr, K));
+                prep_gather_kernel<<<(unsigned)(ip * GATHER_SPLIT), 1024, 0, st>>>(S, n, ip, c, lam,
+                                                                                   nullptr, K));
     GPTQ_LAUNCH(K_MP_STEP, st,
                 mp_init_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, mv, mi, perm));
     if (panel) {  // no tag of an earlier call may match
@@ -1485,7 +1495,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                     hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
   }
   GPTQ_LAUNCH(K_PREP_GATHER, st,
-              prep_gather_kernel<<<(unsigned)ip, 256, 0, st>>>(S, n, ip, c, lam, perm, K));
+              prep_gather_kernel<<<(unsigned)(ip * GATHER_SPLIT), 1024, 0, st>>>(S, n, ip, c, lam,
+                                                                                 perm, K));
   // Blocked Cholesky, one stream. Per panel p: solve the panel's column
   // (trsm), update the next panel's tile column, then one launch that
   // factors the next diagonal block beside the rest of the trailing update.
