@@ -81,6 +81,61 @@ __global__ __launch_bounds__(256) void q_permute_kernel(const uint16_t* __restri
 
 // codes[r][m] = codes_s[r][invperm[m]]; g_idx[m] = invperm[m] / gs. An unset
 // invperm entry (perm was not a permutation) is reported and gives code 0.
+// The same two gathers with the source row staged in LDS (rows of up to
+// QP_LDS_COLS columns, 64 KB of fp16): the row is read once, contiguously,
+// and the permuted reads hit LDS instead of scattering 2- or 1-byte loads
+// over memory. One block per row (grid-stride over rows).
+constexpr int64_t QP_LDS_COLS = 32768;
+__global__ __launch_bounds__(1024) void q_permute_lds_kernel(const uint16_t* __restrict__ W,
+                                                             int64_t ldw,
+                                                             const int32_t* __restrict__ perm,
+                                                             int64_t rows, int64_t cols,
+                                                             uint16_t* __restrict__ Wp,
+                                                             int32_t* __restrict__ invperm,
+                                                             unsigned* __restrict__ status) {
+  extern __shared__ uint16_t qp_row[];
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint16_t* src = W + r * ldw;
+    for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) qp_row[k] = src[k];
+    __syncthreads();
+    uint16_t* dst = Wp + r * cols;
+    for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) {
+      const int64_t pk = perm[k];
+      if (pk < 0 || pk >= cols) {
+        if (r == 0) atomicOr(status, ST_BADPERM);
+        dst[k] = 0;
+        continue;
+      }
+      dst[k] = qp_row[pk];
+      if (r == 0) invperm[pk] = (int32_t)k;
+    }
+    __syncthreads();
+  }
+}
+__global__ __launch_bounds__(1024) void q_finalize_lds_kernel(const uint8_t* __restrict__ codes_s,
+                                                              const int32_t* __restrict__ invperm,
+                                                              int64_t rows, int64_t cols, int gs,
+                                                              uint8_t* __restrict__ codes,
+                                                              int32_t* __restrict__ g_idx,
+                                                              unsigned* __restrict__ status) {
+  extern __shared__ uint8_t qf_row[];
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const uint8_t* src = codes_s + r * cols;
+    for (int64_t k = threadIdx.x; k < cols; k += blockDim.x) qf_row[k] = src[k];
+    __syncthreads();
+    for (int64_t m = threadIdx.x; m < cols; m += blockDim.x) {
+      const int32_t k = invperm[m];
+      if (k < 0 || k >= cols) {
+        if (r == 0) atomicOr(status, ST_BADPERM);
+        if (codes) codes[r * cols + m] = 0;
+        continue;
+      }
+      if (codes) codes[r * cols + m] = qf_row[k];
+      if (r == 0 && g_idx) g_idx[m] = k / gs;
+    }
+    __syncthreads();
+  }
+}
 __global__ __launch_bounds__(256) void q_finalize_kernel(const uint8_t* __restrict__ codes_s,
                                                          const int32_t* __restrict__ invperm,
                                                          int64_t rows, int64_t cols, int gs,
@@ -885,7 +940,15 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
   const uint16_t* Wsrc = W;
   int64_t ldws = ldw;
   uint8_t* csw = codes ? codes : codes_s;  // sweep-order codes (HPTQ: none returned)
-  if (perm) {
+  if (perm && cols <= QP_LDS_COLS) {
+    GPTQ_LAUNCH(K_Q_PERMUTE, st,
+                q_permute_lds_kernel<<<(unsigned)std::min<int64_t>(rows, 65535), 1024,
+                                       (size_t)cols * 2, st>>>(W, ldw, perm, rows, cols, Wp,
+                                                               invperm, status));
+    Wsrc = Wp;
+    ldws = cols;
+    csw = codes_s;
+  } else if (perm) {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(cols, 256), 16),
               (unsigned)std::min<int64_t>(rows, 65535));
     GPTQ_LAUNCH(K_Q_PERMUTE, st,
@@ -975,7 +1038,12 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
     }
     if (s != GPTQ_OK) return s;
   }
-  if (perm) {
+  if (perm && cols <= QP_LDS_COLS) {
+    GPTQ_LAUNCH(K_Q_FINALIZE, st,
+                q_finalize_lds_kernel<<<(unsigned)std::min<int64_t>(rows, 65535), 1024,
+                                        (size_t)cols, st>>>(codes_s, invperm, rows, cols,
+                                                            group_size, codes, g_idx, status));
+  } else if (perm) {
     dim3 grid((unsigned)std::min<int64_t>(cdiv(cols, 256), 16),
               (unsigned)std::min<int64_t>(rows, 65535));
     GPTQ_LAUNCH(K_Q_FINALIZE, st,
