@@ -74,22 +74,23 @@ __global__ __launch_bounds__(256) void prep_perm_kernel(const double* __restrict
 }
 
 // Lower triangle of K (ip x ip, ld ip): K[a][b] = H[p_a][p_b], p_x = perm[n-1-x],
-// H = c*S + lam*I; the padding a, b >= n is the identity. GATHER_SPLIT
-// blocks per row, each a contiguous range of b; the blocks of one row are
+// H = c*S + lam*I; the padding a, b >= n is the identity. `split` blocks
+// per row, each a contiguous range of b; the blocks of one row are
 // consecutive after the XCD remap, so they run on one XCD and the scattered
-// reads of the permuted S row are served from its L2 (with one block per row,
-// the rows in flight did not fit the L2s and most reads of a row went to
-// memory again).
-constexpr int GATHER_SPLIT = 8;
+// reads of the permuted S row are served from its L2. Large matrices take 8
+// blocks of 1024 threads per row (with one block per row, the rows in
+// flight did not fit the L2s and most reads of a row went to memory again);
+// small ones one block of 256 threads, whose rows fit anyway.
+constexpr int64_t GATHER_SPLIT_FROM = 8192;  // features from which rows are split
 __global__ __launch_bounds__(1024) void prep_gather_kernel(const double* __restrict__ S, int64_t n,
                                                            int64_t ip, double c,
                                                            const double* __restrict__ lam_p,
                                                            const int32_t* __restrict__ perm,
-                                                           double* __restrict__ K) {
+                                                           double* __restrict__ K, int split) {
   const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t a = lin / GATHER_SPLIT;
-  const int q = (int)(lin % GATHER_SPLIT);
-  const int64_t lo = (a + 1) * q / GATHER_SPLIT, hi = (a + 1) * (q + 1) / GATHER_SPLIT;
+  const int64_t a = lin / split;
+  const int q = (int)(lin % split);
+  const int64_t lo = (a + 1) * q / split, hi = (a + 1) * (q + 1) / split;
   const double lam = *lam_p;
   double* row = K + a * ip;
   if (a >= n) {
@@ -1443,6 +1444,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
 
   GPTQ_LAUNCH(K_FILL, st, zero_u32_kernel<<<1, 1, 0, st>>>(status));
   GPTQ_LAUNCH(K_PREP_DIAG, st, prep_diag_kernel<<<1, 1024, 0, st>>>(S, n, c, damp, hd, lam));
+  const int gsplit = n >= GATHER_SPLIT_FROM ? 8 : 1, gthreads = gsplit > 1 ? 1024 : 256;
   if (flags & GPTQ_FLAG_MIN_PIVOT) {
     // the order from a pivoted factorization of H in the original order
     double* md = (double*)(base + L.off_md);
@@ -1455,8 +1457,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     const int nwgp = (int)cdiv(ip, MP_T);
     const bool panel = nwgp <= MP_PANEL_MAX_WG && mp_panel_fits(nwgp);
     GPTQ_LAUNCH(K_PREP_GATHER, st,
-                prep_gather_kernel<<<(unsigned)(ip * GATHER_SPLIT), 1024, 0, st>>>(S, n, ip, c, lam,
-                                                                                   nullptr, K));
+                prep_gather_kernel<<<(unsigned)(ip * gsplit), gthreads, 0, st>>>(
+                    S, n, ip, c, lam, nullptr, K, gsplit));
     GPTQ_LAUNCH(K_MP_STEP, st,
                 mp_init_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, mv, mi, perm));
     if (panel) {  // no tag of an earlier call may match
@@ -1495,8 +1497,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                     hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
   }
   GPTQ_LAUNCH(K_PREP_GATHER, st,
-              prep_gather_kernel<<<(unsigned)(ip * GATHER_SPLIT), 1024, 0, st>>>(S, n, ip, c, lam,
-                                                                                 perm, K));
+              prep_gather_kernel<<<(unsigned)(ip * gsplit), gthreads, 0, st>>>(S, n, ip, c, lam,
+                                                                               perm, K, gsplit));
   // Blocked Cholesky, one stream. Per panel p: solve the panel's column
   // (trsm), update the next panel's tile column, then one launch that
   // factors the next diagonal block beside the rest of the trailing update.
