@@ -188,3 +188,34 @@ def test_minpivot_wide_sampled():
     G.hessian_accumulate(S, Xd, overwrite=True)
     perm, U = G.prepare_hinv(S, 3000, damp=0.01, min_pivot=True)
     check_sampled(S, 3000, 0.01, perm, U, STEPS)
+
+
+def test_minpivot_concurrent_streams_match_serial():
+    """Two min-pivot searches on two streams at once (each its own
+    cooperative launches and workspace, as the layer pipeline runs the MLP's
+    two inputs) give the serial results bit for bit, twice in a row."""
+    say("min-pivot on two streams")
+    (S1r, n1), _ = hessian(700, 71)
+    (S2r, n2), _ = hessian(2500, 72)
+    S1 = torch.from_numpy(S1r).to(DEV)
+    S2 = torch.from_numpy(S2r).to(DEV)
+    p1, U1 = G.prepare_hinv(S1, n1, damp=0.01, min_pivot=True)
+    p2, U2 = G.prepare_hinv(S2, n2, damp=0.01, min_pivot=True)
+    ws1 = torch.empty(G.prepare_workspace_bytes(700), dtype=torch.uint8, device=DEV)
+    ws2 = torch.empty(G.prepare_workspace_bytes(2500), dtype=torch.uint8, device=DEV)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(2):
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s1):
+            q1, V1 = G.prepare_hinv(S1, n1, damp=0.01, min_pivot=True, workspace=ws1, sync=False)
+        with torch.cuda.stream(s2):
+            q2, V2 = G.prepare_hinv(S2, n2, damp=0.01, min_pivot=True, workspace=ws2, sync=False)
+        with torch.cuda.stream(s1):
+            G.workspace_status(ws1)
+        with torch.cuda.stream(s2):
+            G.workspace_status(ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(q1, p1) and torch.equal(q2, p2)
+        assert torch.equal(V1.view(torch.int32), U1.view(torch.int32))
+        assert torch.equal(V2.view(torch.int32), U2.view(torch.int32))
