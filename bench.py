@@ -107,8 +107,9 @@ def kernel_work(name, wl, plan, sweeps=1.0):
         f = sum(h.n * h.dim * (h.dim + 1) for h in plan if not h.split8)  # symmetric half
         return f, "flop", "f64_mfma"
     if name == "hessian_split8":
-        # the 16 digit-pair products of the symmetric half, int8 multiply + add
-        f = sum(16 * h.n * h.dim * (h.dim + 1) for h in plan if h.split8)
+        # the 13 digit-pair products (orders a + b <= 4) of the symmetric
+        # half, int8 multiply + add
+        f = sum(13 * h.n * h.dim * (h.dim + 1) for h in plan if h.split8)
         return f, "op", "i8_mfma"
     if name == "hessian_digits":
         # column maxima (read X), digit planes (read X, write 4 int8 per value)

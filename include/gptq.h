@@ -89,10 +89,13 @@ typedef enum {
  * products, after Ozaki, Ogita, Oishi and Rump). Per call, column f of X
  * gets the scale 2^e_f, the smallest power of two above max_k |x_kf|, and
  * each value is rounded to the nearest multiple of 2^(e_f - 30) (ties to
- * even); that fixed-point value is cut into four signed int8 digits and
- * every digit-pair product is summed exactly in int32, then in fp64. The
- * result is X~^T X~ for the rounded X~ (|x~ - x| <= 2^(e_f - 31)), up to the
- * fp64 additions. A column holding NaN or Inf gives NaN in its row and
+ * even); that fixed-point value m 2^(e_f - 30) is cut into four signed int8
+ * digits, m = d0 2^24 + d1 2^16 + d2 2^8 + d3 (d1..d3 in [-128, 127]), and
+ * the digit-pair products of orders a + b <= 4 (13 of the 16) are summed
+ * exactly in int32, then in fp64. The result is X~^T X~ for the rounded X~
+ * (|x~ - x| <= 2^(e_f - 31)) less its digit orders 5 and 6
+ * (2^(e_f + e_g - 60) (2^8 (D2^T D3 + D3^T D2) + D3^T D3), under
+ * 2^(e_f + e_g - 36.99) per token), up to the fp64 additions. A column holding NaN or Inf gives NaN in its row and
  * column of S. The workspace is then required: ws_bytes >=
  * gptq_hessian_split8_workspace_bytes(in_features, n_tokens), else
  * GPTQ_EWORKSPACE (it holds the digit planes, 4 * in_features * n_tokens

@@ -210,19 +210,22 @@ static void hess_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit,
 //   x_kf x_kg = 2^(e_f + e_g - 60) * sum_{a,b} d_a d_b 2^(48 - 8(a + b)),
 // and for every digit order s = a + b the sum T_s = sum_{a+b=s} D_a^T D_b over
 // the tokens is an exact int32 product on v_mfma_i32_32x32x32_i8 (at most
-// 4 * 2^14 per token, 16384 tokens per workgroup). Each T_s is added into
-// fp64 accumulators once it is complete. What this represents exactly is x
-// rounded to 30 fractional bits of its column's scale: an error of at most
-// 2^(e_f - 31) per value, no other error than the fp64 additions.
+// 4 * 2^14 per token, 16384 tokens per workgroup). Only the orders s <= 4 are
+// formed (13 of the 16 digit pairs): the orders 5 and 6 weigh at most
+// (2 * 2^14 * 2^8 + 2^14) * 2^(e_f + e_g - 60) < 2^(e_f + e_g - 36.99) per
+// token, under 2^-6 of what rounding x to the fixed point may already change
+// in a product (up to 2^(e_f + e_g - 30)). Each T_s is added into fp64 accumulators once
+// it is complete. What this represents exactly is x rounded to 30 fractional
+// bits of its column's scale, less the orders 5 and 6 of its digit products;
+// no other error than the fp64 additions.
 
 constexpr int H8_KB = 64;               // tokens per staged chunk
 constexpr int H8_LD = 64;               // LDS row pitch in bytes, 16-byte chunks swizzled
-constexpr int H8_TN = 64;               // workgroup tile: 128 rows x 64 columns of S
-constexpr int H8_ABUF = 4 * GT * H8_LD;     // one chunk of A: 4 digit planes x 128 rows
-constexpr int H8_BBUF = 4 * H8_TN * H8_LD;  // one chunk of B: 4 digit planes x 64 rows
+constexpr int H8_BUF = 4 * GT * H8_LD;  // one chunk of 128 rows: 4 digit planes
 constexpr int H8_GRP = 8;               // tiles are visited in 8x8 groups (L2 reuse)
 constexpr int H8_MAXTOK = 16384;        // tokens per workgroup (int32 range of T_s)
 constexpr int H8_BAD = 0x40000000;      // exponent of a column holding NaN/Inf
+constexpr int H8_ORD = 5;               // digit orders s = a + b formed: 0 .. 4
 
 typedef int i4v __attribute__((ext_vector_type(4)));
 typedef int i16v __attribute__((ext_vector_type(16)));
@@ -318,13 +321,10 @@ __global__ __launch_bounds__(256) void h8_split_kernel(const float* __restrict__
 // 128-tile of a launch slot: the upper triangle of 128x128 tiles is visited
 // in groups of 8x8 tiles (row-major over the triangle of groups, row-major
 // inside a group), so that the workgroups resident on one XCD share operand
-// rows in its L2; each tile is two slots (its left and right 64 columns).
-// Slots of a group that fall below the diagonal or outside the matrix have
-// no tile.
-__device__ inline bool h8_tile_of(int id, int nt, int& a, int& b, int& half) {
+// rows in its L2. Slots of a group that fall below the diagonal or outside
+// the matrix have no tile.
+__device__ inline bool h8_tile_of(int id, int nt, int& a, int& b) {
   const int ng = (nt + H8_GRP - 1) / H8_GRP;
-  half = id & 1;
-  id >>= 1;
   int ga, gb;
   upper_tile(id / (H8_GRP * H8_GRP), ng, ga, gb);
   const int loc = id % (H8_GRP * H8_GRP);
@@ -333,55 +333,55 @@ __device__ inline bool h8_tile_of(int id, int nt, int& a, int& b, int& half) {
   return a <= b && b < nt;
 }
 
-// 128 rows x 64 columns of an upper 128-tile of S (a <= b) for one token
-// split per workgroup: eight waves (two per SIMD), each a 32 x 32
-// v_mfma_i32_32x32x32_i8 tile. Every 64-token chunk stages all four digit
-// planes of the rows and of the columns in LDS, and all 16 digit pairs are
-// multiplied from there; each digit order s = a + b has its own int32
-// accumulator for the whole token range (7 orders x 16 = 112 registers),
-// combined in fp64 at the end. v_mfma_i32_32x32x32_i8 operands (lane l): 16
-// int8 of row l%32 of A (of column l%32 of B) over the tokens 16*(l/32) ..
-// +15 of the 32-token step; A and B are loaded alike, so the pairing of their
-// k indices inside the instruction is the same for both. D reg x: row
-// 8*(x/4) + 4*(l/32) + x%4, col l%32. The next chunk is loaded into
-// registers while the current one is multiplied, and two chunks alternate in
-// LDS.
+// One upper 128-tile of S (a <= b) for one token split per workgroup: eight
+// waves (two per SIMD), wave w takes rows 32 (w / 2) .. +31 and columns
+// 64 (w % 2) .. +63 as two 32 x 32 v_mfma_i32_32x32x32_i8 blocks that share
+// the row operands. Every 64-token chunk stages all four digit planes of the
+// 128 rows and of the 128 columns in LDS, and the 13 digit pairs of orders
+// s = a + b <= 4 are multiplied from there; each order and column block has
+// its own int32 accumulator for the whole token range (2 x 5 x 16 = 160
+// registers), combined in fp64 at the end. v_mfma_i32_32x32x32_i8 operands
+// (lane l): 16 int8 of row l%32 of A (of column l%32 of B) over the tokens
+// 16*(l/32) .. +15 of the 32-token step; A and B are loaded alike, so the
+// pairing of their k indices inside the instruction is the same for both.
+// D reg x: row 8*(x/4) + 4*(l/32) + x%4, col l%32. The next chunk is loaded
+// into registers while the current one is multiplied, and two chunks
+// alternate in LDS.
 __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restrict__ dig, int64_t dpad,
                                                          int64_t npad, const int* __restrict__ exps,
                                                          int64_t n_tokens, int64_t dim, int nt,
                                                          int nslots, int64_t tok_per_split,
                                                          double* __restrict__ S, int64_t lds,
                                                          double* __restrict__ part, bool acc_old) {
-  __shared__ __attribute__((aligned(16))) int8_t sm[2][H8_ABUF + H8_BBUF];
+  __shared__ __attribute__((aligned(16))) int8_t sm[2][2 * H8_BUF];
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int slot = lin % nslots;
   const int split = lin / nslots;
-  int ta, tb, half;
-  if (!h8_tile_of(slot, nt, ta, tb, half)) return;  // uniform per workgroup
-  const int64_t fa = (int64_t)ta * GT, fb = (int64_t)tb * GT + half * H8_TN;
+  int ta, tb;
+  if (!h8_tile_of(slot, nt, ta, tb)) return;  // uniform per workgroup
+  const int64_t fa = (int64_t)ta * GT, fb = (int64_t)tb * GT;
   const int64_t t0 = (int64_t)split * tok_per_split;
   int64_t t1 = t0 + tok_per_split;
   const int64_t tend = round_up(n_tokens, H8_KB);
   if (t1 > tend) t1 = tend;
   const int nst = (int)((t1 - t0) / H8_KB);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wr = w >> 1, wc = w & 1;
-  // loads: A row lrow of all four planes; B row lrow % 64 of planes
-  // 2 (lrow / 64) and 2 (lrow / 64) + 1; 16-byte chunk lch of the 64 tokens
+  // loads: row lrow of all four planes of A and of B; 16-byte chunk lch of
+  // the 64 tokens
   const int lrow = tid >> 2, lch = tid & 3;
-  const int brw = lrow & 63, bpl = (lrow >> 6) * 2;
   // one chunk of a feature: 4 planes x 64 tokens, contiguous (256 bytes)
   constexpr int CHB = 4 * H8_KB;
   const int64_t nchk = npad / H8_KB;
   const int8_t* gA = dig + ((fa + lrow) * nchk + t0 / H8_KB) * CHB + lch * 16;
-  const int8_t* gB = dig + ((fb + brw) * nchk + t0 / H8_KB) * CHB + bpl * H8_KB + lch * 16;
-  i4v ra[4], rb[2];
+  const int8_t* gB = dig + ((fb + lrow) * nchk + t0 / H8_KB) * CHB + lch * 16;
+  i4v ra[4], rb[4];
   auto fetch = [&](int k) {
     if (k > nst - 1) k = nst - 1;  // past the end: reload the last chunk (never used)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       ra[q] = *reinterpret_cast<const i4v*>(gA + (int64_t)k * CHB + q * H8_KB);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 4; ++q)
       rb[q] = *reinterpret_cast<const i4v*>(gB + (int64_t)k * CHB + q * H8_KB);
   };
   // LDS rows of 64 bytes; chunk c of row r sits at position c ^ ((r >> 2) & 3).
@@ -390,23 +390,23 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
   // chunk: row r mod 4 picks the 16-bank quarter, the swizzle the 4 banks)
   auto stash = [&](int buf) {
     int8_t* A = sm[buf] + lrow * H8_LD + ((lch ^ ((lrow >> 2) & 3)) << 4);
-    int8_t* B = sm[buf] + H8_ABUF + bpl * (H8_TN * H8_LD) + brw * H8_LD +
-                ((lch ^ ((brw >> 2) & 3)) << 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) *reinterpret_cast<i4v*>(A + q * (GT * H8_LD)) = ra[q];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<i4v*>(B + q * (H8_TN * H8_LD)) = rb[q];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<i4v*>(A + H8_BUF + q * (GT * H8_LD)) = rb[q];
   };
-  i16v acc[7];
+  i16v acc[2][H8_ORD];
 #pragma unroll
-  for (int o = 0; o < 7; ++o)
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) acc[o][x] = 0;
-  // operand rows: wr*32 + l%32 (A), wc*32 + l%32 (B); both have the same
-  // swizzle, (l%32 >> 2) & 3, since 32-row offsets leave bits 2-3 alone
+    for (int o = 0; o < H8_ORD; ++o)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) acc[cb][o][x] = 0;
+  // operand rows: wr*32 + l%32 (A), wc*64 + cb*32 + l%32 (B); all have the
+  // same swizzle, (l%32 >> 2) & 3, since 32-row offsets leave bits 2-3 alone
   const int sw = ((lane & 31) >> 2) & 3;
   const int arow = (wr * 32 + (lane & 31)) * H8_LD;
-  const int brow = H8_ABUF + (wc * 32 + (lane & 31)) * H8_LD;
+  const int brow = H8_BUF + (wc * 64 + (lane & 31)) * H8_LD;
   const int koff[2] = {(((lane >> 5) + 0) ^ sw) << 4, (((lane >> 5) + 2) ^ sw) << 4};
   fetch(0);
   stash(0);
@@ -416,17 +416,25 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
     const int8_t* base = sm[k & 1];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      i4v av[4], bv[4];
+      i4v av[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < 4; ++q)
         av[q] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + arow + koff[kh]);
-        bv[q] = *reinterpret_cast<const i4v*>(base + q * (H8_TN * H8_LD) + brow + koff[kh]);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        i4v bv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bv[q] = *reinterpret_cast<const i4v*>(base + q * (GT * H8_LD) + brow + cb * 32 * H8_LD +
+                                                koff[kh]);
+#pragma unroll
+        for (int da = 0; da < 4; ++da)
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            if (da + db < H8_ORD)
+              acc[cb][da + db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[da], bv[db],
+                                                                       acc[cb][da + db], 0, 0, 0);
       }
-#pragma unroll
-      for (int da = 0; da < 4; ++da)
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[da + db] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[da], bv[db], acc[da + db], 0, 0, 0);
     }
     // unconditional, so that the load counters stay in issue order on every
     // path (after the last chunk this fills the idle buffer)
@@ -434,41 +442,45 @@ __global__ __launch_bounds__(512, 1) void h8_tile_kernel(const int8_t* __restric
     fetch(k + 2);
     __syncthreads();
   }
-  // S_fg = 2^(e_f + e_g - 60) * sum_s 2^(48 - 8 s) T_s, smallest terms first
-  const int c = wc * 32 + (lane & 31);  // column inside this workgroup's 64
-  const int ec = exps[fb + c];
+  // S_fg = 2^(e_f + e_g - 60) * sum_{s<=4} 2^(48 - 8 s) T_s, smallest terms first
   const int canon = ta * nt - ta * (ta - 1) / 2 + (tb - ta);  // row-major triangle order
   const int ntiles = nt * (nt + 1) / 2;
   double* P = part ? part + ((int64_t)split * ntiles + canon) * (GT * GT) : nullptr;
 #pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    const int r = wr * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
-    const int er = exps[fa + r];
-    double t = (double)acc[6][x];
+  for (int cb = 0; cb < 2; ++cb) {
+    const int c = wc * 64 + cb * 32 + (lane & 31);  // column inside the tile
+    const int ec = exps[fb + c];
 #pragma unroll
-    for (int o = 5; o >= 0; --o) t += __builtin_ldexp((double)acc[o][x], 48 - 8 * o);
-    const double v = (er == H8_BAD || ec == H8_BAD) ? __builtin_nan("")
-                                                    : __builtin_ldexp(t, er + ec - 60);
-    if (P) {
-      P[r * GT + half * H8_TN + c] = v;
-    } else if (fa + r < dim && fb + c < dim) {
-      double* d = S + (fa + r) * lds + fb + c;
-      const double o = acc_old ? *d + v : v;
-      *d = o;
-      // a diagonal 128-tile is written whole by its two halves (the two
-      // triangles are exact integer sums, so they agree bit for bit)
-      if (ta != tb) S[(fb + c) * lds + fa + r] = o;
+    for (int x = 0; x < 16; ++x) {
+      const int r = wr * 32 + 8 * (x >> 2) + 4 * (lane >> 5) + (x & 3);
+      const int er = exps[fa + r];
+      double t = __builtin_ldexp((double)acc[cb][H8_ORD - 1][x], 48 - 8 * (H8_ORD - 1));
+#pragma unroll
+      for (int o = H8_ORD - 2; o >= 0; --o)
+        t += __builtin_ldexp((double)acc[cb][o][x], 48 - 8 * o);
+      const double v = (er == H8_BAD || ec == H8_BAD) ? __builtin_nan("")
+                                                      : __builtin_ldexp(t, er + ec - 60);
+      if (P) {
+        P[r * GT + c] = v;
+      } else if (fa + r < dim && fb + c < dim) {
+        double* d = S + (fa + r) * lds + fb + c;
+        const double o = acc_old ? *d + v : v;
+        *d = o;
+        // a diagonal tile is written whole (its two triangles are exact
+        // integer sums of the same products, so they agree bit for bit)
+        if (ta != tb) S[(fb + c) * lds + fa + r] = o;
+      }
     }
   }
 }
 
-// Token splits: only while the tile halves (one workgroup each, one
-// workgroup per CU) number fewer than two rounds of the GPU, and whenever a
-// workgroup would otherwise take more than H8_MAXTOK tokens.
+// Token splits: only while the tiles (one workgroup each, one workgroup per
+// CU) number fewer than two rounds of the GPU, and whenever a workgroup would
+// otherwise take more than H8_MAXTOK tokens.
 static void h8_plan(int64_t dim, int64_t n, int& nt, int& ntiles, int& nsplit, int64_t& tps) {
   nt = (int)cdiv(dim, GT);
   ntiles = nt * (nt + 1) / 2;
-  int64_t want = cdiv(512, 2 * ntiles);
+  int64_t want = cdiv(512, ntiles);
   int64_t cap_tok = n / 512;
   if (want > cap_tok) want = cap_tok;
   if (want > 64) want = 64;
@@ -485,7 +497,7 @@ struct H8Layout {
   H8Layout(int64_t dim, int64_t n) {
     h8_plan(dim, n, nt, ntiles, nsplit, tps);
     const int ng = (int)cdiv(nt, H8_GRP);
-    nslots = ng * (ng + 1) / 2 * H8_GRP * H8_GRP * 2;
+    nslots = ng * (ng + 1) / 2 * H8_GRP * H8_GRP;
     dpad = round_up(dim, GT);
     npad = round_up(n, H8_KB);
     off_exps = round_up(dpad * 4, 256);

@@ -145,18 +145,19 @@ def test_fullsize_sampled(wname):
         for c in calls:
             e = R8.col_exponent(c)[ucols]
             cu = c[:, ucols]
-            t, mg = R8.fixed_point_gram(cu, e=e)
+            t, mg = R8.split8_gram(cu, e=e)
             Tref += t
             Tmag += mg
-            Tbnd += R8.rounding_bound(cu, e=e)
+            Tbnd += R8.split8_bound(cu, e=e)
     worst = 0.0
     for k, (f, g) in enumerate(pairs):
         exact = O.hessian_entry(X, f, g)
         mag = float(np.abs(X[:, f].astype(F64) * X[:, g].astype(F64)).sum())
         err = abs(Sg[k] - exact)
         if split8:
-            # X~^T X~ summed exactly per chunk; the library adds 7 digit
-            # orders, the chunk to S, and rounds each
+            # the split8 sum (X~^T X~ without the digit orders 5 and 6)
+            # exactly per chunk; the library adds 5 digit orders, the chunk
+            # to S, and rounds each
             i, j = pos[f], pos[g]
             ref, rmag, bnd = Tref[i, j], Tmag[i, j], Tbnd[i, j]
             assert abs(Sg[k] - ref) <= (24 + len(calls)) * 2.0 ** -53 * rmag, (f, g)
@@ -173,7 +174,7 @@ def test_fullsize_sampled(wname):
     # ---- diag, damping, act-order
     say(f"{wname}: diagonal and act-order")
     if split8:
-        d = sum(R8.fixed_point_diag(c) for c in calls)
+        d = sum(R8.split8_diag(c) for c in calls)
         nn = sum(c.shape[0] for c in calls)
     else:
         d, nn = O.hessian_diag(host_chunks(X))
@@ -191,7 +192,7 @@ def test_fullsize_sampled(wname):
     assert np.array_equal(perm[-TRAIL:], pr[-TRAIL:])
     cols_b = pr[-TRAIL:]
     if split8:  # chunk scales come from the full columns, which cols_b keeps
-        Sb = sum(R8.fixed_point_gram(c[:, cols_b], e=R8.col_exponent(c)[cols_b])[0]
+        Sb = sum(R8.split8_gram(c[:, cols_b], e=R8.col_exponent(c)[cols_b])[0]
                  for c in calls)
     else:
         Sb, _ = O.hessian_sum([c[:, cols_b] for c in host_chunks(X)])
