@@ -63,6 +63,9 @@ typedef enum {
                                            saturate to [0, 255] */
 #define GPTQ_FLAG_HESSIAN_SPLIT8 32u    /* gptq_hessian_accumulate: X^T X from int8 digit
                                            slices on the int8 matrix cores (see Step 1) */
+#define GPTQ_FLAG_FACTOR_FORM 64u       /* prepare / quantize: the factor of H itself in
+                                           place of U beyond U's diagonal blocks (see
+                                           Steps 2-3), no full triangular inverse */
 
 /* ---------------------------------------------------------------------------
  * Step 1 — Hessian statistics.  CHMC article, Schritt 2 (H from the layer's

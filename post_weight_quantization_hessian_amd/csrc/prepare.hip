@@ -73,8 +73,11 @@ __global__ __launch_bounds__(256) void prep_perm_kernel(const double* __restrict
   if (k < n && jl == 0) perm[rank] = (int32_t)k;
 }
 
-// Lower triangle of K (ip x ip, ld ip): K[a][b] = H[p_a][p_b], p_x = perm[n-1-x],
-// H = c*S + lam*I; the padding a, b >= n is the identity. `split` blocks
+// Lower triangle of K (ip x ip, ld ip): K[a][b] = H[p_a][p_b], p_x =
+// perm[n-1-(x-off)], H = c*S + lam*I; the padding (a, b < off or >= off + n)
+// is the identity. off = 0 puts the padding after the matrix; off = ip - n
+// before it, so that the 128-tiles of K end where the matrix ends and map to
+// 128-blocks of the sweep order that start at 0. `split` blocks
 // per row, each a contiguous range of b; the blocks of one row are
 // consecutive after the XCD remap, so they run on one XCD and the scattered
 // reads of the permuted S row are served from its L2. Large matrices take 8
@@ -86,22 +89,29 @@ __global__ __launch_bounds__(1024) void prep_gather_kernel(const double* __restr
                                                            int64_t ip, double c,
                                                            const double* __restrict__ lam_p,
                                                            const int32_t* __restrict__ perm,
-                                                           double* __restrict__ K, int split) {
+                                                           double* __restrict__ K, int split,
+                                                           int64_t off) {
   const int64_t lin = xcd_remap(blockIdx.x, gridDim.x);
   const int64_t a = lin / split;
   const int q = (int)(lin % split);
   const int64_t lo = (a + 1) * q / split, hi = (a + 1) * (q + 1) / split;
   const double lam = *lam_p;
   double* row = K + a * ip;
-  if (a >= n) {
+  const int64_t ra = a - off;
+  if (ra < 0 || ra >= n) {
     for (int64_t b = lo + threadIdx.x; b < hi; b += blockDim.x) row[b] = (a == b) ? 1.0 : 0.0;
     return;
   }
   // without perm: H itself in the original order (the min-pivot search)
-  const int64_t pa = perm ? perm[n - 1 - a] : a;
+  const int64_t pa = perm ? perm[n - 1 - ra] : ra;
   const double* srow = S + pa * n;
   for (int64_t b = lo + threadIdx.x; b < hi; b += blockDim.x) {
-    const int64_t pb = perm ? perm[n - 1 - b] : b;
+    const int64_t rb = b - off;
+    if (rb < 0) {
+      row[b] = 0.0;
+      continue;
+    }
+    const int64_t pb = perm ? perm[n - 1 - rb] : rb;
     double v = c * srow[pb];
     if (a == b) v += lam;
     row[b] = v;
@@ -899,6 +909,29 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
   }
 }
 
+// The factor form (K front-padded: sweep index j is row ip-1-j of K):
+//   M[j][k] = U[j][k]  where j and k are in the same 128-block (U's diagonal
+//             block: the inverse of the tile of L in Xb, reversed),
+//   M[j][k] = L[ip-1-j][ip-1-k] = (U^-1)[j][k]  for k in a later block,
+// 0 below the diagonal; fp32. U^-1 = J L J is the upper factor of H itself
+// (H_p = U^-1 U^-T).
+__global__ __launch_bounds__(256) void prep_mout_kernel(const double* __restrict__ K,
+                                                        const double* __restrict__ Xb, int64_t ld,
+                                                        int64_t n, float* __restrict__ M) {
+  const int64_t ip = ld;
+  for (int64_t j = blockIdx.y; j < n; j += gridDim.y) {
+    const int64_t a = ip - 1 - j;
+    const double* kr = K + a * ld;
+    const double* xr = Xb + a * ld;
+    const int64_t blk_end = (j / GT + 1) * GT;  // first column of the next block
+    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; k < n;
+         k += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t b = ip - 1 - k;
+      M[j * n + k] = k < j ? 0.0f : (float)(k < blk_end ? xr[b] : kr[b]);
+    }
+  }
+}
+
 // U[j][k] = Z[n-1-k][n-1-j] (k >= j), 0 below the diagonal; fp32. One 64x64
 // tile of U per workgroup, staged through LDS so that the reads of Z and the
 // writes of U both run along rows.
@@ -1423,7 +1456,10 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   if (in_features == 0) return GPTQ_OK;
   if (!S || !perm || !U || n_tokens_total <= 0 || !(damp >= 0.0) || !std::isfinite(damp))
     return GPTQ_EINVAL;
-  if (flags & ~(GPTQ_FLAG_ACT_ORDER | GPTQ_FLAG_MIN_PIVOT | GPTQ_FLAG_NO_SYNC)) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_ACT_ORDER | GPTQ_FLAG_MIN_PIVOT | GPTQ_FLAG_NO_SYNC |
+                GPTQ_FLAG_FACTOR_FORM))
+    return GPTQ_EINVAL;
+  const bool fac = (flags & GPTQ_FLAG_FACTOR_FORM) != 0;
   if ((flags & GPTQ_FLAG_ACT_ORDER) && (flags & GPTQ_FLAG_MIN_PIVOT)) return GPTQ_EINVAL;
   if (in_features > (int64_t)1 << 20) return GPTQ_EINVAL;
   const PrepLayout L = prep_layout(in_features);
@@ -1458,7 +1494,7 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     const bool panel = nwgp <= MP_PANEL_MAX_WG && mp_panel_fits(nwgp);
     GPTQ_LAUNCH(K_PREP_GATHER, st,
                 prep_gather_kernel<<<(unsigned)(ip * gsplit), gthreads, 0, st>>>(
-                    S, n, ip, c, lam, nullptr, K, gsplit));
+                    S, n, ip, c, lam, nullptr, K, gsplit, 0));
     GPTQ_LAUNCH(K_MP_STEP, st,
                 mp_init_kernel<<<nwg, 256, 0, st>>>(K, ip, n, ip, md, Pt, mv, mi, perm));
     if (panel) {  // no tag of an earlier call may match
@@ -1497,8 +1533,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                     hd, n, (flags & GPTQ_FLAG_ACT_ORDER) != 0, perm));
   }
   GPTQ_LAUNCH(K_PREP_GATHER, st,
-              prep_gather_kernel<<<(unsigned)(ip * gsplit), gthreads, 0, st>>>(S, n, ip, c, lam,
-                                                                               perm, K, gsplit));
+              prep_gather_kernel<<<(unsigned)(ip * gsplit), gthreads, 0, st>>>(
+                  S, n, ip, c, lam, perm, K, gsplit, fac ? ip - n : 0));
   // Blocked Cholesky, one stream. Per panel p: solve the panel's column
   // (trsm), update the next panel's tile column, then one launch that
   // factors the next diagonal block beside the rest of the trailing update.
@@ -1519,7 +1555,8 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   // such tile is read and written once per group. (Column c gets the
   // group's panels up to c - 2 at panel c - 2, and the panels after that
   // from the column updates; a group cut short by the end leaves no tile.)
-  const bool fused = nt <= CHOL_FUSE_NT;
+  // the factor form needs no inverse beyond the diagonal tiles
+  const bool fused = !fac && nt <= CHOL_FUSE_NT;
   int sov = 0, sov0 = 0;  // trailing tiles of the previous panel for this column update
   int kpo = 1;            // panels those tiles take
   GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
@@ -1552,6 +1589,12 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
                 chol_trsm_kernel<<<2 * nt, 256, 0, st>>>(K, Dd, Xb, ip, nt - 1, 0));
   } else {
     GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
+  }
+  if (fac) {
+    dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)std::min<int64_t>(n, 65535));
+    GPTQ_LAUNCH(K_PREP_UOUT, st, prep_mout_kernel<<<grid, 256, 0, st>>>(K, Xb, ip, n, U));
+    if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;
+    return gptq_workspace_status(ws, stream);
   }
   for (int h = 1; h < nt && !fused; h *= 2) {
     const int tiles = level_tiles(h, nt);

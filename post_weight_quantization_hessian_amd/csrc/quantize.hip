@@ -378,7 +378,15 @@ __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 // min-max one, zero point 0, no clipping (the caller passes clip = false);
 // the level k goes to ovals (int16 bits) at the original column, and a level
 // beyond the int16 range is reported (ST_NONFINITE).
-template <int GS, int MODE, int RPL>
+// FAC (MODE 0 only), the factor form: beyond the block's diagonal, the
+// matrix passed holds the factor of H itself, M = U^-1 (upper, H_p = M M^T),
+// and E holds the residuals q - w of the original weights, so the update
+// GEMM leaves sum = (Q - W)[:, :j0] M[:j0, blk]. Since E = (W - Q) U^-1 (the
+// errors are the residuals through U^-1), the block's current values are
+//   W~ = W - E[:, :j0] U[:j0, blk] = W - sum * U[blk, blk]
+// (the blocks of E U^-1 U above the block's rows vanish, U being upper), a
+// product with the block's own diagonal block of U, which the slab holds.
+template <int GS, int MODE, int RPL, bool FAC = false>
 __global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
     const double* __restrict__ part, int P, int64_t part_stride,
@@ -399,6 +407,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   // of this array before the slab is staged.
   __shared__ double Us[QB * QB + 3 * QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
+  __shared__ double udiag[FAC ? QB : 1];  // U[j][j]
   if ((int)blockIdx.x >= nsweep) {
     // workgroups past the sweep's own (256 threads each): the next block's
     // update GEMM over the errors of the blocks before this one, l < gk_end,
@@ -462,6 +471,14 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
                     ? (wblk ? wblk[r[p] * QB + c] : f16_to_f64(W[r[p] * ldw + j0 + c]))
                     : 0.0;
     }
+  // the original weights (fp16 values, exact in fp32) for the residuals
+  float w0[RPL][FAC ? 8 : 1];
+  if constexpr (FAC) {
+#pragma unroll
+    for (int p = 0; p < RPL; ++p)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) w0[p][s] = (float)w[p][s];
+  }
   double acc[RPL][8];
 #pragma unroll
   for (int p = 0; p < RPL; ++p)
@@ -544,7 +561,9 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       }
   }
   for (int j = t; j < QB; j += nthr) {
-    rdiag[j] = j < bw ? 1.0 / (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
+    const double ujj = j < bw ? (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
+    rdiag[j] = j < bw ? 1.0 / ujj : 0.0;
+    if constexpr (FAC) udiag[j] = ujj;
     Us[QB * QB + j] = 0.0;
     Us[QB * QB + QB + j] = 0.0;
     Us[QB * QB + 2 * QB + j] = 0.0;
@@ -589,15 +608,66 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     }
   }
   bool finite = true;
+  if constexpr (!FAC) {
 #pragma unroll
-  for (int p = 0; p < RPL; ++p)
+    for (int p = 0; p < RPL; ++p)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] - acc[p][s] : 0.0;
-      finite = finite && isfinite(w[p][s]);
-    }
-  if (!finite) atomicOr(status, ST_NONFINITE);
+      for (int s = 0; s < 8; ++s) {
+        w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] - acc[p][s] : 0.0;
+        finite = finite && isfinite(w[p][s]);
+      }
+    if (!finite) atomicOr(status, ST_NONFINITE);
+  }
   __syncthreads();
+  if constexpr (FAC) {
+    // t = sum * U[blk, blk] by rows: t_l = U_ll sum_l + sum_{k<l} (U_kk sum_k)
+    // (U_kl / U_kk), the slab holding U_kl / U_kk above its diagonal; sum_k
+    // of column k = 16 m + (k % 16) is slot m of lane k % 16, broadcast to
+    // its row, and reaches the slots m.. 7 (the columns after it).
+    double t2[RPL][8];
+    if (j0 > 0) {
+      double sp[RPL][8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const double ud = udiag[16 * s + q];
+#pragma unroll
+        for (int p = 0; p < RPL; ++p) {
+          sp[p][s] = acc[p][s] * ud;
+          t2[p][s] = sp[p][s];
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const double* urow = Us + (16 * m + kk) * QB + q;
+          double u[8];
+#pragma unroll
+          for (int s = m; s < 8; ++s) u[s] = urow[16 * s];
+          double db[RPL];
+#pragma unroll
+          for (int p = 0; p < RPL; ++p) db[p] = row_bcast_mov_i(sp[p][m], kk);
+#pragma unroll
+          for (int s = m; s < 8; ++s)
+#pragma unroll
+            for (int p = 0; p < RPL; ++p) t2[p][s] = fma(db[p], u[s], t2[p][s]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < RPL; ++p)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) t2[p][s] = 0.0;
+    }
+#pragma unroll
+    for (int p = 0; p < RPL; ++p)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        w[p][s] = (rv[p] && 16 * s + q < bw) ? (double)w0[p][s] - t2[p][s] : 0.0;
+        finite = finite && isfinite(w[p][s]);
+      }
+    if (!finite) atomicOr(status, ST_NONFINITE);
+  }
 
   double scale[RPL], rscale[RPL], zero[RPL], loss[RPL];
   double nout[RPL];  // SSQR: outliers of this lane's columns
@@ -750,7 +820,12 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
           if (o_own) d_own = v - h_own;
           const double e = d_own * rdiag[c];
           codes[r[p] * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero[p], 0.0), 255.0);
-          E[r[p] * lde + j0 + c] = (float)e;
+          if constexpr (FAC) {
+            // the residual q - w of the original weight (exact in fp64)
+            E[r[p] * lde + j0 + c] = (float)fma(scale[p], k_own, -(double)w0[p][0]);
+          } else {
+            E[r[p] * lde + j0 + c] = (float)e;
+          }
           loss[p] += e * e;
           if (SSQR || HPTQ) {
             const int64_t oc = operm ? (int64_t)operm[j0 + c] : j0 + c;
@@ -774,6 +849,11 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
 #pragma unroll
       for (int s = 0; s < 7; ++s) w[p][s] = w[p][s + 1];
       w[p][7] = 0.0;
+      if constexpr (FAC) {
+#pragma unroll
+        for (int s = 0; s < 7; ++s) w0[p][s] = w0[p][s + 1];
+        w0[p][7] = 0.0f;
+      }
     }
   }
 #pragma unroll
@@ -878,23 +958,26 @@ struct SweepArgs {
   const int32_t* operm;
   int64_t cols;
   unsigned long long* ocount;
+  bool fac;  // the factor form (mode 0 only)
 };
 
 template <int GS>
 static gptq_status launch_sweep(hipStream_t st, const SweepArgs& a) {
-#define Q_SWEEP(SS, RP)                                                                        \
+#define Q_SWEEP(SS, RP, FC)                                                                    \
   GPTQ_LAUNCH(K_Q_SWEEP, st,                                                                   \
-              (q_sweep_kernel<GS, SS, RP><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(              \
+              (q_sweep_kernel<GS, SS, RP, FC><<<a.nsweep + a.ng, 64 * a.nw, 0, st>>>(          \
                   a.W, a.ldw, a.wblk, a.part, a.P, a.pstride, a.U, a.ldu, a.vecU, a.rows, a.j0, \
                   a.bw, a.bits, a.E, a.lde, a.codes, a.ldc, a.scales, a.zeros, a.ldg,          \
                   a.row_loss, a.status, a.clip, a.late, a.nsweep, a.gj0, a.gbw, a.gks,         \
                   a.gk_end, a.gpart, a.alpha, a.omask, a.ovals, a.operm, a.cols, a.ocount)))
   if (a.rpl == 2) {  // the plain sweep only (the SSQR/HPTQ state of two rows spills)
-    Q_SWEEP(0, 2);
+    if (a.fac) Q_SWEEP(0, 2, true);
+    else Q_SWEEP(0, 2, false);
   } else {
-    if (a.mode == 1) Q_SWEEP(1, 1);
-    else if (a.mode == 2) Q_SWEEP(2, 1);
-    else Q_SWEEP(0, 1);
+    if (a.mode == 1) Q_SWEEP(1, 1, false);
+    else if (a.mode == 2) Q_SWEEP(2, 1, false);
+    else if (a.fac) Q_SWEEP(0, 1, true);
+    else Q_SWEEP(0, 1, false);
   }
 #undef Q_SWEEP
   return GPTQ_OK;
@@ -911,7 +994,8 @@ extern "C" size_t gptq_quantize_workspace_bytes(int64_t rows, int64_t cols, int 
   return q_layout(rows, cols, group_size).total;
 }
 
-// The whole sweep of a layer; alpha > 0 runs the SSQR rule with its outputs.
+// The whole sweep of a layer; mode 1 (SSQR) and 2 (HPTQ) run those rules
+// with their outputs at alpha; mode 3 is the plain sweep in the factor form.
 // Arguments are validated by the callers; returns after enqueueing.
 static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t cols, int64_t ldw,
                                     const float* U, const int32_t* perm, int bits, int group_size,
@@ -919,6 +1003,8 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
                                     int32_t* g_idx, double* row_loss, int mode, double alpha,
                                     uint8_t* omask, uint16_t* ovals, void* ws,
                                     hipStream_t st) {
+  const bool fac = mode == 3;
+  if (fac) mode = 0;
   const QLayout L = q_layout(rows, cols, group_size);
   char* base = (char*)ws;
   unsigned* status = (unsigned*)(base + L.off_status);
@@ -1002,15 +1088,16 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
         GPTQ_LAUNCH(K_Q_GEMM, st,
                     q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0,
                                                         bw, 0, ks, j0, pc, pstride, 0,
-                                                        P == 1 ? wblk : nullptr, vecU));
-        // one split: the GEMM wrote W~ itself; else the sweep sums the partials
-        if (P == 1) cur = wblk;
+                                                        P == 1 && !fac ? wblk : nullptr, vecU));
+        // one split: the GEMM wrote W~ itself; else (and always in the factor
+        // form, whose sweep turns the sum into W~) the sweep sums the partials
+        if (P == 1 && !fac) cur = wblk;
         else nparts = P;
       }
     }
     SweepArgs a{nw, rpl, nsweep, 0, Wsrc, ldws, cur, pc, nparts, pstride, U, cols, vecU, rows, j0,
                 bw, bits, E, L.lde, csw, cols, scales, zeros, L.ng, row_loss, status, clip,
-                late, 0, 0, 0, 0, pn, mode, alpha, omask, ovals, perm, cols, ocount};
+                late, 0, 0, 0, 0, pn, mode, alpha, omask, ovals, perm, cols, ocount, fac};
     ep = emb_max > 0 ? 0 : -1;
     if (emb_max > 0 && j0 > 0 && j0 + QB < cols) {
       // next block's sum over l < j0 (the errors of blocks < b), in as few
@@ -1071,13 +1158,14 @@ extern "C" gptq_status gptq_quantize_layer(const uint16_t* W, int64_t rows, int6
                                            uint16_t* scales, uint16_t* zeros, int32_t* g_idx,
                                            double* row_loss, void* ws, size_t ws_bytes,
                                            void* stream) {
-  if (flags & ~(GPTQ_FLAG_NO_SYNC | GPTQ_FLAG_NO_CLIP)) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_NO_SYNC | GPTQ_FLAG_NO_CLIP | GPTQ_FLAG_FACTOR_FORM)) return GPTQ_EINVAL;
   gptq_status c = quantize_check(W, rows, cols, ldw, U, bits, group_size, codes, scales, zeros,
                                  row_loss);
   if (c != GPTQ_OK || rows == 0 || cols == 0) return c;
   if (!ws || ws_bytes < q_layout(rows, cols, group_size).total) return GPTQ_EWORKSPACE;
   c = quantize_enqueue(W, rows, cols, ldw, U, perm, bits, group_size,
-                       !(flags & GPTQ_FLAG_NO_CLIP), codes, scales, zeros, g_idx, row_loss, 0, 0.0,
+                       !(flags & GPTQ_FLAG_NO_CLIP), codes, scales, zeros, g_idx, row_loss,
+                       (flags & GPTQ_FLAG_FACTOR_FORM) ? 3 : 0, 0.0,
                        nullptr, nullptr, ws, (hipStream_t)stream);
   if (c != GPTQ_OK) return c;
   if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;

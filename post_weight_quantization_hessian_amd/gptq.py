@@ -26,6 +26,7 @@ GPTQ_FLAG_NO_SYNC = 4
 GPTQ_FLAG_MIN_PIVOT = 8
 GPTQ_FLAG_NO_CLIP = 16
 GPTQ_FLAG_HESSIAN_SPLIT8 = 32
+GPTQ_FLAG_FACTOR_FORM = 64
 
 EXPORTS = {
     "gptq_hessian_workspace_bytes": (C.c_size_t, [C.c_int64, C.c_int64]),
@@ -195,9 +196,12 @@ def prepare_workspace_bytes(in_features: int) -> int:
 
 
 def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
-                 workspace=None, out=None, sync: bool = True, min_pivot: bool = False):
+                 workspace=None, out=None, sync: bool = True, min_pivot: bool = False,
+                 factor_form: bool = False):
     """Damped, optionally act-ordered (or min-pivot-ordered) Hessian ->
-    (perm int32 [i], U fp32 [i x i]).
+    (perm int32 [i], U fp32 [i x i]). ``factor_form=True`` returns the mixed
+    matrix of the factor form instead of U (U's 128-wide diagonal blocks, the
+    factor U^-1 of H beyond them), for quantize_layer(..., factor_form=True).
     ``sync=False`` returns after enqueueing; check with workspace_status()."""
     torch = _torch()
     _need(S, torch.float64, "S", 2)
@@ -212,7 +216,8 @@ def prepare_hinv(S, n_tokens: int, damp: float = 0.01, act_order: bool = False,
     if workspace is None:
         workspace = _workspace(prepare_workspace_bytes(i), S.device)
     flags = ((GPTQ_FLAG_ACT_ORDER if act_order else 0) | (GPTQ_FLAG_MIN_PIVOT if min_pivot else 0)
-             | (0 if sync else GPTQ_FLAG_NO_SYNC))
+             | (0 if sync else GPTQ_FLAG_NO_SYNC)
+             | (GPTQ_FLAG_FACTOR_FORM if factor_form else 0))
     st = lib.gptq_prepare_hinv(_ptr(S), i, int(n_tokens), float(damp), flags, _ptr(perm), _ptr(U),
                                _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_prepare_hinv")
@@ -237,11 +242,12 @@ def quantize_workspace_bytes(rows: int, cols: int, group_size: int) -> int:
 
 
 def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, workspace=None,
-                   out=None, sync: bool = True, clip: bool = True):
+                   out=None, sync: bool = True, clip: bool = True, factor_form: bool = False):
     """Sweep the fp16 weights W [rows x cols] with the factor U (and perm).
     ``out`` may be a QuantizedLayer whose tensors are reused; ``sync=False``
     returns after enqueueing (check with workspace_status()); ``clip=False``
-    is the no-clipping regime (stored codes saturate to [0, 255])."""
+    is the no-clipping regime (stored codes saturate to [0, 255]);
+    ``factor_form=True`` takes U from prepare_hinv(..., factor_form=True)."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(U, torch.float32, "U", 2)
@@ -271,7 +277,8 @@ def quantize_layer(W, U, perm=None, bits: int = 4, group_size: int = 128, worksp
     st = lib.gptq_quantize_layer(_ptr(W), rows, cols, W.stride(0) if rows > 0 else cols, _ptr(U),
                                  _ptr(perm), int(bits), int(group_size),
                                  (0 if sync else GPTQ_FLAG_NO_SYNC)
-                                 | (0 if clip else GPTQ_FLAG_NO_CLIP), _ptr(codes),
+                                 | (0 if clip else GPTQ_FLAG_NO_CLIP)
+                                 | (GPTQ_FLAG_FACTOR_FORM if factor_form else 0), _ptr(codes),
                                  _ptr(scales), _ptr(zeros), _ptr(g_idx), _ptr(row_loss),
                                  _ptr(workspace), workspace.numel(), _stream())
     _check(st, "gptq_quantize_layer")

@@ -44,13 +44,16 @@ def torch_empty_bytes(nbytes, device):
 
 class LayerGroup:
     def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
-                 device, min_pivot=False, hessian="exact", clip=True):
+                 device, min_pivot=False, hessian="exact", clip=True, factor_form=True):
         import torch
         self.dim, self.rows = int(dim), int(rows)
         self.bits, self.group_size = tuple(bits), int(group_size)
         self.act_order, self.damp = bool(act_order), float(damp)
         self.min_pivot = bool(min_pivot)  # the min-pivot order instead of act-order
         self.clip = bool(clip)  # False: the no-clipping sweep (codes may leave [0, maxq])
+        # the plain sweep in the factor form (U's diagonal blocks and the factor
+        # of H beyond them); SSQR, HPTQ and CHMC take U itself
+        self.factor_form = bool(factor_form)
         if self.min_pivot:
             self.act_order = False
         ng = -(-self.dim // self.group_size)
@@ -76,7 +79,7 @@ class LayerGroup:
             torch.empty(self.rows, dtype=torch.float64, device=device), b, self.group_size)
             for b in self.bits]
 
-    def _factor(self, chunks):
+    def _factor(self, chunks, factor_form=False):
         n = 0
         self.n = 0
         for ci, c in enumerate(chunks):
@@ -86,18 +89,21 @@ class LayerGroup:
         self.n = n
         G.prepare_hinv(self.S, n, damp=self.damp, act_order=self.act_order,
                        workspace=self.pws, out=(self.perm, self.U), sync=False,
-                       min_pivot=self.min_pivot)
+                       min_pivot=self.min_pivot, factor_form=factor_form)
 
     def enqueue(self, chunks, W):
         """The whole path for token chunks ``chunks`` (fp32 [n_c x dim] each)
-        and stacked fp16 weights ``W`` [rows x dim], without synchronizing."""
-        self._factor(chunks)
+        and stacked fp16 weights ``W`` [rows x dim], without synchronizing.
+        The sweep runs in the factor form (no inverse of the factor beyond
+        its 128-wide diagonal blocks) unless ``factor_form`` is off."""
+        self._factor(chunks, factor_form=self.factor_form)
         self._swept = True
         for bi, b in enumerate(self.bits):
             G.quantize_layer(W, self.U, self.perm if (self.act_order or self.min_pivot) else None,
                              bits=b,
                              group_size=self.group_size, workspace=self.qws[bi],
-                             out=self.outs[bi], sync=False, clip=self.clip)
+                             out=self.outs[bi], sync=False, clip=self.clip,
+                             factor_form=self.factor_form)
         return self.outs
 
     def ssqr(self, chunks, W, target, iters=12):

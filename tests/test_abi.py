@@ -97,6 +97,10 @@ def test_invalid_arguments_rejected_on_host():
     assert q(ws=NULL) == g.GPTQ_EWORKSPACE
     assert q(wsb=16) == g.GPTQ_EWORKSPACE
     assert q(flags=8) == g.GPTQ_EINVAL
+    assert q(flags=128) == g.GPTQ_EINVAL
+    # the factor form is a flag of the plain sweep (its size checks still apply)
+    assert q(flags=g.GPTQ_FLAG_FACTOR_FORM, ws=NULL) == g.GPTQ_EWORKSPACE
+    assert q(flags=g.GPTQ_FLAG_FACTOR_FORM, bits=1) == g.GPTQ_EINVAL
     assert q(rows=0) == g.GPTQ_OK and q(cols=0) == g.GPTQ_OK  # empty: no-op
     assert L.gptq_workspace_status(NULL, NULL) == g.GPTQ_EINVAL
     # prepare
@@ -110,6 +114,10 @@ def test_invalid_arguments_rejected_on_host():
     assert pw(FAKE, 8, 10, 0.01, 9, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, 0.01, 2, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 8, 10, 0.01, 0, FAKE, FAKE, FAKE, 64, NULL) == g.GPTQ_EWORKSPACE
+    ff = g.GPTQ_FLAG_FACTOR_FORM
+    assert pw(FAKE, 8, 10, 0.01, ff, FAKE, FAKE, FAKE, 64, NULL) == g.GPTQ_EWORKSPACE
+    assert pw(FAKE, 8, 10, 0.01, ff | 128, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
+    assert pw(FAKE, 8, 10, 0.01, ff | 9, FAKE, FAKE, FAKE, 1 << 40, NULL) == g.GPTQ_EINVAL
     assert pw(FAKE, 0, 10, 0.01, 0, NULL, NULL, NULL, 0, NULL) == g.GPTQ_OK
     # hessian
     ha = L.gptq_hessian_accumulate
@@ -141,6 +149,7 @@ def test_ssqr_arguments_rejected_on_host():
     assert qs(alpha=17.0) == g.GPTQ_EINVAL
     assert qs(alpha=float("nan")) == g.GPTQ_EINVAL
     assert qs(flags=g.GPTQ_FLAG_NO_CLIP) == g.GPTQ_EINVAL  # its own rule replaces clipping
+    assert qs(flags=g.GPTQ_FLAG_FACTOR_FORM) == g.GPTQ_EINVAL  # U itself only
     assert qs(flags=g.GPTQ_FLAG_NO_SYNC) == g.GPTQ_EINVAL  # a count needs a synchronize
     assert qs(mask=NULL) == g.GPTQ_EINVAL
     assert qs(ws=NULL, wsb=0) == g.GPTQ_EWORKSPACE
