@@ -124,7 +124,8 @@ def kernel_work(name, wl, plan, sweeps=1.0):
         # (2/3) 128^3 counted there) up to CHOL_MERGE_TILES (at least the m-1
         # tiles of the next column), the others beside the next panel's
         # column update. With the inverse accumulated in the factorization
-        # (nt <= CHOL_FUSE_NT), trsm also solves the p + 1 tiles of X's row
+        # (nt <= CHOL_FUSE_NT, never in the factor form, which needs no inverse
+        # beyond the diagonal tiles), trsm also solves the p + 1 tiles of X's row
         # block p (and the last row block after the loop), and the m (p + 1)
         # inverse tile updates of the step (2 128^3 each, half at j = p, where
         # the operand X_pp is triangular) fill the rest of the merged launch,
@@ -132,7 +133,7 @@ def kernel_work(name, wl, plan, sweeps=1.0):
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
-            fused = nt <= CHOL_FUSE_NT
+            fused = nt <= CHOL_FUSE_NT and not h.factor_form
             if name == "chol_potrf":
                 f += 2 * 128 ** 3 / 3.0  # panel 0
             if name == "chol_trsm" and fused:
@@ -161,7 +162,7 @@ def kernel_work(name, wl, plan, sweeps=1.0):
         f = 0.0
         for h in plan:
             nt = -(-h.dim // 128)
-            hh = 1 if nt > CHOL_FUSE_NT else nt
+            hh = nt if (h.factor_form or nt <= CHOL_FUSE_NT) else 1  # no doubling levels
             while hh < nt:
                 for q0 in range(0, nt, 2 * hh):
                     h2 = min(hh, nt - q0 - hh)
@@ -236,9 +237,11 @@ def quant_gemm_split(rows, cols):
 
 
 class HPlan:
-    def __init__(self, name, dim, n, rows, split8=False):
+    def __init__(self, name, dim, n, rows, split8=False, factor_form=False):
         self.name, self.dim, self.n, self.rows = name, dim, n, rows
         self.split8 = split8
+        # the plain sweep's factor form: no inverse beyond the diagonal tiles
+        self.factor_form = factor_form
 
 
 # ---------------------------------------------------------------- HBM traffic
@@ -488,7 +491,10 @@ def main():
                          clip=not args.no_clip,
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
-        plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0], split8=grp.split8))
+        # the plain sweep takes the factor form; SSQR, HPTQ and CHMC take U
+        grp.factor_form = args.ssqr is None and args.hptq is None and args.chmc is None
+        plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0], split8=grp.split8,
+                          factor_form=grp.factor_form))
         layer_rows[h.name] = [(l.name, l.rows) for l in wl.layers_of(h.name)]
     torch.cuda.synchronize()
 
