@@ -27,6 +27,20 @@ CHMC_DAMP = 0.05
 # tiles, either is a few microseconds)
 SPLIT8_MIN_DIM = 256
 
+# "auto" sweeps in the factor form above 48 panels of 128 features, where the
+# library's factor would otherwise run a separate triangular inverse (measured
+# 722 -> 599 ms per 70B-shape step); below, the inverse rides along inside the
+# factorization's own launches and U is taken as it is (the factor form's
+# per-block conversion measured 5.35 -> 5.73 ms per Qwen MLP step there)
+FACTOR_FORM_MIN_DIM = 48 * 128 + 1
+
+
+def factor_form_mode(mode, dim):
+    """True | False | 'auto' -> True when the plain sweep takes the factor form."""
+    if mode == "auto":
+        return dim >= FACTOR_FORM_MIN_DIM
+    return bool(mode)
+
 
 def hessian_mode(mode, dim):
     """'exact' | 'split8' | 'auto' -> True when the layer uses split8."""
@@ -44,7 +58,7 @@ def torch_empty_bytes(nbytes, device):
 
 class LayerGroup:
     def __init__(self, dim, rows, *, max_chunk_tokens, bits, group_size, act_order, damp,
-                 device, min_pivot=False, hessian="exact", clip=True, factor_form=True):
+                 device, min_pivot=False, hessian="exact", clip=True, factor_form="auto"):
         import torch
         self.dim, self.rows = int(dim), int(rows)
         self.bits, self.group_size = tuple(bits), int(group_size)
@@ -53,7 +67,7 @@ class LayerGroup:
         self.clip = bool(clip)  # False: the no-clipping sweep (codes may leave [0, maxq])
         # the plain sweep in the factor form (U's diagonal blocks and the factor
         # of H beyond them); SSQR, HPTQ and CHMC take U itself
-        self.factor_form = bool(factor_form)
+        self.factor_form = factor_form_mode(factor_form, self.dim)
         if self.min_pivot:
             self.act_order = False
         ng = -(-self.dim // self.group_size)
@@ -95,7 +109,9 @@ class LayerGroup:
         """The whole path for token chunks ``chunks`` (fp32 [n_c x dim] each)
         and stacked fp16 weights ``W`` [rows x dim], without synchronizing.
         The sweep runs in the factor form (no inverse of the factor beyond
-        its 128-wide diagonal blocks) unless ``factor_form`` is off."""
+        its 128-wide diagonal blocks) when ``factor_form`` says so. The bit
+        widths run one after the other on the current stream (a side stream
+        per extra bit width measured 599 -> 606 ms per 70B-shape step)."""
         self._factor(chunks, factor_form=self.factor_form)
         self._swept = True
         for bi, b in enumerate(self.bits):

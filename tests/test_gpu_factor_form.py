@@ -139,9 +139,10 @@ def test_factor_form_identity_hessian_is_rtn():
                                          ("tinyllama_block", "down_in"),
                                          ("smollm_q576", "x")])
 def test_factor_form_workload_layers(wname, hname):
-    """The benchmark's configuration (LayerGroup.enqueue: the Hessian mode of
-    the benchmark, the factor form, every bit width on one stream) against
-    the oracle's blocked sweep on the exact S."""
+    """The benchmark's launch configuration (LayerGroup.enqueue: the Hessian
+    mode of the benchmark, every bit width on one stream), here with the
+    factor form forced on (the benchmark takes it above 6144 features),
+    against the oracle's sweep on the exact S."""
     wl = WORKLOADS[wname]
     X, W = workload_inputs(wl, hname)
     dim = X.shape[1]
@@ -149,7 +150,7 @@ def test_factor_form_workload_layers(wname, hname):
               for s in range(0, X.shape[0], wl.token_chunk)]
     grp = LayerGroup(dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
                      bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
-                     damp=wl.damp, device=DEV, hessian="auto")
+                     damp=wl.damp, device=DEV, hessian="auto", factor_form=True)
     assert grp.factor_form and grp.split8 == hessian_mode("auto", dim)
     grp.enqueue(chunks, torch.from_numpy(W).to(DEV))
     grp.check()
