@@ -257,7 +257,8 @@ KERNEL_CLASS = {  # device function name -> timing class
     "trtri_diag_kernel": "trtri_diag", "q_gemm_kernel": "quant_gemm",
     "q_sweep_kernel": "quant_sweep",
     "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout",
-    "prep_uout_z_kernel": "prepare_uout", "mp_init_kernel": "minpivot_step",
+    "prep_uout_z_kernel": "prepare_uout", "prep_mout_kernel": "prepare_uout",
+    "mp_init_kernel": "minpivot_step",
     "mp_step_kernel": "minpivot_step", "mp_panel_kernel": "minpivot_step",
     "mp_update_kernel": "minpivot_update",
     "h8_tile_kernel": "hessian_split8", "h8_colmax_kernel": "hessian_digits",
@@ -295,6 +296,28 @@ def source_hash(csrc=None):
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
             h.update(_code_only(open(os.path.join(csrc, f), encoding="utf-8").read()).encode())
+    return h.hexdigest()
+
+
+def kernel_source_hash(kernel_class, csrc=None):
+    """sha256 over the code of the sources that define the kernels of one
+    timing class, and every header: a class's counters stay valid while
+    that code is unchanged (None if no source defines the class)."""
+    import hashlib
+    import re
+    csrc = csrc or CSRC
+    names = [k for k, c in KERNEL_CLASS.items() if c == kernel_class]
+    files = sorted(os.listdir(csrc))
+    code = {f: _code_only(open(os.path.join(csrc, f), encoding="utf-8").read()) for f in files
+            if f.endswith((".hip", ".h"))}
+    own = [f for f in files if f.endswith(".hip")
+           and any(re.search(rf"\b{n}\s*\(", code[f]) for n in names)]
+    if not own:
+        return None
+    h = hashlib.sha256()
+    for f in sorted(own) + [f for f in files if f.endswith(".h")]:
+        h.update(f.encode())
+        h.update(code[f].encode())
     return h.hexdigest()
 
 
@@ -337,7 +360,8 @@ def counters_summary(args):
         wb = write[k][0] * 1024.0 * w_fac
         kernels[k] = {"fetch_kib_per_dispatch": fetch[k][0], "write_kib_per_dispatch": write[k][0],
                       "dispatches": fetch[k][1], "bytes_per_launch": fb + wb,
-                      "read_bytes_per_launch": fb, "write_bytes_per_launch": wb}
+                      "read_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+                      "source_sha256": kernel_source_hash(k)}
     out = {"workload": args.workload, "source_sha256": source_hash(),
            "fetch_scale": f_fac, "write_scale": w_fac,
            "copy_reference": "bench.py --calibrate-copy 1024 (1 GiB device copy, 5 dispatches)",
@@ -354,14 +378,18 @@ def counters_summary(args):
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of ``kernel`` from the committed counter summary,
-    or None when there is none or the sources changed since it was taken."""
+    or None when there is none or the code of that kernel's sources (or of a
+    header) changed since it was taken."""
     try:
         d = json.load(open(traffic_path(workload)))
     except (OSError, ValueError):
         return None
-    if d.get("source_sha256") != source_hash() or kernel not in d.get("kernels", {}):
+    k = d.get("kernels", {}).get(kernel)
+    if k is None or k.get("source_sha256") is None:
         return None
-    return d["kernels"][kernel]["bytes_per_launch"]
+    if k["source_sha256"] != kernel_source_hash(kernel):
+        return None
+    return k["bytes_per_launch"]
 
 
 # ---------------------------------------------------------------- CPU oracle
