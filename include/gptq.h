@@ -128,6 +128,17 @@ gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
  *        factor with U^T U = (H[perm][:,perm])^-1, zeros below the diagonal.
  * Computed in fp64 (one Cholesky of the order-reversed permuted Hessian and
  * one triangular inverse), stored as fp32. S is read, never written.
+ * With GPTQ_FLAG_FACTOR_FORM the output in U is instead the matrix M that
+ * gptq_quantize_layer takes with the same flag (The Geometry of LLM
+ * Quantization 2.2: the nearest-plane step needs a triangular factor of the
+ * lattice's Gram matrix, here H itself):
+ *   M[j][k] = U[j][k]  for j <= k in the same 128-wide block of sweep
+ *                      positions (blocks start at 0; the last may be short),
+ *   M[j][k] = R[j][k]  for k in a later block, R = U^-1 the upper triangular
+ *                      factor with R R^T = H[perm][:,perm],
+ *   0 below the diagonal. R is the order-reversed Cholesky factor of the
+ * permuted H, so only the 128 x 128 diagonal blocks are inverted: no full
+ * triangular inverse runs. The flag combines with either order.
  * All work is enqueued on `stream`.
  * Workspace: gptq_prepare_workspace_bytes(in_features) bytes.
  * Synchronizes `stream` once at the end to read the factorisation status;
@@ -151,7 +162,9 @@ gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_to
  * U[j, j+1:]); the lazy form applies the update of a 128-column block to the
  * columns after it only when they are reached (same sums, other order).
  *   W     fp16 [rows x cols], leading dimension ldw (>= cols), original order.
- *   U     fp32 [cols x cols] from gptq_prepare_hinv (sweep order).
+ *   U     fp32 [cols x cols] from gptq_prepare_hinv (sweep order); with
+ *         GPTQ_FLAG_FACTOR_FORM the matrix M that gptq_prepare_hinv returns
+ *         with that flag (U's diagonal blocks, R = U^-1 beyond them).
  *   perm  int32[cols] from gptq_prepare_hinv, or NULL for the identity.
  *   bits  2..8; group_size one of 16, 32, 64, 128 (groups = group_size
  *         consecutive columns in sweep order; the last may be shorter).
@@ -174,7 +187,12 @@ gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_to
  * flags: 0, GPTQ_FLAG_NO_SYNC, GPTQ_FLAG_NO_CLIP (The Geometry of LLM
  * Quantization 2.3, the no-clipping regime of Satz 5: code = rint(v/scale) +
  * zero without the clamp; the errors, the propagation and row_loss use that
- * unclamped code, the stored byte is it saturated to [0, 255]). Synchronizes
+ * unclamped code, the stored byte is it saturated to [0, 255]),
+ * GPTQ_FLAG_FACTOR_FORM (the same sweep, carried differently: since the
+ * scaled errors are E = (W - Q) U^-1, the sum over the earlier blocks is
+ * formed from the residuals q - w of the original weights through R, and the
+ * block's current values are W - that sum times U's diagonal block; results
+ * agree with the plain form up to rounding). Synchronizes
  * `stream` at the end unless
  * GPTQ_FLAG_NO_SYNC; returns GPTQ_ENONFINITE if a weight is NaN/Inf or a
  * scale overflows fp16 (outputs are then unspecified).
