@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--hessian", choices=("auto", "exact", "split8"), default="auto",
                     help="Hessian products: exact fp64, int8 digit slices, or split8 from "
                          "256 input features on (auto)")
+    ap.add_argument("--factor-form", choices=("auto", "on", "off"), default="auto",
+                    help="the plain sweep in the factor form (no triangular inverse beyond "
+                         "the 128-wide diagonal blocks): from 768 features (auto), always "
+                         "or never")
     ap.add_argument("--no-clip", action="store_true",
                     help="the no-clipping sweep: levels are not clamped to [0, maxq]")
     ap.add_argument("--ssqr", type=float, default=None, metavar="TARGET",
@@ -516,6 +520,7 @@ def main():
         grp = LayerGroup(h.dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
                          bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
                          min_pivot=args.order == "min_pivot", hessian=args.hessian,
+                         factor_form={"auto": "auto", "on": True, "off": False}[args.factor_form],
                          clip=not args.no_clip,
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
@@ -710,9 +715,11 @@ def main():
                    "damp": CHMC_DAMP if args.chmc is not None else wl.damp,
                    "weights_per_step": weights,
                    "hessian": {h.name: ("split8" if h.split8 else "exact") for h in plan},
+                   "factor_form": {h.name: h.factor_form for h in plan},
                    "arithmetic": "Hessian: exact fp64 products, or (split8) int8 digit-slice "
                                  "products summed exactly in int32 and combined in fp64; "
-                                 "fp64 Cholesky/inverse and sweep, fp32 MFMA lazy update"},
+                                 "fp64 Cholesky (and, outside the factor form, inverse) and "
+                                 "sweep, fp32 MFMA lazy update"},
         "roofline": roofline,
         "ssqr": None if args.ssqr is None else {
             "target": args.ssqr, "iters": args.ssqr_iters, "sweeps_per_search": sweeps,

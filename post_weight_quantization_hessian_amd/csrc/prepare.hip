@@ -1557,13 +1557,17 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
   // from the column updates; a group cut short by the end leaves no tile.)
   // the factor form needs no inverse beyond the diagonal tiles
   const bool fused = !fac && nt <= CHOL_FUSE_NT;
+  // grouped trailing updates pay off where the trailing tiles are most of the
+  // work; up to CHOL_FUSE_NT panels (the factor form there) every panel
+  // applies its own update, as the fused form does, minus the inverse tiles
+  const int cgroup = nt <= CHOL_FUSE_NT ? 1 : CHOL_GROUP;
   int sov = 0, sov0 = 0;  // trailing tiles of the previous panel for this column update
   int kpo = 1;            // panels those tiles take
   GPTQ_LAUNCH(K_CHOL_POTRF, st, chol_potrf_kernel<<<1, 256, 0, st>>>(K, Dd, ip, 0, status));
   for (int p = 0; p + 1 < nt; ++p) {
     const int mt = nt - 1 - p;
-    const int r = p % CHOL_GROUP;
-    const bool col_only = !fused && r < CHOL_GROUP - 1;
+    const int r = p % cgroup;
+    const bool col_only = !fused && r < cgroup - 1;
     const int kp = fused ? 1 : r + 1;
     const int rest = col_only ? mt - 1 : (mt - 1) * mt / 2;
     const int xs = fused ? 2 * (p + 1) : 0;   // inverse row-solve workgroups

@@ -27,12 +27,12 @@ CHMC_DAMP = 0.05
 # tiles, either is a few microseconds)
 SPLIT8_MIN_DIM = 256
 
-# "auto" sweeps in the factor form above 48 panels of 128 features, where the
-# library's factor would otherwise run a separate triangular inverse (measured
-# 722 -> 599 ms per 70B-shape step); below, the inverse rides along inside the
-# factorization's own launches and U is taken as it is (the factor form's
-# per-block conversion measured 5.35 -> 5.73 ms per Qwen MLP step there)
-FACTOR_FORM_MIN_DIM = 48 * 128 + 1
+# "auto" sweeps in the factor form (no triangular inverse beyond the 128-wide
+# diagonal blocks) from 768 features on. Measured per step, factor form
+# against U: 70B-shape 599 against 722 ms, TinyLlama block 12.10 against
+# 12.58 ms, Qwen MLP 4.82 against 5.34 ms; the 576-feature layer (five
+# launch-bound panels) 0.517 against 0.502 ms, so smaller layers take U.
+FACTOR_FORM_MIN_DIM = 768
 
 
 def factor_form_mode(mode, dim):

@@ -141,7 +141,7 @@ def test_factor_form_identity_hessian_is_rtn():
 def test_factor_form_workload_layers(wname, hname):
     """The benchmark's launch configuration (LayerGroup.enqueue: the Hessian
     mode of the benchmark, every bit width on one stream), here with the
-    factor form forced on (the benchmark takes it above 6144 features),
+    factor form forced on (the benchmark takes it from 768 features),
     against the oracle's sweep on the exact S."""
     wl = WORKLOADS[wname]
     X, W = workload_inputs(wl, hname)
@@ -181,3 +181,31 @@ def test_factor_form_workload_layers(wname, hname):
         if not wl.act_order:
             gpu["g_idx"] = g_idx
         compare_layer(gpu, ref, name=f"factor-form {wname}/{hname}/b{bits}")
+
+
+@pytest.mark.parametrize("dim,rows,gs", [(300, 40, 64), (700, 24, 128)])
+def test_factor_form_with_min_pivot_order(dim, rows, gs):
+    """The min-pivot order (The Geometry of LLM Quantization 2.3) in the
+    factor form: the same order as with U, and the layer at the parity bar
+    against the oracle swept in that order."""
+    say(f"factor-form min-pivot dim={dim}")
+    W, X = rand_inputs(rows, dim, 2 * dim, dim + 5)
+    S, n = gpu_hessian([X], dim)
+    p_u, _ = G.prepare_hinv(S, n, damp=0.01, min_pivot=True)
+    perm, M = G.prepare_hinv(S, n, damp=0.01, min_pivot=True, factor_form=True)
+    assert torch.equal(perm, p_u)
+    q = G.quantize_layer(torch.from_numpy(W).to(DEV), M, perm, bits=4, group_size=gs,
+                         factor_form=True)
+    torch.cuda.synchronize()
+    Sr, nr = O.hessian_sum(X)
+    H = O.damped_hessian(Sr, nr, 0.01)
+    pr = perm.cpu().numpy().astype(np.int64)
+    assert np.array_equal(np.sort(pr), np.arange(dim))  # (the order itself: test_gpu_minpivot)
+    res = O.gptq_sweep(W.astype(np.float64)[:, pr], O.hinv_upper(O.permute_sym(H, pr)), 4, gs)
+    codes = np.empty_like(res["codes"])
+    codes[:, pr] = res["codes"]
+    g_idx = np.empty(dim, dtype=np.int64)
+    g_idx[pr] = np.arange(dim) // gs
+    ref = dict(codes=codes, scales=res["scales"], zeros=res["zeros"], row_loss=res["row_loss"],
+               g_idx=g_idx)
+    compare_layer(to_numpy_layer(q), ref, name=f"factor-form min-pivot {dim}")
