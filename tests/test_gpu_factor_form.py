@@ -209,3 +209,54 @@ def test_factor_form_with_min_pivot_order(dim, rows, gs):
     ref = dict(codes=codes, scales=res["scales"], zeros=res["zeros"], row_loss=res["row_loss"],
                g_idx=g_idx)
     compare_layer(to_numpy_layer(q), ref, name=f"factor-form min-pivot {dim}")
+
+
+def test_workload_inputs_on_concurrent_streams_like_the_benchmark():
+    """The benchmark's step for the Qwen MLP workload: both calibration inputs
+    (896 and 4864 features, the stacked gate/up rows and the down rows) as
+    LayerGroups enqueued asynchronously on two streams at once, largest
+    Hessian first; each against the oracle (and the same results as one
+    input at a time)."""
+    wl = WORKLOADS["qwen05b_mlp"]
+    order = sorted(wl.inputs, key=lambda h: -h.dim)
+    groups, inputs = [], []
+    for h in order:
+        X, W = workload_inputs(wl, h.name)
+        chunks = [torch.from_numpy(X[s:s + wl.token_chunk]).to(DEV)
+                  for s in range(0, X.shape[0], wl.token_chunk)]
+        grp = LayerGroup(h.dim, W.shape[0], max_chunk_tokens=max(c.shape[0] for c in chunks),
+                         bits=wl.bits, group_size=wl.group_size, act_order=wl.act_order,
+                         damp=wl.damp, device=DEV, hessian="auto")
+        groups.append(grp)
+        inputs.append((X, W, chunks, torch.from_numpy(W).to(DEV)))
+    streams = [torch.cuda.Stream(device=DEV) for _ in order]
+    torch.cuda.synchronize()
+    for grp, (_, _, chunks, Wd), s in zip(groups, inputs, streams):
+        with torch.cuda.stream(s):
+            grp.enqueue(chunks, Wd)
+    torch.cuda.synchronize()
+    for grp, s in zip(groups, streams):
+        with torch.cuda.stream(s):
+            grp.check()
+    conc = [[(q.codes.clone(), q.row_loss.clone()) for q in g.outs] for g in groups]
+    for grp, (_, _, chunks, Wd) in zip(groups, inputs):  # one at a time
+        grp.enqueue(chunks, Wd)
+        grp.check()
+    for grp, c in zip(groups, conc):
+        for (codes, loss), q in zip(c, grp.outs):
+            assert torch.equal(codes, q.codes) and torch.equal(loss, q.row_loss)
+    for h, grp, (X, W, _, _) in zip(order, groups, inputs):
+        dim = h.dim
+        Sr, nr = O.hessian_sum([X[s:s + wl.token_chunk] for s in range(0, X.shape[0],
+                                                                        wl.token_chunk)])
+        H = O.damped_hessian(Sr, nr, wl.damp)
+        pr = np.arange(dim)
+        Ur = O.hinv_upper(O.permute_sym(H, pr))
+        for bi, bits in enumerate(wl.bits):
+            say(f"concurrent {wl.name}/{h.name} bits={bits} factor_form={grp.factor_form}")
+            res = O.gptq_sweep(W.astype(np.float64), Ur, bits, wl.group_size, block=128)
+            ref = dict(codes=res["codes"], scales=res["scales"], zeros=res["zeros"],
+                       row_loss=res["row_loss"], g_idx=np.arange(dim) // wl.group_size)
+            gpu = to_numpy_layer(grp.outs[bi])
+            gpu["g_idx"] = ref["g_idx"]
+            compare_layer(gpu, ref, name=f"concurrent {wl.name}/{h.name}/b{bits}")
