@@ -214,42 +214,54 @@ __device__ __forceinline__ void q_gemm_tile(const float* __restrict__ E, int64_t
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int nchunks = k_hi > k_lo ? (int)((k_hi - k_lo) / 32) : 0;
 
-  // E loader: row t>>2, 8 floats at (t&3)*8; U loader: row t>>3, 16 floats at (t&7)*16
+  // E loader: row t>>2, 8 floats at (t&3)*8; U loader: row t>>3, 16 floats at (t&7)*16.
+  // Chunks are loaded two ahead into two register sets (the E rows come from
+  // memory once per block, so a load in flight needs more than one chunk of
+  // products to arrive), the loop unrolled by two so that each set keeps its
+  // registers.
   const int er = t >> 2, ec = (t & 3) * 8;
   const int ur = t >> 3, uc = (t & 7) * 16;
-  f4 eR[2], uR[4];
-  auto fetch = [&](int c) {
+  const bool vfull = vecU && bw == QB;  // every U load a whole float4
+  struct Stage {
+    f4 e[2], u[4];
+  };
+  auto fetch = [&](int c, Stage& S) {
     const int64_t l0 = k_lo + (int64_t)c * 32;
     if (r0 + er < rows) {
       const float* pe = E + (r0 + er) * lde + l0 + ec;
-      eR[0] = *reinterpret_cast<const f4*>(pe);
-      eR[1] = *reinterpret_cast<const f4*>(pe + 4);
+      S.e[0] = *reinterpret_cast<const f4*>(pe);
+      S.e[1] = *reinterpret_cast<const f4*>(pe + 4);
     } else {
-      eR[0] = f4{0, 0, 0, 0};
-      eR[1] = f4{0, 0, 0, 0};
+      S.e[0] = f4{0, 0, 0, 0};
+      S.e[1] = f4{0, 0, 0, 0};
     }
     const float* pu = U + (l0 + ur) * ldu + j0 + uc;
+    if (vfull) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int cc = uc + 4 * q;
-      if (vecU && cc + 3 < bw) {
-        uR[q] = *reinterpret_cast<const f4*>(pu + 4 * q);
-      } else {
+      for (int q = 0; q < 4; ++q) S.u[q] = *reinterpret_cast<const f4*>(pu + 4 * q);
+    } else {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) uR[q][x] = (cc + x < bw) ? pu[4 * q + x] : 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const int cc = uc + 4 * q;
+        if (vecU && cc + 3 < bw) {
+          S.u[q] = *reinterpret_cast<const f4*>(pu + 4 * q);
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) S.u[q][x] = (cc + x < bw) ? pu[4 * q + x] : 0.0f;
+        }
       }
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const Stage& S) {
     float* se = &Es[buf][er * QE_LD + ec];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-      se[x] = eR[0][x];
-      se[4 + x] = eR[1][x];
+      se[x] = S.e[0][x];
+      se[4 + x] = S.e[1][x];
     }
     float* su = &Us[buf][ur * QU_LD + uc];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<f4*>(su + 4 * q) = uR[q];
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<f4*>(su + 4 * q) = S.u[q];
   };
 
   f16 acc[2];
@@ -261,35 +273,47 @@ __device__ __forceinline__ void q_gemm_tile(const float* __restrict__ E, int64_t
       acc[i][x] = 0.0f;
       acc64[i][x] = 0.0;
     }
+  auto compute = [&](int cur) {
+    const float* es = Es[cur];
+    const float* us = Us[cur];
+#pragma unroll
+    for (int kk = 0; kk < 32; kk += 2) {
+      const int k = kk + (lane >> 5);
+      const float a0 = es[(lane & 31) * QE_LD + k];
+      const float a1 = es[(32 + (lane & 31)) * QE_LD + k];
+      const float b = us[k * QU_LD + w * 32 + (lane & 31)];
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        acc64[i][x] += (double)acc[i][x];
+        acc[i][x] = 0.0f;
+      }
+  };
 
   if (nchunks > 0) {
-    fetch(0);
-    store(0);
+    Stage A, B;
+    fetch(0, A);
+    store(0, A);
+    if (nchunks > 1) fetch(1, A);
     __syncthreads();
-    for (int c = 0; c < nchunks; ++c) {
-      const int cur = c & 1;
-      const bool more = c + 1 < nchunks;
-      if (more) fetch(c + 1);
-      const float* es = Es[cur];
-      const float* us = Us[cur];
-#pragma unroll
-      for (int kk = 0; kk < 32; kk += 2) {
-        const int k = kk + (lane >> 5);
-        const float a0 = es[(lane & 31) * QE_LD + k];
-        const float a1 = es[(32 + (lane & 31)) * QE_LD + k];
-        const float b = us[k * QU_LD + w * 32 + (lane & 31)];
-        acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          acc64[i][x] += (double)acc[i][x];
-          acc[i][x] = 0.0f;
-        }
-      if (more) store(cur ^ 1);
+    int c = 0;
+    for (;;) {
+      // buffer c & 1 holds chunk c, A chunk c + 1
+      if (c + 2 < nchunks) fetch(c + 2, B);
+      compute(c & 1);
+      if (c + 1 < nchunks) store((c + 1) & 1, A);
       __syncthreads();
+      if (++c >= nchunks) break;
+      // buffer c & 1 holds chunk c, B chunk c + 1
+      if (c + 2 < nchunks) fetch(c + 2, A);
+      compute(c & 1);
+      if (c + 1 < nchunks) store((c + 1) & 1, B);
+      __syncthreads();
+      if (++c >= nchunks) break;
     }
   }
   const int col = w * 32 + (lane & 31);
@@ -471,14 +495,6 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
                     ? (wblk ? wblk[r[p] * QB + c] : f16_to_f64(W[r[p] * ldw + j0 + c]))
                     : 0.0;
     }
-  // the original weights (fp16 values, exact in fp32) for the residuals
-  float w0[RPL][FAC ? 8 : 1];
-  if constexpr (FAC) {
-#pragma unroll
-    for (int p = 0; p < RPL; ++p)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) w0[p][s] = (float)w[p][s];
-  }
   double acc[RPL][8];
 #pragma unroll
   for (int p = 0; p < RPL; ++p)
@@ -620,13 +636,13 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   }
   __syncthreads();
   if constexpr (FAC) {
-    // t = sum * U[blk, blk] by rows: t_l = U_ll sum_l + sum_{k<l} (U_kk sum_k)
-    // (U_kl / U_kk), the slab holding U_kl / U_kk above its diagonal; sum_k
-    // of column k = 16 m + (k % 16) is slot m of lane k % 16, broadcast to
-    // its row, and reaches the slots m.. 7 (the columns after it).
-    double t2[RPL][8];
+    // w (the original weights here) -= t = sum * U[blk, blk] by rows: t_l =
+    // U_ll sum_l + sum_{k<l} (U_kk sum_k) (U_kl / U_kk), the slab holding
+    // U_kl / U_kk above its diagonal; U_kk sum_k of column k = 16 m +
+    // (k % 16) is slot m of lane k % 16, broadcast to its row, and reaches
+    // the slots m .. 7 (the columns after it).
     if (j0 > 0) {
-      double sp[RPL][8];
+      double sp[RPL][8], t2[RPL][8];
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const double ud = udiag[16 * s + q];
@@ -653,22 +669,20 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
             for (int p = 0; p < RPL; ++p) t2[p][s] = fma(db[p], u[s], t2[p][s]);
         }
       }
-    } else {
 #pragma unroll
       for (int p = 0; p < RPL; ++p)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) t2[p][s] = 0.0;
+        for (int s = 0; s < 8; ++s) w[p][s] -= t2[p][s];
     }
 #pragma unroll
     for (int p = 0; p < RPL; ++p)
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        w[p][s] = (rv[p] && 16 * s + q < bw) ? (double)w0[p][s] - t2[p][s] : 0.0;
+        w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] : 0.0;
         finite = finite && isfinite(w[p][s]);
       }
     if (!finite) atomicOr(status, ST_NONFINITE);
   }
-
   double scale[RPL], rscale[RPL], zero[RPL], loss[RPL];
   double nout[RPL];  // SSQR: outliers of this lane's columns
   // range of the level k = code - zero: [-zero, maxq - zero], or unbounded
@@ -790,6 +804,14 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
         }
       }
     };
+    // factor form: this tile's original weights for the stored residuals,
+    // loaded before its column chain so that the load has arrived by its end
+    uint16_t wraw[RPL];
+    if constexpr (FAC) {
+#pragma unroll
+      for (int p = 0; p < RPL; ++p)
+        wraw[p] = (rv[p] && 16 * tt + q < bw) ? W[r[p] * ldw + j0 + 16 * tt + q] : (uint16_t)0;
+    }
     if (bw == QB) {
       switch (8 - tt) {
         case 8: tile(std::integral_constant<int, 8>{}, std::true_type{}); break;
@@ -822,7 +844,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
           codes[r[p] * ldc + j0 + c] = (uint8_t)fmin(fmax(k_own + zero[p], 0.0), 255.0);
           if constexpr (FAC) {
             // the residual q - w of the original weight (exact in fp64)
-            E[r[p] * lde + j0 + c] = (float)fma(scale[p], k_own, -(double)w0[p][0]);
+            E[r[p] * lde + j0 + c] = (float)fma(scale[p], k_own, -f16_to_f64(wraw[p]));
           } else {
             E[r[p] * lde + j0 + c] = (float)e;
           }
@@ -849,11 +871,6 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
 #pragma unroll
       for (int s = 0; s < 7; ++s) w[p][s] = w[p][s + 1];
       w[p][7] = 0.0;
-      if constexpr (FAC) {
-#pragma unroll
-        for (int s = 0; s < 7; ++s) w0[p][s] = w0[p][s + 1];
-        w0[p][7] = 0.0f;
-      }
     }
   }
 #pragma unroll
