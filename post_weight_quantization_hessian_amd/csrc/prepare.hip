@@ -909,12 +909,39 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
   }
 }
 
-// The factor form (K front-padded: sweep index j is row ip-1-j of K):
+// The factor form, beyond the diagonal tiles: T_ab = L_ab X_bb for every
+// tile a > b of K (X_bb = L_bb^-1 from trtri_diag_kernel), in place, one
+// workgroup per tile. In sweep order (K front-padded: sweep index j is row
+// ip-1-j of K) this is R[blk_a, blk_b] U[blk_b, blk_b] with R = J L J = U^-1
+// the upper factor of H itself (H_p = R R^T); the sweep's residuals Q - W
+// through it give E U (E = (W - Q) R and, U being upper, R[:j0, :j0]
+// U[:j0, blk] = -R[:j0, blk] U[blk, blk]).
+__global__ __launch_bounds__(256) void prep_mfac_kernel(double* __restrict__ K,
+                                                        const double* __restrict__ Xb,
+                                                        int64_t ld) {
+  __shared__ double smem[4 * GCH];
+  const int id = (int)blockIdx.x;  // strict lower tiles, row-major: a > b
+  int a = (int)((1.0 + sqrt(1.0 + 8.0 * id)) * 0.5);
+  while (a * (a - 1) / 2 > id) --a;
+  while ((a + 1) * a / 2 <= id) ++a;
+  const int b = id - a * (a - 1) / 2;
+  double* C = K + (int64_t)a * GT * ld + (int64_t)b * GT;
+  // A[m][k] = L_ab (K along its rows, staged transposed); B[k][n] = X_bb
+  LdTrans64 la{C, ld, {}};
+  LdDirect64 lb{Xb + (int64_t)b * GT * ld + (int64_t)b * GT, ld, {}};
+  d4 acc[4][4];
+  zero_acc(acc);
+  gemm64_loop(la, lb, GT / GK, smem, smem + 2 * GCH, acc);
+  // every load of the tile has completed in the loop: overwrite it
+  for_each_acc(acc, [&](int r, int c, double v) { C[r * ld + c] = v; });
+}
+
+// The factor-form matrix (K front-padded: sweep index j is row ip-1-j of K):
 //   M[j][k] = U[j][k]  where j and k are in the same 128-block (U's diagonal
 //             block: the inverse of the tile of L in Xb, reversed),
-//   M[j][k] = L[ip-1-j][ip-1-k] = (U^-1)[j][k]  for k in a later block,
-// 0 below the diagonal; fp32. U^-1 = J L J is the upper factor of H itself
-// (H_p = U^-1 U^-T).
+//   M[j][k] = T[ip-1-j][ip-1-k] = (R U)[j][k] over k's block  for k in a
+//             later block (prep_mfac_kernel),
+// 0 below the diagonal; fp32.
 __global__ __launch_bounds__(256) void prep_mout_kernel(const double* __restrict__ K,
                                                         const double* __restrict__ Xb, int64_t ld,
                                                         int64_t n, float* __restrict__ M) {
@@ -1595,6 +1622,9 @@ extern "C" gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, i
     GPTQ_LAUNCH(K_TRTRI_DIAG, st, trtri_diag_kernel<<<nt, 256, 0, st>>>(K, Dd, Xb, ip));
   }
   if (fac) {
+    if (nt > 1)
+      GPTQ_LAUNCH(K_PREP_UOUT, st,
+                  prep_mfac_kernel<<<(unsigned)(nt * (nt - 1) / 2), 256, 0, st>>>(K, Xb, ip));
     dim3 grid((unsigned)std::min<int64_t>(cdiv(n, 256), 64), (unsigned)std::min<int64_t>(n, 65535));
     GPTQ_LAUNCH(K_PREP_UOUT, st, prep_mout_kernel<<<grid, 256, 0, st>>>(K, Xb, ip, n, U));
     if (flags & GPTQ_FLAG_NO_SYNC) return GPTQ_OK;

@@ -403,13 +403,12 @@ __device__ inline double row_ror8(double v) { return dpp_f64<0x128>(v); }
 // the level k goes to ovals (int16 bits) at the original column, and a level
 // beyond the int16 range is reported (ST_NONFINITE).
 // FAC (MODE 0 only), the factor form: beyond the block's diagonal, the
-// matrix passed holds the factor of H itself, M = U^-1 (upper, H_p = M M^T),
-// and E holds the residuals q - w of the original weights, so the update
-// GEMM leaves sum = (Q - W)[:, :j0] M[:j0, blk]. Since E = (W - Q) U^-1 (the
-// errors are the residuals through U^-1), the block's current values are
-//   W~ = W - E[:, :j0] U[:j0, blk] = W - sum * U[blk, blk]
-// (the blocks of E U^-1 U above the block's rows vanish, U being upper), a
-// product with the block's own diagonal block of U, which the slab holds.
+// matrix passed holds (R U)[blk_a, blk_b] = R[blk_a, blk_b] U[blk_b, blk_b]
+// for the factor R = U^-1 of H itself, and E holds the residuals q - w of the
+// original weights. Since E = (W - Q) R and, U being upper, R[:j0, :j0]
+// U[:j0, blk] = -R[:j0, blk] U[blk, blk], the update sum (Q - W)[:, :j0]
+// (R U)[:j0, blk] is E[:, :j0] U[:j0, blk], the same current values; only
+// the stored E differs.
 template <int GS, int MODE, int RPL, bool FAC = false>
 __global__ __launch_bounds__(512) void q_sweep_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, const double* __restrict__ wblk,
@@ -431,7 +430,6 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
   // of this array before the slab is staged.
   __shared__ double Us[QB * QB + 3 * QB];
   __shared__ double rdiag[QB];  // 1 / U[j][j]
-  __shared__ double udiag[FAC ? QB : 1];  // U[j][j]
   if ((int)blockIdx.x >= nsweep) {
     // workgroups past the sweep's own (256 threads each): the next block's
     // update GEMM over the errors of the blocks before this one, l < gk_end,
@@ -577,9 +575,7 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
       }
   }
   for (int j = t; j < QB; j += nthr) {
-    const double ujj = j < bw ? (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
-    rdiag[j] = j < bw ? 1.0 / ujj : 0.0;
-    if constexpr (FAC) udiag[j] = ujj;
+    rdiag[j] = j < bw ? 1.0 / (double)U[(j0 + j) * ldu + j0 + j] : 0.0;
     Us[QB * QB + j] = 0.0;
     Us[QB * QB + QB + j] = 0.0;
     Us[QB * QB + 2 * QB + j] = 0.0;
@@ -624,65 +620,16 @@ __global__ __launch_bounds__(512) void q_sweep_kernel(
     }
   }
   bool finite = true;
-  if constexpr (!FAC) {
 #pragma unroll
-    for (int p = 0; p < RPL; ++p)
+  for (int p = 0; p < RPL; ++p)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] - acc[p][s] : 0.0;
-        finite = finite && isfinite(w[p][s]);
-      }
-    if (!finite) atomicOr(status, ST_NONFINITE);
-  }
-  __syncthreads();
-  if constexpr (FAC) {
-    // w (the original weights here) -= t = sum * U[blk, blk] by rows: t_l =
-    // U_ll sum_l + sum_{k<l} (U_kk sum_k) (U_kl / U_kk), the slab holding
-    // U_kl / U_kk above its diagonal; U_kk sum_k of column k = 16 m +
-    // (k % 16) is slot m of lane k % 16, broadcast to its row, and reaches
-    // the slots m .. 7 (the columns after it).
-    if (j0 > 0) {
-      double sp[RPL][8], t2[RPL][8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const double ud = udiag[16 * s + q];
-#pragma unroll
-        for (int p = 0; p < RPL; ++p) {
-          sp[p][s] = acc[p][s] * ud;
-          t2[p][s] = sp[p][s];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-          const double* urow = Us + (16 * m + kk) * QB + q;
-          double u[8];
-#pragma unroll
-          for (int s = m; s < 8; ++s) u[s] = urow[16 * s];
-          double db[RPL];
-#pragma unroll
-          for (int p = 0; p < RPL; ++p) db[p] = row_bcast_mov_i(sp[p][m], kk);
-#pragma unroll
-          for (int s = m; s < 8; ++s)
-#pragma unroll
-            for (int p = 0; p < RPL; ++p) t2[p][s] = fma(db[p], u[s], t2[p][s]);
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < RPL; ++p)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) w[p][s] -= t2[p][s];
+    for (int s = 0; s < 8; ++s) {
+      w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] - acc[p][s] : 0.0;
+      finite = finite && isfinite(w[p][s]);
     }
-#pragma unroll
-    for (int p = 0; p < RPL; ++p)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        w[p][s] = (rv[p] && 16 * s + q < bw) ? w[p][s] : 0.0;
-        finite = finite && isfinite(w[p][s]);
-      }
-    if (!finite) atomicOr(status, ST_NONFINITE);
-  }
+  if (!finite) atomicOr(status, ST_NONFINITE);
+  __syncthreads();
+
   double scale[RPL], rscale[RPL], zero[RPL], loss[RPL];
   double nout[RPL];  // SSQR: outliers of this lane's columns
   // range of the level k = code - zero: [-zero, maxq - zero], or unbounded
@@ -1105,10 +1052,9 @@ static gptq_status quantize_enqueue(const uint16_t* W, int64_t rows, int64_t col
         GPTQ_LAUNCH(K_Q_GEMM, st,
                     q_gemm_kernel<<<grid, 256, 0, st>>>(E, L.lde, U, cols, Wsrc, ldws, rows, j0,
                                                         bw, 0, ks, j0, pc, pstride, 0,
-                                                        P == 1 && !fac ? wblk : nullptr, vecU));
-        // one split: the GEMM wrote W~ itself; else (and always in the factor
-        // form, whose sweep turns the sum into W~) the sweep sums the partials
-        if (P == 1 && !fac) cur = wblk;
+                                                        P == 1 ? wblk : nullptr, vecU));
+        // one split: the GEMM wrote W~ itself; else the sweep sums the partials
+        if (P == 1) cur = wblk;
         else nparts = P;
       }
     }

@@ -1,17 +1,17 @@
 """CPU: the factor form of the blocked sweep reproduces the oracle's sweep.
 
-The library's benchmark path sweeps with R = U^-1 (the order-reversed
-Cholesky factor of H_p, H_p = R R^T) beyond U's 128-wide diagonal blocks:
-with the scaled errors E = (W - Q) R (from W - Q = E U, since each column's
-total change is the sum of its errors through U), the current values of a
-block are
+The library's benchmark path sweeps with M = R[blk_a, blk_b] U[blk_b, blk_b]
+beyond U's 128-wide diagonal blocks, R = U^-1 the order-reversed Cholesky
+factor of H_p (H_p = R R^T): with the scaled errors E = (W - Q) R (from
+W - Q = E U, since each column's total change is the sum of its errors
+through U), the current values of a block are
     W~[:, blk] = W[:, blk] - E[:, :j0] U[:j0, blk]
-               = W[:, blk] + (W - Q)[:, :j0] R[:j0, blk] U[blk, blk]
-(E U = (W - Q) R U, and the blocks of R U above the block's rows give
--R[:j0, blk] U[blk, blk], U being upper). This test restates that sweep in
-plain numpy, written from the derivation above (not from the library), and
-holds it to the oracle's strict sweep (CHMC article, Methodik, Schritt 2)
-exactly in fp64 on small problems: every code, grid and the loss.
+               = W[:, blk] - (Q - W)[:, :j0] M[:j0, blk]
+(R[:j0, :j0] U[:j0, blk] = -R[:j0, blk] U[blk, blk], U being upper). This
+test restates that sweep in plain numpy, written from the derivation above
+(not from the library), and holds it to the oracle's strict sweep (CHMC
+article, Methodik, Schritt 2) exactly in fp64 on small problems: every code,
+grid and the loss.
 """
 import numpy as np
 import pytest
@@ -26,6 +26,10 @@ def factor_form_sweep(Wp, Hp, bits, gs):
     n = Hp.shape[0]
     R = np.linalg.cholesky(Hp[::-1, ::-1])[::-1, ::-1]  # upper, Hp = R R^T
     U = np.linalg.inv(R)
+    M = np.zeros_like(R)  # R U over the block columns, beyond the diagonal blocks
+    for b0 in range(0, n, B):
+        b1 = min(b0 + B, n)
+        M[:b0, b0:b1] = R[:b0, b0:b1] @ U[b0:b1, b0:b1]
     maxq = (1 << bits) - 1
     rows = Wp.shape[0]
     codes = np.zeros((rows, n), np.int64)
@@ -36,7 +40,7 @@ def factor_form_sweep(Wp, Hp, bits, gs):
     for j0 in range(0, n, B):
         j1 = min(j0 + B, n)
         Ub = U[j0:j1, j0:j1]
-        V = Wp[:, j0:j1] + resid[:, :j0] @ R[:j0, j0:j1] @ Ub
+        V = Wp[:, j0:j1] - resid[:, :j0] @ M[:j0, j0:j1]
         for jj in range(j1 - j0):
             j = j0 + jj
             g = j // gs
@@ -47,7 +51,7 @@ def factor_form_sweep(Wp, Hp, bits, gs):
             e = (V[:, jj] - dq) / Ub[jj, jj]
             loss += e * e
             V[:, jj + 1:] -= np.outer(e, Ub[jj, jj + 1:])
-            resid[:, j] = Wp[:, j] - dq
+            resid[:, j] = dq - Wp[:, j]
     return codes, scales, zeros, loss
 
 

@@ -1,15 +1,15 @@
 """GPU: the sweep in the factor form against the fp64 oracle.
 
 prepare_hinv(..., factor_form=True) returns, in sweep order, U's 128-wide
-diagonal blocks and, beyond them, the factor R = U^-1 of H_p itself (H_p =
-R R^T, so R needs no inverse: it is the order-reversed Cholesky factor). The
-sweep then carries the residuals q - w of the original weights through R and
-turns the sum into the current values with the block's own diagonal block of
-U. In exact arithmetic this is the same sweep (The Geometry of LLM
-Quantization 2.2: the nearest-plane step works with a triangular factor of the
-lattice's Gram matrix; E = (W - Q) U^-1), so codes, scales, zero points and
-the loss are held to the oracle's sweep (CHMC article, Methodik, Schritt 2)
-at the usual bar. Shapes: ragged columns (not a multiple of 128), every group
+diagonal blocks and, beyond them, R[blk_a, blk_b] U[blk_b, blk_b] with R =
+U^-1 the factor of H_p itself (H_p = R R^T, so R needs no inverse: it is the
+order-reversed Cholesky factor; only the diagonal blocks are inverted). The
+sweep then carries the residuals q - w of the original weights through that
+matrix, which gives the same update sums as the errors through U (The
+Geometry of LLM Quantization 2.2: the nearest-plane step works with a
+triangular factor of the lattice's Gram matrix; E = (W - Q) U^-1), so codes,
+scales, zero points and the loss are held to the oracle's sweep (CHMC
+article, Methodik, Schritt 2) at the usual bar. Shapes: ragged columns (not a multiple of 128), every group
 size, 2 to 8 bits, act-order on and off, the no-clipping sweep, and the full
 small and medium workload layers in the benchmark's configuration.
 """
@@ -42,13 +42,15 @@ def say(msg):
 
 
 def expected_matrix(Ur):
-    """U's diagonal blocks, U^-1 beyond them (oracle U)."""
+    """U's diagonal blocks, R[blk_a, blk_b] U[blk_b, blk_b] beyond them (R =
+    U^-1, from the oracle's U)."""
     R = np.linalg.inv(Ur)
-    M = np.triu(R)
     n = Ur.shape[0]
-    for j0 in range(0, n, B):
-        j1 = min(j0 + B, n)
-        M[j0:j1, j0:j1] = Ur[j0:j1, j0:j1]
+    M = np.zeros_like(Ur)
+    for b0 in range(0, n, B):
+        b1 = min(b0 + B, n)
+        M[b0:b1, b0:b1] = Ur[b0:b1, b0:b1]
+        M[:b0, b0:b1] = R[:b0, b0:b1] @ Ur[b0:b1, b0:b1]
     return M
 
 
@@ -69,12 +71,15 @@ def test_factor_form_matrix_matches_oracle(dim, act):
     Me = expected_matrix(Ur)
     Mg = M.cpu().numpy().astype(np.float64)
     assert np.all(np.tril(Mg, -1) == 0)
-    # per 128-block of rows and columns: fp32 storage of fp64 values
-    for a0 in range(0, dim, B):
-        for b0 in range(a0, dim, B):
+    # per 128-block of rows and columns: fp32 storage of fp64 values (the
+    # off-diagonal blocks relative to the block column of R U's scale)
+    for b0 in range(0, dim, B):
+        col = np.max(np.abs(Me[:b0 + B, b0:b0 + B])) if b0 else 0.0
+        for a0 in range(0, b0 + 1, B):
             e = Me[a0:a0 + B, b0:b0 + B]
             g = Mg[a0:a0 + B, b0:b0 + B]
-            err = np.max(np.abs(g - e)) / max(np.max(np.abs(e)), 1e-300)
+            scale = np.max(np.abs(e)) if a0 == b0 else col
+            err = np.max(np.abs(g - e)) / max(scale, 1e-300)
             assert err < 2e-6, (a0, b0, err)
 
 

@@ -190,8 +190,8 @@ def test_fullsize_sampled(wname):
         assert abs(hdiag[perm[k]] - hdiag[pr[k]]) <= 1e-12 * hdiag[pr[k]], k
 
     # ---- trailing block of the factor-form matrix from the trailing block of
-    # H_p alone: U's two diagonal 128-blocks, R = U^-1 above them (the
-    # trailing block of R is the inverse of the trailing block of U)
+    # H_p alone: U's two diagonal 128-blocks, R U_bb above them (the trailing
+    # block of R = U^-1 is the inverse of the trailing block of U)
     say(f"{wname}: trailing {TRAIL}x{TRAIL} block of the factor-form matrix")
     assert grp.factor_form and dim % 128 == 0
     assert np.array_equal(perm[-TRAIL:], pr[-TRAIL:])
@@ -204,7 +204,9 @@ def test_fullsize_sampled(wname):
     Ub = O.hinv_upper(O.damped_hessian(Sb, n, wl.damp, lam=lam))
     Rb = np.linalg.inv(Ub)
     Mg = U[-TRAIL:, -TRAIL:].double().cpu().numpy()
-    for (a0, b0, ref) in ((0, 0, Ub), (128, 128, Ub), (0, 128, Rb)):
+    RU = Rb.copy()
+    RU[:128, 128:] = Rb[:128, 128:] @ Ub[128:, 128:]
+    for (a0, b0, ref) in ((0, 0, Ub), (128, 128, Ub), (0, 128, RU)):
         e = ref[a0:a0 + 128, b0:b0 + 128]
         g_ = Mg[a0:a0 + 128, b0:b0 + 128]
         rowmax = np.abs(e).max(axis=1, keepdims=True)
@@ -212,10 +214,11 @@ def test_fullsize_sampled(wname):
         assert np.all(np.abs(g_ - e) <= bound), (a0, b0, float(np.max(np.abs(g_ - e) / rowmax)))
     assert np.all(Mg[128:, :128] == 0)
 
-    # ---- sampled rows: zero below the diagonal, and the last column of R,
-    # R[j][dim-1] = H_p[j][dim-1] / sqrt(H_p[dim-1][dim-1]) (H_p = R R^T with
-    # R upper: its last column meets only R's last diagonal entry)
-    say(f"{wname}: the last column of R on sampled rows")
+    # ---- sampled rows: zero below the diagonal, and the last block column:
+    # (R U)[j, B] = H_p[j, B] H_p[B, B]^-1 for the last 128-block B (H_p =
+    # R R^T with R upper: R[j, B] R[B, B]^T = H_p[j, B], and R[B, B]^-T
+    # U[B, B] = U[B, B]^T U[B, B] = H_p[B, B]^-1)
+    say(f"{wname}: the last block column of the factor-form matrix on sampled rows")
     Hd = S * (2.0 / n)
     Hd.diagonal().add_(lam)
     J = sorted(set([0, 1, dim // 3, dim // 2, dim - TRAIL - 1]
@@ -225,9 +228,11 @@ def test_fullsize_sampled(wname):
     Mrows = U[jt].double()
     assert torch.all(Mrows[cols[None, :] < jt[:, None]] == 0), "entries below the diagonal"
     pt = torch.from_numpy(perm).to(DEV)
-    hl = Hd[pt[jt], pt[dim - 1]]
-    rl = hl / torch.sqrt(Hd[pt[dim - 1], pt[dim - 1]])
-    rel = ((Mrows[:, dim - 1] - rl).abs() / rl.abs().max()).max().item()
+    last = pt[dim - 128:]
+    HjB = Hd[pt[jt]][:, last]
+    HBB = Hd[last][:, last]
+    ref = torch.linalg.solve(HBB, HjB.T).T  # H_p[j, B] H_p[B, B]^-1 (HBB symmetric)
+    rel = ((Mrows[:, dim - 128:] - ref).abs().max() / ref.abs().max()).item()
     assert rel <= U_TOL, rel
 
     # ---- the oracle's stored sweep of 64 sampled rows (whole-Hessian oracle)
