@@ -134,11 +134,13 @@ gptq_status gptq_hessian_accumulate(double* S, int64_t in_features,
  * lattice's Gram matrix, here H itself):
  *   M[j][k] = U[j][k]  for j <= k in the same 128-wide block of sweep
  *                      positions (blocks start at 0; the last may be short),
- *   M[j][k] = R[j][k]  for k in a later block, R = U^-1 the upper triangular
- *                      factor with R R^T = H[perm][:,perm],
+ *   M[j][k] = (R U)[j][k] over k's block, i.e. sum of R[j][l] U[l][k] for l in
+ *                      k's block, for k in a later block; R = U^-1 is the
+ *                      upper triangular factor with R R^T = H[perm][:,perm],
  *   0 below the diagonal. R is the order-reversed Cholesky factor of the
  * permuted H, so only the 128 x 128 diagonal blocks are inverted: no full
- * triangular inverse runs. The flag combines with either order.
+ * triangular inverse runs (each tile beyond them is one 128 x 128 product).
+ * The flag combines with either order.
  * All work is enqueued on `stream`.
  * Workspace: gptq_prepare_workspace_bytes(in_features) bytes.
  * Synchronizes `stream` once at the end to read the factorisation status;
@@ -164,7 +166,7 @@ gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_to
  *   W     fp16 [rows x cols], leading dimension ldw (>= cols), original order.
  *   U     fp32 [cols x cols] from gptq_prepare_hinv (sweep order); with
  *         GPTQ_FLAG_FACTOR_FORM the matrix M that gptq_prepare_hinv returns
- *         with that flag (U's diagonal blocks, R = U^-1 beyond them).
+ *         with that flag (U's diagonal blocks, R U over each block beyond).
  *   perm  int32[cols] from gptq_prepare_hinv, or NULL for the identity.
  *   bits  2..8; group_size one of 16, 32, 64, 128 (groups = group_size
  *         consecutive columns in sweep order; the last may be shorter).
@@ -189,10 +191,10 @@ gptq_status gptq_prepare_hinv(const double* S, int64_t in_features, int64_t n_to
  * zero without the clamp; the errors, the propagation and row_loss use that
  * unclamped code, the stored byte is it saturated to [0, 255]),
  * GPTQ_FLAG_FACTOR_FORM (the same sweep, carried differently: since the
- * scaled errors are E = (W - Q) U^-1, the sum over the earlier blocks is
- * formed from the residuals q - w of the original weights through R, and the
- * block's current values are W - that sum times U's diagonal block; results
- * agree with the plain form up to rounding). Synchronizes
+ * scaled errors are E = (W - Q) R, R = U^-1, the sum over the earlier blocks
+ * E[:, :j0] U[:j0, blk] equals (Q - W)[:, :j0] M[:j0, blk], formed from the
+ * residuals q - w of the original weights; results agree with the plain
+ * form up to rounding). Synchronizes
  * `stream` at the end unless
  * GPTQ_FLAG_NO_SYNC; returns GPTQ_ENONFINITE if a weight is NaN/Inf or a
  * scale overflows fp16 (outputs are then unspecified).
