@@ -262,6 +262,7 @@ KERNEL_CLASS = {  # device function name -> timing class
     "q_sweep_kernel": "quant_sweep",
     "prep_gather_kernel": "prepare_gather", "prep_uout_kernel": "prepare_uout",
     "prep_uout_z_kernel": "prepare_uout", "prep_mout_kernel": "prepare_uout",
+    "prep_mfac_kernel": "prepare_uout",
     "mp_init_kernel": "minpivot_step",
     "mp_step_kernel": "minpivot_step", "mp_panel_kernel": "minpivot_step",
     "mp_update_kernel": "minpivot_update",
