@@ -525,8 +525,8 @@ def main():
                          clip=not args.no_clip,
                          damp=wl.damp, device=dev)
         dev_inputs[h.name] = (chunks, torch.from_numpy(W).to(dev), grp)
-        # the plain sweep may take the factor form; SSQR, HPTQ and CHMC take U
-        plain = args.ssqr is None and args.hptq is None and args.chmc is None
+        # the plain and CHMC sweeps may take the factor form; SSQR and HPTQ take U
+        plain = args.ssqr is None and args.hptq is None
         plan.append(HPlan(h.name, h.dim, wl.n_tokens, W.shape[0], split8=grp.split8,
                           factor_form=grp.factor_form and plain))
         layer_rows[h.name] = [(l.name, l.rows) for l in wl.layers_of(h.name)]

@@ -430,7 +430,10 @@ gptq_status gptq_hptq_decode(const uint32_t* words, int64_t nwords, const int64_
  *   omega   (in, fp64, device, [cols x rank] row-major) the Gaussian sketch;
  *   rank    in [0, min(64, rows, cols)] (0: no low-rank part; omega, A, B
  *           may then be NULL); bits in [2, 8]; group_size 32, 64 or 128;
- *   flags   0 or GPTQ_FLAG_NO_SYNC;
+ *   flags   0, GPTQ_FLAG_NO_SYNC, GPTQ_FLAG_FACTOR_FORM (U is then the
+ *           factor-form matrix of gptq_prepare_hinv with that flag, and the
+ *           residual sweep forms its update sums from the residuals q - r of
+ *           the residual matrix's entries, as gptq_quantize_layer does);
  *   A       (out, fp16 bits [rows x rank]), B (out, fp16 bits [rank x cols]);
  *           each component is determined up to a common sign of its column
  *           of A and row of B;

@@ -578,7 +578,7 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
     const double* __restrict__ cur, const float* __restrict__ U,
     const int32_t* __restrict__ perm, int bits, double* __restrict__ ET,
     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
-    double* __restrict__ row_loss, unsigned* __restrict__ status) {
+    double* __restrict__ row_loss, unsigned* __restrict__ status, bool fac) {
   constexpr int RP = G >= 64 ? G / 64 : 1;  // rows per lane
   constexpr int NC = CH_QB / 4;             // columns per wave
   constexpr int KPT = CH_SB * G / 256;      // errors per thread in the ET copy
@@ -744,7 +744,11 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
   };
 
   // errors of sub-block sb from LDS to ET (sweep order): thread t takes row
-  // t % G of the columns KPT (t / G) .. KPT (t / G) + KPT - 1
+  // t % G of the columns KPT (t / G) .. KPT (t / G) + KPT - 1. In the factor
+  // form (U holds R U over each block beyond U's diagonal blocks, R = U^-1)
+  // ET takes the residual q - r of the swept value r (the residual matrix's
+  // entry) instead: the dequantized value from the block's code and grid,
+  // the entry read again from ResT, their difference exact in fp64
   auto store_e = [&](int sb) {
     const int r = t % G, k0 = KPT * (t / G);
     const int64_t gr = grp * G + r;
@@ -752,9 +756,19 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
     if (gr < rows) {
       const double* es = &Es[sb & 1][0][0];
       double* dst = ET + (j0 + CH_SB * sb) * rows + gr;
+      if (fac) {
 #pragma unroll
-      for (int k = 0; k < KPT; ++k)
-        if (k0 + k < kn) dst[(k0 + k) * rows] = es[(k0 + k) * G + r];
+        for (int k = 0; k < KPT; ++k)
+          if (k0 + k < kn) {
+            const int c = CH_SB * sb + k0 + k;
+            const double dq = Sd[c] * ((double)Ks[c][r] - Zd[c]);
+            dst[(k0 + k) * rows] = dq - ResT[(int64_t)Pm[c] * rows + gr];
+          }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KPT; ++k)
+          if (k0 + k < kn) dst[(k0 + k) * rows] = es[(k0 + k) * G + r];
+      }
     }
   };
 
@@ -911,8 +925,9 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
                                        uint16_t* B, uint8_t* codes, uint16_t* scales,
                                        uint16_t* zeros, double* row_loss, void* ws,
                                        size_t ws_bytes, void* stream, void* u_stream) {
-  if (flags & ~GPTQ_FLAG_NO_SYNC) return GPTQ_EINVAL;
+  if (flags & ~(GPTQ_FLAG_NO_SYNC | GPTQ_FLAG_FACTOR_FORM)) return GPTQ_EINVAL;
   if (rows <= 0 || cols <= 0 || n_tokens <= 0) return GPTQ_EINVAL;
+  const bool fac = (flags & GPTQ_FLAG_FACTOR_FORM) != 0;
   if (bits < 2 || bits > 8) return GPTQ_EINVAL;
   if (group_size != 32 && group_size != 64 && group_size != 128) return GPTQ_EINVAL;
   if (rank < 0 || rank > CH_RMAX || rank > rows || rank > cols) return GPTQ_EINVAL;
@@ -1039,7 +1054,7 @@ extern "C" gptq_status gptq_chmc_layer(const uint16_t* W, int64_t rows, int64_t 
   GPTQ_LAUNCH(K_CH_SWEEP, st,                                                                    \
               ch_sweep_rows_kernel<GS><<<ngr, 256, 0, st>>>(Res, o, i, j0, bw, cur, U, perm,      \
                                                              bits, E, codes, scales, zeros,      \
-                                                             row_loss, status))
+                                                             row_loss, status, fac))
     if (group_size == 32) CH_SWEEP(32);
     else if (group_size == 64) CH_SWEEP(64);
     else CH_SWEEP(128);

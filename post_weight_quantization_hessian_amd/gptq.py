@@ -551,7 +551,8 @@ def chmc_workspace_bytes(rows: int, cols: int, rank: int) -> int:
 
 def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_size: int = 128,
                bpw_target: float = 4.2875, sync: bool = True, workspace=None,
-               u_stream=None, out: CHMCLayer | None = None) -> CHMCLayer:
+               u_stream=None, out: CHMCLayer | None = None,
+               factor_form: bool = False) -> CHMCLayer:
     """The CHMC layer on the device: energies from diag(S), the rank-``rank``
     fp16 factors of W from the sketch ``omega`` (fp64 [cols x >= rank]; its
     first ``rank`` columns are used), the residual swept with one grid per
@@ -559,7 +560,8 @@ def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_s
     largest that fits ``bpw_target``. ``u_stream``: a torch stream on which U and
     perm are still being produced; the frontend then overlaps with that work
     and only the sweep waits for it. ``out``: buffers from chmc_outputs of the
-    same shape, rank, bits and group size to write into."""
+    same shape, rank, bits and group size to write into. ``factor_form``: U
+    is the matrix of prepare_hinv(..., factor_form=True)."""
     torch = _torch()
     _need(W, torch.float16, "W", 2)
     _need(S, torch.float64, "S", 2)
@@ -592,7 +594,9 @@ def chmc_layer(W, S, n_tokens, U, perm, omega, rank=None, bits: int = 4, group_s
     ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
     st = lib.gptq_chmc_layer(_ptr(W), rows, cols, W.stride(0), _ptr(S), int(n_tokens), _ptr(U),
                              _ptr(perm), _ptr(om), r, int(bits), int(group_size),
-                             0 if sync else GPTQ_FLAG_NO_SYNC, _ptr(A), _ptr(B), _ptr(codes),
+                             (0 if sync else GPTQ_FLAG_NO_SYNC)
+                             | (GPTQ_FLAG_FACTOR_FORM if factor_form else 0), _ptr(A), _ptr(B),
+                             _ptr(codes),
                              _ptr(scales), _ptr(zeros), _ptr(row_loss), _ptr(ws), ws.numel(),
                              _stream(),
                              C.c_void_p(u_stream.cuda_stream) if u_stream is not None

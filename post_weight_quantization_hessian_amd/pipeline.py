@@ -66,7 +66,8 @@ class LayerGroup:
         self.min_pivot = bool(min_pivot)  # the min-pivot order instead of act-order
         self.clip = bool(clip)  # False: the no-clipping sweep (codes may leave [0, maxq])
         # the plain sweep in the factor form (U's diagonal blocks and the factor
-        # of H beyond them); SSQR, HPTQ and CHMC take U itself
+        # of H beyond them), and so does the CHMC residual sweep; SSQR and HPTQ
+        # take U itself
         self.factor_form = factor_form_mode(factor_form, self.dim)
         if self.min_pivot:
             self.act_order = False
@@ -166,7 +167,7 @@ class LayerGroup:
         fork.record(main)
         G.prepare_hinv(self.S, n, damp=damp, act_order=self.act_order,
                        workspace=self.pws, out=(self.perm, self.U), sync=False,
-                       min_pivot=self.min_pivot)
+                       min_pivot=self.min_pivot, factor_form=self.factor_form)
         perm = self.perm if (self.act_order or self.min_pivot) else None
         out, r0 = [], 0
         with torch.cuda.stream(self.cstream):
@@ -183,7 +184,7 @@ class LayerGroup:
                     G.chmc_layer(W[r0:r0 + rows], self.S, self.n, self.U, perm, omega, rank=r,
                                  bits=b, group_size=self.group_size, bpw_target=bpw,
                                  sync=False, workspace=self.cws[key], u_stream=main,
-                                 out=self.couts[key])
+                                 out=self.couts[key], factor_form=self.factor_form)
                     out.append((name, b, self.couts[key]))
                 r0 += rows
             join = torch.cuda.Event()

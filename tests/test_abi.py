@@ -240,6 +240,9 @@ def test_chmc_host_checks():
     assert ch(n=0) == g.GPTQ_EINVAL
     assert ch(ldw=127) == g.GPTQ_EINVAL
     assert ch(flags=1) == g.GPTQ_EINVAL
+    assert ch(flags=g.GPTQ_FLAG_FACTOR_FORM | 1) == g.GPTQ_EINVAL
+    # the factor form passes the flag check (the workspace check comes next)
+    assert ch(flags=g.GPTQ_FLAG_FACTOR_FORM, ws=NULL) == g.GPTQ_EWORKSPACE
     assert ch(om=NULL) == g.GPTQ_EINVAL
     assert ch(A=NULL) == g.GPTQ_EINVAL
     assert ch(ws=NULL, wsb=0) == g.GPTQ_EWORKSPACE

@@ -332,12 +332,13 @@ def test_chmc_pipeline_two_streams_equals_serial_calls():
     S = torch.empty((dim, dim), dtype=torch.float64, device=DEV)
     G.hessian_accumulate(S, chunks[0], overwrite=True)
     G.hessian_accumulate(S, chunks[1])
-    perm, U = G.prepare_hinv(S, n, damp=CHMC_DAMP, act_order=True)
+    ff = grp.factor_form  # the group's form (U below 768 features)
+    perm, U = G.prepare_hinv(S, n, damp=CHMC_DAMP, act_order=True, factor_form=ff)
     ref, r0 = {}, 0
     for name, rows in layers:
         for b in (4, 3):
             ref[(name, b)] = G.chmc_layer(Wd[r0:r0 + rows], S, n, U, perm, om, bits=b,
-                                          group_size=gs, bpw_target=bpw)
+                                          group_size=gs, bpw_target=bpw, factor_form=ff)
         r0 += rows
     for rep in range(2):
         out = grp.chmc(chunks, Wd, layers, bpw, om)
@@ -351,3 +352,27 @@ def test_chmc_pipeline_two_streams_equals_serial_calls():
             for x, y in ((q.A, e.A), (q.B, e.B), (q.codes, e.codes), (q.scales, e.scales),
                          (q.zeros, e.zeros), (q.row_loss, e.row_loss)):
                 assert torch.equal(x, y), (rep, name, b)
+
+
+@pytest.mark.parametrize("rows,cols,n,bits,gs,act,rank", [
+    (200, 333, 700, 3, 64, False, 5),
+    (300, 896, 1900, 4, 128, True, 6),
+])
+def test_chmc_factor_form_matches_oracle(rows, cols, n, bits, gs, act, rank):
+    """The residual sweep in the factor form (U's diagonal blocks, R U beyond
+    them; the residuals q - r through it give the errors' update sums)
+    against the oracle's CHMC layer, at the same bar."""
+    say(f"chmc factor form {rows}x{cols} b{bits} g{gs} act={act} rank={rank}")
+    W, X = problem(rows, cols, n, rows * 11 + cols, lowrank=2)
+    S = torch.zeros((cols, cols), dtype=torch.float64, device=DEV)
+    G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
+    perm, M = G.prepare_hinv(S, n, damp=O.CHMC_DAMP, act_order=act, factor_form=True)
+    om = np.random.default_rng(rows + 1).standard_normal((cols, 64))
+    Sr, nr = O.hessian_sum(X)
+    ref = O.chmc_layer(W, Sr, nr, om, bits=bits, group_size=gs, act_order=act, rank=rank)
+    if act:
+        assert np.array_equal(perm.cpu().numpy(), ref["perm"])
+    res = G.chmc_layer(torch.from_numpy(W).to(DEV), S, n, M, perm if act else None,
+                       torch.from_numpy(om).to(DEV), rank=rank, bits=bits, group_size=gs,
+                       factor_form=True)
+    compare_chmc(res, ref, f"chmc factor form {rows}x{cols}")
