@@ -748,8 +748,9 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
   // form (U holds R U over each block beyond U's diagonal blocks, R = U^-1)
   // ET takes the residual q - r of the swept value r (the residual matrix's
   // entry) instead: the dequantized value from the block's code and grid,
-  // the entry read again from ResT, their difference exact in fp64
-  auto store_e = [&](int sb) {
+  // the entry (read from ResT while the sub-block was swept, in rv), their
+  // difference exact in fp64
+  auto store_e = [&](int sb, const double (&rv)[KPT]) {
     const int r = t % G, k0 = KPT * (t / G);
     const int64_t gr = grp * G + r;
     const int kn = min(CH_SB, bw - CH_SB * sb);
@@ -762,7 +763,7 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
           if (k0 + k < kn) {
             const int c = CH_SB * sb + k0 + k;
             const double dq = Sd[c] * ((double)Ks[c][r] - Zd[c]);
-            dst[(k0 + k) * rows] = dq - ResT[(int64_t)Pm[c] * rows + gr];
+            dst[(k0 + k) * rows] = dq - rv[k];
           }
       } else {
 #pragma unroll
@@ -772,10 +773,29 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
     }
   };
 
+  // factor form: the residual matrix's entries of sub-block sb, loaded when
+  // its sweep starts and used by its store one sub-block later
+  auto load_r = [&](int sb, double (&rv)[KPT]) {
+    const int r = t % G, k0 = KPT * (t / G);
+    const int64_t gr = grp * G + r;
+    const int kn = min(CH_SB, bw - CH_SB * sb);
+#pragma unroll
+    for (int k = 0; k < KPT; ++k)
+      rv[k] = (gr < rows && k0 + k < kn)
+                  ? ResT[(int64_t)Pm[CH_SB * sb + k0 + k] * rows + gr] : 0.0;
+  };
+  double rA[KPT], rB[KPT];
+#pragma unroll
+  for (int k = 0; k < KPT; ++k) rA[k] = rB[k] = 0.0;
   const int nsb = (bw + CH_SB - 1) / CH_SB;
   for (int sb = 0; sb < nsb; ++sb) {
     const int owner = sb >> 1;
-    if (sb > 0) store_e(sb - 1);
+    if (fac) {
+#pragma unroll
+      for (int k = 0; k < KPT; ++k) rA[k] = rB[k];  // sub-block sb - 1
+      load_r(sb, rB);
+    }
+    if (sb > 0) store_e(sb - 1, rA);
     if (wv == owner) {
       if (sb & 1) {
         if (sb > 0) apply(sb - 1, std::integral_constant<int, CH_SB>{},
@@ -793,7 +813,7 @@ __global__ __launch_bounds__(256) void ch_sweep_rows_kernel(
     }
     __syncthreads();
   }
-  store_e(nsb - 1);
+  store_e(nsb - 1, rB);
   // codes and grids to the original columns
   if (!perm && bw == CH_QB && (cols & 3) == 0 && ((uintptr_t)codes & 3) == 0) {
     // four consecutive columns of a row per store: lane = column quad
