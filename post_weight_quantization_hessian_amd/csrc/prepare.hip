@@ -8,6 +8,14 @@
 // which is upper triangular with U^T U = Hp^-1. One Cholesky and one
 // triangular inverse, both blocked by 128 in fp64 on MFMA; K is padded to a
 // multiple of 128 with an identity block so no kernel needs edge masks.
+// The factor form skips the inverse beyond the 128 x 128 diagonal tiles:
+// R = J L J = U^-1 is the upper factor of Hp itself (Hp = R R^T), and the
+// output holds U's diagonal blocks and R U over each block beyond them (one
+// 128 x 128 product per tile of L), which the sweep takes with the
+// residuals Q - W in place of the scaled errors (The Geometry of LLM
+// Quantization 2.1-2.2: any triangular factor of the Hessian serves the
+// nearest-plane step). K is then padded before the matrix, so that its tiles
+// end at the matrix end and map onto the sweep's 128-blocks.
 #include "gemm64.h"
 #include "trtri_order.h"
 

@@ -15,6 +15,11 @@
 // residual is broadcast to its row with row_newbcast (one 64-bit DPP move).
 // Group min/max and the loss are reduced over the row with quad permutes and
 // row rotations.
+// In the factor form the matrix beyond U's diagonal blocks is R U over each
+// block (R = U^-1, prepare.hip) and E holds the residuals Q - W of the
+// original weights: (Q - W)[:, :j0] (R U)[:j0, blk] is the same update sum
+// as E[:, :j0] U[:j0, blk] (E = (W - Q) R), so the GEMM and the in-block
+// sweep are unchanged and only the stored E differs.
 #include <type_traits>
 
 #include "common.h"
