@@ -924,7 +924,7 @@ __global__ __launch_bounds__(256) void prep_uout_kernel(const double* __restrict
 // the upper factor of H itself (H_p = R R^T); the sweep's residuals Q - W
 // through it give E U (E = (W - Q) R and, U being upper, R[:j0, :j0]
 // U[:j0, blk] = -R[:j0, blk] U[blk, blk]).
-__global__ __launch_bounds__(256) void prep_mfac_kernel(double* __restrict__ K,
+__global__ __launch_bounds__(256, 2) void prep_mfac_kernel(double* __restrict__ K,
                                                         const double* __restrict__ Xb,
                                                         int64_t ld) {
   __shared__ double smem[4 * GCH];
