@@ -93,3 +93,26 @@ def test_noalloc_rejects_a_layer_beyond_its_array():
     st = f(fake, rows, cols, cols, fake, None, 4, 128, 0, fake, fake, fake, fake, fake,
            G._stream())
     assert st == G.GPTQ_EWORKSPACE
+
+
+def test_noalloc_factor_form_matches_workspace_entry_point():
+    """The flags pass through: the factor form (the matrix of prepare_hinv
+    with that flag) gives the workspace entry point's results bit for bit,
+    on two calls in a row, the second smaller."""
+    for rows, cols, bits, gs, seed in [(256, 1024, 4, 128, 21), (64, 300, 3, 32, 22)]:
+        say(f"noalloc factor form {rows}x{cols} b{bits} g{gs}")
+        rng = np.random.default_rng(seed)
+        n = 2 * cols + 7
+        X = (rng.standard_normal((n, cols)) + 0.7 * rng.standard_normal((n, 1))).astype(np.float32)
+        S = torch.zeros((cols, cols), dtype=torch.float64, device=DEV)
+        G.hessian_accumulate(S, torch.from_numpy(X).to(DEV), overwrite=True)
+        perm, M = G.prepare_hinv(S, n, damp=0.01, act_order=True, factor_form=True)
+        W = weights(rows, cols, seed + 100)
+        ref = G.quantize_layer(W, M, perm, bits=bits, group_size=gs, factor_form=True)
+        out = outputs(rows, cols, gs, bits)
+        st = noalloc(W, M, perm, bits, gs, out, flags=G.GPTQ_FLAG_FACTOR_FORM)
+        assert st == G.GPTQ_OK, G.lib.gptq_status_string(st)
+        torch.cuda.synchronize()
+        for x, y in ((out.codes, ref.codes), (out.scales, ref.scales), (out.zeros, ref.zeros),
+                     (out.g_idx, ref.g_idx), (out.row_loss, ref.row_loss)):
+            assert torch.equal(x, y)
